@@ -1,0 +1,169 @@
+"""fp64 CPU oracle for the gated linear-attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: the plain, slow checker that the GPU library is
+compared against. Only the tests, the smoke check and the benchmark's CPU
+baseline may import it; the GPU library never does, and this package imports
+nothing from it. The arithmetic lives in ``gla_oracle.c`` (plain C, fp64,
+OpenMP over independent slabs); this module only builds that file with gcc and
+marshals numpy arrays into it.
+
+Formulations (each function returns ``(o, S_out, z_out)`` as float64 arrays):
+
+* :func:`recurrent` -- decay, rank-1 update per token, then the frame readout.
+* :func:`quadratic` -- explicit weighted sum over key tokens (O(N^2 d)).
+* :func:`chunked`   -- chunk sums of phi(k) v^T, per-frame sum, scan, readout.
+
+Definitions followed: the gated linear attention token mixer of "SANA-Video
+2.0: Hybrid Linear Attention with Attention Residuals for Efficient Video
+Generation" (section "Hybrid Linear-Softmax Attention"), its fixed D x D state
+updated additively block by block ("SANA-Video: Efficient Video Generation with
+Block Linear Diffusion Transformer", ICLR 2026 oral talk, block KV cache
+passage) and frame-wise decay gates ("SANA-WM" analysis page, method
+components). The readings where the pages are silent are stated in
+``gla_oracle.c``.
+
+Input arrays are ``[B, H, N, d]``; their dtype selects the exact upcast:
+``uint16`` holds bfloat16 bit patterns, ``float32`` and ``float64`` are used
+as they are. ``gamma`` is ``[B, H, F]``, ``S_in`` ``[B, H, d, d]``, ``z_in``
+``[B, H, d]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+BIDIR = 0
+FRAMECAUSAL = 1
+
+_DT = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.float64): 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile ``gla_oracle.c`` into ``liboracle.so`` next to it (gcc, fp64)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp = ctypes.c_void_p
+    common = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+              ctypes.c_double]
+    lib.gla_oracle_recurrent.argtypes = common + [ctypes.c_int]
+    lib.gla_oracle_quadratic.argtypes = common + [ctypes.c_int]
+    lib.gla_oracle_chunked.argtypes = common + [ctypes.c_int, ctypes.c_int]
+    for fn in (lib.gla_oracle_recurrent, lib.gla_oracle_quadratic, lib.gla_oracle_chunked):
+        fn.restype = ctypes.c_int
+    lib.gla_oracle_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    """Threads the oracle's OpenMP runtime would use by default."""
+    return int(_load().gla_oracle_max_threads())
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _prep(mode, q, k, v, g, gamma, S_in, z_in, F, T, outputs):
+    k = np.ascontiguousarray(k)
+    if k.ndim != 4:
+        raise ValueError("k must be [B, H, N, d]")
+    B, H, N, d = k.shape
+    dt = _DT.get(k.dtype)
+    if dt is None:
+        raise TypeError("unsupported input dtype %s" % k.dtype)
+    v = np.ascontiguousarray(v)
+    arrays = [v]
+    if outputs:
+        q = np.ascontiguousarray(q)
+        g = np.ascontiguousarray(g)
+        arrays += [q, g]
+    else:
+        q = g = None
+    for a in arrays:
+        if a.shape != k.shape or a.dtype != k.dtype:
+            raise ValueError("q, k, v, g must share shape and dtype")
+    if mode == BIDIR:
+        F, T = 1, N
+        gamma = S_in = z_in = None
+    else:
+        if F is None:
+            if gamma is None:
+                raise ValueError("frame-causal mode needs F (or gamma)")
+            F = np.shape(gamma)[-1]
+        if T is None:
+            T = N // F
+        if F * T != N:
+            raise ValueError("N must equal F * T")
+        gamma = np.ascontiguousarray(np.broadcast_to(np.asarray(gamma, np.float64), (B, H, F)))
+        if S_in is not None:
+            S_in = np.ascontiguousarray(np.asarray(S_in, np.float64).reshape(B, H, d, d))
+        if z_in is not None:
+            z_in = np.ascontiguousarray(np.asarray(z_in, np.float64).reshape(B, H, d))
+    o = np.empty((B, H, N, d), np.float64) if outputs else None
+    S_out = np.empty((B, H, d, d), np.float64)
+    z_out = np.empty((B, H, d), np.float64)
+    return q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d, dt
+
+
+def _run(fn, mode, q, k, v, g, gamma, S_in, z_in, F, T, eps, outputs, extra, nthreads):
+    (q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d, dt) = _prep(
+        mode, q, k, v, g, gamma, S_in, z_in, F, T, outputs)
+    fn(mode, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in),
+       _ptr(o), _ptr(S_out), _ptr(z_out), B, H, F, T, d, float(eps), *extra, int(nthreads))
+    return o, S_out, z_out
+
+
+def recurrent(mode, q, k, v, g, gamma=None, S_in=None, z_in=None, F=None, T=None,
+              eps=1e-6, outputs=True, nthreads=0):
+    """Recurrent form R. ``outputs=False`` computes only (S_out, z_out)."""
+    return _run(_load().gla_oracle_recurrent, mode, q, k, v, g, gamma, S_in, z_in, F, T, eps,
+                outputs, (), nthreads)
+
+
+def quadratic(mode, q, k, v, g, gamma=None, S_in=None, z_in=None, F=None, T=None,
+              eps=1e-6, outputs=True, nthreads=0):
+    """Quadratic brute-force form Q (O(N^2 d) per slab: small inputs only)."""
+    return _run(_load().gla_oracle_quadratic, mode, q, k, v, g, gamma, S_in, z_in, F, T, eps,
+                outputs, (), nthreads)
+
+
+def chunked(mode, q, k, v, g, gamma=None, S_in=None, z_in=None, F=None, T=None,
+            eps=1e-6, C=7, outputs=True, nthreads=0):
+    """Chunked form C with chunk length ``C`` (the last chunk of a frame may be shorter)."""
+    return _run(_load().gla_oracle_chunked, mode, q, k, v, g, gamma, S_in, z_in, F, T, eps,
+                outputs, (int(C),), nthreads)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns (uint16) as float64."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+if __name__ == "__main__":  # pragma: no cover
+    print(build())
+    sys.exit(0)

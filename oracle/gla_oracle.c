@@ -1,0 +1,353 @@
+/*
+ * gla_oracle.c -- fp64 CPU oracle for the gated linear-attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the checker that the GPU library is
+ * compared against. It shares no code, header, table or helper with the HIP
+ * library; only the test suite, the smoke check and the benchmark's CPU
+ * baseline load it. The product path never calls it.
+ *
+ * What is computed (per batch b and head h, each an independent N x d slab):
+ *
+ *   phi(x)   = max(x, 0)                         ReLU feature map
+ *   sigma(x) = 1 / (1 + exp(-x))                 output gate
+ *
+ *   frame-causal mode, tokens grouped into F frames of T tokens:
+ *     S_{-1} = S_in (or 0), z_{-1} = z_in (or 0)
+ *     S_f = gamma_f * S_{f-1} + sum_{t in f} phi(k_t) v_t^T      (d x d)
+ *     z_f = gamma_f * z_{f-1} + sum_{t in f} phi(k_t)            (d)
+ *     o_t = sigma(g_t) (.) (phi(q_t)^T S_f) / (phi(q_t)^T z_f + eps),  t in f
+ *     S_out = S_{F-1}, z_out = z_{F-1}
+ *
+ *   bidirectional mode: one state over the whole sequence, no decay, no carry:
+ *     S = sum_t phi(k_t) v_t^T, z = sum_t phi(k_t), same readout for every t.
+ *
+ * Sources:
+ *  - "SANA-Video 2.0: Hybrid Linear Attention with Attention Residuals for
+ *    Efficient Video Generation" (project page), section "Hybrid Linear-Softmax
+ *    Attention": gated linear attention carries the O(N) token mixing.
+ *  - "SANA-Video: Efficient Video Generation with Block Linear Diffusion
+ *    Transformer" (ICLR 2026 oral, talk transcript), block KV cache passage:
+ *    the linear-attention state has a fixed D x D shape independent of the
+ *    sequence length, and each new block adds its K^T V contribution to the
+ *    cached state (block-causal linear attention, global history).
+ *  - "SANA-WM: Efficient Minute-Scale World Modeling with Hybrid Linear
+ *    Diffusion Transformer" (analysis page), method components: plain
+ *    cumulative linear attention has no decay and drifts at minute scale; the
+ *    frame-wise variant adds decay gates to the recurrent state.
+ *  The pages print neither the feature map, the gate, the normaliser nor eps;
+ *  the readings taken (ReLU, sigmoid gate after normalisation, normaliser z
+ *  decayed with the same gamma, eps added to the denominator, a frame's own
+ *  tokens included in its state) are the plainest ones and are listed with the
+ *  design notes of this repository.
+ *
+ * Three formulations, written independently of each other:
+ *   R  recurrent: decay, then one rank-1 update per token, then the frame's
+ *      readout (the whole frame is in the state before any of its outputs)
+ *   Q  quadratic: o_t from the explicit weighted sum over all earlier-or-same
+ *      frame tokens, A_ts = (phi(q_t).phi(k_s)) * prod_{m=frame(s)+1}^{frame(t)} gamma_m
+ *   C  chunked:   per-chunk sums of phi(k)v^T, summed per frame, then the scan
+ *
+ * Inputs are read element by element and converted exactly to double:
+ *   dtype 0 = float32, 1 = bfloat16 (stored as uint16 bit patterns),
+ *   2 = float64.  gamma, S_in, z_in and all outputs are float64.
+ * Layout: q, k, v, g, o are [B][H][N][d] row-major; gamma is [B][H][F];
+ *   S is [B][H][d][d] (S[i][j]: i = key feature, j = value feature); z [B][H][d].
+ * Parallelism: OpenMP over independent (b, h, value-column block) tasks. The
+ *   columns of S and o are independent sums; splitting them across threads
+ *   does not change the order of any floating-point operation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+enum { ORC_BIDIR = 0, ORC_FRAMECAUSAL = 1 };
+
+/* exact conversion of one stored input element to double */
+static double ld(const void *p, int dt, size_t i) {
+  if (dt == ORC_F64) return ((const double *)p)[i];
+  if (dt == ORC_F32) return (double)((const float *)p)[i];
+  uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16; /* bf16 -> f32 */
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static double relu(double x) { return x > 0.0 ? x : 0.0; }
+static double sigm(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static int set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  return omp_get_max_threads();
+#else
+  (void)nthreads;
+  return 1;
+#endif
+}
+
+int gla_oracle_max_threads(void) { return set_threads(0); }
+
+/* ------------------------------------------------------------------------ */
+/* R: recurrent form                                                         */
+/* ------------------------------------------------------------------------ */
+/* mode: ORC_BIDIR (F must be 1, T = N, gamma/S_in/z_in ignored) or
+ * ORC_FRAMECAUSAL. q, g and o may all be NULL: then only the state is
+ * produced (the block-cache commit). S_in/z_in may be NULL (zero state).
+ * S_out/z_out may be NULL. Returns the number of threads used. */
+int gla_oracle_recurrent(int mode, int dt, const void *q, const void *k, const void *v,
+                         const void *g, const double *gamma, const double *S_in,
+                         const double *z_in, double *o, double *S_out, double *z_out,
+                         int B, int H, int F, int T, int d, double eps, int nthreads) {
+  const int CB = 8; /* value columns per task */
+  const int ncb = (d + CB - 1) / CB;
+  const long ntask = (long)B * H * ncb;
+  const size_t N = (size_t)F * T;
+  const int used = set_threads(nthreads);
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long task = 0; task < ntask; ++task) {
+    const long bh = task / ncb;
+    const int j0 = (int)(task % ncb) * CB;
+    const int nj = (j0 + CB <= d) ? CB : d - j0;
+    double *S = (double *)calloc((size_t)d * CB, sizeof(double)); /* S[i][jj] */
+    double *z = (double *)calloc((size_t)d, sizeof(double));
+    double *fk = (double *)malloc((size_t)d * sizeof(double));
+    const size_t base = (size_t)bh * N * d;
+
+    if (mode == ORC_FRAMECAUSAL && S_in) {
+      for (int i = 0; i < d; ++i)
+        for (int jj = 0; jj < nj; ++jj) S[i * CB + jj] = S_in[(size_t)bh * d * d + (size_t)i * d + j0 + jj];
+    }
+    if (mode == ORC_FRAMECAUSAL && z_in) {
+      for (int i = 0; i < d; ++i) z[i] = z_in[(size_t)bh * d + i];
+    }
+
+    for (int f = 0; f < F; ++f) {
+      if (mode == ORC_FRAMECAUSAL) {
+        const double gm = gamma[(size_t)bh * F + f];
+        for (int i = 0; i < d; ++i) {
+          z[i] *= gm;
+          for (int jj = 0; jj < nj; ++jj) S[i * CB + jj] *= gm;
+        }
+      }
+      /* rank-1 update for every token of the frame */
+      for (int t = 0; t < T; ++t) {
+        const size_t row = base + ((size_t)f * T + t) * d;
+        for (int i = 0; i < d; ++i) fk[i] = relu(ld(k, dt, row + i));
+        for (int i = 0; i < d; ++i) {
+          z[i] += fk[i];
+          for (int jj = 0; jj < nj; ++jj) S[i * CB + jj] += fk[i] * ld(v, dt, row + j0 + jj);
+        }
+      }
+      /* readout: every token of the frame sees the state including its frame */
+      if (o) {
+        for (int t = 0; t < T; ++t) {
+          const size_t row = base + ((size_t)f * T + t) * d;
+          double den = 0.0;
+          for (int i = 0; i < d; ++i) den += relu(ld(q, dt, row + i)) * z[i];
+          for (int jj = 0; jj < nj; ++jj) {
+            double num = 0.0;
+            for (int i = 0; i < d; ++i) num += relu(ld(q, dt, row + i)) * S[i * CB + jj];
+            o[row + j0 + jj] = sigm(ld(g, dt, row + j0 + jj)) * num / (den + eps);
+          }
+        }
+      }
+    }
+
+    if (S_out) {
+      for (int i = 0; i < d; ++i)
+        for (int jj = 0; jj < nj; ++jj) S_out[(size_t)bh * d * d + (size_t)i * d + j0 + jj] = S[i * CB + jj];
+    }
+    if (z_out && j0 == 0) {
+      for (int i = 0; i < d; ++i) z_out[(size_t)bh * d + i] = z[i];
+    }
+    free(S);
+    free(z);
+    free(fk);
+  }
+  return used;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q: quadratic (brute-force) form                                           */
+/* ------------------------------------------------------------------------ */
+/* decay weight between a key in frame fs and a query in frame ft:
+ *   prod_{m=fs+1}^{ft} gamma_m if fs <= ft (empty product = 1), else 0 */
+static double pair_decay(const double *gm, int fs, int ft) {
+  if (fs > ft) return 0.0;
+  double w = 1.0;
+  for (int m = fs + 1; m <= ft; ++m) w *= gm[m];
+  return w;
+}
+
+/* weight of the carried-in state seen from frame ft: prod_{m=0}^{ft} gamma_m */
+static double carry_decay(const double *gm, int ft) {
+  double w = 1.0;
+  for (int m = 0; m <= ft; ++m) w *= gm[m];
+  return w;
+}
+
+int gla_oracle_quadratic(int mode, int dt, const void *q, const void *k, const void *v,
+                         const void *g, const double *gamma, const double *S_in,
+                         const double *z_in, double *o, double *S_out, double *z_out,
+                         int B, int H, int F, int T, int d, double eps, int nthreads) {
+  const size_t N = (size_t)F * T;
+  const long ntask = (long)B * H * (long)N;
+  const int used = set_threads(nthreads);
+
+  /* outputs: one task per query token */
+  if (o) {
+#pragma omp parallel for schedule(static)
+    for (long task = 0; task < ntask; ++task) {
+      const long bh = task / (long)N;
+      const size_t t = (size_t)(task % (long)N);
+      const int ft = (int)(t / T);
+      const size_t base = (size_t)bh * N * d;
+      const double *gm = gamma ? gamma + (size_t)bh * F : NULL;
+      double *num = (double *)calloc((size_t)d, sizeof(double));
+      double den = 0.0;
+      for (size_t s = 0; s < N; ++s) {
+        const int fs = (int)(s / T);
+        double w = (mode == ORC_BIDIR) ? 1.0 : pair_decay(gm, fs, ft);
+        if (w == 0.0 && fs > ft) continue;
+        double a = 0.0;
+        for (int i = 0; i < d; ++i)
+          a += relu(ld(q, dt, base + t * d + i)) * relu(ld(k, dt, base + s * d + i));
+        a *= w;
+        den += a;
+        for (int j = 0; j < d; ++j) num[j] += a * ld(v, dt, base + s * d + j);
+      }
+      if (mode == ORC_FRAMECAUSAL && (S_in || z_in)) {
+        const double c = carry_decay(gm, ft);
+        for (int j = 0; j < d && S_in; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < d; ++i)
+            acc += relu(ld(q, dt, base + t * d + i)) * S_in[(size_t)bh * d * d + (size_t)i * d + j];
+          num[j] += c * acc;
+        }
+        if (z_in) {
+          double acc = 0.0;
+          for (int i = 0; i < d; ++i) acc += relu(ld(q, dt, base + t * d + i)) * z_in[(size_t)bh * d + i];
+          den += c * acc;
+        }
+      }
+      for (int j = 0; j < d; ++j)
+        o[base + t * d + j] = sigm(ld(g, dt, base + t * d + j)) * num[j] / (den + eps);
+      free(num);
+    }
+  }
+
+  /* final state as an explicit weighted sum: S_out = sum_s w_s phi(k_s) v_s^T + c S_in */
+  if (S_out || z_out) {
+    const long nbh = (long)B * H;
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < nbh; ++bh) {
+      const size_t base = (size_t)bh * N * d;
+      const double *gm = gamma ? gamma + (size_t)bh * F : NULL;
+      const int fl = F - 1;
+      for (int i = 0; i < d; ++i) {
+        double zi = 0.0;
+        for (size_t s = 0; s < N; ++s) {
+          const double w = (mode == ORC_BIDIR) ? 1.0 : pair_decay(gm, (int)(s / T), fl);
+          zi += w * relu(ld(k, dt, base + s * d + i));
+        }
+        if (mode == ORC_FRAMECAUSAL && z_in) zi += carry_decay(gm, fl) * z_in[(size_t)bh * d + i];
+        if (z_out) z_out[(size_t)bh * d + i] = zi;
+        if (!S_out) continue;
+        for (int j = 0; j < d; ++j) {
+          double sij = 0.0;
+          for (size_t s = 0; s < N; ++s) {
+            const double w = (mode == ORC_BIDIR) ? 1.0 : pair_decay(gm, (int)(s / T), fl);
+            sij += w * relu(ld(k, dt, base + s * d + i)) * ld(v, dt, base + s * d + j);
+          }
+          if (mode == ORC_FRAMECAUSAL && S_in)
+            sij += carry_decay(gm, fl) * S_in[(size_t)bh * d * d + (size_t)i * d + j];
+          S_out[(size_t)bh * d * d + (size_t)i * d + j] = sij;
+        }
+      }
+    }
+  }
+  return used;
+}
+
+/* ------------------------------------------------------------------------ */
+/* C: chunked form                                                           */
+/* ------------------------------------------------------------------------ */
+/* Each frame (the whole sequence in bidirectional mode) is cut into chunks of
+ * C tokens, the last one possibly shorter. Per chunk: U_c = sum phi(k)v^T and
+ * u_c = sum phi(k). Per frame: U_f = sum of its chunks. Then the scan
+ * S_f = gamma_f S_{f-1} + U_f (bidirectional: S = U of the single frame) and
+ * the readout of every token of frame f against S_f. */
+int gla_oracle_chunked(int mode, int dt, const void *q, const void *k, const void *v,
+                       const void *g, const double *gamma, const double *S_in,
+                       const double *z_in, double *o, double *S_out, double *z_out, int B,
+                       int H, int F, int T, int d, double eps, int C, int nthreads) {
+  const size_t N = (size_t)F * T;
+  const long nbh = (long)B * H;
+  const int used = set_threads(nthreads);
+  if (C < 1) C = 1;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < nbh; ++bh) {
+    const size_t base = (size_t)bh * N * d;
+    const size_t dd = (size_t)d * d;
+    double *Uf = (double *)malloc(dd * sizeof(double));
+    double *uf = (double *)malloc((size_t)d * sizeof(double));
+    double *Uc = (double *)malloc(dd * sizeof(double));
+    double *uc = (double *)malloc((size_t)d * sizeof(double));
+    double *S = (double *)calloc(dd, sizeof(double));
+    double *z = (double *)calloc((size_t)d, sizeof(double));
+    if (mode == ORC_FRAMECAUSAL && S_in) memcpy(S, S_in + (size_t)bh * dd, dd * sizeof(double));
+    if (mode == ORC_FRAMECAUSAL && z_in) memcpy(z, z_in + (size_t)bh * d, (size_t)d * sizeof(double));
+
+    for (int f = 0; f < F; ++f) {
+      memset(Uf, 0, dd * sizeof(double));
+      memset(uf, 0, (size_t)d * sizeof(double));
+      for (int c0 = 0; c0 < T; c0 += C) {
+        const int c1 = (c0 + C < T) ? c0 + C : T;
+        memset(Uc, 0, dd * sizeof(double));
+        memset(uc, 0, (size_t)d * sizeof(double));
+        for (int t = c0; t < c1; ++t) {
+          const size_t row = base + ((size_t)f * T + t) * d;
+          for (int i = 0; i < d; ++i) {
+            const double fk = relu(ld(k, dt, row + i));
+            uc[i] += fk;
+            for (int j = 0; j < d; ++j) Uc[(size_t)i * d + j] += fk * ld(v, dt, row + j);
+          }
+        }
+        for (size_t e = 0; e < dd; ++e) Uf[e] += Uc[e];
+        for (int i = 0; i < d; ++i) uf[i] += uc[i];
+      }
+      const double gm = (mode == ORC_FRAMECAUSAL) ? gamma[(size_t)bh * F + f] : 1.0;
+      for (size_t e = 0; e < dd; ++e) S[e] = gm * S[e] + Uf[e];
+      for (int i = 0; i < d; ++i) z[i] = gm * z[i] + uf[i];
+
+      if (o) {
+        for (int t = 0; t < T; ++t) {
+          const size_t row = base + ((size_t)f * T + t) * d;
+          double den = 0.0;
+          for (int i = 0; i < d; ++i) den += relu(ld(q, dt, row + i)) * z[i];
+          for (int j = 0; j < d; ++j) {
+            double num = 0.0;
+            for (int i = 0; i < d; ++i) num += relu(ld(q, dt, row + i)) * S[(size_t)i * d + j];
+            o[row + j] = sigm(ld(g, dt, row + j)) * num / (den + eps);
+          }
+        }
+      }
+    }
+    if (S_out) memcpy(S_out + (size_t)bh * dd, S, dd * sizeof(double));
+    if (z_out) memcpy(z_out + (size_t)bh * d, z, (size_t)d * sizeof(double));
+    free(Uf);
+    free(uf);
+    free(Uc);
+    free(uc);
+    free(S);
+    free(z);
+  }
+  return used;
+}
