@@ -1,1 +1,239 @@
-"""MI355X-native gated linear-attention forward pass (placeholder; binding follows)."""
+"""MI355X-native gated linear-attention forward pass.
+
+A thin Python binding over ``libgla.so``, the C-ABI library whose entry points
+are declared in ``include/gla.h``. Every step of the computation runs in that
+library's HIP kernels; this module only checks and marshals arguments, and uses
+PyTorch for device memory and streams. If the library is not built, every call
+raises: there is no CPU fallback.
+
+Entry points (same names as the C ABI):
+
+* :func:`gla_fwd_bidir` -- bidirectional (whole-sequence) gated linear attention
+* :func:`gla_fwd_framecausal` -- frame-causal attention with per-frame decay and
+  an optional carried state (the block KV cache)
+* :func:`gla_state_carry` -- the carried state after more frames, from k, v only
+* ``gla_*_workspace`` -- workspace sizes in bytes
+
+The operation is the gated linear attention token mixer of "SANA-Video 2.0:
+Hybrid Linear Attention with Attention Residuals for Efficient Video
+Generation" (section "Hybrid Linear-Softmax Attention"), with the fixed D x D
+state and additive per-block update of the SANA-Video ICLR 2026 oral talk
+(block KV cache passage) and frame-wise decay gates ("SANA-WM" analysis page).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "GlaError", "gla_fwd_bidir", "gla_fwd_framecausal", "gla_state_carry",
+    "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace", "gla_state_carry_workspace",
+    "library_path", "load_library",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgla.so")
+_lib = None
+
+GLA_F32 = 0
+GLA_BF16 = 1
+
+
+class GlaError(RuntimeError):
+    """A non-OK status from libgla (the message carries the library's detail)."""
+
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__("libgla status %d (%s): %s" % (status, name, detail))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgla.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libgla.so is not built (%s); run `python -m "
+                           "gated_linear_attention_fwd_amd.build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.gla_fwd_bidir_workspace.argtypes = [i32, i32, i64, i32]
+    lib.gla_fwd_bidir_workspace.restype = sz
+    lib.gla_fwd_framecausal_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.gla_fwd_framecausal_workspace.restype = sz
+    lib.gla_state_carry_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.gla_state_carry_workspace.restype = sz
+    lib.gla_fwd_bidir.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, vp, sz, vp]
+    lib.gla_fwd_bidir.restype = i32
+    lib.gla_fwd_framecausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                        i32, i32, i32, f32, vp, sz, vp]
+    lib.gla_fwd_framecausal.restype = i32
+    lib.gla_state_carry.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
+                                    sz, vp]
+    lib.gla_state_carry.restype = i32
+    lib.gla_status_string.argtypes = [i32]
+    lib.gla_status_string.restype = ctypes.c_char_p
+    lib.gla_last_error.argtypes = []
+    lib.gla_last_error.restype = ctypes.c_char_p
+    lib.gla_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        raise GlaError(status, lib.gla_status_string(status).decode(),
+                       lib.gla_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GLA_F32
+    if t.dtype == torch.bfloat16:
+        return GLA_BF16
+    raise TypeError("inputs must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _require_device(*ts: Optional[torch.Tensor]) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libgla runs on the GPU only; got a tensor on %s" % t.device)
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _qkvg(*ts: Optional[torch.Tensor]):
+    ref = next(t for t in ts if t is not None)
+    if ref.dim() != 4:
+        raise ValueError("q, k, v, g must be [B, H, N, d]")
+    for t in ts:
+        if t is not None and (t.shape != ref.shape or t.dtype != ref.dtype):
+            raise ValueError("q, k, v, g must share shape and dtype")
+    return ref
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def gla_fwd_bidir_workspace(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().gla_fwd_bidir_workspace(B, H, N, d))
+
+
+def gla_fwd_framecausal_workspace(B: int, H: int, F: int, T: int, d: int) -> int:
+    return int(load_library().gla_fwd_framecausal_workspace(B, H, F, T, d))
+
+
+def gla_state_carry_workspace(B: int, H: int, F: int, T: int, d: int) -> int:
+    return int(load_library().gla_state_carry_workspace(B, H, F, T, d))
+
+
+def gla_fwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """o = sigmoid(g) * phi(q) S / (phi(q) z + eps) with one state over all N tokens."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g)
+    dt = _dtype_code(ref)
+    o = torch.empty_like(ref) if out is None else out
+    dev = _require_device(q, k, v, g, o, workspace)
+    B, H, N, d = ref.shape
+    ws, wsb = _workspace(lib.gla_fwd_bidir_workspace(B, H, N, d), dev, workspace)
+    _check(lib.gla_fwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), B, H, N, d,
+                             dt, eps, _ptr(ws), wsb, _stream_handle(stream, dev)))
+    return o
+
+
+def gla_fwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        gamma: torch.Tensor, S_in: Optional[torch.Tensor] = None,
+                        z_in: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                        out: Optional[torch.Tensor] = None, S_out: Optional[torch.Tensor] = None,
+                        z_out: Optional[torch.Tensor] = None, return_state: bool = False,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Frame-causal gated linear attention; F = gamma.shape[-1], T = N / F.
+
+    Returns ``o``, or ``(o, S_out, z_out)`` when ``return_state`` is set or
+    S_out/z_out are given (S_out may be S_in for an in-place carry)."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if F == 0 or N % F:
+        if not (F == 0 and N == 0):
+            raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    want_state = return_state or S_out is not None or z_out is not None
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
+    if want_state and z_out is None:
+        z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    o = torch.empty_like(ref) if out is None else out
+    dev = _require_device(q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, workspace)
+    ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
+    _check(lib.gla_fwd_framecausal(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in),
+                                   _ptr(z_in), _ptr(o), _ptr(S_out), _ptr(z_out), B, H, F, T, d,
+                                   dt, eps, _ptr(ws), wsb,
+                                   _stream_handle(stream, dev)))
+    return (o, S_out, z_out) if want_state else o
+
+
+def gla_state_carry(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+                    S_in: Optional[torch.Tensor] = None, z_in: Optional[torch.Tensor] = None,
+                    S_out: Optional[torch.Tensor] = None, z_out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """State (S, z) after the frames of k, v: the block KV cache commit."""
+    lib = load_library()
+    ref = _qkvg(k, v)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    if S_out is None:
+        S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
+    if z_out is None:
+        z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    dev = _require_device(k, v, gamma, S_in, z_in, S_out, z_out, workspace)
+    ws, wsb = _workspace(lib.gla_state_carry_workspace(B, H, F, T, d), dev, workspace)
+    _check(lib.gla_state_carry(_ptr(k), _ptr(v), _ptr(gamma), _ptr(S_in), _ptr(z_in),
+                               _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt,
+                               _ptr(ws), wsb, _stream_handle(stream, dev)))
+    return S_out, z_out

@@ -1,0 +1,68 @@
+// common.hpp -- device helpers shared by the HIP kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+// bfloat16 storage type: raw bits. The library never relies on a vendor bf16
+// class so that the rounding used for the output is the one written here.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even. Inputs are finite (NaN handling is not needed
+// for the outputs of this operation on finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float relu(float x) { return x > 0.f ? x : 0.f; }
+
+// Logistic sigmoid in fp32; exp overflow to +inf gives exactly 0, as it should.
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// Element access for the two storage dtypes.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float *p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float *p, int64_t i, float x) { p[i] = x; }
+  // 4 consecutive elements (16-byte aligned when i % 4 == 0)
+  __device__ __forceinline__ static float4 load4(const float *p, int64_t i) {
+    return *reinterpret_cast<const float4 *>(p + i);
+  }
+  __device__ __forceinline__ static void store4(float *p, int64_t i, float4 x) {
+    *reinterpret_cast<float4 *>(p + i) = x;
+  }
+};
+
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t *p, int64_t i) {
+    return bf16_to_f32(p[i].bits);
+  }
+  __device__ __forceinline__ static void store(bf16_t *p, int64_t i, float x) {
+    p[i].bits = f32_to_bf16_rne(x);
+  }
+  __device__ __forceinline__ static float4 load4(const bf16_t *p, int64_t i) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(p + i);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+  }
+  __device__ __forceinline__ static void store4(bf16_t *p, int64_t i, float4 x) {
+    uint2 w;
+    w.x = static_cast<uint32_t>(f32_to_bf16_rne(x.x)) |
+          (static_cast<uint32_t>(f32_to_bf16_rne(x.y)) << 16);
+    w.y = static_cast<uint32_t>(f32_to_bf16_rne(x.z)) |
+          (static_cast<uint32_t>(f32_to_bf16_rne(x.w)) << 16);
+    *reinterpret_cast<uint2 *>(p + i) = w;
+  }
+};
+
+}  // namespace gla

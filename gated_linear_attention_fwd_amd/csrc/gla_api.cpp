@@ -1,0 +1,338 @@
+// gla_api.cpp -- the exported C ABI: validation, planning and launches.
+//
+// Entry points and their contract are declared and documented in include/gla.h.
+// Everything here runs on the host; nothing is enqueued unless every argument
+// passed validation.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/gla.h"
+#include "plan.hpp"
+
+#define GLA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace gla {
+
+hipError_t launch_kv_valu(const Plan &p, int dtype, const KvArgs &a, hipStream_t s);
+hipError_t launch_readout_valu(const Plan &p, int dtype, const ReadoutArgs &a, hipStream_t s);
+hipError_t launch_kv_mfma(const Plan &p, const KvArgs &a, hipStream_t s);
+hipError_t launch_readout_mfma(const Plan &p, const ReadoutArgs &a, hipStream_t s);
+bool mfma_supports(int d);
+
+namespace {
+
+constexpr int64_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several times
+constexpr int64_t kMinPartTokens = 128;
+constexpr int64_t kMinSplitTokens = 64;
+constexpr int64_t kTokenAlign = 32;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+thread_local char g_last_error[512] = "";
+
+gla_status fail(gla_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  const void *p;
+  size_t n;
+  const char *name;
+};
+
+bool overlap(const Range &a, const Range &b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Path override for testing: GLA_PATH=valu forces the vector-ALU kernels.
+int path_override() {
+  const char *e = getenv("GLA_PATH");
+  if (!e) return -1;
+  if (!strcmp(e, "valu")) return 0;
+  if (!strcmp(e, "mfma")) return 1;
+  return -1;
+}
+
+gla_status check_dims(int B, int H, int d, int dt) {
+  if (B < 0 || H < 0) return fail(GLA_ERR_SHAPE, "B=%d and H=%d must be >= 0", B, H);
+  if (d != 16 && d != 32 && d != 64 && d != 128)
+    return fail(GLA_ERR_UNSUPPORTED, "head dimension d=%d not in {16, 32, 64, 128}", d);
+  if (dt != GLA_F32 && dt != GLA_BF16) return fail(GLA_ERR_UNSUPPORTED, "dtype %d unknown", dt);
+  return GLA_OK;
+}
+
+gla_status check_eps(float eps) {
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(GLA_ERR_VALUE, "eps=%g must be finite and >= 0", (double)eps);
+  return GLA_OK;
+}
+
+gla_status check_tensor_align(const void *p, const char *name) {
+  if (p && !aligned(p, 16)) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return GLA_OK;
+}
+
+gla_status check_ws(const Plan &p, void *ws, size_t ws_bytes) {
+  if (p.ws_bytes == 0) return GLA_OK;
+  if (!ws) return fail(GLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", p.ws_bytes);
+  if (ws_bytes < p.ws_bytes)
+    return fail(GLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, p.ws_bytes);
+  if (!aligned(ws, 256)) return fail(GLA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  return GLA_OK;
+}
+
+gla_status check_no_overlap(const Range *outs, int nout, const Range *all, int nall) {
+  for (int i = 0; i < nout; ++i)
+    for (int j = 0; j < nall; ++j) {
+      if (outs[i].p == all[j].p && !strcmp(outs[i].name, all[j].name)) continue;  // itself
+      if (overlap(outs[i], all[j]))
+        return fail(GLA_ERR_ALIAS, "%s overlaps %s", outs[i].name, all[j].name);
+    }
+  return GLA_OK;
+}
+
+gla_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(GLA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return GLA_OK;
+}
+
+#define GLA_TRY(expr)                     \
+  do {                                    \
+    gla_status _st = (expr);              \
+    if (_st != GLA_OK) return _st;        \
+  } while (0)
+
+// Shared body of gla_fwd_framecausal (with outputs) and gla_state_carry.
+gla_status run_framecausal(const void *q, const void *k, const void *v, const void *g,
+                           const float *gamma, const float *S_in, const float *z_in, void *o,
+                           float *S_out, float *z_out, int B, int H, int F, int T, int d,
+                           gla_dtype dt, float eps, void *ws, size_t ws_bytes, void *stream,
+                           bool outputs) {
+  GLA_TRY(check_dims(B, H, d, dt));
+  if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%d must be >= 0", F, T);
+  if (outputs) GLA_TRY(check_eps(eps));
+  if ((S_in == nullptr) != (z_in == nullptr))
+    return fail(GLA_ERR_NULL, "S_in and z_in must both be given or both be NULL");
+  if ((S_out == nullptr) != (z_out == nullptr))
+    return fail(GLA_ERR_NULL, "S_out and z_out must both be given or both be NULL");
+  if (!outputs && !S_out) return fail(GLA_ERR_NULL, "S_out and z_out are required");
+
+  const int64_t BH = (int64_t)B * H;
+  const int64_t N = (int64_t)F * T;
+  const size_t es = dt == GLA_F32 ? 4 : 2;
+  const size_t tensor_bytes = (size_t)(BH * N * d) * es;
+  const bool have_tokens = BH > 0 && N > 0;
+  if (have_tokens) {
+    if (!k || !v) return fail(GLA_ERR_NULL, "k and v are required");
+    if (outputs && (!q || !g || !o)) return fail(GLA_ERR_NULL, "q, g and o are required");
+  }
+  if (BH > 0 && F > 0 && !gamma) return fail(GLA_ERR_NULL, "gamma is required when F > 0");
+  GLA_TRY(check_tensor_align(q, "q"));
+  GLA_TRY(check_tensor_align(k, "k"));
+  GLA_TRY(check_tensor_align(v, "v"));
+  GLA_TRY(check_tensor_align(g, "g"));
+  GLA_TRY(check_tensor_align(o, "o"));
+  GLA_TRY(check_tensor_align(S_in, "S_in"));
+  GLA_TRY(check_tensor_align(z_in, "z_in"));
+  GLA_TRY(check_tensor_align(S_out, "S_out"));
+  GLA_TRY(check_tensor_align(z_out, "z_out"));
+  if (gamma && !aligned(gamma, 4)) return fail(GLA_ERR_ALIGN, "gamma is not 4-byte aligned");
+
+  Plan p;
+  if (!make_plan(BH, F, T, d, &p)) return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
+  if (BH == 0) return GLA_OK;
+  GLA_TRY(check_ws(p, ws, ws_bytes));
+
+  const size_t sbytes = (size_t)(BH * d * d) * 4, zbytes = (size_t)(BH * d) * 4;
+  const Range all[] = {{q, tensor_bytes, "q"},       {k, tensor_bytes, "k"},
+                       {v, tensor_bytes, "v"},       {g, tensor_bytes, "g"},
+                       {gamma, (size_t)(BH * F) * 4, "gamma"},
+                       {S_in, sbytes, "S_in"},       {z_in, zbytes, "z_in"},
+                       {o, outputs ? tensor_bytes : 0, "o"},
+                       {S_out, sbytes, "S_out"},     {z_out, zbytes, "z_out"},
+                       {ws, p.ws_bytes, "workspace"}};
+  // S_out may be S_in exactly (and z_out z_in): compare them without the inputs.
+  const Range outs_o[] = {{o, outputs ? tensor_bytes : 0, "o"}, {ws, p.ws_bytes, "workspace"}};
+  GLA_TRY(check_no_overlap(outs_o, 2, all, 11));
+  const Range outs_s[] = {{S_out, sbytes, "S_out"}, {z_out, zbytes, "z_out"}};
+  const Range others[] = {all[0], all[1], all[2], all[3], all[4], all[7], all[8], all[9], all[10]};
+  GLA_TRY(check_no_overlap(outs_s, 2, others, 9));
+  if (S_out && S_in && S_out != S_in && overlap(outs_s[0], all[5]))
+    return fail(GLA_ERR_ALIAS, "S_out partially overlaps S_in");
+  if (z_out && z_in && z_out != z_in && overlap(outs_s[1], all[6]))
+    return fail(GLA_ERR_ALIAS, "z_out partially overlaps z_in");
+  if (S_out && overlap(outs_s[0], all[6])) return fail(GLA_ERR_ALIAS, "S_out overlaps z_in");
+  if (z_out && overlap(outs_s[1], all[5])) return fail(GLA_ERR_ALIAS, "z_out overlaps S_in");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Path path = select_path(dt, d);
+  float *wsf = static_cast<float *>(ws);
+  if (F > 0) GLA_TRY(launched(launch_kv(p, dt, path, KvArgs{k, v, wsf}, s), "kv"));
+  GLA_TRY(launched(launch_scan(p, ScanArgs{wsf, gamma, S_in, z_in, S_out, z_out, outputs ? 1 : 0},
+                               s),
+                   "scan"));
+  if (outputs && have_tokens)
+    GLA_TRY(launched(launch_readout(p, dt, path, ReadoutArgs{q, g, o, wsf, eps}, s), "readout"));
+  return GLA_OK;
+}
+
+}  // namespace
+
+bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
+  Plan p;
+  p.BH = BH;
+  p.F = F;
+  p.T = T;
+  p.d = d;
+  if (BH < 0 || F < 0 || T < 0) return false;
+  const int64_t units = BH * F;
+  if (units > 0 && T > 0) {
+    int64_t P = 1, R = 1;
+    if (units < kTargetWorkgroups) {
+      P = std::min(ceil_div(kTargetWorkgroups, units), std::max<int64_t>(1, ceil_div(T, kMinPartTokens)));
+      R = std::min(ceil_div(kTargetWorkgroups, units), std::max<int64_t>(1, ceil_div(T, kMinSplitTokens)));
+    }
+    p.part_len = round_up(ceil_div(T, P), kTokenAlign);
+    p.P = (int)ceil_div(T, p.part_len);
+    p.read_len = round_up(ceil_div(T, R), kTokenAlign);
+    p.R = (int)ceil_div(T, p.read_len);
+  } else {
+    p.P = p.R = 1;
+    p.part_len = p.read_len = round_up(T, kTokenAlign);
+  }
+  // indexing limits: 1-D grids of 256-thread workgroups, 64-bit element offsets
+  const int64_t max_grid = (int64_t(1) << 31) / 256;
+  if (units > 0 && (units * std::max(p.P, p.R) >= max_grid)) return false;
+  if (T > 0 && units > (int64_t(1) << 62) / T / std::max(d, 1)) return false;
+  const int64_t E = p.state_elems();
+  if (BH * ceil_div(E, 256) >= max_grid) return false;
+  p.ws_bytes = (size_t)round_up(units * p.P * E * 4, 256);
+  *plan = p;
+  return true;
+}
+
+Path select_path(int dtype, int d) {
+  const int ov = path_override();
+  const bool mfma_ok = dtype == GLA_BF16 && mfma_supports(d);
+  if (ov == 0) return Path::kValu;
+  return mfma_ok ? Path::kMfma : Path::kValu;
+}
+
+hipError_t launch_kv(const Plan &p, int dtype, Path path, const KvArgs &a, hipStream_t s) {
+  if (path == Path::kMfma) return launch_kv_mfma(p, a, s);
+  return launch_kv_valu(p, dtype, a, s);
+}
+
+hipError_t launch_readout(const Plan &p, int dtype, Path path, const ReadoutArgs &a,
+                          hipStream_t s) {
+  if (path == Path::kMfma) return launch_readout_mfma(p, a, s);
+  return launch_readout_valu(p, dtype, a, s);
+}
+
+}  // namespace gla
+
+using namespace gla;
+
+GLA_EXPORT size_t gla_fwd_bidir_workspace(int B, int H, int64_t N, int d) {
+  Plan p;
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return 0;
+  if (!make_plan((int64_t)B * H, N > 0 ? 1 : 0, N, d, &p)) return 0;
+  return p.ws_bytes;
+}
+
+GLA_EXPORT size_t gla_fwd_framecausal_workspace(int B, int H, int F, int T, int d) {
+  Plan p;
+  if (B < 0 || H < 0 || F < 0 || T < 0 || d <= 0) return 0;
+  if (!make_plan((int64_t)B * H, F, T, d, &p)) return 0;
+  return p.ws_bytes;
+}
+
+GLA_EXPORT size_t gla_state_carry_workspace(int B, int H, int F, int T, int d) {
+  return gla_fwd_framecausal_workspace(B, H, F, T, d);
+}
+
+GLA_EXPORT gla_status gla_fwd_bidir(const void *q, const void *k, const void *v, const void *g,
+                                    void *o, int B, int H, int64_t N, int d, gla_dtype dt,
+                                    float eps, void *ws, size_t ws_bytes, void *stream) {
+  if (N < 0) return fail(GLA_ERR_SHAPE, "N=%lld must be >= 0", (long long)N);
+  // One frame holding the whole sequence, no decay and no carried state.
+  const int F = N > 0 ? 1 : 0;
+  GLA_TRY(check_dims(B, H, d, dt));
+  GLA_TRY(check_eps(eps));
+  const int64_t BH = (int64_t)B * H;
+  if (BH == 0 || N == 0) return GLA_OK;
+  if (!q || !k || !v || !g || !o) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
+  GLA_TRY(check_tensor_align(q, "q"));
+  GLA_TRY(check_tensor_align(k, "k"));
+  GLA_TRY(check_tensor_align(v, "v"));
+  GLA_TRY(check_tensor_align(g, "g"));
+  GLA_TRY(check_tensor_align(o, "o"));
+  Plan p;
+  if (!make_plan(BH, F, N, d, &p)) return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
+  GLA_TRY(check_ws(p, ws, ws_bytes));
+  const size_t tb = (size_t)(BH * N * d) * (dt == GLA_F32 ? 4 : 2);
+  const Range all[] = {{q, tb, "q"}, {k, tb, "k"}, {v, tb, "v"}, {g, tb, "g"},
+                       {o, tb, "o"}, {ws, p.ws_bytes, "workspace"}};
+  const Range outs[] = {all[4], all[5]};
+  GLA_TRY(check_no_overlap(outs, 2, all, 6));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Path path = select_path(dt, d);
+  float *wsf = static_cast<float *>(ws);
+  GLA_TRY(launched(launch_kv(p, dt, path, KvArgs{k, v, wsf}, s), "kv"));
+  GLA_TRY(launched(launch_scan(p, ScanArgs{wsf, nullptr, nullptr, nullptr, nullptr, nullptr, 1}, s),
+                   "scan"));
+  GLA_TRY(launched(launch_readout(p, dt, path, ReadoutArgs{q, g, o, wsf, eps}, s), "readout"));
+  return GLA_OK;
+}
+
+GLA_EXPORT gla_status gla_fwd_framecausal(const void *q, const void *k, const void *v,
+                                          const void *g, const float *gamma, const float *S_in,
+                                          const float *z_in, void *o, float *S_out, float *z_out,
+                                          int B, int H, int F, int T, int d, gla_dtype dt,
+                                          float eps, void *ws, size_t ws_bytes, void *stream) {
+  return run_framecausal(q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d, dt, eps,
+                         ws, ws_bytes, stream, true);
+}
+
+GLA_EXPORT gla_status gla_state_carry(const void *k, const void *v, const float *gamma,
+                                      const float *S_in, const float *z_in, float *S_out,
+                                      float *z_out, int B, int H, int F, int T, int d,
+                                      gla_dtype dt, void *ws, size_t ws_bytes, void *stream) {
+  return run_framecausal(nullptr, k, v, nullptr, gamma, S_in, z_in, nullptr, S_out, z_out, B, H,
+                         F, T, d, dt, 0.f, ws, ws_bytes, stream, false);
+}
+
+GLA_EXPORT const char *gla_status_string(gla_status s) {
+  switch (s) {
+    case GLA_OK: return "ok";
+    case GLA_ERR_NULL: return "required pointer is NULL";
+    case GLA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case GLA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case GLA_ERR_ALIGN: return "misaligned pointer";
+    case GLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GLA_ERR_VALUE: return "invalid scalar argument";
+    case GLA_ERR_HIP: return "HIP runtime error";
+    case GLA_ERR_ALIAS: return "output overlaps another argument";
+  }
+  return "unknown status";
+}
+
+GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
+
+GLA_EXPORT int gla_version(void) { return 10000; }

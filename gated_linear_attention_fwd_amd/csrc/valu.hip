@@ -1,0 +1,203 @@
+// valu.hip -- fp32 vector-ALU kernels for the KV sums and the readout.
+//
+// These serve the float32 dtype and any (dtype, d) pair without a matrix-core
+// kernel, and act as an independent cross-check of the MFMA kernels (no
+// transposed LDS tiles, no operand packing). Same contract as the MFMA path:
+//   kv:      U = sum_{t in part} phi(k_t) v_t^T, u = sum phi(k_t)
+//   readout: o_t = sigmoid(g_t) * (phi(q_t)^T S_f) / (phi(q_t)^T z_f + eps)
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace gla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKvTile = 32;  // tokens staged in LDS per step
+
+// One workgroup per (slab, frame, part). Thread layout: key feature i = tid % D,
+// value columns j = tid / D + (256 / D) * c for c < D*D/256. Each token adds
+// phi(k[i]) * v[j] to the thread's entries; u[i] is kept by threads with
+// tid < D.
+template <typename TIn, int D>
+__global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict__ k,
+                                                           const TIn *__restrict__ v,
+                                                           float *__restrict__ ws, int F,
+                                                           int64_t T, int P, int64_t part_len) {
+  static_assert(D * D >= kThreads && (D * D) % kThreads == 0, "D must be 16..128");
+  constexpr int EPT = D * D / kThreads;
+  constexpr int JS = kThreads / D;
+  __shared__ float sk[kKvTile][D];
+  __shared__ float sv[kKvTile][D];
+
+  const int tid = threadIdx.x;
+  const int64_t wg = blockIdx.x;
+  const int p = (int)(wg % P);
+  const int f = (int)((wg / P) % F);
+  const int64_t bh = wg / ((int64_t)P * F);
+  const int64_t N = (int64_t)F * T;
+  const int64_t t0 = min((int64_t)p * part_len, T);
+  const int64_t t1 = min(t0 + part_len, T);
+  const TIn *kb = k + (bh * N + (int64_t)f * T) * D;
+  const TIn *vb = v + (bh * N + (int64_t)f * T) * D;
+
+  const int i = tid % D;
+  const int jc = tid / D;
+  float acc[EPT];
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) acc[c] = 0.f;
+  float uacc = 0.f;
+
+  for (int64_t c0 = t0; c0 < t1; c0 += kKvTile) {
+    const int n = (int)min((int64_t)kKvTile, t1 - c0);
+    __syncthreads();
+    for (int e = tid; e < kKvTile * D; e += kThreads) {
+      const int tt = e / D, ii = e % D;
+      float kk = 0.f, vv = 0.f;
+      if (tt < n) {
+        kk = relu(Elem<TIn>::load(kb, (c0 + tt) * D + ii));
+        vv = Elem<TIn>::load(vb, (c0 + tt) * D + ii);
+      }
+      sk[tt][ii] = kk;
+      sv[tt][ii] = vv;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < n; ++tt) {
+      const float kk = sk[tt][i];
+      uacc += kk;
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) acc[c] = fmaf(kk, sv[tt][jc + JS * c], acc[c]);
+    }
+  }
+
+  float *out = ws + wg * ((int64_t)D * D + D);
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) out[i * D + jc + JS * c] = acc[c];
+  if (jc == 0) out[D * D + i] = uacc;
+}
+
+// One workgroup per (slab, frame, split). Thread layout: 4 value columns
+// j = 4 * (tid % (D/4)) .. +3 of token tid / (D/4) of the current tile. phi(q)
+// of the tile is staged in LDS; S_f comes from LDS (D <= 64) or global memory.
+template <typename TIn, int D>
+__global__ __launch_bounds__(kThreads) void readout_valu_kernel(
+    const TIn *__restrict__ q, const TIn *__restrict__ g, TIn *__restrict__ o,
+    const float *__restrict__ ws, int F, int64_t T, int P, int R, int64_t read_len, float eps) {
+  constexpr int CG = D / 4;             // column groups
+  constexpr int TT = kThreads / CG;     // tokens per tile
+  constexpr bool kSInLds = (D <= 64);
+  __shared__ float sS[kSInLds ? D * D : 1];
+  __shared__ float sz[D];
+  __shared__ float sq[TT][D];
+
+  const int tid = threadIdx.x;
+  const int64_t wg = blockIdx.x;
+  const int r = (int)(wg % R);
+  const int f = (int)((wg / R) % F);
+  const int64_t bh = wg / ((int64_t)R * F);
+  const int64_t N = (int64_t)F * T;
+  const int64_t t0 = min((int64_t)r * read_len, T);
+  const int64_t t1 = min(t0 + read_len, T);
+  if (t0 >= t1) return;
+
+  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * ((int64_t)D * D + D);
+  if (kSInLds)
+    for (int e = tid; e < D * D; e += kThreads) sS[e] = Sg[e];
+  for (int e = tid; e < D; e += kThreads) sz[e] = Sg[D * D + e];
+  const float *Sp = kSInLds ? sS : Sg;
+
+  const int64_t row0 = bh * N + (int64_t)f * T;
+  const int cg = tid % CG;
+  const int tl = tid / CG;
+
+  for (int64_t c0 = t0; c0 < t1; c0 += TT) {
+    const int n = (int)min((int64_t)TT, t1 - c0);
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kThreads) {
+      const int tt = e / D, ii = e % D;
+      sq[tt][ii] = (tt < n) ? relu(Elem<TIn>::load(q, (row0 + c0 + tt) * D + ii)) : 0.f;
+    }
+    __syncthreads();
+    if (tl < n) {
+      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+      float den = 0.f;
+      for (int ii = 0; ii < D; ++ii) {
+        const float qi = sq[tl][ii];
+        den = fmaf(qi, sz[ii], den);
+        const float4 s4 = *reinterpret_cast<const float4 *>(Sp + ii * D + 4 * cg);
+        num.x = fmaf(qi, s4.x, num.x);
+        num.y = fmaf(qi, s4.y, num.y);
+        num.z = fmaf(qi, s4.z, num.z);
+        num.w = fmaf(qi, s4.w, num.w);
+      }
+      const float inv = 1.f / (den + eps);
+      const int64_t off = (row0 + c0 + tl) * D + 4 * cg;
+      const float4 gg = Elem<TIn>::load4(g, off);
+      float4 out;
+      out.x = sigmoid(gg.x) * (num.x * inv);
+      out.y = sigmoid(gg.y) * (num.y * inv);
+      out.z = sigmoid(gg.z) * (num.z * inv);
+      out.w = sigmoid(gg.w) * (num.w * inv);
+      Elem<TIn>::store4(o, off, out);
+    }
+  }
+}
+
+template <typename TIn>
+hipError_t kv_valu_dispatch(const Plan &p, const KvArgs &a, hipStream_t s) {
+  const int64_t grid = p.BH * p.F * p.P;
+  const TIn *k = static_cast<const TIn *>(a.k);
+  const TIn *v = static_cast<const TIn *>(a.v);
+#define GLA_KV_CASE(DD)                                                                   \
+  case DD:                                                                                \
+    hipLaunchKernelGGL((kv_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), 0, \
+                       s, k, v, a.ws, p.F, p.T, p.P, p.part_len);                         \
+    break;
+  switch (p.d) {
+    GLA_KV_CASE(16)
+    GLA_KV_CASE(32)
+    GLA_KV_CASE(64)
+    GLA_KV_CASE(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef GLA_KV_CASE
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t readout_valu_dispatch(const Plan &p, const ReadoutArgs &a, hipStream_t s) {
+  const int64_t grid = p.BH * p.F * p.R;
+  const TIn *q = static_cast<const TIn *>(a.q);
+  const TIn *g = static_cast<const TIn *>(a.g);
+  TIn *o = static_cast<TIn *>(a.o);
+#define GLA_RO_CASE(DD)                                                                     \
+  case DD:                                                                                  \
+    hipLaunchKernelGGL((readout_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), \
+                       0, s, q, g, o, a.ws, p.F, p.T, p.P, p.R, p.read_len, a.eps);         \
+    break;
+  switch (p.d) {
+    GLA_RO_CASE(16)
+    GLA_RO_CASE(32)
+    GLA_RO_CASE(64)
+    GLA_RO_CASE(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef GLA_RO_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kv_valu(const Plan &p, int dtype, const KvArgs &a, hipStream_t s) {
+  if (p.BH * p.F * p.P == 0) return hipSuccess;
+  return dtype == 0 ? kv_valu_dispatch<float>(p, a, s) : kv_valu_dispatch<bf16_t>(p, a, s);
+}
+
+hipError_t launch_readout_valu(const Plan &p, int dtype, const ReadoutArgs &a, hipStream_t s) {
+  if (p.BH * p.F * p.R == 0 || p.T == 0) return hipSuccess;
+  return dtype == 0 ? readout_valu_dispatch<float>(p, a, s)
+                    : readout_valu_dispatch<bf16_t>(p, a, s);
+}
+
+}  // namespace gla

@@ -161,3 +161,40 @@ def stream_block_inputs(w: Workload, block: int, gamma_all: Optional[np.ndarray]
         gamma_all = stream_gamma(w)
     gamma = np.ascontiguousarray(gamma_all[:, :, f0:f0 + nf])
     return dict(q=q, k=k, v=v, g=g, gamma=gamma)
+
+
+def device_inputs(w: Workload, device, block: Optional[int] = None):
+    """Inputs drawn on the GPU (torch's Philox generator), for the two workloads
+    whose host draw would take minutes: q, k, v, g as torch tensors on
+    ``device`` in the workload dtype, gamma as float32 [B, H, F_block].
+
+    Seed: ``seed * 1000`` for a one-shot call, ``seed * 1000 + block + 1`` for
+    a streamed block; the draw order is q, k, v, g; gamma is the host draw of
+    :func:`stream_gamma` (sliced to the block). Same distributions as the host
+    recipe, different random numbers."""
+    import torch
+
+    if block is None:
+        f0, nf = 0, w.F
+        tag = 0
+    else:
+        f0, nf = stream_block_bounds(w)[block]
+        tag = block + 1
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed * 1000 + tag)
+    shape = (w.B, w.H, nf * w.T, w.d)
+    s = 1.0 / float(np.sqrt(w.d)) if w.scale_qkv else 1.0
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+    def draw(scale):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        return x if tdt == torch.float32 else x.to(tdt)
+
+    q = draw(s)
+    k = draw(s)
+    v = draw(s)
+    g = draw(1.0)
+    gamma = torch.from_numpy(np.ascontiguousarray(stream_gamma(w)[:, :, f0:f0 + nf])).to(device)
+    return dict(q=q, k=k, v=v, g=g, gamma=gamma)

@@ -1,0 +1,117 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) gated linear-attention forward library.
+ *
+ * The operation is the gated linear-attention token mixer that carries the
+ * O(N) part of the hybrid video DiT described in "SANA-Video 2.0: Hybrid
+ * Linear Attention with Attention Residuals for Efficient Video Generation"
+ * (project page, section "Hybrid Linear-Softmax Attention"). For each batch b
+ * and head h, over tokens t = 0..N-1 with head dimension d:
+ *
+ *   phi(x) = max(x, 0),  sigma(x) = 1 / (1 + exp(-x))
+ *   state    S in R^{d x d} (S[i][j]: i = key feature, j = value feature)
+ *   normaliser z in R^d
+ *   o_t = sigma(g_t) (.) (phi(q_t)^T S) / (phi(q_t)^T z + eps)
+ *
+ * Two modes:
+ *  - bidirectional: one state over the whole sequence,
+ *      S = sum_t phi(k_t) v_t^T, z = sum_t phi(k_t);
+ *  - frame-causal (block-causal over video frames of T tokens each, F frames):
+ *      S_f = gamma_f S_{f-1} + sum_{t in frame f} phi(k_t) v_t^T,
+ *      z_f = gamma_f z_{f-1} + sum_{t in frame f} phi(k_t),
+ *      S_{-1} = S_in (or 0), and every token of frame f reads S_f, z_f.
+ *    The fixed D x D state and its additive per-block update are the block KV
+ *    cache of "SANA-Video: Efficient Video Generation with Block Linear
+ *    Diffusion Transformer" (ICLR 2026 oral, block KV cache passage); the
+ *    per-frame decay gamma_f follows the frame-wise decay gates of the
+ *    "SANA-WM" analysis page (method components).
+ *
+ * Conventions for every entry point:
+ *  - Layout: q, k, v, g, o are [B][H][N][d] row-major (each (b, h) slab is a
+ *    contiguous N x d matrix; N = F * T in frame-causal mode). gamma is
+ *    [B][H][F] float32; S_* are [B][H][d][d] float32; z_* are [B][H][d] float32.
+ *  - dtype: GLA_F32 (float32 inputs and output) or GLA_BF16 (bfloat16 inputs
+ *    and output, float32 accumulation; the output is rounded to nearest even).
+ *  - Supported head dimensions: d in {16, 32, 64, 128}.
+ *  - Pointers are device memory of the current HIP device, owned by the
+ *    caller. The library never allocates, frees or synchronises; all work is
+ *    enqueued asynchronously on `stream` (a hipStream_t; NULL is the default
+ *    stream). Tensor pointers must be 16-byte aligned, gamma 4-byte aligned,
+ *    the workspace 256-byte aligned.
+ *  - Aliasing: S_out may equal S_in and z_out may equal z_in (in-place
+ *    update). No other overlap is allowed (checked: GLA_ERR_ALIAS).
+ *  - Errors: every argument is validated on the host before anything is
+ *    enqueued; on any status other than GLA_OK nothing was launched. A failed
+ *    launch returns GLA_ERR_HIP. Faults during execution surface at the
+ *    caller's next synchronisation. gla_last_error() gives a thread-local
+ *    message for the last non-OK status. No C++ exception crosses the ABI.
+ *  - Determinism: results are bitwise identical from run to run for the same
+ *    inputs and shapes (fixed reduction order, no floating-point atomics).
+ *  - Empty inputs: B, H, N, F or T may be 0; the call then only produces the
+ *    state outputs implied by the definition (e.g. F = 0 gives S_out = S_in).
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gla_status {
+  GLA_OK = 0,
+  GLA_ERR_NULL = 1,        /* a required pointer is NULL, or only one of a pair is given */
+  GLA_ERR_SHAPE = 2,       /* negative or inconsistent sizes, or sizes that overflow */
+  GLA_ERR_UNSUPPORTED = 3, /* head dimension or dtype not supported */
+  GLA_ERR_ALIGN = 4,       /* pointer misaligned */
+  GLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the *_workspace query */
+  GLA_ERR_VALUE = 6,       /* eps negative or not finite */
+  GLA_ERR_HIP = 7,         /* the HIP runtime reported an error at launch */
+  GLA_ERR_ALIAS = 8        /* an output overlaps an input or the workspace */
+} gla_status;
+
+typedef enum gla_dtype { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+/* Workspace bytes needed by the matching call for these sizes (0 if none).
+ * Returns 0 for invalid sizes as well; the call itself reports those. */
+size_t gla_fwd_bidir_workspace(int B, int H, int64_t N, int d);
+size_t gla_fwd_framecausal_workspace(int B, int H, int F, int T, int d);
+size_t gla_state_carry_workspace(int B, int H, int F, int T, int d);
+
+/* Bidirectional (whole-sequence, non-causal) gated linear attention.
+ * Reads q, k, v, g [B][H][N][d]; writes o [B][H][N][d]. */
+gla_status gla_fwd_bidir(const void *q, const void *k, const void *v, const void *g, void *o,
+                         int B, int H, int64_t N, int d, gla_dtype dt, float eps, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* Frame-causal gated linear attention with per-frame decay gamma [B][H][F].
+ * S_in/z_in: carried-in state (both NULL: zero state). S_out/z_out: state after
+ * the last frame (both NULL: not written). o [B][H][F*T][d]. */
+gla_status gla_fwd_framecausal(const void *q, const void *k, const void *v, const void *g,
+                               const float *gamma, const float *S_in, const float *z_in,
+                               void *o, float *S_out, float *z_out, int B, int H, int F, int T,
+                               int d, gla_dtype dt, float eps, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/* Block-cache commit: the state after F more frames, from k, v and gamma only
+ * (no queries, no output). Equals the S_out/z_out of gla_fwd_framecausal on the
+ * same inputs. S_out and z_out are required. */
+gla_status gla_state_carry(const void *k, const void *v, const float *gamma, const float *S_in,
+                           const float *z_in, float *S_out, float *z_out, int B, int H, int F,
+                           int T, int d, gla_dtype dt, void *ws, size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *gla_status_string(gla_status s);
+
+/* Thread-local detail for the last non-OK status returned on this thread. */
+const char *gla_last_error(void);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int gla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

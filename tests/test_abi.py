@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/gla.h
+declares, sizes its workspace as documented and rejects bad arguments on the
+host before anything is launched (every call below fails validation or has no
+work, so no HIP call is made)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_attention_fwd_amd as gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, VALUE, HIP, ALIAS = range(9)
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gla.library_path()):
+        from gated_linear_attention_fwd_amd import build
+        build.build_library()
+    return gla.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(gla_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("gla_fwd_bidir", "gla_fwd_framecausal", "gla_state_carry",
+              "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace",
+              "gla_state_carry_workspace", "gla_status_string", "gla_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.gla_status_string(s).decode()
+    assert lib.gla_status_string(99).decode() == "unknown status"
+    assert lib.gla_version() == 10000
+
+
+def test_workspace_sizes(lib):
+    # 720p/60s: one part per frame, (d*d + d) floats per (slab, frame)
+    assert gla.gla_fwd_framecausal_workspace(1, 32, 241, 920, 64) == 32 * 241 * 4160 * 4
+    assert gla.gla_state_carry_workspace(1, 32, 241, 920, 64) == 32 * 241 * 4160 * 4
+    # small problems are cut into parts to fill the GPU: the size grows accordingly
+    small = gla.gla_fwd_framecausal_workspace(1, 8, 5, 256, 64)
+    assert small > 8 * 5 * 4160 * 4 and small % 256 == 0
+    assert gla.gla_fwd_bidir_workspace(1, 32, 19320, 64) % (4160 * 4) == 0
+    assert gla.gla_fwd_bidir_workspace(1, 32, 19320, 64) > 32 * 4160 * 4
+    # empty and invalid sizes need nothing
+    assert gla.gla_fwd_framecausal_workspace(0, 32, 241, 920, 64) == 0
+    assert gla.gla_fwd_bidir_workspace(1, 1, 0, 64) == 0
+    assert gla.gla_fwd_framecausal_workspace(1, 1, -1, 4, 64) == 0
+
+
+FAKE = 0x10000  # an aligned non-NULL address; never dereferenced on these paths
+
+
+def p(x):
+    return ctypes.c_void_p(x) if x else None
+
+
+def bidir(lib, q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, g=FAKE + 0x3000000,
+          o=FAKE + 0x4000000, B=1, H=1, N=64, d=64, dt=BF16, eps=1e-6, ws=FAKE + 0x8000000,
+          wsb=1 << 30):
+    return lib.gla_fwd_bidir(p(q), p(k), p(v), p(g), p(o), B, H, N, d, dt, eps, p(ws), wsb, None)
+
+
+def framecausal(lib, q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, g=FAKE + 0x3000000,
+                gamma=FAKE + 0x5000000, S_in=None, z_in=None, o=FAKE + 0x4000000, S_out=None,
+                z_out=None, B=1, H=1, F=2, T=32, d=64, dt=BF16, eps=1e-6, ws=FAKE + 0x8000000,
+                wsb=1 << 30):
+    return lib.gla_fwd_framecausal(p(q), p(k), p(v), p(g), p(gamma), p(S_in), p(z_in), p(o),
+                                   p(S_out), p(z_out), B, H, F, T, d, dt, eps, p(ws), wsb, None)
+
+
+def carry(lib, k=FAKE, v=FAKE + 0x1000000, gamma=FAKE + 0x5000000, S_in=None, z_in=None,
+          S_out=FAKE + 0x6000000, z_out=FAKE + 0x7000000, B=1, H=1, F=2, T=32, d=64, dt=BF16,
+          ws=FAKE + 0x8000000, wsb=1 << 30):
+    return lib.gla_state_carry(p(k), p(v), p(gamma), p(S_in), p(z_in), p(S_out), p(z_out), B, H,
+                               F, T, d, dt, p(ws), wsb, None)
+
+
+def test_bidir_validation(lib):
+    assert bidir(lib, d=48) == UNSUP
+    assert bidir(lib, d=256) == UNSUP
+    assert bidir(lib, dt=7) == UNSUP
+    assert bidir(lib, B=-1) == SHAPE
+    assert bidir(lib, N=-5) == SHAPE
+    assert bidir(lib, eps=-1.0) == VALUE
+    assert bidir(lib, eps=float("nan")) == VALUE
+    assert bidir(lib, eps=float("inf")) == VALUE
+    assert bidir(lib, q=0) == NULL
+    assert bidir(lib, o=0) == NULL
+    assert bidir(lib, k=FAKE + 0x1000008) == ALIGN
+    assert bidir(lib, ws=0) == WS
+    assert bidir(lib, wsb=16) == WS
+    assert bidir(lib, ws=FAKE + 0x8000010) == ALIGN
+    assert bidir(lib, o=FAKE + 0x100) == ALIAS  # o overlaps q
+    assert bidir(lib, ws=FAKE + 0x4000000) == ALIAS  # workspace overlaps o
+    assert "overlaps" in lib.gla_last_error().decode()
+    # empty problems are valid and launch nothing
+    assert bidir(lib, N=0) == OK
+    assert bidir(lib, B=0) == OK
+    assert bidir(lib, H=0, q=0, k=0, v=0, g=0, o=0) == OK
+
+
+def test_framecausal_validation(lib):
+    assert framecausal(lib, d=8) == UNSUP
+    assert framecausal(lib, F=-1) == SHAPE
+    assert framecausal(lib, T=-1) == SHAPE
+    assert framecausal(lib, gamma=0) == NULL
+    assert framecausal(lib, S_in=FAKE + 0x6000000) == NULL  # S_in without z_in
+    assert framecausal(lib, z_out=FAKE + 0x7000000) == NULL  # z_out without S_out
+    assert framecausal(lib, g=0) == NULL
+    assert framecausal(lib, gamma=FAKE + 0x5000002) == ALIGN
+    assert framecausal(lib, S_out=FAKE + 0x6000004, z_out=FAKE + 0x7000000) == ALIGN
+    assert framecausal(lib, eps=-1e-3) == VALUE
+    assert framecausal(lib, wsb=0) == WS
+    assert framecausal(lib, S_out=FAKE, z_out=FAKE + 0x7000000) == ALIAS  # S_out overlaps q
+    assert framecausal(lib, S_in=FAKE + 0x6000000, z_in=FAKE + 0x6000000 + 64,
+                       S_out=FAKE + 0x6000000 + 1024, z_out=FAKE + 0x7000000) == ALIAS
+    assert framecausal(lib, B=0) == OK
+    assert "gamma" in (framecausal(lib, gamma=0) and lib.gla_last_error().decode())
+
+
+def test_state_carry_validation(lib):
+    assert carry(lib, S_out=0, z_out=0) == NULL
+    assert carry(lib, d=100) == UNSUP
+    assert carry(lib, k=0) == NULL
+    assert carry(lib, wsb=8) == WS
+    assert carry(lib, S_out=FAKE, z_out=FAKE + 0x7000000) == ALIAS
+    assert carry(lib, H=0) == OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 32, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        gla.gla_fwd_bidir(x, x, x, x)
+    with pytest.raises(TypeError):
+        gla.gla_fwd_bidir(x.double(), x.double(), x.double(), x.double())

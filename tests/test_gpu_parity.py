@@ -1,0 +1,327 @@
+"""GPU parity: libgla (through its C ABI) against the fp64 oracle.
+
+Bar: the slab-normalised error (gla_testutil.slab_rel_err) of o is at most
+1e-4 for float32 inputs and 2e-2 for bfloat16 inputs with float32
+accumulation; carried states (fp32 in both cases) are compared by
+max|dS| / max|S| <= 1e-4.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gated_linear_attention_fwd_amd as gla
+import oracle
+from gated_linear_attention_fwd_amd import synth
+from gla_testutil import TOL, max_abs_over_max, slab_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+STATE_TOL = 1e-4
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gla.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(params=["auto", "valu"])
+def path(request, monkeypatch):
+    """Run with the default kernel choice and with the vector-ALU kernels forced."""
+    if request.param == "valu":
+        monkeypatch.setenv("GLA_PATH", "valu")
+    else:
+        monkeypatch.delenv("GLA_PATH", raising=False)
+    return request.param
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    h = host(t)
+    return oracle.bf16_to_f64(h) if h.dtype == np.uint16 else h.astype(np.float64)
+
+
+def state_err(a, ref) -> float:
+    return max_abs_over_max(a.detach().cpu().numpy() if isinstance(a, torch.Tensor) else a, ref)
+
+
+def report(name, **errs):
+    print(name, " ".join("%s=%.3e" % kv for kv in errs.items()), flush=True)
+
+
+def check_framecausal(x, dtype, eps=1e-6, S_in=None, z_in=None, name=""):
+    q, k, v, g = (dev(x[n]) for n in "qkvg")
+    gamma = dev(x["gamma"])
+    Si = None if S_in is None else dev(S_in.astype(np.float32))
+    zi = None if z_in is None else dev(z_in.astype(np.float32))
+    o, S, z = gla.gla_fwd_framecausal(q, k, v, g, gamma, Si, zi, eps=eps, return_state=True)
+    ro, rS, rz = oracle.recurrent(oracle.FRAMECAUSAL, x["q"], x["k"], x["v"], x["g"],
+                                  x["gamma"], S_in=None if Si is None else host(Si),
+                                  z_in=None if zi is None else host(zi), eps=eps)
+    e_o, e_S, e_z = slab_rel_err(f64(o), ro), state_err(S, rS), state_err(z, rz)
+    report(name or "framecausal", o=e_o, S=e_S, z=e_z)
+    assert e_o <= TOL[dtype]
+    assert e_S <= STATE_TOL and e_z <= STATE_TOL
+    return o, S, z
+
+
+def check_bidir(x, dtype, eps=1e-6, name=""):
+    q, k, v, g = (dev(x[n]) for n in "qkvg")
+    o = gla.gla_fwd_bidir(q, k, v, g, eps=eps)
+    ro, _, _ = oracle.recurrent(oracle.BIDIR, x["q"], x["k"], x["v"], x["g"], eps=eps)
+    e = slab_rel_err(f64(o), ro)
+    report(name or "bidir", o=e)
+    assert e <= TOL[dtype]
+    return o
+
+
+# ------------------------------------------------------------------ workloads
+
+def test_tiny_workload_both_modes(path):
+    """B=1, H=2, d=16, 4 frames x 16 tokens, float32, both modes."""
+    w = synth.WORKLOADS[1]
+    x = synth.workload_inputs(w)
+    check_bidir(x, w.dtype, w.eps, name="tiny bidir " + path)
+    check_framecausal(x, w.dtype, w.eps, name="tiny framecausal " + path)
+
+
+def test_small_workload(path):
+    """B=1, H=8, d=64, 5 frames x 256 tokens, bf16, frame-causal."""
+    w = synth.WORKLOADS[2]
+    x = synth.workload_inputs(w)
+    check_framecausal(x, w.dtype, w.eps, name="small framecausal " + path)
+
+
+@pytest.mark.parametrize("mode", ["bidir", "framecausal"])
+def test_720p_5s_workload(mode):
+    """B=1, H=32, d=64, 21 frames x 920 tokens, bf16; every head against the oracle."""
+    w = synth.WORKLOADS[3]
+    x = synth.workload_inputs(w)
+    if mode == "bidir":
+        check_bidir(x, w.dtype, w.eps, name="720p/5s bidir")
+    else:
+        check_framecausal(x, w.dtype, w.eps, name="720p/5s framecausal")
+
+
+def _sampled_heads(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0), (B - 1, H - 1)}
+    while len(picks) < n:
+        picks.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(picks)
+
+
+def test_720p_60s_workload_sampled_heads():
+    """The 720p/60s shape (B=1, H=32, d=64, 241 frames x 920 tokens, bf16) in one
+    call, as timed by the benchmark; three whole heads are recomputed by the
+    oracle (heads are independent, so the oracle sees exactly their inputs)."""
+    w = synth.WORKLOADS[4]
+    x = synth.device_inputs(w, DEV)
+    o, S, z = gla.gla_fwd_framecausal(x["q"], x["k"], x["v"], x["g"], x["gamma"], eps=w.eps,
+                                      return_state=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    for b, h in _sampled_heads(w.B, w.H, 3, 4):
+        hx = {n: host(x[n][b:b + 1, h:h + 1]) for n in "qkvg"}
+        hg = host(x["gamma"][b:b + 1, h:h + 1])
+        ro, rS, rz = oracle.recurrent(oracle.FRAMECAUSAL, hx["q"], hx["k"], hx["v"], hx["g"], hg,
+                                      eps=w.eps)
+        e_o = slab_rel_err(f64(o[b:b + 1, h:h + 1]), ro)
+        e_S, e_z = state_err(S[b:b + 1, h:h + 1], rS), state_err(z[b:b + 1, h:h + 1], rz)
+        report("720p/60s head (%d,%d)" % (b, h), o=e_o, S=e_S, z=e_z)
+        assert e_o <= TOL[w.dtype] and e_S <= STATE_TOL and e_z <= STATE_TOL
+
+
+def test_streaming_blocks_sampled_heads():
+    """Block-causal streaming: the 720p/60s video as 8 blocks of 30/31 frames,
+    B=2, H=40, d=128, bf16, the fp32 state carried in place between calls. Two
+    whole heads are recomputed by the oracle over all 241 frames in one shot
+    (block split == one shot is a property of the method)."""
+    w = synth.WORKLOADS[5]
+    heads = _sampled_heads(w.B, w.H, 2, 5)
+    S = torch.zeros((w.B, w.H, w.d, w.d), dtype=torch.float32, device=DEV)
+    z = torch.zeros((w.B, w.H, w.d), dtype=torch.float32, device=DEV)
+    got = {bh: [] for bh in heads}
+    ins = {bh: {n: [] for n in "qkvg"} for bh in heads}
+    for blk in range(len(w.blocks)):
+        x = synth.device_inputs(w, DEV, block=blk)
+        o, _, _ = gla.gla_fwd_framecausal(x["q"], x["k"], x["v"], x["g"], x["gamma"], S, z,
+                                          eps=w.eps, S_out=S, z_out=z)
+        for (b, h) in heads:
+            got[(b, h)].append(f64(o[b:b + 1, h:h + 1]))
+            for n in "qkvg":
+                ins[(b, h)][n].append(host(x[n][b:b + 1, h:h + 1]))
+        del x, o
+    torch.cuda.synchronize()
+    gamma_all = synth.stream_gamma(w)
+    for (b, h) in heads:
+        hx = {n: np.concatenate(ins[(b, h)][n], axis=2) for n in "qkvg"}
+        ro, rS, rz = oracle.recurrent(oracle.FRAMECAUSAL, hx["q"], hx["k"], hx["v"], hx["g"],
+                                      gamma_all[b:b + 1, h:h + 1], eps=w.eps)
+        e_o = slab_rel_err(np.concatenate(got[(b, h)], axis=2), ro)
+        e_S, e_z = state_err(S[b:b + 1, h:h + 1], rS), state_err(z[b:b + 1, h:h + 1], rz)
+        report("streaming head (%d,%d)" % (b, h), o=e_o, S=e_S, z=e_z)
+        assert e_o <= TOL[w.dtype] and e_S <= STATE_TOL and e_z <= STATE_TOL
+
+
+# ------------------------------------------------------------------ shapes and edge cases
+
+SHAPES = [
+    # B, H, F, T, d, dtype
+    (1, 1, 1, 1, 16, "f32"),
+    (1, 2, 3, 37, 32, "bf16"),
+    (2, 1, 2, 100, 64, "bf16"),
+    (1, 1, 3, 129, 128, "bf16"),
+    (1, 3, 2, 33, 16, "bf16"),
+    (1, 1, 2, 920, 64, "bf16"),
+    (2, 2, 4, 61, 128, "f32"),
+    (1, 2, 3, 45, 64, "f32"),
+    (1, 1, 2, 300, 32, "f32"),
+    (1, 1, 1, 1000, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dH%dF%dT%dd%d%s" % s)
+def test_shapes_framecausal_with_carry(shape, path):
+    B, H, F, T, d, dt = shape
+    x = synth.random_inputs(B, H, F, T, d, dt, seed=SHAPES.index(shape), gamma_mu=1.0)
+    rng = np.random.default_rng(1)
+    S_in = rng.standard_normal((B, H, d, d))
+    z_in = np.abs(rng.standard_normal((B, H, d))) * 4
+    check_framecausal(x, dt, S_in=S_in, z_in=z_in, name="shape %s %s" % (shape, path))
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dH%dF%dT%dd%d%s" % s)
+def test_shapes_bidir(shape, path):
+    B, H, F, T, d, dt = shape
+    x = synth.random_inputs(B, H, F, T, d, dt, seed=100 + SHAPES.index(shape))
+    check_bidir(x, dt, name="bidir shape %s %s" % (shape, path))
+
+
+def test_worked_example_zero_padded():
+    """The hand-derived d=2 example (tests/golden) embedded in d=16 with zero
+    padding (padded features contribute nothing), float32, eps=0."""
+    import json
+    import os
+    from fractions import Fraction
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                     "worked_example_d2.json")))
+    d = 16
+    gmap = {"0": 0.0, "ln3": np.log(3.0), "-ln3": -np.log(3.0)}
+
+    def pad(rows):
+        a = np.zeros((1, 1, len(rows), d), np.float32)
+        a[0, 0, :, :2] = np.asarray(rows, np.float32)
+        return a
+    q, k, v = pad(ex["q"]), pad(ex["k"]), pad(ex["v"])
+    g = pad([[gmap[s] for s in r] for r in ex["g"]])
+    gamma = dev(np.asarray(ex["gamma"], np.float32).reshape(1, 1, 2))
+    fr = lambda a: np.vectorize(lambda s: float(Fraction(s)))(np.asarray(a, dtype=object))
+    o = gla.gla_fwd_bidir(dev(q), dev(k), dev(v), dev(g), eps=0.0)
+    assert np.allclose(host(o)[0, 0, :, :2], fr(ex["bidir"]["o"]), rtol=1e-6, atol=1e-6)
+    assert np.all(host(o)[0, 0, :, 2:] == 0)
+    o, S, z = gla.gla_fwd_framecausal(dev(q), dev(k), dev(v), dev(g), gamma, eps=0.0,
+                                      return_state=True)
+    assert np.allclose(host(o)[0, 0, :, :2], fr(ex["framecausal"]["o"]), rtol=1e-6, atol=1e-6)
+    assert np.allclose(host(S)[0, 0, :2, :2], fr(ex["framecausal"]["S_out"]), rtol=1e-6)
+    c = ex["framecausal_carry"]
+    Si = np.zeros((1, 1, d, d), np.float32)
+    Si[0, 0, :2, :2] = c["S_in"]
+    zi = np.zeros((1, 1, d), np.float32)
+    zi[0, 0, :2] = c["z_in"]
+    o, S, z = gla.gla_fwd_framecausal(dev(q), dev(k), dev(v), dev(g), gamma, dev(Si), dev(zi),
+                                      eps=0.0, return_state=True)
+    assert np.allclose(host(o)[0, 0, :, :2], fr(c["o"]), rtol=1e-6, atol=1e-6)
+    assert np.allclose(host(S)[0, 0, :2, :2], fr(c["S_out"]), rtol=1e-6)
+    assert np.allclose(host(z)[0, 0, :2], fr(c["z_out"]), rtol=1e-6)
+
+
+def test_empty_and_degenerate_sizes():
+    d = 64
+    # F = 0: the state passes through unchanged
+    S_in = torch.randn(1, 2, d, d, device=DEV)
+    z_in = torch.rand(1, 2, d, device=DEV)
+    e = torch.empty(1, 2, 0, d, device=DEV, dtype=torch.bfloat16)
+    gamma0 = torch.empty(1, 2, 0, device=DEV)
+    o, S, z = gla.gla_fwd_framecausal(e, e, e, e, gamma0, S_in, z_in, return_state=True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(S, S_in) and torch.equal(z, z_in)
+    # T = 0: frames without tokens only decay the state
+    gamma = torch.tensor([[[0.5, 0.25]]], device=DEV).expand(1, 2, 2).contiguous()
+    S, z = gla.gla_state_carry(e, e, gamma, S_in, z_in)
+    torch.cuda.synchronize()
+    assert torch.allclose(S, S_in * 0.125) and torch.allclose(z, z_in * 0.125)
+    # N = 0 bidirectional and B = 0 are no-ops
+    assert gla.gla_fwd_bidir(e, e, e, e).numel() == 0
+    e0 = torch.empty(0, 2, 64, d, device=DEV, dtype=torch.bfloat16)
+    assert gla.gla_fwd_bidir(e0, e0, e0, e0).numel() == 0
+    # a single token, all queries non-positive: o = 0 exactly
+    x = synth.random_inputs(1, 1, 1, 1, d, "bf16", seed=3)
+    q = -dev(x["q"]).abs()
+    o = gla.gla_fwd_bidir(q, dev(x["k"]), dev(x["v"]), dev(x["g"]))
+    assert torch.count_nonzero(o) == 0
+
+
+def test_in_place_carry_and_state_carry_entry_point(path):
+    """S_out = S_in in place; gla_state_carry gives the same state as the forward."""
+    x = synth.random_inputs(2, 3, 6, 200, 64, "bf16", seed=31)
+    q, k, v, g, gamma = (dev(x[n]) for n in ("q", "k", "v", "g", "gamma"))
+    S0 = torch.randn(2, 3, 64, 64, device=DEV)
+    z0 = torch.rand(2, 3, 64, device=DEV)
+    o_ref, S_ref, z_ref = gla.gla_fwd_framecausal(q, k, v, g, gamma, S0, z0, return_state=True)
+    S, z = S0.clone(), z0.clone()
+    o = gla.gla_fwd_framecausal(q, k, v, g, gamma, S, z, S_out=S, z_out=z)[0]
+    Sc, zc = gla.gla_state_carry(k, v, gamma, S0, z0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref) and torch.equal(z, z_ref)
+    assert torch.equal(Sc, S_ref) and torch.equal(zc, z_ref)
+
+
+def test_block_split_resume_and_determinism():
+    """Blocks with the state carried (and once through a host copy) reproduce the
+    one-shot call; repeated calls are bitwise identical."""
+    B, H, T, d = 1, 4, 920, 64
+    blocks = (5, 3, 4)
+    F = sum(blocks)
+    x = synth.random_inputs(B, H, F, T, d, "bf16", seed=41, scale_qkv=True, gamma_mu=3.0)
+    q, k, v, g, gamma = (dev(x[n]) for n in ("q", "k", "v", "g", "gamma"))
+    o1, S1, z1 = gla.gla_fwd_framecausal(q, k, v, g, gamma, return_state=True)
+    o2, S2, z2 = gla.gla_fwd_framecausal(q, k, v, g, gamma, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(z1, z2)
+
+    S = torch.zeros(B, H, d, d, device=DEV)
+    z = torch.zeros(B, H, d, device=DEV)
+    outs, f0 = [], 0
+    for i, nf in enumerate(blocks):
+        sl = slice(f0 * T, (f0 + nf) * T)
+        ob = gla.gla_fwd_framecausal(q[:, :, sl].contiguous(), k[:, :, sl].contiguous(),
+                                     v[:, :, sl].contiguous(), g[:, :, sl].contiguous(),
+                                     gamma[:, :, f0:f0 + nf].contiguous(), S, z, S_out=S,
+                                     z_out=z)[0]
+        outs.append(ob)
+        if i == 0:  # resume from a host copy of the block cache
+            Sh, zh = S.cpu().numpy(), z.cpu().numpy()
+            S = torch.from_numpy(Sh).to(DEV)
+            z = torch.from_numpy(zh).to(DEV)
+        f0 += nf
+    ob = torch.cat(outs, dim=2)
+    torch.cuda.synchronize()
+    e_o = slab_rel_err(f64(ob), f64(o1))
+    report("block split vs one shot", o=e_o, S=state_err(S, S1.cpu().numpy()))
+    assert e_o <= 1e-6 and state_err(S, S1.cpu().numpy()) <= 1e-6
