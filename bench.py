@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the gated linear-attention forward pass on one MI355X.
+
+One step is one complete library call over the whole workload: the per-frame
+KV sums, the decayed state scan and the readout with its normalise-and-gate
+epilogue. Default workload: the 720p/60s latent-video shape (B=1, H=32, d=64,
+241 frames x 920 tokens, bf16, frame-causal, state carried across frames).
+
+Prints ONE JSON line with tokens/s, the roofline of the dominant kernel
+(measured with HIP events inside the timed work's stream), the whole call's
+fraction of the HBM roofline, and the fp64 CPU oracle timed on a bounded sample
+of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GLA fwd tokens/s at 720p/60s shape; % HBM/MFMA roofline vs CPU oracle"
+HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
+BF16_MFMA_PEAK = 2.5e15  # dense bf16 matrix-core peak, flop/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5],
+                    help="2 small, 3 720p/5s, 4 720p/60s (default), 5 streamed 8 blocks")
+    ap.add_argument("--mode", default="framecausal", choices=["framecausal", "bidir"])
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="heads of the workload the CPU oracle runs (0: skip)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gated_linear_attention_fwd_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    for p in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        txt = open(p).read()
+        for m in re.finditer(r"<!-- traffic (\{.*?\}) -->", txt):
+            rec = json.loads(m.group(1))
+            if (rec.get("kernel") == kernel and rec.get("workload") == workload
+                    and rec.get("source_hash") == source_hash()):
+                return rec
+    return None
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; --gpus %d (WORLD_SIZE=%d) is not "
+              "supported. Heads and batch shard across GPUs with no exchange; see the design "
+              "notes." % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_fwd_amd as gla
+    from gated_linear_attention_fwd_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gla.load_library()
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    mode = args.mode
+    if mode not in w.modes and args.workload != 3:
+        mode = w.modes[0]
+    es = 4 if w.dtype == "f32" else 2
+    print("bench: workload %s mode %s, drawing inputs on the device" % (w.name, mode),
+          file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- inputs
+    if args.workload == 5:
+        blocks = [synth.device_inputs(w, dev, block=b) for b in range(len(w.blocks))]
+    elif args.workload == 4:
+        blocks = [synth.device_inputs(w, dev)]
+    else:
+        x = synth.workload_inputs(w)
+        tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+        def todev(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+            return torch.from_numpy(a).to(dev)
+        blocks = [{n: todev(x[n]) for n in ("q", "k", "v", "g", "gamma")}]
+    d = w.d
+    S = torch.zeros((w.B, w.H, d, d), dtype=torch.float32, device=dev)
+    z = torch.zeros((w.B, w.H, d), dtype=torch.float32, device=dev)
+    outs = [torch.empty_like(b["q"]) for b in blocks]
+    if mode == "bidir":
+        wsb = gla.gla_fwd_bidir_workspace(w.B, w.H, w.N, d)
+    else:
+        wsb = max(gla.gla_fwd_framecausal_workspace(w.B, w.H, b["gamma"].shape[-1], w.T, d)
+                  for b in blocks)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        if mode == "bidir":
+            b = blocks[0]
+            gla.gla_fwd_bidir(b["q"], b["k"], b["v"], b["g"], eps=w.eps, out=outs[0], workspace=ws)
+            return
+        carry = len(blocks) > 1
+        if carry:
+            S.zero_()
+            z.zero_()
+        for b, o in zip(blocks, outs):
+            gla.gla_fwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"],
+                                    S if carry else None, z if carry else None, eps=w.eps,
+                                    out=o, S_out=S, z_out=z, workspace=ws)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed region
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    tokens = w.B * w.N
+    value = tokens / (ms_per_step / 1e3)
+
+    # ---------------------------------------------------------------- per-kernel times
+    launches_per_step = 3 * len(blocks)
+    gla.profile_begin(launches_per_step * args.steps)
+    for _ in range(args.steps):
+        step()
+    prof = gla.profile_end()
+    torch.cuda.synchronize()
+    per_unit = {"kv": 2 * d * es, "readout": 3 * d * es, "scan": 0}  # bytes per token-head
+    token_heads = w.B * w.H * w.N
+    kernels = {}
+    for name, (n, total) in prof.items():
+        avg_ms = total / n
+        launches_per_call = n / args.steps
+        alg = per_unit.get(name, 0) * token_heads / launches_per_call
+        kernels[name] = {"avg_ms": round(avg_ms, 5), "launches_per_step": launches_per_call,
+                         "alg_bytes_per_launch": int(alg),
+                         "alg_GBps": round(alg / (avg_ms / 1e3) / 1e9, 1) if alg else 0.0}
+    dom = max(prof, key=lambda k: prof[k][1])
+    dk = kernels[dom]
+    achieved = dk["alg_bytes_per_launch"] / (dk["avg_ms"] / 1e3)
+    traffic_rec = committed_traffic(dom, w.name + "/" + mode)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
+                "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+                "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
+    call_bytes = w.io_bytes()
+    call = {"alg_bytes": call_bytes, "GBps": round(call_bytes / (ms_per_step / 1e3) / 1e9, 1),
+            "frac_of_hbm_peak": round(call_bytes / (ms_per_step / 1e3) / HBM_PEAK, 4),
+            "flops": 4 * d * d * token_heads,
+            "frac_of_bf16_mfma_peak": round(4 * d * d * token_heads / (ms_per_step / 1e3)
+                                            / BF16_MFMA_PEAK, 4)}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    parity = None
+    if not args.no_cpu and args.cpu_heads > 0:
+        cpu, parity = cpu_baseline(args, w, mode, blocks, outs, value)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded normal draws in the latent-video shape; no dataset)",
+        "config": {"workload": w.name, "mode": mode, "B": w.B, "H": w.H, "d": d, "F": w.F,
+                   "T": w.T, "N": w.N, "blocks": list(w.blocks) or [w.F], "eps": w.eps},
+        "roofline": roofline, "call": call, "kernels": kernels, "cpu_baseline": cpu,
+        "parity": parity, "wall_s": round(wall, 3), "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(args, w, mode, blocks, outs, gpu_value):
+    """Time the fp64 oracle (recurrent form) on a bounded sample of heads of the
+    same workload, scale to tokens/s of the whole workload, and check the GPU
+    output of those heads against it."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    nh = min(args.cpu_heads, w.B * w.H)
+    heads = [(i // w.H, i % w.H) for i in range(nh)]
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.contiguous().cpu().numpy()
+
+    def sel(t):  # the sampled heads, as a [1, nh, ...] array
+        return np.concatenate([host(t[b:b + 1, h:h + 1]) for (b, h) in heads], axis=1)
+
+    x = {n: np.concatenate([sel(b[n]) for b in blocks], axis=2) for n in "qkvg"}
+    gamma = np.concatenate([sel(b["gamma"]) for b in blocks], axis=2)
+    got = np.concatenate([sel(o) for o in outs], axis=2)
+    threads = oracle.max_threads()
+    ntask = nh * ((w.d + 7) // 8)
+    print("bench: CPU oracle on %d heads, %d threads" % (nh, min(threads, ntask)),
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    if mode == "bidir":
+        ref, _, _ = oracle.recurrent(oracle.BIDIR, x["q"], x["k"], x["v"], x["g"], eps=w.eps)
+    else:
+        ref, _, _ = oracle.recurrent(oracle.FRAMECAUSAL, x["q"], x["k"], x["v"], x["g"], gamma,
+                                     eps=w.eps)
+    el = time.perf_counter() - t0
+    # the whole workload is B*H*N head-tokens for B*N tokens
+    cpu_tokens_per_s = nh * w.N / el / w.H
+    cpu = {"value": round(cpu_tokens_per_s, 1), "unit": "tokens/s",
+           "cores": int(min(threads, ntask)), "kind": "oracle",
+           "sample": "%d of %d heads (all %d tokens each), recurrent fp64 form, %.1f s; "
+                     "tokens/s = head-tokens/s / H" % (nh, w.B * w.H, w.N, el),
+           "host_cpu": host_cpu_model(), "gpu_over_cpu": round(gpu_value / cpu_tokens_per_s, 1)}
+    o64 = oracle.bf16_to_f64(got) if got.dtype == np.uint16 else got.astype(np.float64)
+    r2 = ref.reshape(1, nh, -1)
+    rms = np.sqrt(np.mean(r2 * r2, axis=-1, keepdims=True))
+    err = np.abs(o64.reshape(r2.shape) - r2) / np.maximum(np.maximum(np.abs(r2), rms), 1e-300)
+    parity = {"heads": nh, "max_slab_rel_err": float(err.max()),
+              "bar": 1e-4 if w.dtype == "f32" else 2e-2}
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    main()

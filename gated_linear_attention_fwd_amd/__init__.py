@@ -31,7 +31,7 @@ import torch
 __all__ = [
     "GlaError", "gla_fwd_bidir", "gla_fwd_framecausal", "gla_state_carry",
     "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace", "gla_state_carry_workspace",
-    "library_path", "load_library",
+    "library_path", "load_library", "profile_begin", "profile_end",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +48,11 @@ class GlaError(RuntimeError):
     def __init__(self, status: int, name: str, detail: str):
         super().__init__("libgla status %d (%s): %s" % (status, name, detail))
         self.status = status
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 16), ("launches", ctypes.c_int),
+                ("total_ms", ctypes.c_double)]
 
 
 def library_path() -> str:
@@ -84,6 +89,10 @@ def load_library():
     lib.gla_last_error.argtypes = []
     lib.gla_last_error.restype = ctypes.c_char_p
     lib.gla_version.restype = i32
+    lib.gla_profile_begin.argtypes = [i32]
+    lib.gla_profile_begin.restype = i32
+    lib.gla_profile_end.argtypes = [ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32)]
+    lib.gla_profile_end.restype = i32
     _lib = lib
     return lib
 
@@ -237,3 +246,17 @@ def gla_state_carry(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
                                _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt,
                                _ptr(ws), wsb, _stream_handle(stream, dev)))
     return S_out, z_out
+
+
+def profile_begin(max_launches: int = 4096) -> None:
+    """Start timing every kernel the entry points launch (HIP events on their stream)."""
+    _check(load_library().gla_profile_begin(int(max_launches)))
+
+
+def profile_end() -> dict:
+    """Stop timing; returns {kernel kind: (launches, summed milliseconds)}."""
+    lib = load_library()
+    out = (_KernelTime * 8)()
+    n = ctypes.c_int(0)
+    _check(lib.gla_profile_end(out, 8, ctypes.byref(n)))
+    return {out[i].name.decode(): (out[i].launches, out[i].total_ms) for i in range(min(n.value, 8))}

@@ -11,6 +11,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/gla.h"
 #include "plan.hpp"
@@ -111,6 +113,36 @@ gla_status launched(hipError_t e, const char *what) {
   return GLA_OK;
 }
 
+// ---- optional event timing of every launch (gla_profile_begin/end) ----
+enum Kind { kKindKv = 0, kKindScan = 1, kKindReadout = 2, kNumKinds = 3 };
+const char *const kKindNames[kNumKinds] = {"kv", "scan", "readout"};
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  int cap = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // start/stop pairs
+  std::vector<int> kind;
+};
+Profiler g_prof;
+
+template <class Fn>
+hipError_t timed(Kind k, hipStream_t s, Fn &&fn) {
+  int slot = -1;
+  {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    if (g_prof.on && g_prof.used < g_prof.cap) {
+      slot = g_prof.used++;
+      g_prof.kind[slot] = k;
+    }
+  }
+  if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot], s);
+  const hipError_t e = fn();
+  if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+  return e;
+}
+
 #define GLA_TRY(expr)                     \
   do {                                    \
     gla_status _st = (expr);              \
@@ -182,12 +214,17 @@ gla_status run_framecausal(const void *q, const void *k, const void *v, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Path path = select_path(dt, d);
   float *wsf = static_cast<float *>(ws);
-  if (F > 0) GLA_TRY(launched(launch_kv(p, dt, path, KvArgs{k, v, wsf}, s), "kv"));
-  GLA_TRY(launched(launch_scan(p, ScanArgs{wsf, gamma, S_in, z_in, S_out, z_out, outputs ? 1 : 0},
-                               s),
-                   "scan"));
+  if (F > 0)
+    GLA_TRY(launched(
+        timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, wsf}, s); }), "kv"));
+  const ScanArgs sa{wsf, gamma, S_in, z_in, S_out, z_out, outputs ? 1 : 0};
+  GLA_TRY(launched(timed(kKindScan, s, [&] { return launch_scan(p, sa, s); }), "scan"));
   if (outputs && have_tokens)
-    GLA_TRY(launched(launch_readout(p, dt, path, ReadoutArgs{q, g, o, wsf, eps}, s), "readout"));
+    GLA_TRY(launched(timed(kKindReadout, s,
+                           [&] {
+                             return launch_readout(p, dt, path, ReadoutArgs{q, g, o, wsf, eps}, s);
+                           }),
+                     "readout"));
   return GLA_OK;
 }
 
@@ -294,10 +331,14 @@ GLA_EXPORT gla_status gla_fwd_bidir(const void *q, const void *k, const void *v,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Path path = select_path(dt, d);
   float *wsf = static_cast<float *>(ws);
-  GLA_TRY(launched(launch_kv(p, dt, path, KvArgs{k, v, wsf}, s), "kv"));
-  GLA_TRY(launched(launch_scan(p, ScanArgs{wsf, nullptr, nullptr, nullptr, nullptr, nullptr, 1}, s),
-                   "scan"));
-  GLA_TRY(launched(launch_readout(p, dt, path, ReadoutArgs{q, g, o, wsf, eps}, s), "readout"));
+  GLA_TRY(launched(
+      timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, wsf}, s); }), "kv"));
+  const ScanArgs sa{wsf, nullptr, nullptr, nullptr, nullptr, nullptr, 1};
+  GLA_TRY(launched(timed(kKindScan, s, [&] { return launch_scan(p, sa, s); }), "scan"));
+  GLA_TRY(launched(
+      timed(kKindReadout, s,
+            [&] { return launch_readout(p, dt, path, ReadoutArgs{q, g, o, wsf, eps}, s); }),
+      "readout"));
   return GLA_OK;
 }
 
@@ -336,3 +377,57 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
 GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
 
 GLA_EXPORT int gla_version(void) { return 10000; }
+
+GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
+  if (max_launches < 1 || max_launches > 65536)
+    return fail(GLA_ERR_VALUE, "max_launches=%d must be in 1..65536", max_launches);
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (g_prof.on) return fail(GLA_ERR_VALUE, "a profiling session is already open");
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  g_prof.kind.assign((size_t)max_launches, 0);
+  for (auto &e : g_prof.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto &x : g_prof.ev)
+        if (x) (void)hipEventDestroy(x);
+      g_prof.ev.clear();
+      return fail(GLA_ERR_HIP, "hipEventCreate failed");
+    }
+  }
+  g_prof.cap = max_launches;
+  g_prof.used = 0;
+  g_prof.on = true;
+  return GLA_OK;
+}
+
+GLA_EXPORT gla_status gla_profile_end(gla_kernel_time *out, int max_out, int *n_out) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (!g_prof.on) return fail(GLA_ERR_VALUE, "no profiling session is open");
+  double total[kNumKinds] = {0, 0, 0};
+  int count[kNumKinds] = {0, 0, 0};
+  gla_status st = GLA_OK;
+  for (int i = 0; i < g_prof.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) {
+      st = fail(GLA_ERR_HIP, "reading profiling events failed");
+      break;
+    }
+    total[g_prof.kind[i]] += ms;
+    count[g_prof.kind[i]] += 1;
+  }
+  for (auto &e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.on = false;
+  int n = 0;
+  for (int k = 0; k < kNumKinds; ++k) {
+    if (count[k] == 0) continue;
+    if (out && n < max_out) {
+      snprintf(out[n].name, sizeof out[n].name, "%s", kKindNames[k]);
+      out[n].launches = count[k];
+      out[n].total_ms = total[k];
+    }
+    ++n;
+  }
+  if (n_out) *n_out = n;
+  return st;
+}

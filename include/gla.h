@@ -33,7 +33,7 @@
  *    and output, float32 accumulation; the output is rounded to nearest even).
  *  - Supported head dimensions: d in {16, 32, 64, 128}.
  *  - Pointers are device memory of the current HIP device, owned by the
- *    caller. The library never allocates, frees or synchronises; all work is
+ *    caller. The entry points never allocate, free or synchronise; all work is
  *    enqueued asynchronously on `stream` (a hipStream_t; NULL is the default
  *    stream). Tensor pointers must be 16-byte aligned, gamma 4-byte aligned,
  *    the workspace 256-byte aligned.
@@ -109,6 +109,26 @@ const char *gla_last_error(void);
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
 int gla_version(void);
+
+/* ---- kernel timing for measurement tools ---------------------------------
+ * Between gla_profile_begin and gla_profile_end, every kernel launched by the
+ * entry points (on any stream, from any thread) is bracketed by a pair of HIP
+ * events recorded on its stream. gla_profile_end waits for those events and
+ * returns, per kernel kind ("kv", "scan", "readout"), the number of launches
+ * and their summed event time. At most max_launches launches are timed; later
+ * ones run untimed. Not meant to overlap with itself: one session at a time.
+ * gla_profile_begin creates 2 * max_launches HIP events (max_launches must be
+ * 1..65536, else GLA_ERR_VALUE); gla_profile_end destroys them. Returns
+ * GLA_ERR_HIP if events cannot be created or read, GLA_ERR_VALUE if no session
+ * is open. */
+typedef struct gla_kernel_time {
+  char name[16];
+  int launches;
+  double total_ms;
+} gla_kernel_time;
+
+gla_status gla_profile_begin(int max_launches);
+gla_status gla_profile_end(gla_kernel_time *out, int max_out, int *n_out);
 
 #ifdef __cplusplus
 }
