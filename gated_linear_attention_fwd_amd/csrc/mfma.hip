@@ -1,11 +1,437 @@
-// mfma.hip -- bf16 matrix-core kernels (placeholder until the MFMA path lands).
+// mfma.hip -- bf16 matrix-core (MFMA) kernels for gfx950: KV sums and readout.
+//
+// Both contractions of the gated linear attention run on
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation; bf16 x bf16 products are exact
+// in fp32):
+//
+//   kv:      U = phi(K)^T V over a token range (d x C times C x d), u = phi(K)^T 1
+//   readout: o^T = S_f^T phi(Q)^T (d x d times d x C), den = phi(Q) z_f, then
+//            o = sigmoid(g) * num / (den + eps), rounded to bf16
+//
+// The state is fp32; for the readout it is split as S = S_hi + S_lo with both
+// parts bf16 (S_lo = bf16(S - S_hi)), so the product keeps ~16 bits of S.
+//
+// MFMA 32x32x16 bf16 operand layout (lane l, half h = l / 32):
+//   A[m][k]: lane holds m = l % 32, k = 8h .. 8h+7
+//   B[k][n]: lane holds n = l % 32, k = 8h .. 8h+7
+//   C[m][n]: element r holds m = 8(r/4) + 4h + r%4, n = l % 32
+// Any consistent relabelling of k between A and B gives the same sum.
+//
+// KV: the contraction runs over tokens, the slow axis of the [N][d] layout, so
+// both operands are read transposed out of row-major LDS tiles with
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane j supplies
+// the address of 4 consecutive bf16 in row j/4 (columns 4(j%4)..) of a 4 x 16
+// block and receives column j of that block (rows 0..3).
 #include "common.hpp"
 #include "plan.hpp"
 
 namespace gla {
-bool mfma_supports(int) { return false; }
-hipError_t launch_kv_mfma(const Plan &, const KvArgs &, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_readout_mfma(const Plan &, const ReadoutArgs &, hipStream_t) {
-  return hipErrorInvalidValue;
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// ReLU of two packed bf16: as signed 16-bit integers every negative bf16
+// (including -0) is negative, so max(x, 0) in int16 is max(x, +0) in bf16.
+__device__ __forceinline__ uint32_t relu2(uint32_t w) {
+  i16x2 v = __builtin_bit_cast(i16x2, w);
+  v = __builtin_elementwise_max(v, (i16x2){0, 0});
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint4 relu8(uint4 x) {
+  return make_uint4(relu2(x.x), relu2(x.y), relu2(x.z), relu2(x.w));
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ bf16x8 tr_fragment(const lds_char *tile, int row, int col, int pitch) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)(tile + row * pitch + col * 2));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)(tile + (row + 4) * pitch + col * 2));
+  const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+// ---------------------------------------------------------------------------
+// KV sums
+// ---------------------------------------------------------------------------
+template <int D>
+struct KvCfg {
+  static constexpr int CH = 64;             // tokens per LDS chunk (4 k-steps of 16)
+  static constexpr int PITCH = 2 * D + 32;  // bytes per LDS row: 4 rows hit disjoint banks
+  static constexpr int MB = D / 32;         // 32 x 32 blocks per side of U
+  // D <= 64: every wave owns all MB x MB blocks and one k-step of each chunk
+  // (partials summed across waves at the end). D = 128: the 4 x 4 blocks are
+  // split 2 x 2 over the waves, each wave runs every k-step.
+  static constexpr bool kSplitTokens = (D <= 64);
+  static constexpr int TM = kSplitTokens ? MB : MB / 2;
+  static constexpr int ROW_CHUNKS = D / 8;                 // 16-byte pieces per row
+  static constexpr int CPT = CH * ROW_CHUNKS / kThreads;   // pieces per thread per array
+  static constexpr int ROWS_PER_PASS = kThreads / ROW_CHUNKS;
+  static constexpr int TILE_BYTES = CH * PITCH;
+  static constexpr int RED_BYTES = kSplitTokens ? 4 * 1024 * 4 : 0;  // 4 waves x 32x32 fp32
+  static constexpr int U_RED_BYTES = 4 * D * 4;                       // 4 waves x D fp32
+  static constexpr int SMEM = (2 * TILE_BYTES > RED_BYTES ? 2 * TILE_BYTES : RED_BYTES);
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__restrict__ k,
+                                                           const uint16_t *__restrict__ v,
+                                                           float *__restrict__ ws, int F,
+                                                           int64_t T, int P, int64_t part_len) {
+  using C = KvCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM + C::U_RED_BYTES];
+  lds_char *const sbase = (lds_char *)smem;
+  lds_char *const tk = sbase;
+  lds_char *const tv = sbase + C::TILE_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t wg = blockIdx.x;
+  const int p = (int)(wg % P);
+  const int f = (int)((wg / P) % F);
+  const int64_t bh = wg / ((int64_t)P * F);
+  const int64_t N = (int64_t)F * T;
+  const int64_t t0 = min((int64_t)p * part_len, T);
+  const int64_t t1 = min(t0 + part_len, T);
+  const int L = (int)(t1 - t0);
+  const int nchunks = (L + C::CH - 1) / C::CH;
+  const uint4 *kb = reinterpret_cast<const uint4 *>(k + (bh * N + (int64_t)f * T + t0) * D);
+  const uint4 *vb = reinterpret_cast<const uint4 *>(v + (bh * N + (int64_t)f * T + t0) * D);
+
+  // this thread's 16-byte pieces: fixed column piece c, rows r0 + i * ROWS_PER_PASS
+  const int c = tid % C::ROW_CHUNKS;
+  const int r0 = tid / C::ROW_CHUNKS;
+  uint4 rk[C::CPT], rv[C::CPT];
+  auto load = [&](int chunk) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = chunk * C::CH + r0 + i * C::ROWS_PER_PASS;
+      if (row < L) {
+        rk[i] = kb[(int64_t)row * C::ROW_CHUNKS + c];
+        rv[i] = vb[(int64_t)row * C::ROW_CHUNKS + c];
+      } else {
+        rk[i] = make_uint4(0, 0, 0, 0);
+        rv[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  float uacc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
+  f32x16 acc[C::TM][C::TM];
+#pragma unroll
+  for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+    for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // lane geometry of the transposed fragment reads
+  const int h = lane >> 5;
+  const int grp = (lane >> 4) & 1;
+  const int j = lane & 15;
+  const int frag_row = 8 * h + (j >> 2);
+  const int frag_col = 16 * grp + 4 * (j & 3);
+  const int wm = C::kSplitTokens ? 0 : (wave >> 1);
+  const int wn = C::kSplitTokens ? 0 : (wave & 1);
+
+  if (nchunks > 0) load(0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = r0 + i * C::ROWS_PER_PASS;
+      const uint4 kk = relu8(rk[i]);
+      *reinterpret_cast<uint4 *>(smem + row * C::PITCH + c * 16) = kk;
+      *reinterpret_cast<uint4 *>(smem + C::TILE_BYTES + row * C::PITCH + c * 16) = rv[i];
+      uacc[0] += lo_bf16(kk.x);
+      uacc[1] += hi_bf16(kk.x);
+      uacc[2] += lo_bf16(kk.y);
+      uacc[3] += hi_bf16(kk.y);
+      uacc[4] += lo_bf16(kk.z);
+      uacc[5] += hi_bf16(kk.z);
+      uacc[6] += lo_bf16(kk.w);
+      uacc[7] += hi_bf16(kk.w);
+    }
+    __syncthreads();
+    if (ch + 1 < nchunks) load(ch + 1);
+
+    constexpr int KS_PER_WAVE = C::kSplitTokens ? 1 : 4;
+#pragma unroll
+    for (int kk = 0; kk < KS_PER_WAVE; ++kk) {
+      const int ks = C::kSplitTokens ? wave : kk;
+      bf16x8 fa[C::TM], fb[C::TM];
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a) {
+        fa[a] = tr_fragment(tk, ks * 16 + frag_row, 32 * (wm * C::TM + a) + frag_col, C::PITCH);
+        fb[a] = tr_fragment(tv, ks * 16 + frag_row, 32 * (wn * C::TM + a) + frag_col, C::PITCH);
+      }
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_32x32x16(fa[a], fb[b], acc[a][b]);
+    }
+  }
+
+  float *out = ws + wg * ((int64_t)D * D + D);
+
+  // U blocks
+  if constexpr (C::kSplitTokens) {
+    float *red = (float *)smem;  // [wave][r][lane]
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b) {
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[wave * 1024 + r * 64 + lane] = acc[a][b][r];
+        __syncthreads();
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int idx = tid + kThreads * e4;
+          const float s = red[idx] + red[1024 + idx] + red[2048 + idx] + red[3072 + idx];
+          const int r = idx >> 6, ln = idx & 63;
+          const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+          out[(32 * a + m) * D + 32 * b + (ln & 31)] = s;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 8 * (r >> 2) + 4 * h + (r & 3);
+          out[(32 * (wm * C::TM + a) + m) * D + 32 * (wn * C::TM + b) + (lane & 31)] =
+              acc[a][b][r];
+        }
+  }
+
+  // u: sum this thread's 8 features over lanes with the same column piece, then waves
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int off = C::ROW_CHUNKS; off < 64; off <<= 1) uacc[e] += __shfl_xor(uacc[e], off);
+  }
+  float *ured = (float *)(smem + C::SMEM);
+  if (lane < C::ROW_CHUNKS) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ured[wave * D + lane * 8 + e] = uacc[e];
+  }
+  __syncthreads();
+  if (tid < D) out[D * D + tid] = ured[tid] + ured[D + tid] + ured[2 * D + tid] + ured[3 * D + tid];
+}
+
+// ---------------------------------------------------------------------------
+// Readout
+// ---------------------------------------------------------------------------
+template <int D>
+struct RoCfg {
+  static constexpr int MB = D / 32;            // 32-feature output blocks
+  static constexpr int TG = 4 / MB;            // token groups of 32 across the waves
+  static constexpr int BLK = 32 * TG;          // tokens per iteration
+  static constexpr int KS = D / 16;            // k-steps over the input features
+  static constexpr int PITCH = 2 * D + 16;     // bytes per LDS row of phi(q)
+  static constexpr int ROW_CHUNKS = D / 8;
+  static constexpr int CPT = BLK * ROW_CHUNKS / kThreads;  // 16-byte pieces per thread
+  static constexpr int ROWS_PER_PASS = kThreads / ROW_CHUNKS;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void readout_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ g, uint16_t *__restrict__ o,
+    const float *__restrict__ ws, int F, int64_t T, int P, int R, int64_t read_len, float eps) {
+  using C = RoCfg<D>;
+  __shared__ __attribute__((aligned(16))) char qtile[C::BLK * C::PITCH];
+  __shared__ float den_s[C::BLK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int mb = wave % C::MB;
+  const int tg = wave / C::MB;
+  const int64_t wg = blockIdx.x;
+  const int r = (int)(wg % R);
+  const int f = (int)((wg / R) % F);
+  const int64_t bh = wg / ((int64_t)R * F);
+  const int64_t N = (int64_t)F * T;
+  const int64_t t0 = min((int64_t)r * read_len, T);
+  const int64_t t1 = min(t0 + read_len, T);
+  const int L = (int)(t1 - t0);
+  if (L <= 0) return;
+  const int64_t row0 = bh * N + (int64_t)f * T + t0;  // first token row of this split
+
+  // A = S_f^T as bf16 hi/lo fragments: lane holds S[16ks + 8h + e][32mb + lane%32]
+  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * ((int64_t)D * D + D);
+  bf16x8 ahi[C::KS], alo[C::KS];
+  {
+    const int jcol = 32 * mb + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      i16x8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float s = Sg[(16 * ks + 8 * h + e) * D + jcol];
+        const uint16_t sh = f32_to_bf16_rne(s);
+        const uint16_t sl = f32_to_bf16_rne(s - bf16_to_f32(sh));
+        hv[e] = (short)sh;
+        lv[e] = (short)sl;
+      }
+      ahi[ks] = __builtin_bit_cast(bf16x8, hv);
+      alo[ks] = __builtin_bit_cast(bf16x8, lv);
+    }
+  }
+  // this thread's 16-byte piece of each phi(q) row and the matching z values
+  const int c = tid % C::ROW_CHUNKS;
+  const int r0 = tid / C::ROW_CHUNKS;
+  float zc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zc[e] = Sg[D * D + 8 * c + e];
+
+  const uint4 *qb = reinterpret_cast<const uint4 *>(q + row0 * D);
+  uint4 rq[C::CPT];
+  auto load_q = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = blk * C::BLK + r0 + i * C::ROWS_PER_PASS;
+      rq[i] = (row < L) ? qb[(int64_t)row * C::ROW_CHUNKS + c] : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  const int nblk = (L + C::BLK - 1) / C::BLK;
+  load_q(0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    // phi(q) into LDS, and den = phi(q) . z per token
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = r0 + i * C::ROWS_PER_PASS;
+      const uint4 w = relu8(rq[i]);
+      *reinterpret_cast<uint4 *>(qtile + row * C::PITCH + c * 16) = w;
+      float dp = lo_bf16(w.x) * zc[0];
+      dp = fmaf(hi_bf16(w.x), zc[1], dp);
+      dp = fmaf(lo_bf16(w.y), zc[2], dp);
+      dp = fmaf(hi_bf16(w.y), zc[3], dp);
+      dp = fmaf(lo_bf16(w.z), zc[4], dp);
+      dp = fmaf(hi_bf16(w.z), zc[5], dp);
+      dp = fmaf(lo_bf16(w.w), zc[6], dp);
+      dp = fmaf(hi_bf16(w.w), zc[7], dp);
+#pragma unroll
+      for (int off = 1; off < C::ROW_CHUNKS; off <<= 1) dp += __shfl_xor(dp, off);
+      if (c == 0) den_s[row] = dp;
+    }
+    __syncthreads();
+    if (blk + 1 < nblk) load_q(blk + 1);
+
+    // this wave's tokens and output features
+    const int tl = 32 * tg + (lane & 31);        // token within the block
+    const int tok = blk * C::BLK + tl;           // token within the split
+    const bool valid = tok < L;
+    const int64_t grow = (row0 + tok) * D + 32 * mb + 4 * h;
+    uint2 gr[4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      gr[rg] = valid ? *reinterpret_cast<const uint2 *>(g + grow + 8 * rg) : make_uint2(0, 0);
+
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const uint4 bw =
+          *reinterpret_cast<const uint4 *>(qtile + tl * C::PITCH + (16 * ks + 8 * h) * 2);
+      const bf16x8 bf = __builtin_bit_cast(bf16x8, bw);
+      acc = mfma_32x32x16(ahi[ks], bf, acc);
+      acc = mfma_32x32x16(alo[ks], bf, acc);
+    }
+
+    const float inv = 1.f / (den_s[tl] + eps);
+    if (valid) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const float o0 = sigmoid(lo_bf16(gr[rg].x)) * (acc[4 * rg + 0] * inv);
+        const float o1 = sigmoid(hi_bf16(gr[rg].x)) * (acc[4 * rg + 1] * inv);
+        const float o2 = sigmoid(lo_bf16(gr[rg].y)) * (acc[4 * rg + 2] * inv);
+        const float o3 = sigmoid(hi_bf16(gr[rg].y)) * (acc[4 * rg + 3] * inv);
+        uint2 ow;
+        ow.x = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+        ow.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
+        *reinterpret_cast<uint2 *>(o + grow + 8 * rg) = ow;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool mfma_supports(int d) { return d == 32 || d == 64 || d == 128; }
+
+hipError_t launch_kv_mfma(const Plan &p, const KvArgs &a, hipStream_t s) {
+  const int64_t grid = p.BH * p.F * p.P;
+  if (grid == 0) return hipSuccess;
+  const uint16_t *k = static_cast<const uint16_t *>(a.k);
+  const uint16_t *v = static_cast<const uint16_t *>(a.v);
+  switch (p.d) {
+    case 32:
+      hipLaunchKernelGGL(kv_mfma_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
+                         a.ws, p.F, p.T, p.P, p.part_len);
+      break;
+    case 64:
+      hipLaunchKernelGGL(kv_mfma_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
+                         a.ws, p.F, p.T, p.P, p.part_len);
+      break;
+    case 128:
+      hipLaunchKernelGGL(kv_mfma_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
+                         a.ws, p.F, p.T, p.P, p.part_len);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_readout_mfma(const Plan &p, const ReadoutArgs &a, hipStream_t s) {
+  const int64_t grid = p.BH * p.F * p.R;
+  if (grid == 0 || p.T == 0) return hipSuccess;
+  const uint16_t *q = static_cast<const uint16_t *>(a.q);
+  const uint16_t *g = static_cast<const uint16_t *>(a.g);
+  uint16_t *o = static_cast<uint16_t *>(a.o);
+  switch (p.d) {
+    case 32:
+      hipLaunchKernelGGL(readout_mfma_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
+                         g, o, a.ws, p.F, p.T, p.P, p.R, p.read_len, a.eps);
+      break;
+    case 64:
+      hipLaunchKernelGGL(readout_mfma_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
+                         g, o, a.ws, p.F, p.T, p.P, p.R, p.read_len, a.eps);
+      break;
+    case 128:
+      hipLaunchKernelGGL(readout_mfma_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
+                         g, o, a.ws, p.F, p.T, p.P, p.R, p.read_len, a.eps);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace gla
