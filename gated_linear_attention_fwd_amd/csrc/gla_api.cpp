@@ -33,6 +33,10 @@ constexpr int64_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several t
 constexpr int64_t kMinPartTokens = 128;
 constexpr int64_t kMinSplitTokens = 64;
 constexpr int64_t kTokenAlign = 32;
+constexpr int64_t kMaxGroupFrames = 8;
+// kv workgroups resident at once on 256 CUs (4 per CU at d <= 64): grouping
+// frames down to about this many workgroups removes the tail of a second wave.
+constexpr int64_t kResidentKvWorkgroups = 1024;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -216,13 +220,14 @@ gla_status run_framecausal(const void *q, const void *k, const void *v, const vo
   float *wsf = static_cast<float *>(ws);
   if (F > 0)
     GLA_TRY(launched(
-        timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, wsf}, s); }), "kv"));
+        timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, gamma, wsf}, s); }), "kv"));
   const ScanArgs sa{wsf, gamma, S_in, z_in, S_out, z_out, outputs ? 1 : 0};
   GLA_TRY(launched(timed(kKindScan, s, [&] { return launch_scan(p, sa, s); }), "scan"));
   if (outputs && have_tokens)
     GLA_TRY(launched(timed(kKindReadout, s,
                            [&] {
-                             return launch_readout(p, dt, path, ReadoutArgs{q, g, o, wsf, eps}, s);
+                             return launch_readout(p, dt, path,
+                                                   ReadoutArgs{q, g, o, gamma, wsf, eps}, s);
                            }),
                      "readout"));
   return GLA_OK;
@@ -248,6 +253,14 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
     p.P = (int)ceil_div(T, p.part_len);
     p.read_len = round_up(ceil_div(T, R), kTokenAlign);
     p.R = (int)ceil_div(T, p.read_len);
+    // Enough frames for a full grid: group consecutive frames in one kv workgroup.
+    // (The d = 128 matrix-core kernel keeps no running state and so runs one
+    // frame per workgroup.)
+    const bool can_group = p.P == 1 && d <= 64;
+    if (can_group && units >= 2 * kTargetWorkgroups)
+      p.G = (int)std::min<int64_t>(kMaxGroupFrames, ceil_div(units, kResidentKvWorkgroups));
+    if (const char *e = getenv("GLA_FRAMES_PER_GROUP"))
+      if (can_group && atoi(e) >= 1) p.G = std::min(atoi(e), std::max(F, 1));
   } else {
     p.P = p.R = 1;
     p.part_len = p.read_len = round_up(T, kTokenAlign);
@@ -258,7 +271,8 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
   if (T > 0 && units > (int64_t(1) << 62) / T / std::max(d, 1)) return false;
   const int64_t E = p.state_elems();
   if (BH * ceil_div(E, 256) >= max_grid) return false;
-  p.ws_bytes = (size_t)round_up(units * p.P * E * 4, 256);
+  p.NG = (int)ceil_div(F, p.G);
+  p.ws_bytes = (size_t)round_up((units * p.P + BH * p.NG) * E * 4, 256);
   *plan = p;
   return true;
 }
@@ -332,12 +346,15 @@ GLA_EXPORT gla_status gla_fwd_bidir(const void *q, const void *k, const void *v,
   const Path path = select_path(dt, d);
   float *wsf = static_cast<float *>(ws);
   GLA_TRY(launched(
-      timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, wsf}, s); }), "kv"));
+      timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, nullptr, wsf}, s); }),
+      "kv"));
   const ScanArgs sa{wsf, nullptr, nullptr, nullptr, nullptr, nullptr, 1};
   GLA_TRY(launched(timed(kKindScan, s, [&] { return launch_scan(p, sa, s); }), "scan"));
   GLA_TRY(launched(
       timed(kKindReadout, s,
-            [&] { return launch_readout(p, dt, path, ReadoutArgs{q, g, o, wsf, eps}, s); }),
+            [&] {
+              return launch_readout(p, dt, path, ReadoutArgs{q, g, o, nullptr, wsf, eps}, s);
+            }),
       "readout"));
   return GLA_OK;
 }

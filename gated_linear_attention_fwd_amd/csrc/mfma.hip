@@ -33,10 +33,35 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
+
+// q, k, v and g are read exactly once and o is written once: nontemporal
+// loads and stores keep that stream from displacing lines the next kernel
+// reuses (measured on the 720p/60s shape: kv -10%, readout -7%). Every such
+// access is a 16-byte-per-lane instruction covering whole rows.
+#ifndef GLA_KV_NT_LOADS
+#define GLA_KV_NT_LOADS 1
+#endif
+#ifndef GLA_RO_NT_LOADS
+#define GLA_RO_NT_LOADS 1
+#endif
+#ifndef GLA_RO_NT_STORES
+#define GLA_RO_NT_STORES 1
+#endif
+
+template <bool kNt>
+__device__ __forceinline__ uint4 ld_stream16(const uint4 *p) {
+  if constexpr (kNt) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+  } else {
+    return *p;
+  }
+}
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -72,13 +97,17 @@ __device__ __forceinline__ bf16x8 tr_fragment(const lds_char *tile, int row, int
 template <int D>
 struct KvCfg {
   static constexpr int CH = 64;             // tokens per LDS chunk (4 k-steps of 16)
-  static constexpr int PITCH = 2 * D + 32;  // bytes per LDS row: 4 rows hit disjoint banks
+  static constexpr int PITCH = 2 * D + 32;  // bytes per LDS row
   static constexpr int MB = D / 32;         // 32 x 32 blocks per side of U
-  // D <= 64: every wave owns all MB x MB blocks and one k-step of each chunk
-  // (partials summed across waves at the end). D = 128: the 4 x 4 blocks are
-  // split 2 x 2 over the waves, each wave runs every k-step.
-  static constexpr bool kSplitTokens = (D <= 64);
+  // D = 32: every wave owns the single block and one k-step of each chunk
+  // (partials summed across waves per frame). D >= 64: the MB x MB blocks are
+  // split 2 x 2 over the waves and each wave runs every k-step, so a wave owns
+  // its blocks outright and no cross-wave sum is needed.
+  static constexpr bool kSplitTokens = (D == 32);
   static constexpr int TM = kSplitTokens ? MB : MB / 2;
+  // running decayed state kept across the frames of a group (G > 1 happens
+  // only for d <= 64)
+  static constexpr bool kGroups = (D <= 64);
   static constexpr int ROW_CHUNKS = D / 8;                 // 16-byte pieces per row
   static constexpr int CPT = CH * ROW_CHUNKS / kThreads;   // pieces per thread per array
   static constexpr int ROWS_PER_PASS = kThreads / ROW_CHUNKS;
@@ -88,11 +117,20 @@ struct KvCfg {
   static constexpr int SMEM = (2 * TILE_BYTES > RED_BYTES ? 2 * TILE_BYTES : RED_BYTES);
 };
 
+// One workgroup per (slab, group of G frames, part). Per frame the MFMA
+// accumulators collect that frame's U_f; a per-thread running state then
+// becomes S_loc_f = gamma_f * S_loc_{f-1} + U_f and is written to the frame's
+// slot (z likewise). d = 128 keeps no running state (it would cost 64 more
+// registers per lane) and runs one frame per workgroup. Chunks are numbered
+// across the group's frames so that the next chunk's loads (possibly the next
+// frame's) overlap the MFMAs and the write-out of the current one.
 template <int D>
 __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__restrict__ k,
                                                            const uint16_t *__restrict__ v,
+                                                           const float *__restrict__ gamma,
                                                            float *__restrict__ ws, int F,
-                                                           int64_t T, int P, int64_t part_len) {
+                                                           int64_t T, int P, int G,
+                                                           int64_t part_len) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM + C::U_RED_BYTES];
   lds_char *const sbase = (lds_char *)smem;
@@ -102,29 +140,37 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int NG = (F + G - 1) / G;
   const int64_t wg = blockIdx.x;
   const int p = (int)(wg % P);
-  const int f = (int)((wg / P) % F);
-  const int64_t bh = wg / ((int64_t)P * F);
+  const int grp = (int)((wg / P) % NG);
+  const int64_t bh = wg / ((int64_t)P * NG);
   const int64_t N = (int64_t)F * T;
   const int64_t t0 = min((int64_t)p * part_len, T);
   const int64_t t1 = min(t0 + part_len, T);
   const int L = (int)(t1 - t0);
-  const int nchunks = (L + C::CH - 1) / C::CH;
-  const uint4 *kb = reinterpret_cast<const uint4 *>(k + (bh * N + (int64_t)f * T + t0) * D);
-  const uint4 *vb = reinterpret_cast<const uint4 *>(v + (bh * N + (int64_t)f * T + t0) * D);
+  const int f_begin = grp * G;
+  const int nf = C::kGroups ? min(F, f_begin + G) - f_begin : 1;  // d = 128: G == 1
+  const int ncf = (L + C::CH - 1) / C::CH;  // chunks per frame
+  const int total = nf * ncf;
+  const uint4 *kb = reinterpret_cast<const uint4 *>(k + (bh * N + (int64_t)f_begin * T + t0) * D);
+  const uint4 *vb = reinterpret_cast<const uint4 *>(v + (bh * N + (int64_t)f_begin * T + t0) * D);
+  const int64_t frame_pieces = T * C::ROW_CHUNKS;  // 16-byte pieces per frame
 
   // this thread's 16-byte pieces: fixed column piece c, rows r0 + i * ROWS_PER_PASS
   const int c = tid % C::ROW_CHUNKS;
   const int r0 = tid / C::ROW_CHUNKS;
   uint4 rk[C::CPT], rv[C::CPT];
   auto load = [&](int chunk) {
+    const int fi = chunk / ncf;
+    const int base = (chunk - fi * ncf) * C::CH;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int row = chunk * C::CH + r0 + i * C::ROWS_PER_PASS;
+      const int row = base + r0 + i * C::ROWS_PER_PASS;
       if (row < L) {
-        rk[i] = kb[(int64_t)row * C::ROW_CHUNKS + c];
-        rv[i] = vb[(int64_t)row * C::ROW_CHUNKS + c];
+        const int64_t off = fi * frame_pieces + (int64_t)row * C::ROW_CHUNKS + c;
+        rk[i] = ld_stream16<GLA_KV_NT_LOADS>(kb + off);
+        rv[i] = ld_stream16<GLA_KV_NT_LOADS>(vb + off);
       } else {
         rk[i] = make_uint4(0, 0, 0, 0);
         rv[i] = make_uint4(0, 0, 0, 0);
@@ -145,99 +191,137 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
 
   // lane geometry of the transposed fragment reads
   const int h = lane >> 5;
-  const int grp = (lane >> 4) & 1;
+  const int grp16 = (lane >> 4) & 1;
   const int j = lane & 15;
   const int frag_row = 8 * h + (j >> 2);
-  const int frag_col = 16 * grp + 4 * (j & 3);
+  const int frag_col = 16 * grp16 + 4 * (j & 3);
   const int wm = C::kSplitTokens ? 0 : (wave >> 1);
   const int wn = C::kSplitTokens ? 0 : (wave & 1);
+  float *red = (float *)smem;                 // [wave][r][lane], aliases the tiles
+  float *ured = (float *)(smem + C::SMEM);    // [wave][D]
 
-  if (nchunks > 0) load(0);
-  for (int ch = 0; ch < nchunks; ++ch) {
-    __syncthreads();
+  // running state of the group: accumulator layout (d = 64) or the layout of
+  // the cross-wave sum (d = 32)
+  constexpr int kSt = !C::kGroups ? 1 : (C::kSplitTokens ? C::TM * C::TM * 4 : C::TM * C::TM * 16);
+  float st[kSt];
+  float zst = 0.f;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int row = r0 + i * C::ROWS_PER_PASS;
-      const uint4 kk = relu8(rk[i]);
-      *reinterpret_cast<uint4 *>(smem + row * C::PITCH + c * 16) = kk;
-      *reinterpret_cast<uint4 *>(smem + C::TILE_BYTES + row * C::PITCH + c * 16) = rv[i];
-      uacc[0] += lo_bf16(kk.x);
-      uacc[1] += hi_bf16(kk.x);
-      uacc[2] += lo_bf16(kk.y);
-      uacc[3] += hi_bf16(kk.y);
-      uacc[4] += lo_bf16(kk.z);
-      uacc[5] += hi_bf16(kk.z);
-      uacc[6] += lo_bf16(kk.w);
-      uacc[7] += hi_bf16(kk.w);
-    }
-    __syncthreads();
-    if (ch + 1 < nchunks) load(ch + 1);
+  for (int e = 0; e < kSt; ++e) st[e] = 0.f;
 
-    constexpr int KS_PER_WAVE = C::kSplitTokens ? 1 : 4;
-#pragma unroll
-    for (int kk = 0; kk < KS_PER_WAVE; ++kk) {
-      const int ks = C::kSplitTokens ? wave : kk;
-      bf16x8 fa[C::TM], fb[C::TM];
-#pragma unroll
-      for (int a = 0; a < C::TM; ++a) {
-        fa[a] = tr_fragment(tk, ks * 16 + frag_row, 32 * (wm * C::TM + a) + frag_col, C::PITCH);
-        fb[a] = tr_fragment(tv, ks * 16 + frag_row, 32 * (wn * C::TM + a) + frag_col, C::PITCH);
-      }
+  if (total > 0) load(0);
+  for (int fi = 0; fi < nf; ++fi) {
+    const float gm = fi > 0 ? gamma[bh * F + f_begin + fi] : 0.f;
+    if (fi > 0) {
 #pragma unroll
       for (int a = 0; a < C::TM; ++a)
 #pragma unroll
-        for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_32x32x16(fa[a], fb[b], acc[a][b]);
+        for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
+    }
+    for (int cc = 0; cc < ncf; ++cc) {
+      const int ch = fi * ncf + cc;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < C::CPT; ++i) {
+        const int row = r0 + i * C::ROWS_PER_PASS;
+        const uint4 kk = relu8(rk[i]);
+        *reinterpret_cast<uint4 *>(smem + row * C::PITCH + c * 16) = kk;
+        *reinterpret_cast<uint4 *>(smem + C::TILE_BYTES + row * C::PITCH + c * 16) = rv[i];
+        uacc[0] += lo_bf16(kk.x);
+        uacc[1] += hi_bf16(kk.x);
+        uacc[2] += lo_bf16(kk.y);
+        uacc[3] += hi_bf16(kk.y);
+        uacc[4] += lo_bf16(kk.z);
+        uacc[5] += hi_bf16(kk.z);
+        uacc[6] += lo_bf16(kk.w);
+        uacc[7] += hi_bf16(kk.w);
+      }
+      __syncthreads();
+      if (ch + 1 < total) load(ch + 1);
+
+      constexpr int KS_PER_WAVE = C::kSplitTokens ? 1 : 4;
+#pragma unroll
+      for (int kk = 0; kk < KS_PER_WAVE; ++kk) {
+        const int ks = C::kSplitTokens ? wave : kk;
+        bf16x8 fa[C::TM], fb[C::TM];
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a) {
+          fa[a] = tr_fragment(tk, ks * 16 + frag_row, 32 * (wm * C::TM + a) + frag_col, C::PITCH);
+          fb[a] = tr_fragment(tv, ks * 16 + frag_row, 32 * (wn * C::TM + a) + frag_col, C::PITCH);
+        }
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+          for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_32x32x16(fa[a], fb[b], acc[a][b]);
+      }
+    }
+
+    // ---- write the frame's slot: S_loc (blocks of 32 x 32) and z_loc
+    float *out = ws + ((bh * F + f_begin + fi) * (int64_t)P + p) * ((int64_t)D * D + D);
+    // Recompute the write-out offsets from an opaque copy of the thread id each
+    // frame; hoisted out of the frame loop they would stay live in registers.
+    int tidv = tid;
+    asm volatile("" : "+v"(tidv));
+    const int lanev = tidv & 63;
+    if constexpr (C::kSplitTokens) {
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b) {
+          __syncthreads();
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[wave * 1024 + r * 64 + lanev] = acc[a][b][r];
+          __syncthreads();
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int idx = tidv + kThreads * e4;
+            const float sum = red[idx] + red[1024 + idx] + red[2048 + idx] + red[3072 + idx];
+            float &sv = st[(a * C::TM + b) * 4 + e4];
+            sv = fmaf(gm, sv, sum);  // kSplitTokens implies kGroups
+            const int r = idx >> 6, ln = idx & 63;
+            const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+            out[(32 * a + m) * D + 32 * b + (ln & 31)] = sv;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float sv = acc[a][b][r];
+            if constexpr (C::kGroups) {
+              float &run = st[(a * C::TM + b) * 16 + r];
+              run = fmaf(gm, run, sv);
+              sv = run;
+            }
+            const int m = 8 * (r >> 2) + 4 * (lanev >> 5) + (r & 3);
+            out[(32 * (wm * C::TM + a) + m) * D + 32 * (wn * C::TM + b) + (lanev & 31)] = sv;
+          }
+    }
+    // z_loc: sum the thread's 8 features over lanes with the same column piece, then waves
+    float us[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      us[e] = uacc[e];
+#pragma unroll
+      for (int off = C::ROW_CHUNKS; off < 64; off <<= 1) us[e] += __shfl_xor(us[e], off);
+    }
+    __syncthreads();  // previous frame's ured reads are done
+    if (lanev < C::ROW_CHUNKS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ured[wave * D + lanev * 8 + e] = us[e];
+    }
+    __syncthreads();
+    if (tidv < D) {
+      zst = fmaf(gm, zst, ured[tidv] + ured[D + tidv] + ured[2 * D + tidv] + ured[3 * D + tidv]);
+      out[D * D + tidv] = zst;
     }
   }
-
-  float *out = ws + wg * ((int64_t)D * D + D);
-
-  // U blocks
-  if constexpr (C::kSplitTokens) {
-    float *red = (float *)smem;  // [wave][r][lane]
-#pragma unroll
-    for (int a = 0; a < C::TM; ++a)
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b) {
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[wave * 1024 + r * 64 + lane] = acc[a][b][r];
-        __syncthreads();
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int idx = tid + kThreads * e4;
-          const float s = red[idx] + red[1024 + idx] + red[2048 + idx] + red[3072 + idx];
-          const int r = idx >> 6, ln = idx & 63;
-          const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-          out[(32 * a + m) * D + 32 * b + (ln & 31)] = s;
-        }
-      }
-  } else {
-#pragma unroll
-    for (int a = 0; a < C::TM; ++a)
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = 8 * (r >> 2) + 4 * h + (r & 3);
-          out[(32 * (wm * C::TM + a) + m) * D + 32 * (wn * C::TM + b) + (lane & 31)] =
-              acc[a][b][r];
-        }
-  }
-
-  // u: sum this thread's 8 features over lanes with the same column piece, then waves
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-#pragma unroll
-    for (int off = C::ROW_CHUNKS; off < 64; off <<= 1) uacc[e] += __shfl_xor(uacc[e], off);
-  }
-  float *ured = (float *)(smem + C::SMEM);
-  if (lane < C::ROW_CHUNKS) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ured[wave * D + lane * 8 + e] = uacc[e];
-  }
-  __syncthreads();
-  if (tid < D) out[D * D + tid] = ured[tid] + ured[D + tid] + ured[2 * D + tid] + ured[3 * D + tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -255,12 +339,23 @@ struct RoCfg {
   static constexpr int ROWS_PER_PASS = kThreads / ROW_CHUNKS;
 };
 
+// One workgroup per (slab, frame, split). q, g and o move through LDS so that
+// every global access is a 16-byte-per-lane load or store covering whole rows;
+// the MFMA operand reads (phi(q), B layout) and the epilogue's C-layout
+// gather of g / scatter of o happen in LDS. Per block of tokens:
+//   1. phi(q) and g rows -> LDS; den = phi(q) . z_f computed on the way
+//   2. acc = S_f^T phi(q)^T over the input features (hi and lo parts of S_f)
+//   3. o = sigmoid(g) * acc / (den + eps) -> bf16, written over g in LDS
+//   4. o rows -> global memory
 template <int D>
-__global__ __launch_bounds__(kThreads) void readout_mfma_kernel(
+__global__ __launch_bounds__(kThreads) void readout_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ g, uint16_t *__restrict__ o,
-    const float *__restrict__ ws, int F, int64_t T, int P, int R, int64_t read_len, float eps) {
+    const float *__restrict__ gamma, const float *__restrict__ ws, int F, int64_t T, int P,
+    int G, int64_t carry_offset, int R, int64_t read_len, float eps) {
   using C = RoCfg<D>;
+  constexpr int GP = 2 * D + 16;  // bytes per LDS row of g / o
   __shared__ __attribute__((aligned(16))) char qtile[C::BLK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) char gtile[C::BLK * GP];
   __shared__ float den_s[C::BLK];
 
   const int tid = threadIdx.x;
@@ -278,10 +373,14 @@ __global__ __launch_bounds__(kThreads) void readout_mfma_kernel(
   const int64_t t1 = min(t0 + read_len, T);
   const int L = (int)(t1 - t0);
   if (L <= 0) return;
-  const int64_t row0 = bh * N + (int64_t)f * T + t0;  // first token row of this split
+  const int64_t row0 = bh * N + (int64_t)f * T + t0;
 
-  // A = S_f^T as bf16 hi/lo fragments: lane holds S[16ks + 8h + e][32mb + lane%32]
-  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * ((int64_t)D * D + D);
+  // S_f = S_loc_f + w_f * carry of the frame's group, as bf16 hi/lo A fragments
+  constexpr int64_t E = (int64_t)D * D + D;
+  const int NG = (F + G - 1) / G;
+  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;
+  const float *Cg = ws + carry_offset + (bh * NG + f / G) * E;
+  const float w = carry_weight(gamma ? gamma + bh * F : nullptr, f, G);
   bf16x8 ahi[C::KS], alo[C::KS];
   {
     const int jcol = 32 * mb + (lane & 31);
@@ -290,42 +389,51 @@ __global__ __launch_bounds__(kThreads) void readout_mfma_kernel(
       i16x8 hv, lv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float s = Sg[(16 * ks + 8 * h + e) * D + jcol];
-        const uint16_t sh = f32_to_bf16_rne(s);
-        const uint16_t sl = f32_to_bf16_rne(s - bf16_to_f32(sh));
+        const int idx = (16 * ks + 8 * h + e) * D + jcol;
+        const float sv = fmaf(w, Cg[idx], Sg[idx]);
+        const uint16_t sh = f32_to_bf16_rne(sv);
+        const uint16_t sl = f32_to_bf16_rne(sv - bf16_to_f32(sh));
         hv[e] = (short)sh;
         lv[e] = (short)sl;
       }
       ahi[ks] = __builtin_bit_cast(bf16x8, hv);
       alo[ks] = __builtin_bit_cast(bf16x8, lv);
+      asm volatile("" ::: "memory");  // one k-step of loads in flight at a time (registers)
     }
   }
-  // this thread's 16-byte piece of each phi(q) row and the matching z values
   const int c = tid % C::ROW_CHUNKS;
   const int r0 = tid / C::ROW_CHUNKS;
   float zc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zc[e] = Sg[D * D + 8 * c + e];
+  for (int e = 0; e < 8; ++e) zc[e] = fmaf(w, Cg[D * D + 8 * c + e], Sg[D * D + 8 * c + e]);
 
   const uint4 *qb = reinterpret_cast<const uint4 *>(q + row0 * D);
-  uint4 rq[C::CPT];
-  auto load_q = [&](int blk) {
+  const uint4 *gb = reinterpret_cast<const uint4 *>(g + row0 * D);
+  uint4 *ob = reinterpret_cast<uint4 *>(o + row0 * D);
+  uint4 rq[C::CPT], rgv[C::CPT];
+  auto load = [&](int blk) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = blk * C::BLK + r0 + i * C::ROWS_PER_PASS;
-      rq[i] = (row < L) ? qb[(int64_t)row * C::ROW_CHUNKS + c] : make_uint4(0, 0, 0, 0);
+      const bool ok = row < L;
+      rq[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(qb + (int64_t)row * C::ROW_CHUNKS + c)
+                 : make_uint4(0, 0, 0, 0);
+      rgv[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(gb + (int64_t)row * C::ROW_CHUNKS + c)
+                  : make_uint4(0, 0, 0, 0);
     }
   };
 
+  const int tl = 32 * tg + (lane & 31);
   const int nblk = (L + C::BLK - 1) / C::BLK;
-  load_q(0);
+  load(0);
   for (int blk = 0; blk < nblk; ++blk) {
-    // phi(q) into LDS, and den = phi(q) . z per token
+    __syncthreads();  // the previous block's o rows have been read out of gtile
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = r0 + i * C::ROWS_PER_PASS;
       const uint4 w = relu8(rq[i]);
       *reinterpret_cast<uint4 *>(qtile + row * C::PITCH + c * 16) = w;
+      *reinterpret_cast<uint4 *>(gtile + row * GP + c * 16) = rgv[i];
       float dp = lo_bf16(w.x) * zc[0];
       dp = fmaf(hi_bf16(w.x), zc[1], dp);
       dp = fmaf(lo_bf16(w.y), zc[2], dp);
@@ -339,17 +447,7 @@ __global__ __launch_bounds__(kThreads) void readout_mfma_kernel(
       if (c == 0) den_s[row] = dp;
     }
     __syncthreads();
-    if (blk + 1 < nblk) load_q(blk + 1);
-
-    // this wave's tokens and output features
-    const int tl = 32 * tg + (lane & 31);        // token within the block
-    const int tok = blk * C::BLK + tl;           // token within the split
-    const bool valid = tok < L;
-    const int64_t grow = (row0 + tok) * D + 32 * mb + 4 * h;
-    uint2 gr[4];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-      gr[rg] = valid ? *reinterpret_cast<const uint2 *>(g + grow + 8 * rg) : make_uint2(0, 0);
+    if (blk + 1 < nblk) load(blk + 1);
 
     f32x16 acc;
 #pragma unroll
@@ -362,22 +460,35 @@ __global__ __launch_bounds__(kThreads) void readout_mfma_kernel(
       acc = mfma_32x32x16(ahi[ks], bf, acc);
       acc = mfma_32x32x16(alo[ks], bf, acc);
     }
-
     const float inv = 1.f / (den_s[tl] + eps);
-    if (valid) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const float o0 = sigmoid(lo_bf16(gr[rg].x)) * (acc[4 * rg + 0] * inv);
-        const float o1 = sigmoid(hi_bf16(gr[rg].x)) * (acc[4 * rg + 1] * inv);
-        const float o2 = sigmoid(lo_bf16(gr[rg].y)) * (acc[4 * rg + 2] * inv);
-        const float o3 = sigmoid(hi_bf16(gr[rg].y)) * (acc[4 * rg + 3] * inv);
-        uint2 ow;
-        ow.x = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
-        ow.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
-        *reinterpret_cast<uint2 *>(o + grow + 8 * rg) = ow;
-      }
+    for (int rg = 0; rg < 4; ++rg) {
+      uint2 *cell = reinterpret_cast<uint2 *>(gtile + tl * GP + (32 * mb + 8 * rg + 4 * h) * 2);
+      const uint2 gv = *cell;
+      const float o0 = sigmoid(lo_bf16(gv.x)) * (acc[4 * rg + 0] * inv);
+      const float o1 = sigmoid(hi_bf16(gv.x)) * (acc[4 * rg + 1] * inv);
+      const float o2 = sigmoid(lo_bf16(gv.y)) * (acc[4 * rg + 2] * inv);
+      const float o3 = sigmoid(hi_bf16(gv.y)) * (acc[4 * rg + 3] * inv);
+      uint2 ow;
+      ow.x = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+      ow.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
+      *cell = ow;
     }
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = r0 + i * C::ROWS_PER_PASS;
+      const int tok = blk * C::BLK + row;
+      if (tok < L) {
+        const uint4 ov = *reinterpret_cast<const uint4 *>(gtile + row * GP + c * 16);
+        if constexpr (GLA_RO_NT_STORES != 0) {
+          const u32x4 x = {ov.x, ov.y, ov.z, ov.w};
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(ob + (int64_t)tok * C::ROW_CHUNKS + c));
+        } else {
+          ob[(int64_t)tok * C::ROW_CHUNKS + c] = ov;
+        }
+      }
+    }
   }
 }
 
@@ -386,22 +497,22 @@ __global__ __launch_bounds__(kThreads) void readout_mfma_kernel(
 bool mfma_supports(int d) { return d == 32 || d == 64 || d == 128; }
 
 hipError_t launch_kv_mfma(const Plan &p, const KvArgs &a, hipStream_t s) {
-  const int64_t grid = p.BH * p.F * p.P;
+  const int64_t grid = p.BH * p.NG * p.P;
   if (grid == 0) return hipSuccess;
   const uint16_t *k = static_cast<const uint16_t *>(a.k);
   const uint16_t *v = static_cast<const uint16_t *>(a.v);
   switch (p.d) {
     case 32:
       hipLaunchKernelGGL(kv_mfma_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
-                         a.ws, p.F, p.T, p.P, p.part_len);
+                         a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len);
       break;
     case 64:
       hipLaunchKernelGGL(kv_mfma_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
-                         a.ws, p.F, p.T, p.P, p.part_len);
+                         a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len);
       break;
     case 128:
       hipLaunchKernelGGL(kv_mfma_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
-                         a.ws, p.F, p.T, p.P, p.part_len);
+                         a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len);
       break;
     default:
       return hipErrorInvalidValue;
@@ -417,16 +528,19 @@ hipError_t launch_readout_mfma(const Plan &p, const ReadoutArgs &a, hipStream_t 
   uint16_t *o = static_cast<uint16_t *>(a.o);
   switch (p.d) {
     case 32:
-      hipLaunchKernelGGL(readout_mfma_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
-                         g, o, a.ws, p.F, p.T, p.P, p.R, p.read_len, a.eps);
+      hipLaunchKernelGGL(readout_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
+                         g, o, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(), p.R,
+                         p.read_len, a.eps);
       break;
     case 64:
-      hipLaunchKernelGGL(readout_mfma_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
-                         g, o, a.ws, p.F, p.T, p.P, p.R, p.read_len, a.eps);
+      hipLaunchKernelGGL(readout_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
+                         g, o, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(), p.R,
+                         p.read_len, a.eps);
       break;
     case 128:
-      hipLaunchKernelGGL(readout_mfma_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
-                         g, o, a.ws, p.F, p.T, p.P, p.R, p.read_len, a.eps);
+      hipLaunchKernelGGL(readout_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
+                         g, o, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(), p.R,
+                         p.read_len, a.eps);
       break;
     default:
       return hipErrorInvalidValue;

@@ -4,17 +4,23 @@
 // frames of T tokens (bidirectional mode: one frame of all N tokens). The
 // forward pass runs as three launches on the caller's stream:
 //
-//   1. kv      one workgroup per (slab, frame, part): the part's sums
-//              U = sum phi(k) v^T (d x d) and u = sum phi(k) (d), fp32, into
-//              the workspace slot of that (slab, frame, part);
-//   2. scan    one thread per (slab, state element): sums the parts of each
-//              frame in a fixed order and runs S_f = gamma_f S_{f-1} + U_f
-//              over the frames, leaving S_f in the frame's part-0 slot;
-//   3. readout one workgroup per (slab, frame, split): phi(q) S_f, phi(q) z_f,
-//              the normalise-and-gate epilogue, the store of o.
+//   1. kv      one workgroup per (slab, group of G consecutive frames, part).
+//              It keeps the decayed running sum of its frames in its
+//              accumulators, S_loc_f = gamma_f S_loc_{f-1} + U_f (S_loc = U
+//              at the group's first frame), with U_f = sum phi(k) v^T over the
+//              part's tokens, and writes S_loc_f and z_loc_f (fp32) into the
+//              workspace slot of every (slab, frame, part);
+//   2. carry   one thread per (slab, state element): walks the groups in order,
+//              carry_0 = S_in (or 0), carry_{g+1} = S_loc_{last of g} +
+//              (prod of gamma over g) carry_g, and stores carry_g per group;
+//              with several parts per frame (G = 1) it also sums the parts;
+//   3. readout one workgroup per (slab, frame, split): S_f = S_loc_f +
+//              (prod_{m=first of group}^{f} gamma_m) carry_g, then phi(q) S_f,
+//              phi(q) z_f, the normalise-and-gate epilogue and the store of o.
 //
-// Parts and splits exist only to give small problems enough workgroups; the
-// partition depends on the sizes alone, so results are bitwise reproducible.
+// Groups cut the workspace traffic of the scan (only one state per group is
+// chained) and parts give small problems enough workgroups; the partition
+// depends on the sizes alone, so results are bitwise reproducible.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,9 +38,14 @@ struct Plan {
   int64_t part_len = 0;  // tokens per kv part (a multiple of 32)
   int R = 1;             // readout splits per frame
   int64_t read_len = 0;  // tokens per readout split (a multiple of 32)
-  size_t ws_bytes = 0;   // workspace: BH * F * P * (d*d + d) floats, 256-byte rounded
+  int G = 1;             // frames per kv group (G > 1 only with P == 1)
+  int NG = 0;            // groups per slab, ceil(F / G)
+  size_t ws_bytes = 0;   // workspace bytes, 256-byte rounded:
+                         //   slots  BH * F * P  states of d*d + d floats
+                         //   carry  BH * NG     states of d*d + d floats
 
   int64_t state_elems() const { return (int64_t)d * d + d; }
+  int64_t carry_offset() const { return BH * F * (int64_t)P * state_elems(); }  // floats
 };
 
 // Cut sizes into a plan. Returns false if the sizes overflow the indexing.
@@ -48,6 +59,7 @@ Path select_path(int dtype, int d);
 struct KvArgs {
   const void *k;
   const void *v;
+  const float *gamma;  // NULL: no decay (bidirectional; then G == 1)
   float *ws;
 };
 
@@ -58,16 +70,25 @@ struct ScanArgs {
   const float *z_in;
   float *S_out;        // NULL: not written
   float *z_out;
-  int store_frames;    // 1: keep S_f of every frame for the readout
+  int keep_frames;     // 1: leave what the readout needs (carries, summed parts)
 };
 
 struct ReadoutArgs {
   const void *q;
   const void *g;
   void *o;
+  const float *gamma;  // NULL: no decay
   const float *ws;
   float eps;
 };
+
+// Decay weight of a frame's carry-in: prod_{m = first frame of f's group}^{f} gamma_m.
+__device__ __forceinline__ float carry_weight(const float *gamma_slab, int f, int G) {
+  float w = 1.f;
+  if (gamma_slab)
+    for (int m = (f / G) * G; m <= f; ++m) w *= gamma_slab[m];
+  return w;
+}
 
 hipError_t launch_kv(const Plan &p, int dtype, Path path, const KvArgs &a, hipStream_t s);
 hipError_t launch_scan(const Plan &p, const ScanArgs &a, hipStream_t s);

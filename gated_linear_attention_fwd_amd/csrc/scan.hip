@@ -1,16 +1,24 @@
-// scan.hip -- inter-frame decayed state scan.
+// scan.hip -- the carry chain of the decayed state scan across frame groups.
 //
-// S_f = gamma_f * S_{f-1} + U_f and z_f = gamma_f * z_{f-1} + u_f, S_{-1} = S_in
-// (or 0): the frame-wise decayed running state of the gated linear attention
-// (decay gates: "SANA-WM" analysis page, method components; additive update of
-// a fixed D x D state carried block to block: SANA-Video ICLR 2026 oral talk,
-// block KV cache passage). Bidirectional mode is the same scan with one frame
-// and no decay.
+// The running state of the frame-causal gated linear attention obeys
+// S_f = gamma_f * S_{f-1} + U_f (and z likewise), S_{-1} = S_in or 0: the
+// frame-wise decay of the "SANA-WM" analysis page (method components) applied
+// to the fixed D x D state that the SANA-Video ICLR 2026 oral talk carries
+// additively from block to block (block KV cache passage). The kv kernel has
+// already folded each group of G consecutive frames into its local sums
+// S_loc; what remains is the chain over groups:
 //
-// One thread owns one of the d*d + d state elements of one slab and walks the
-// frames in order. The chain of FMAs is serial, the loads are not: a batch of
-// FB frames is loaded first (summing each frame's parts in a fixed order), then
-// folded in, so FB loads per thread are in flight at once.
+//   carry_0 = S_in (or 0)
+//   carry_{g+1} = S_loc_{last frame of g} + (prod_{m in g} gamma_m) * carry_g
+//
+// and S_out = carry_{NG}. With several parts per frame (then G = 1) the parts
+// of a frame are summed here in a fixed order, and the sum is left in part 0
+// for the readout. Bidirectional mode is the same walk with one frame and no
+// decay.
+//
+// One thread owns one of the d*d + d state elements of one slab. The chain of
+// FMAs is serial, the loads are not: a batch of groups is loaded first, then
+// folded in, so many loads per thread are in flight at once.
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -18,12 +26,12 @@ namespace gla {
 namespace {
 
 constexpr int kScanThreads = 256;
-constexpr int kFrameBatch = 16;
+constexpr int kGroupBatch = 16;
 
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(
+__global__ __launch_bounds__(kScanThreads) void carry_kernel(
     float *__restrict__ ws, const float *__restrict__ gamma, const float *S_in,
-    const float *z_in, float *S_out, float *z_out, int F, int P, int d, int64_t blocks_per_slab,
-    int store_frames) {
+    const float *z_in, float *S_out, float *z_out, int F, int P, int G, int NG, int d,
+    int64_t blocks_per_slab, int64_t carry_offset, int keep_frames) {
   const int64_t dd = (int64_t)d * d;
   const int64_t E = dd + d;
   const int64_t bh = blockIdx.x / blocks_per_slab;
@@ -34,31 +42,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   if (S_in) s = (e < dd) ? S_in[bh * dd + e] : z_in[bh * d + (e - dd)];
 
   const int64_t frame_stride = (int64_t)P * E;
-  float *base = ws + bh * (int64_t)F * frame_stride + e;
+  float *slots = ws + bh * (int64_t)F * frame_stride + e;
+  float *carry = ws + carry_offset + bh * (int64_t)NG * E + e;
   const float *gm_slab = gamma ? gamma + bh * F : nullptr;
 
-  for (int f0 = 0; f0 < F; f0 += kFrameBatch) {
-    float acc[kFrameBatch];
-    float gm[kFrameBatch];
+  for (int g0 = 0; g0 < NG; g0 += kGroupBatch) {
+    float x[kGroupBatch];
+    float w[kGroupBatch];
 #pragma unroll
-    for (int j = 0; j < kFrameBatch; ++j) {
-      const int f = f0 + j;
-      acc[j] = 0.f;
-      gm[j] = 1.f;
-      if (f < F) {
-        const float *src = base + (int64_t)f * frame_stride;
+    for (int j = 0; j < kGroupBatch; ++j) {
+      const int grp = g0 + j;
+      x[j] = 0.f;
+      w[j] = 1.f;
+      if (grp < NG) {
+        const int last = min(F, (grp + 1) * G) - 1;
+        const float *src = slots + (int64_t)last * frame_stride;
         float a = src[0];
         for (int p = 1; p < P; ++p) a += src[(int64_t)p * E];
-        acc[j] = a;
-        if (gm_slab) gm[j] = gm_slab[f];
+        x[j] = a;
+        if (gm_slab)
+          for (int m = grp * G; m <= last; ++m) w[j] *= gm_slab[m];
       }
     }
 #pragma unroll
-    for (int j = 0; j < kFrameBatch; ++j) {
-      const int f = f0 + j;
-      if (f < F) {
-        s = fmaf(gm[j], s, acc[j]);
-        if (store_frames) base[(int64_t)f * frame_stride] = s;
+    for (int j = 0; j < kGroupBatch; ++j) {
+      const int grp = g0 + j;
+      if (grp < NG) {
+        if (keep_frames) {
+          carry[(int64_t)grp * E] = s;
+          if (P > 1) slots[(int64_t)(min(F, (grp + 1) * G) - 1) * frame_stride] = x[j];
+        }
+        s = fmaf(w[j], s, x[j]);
       }
     }
   }
@@ -78,9 +92,9 @@ hipError_t launch_scan(const Plan &p, const ScanArgs &a, hipStream_t stream) {
   const int64_t blocks_per_slab = (E + kScanThreads - 1) / kScanThreads;
   const int64_t grid = p.BH * blocks_per_slab;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)grid), dim3(kScanThreads), 0, stream, a.ws,
-                     a.gamma, a.S_in, a.z_in, a.S_out, a.z_out, p.F, p.P, p.d, blocks_per_slab,
-                     a.store_frames);
+  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)grid), dim3(kScanThreads), 0, stream, a.ws,
+                     a.gamma, a.S_in, a.z_in, a.S_out, a.z_out, p.F, p.P, p.G, p.NG, p.d,
+                     blocks_per_slab, p.carry_offset(), a.keep_frames);
   return hipGetLastError();
 }
 

@@ -14,15 +14,19 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKvTile = 32;  // tokens staged in LDS per step
 
-// One workgroup per (slab, frame, part). Thread layout: key feature i = tid % D,
-// value columns j = tid / D + (256 / D) * c for c < D*D/256. Each token adds
-// phi(k[i]) * v[j] to the thread's entries; u[i] is kept by threads with
-// tid < D.
+// One workgroup per (slab, group of frames, part). Thread layout: key feature
+// i = tid % D, value columns j = tid / D + (256 / D) * c for c < D*D/256. Each
+// token adds phi(k[i]) * v[j] to the thread's entries; u[i] is kept by threads
+// with tid < D. Entering each frame after the group's first, the running sums
+// are scaled by that frame's gamma; after each frame they are written to the
+// frame's slot (S_loc_f, z_loc_f).
 template <typename TIn, int D>
 __global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict__ k,
                                                            const TIn *__restrict__ v,
+                                                           const float *__restrict__ gamma,
                                                            float *__restrict__ ws, int F,
-                                                           int64_t T, int P, int64_t part_len) {
+                                                           int64_t T, int P, int G,
+                                                           int64_t part_len) {
   static_assert(D * D >= kThreads && (D * D) % kThreads == 0, "D must be 16..128");
   constexpr int EPT = D * D / kThreads;
   constexpr int JS = kThreads / D;
@@ -30,15 +34,16 @@ __global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict
   __shared__ float sv[kKvTile][D];
 
   const int tid = threadIdx.x;
+  const int NG = (F + G - 1) / G;
   const int64_t wg = blockIdx.x;
   const int p = (int)(wg % P);
-  const int f = (int)((wg / P) % F);
-  const int64_t bh = wg / ((int64_t)P * F);
+  const int grp = (int)((wg / P) % NG);
+  const int64_t bh = wg / ((int64_t)P * NG);
   const int64_t N = (int64_t)F * T;
   const int64_t t0 = min((int64_t)p * part_len, T);
   const int64_t t1 = min(t0 + part_len, T);
-  const TIn *kb = k + (bh * N + (int64_t)f * T) * D;
-  const TIn *vb = v + (bh * N + (int64_t)f * T) * D;
+  const int f_begin = grp * G;
+  const int f_end = min(F, f_begin + G);
 
   const int i = tid % D;
   const int jc = tid / D;
@@ -47,32 +52,41 @@ __global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict
   for (int c = 0; c < EPT; ++c) acc[c] = 0.f;
   float uacc = 0.f;
 
-  for (int64_t c0 = t0; c0 < t1; c0 += kKvTile) {
-    const int n = (int)min((int64_t)kKvTile, t1 - c0);
-    __syncthreads();
-    for (int e = tid; e < kKvTile * D; e += kThreads) {
-      const int tt = e / D, ii = e % D;
-      float kk = 0.f, vv = 0.f;
-      if (tt < n) {
-        kk = relu(Elem<TIn>::load(kb, (c0 + tt) * D + ii));
-        vv = Elem<TIn>::load(vb, (c0 + tt) * D + ii);
+  for (int f = f_begin; f < f_end; ++f) {
+    if (f > f_begin) {
+      const float gm = gamma[bh * F + f];
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) acc[c] *= gm;
+      uacc *= gm;
+    }
+    const TIn *kb = k + (bh * N + (int64_t)f * T) * D;
+    const TIn *vb = v + (bh * N + (int64_t)f * T) * D;
+    for (int64_t c0 = t0; c0 < t1; c0 += kKvTile) {
+      const int n = (int)min((int64_t)kKvTile, t1 - c0);
+      __syncthreads();
+      for (int e = tid; e < kKvTile * D; e += kThreads) {
+        const int tt = e / D, ii = e % D;
+        float kk = 0.f, vv = 0.f;
+        if (tt < n) {
+          kk = relu(Elem<TIn>::load(kb, (c0 + tt) * D + ii));
+          vv = Elem<TIn>::load(vb, (c0 + tt) * D + ii);
+        }
+        sk[tt][ii] = kk;
+        sv[tt][ii] = vv;
       }
-      sk[tt][ii] = kk;
-      sv[tt][ii] = vv;
-    }
-    __syncthreads();
-    for (int tt = 0; tt < n; ++tt) {
-      const float kk = sk[tt][i];
-      uacc += kk;
+      __syncthreads();
+      for (int tt = 0; tt < n; ++tt) {
+        const float kk = sk[tt][i];
+        uacc += kk;
 #pragma unroll
-      for (int c = 0; c < EPT; ++c) acc[c] = fmaf(kk, sv[tt][jc + JS * c], acc[c]);
+        for (int c = 0; c < EPT; ++c) acc[c] = fmaf(kk, sv[tt][jc + JS * c], acc[c]);
+      }
     }
+    float *out = ws + ((bh * F + f) * (int64_t)P + p) * ((int64_t)D * D + D);
+#pragma unroll
+    for (int c = 0; c < EPT; ++c) out[i * D + jc + JS * c] = acc[c];
+    if (jc == 0) out[D * D + i] = uacc;
   }
-
-  float *out = ws + wg * ((int64_t)D * D + D);
-#pragma unroll
-  for (int c = 0; c < EPT; ++c) out[i * D + jc + JS * c] = acc[c];
-  if (jc == 0) out[D * D + i] = uacc;
 }
 
 // One workgroup per (slab, frame, split). Thread layout: 4 value columns
@@ -81,7 +95,8 @@ __global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict
 template <typename TIn, int D>
 __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ g, TIn *__restrict__ o,
-    const float *__restrict__ ws, int F, int64_t T, int P, int R, int64_t read_len, float eps) {
+    const float *__restrict__ gamma, const float *__restrict__ ws, int F, int64_t T, int P,
+    int G, int64_t carry_offset, int R, int64_t read_len, float eps) {
   constexpr int CG = D / 4;             // column groups
   constexpr int TT = kThreads / CG;     // tokens per tile
   constexpr bool kSInLds = (D <= 64);
@@ -99,11 +114,15 @@ __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
   const int64_t t1 = min(t0 + read_len, T);
   if (t0 >= t1) return;
 
-  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * ((int64_t)D * D + D);
+  // S_f = S_loc_f + w_f * carry of the frame's group
+  constexpr int64_t E = (int64_t)D * D + D;
+  const int NG = (F + G - 1) / G;
+  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;
+  const float *Cg = ws + carry_offset + (bh * NG + f / G) * E;
+  const float w = carry_weight(gamma ? gamma + bh * F : nullptr, f, G);
   if (kSInLds)
-    for (int e = tid; e < D * D; e += kThreads) sS[e] = Sg[e];
-  for (int e = tid; e < D; e += kThreads) sz[e] = Sg[D * D + e];
-  const float *Sp = kSInLds ? sS : Sg;
+    for (int e = tid; e < D * D; e += kThreads) sS[e] = fmaf(w, Cg[e], Sg[e]);
+  for (int e = tid; e < D; e += kThreads) sz[e] = fmaf(w, Cg[D * D + e], Sg[D * D + e]);
 
   const int64_t row0 = bh * N + (int64_t)f * T;
   const int cg = tid % CG;
@@ -123,7 +142,15 @@ __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
       for (int ii = 0; ii < D; ++ii) {
         const float qi = sq[tl][ii];
         den = fmaf(qi, sz[ii], den);
-        const float4 s4 = *reinterpret_cast<const float4 *>(Sp + ii * D + 4 * cg);
+        float4 s4;
+        if (kSInLds) {
+          s4 = *reinterpret_cast<const float4 *>(sS + ii * D + 4 * cg);
+        } else {
+          const float4 a4 = *reinterpret_cast<const float4 *>(Sg + ii * D + 4 * cg);
+          const float4 c4 = *reinterpret_cast<const float4 *>(Cg + ii * D + 4 * cg);
+          s4 = make_float4(fmaf(w, c4.x, a4.x), fmaf(w, c4.y, a4.y), fmaf(w, c4.z, a4.z),
+                           fmaf(w, c4.w, a4.w));
+        }
         num.x = fmaf(qi, s4.x, num.x);
         num.y = fmaf(qi, s4.y, num.y);
         num.z = fmaf(qi, s4.z, num.z);
@@ -144,13 +171,13 @@ __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
 
 template <typename TIn>
 hipError_t kv_valu_dispatch(const Plan &p, const KvArgs &a, hipStream_t s) {
-  const int64_t grid = p.BH * p.F * p.P;
+  const int64_t grid = p.BH * p.NG * p.P;
   const TIn *k = static_cast<const TIn *>(a.k);
   const TIn *v = static_cast<const TIn *>(a.v);
 #define GLA_KV_CASE(DD)                                                                   \
   case DD:                                                                                \
     hipLaunchKernelGGL((kv_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), 0, \
-                       s, k, v, a.ws, p.F, p.T, p.P, p.part_len);                         \
+                       s, k, v, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len);           \
     break;
   switch (p.d) {
     GLA_KV_CASE(16)
@@ -173,7 +200,8 @@ hipError_t readout_valu_dispatch(const Plan &p, const ReadoutArgs &a, hipStream_
 #define GLA_RO_CASE(DD)                                                                     \
   case DD:                                                                                  \
     hipLaunchKernelGGL((readout_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), \
-                       0, s, q, g, o, a.ws, p.F, p.T, p.P, p.R, p.read_len, a.eps);         \
+                       0, s, q, g, o, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(), \
+                       p.R, p.read_len, a.eps);                                             \
     break;
   switch (p.d) {
     GLA_RO_CASE(16)
@@ -190,7 +218,7 @@ hipError_t readout_valu_dispatch(const Plan &p, const ReadoutArgs &a, hipStream_
 }  // namespace
 
 hipError_t launch_kv_valu(const Plan &p, int dtype, const KvArgs &a, hipStream_t s) {
-  if (p.BH * p.F * p.P == 0) return hipSuccess;
+  if (p.BH * p.NG * p.P == 0) return hipSuccess;
   return dtype == 0 ? kv_valu_dispatch<float>(p, a, s) : kv_valu_dispatch<bf16_t>(p, a, s);
 }
 

@@ -325,3 +325,24 @@ def test_block_split_resume_and_determinism():
     e_o = slab_rel_err(f64(ob), f64(o1))
     report("block split vs one shot", o=e_o, S=state_err(S, S1.cpu().numpy()))
     assert e_o <= 1e-6 and state_err(S, S1.cpu().numpy()) <= 1e-6
+
+
+@pytest.mark.parametrize("G", [2, 3, 8])
+@pytest.mark.parametrize("d,dt", [(64, "bf16"), (32, "bf16"), (64, "f32")])
+def test_frame_groups_with_carry(G, d, dt, path, monkeypatch):
+    """kv workgroups that own G consecutive frames (running decayed sum in the
+    accumulators, chained by the carry kernel), with a ragged last group and a
+    carried-in state; T <= 128 keeps one part per frame so grouping applies."""
+    monkeypatch.setenv("GLA_FRAMES_PER_GROUP", str(G))
+    x = synth.random_inputs(1, 3, 7, 100, d, dt, seed=50 + G + d, gamma_mu=1.0)
+    rng = np.random.default_rng(G)
+    S_in = rng.standard_normal((1, 3, d, d))
+    z_in = np.abs(rng.standard_normal((1, 3, d))) * 4
+    check_framecausal(x, dt, S_in=S_in, z_in=z_in, name="groups G=%d d=%d %s %s" % (G, d, dt, path))
+    k, v, gamma = dev(x["k"]), dev(x["v"]), dev(x["gamma"])
+    Sc, zc = gla.gla_state_carry(k, v, gamma, dev(S_in.astype(np.float32)),
+                                 dev(z_in.astype(np.float32)))
+    _, rS, rz = oracle.recurrent(oracle.FRAMECAUSAL, None, x["k"], x["v"], None, x["gamma"],
+                                 S_in=S_in.astype(np.float32), z_in=z_in.astype(np.float32),
+                                 outputs=False)
+    assert state_err(Sc, rS) <= STATE_TOL and state_err(zc, rz) <= STATE_TOL
