@@ -34,8 +34,8 @@ BF16_MFMA_PEAK = 2.5e15  # dense bf16 matrix-core peak, flop/s
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5],
                     help="2 small, 3 720p/5s, 4 720p/60s (default), 5 streamed 8 blocks")
     ap.add_argument("--mode", default="framecausal", choices=["framecausal", "bidir"])
@@ -181,7 +181,7 @@ def main():
         step()
     prof = gla.profile_end()
     torch.cuda.synchronize()
-    per_unit = {"kv": 2 * d * es, "readout": 3 * d * es, "scan": 0}  # bytes per token-head
+    per_unit = {"kv": 2 * d * es, "readout": 3 * d * es, "carry": 0}  # bytes per token-head
     token_heads = w.B * w.H * w.N
     kernels = {}
     for name, (n, total) in prof.items():

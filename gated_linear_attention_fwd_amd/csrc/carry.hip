@@ -1,4 +1,4 @@
-// scan.hip -- the carry chain of the decayed state scan across frame groups.
+// carry.hip -- the carry chain of the decayed state scan across frame groups.
 //
 // The running state of the frame-causal gated linear attention obeys
 // S_f = gamma_f * S_{f-1} + U_f (and z likewise), S_{-1} = S_in or 0: the
@@ -25,17 +25,17 @@
 namespace gla {
 namespace {
 
-constexpr int kScanThreads = 256;
+constexpr int kCarryThreads = 256;
 constexpr int kGroupBatch = 16;
 
-__global__ __launch_bounds__(kScanThreads) void carry_kernel(
+__global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     float *__restrict__ ws, const float *__restrict__ gamma, const float *S_in,
     const float *z_in, float *S_out, float *z_out, int F, int P, int G, int NG, int d,
     int64_t blocks_per_slab, int64_t carry_offset, int keep_frames) {
   const int64_t dd = (int64_t)d * d;
   const int64_t E = dd + d;
   const int64_t bh = blockIdx.x / blocks_per_slab;
-  const int64_t e = (blockIdx.x % blocks_per_slab) * kScanThreads + threadIdx.x;
+  const int64_t e = (blockIdx.x % blocks_per_slab) * kCarryThreads + threadIdx.x;
   if (e >= E) return;
 
   float s = 0.f;
@@ -87,12 +87,12 @@ __global__ __launch_bounds__(kScanThreads) void carry_kernel(
 
 }  // namespace
 
-hipError_t launch_scan(const Plan &p, const ScanArgs &a, hipStream_t stream) {
+hipError_t launch_carry(const Plan &p, const CarryArgs &a, hipStream_t stream) {
   const int64_t E = p.state_elems();
-  const int64_t blocks_per_slab = (E + kScanThreads - 1) / kScanThreads;
+  const int64_t blocks_per_slab = (E + kCarryThreads - 1) / kCarryThreads;
   const int64_t grid = p.BH * blocks_per_slab;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)grid), dim3(kScanThreads), 0, stream, a.ws,
+  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)grid), dim3(kCarryThreads), 0, stream, a.ws,
                      a.gamma, a.S_in, a.z_in, a.S_out, a.z_out, p.F, p.P, p.G, p.NG, p.d,
                      blocks_per_slab, p.carry_offset(), a.keep_frames);
   return hipGetLastError();

@@ -118,8 +118,8 @@ gla_status launched(hipError_t e, const char *what) {
 }
 
 // ---- optional event timing of every launch (gla_profile_begin/end) ----
-enum Kind { kKindKv = 0, kKindScan = 1, kKindReadout = 2, kNumKinds = 3 };
-const char *const kKindNames[kNumKinds] = {"kv", "scan", "readout"};
+enum Kind { kKindKv = 0, kKindCarry = 1, kKindReadout = 2, kNumKinds = 3 };
+const char *const kKindNames[kNumKinds] = {"kv", "carry", "readout"};
 
 struct Profiler {
   std::mutex mu;
@@ -221,8 +221,8 @@ gla_status run_framecausal(const void *q, const void *k, const void *v, const vo
   if (F > 0)
     GLA_TRY(launched(
         timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, gamma, wsf}, s); }), "kv"));
-  const ScanArgs sa{wsf, gamma, S_in, z_in, S_out, z_out, outputs ? 1 : 0};
-  GLA_TRY(launched(timed(kKindScan, s, [&] { return launch_scan(p, sa, s); }), "scan"));
+  const CarryArgs sa{wsf, gamma, S_in, z_in, S_out, z_out, outputs ? 1 : 0};
+  GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, sa, s); }), "carry"));
   if (outputs && have_tokens)
     GLA_TRY(launched(timed(kKindReadout, s,
                            [&] {
@@ -348,8 +348,8 @@ GLA_EXPORT gla_status gla_fwd_bidir(const void *q, const void *k, const void *v,
   GLA_TRY(launched(
       timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, nullptr, wsf}, s); }),
       "kv"));
-  const ScanArgs sa{wsf, nullptr, nullptr, nullptr, nullptr, nullptr, 1};
-  GLA_TRY(launched(timed(kKindScan, s, [&] { return launch_scan(p, sa, s); }), "scan"));
+  const CarryArgs sa{wsf, nullptr, nullptr, nullptr, nullptr, nullptr, 1};
+  GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, sa, s); }), "carry"));
   GLA_TRY(launched(
       timed(kKindReadout, s,
             [&] {

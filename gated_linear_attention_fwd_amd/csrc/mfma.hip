@@ -52,6 +52,21 @@ constexpr int kThreads = 256;
 #ifndef GLA_RO_NT_STORES
 #define GLA_RO_NT_STORES 1
 #endif
+#ifndef GLA_RO_XCD_REMAP
+#define GLA_RO_XCD_REMAP 1
+#endif
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
+// Renumbering so that XCD x runs a contiguous range of work items keeps
+// neighbouring frames (which share their group's carried state) on one L2.
+// A bijection on [0, n): the first 8 * floor(n / 8) ids are remapped, the
+// remainder keep their id.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t w, int64_t n) {
+  const int64_t per = n / kXcds;
+  if (w >= per * kXcds) return w;
+  return (w % kXcds) * per + w / kXcds;
+}
 
 template <bool kNt>
 __device__ __forceinline__ uint4 ld_stream16(const uint4 *p) {
@@ -364,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
   const int h = lane >> 5;
   const int mb = wave % C::MB;
   const int tg = wave / C::MB;
-  const int64_t wg = blockIdx.x;
+  const int64_t wg = GLA_RO_XCD_REMAP ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
   const int r = (int)(wg % R);
   const int f = (int)((wg / R) % F);
   const int64_t bh = wg / ((int64_t)R * F);

@@ -63,7 +63,7 @@ struct KvArgs {
   float *ws;
 };
 
-struct ScanArgs {
+struct CarryArgs {
   float *ws;
   const float *gamma;  // NULL: no decay (bidirectional)
   const float *S_in;   // NULL: zero carried state
@@ -91,7 +91,7 @@ __device__ __forceinline__ float carry_weight(const float *gamma_slab, int f, in
 }
 
 hipError_t launch_kv(const Plan &p, int dtype, Path path, const KvArgs &a, hipStream_t s);
-hipError_t launch_scan(const Plan &p, const ScanArgs &a, hipStream_t s);
+hipError_t launch_carry(const Plan &p, const CarryArgs &a, hipStream_t s);
 hipError_t launch_readout(const Plan &p, int dtype, Path path, const ReadoutArgs &a,
                           hipStream_t s);
 

@@ -114,7 +114,7 @@ int gla_version(void);
  * Between gla_profile_begin and gla_profile_end, every kernel launched by the
  * entry points (on any stream, from any thread) is bracketed by a pair of HIP
  * events recorded on its stream. gla_profile_end waits for those events and
- * returns, per kernel kind ("kv", "scan", "readout"), the number of launches
+ * returns, per kernel kind ("kv", "carry", "readout"), the number of launches
  * and their summed event time. At most max_launches launches are timed; later
  * ones run untimed. Not meant to overlap with itself: one session at a time.
  * gla_profile_begin creates 2 * max_launches HIP events (max_launches must be
