@@ -33,7 +33,7 @@ constexpr int64_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several t
 constexpr int64_t kMinPartTokens = 128;
 constexpr int64_t kMinSplitTokens = 64;
 constexpr int64_t kTokenAlign = 32;
-constexpr int64_t kMaxGroupFrames = 8;
+constexpr int64_t kMaxGroupFrames = 8;  // the kv kernels hold up to 8 decays
 // kv workgroups resident at once on 256 CUs (4 per CU at d <= 64): grouping
 // frames down to about this many workgroups removes the tail of a second wave.
 constexpr int64_t kResidentKvWorkgroups = 1024;
@@ -260,7 +260,8 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
     if (can_group && units >= 2 * kTargetWorkgroups)
       p.G = (int)std::min<int64_t>(kMaxGroupFrames, ceil_div(units, kResidentKvWorkgroups));
     if (const char *e = getenv("GLA_FRAMES_PER_GROUP"))
-      if (can_group && atoi(e) >= 1) p.G = std::min(atoi(e), std::max(F, 1));
+      if (can_group && atoi(e) >= 1)
+        p.G = (int)std::min<int64_t>({(int64_t)atoi(e), (int64_t)std::max(F, 1), kMaxGroupFrames});
   } else {
     p.P = p.R = 1;
     p.part_len = p.read_len = round_up(T, kTokenAlign);

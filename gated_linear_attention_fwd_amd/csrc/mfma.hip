@@ -38,6 +38,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
+constexpr int kMaxGroup = 8;  // most frames per kv workgroup (the plan's limit)
 
 // q, k, v and g are read exactly once and o is written once: nontemporal
 // loads and stores keep that stream from displacing lines the next kernel
@@ -51,6 +52,9 @@ constexpr int kThreads = 256;
 #endif
 #ifndef GLA_RO_NT_STORES
 #define GLA_RO_NT_STORES 1
+#endif
+#ifndef GLA_LDS_BARRIER
+#define GLA_LDS_BARRIER 1
 #endif
 #ifndef GLA_RO_XCD_REMAP
 #define GLA_RO_XCD_REMAP 1
@@ -76,6 +80,21 @@ __device__ __forceinline__ uint4 ld_stream16(const uint4 *p) {
   } else {
     return *p;
   }
+}
+
+// Workgroup barrier for data exchanged through LDS only. __syncthreads() also
+// fences global memory, which on this architecture waits for every
+// outstanding global load and store (vmcnt(0)) -- including the prefetch of
+// the next tile and the stores of the previous one -- before the barrier.
+// Waiting for LDS operations alone (lgkmcnt(0)) is enough for LDS data.
+__device__ __forceinline__ void sync_lds() {
+#if GLA_LDS_BARRIER
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#else
+  __syncthreads();
+#endif
 }
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -223,9 +242,105 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
 #pragma unroll
   for (int e = 0; e < kSt; ++e) st[e] = 0.f;
 
+  // the group's decays, loaded once up front (a load per frame would stall
+  // every frame's write-out for a full memory latency)
+  float gms[C::kGroups ? kMaxGroup : 1];
+#pragma unroll
+  for (int e = 0; e < (C::kGroups ? kMaxGroup : 1); ++e)
+    gms[e] = (e > 0 && e < nf) ? gamma[bh * F + f_begin + e] : 0.f;
+
+  // After a frame's last chunk, frame_close() folds U_f into the running state
+  // (registers; z through an LDS sum), and store_state() writes the slot. The
+  // stores are issued one chunk later, right after that chunk's loads have
+  // been waited for: vmcnt counts loads and stores alike, so stores issued
+  // behind an outstanding prefetch would make its wait include them.
+  auto frame_close = [&](int fi) {
+    float gm = 0.f;
+#pragma unroll
+    for (int e = 1; e < (C::kGroups ? kMaxGroup : 1); ++e) gm = (fi == e) ? gms[e] : gm;
+    if constexpr (C::kSplitTokens) {
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b) {
+          sync_lds();
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[wave * 1024 + r * 64 + lane] = acc[a][b][r];
+          sync_lds();
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int idx = tid + kThreads * e4;
+            const float sum = red[idx] + red[1024 + idx] + red[2048 + idx] + red[3072 + idx];
+            float &sv = st[(a * C::TM + b) * 4 + e4];
+            sv = fmaf(gm, sv, sum);  // kSplitTokens implies kGroups
+          }
+        }
+    } else if constexpr (C::kGroups) {
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float &run = st[(a * C::TM + b) * 16 + r];
+            run = fmaf(gm, run, acc[a][b][r]);
+          }
+    }
+    // z: sum the thread's 8 features over lanes with the same column piece, then waves
+    float us[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      us[e] = uacc[e];
+#pragma unroll
+      for (int off = C::ROW_CHUNKS; off < 64; off <<= 1) us[e] += __shfl_xor(us[e], off);
+    }
+    sync_lds();  // previous frame's ured reads (and the red rounds) are done
+    if (lane < C::ROW_CHUNKS) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ured[wave * D + lane * 8 + e] = us[e];
+    }
+    sync_lds();
+    if (tid < D)
+      zst = fmaf(gm, zst, ured[tid] + ured[D + tid] + ured[2 * D + tid] + ured[3 * D + tid]);
+  };
+
+  auto store_state = [&](int fi) {
+    float *out = ws + ((bh * F + f_begin + fi) * (int64_t)P + p) * ((int64_t)D * D + D);
+    // Recompute the offsets from an opaque copy of the thread id: hoisted out
+    // of the loop they would stay live in registers.
+    int tidv = tid;
+    asm volatile("" : "+v"(tidv));
+    const int lanev = tidv & 63;
+    if constexpr (C::kSplitTokens) {
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int idx = tidv + kThreads * e4;
+            const int r = idx >> 6, ln = idx & 63;
+            const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+            out[(32 * a + m) * D + 32 * b + (ln & 31)] = st[(a * C::TM + b) * 4 + e4];
+          }
+    } else {
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float sv = C::kGroups ? st[(a * C::TM + b) * 16 + r] : acc[a][b][r];
+            const int m = 8 * (r >> 2) + 4 * (lanev >> 5) + (r & 3);
+            out[(32 * (wm * C::TM + a) + m) * D + 32 * (wn * C::TM + b) + (lanev & 31)] = sv;
+          }
+    }
+    if (tidv < D) out[D * D + tidv] = zst;
+  };
+
+  int pending = -1;  // frame whose slot is still to be written
   if (total > 0) load(0);
   for (int fi = 0; fi < nf; ++fi) {
-    const float gm = fi > 0 ? gamma[bh * F + f_begin + fi] : 0.f;
     if (fi > 0) {
 #pragma unroll
       for (int a = 0; a < C::TM; ++a)
@@ -238,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
     }
     for (int cc = 0; cc < ncf; ++cc) {
       const int ch = fi * ncf + cc;
-      __syncthreads();
+      sync_lds();
 #pragma unroll
       for (int i = 0; i < C::CPT; ++i) {
         const int row = r0 + i * C::ROWS_PER_PASS;
@@ -254,7 +369,11 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
         uacc[6] += lo_bf16(kk.w);
         uacc[7] += hi_bf16(kk.w);
       }
-      __syncthreads();
+      sync_lds();
+      if (pending >= 0) {
+        store_state(pending);
+        pending = -1;
+      }
       if (ch + 1 < total) load(ch + 1);
 
       constexpr int KS_PER_WAVE = C::kSplitTokens ? 1 : 4;
@@ -273,70 +392,11 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
           for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_32x32x16(fa[a], fb[b], acc[a][b]);
       }
     }
-
-    // ---- write the frame's slot: S_loc (blocks of 32 x 32) and z_loc
-    float *out = ws + ((bh * F + f_begin + fi) * (int64_t)P + p) * ((int64_t)D * D + D);
-    // Recompute the write-out offsets from an opaque copy of the thread id each
-    // frame; hoisted out of the frame loop they would stay live in registers.
-    int tidv = tid;
-    asm volatile("" : "+v"(tidv));
-    const int lanev = tidv & 63;
-    if constexpr (C::kSplitTokens) {
-#pragma unroll
-      for (int a = 0; a < C::TM; ++a)
-#pragma unroll
-        for (int b = 0; b < C::TM; ++b) {
-          __syncthreads();
-#pragma unroll
-          for (int r = 0; r < 16; ++r) red[wave * 1024 + r * 64 + lanev] = acc[a][b][r];
-          __syncthreads();
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const int idx = tidv + kThreads * e4;
-            const float sum = red[idx] + red[1024 + idx] + red[2048 + idx] + red[3072 + idx];
-            float &sv = st[(a * C::TM + b) * 4 + e4];
-            sv = fmaf(gm, sv, sum);  // kSplitTokens implies kGroups
-            const int r = idx >> 6, ln = idx & 63;
-            const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-            out[(32 * a + m) * D + 32 * b + (ln & 31)] = sv;
-          }
-        }
-    } else {
-#pragma unroll
-      for (int a = 0; a < C::TM; ++a)
-#pragma unroll
-        for (int b = 0; b < C::TM; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float sv = acc[a][b][r];
-            if constexpr (C::kGroups) {
-              float &run = st[(a * C::TM + b) * 16 + r];
-              run = fmaf(gm, run, sv);
-              sv = run;
-            }
-            const int m = 8 * (r >> 2) + 4 * (lanev >> 5) + (r & 3);
-            out[(32 * (wm * C::TM + a) + m) * D + 32 * (wn * C::TM + b) + (lanev & 31)] = sv;
-          }
-    }
-    // z_loc: sum the thread's 8 features over lanes with the same column piece, then waves
-    float us[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      us[e] = uacc[e];
-#pragma unroll
-      for (int off = C::ROW_CHUNKS; off < 64; off <<= 1) us[e] += __shfl_xor(us[e], off);
-    }
-    __syncthreads();  // previous frame's ured reads are done
-    if (lanev < C::ROW_CHUNKS) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ured[wave * D + lanev * 8 + e] = us[e];
-    }
-    __syncthreads();
-    if (tidv < D) {
-      zst = fmaf(gm, zst, ured[tidv] + ured[D + tidv] + ured[2 * D + tidv] + ured[3 * D + tidv]);
-      out[D * D + tidv] = zst;
-    }
+    frame_close(fi);
+    if (pending >= 0 || ncf == 0) store_state(fi);  // no chunk follows to carry the store
+    else pending = fi;
   }
+  if (pending >= 0) store_state(pending);
 }
 
 // ---------------------------------------------------------------------------
@@ -442,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
   const int nblk = (L + C::BLK - 1) / C::BLK;
   load(0);
   for (int blk = 0; blk < nblk; ++blk) {
-    __syncthreads();  // the previous block's o rows have been read out of gtile
+    sync_lds();  // the previous block's o rows have been read out of gtile
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = r0 + i * C::ROWS_PER_PASS;
@@ -461,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
       for (int off = 1; off < C::ROW_CHUNKS; off <<= 1) dp += __shfl_xor(dp, off);
       if (c == 0) den_s[row] = dp;
     }
-    __syncthreads();
+    sync_lds();
     if (blk + 1 < nblk) load(blk + 1);
 
     f32x16 acc;
@@ -489,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
       ow.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
       *cell = ow;
     }
-    __syncthreads();
+    sync_lds();
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = r0 + i * C::ROWS_PER_PASS;
