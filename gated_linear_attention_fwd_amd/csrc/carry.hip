@@ -11,10 +11,11 @@
 //   carry_0 = S_in (or 0)
 //   carry_{g+1} = S_loc_{last frame of g} + (prod_{m in g} gamma_m) * carry_g
 //
-// and S_out = carry_{NG}. With several parts per frame (then G = 1) the parts
-// of a frame are summed here in a fixed order, and the sum is left in part 0
-// for the readout. Bidirectional mode is the same walk with one frame and no
-// decay.
+// and S_out = carry_{NG}. With one frame per group (G = 1) no carries are
+// kept: the walk is the plain scan S_f = gamma_f S_{f-1} + U_f, and S_f is
+// written in place over the frame's slot (part 0, after summing the frame's
+// parts in a fixed order), which is all the readout needs. Bidirectional mode
+// is that walk with one frame and no decay.
 //
 // One thread owns one of the d*d + d state elements of one slab. The chain of
 // FMAs is serial, the loads are not: a batch of groups is loaded first, then
@@ -68,11 +69,9 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     for (int j = 0; j < kGroupBatch; ++j) {
       const int grp = g0 + j;
       if (grp < NG) {
-        if (keep_frames) {
-          carry[(int64_t)grp * E] = s;
-          if (P > 1) slots[(int64_t)(min(F, (grp + 1) * G) - 1) * frame_stride] = x[j];
-        }
+        if (keep_frames && G > 1) carry[(int64_t)grp * E] = s;
         s = fmaf(w[j], s, x[j]);
+        if (keep_frames && G == 1) slots[(int64_t)grp * frame_stride] = s;
       }
     }
   }

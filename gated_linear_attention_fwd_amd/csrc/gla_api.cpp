@@ -254,8 +254,7 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
     p.read_len = round_up(ceil_div(T, R), kTokenAlign);
     p.R = (int)ceil_div(T, p.read_len);
     // Enough frames for a full grid: group consecutive frames in one kv workgroup.
-    // (The d = 128 matrix-core kernel keeps no running state and so runs one
-    // frame per workgroup.)
+    // (The d = 128 matrix-core kernel keeps no running state: one frame each.)
     const bool can_group = p.P == 1 && d <= 64;
     if (can_group && units >= 2 * kTargetWorkgroups)
       p.G = (int)std::min<int64_t>(kMaxGroupFrames, ceil_div(units, kResidentKvWorkgroups));
@@ -273,7 +272,8 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
   const int64_t E = p.state_elems();
   if (BH * ceil_div(E, 256) >= max_grid) return false;
   p.NG = (int)ceil_div(F, p.G);
-  p.ws_bytes = (size_t)round_up((units * p.P + BH * p.NG) * E * 4, 256);
+  // carries are kept only for groups of several frames (G == 1 scans in place)
+  p.ws_bytes = (size_t)round_up((units * p.P + (p.G > 1 ? BH * p.NG : 0)) * E * 4, 256);
   *plan = p;
   return true;
 }

@@ -53,9 +53,6 @@ constexpr int kMaxGroup = 8;  // most frames per kv workgroup (the plan's limit)
 #ifndef GLA_RO_NT_STORES
 #define GLA_RO_NT_STORES 1
 #endif
-#ifndef GLA_LDS_BARRIER
-#define GLA_LDS_BARRIER 1
-#endif
 #ifndef GLA_RO_XCD_REMAP
 #define GLA_RO_XCD_REMAP 1
 #endif
@@ -88,13 +85,9 @@ __device__ __forceinline__ uint4 ld_stream16(const uint4 *p) {
 // the next tile and the stores of the previous one -- before the barrier.
 // Waiting for LDS operations alone (lgkmcnt(0)) is enough for LDS data.
 __device__ __forceinline__ void sync_lds() {
-#if GLA_LDS_BARRIER
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-#else
-  __syncthreads();
-#endif
 }
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -139,8 +132,9 @@ struct KvCfg {
   // its blocks outright and no cross-wave sum is needed.
   static constexpr bool kSplitTokens = (D == 32);
   static constexpr int TM = kSplitTokens ? MB : MB / 2;
-  // running decayed state kept across the frames of a group (G > 1 happens
-  // only for d <= 64)
+  // running decayed state kept across the frames of a group; at d = 128 it
+  // would need 64 more registers per lane (1 wave/SIMD), so d = 128 runs one
+  // frame per workgroup
   static constexpr bool kGroups = (D <= 64);
   static constexpr int ROW_CHUNKS = D / 8;                 // 16-byte pieces per row
   static constexpr int CPT = CH * ROW_CHUNKS / kThreads;   // pieces per thread per array
@@ -454,22 +448,36 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
   constexpr int64_t E = (int64_t)D * D + D;
   const int NG = (F + G - 1) / G;
   const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;
+  // G == 1: the carry kernel has completed S_f in place (no carries kept)
+  const bool has_carry = G > 1;
   const float *Cg = ws + carry_offset + (bh * NG + f / G) * E;
   const float w = carry_weight(gamma ? gamma + bh * F : nullptr, f, G);
   bf16x8 ahi[C::KS], alo[C::KS];
+  // S = hi + lo, both bf16: returns hi in the low half, lo in the high half
+  auto split = [&](float sv) -> uint32_t {
+    const uint16_t sh = f32_to_bf16_rne(sv);
+    return (uint32_t)sh | ((uint32_t)f32_to_bf16_rne(sv - bf16_to_f32(sh)) << 16);
+  };
   {
     const int jcol = 32 * mb + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       i16x8 hv, lv;
+      if (has_carry) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int idx = (16 * ks + 8 * h + e) * D + jcol;
-        const float sv = fmaf(w, Cg[idx], Sg[idx]);
-        const uint16_t sh = f32_to_bf16_rne(sv);
-        const uint16_t sl = f32_to_bf16_rne(sv - bf16_to_f32(sh));
-        hv[e] = (short)sh;
-        lv[e] = (short)sl;
+        for (int e = 0; e < 8; ++e) {
+          const int idx = (16 * ks + 8 * h + e) * D + jcol;
+          const uint32_t hl = split(fmaf(w, Cg[idx], Sg[idx]));
+          hv[e] = (short)(hl & 0xFFFFu);
+          lv[e] = (short)(hl >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t hl = split(Sg[(16 * ks + 8 * h + e) * D + jcol]);
+          hv[e] = (short)(hl & 0xFFFFu);
+          lv[e] = (short)(hl >> 16);
+        }
       }
       ahi[ks] = __builtin_bit_cast(bf16x8, hv);
       alo[ks] = __builtin_bit_cast(bf16x8, lv);
@@ -480,7 +488,8 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
   const int r0 = tid / C::ROW_CHUNKS;
   float zc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zc[e] = fmaf(w, Cg[D * D + 8 * c + e], Sg[D * D + 8 * c + e]);
+  for (int e = 0; e < 8; ++e)
+    zc[e] = has_carry ? fmaf(w, Cg[D * D + 8 * c + e], Sg[D * D + 8 * c + e]) : Sg[D * D + 8 * c + e];
 
   const uint4 *qb = reinterpret_cast<const uint4 *>(q + row0 * D);
   const uint4 *gb = reinterpret_cast<const uint4 *>(g + row0 * D);

@@ -13,10 +13,12 @@
 //   2. carry   one thread per (slab, state element): walks the groups in order,
 //              carry_0 = S_in (or 0), carry_{g+1} = S_loc_{last of g} +
 //              (prod of gamma over g) carry_g, and stores carry_g per group;
-//              with several parts per frame (G = 1) it also sums the parts;
+//              with one frame per group (G = 1) it is the plain scan, summing
+//              the frame's parts and leaving S_f in place in the slot;
 //   3. readout one workgroup per (slab, frame, split): S_f = S_loc_f +
-//              (prod_{m=first of group}^{f} gamma_m) carry_g, then phi(q) S_f,
-//              phi(q) z_f, the normalise-and-gate epilogue and the store of o.
+//              (prod_{m=first of group}^{f} gamma_m) carry_g (G > 1) or the
+//              slot itself (G = 1), then phi(q) S_f, phi(q) z_f, the
+//              normalise-and-gate epilogue and the store of o.
 //
 // Groups cut the workspace traffic of the scan (only one state per group is
 // chained) and parts give small problems enough workgroups; the partition
@@ -42,7 +44,7 @@ struct Plan {
   int NG = 0;            // groups per slab, ceil(F / G)
   size_t ws_bytes = 0;   // workspace bytes, 256-byte rounded:
                          //   slots  BH * F * P  states of d*d + d floats
-                         //   carry  BH * NG     states of d*d + d floats
+                         //   carry  BH * NG     states of d*d + d floats (G > 1 only)
 
   int64_t state_elems() const { return (int64_t)d * d + d; }
   int64_t carry_offset() const { return BH * F * (int64_t)P * state_elems(); }  // floats

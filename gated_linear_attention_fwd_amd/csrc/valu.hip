@@ -118,8 +118,9 @@ __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
   constexpr int64_t E = (int64_t)D * D + D;
   const int NG = (F + G - 1) / G;
   const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;
-  const float *Cg = ws + carry_offset + (bh * NG + f / G) * E;
-  const float w = carry_weight(gamma ? gamma + bh * F : nullptr, f, G);
+  // G == 1: the carry kernel has completed S_f in place (no carries kept)
+  const float *Cg = G > 1 ? ws + carry_offset + (bh * NG + f / G) * E : Sg;
+  const float w = G > 1 ? carry_weight(gamma ? gamma + bh * F : nullptr, f, G) : 0.f;
   if (kSInLds)
     for (int e = tid; e < D * D; e += kThreads) sS[e] = fmaf(w, Cg[e], Sg[e]);
   for (int e = tid; e < D; e += kThreads) sz[e] = fmaf(w, Cg[D * D + e], Sg[D * D + e]);

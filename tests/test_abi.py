@@ -60,12 +60,12 @@ def test_workspace_sizes(lib):
     E = 64 * 64 + 64
     assert gla.gla_fwd_framecausal_workspace(1, 32, 241, 920, 64) == (32 * 241 + 32 * 31) * E * 4
     assert gla.gla_state_carry_workspace(1, 32, 241, 920, 64) == (32 * 241 + 32 * 31) * E * 4
-    # d = 128 runs one frame per group: a carry per frame
+    # d = 128 runs one frame per group: the scan completes each state in place
     E2 = 128 * 128 + 128
-    assert gla.gla_fwd_framecausal_workspace(2, 40, 30, 920, 128) == (80 * 30 * 2) * E2 * 4
+    assert gla.gla_fwd_framecausal_workspace(2, 40, 30, 920, 128) == 80 * 30 * E2 * 4
     # small problems are cut into parts to fill the GPU: the size grows accordingly
     small = gla.gla_fwd_framecausal_workspace(1, 8, 5, 256, 64)
-    assert small > 8 * 5 * 4160 * 4 * 2 and small % 256 == 0
+    assert small > 8 * 5 * 4160 * 4 and small % 256 == 0
     assert gla.gla_fwd_bidir_workspace(1, 32, 19320, 64) % (4160 * 4) == 0
     assert gla.gla_fwd_bidir_workspace(1, 32, 19320, 64) > 32 * 4160 * 4
     # empty and invalid sizes need nothing
