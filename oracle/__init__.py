@@ -44,6 +44,15 @@ _lib = None
 BIDIR = 0
 FRAMECAUSAL = 1
 
+
+class Rope(ctypes.Structure):
+    """3D rotary positions: token l of frame f sits at (frame_offset + f,
+    l // grid_w, l % grid_w); pairs of features turn with t, y, x in sections of
+    dim_t, dim_h, dim_w features; pair j of an m-pair section by pos * theta**(-j/m)."""
+    _fields_ = [("grid_h", ctypes.c_int), ("grid_w", ctypes.c_int),
+                ("frame_offset", ctypes.c_int), ("dim_t", ctypes.c_int),
+                ("dim_h", ctypes.c_int), ("dim_w", ctypes.c_int), ("theta", ctypes.c_double)]
+
 _DT = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.float64): 2}
 
 
@@ -75,6 +84,11 @@ def _load():
     for fn in (lib.gla_oracle_recurrent, lib.gla_oracle_quadratic, lib.gla_oracle_chunked):
         fn.restype = ctypes.c_int
     lib.gla_oracle_max_threads.restype = ctypes.c_int
+    lib.gla_oracle_rope_recurrent.argtypes = common + [ctypes.POINTER(Rope), ctypes.c_int]
+    lib.gla_oracle_rope_recurrent.restype = ctypes.c_int
+    lib.gla_oracle_rope_quadratic.argtypes = common[:10] + common[12:] + [
+        ctypes.POINTER(Rope), ctypes.c_int]
+    lib.gla_oracle_rope_quadratic.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -157,6 +171,63 @@ def chunked(mode, q, k, v, g, gamma=None, S_in=None, z_in=None, F=None, T=None,
     """Chunked form C with chunk length ``C`` (the last chunk of a frame may be shorter)."""
     return _run(_load().gla_oracle_chunked, mode, q, k, v, g, gamma, S_in, z_in, F, T, eps,
                 outputs, (int(C),), nthreads)
+
+
+def _rope(rope, T, d):
+    r = rope if isinstance(rope, Rope) else Rope(**rope)
+    if r.grid_h * r.grid_w != T or r.dim_t + r.dim_h + r.dim_w != d:
+        raise ValueError("rope grid must cover T tokens and its sections d features")
+    if any(x % 2 for x in (r.dim_t, r.dim_h, r.dim_w)):
+        raise ValueError("rope sections must be even")
+    return r
+
+
+def rope_recurrent(mode, q, k, v, g, gamma=None, S_in=None, z_in=None, F=None, T=None,
+                   eps=1e-6, rope=None, outputs=True, nthreads=0):
+    """Recurrent form with 3D rotary positions (numerator rotated, normaliser not).
+
+    In bidirectional mode F and T give the positions (N = F * T)."""
+    lib = _load()
+    if mode == BIDIR:
+        N = np.shape(k)[2]
+        Fp, Tp = (F, T) if F else (1, N)
+        q_, k_, v_, g_, _, _, _, o, S_out, z_out, B, H, _, _, d, dt = _prep(
+            BIDIR, q, k, v, g, None, None, None, None, None, outputs)
+        r = _rope(rope, Tp, d)
+        lib.gla_oracle_rope_recurrent(BIDIR, dt, _ptr(q_), _ptr(k_), _ptr(v_), _ptr(g_), None,
+                                      None, None, _ptr(o), _ptr(S_out), _ptr(z_out), B, H, Fp, Tp,
+                                      d, float(eps), ctypes.byref(r), int(nthreads))
+        return o, S_out, z_out
+    (q_, k_, v_, g_, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d, dt) = _prep(
+        mode, q, k, v, g, gamma, S_in, z_in, F, T, outputs)
+    r = _rope(rope, T, d)
+    lib.gla_oracle_rope_recurrent(mode, dt, _ptr(q_), _ptr(k_), _ptr(v_), _ptr(g_), _ptr(gamma),
+                                  _ptr(S_in), _ptr(z_in), _ptr(o), _ptr(S_out), _ptr(z_out), B, H,
+                                  F, T, d, float(eps), ctypes.byref(r), int(nthreads))
+    return o, S_out, z_out
+
+
+def rope_quadratic(mode, q, k, v, g, gamma=None, S_in=None, z_in=None, F=None, T=None,
+                   eps=1e-6, rope=None, nthreads=0):
+    """Quadratic form with 3D rotary positions; returns o only."""
+    lib = _load()
+    if mode == BIDIR:
+        N = np.shape(k)[2]
+        Fp, Tp = (F, T) if F else (1, N)
+        q_, k_, v_, g_, _, _, _, o, _, _, B, H, _, _, d, dt = _prep(
+            BIDIR, q, k, v, g, None, None, None, None, None, True)
+        r = _rope(rope, Tp, d)
+        lib.gla_oracle_rope_quadratic(BIDIR, dt, _ptr(q_), _ptr(k_), _ptr(v_), _ptr(g_), None,
+                                      None, None, _ptr(o), B, H, Fp, Tp, d, float(eps),
+                                      ctypes.byref(r), int(nthreads))
+        return o
+    (q_, k_, v_, g_, gamma, S_in, z_in, o, _, _, B, H, F, T, d, dt) = _prep(
+        mode, q, k, v, g, gamma, S_in, z_in, F, T, True)
+    r = _rope(rope, T, d)
+    lib.gla_oracle_rope_quadratic(mode, dt, _ptr(q_), _ptr(k_), _ptr(v_), _ptr(g_), _ptr(gamma),
+                                  _ptr(S_in), _ptr(z_in), _ptr(o), B, H, F, T, d, float(eps),
+                                  ctypes.byref(r), int(nthreads))
+    return o
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

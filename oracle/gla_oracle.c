@@ -351,3 +351,169 @@ int gla_oracle_chunked(int mode, int dt, const void *q, const void *k, const voi
   }
   return used;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Rotary (3D RoPE) variant                                                  */
+/* ------------------------------------------------------------------------ */
+/* The SANA-Video ICLR 2026 oral talk (passage on temporal modeling) adds 3D
+ * RoPE to the linear attention; the pages do not say where it sits relative
+ * to the feature map. Reading taken (RoFormer's form of rotary linear
+ * attention): the numerator uses rotated features R_t phi(q_t) and R_s phi(k_s),
+ * the normaliser keeps the unrotated phi(q_t) . phi(k_s), so it stays positive:
+ *
+ *   o_t = sigma(g_t) (.) sum_s w_ts (R_t phi(q_t))^T (R_s phi(k_s)) v_s
+ *                       / (sum_s w_ts phi(q_t)^T phi(k_s) + eps)
+ *
+ * Token n of the call (frame f = n / T, in-frame index l = n % T) sits at
+ * (t, y, x) = (frame_offset + f, l / grid_w, l % grid_w). Features are rotated
+ * in adjacent pairs (2p, 2p+1); the first dim_t/2 pairs turn with t, the next
+ * dim_h/2 with y, the last dim_w/2 with x. Within a section of m pairs, pair j
+ * turns by angle pos * theta^(-j/m). */
+typedef struct orc_rope {
+  int grid_h, grid_w, frame_offset, dim_t, dim_h, dim_w;
+  double theta;
+} orc_rope;
+
+static void rope_rotate(double *x, int d, int T, size_t n, const orc_rope *r) {
+  const int f = (int)(n / (size_t)T);
+  const int l = (int)(n % (size_t)T);
+  const double pt = (double)(r->frame_offset + f);
+  const double py = (double)(l / r->grid_w);
+  const double px = (double)(l % r->grid_w);
+  const int Pt = r->dim_t / 2, Ph = r->dim_h / 2, Pw = r->dim_w / 2;
+  for (int p = 0; p < d / 2; ++p) {
+    double pos;
+    int j, m;
+    if (p < Pt) {
+      pos = pt; j = p; m = Pt;
+    } else if (p < Pt + Ph) {
+      pos = py; j = p - Pt; m = Ph;
+    } else {
+      pos = px; j = p - Pt - Ph; m = Pw;
+    }
+    const double ang = pos * pow(r->theta, -(double)j / (double)m);
+    const double c = cos(ang), s = sin(ang);
+    const double a = x[2 * p], b = x[2 * p + 1];
+    x[2 * p] = a * c - b * s;
+    x[2 * p + 1] = a * s + b * c;
+  }
+}
+
+/* Recurrent form with rotation: the state collects rotated keys, the
+ * normaliser unrotated ones. Arguments as gla_oracle_recurrent, plus the
+ * rotation (rope must not be NULL; T must equal grid_h * grid_w). */
+int gla_oracle_rope_recurrent(int mode, int dt, const void *q, const void *k, const void *v,
+                              const void *g, const double *gamma, const double *S_in,
+                              const double *z_in, double *o, double *S_out, double *z_out, int B,
+                              int H, int F, int T, int d, double eps, const orc_rope *rope,
+                              int nthreads) {
+  const long nbh = (long)B * H;
+  const size_t N = (size_t)F * T;
+  const int used = set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < nbh; ++bh) {
+    const size_t base = (size_t)bh * N * d;
+    const size_t dd = (size_t)d * d;
+    double *S = (double *)calloc(dd, sizeof(double));
+    double *z = (double *)calloc((size_t)d, sizeof(double));
+    double *fk = (double *)malloc((size_t)d * sizeof(double));
+    double *rk = (double *)malloc((size_t)d * sizeof(double));
+    double *fq = (double *)malloc((size_t)d * sizeof(double));
+    double *rq = (double *)malloc((size_t)d * sizeof(double));
+    if (mode == ORC_FRAMECAUSAL && S_in) memcpy(S, S_in + (size_t)bh * dd, dd * sizeof(double));
+    if (mode == ORC_FRAMECAUSAL && z_in) memcpy(z, z_in + (size_t)bh * d, (size_t)d * sizeof(double));
+    /* bidirectional: one frame holding all tokens (positions still use T) */
+    const int nframes = (mode == ORC_FRAMECAUSAL) ? F : 1;
+    const size_t per = (mode == ORC_FRAMECAUSAL) ? (size_t)T : N;
+    for (int f = 0; f < nframes; ++f) {
+      if (mode == ORC_FRAMECAUSAL) {
+        const double gm = gamma[(size_t)bh * F + f];
+        for (size_t e = 0; e < dd; ++e) S[e] *= gm;
+        for (int i = 0; i < d; ++i) z[i] *= gm;
+      }
+      for (size_t t = 0; t < per; ++t) {
+        const size_t n = (size_t)f * per + t;
+        const size_t row = base + n * d;
+        for (int i = 0; i < d; ++i) rk[i] = fk[i] = relu(ld(k, dt, row + i));
+        rope_rotate(rk, d, T, n, rope);
+        for (int i = 0; i < d; ++i) {
+          z[i] += fk[i];
+          for (int j = 0; j < d; ++j) S[(size_t)i * d + j] += rk[i] * ld(v, dt, row + j);
+        }
+      }
+      if (!o) continue;
+      for (size_t t = 0; t < per; ++t) {
+        const size_t n = (size_t)f * per + t;
+        const size_t row = base + n * d;
+        for (int i = 0; i < d; ++i) rq[i] = fq[i] = relu(ld(q, dt, row + i));
+        rope_rotate(rq, d, T, n, rope);
+        double den = 0.0;
+        for (int i = 0; i < d; ++i) den += fq[i] * z[i];
+        for (int j = 0; j < d; ++j) {
+          double num = 0.0;
+          for (int i = 0; i < d; ++i) num += rq[i] * S[(size_t)i * d + j];
+          o[row + j] = sigm(ld(g, dt, row + j)) * num / (den + eps);
+        }
+      }
+    }
+    if (S_out) memcpy(S_out + (size_t)bh * dd, S, dd * sizeof(double));
+    if (z_out) memcpy(z_out + (size_t)bh * d, z, (size_t)d * sizeof(double));
+    free(S); free(z); free(fk); free(rk); free(fq); free(rq);
+  }
+  return used;
+}
+
+/* Quadratic form with rotation: explicit pairwise weights, no state. */
+int gla_oracle_rope_quadratic(int mode, int dt, const void *q, const void *k, const void *v,
+                              const void *g, const double *gamma, const double *S_in,
+                              const double *z_in, double *o, int B, int H, int F, int T, int d,
+                              double eps, const orc_rope *rope, int nthreads) {
+  const size_t N = (size_t)F * T;
+  const long ntask = (long)B * H * (long)N;
+  const int used = set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+  for (long task = 0; task < ntask; ++task) {
+    const long bh = task / (long)N;
+    const size_t t = (size_t)(task % (long)N);
+    const int ft = (int)(t / T);
+    const size_t base = (size_t)bh * N * d;
+    const double *gm = gamma ? gamma + (size_t)bh * F : NULL;
+    double *fq = (double *)malloc((size_t)d * sizeof(double));
+    double *rq = (double *)malloc((size_t)d * sizeof(double));
+    double *fk = (double *)malloc((size_t)d * sizeof(double));
+    double *rk = (double *)malloc((size_t)d * sizeof(double));
+    double *num = (double *)calloc((size_t)d, sizeof(double));
+    double den = 0.0;
+    for (int i = 0; i < d; ++i) rq[i] = fq[i] = relu(ld(q, dt, base + t * d + i));
+    rope_rotate(rq, d, T, t, rope);
+    for (size_t s = 0; s < N; ++s) {
+      const int fs = (int)(s / T);
+      const double w = (mode == ORC_BIDIR) ? 1.0 : pair_decay(gm, fs, ft);
+      if (w == 0.0 && fs > ft) continue;
+      for (int i = 0; i < d; ++i) rk[i] = fk[i] = relu(ld(k, dt, base + s * d + i));
+      rope_rotate(rk, d, T, s, rope);
+      double an = 0.0, ad = 0.0;
+      for (int i = 0; i < d; ++i) {
+        an += rq[i] * rk[i];
+        ad += fq[i] * fk[i];
+      }
+      den += w * ad;
+      for (int j = 0; j < d; ++j) num[j] += w * an * ld(v, dt, base + s * d + j);
+    }
+    if (mode == ORC_FRAMECAUSAL && S_in) {
+      const double c = carry_decay(gm, ft);
+      for (int j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += rq[i] * S_in[(size_t)bh * d * d + (size_t)i * d + j];
+        num[j] += c * acc;
+      }
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += fq[i] * z_in[(size_t)bh * d + i];
+      den += c * acc;
+    }
+    for (int j = 0; j < d; ++j)
+      o[base + t * d + j] = sigm(ld(g, dt, base + t * d + j)) * num[j] / (den + eps);
+    free(fq); free(rq); free(fk); free(rk); free(num);
+  }
+  return used;
+}
