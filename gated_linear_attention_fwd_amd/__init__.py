@@ -12,6 +12,11 @@ Entry points (same names as the C ABI):
 * :func:`gla_fwd_framecausal` -- frame-causal attention with per-frame decay and
   an optional carried state (the block KV cache)
 * :func:`gla_state_carry` -- the carried state after more frames, from k, v only
+* :func:`gla_fwd_bidir_ex`, :func:`gla_fwd_framecausal_ex`,
+  :func:`gla_state_carry_ex` -- the same on any [B, H, N, d]-shaped view whose
+  feature axis is contiguous (e.g. ``x.transpose(1, 2)`` of a [B, N, H, d]
+  tensor, or slices of a fused [B, N, 3, H, d] projection), with optional 3D
+  rotary positions (:class:`Rope3D`)
 * ``gla_*_workspace`` -- workspace sizes in bytes
 
 The operation is the gated linear attention token mixer of "SANA-Video 2.0:
@@ -29,9 +34,11 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "GlaError", "gla_fwd_bidir", "gla_fwd_framecausal", "gla_state_carry",
+    "GlaError", "Rope3D", "gla_fwd_bidir", "gla_fwd_framecausal", "gla_state_carry",
+    "gla_fwd_bidir_ex", "gla_fwd_framecausal_ex", "gla_state_carry_ex",
     "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace", "gla_state_carry_workspace",
-    "library_path", "load_library", "profile_begin", "profile_end",
+    "gla_fwd_bidir_ex_workspace", "library_path", "load_library", "profile_begin",
+    "profile_end",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +60,26 @@ class GlaError(RuntimeError):
 class _KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 16), ("launches", ctypes.c_int),
                 ("total_ms", ctypes.c_double)]
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class Rope3D(ctypes.Structure):
+    """3D rotary positions (``gla_rope3d``): token l of frame f sits at
+    (frame_offset + f, l // grid_w, l % grid_w); feature pairs form sections of
+    dim_t, dim_h and dim_w features turning with each axis, pair j of an m-pair
+    section by pos * theta ** (-j / m)."""
+    _fields_ = [("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("frame_offset", ctypes.c_int32), ("dim_t", ctypes.c_int32),
+                ("dim_h", ctypes.c_int32), ("dim_w", ctypes.c_int32),
+                ("theta", ctypes.c_double)]
+
+    def __init__(self, grid_h: int, grid_w: int, dim_t: int, dim_h: int, dim_w: int,
+                 theta: float = 10000.0, frame_offset: int = 0):
+        super().__init__(grid_h, grid_w, frame_offset, dim_t, dim_h, dim_w, theta)
 
 
 def library_path() -> str:
@@ -84,6 +111,18 @@ def load_library():
     lib.gla_state_carry.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                     sz, vp]
     lib.gla_state_carry.restype = i32
+    tp, rp = ctypes.POINTER(_Tensor), ctypes.POINTER(Rope3D)
+    lib.gla_fwd_bidir_ex_workspace.argtypes = [i32, i32, i32, i32, i32, rp]
+    lib.gla_fwd_bidir_ex_workspace.restype = sz
+    lib.gla_fwd_bidir_ex.argtypes = [tp, tp, tp, tp, tp, i32, i32, i32, i32, i32, i32, f32, rp,
+                                     vp, sz, vp]
+    lib.gla_fwd_bidir_ex.restype = i32
+    lib.gla_fwd_framecausal_ex.argtypes = [tp, tp, tp, tp, vp, vp, vp, tp, vp, vp, i32, i32, i32,
+                                           i32, i32, i32, f32, rp, vp, sz, vp]
+    lib.gla_fwd_framecausal_ex.restype = i32
+    lib.gla_state_carry_ex.argtypes = [tp, tp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                       rp, vp, sz, vp]
+    lib.gla_state_carry_ex.restype = i32
     lib.gla_status_string.argtypes = [i32]
     lib.gla_status_string.restype = ctypes.c_char_p
     lib.gla_last_error.argtypes = []
@@ -130,6 +169,41 @@ def _require_device(*ts: Optional[torch.Tensor]) -> torch.device:
         elif t.device != dev:
             raise ValueError("all tensors must be on one device")
     return dev
+
+
+def _require_device_any_layout(*ts: Optional[torch.Tensor]) -> torch.device:
+    """Like _require_device, for the strided entry points: any layout whose
+    last (feature) axis has unit stride."""
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libgla runs on the GPU only; got a tensor on %s" % t.device)
+        if t.dim() == 4 and t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("the feature axis must have unit stride")
+        if t.dim() != 4 and not t.is_contiguous():
+            raise ValueError("gamma and the states must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _view(t: Optional[torch.Tensor]):
+    """gla_tensor of a [B, H, N, d] view (NULL data when absent or empty)."""
+    if t is None:
+        return None
+    sb, sh, sn, _ = t.stride()
+    return ctypes.byref(_Tensor(t.data_ptr() if t.numel() else None, sb, sh, sn))
+
+
+def _rope(rope):
+    if rope is None:
+        return None
+    r = rope if isinstance(rope, Rope3D) else Rope3D(**rope)
+    return ctypes.byref(r)
 
 
 def _qkvg(*ts: Optional[torch.Tensor]):
@@ -245,6 +319,113 @@ def gla_state_carry(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
     _check(lib.gla_state_carry(_ptr(k), _ptr(v), _ptr(gamma), _ptr(S_in), _ptr(z_in),
                                _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt,
                                _ptr(ws), wsb, _stream_handle(stream, dev)))
+    return S_out, z_out
+
+
+def gla_fwd_bidir_ex_workspace(B: int, H: int, F: int, T: int, d: int, rope=None) -> int:
+    return int(load_library().gla_fwd_bidir_ex_workspace(B, H, F, T, d, _rope(rope)))
+
+
+def _frames_of(N: int, rope, F: Optional[int]) -> Tuple[int, int]:
+    """(F, T) of a bidirectional call: T from the rotary grid, else one frame."""
+    if rope is not None:
+        r = rope if isinstance(rope, Rope3D) else Rope3D(**rope)
+        T = r.grid_h * r.grid_w
+        if N % T:
+            raise ValueError("N=%d is not a multiple of the grid's %d tokens" % (N, T))
+        return N // T, T
+    if F:
+        if N % F:
+            raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+        return F, N // F
+    return (1, N) if N else (0, 0)
+
+
+def gla_fwd_bidir_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     eps: float = 1e-6, rope=None, frames: Optional[int] = None,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """gla_fwd_bidir on [B, H, N, d] views of any layout with a contiguous
+    feature axis, optionally with 3D rotary positions (frames of
+    grid_h * grid_w tokens). ``out`` defaults to torch.empty_like(q)."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F, T = _frames_of(N, rope, frames)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != ref.shape or o.dtype != ref.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    dev = _require_device_any_layout(q, k, v, g, o, workspace)
+    ws, wsb = _workspace(lib.gla_fwd_bidir_ex_workspace(B, H, F, T, d, _rope(rope)), dev,
+                         workspace)
+    _check(lib.gla_fwd_bidir_ex(_view(q), _view(k), _view(v), _view(g), _view(o), B, H, F, T, d,
+                                dt, eps, _rope(rope), _ptr(ws), wsb, _stream_handle(stream, dev)))
+    return o
+
+
+def gla_fwd_framecausal_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                           gamma: torch.Tensor, S_in: Optional[torch.Tensor] = None,
+                           z_in: Optional[torch.Tensor] = None, eps: float = 1e-6, rope=None,
+                           out: Optional[torch.Tensor] = None,
+                           S_out: Optional[torch.Tensor] = None,
+                           z_out: Optional[torch.Tensor] = None, return_state: bool = False,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """gla_fwd_framecausal on views of any layout with a contiguous feature
+    axis, optionally with 3D rotary positions. ``out`` defaults to
+    torch.empty_like(q)."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    want_state = return_state or S_out is not None or z_out is not None
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
+    if want_state and z_out is None:
+        z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != ref.shape or o.dtype != ref.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    dev = _require_device_any_layout(q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, workspace)
+    ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
+    _check(lib.gla_fwd_framecausal_ex(_view(q), _view(k), _view(v), _view(g), _ptr(gamma),
+                                      _ptr(S_in), _ptr(z_in), _view(o), _ptr(S_out), _ptr(z_out),
+                                      B, H, F, T, d, dt, eps, _rope(rope), _ptr(ws), wsb,
+                                      _stream_handle(stream, dev)))
+    return (o, S_out, z_out) if want_state else o
+
+
+def gla_state_carry_ex(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+                       S_in: Optional[torch.Tensor] = None, z_in: Optional[torch.Tensor] = None,
+                       S_out: Optional[torch.Tensor] = None, z_out: Optional[torch.Tensor] = None,
+                       rope=None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gla_state_carry on views of any layout, optionally with rotary positions."""
+    lib = load_library()
+    ref = _qkvg(k, v)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    if S_out is None:
+        S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
+    if z_out is None:
+        z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    dev = _require_device_any_layout(k, v, gamma, S_in, z_in, S_out, z_out, workspace)
+    ws, wsb = _workspace(lib.gla_state_carry_workspace(B, H, F, T, d), dev, workspace)
+    _check(lib.gla_state_carry_ex(_view(k), _view(v), _ptr(gamma), _ptr(S_in), _ptr(z_in),
+                                  _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt, _rope(rope),
+                                  _ptr(ws), wsb, _stream_handle(stream, dev)))
     return S_out, z_out
 
 

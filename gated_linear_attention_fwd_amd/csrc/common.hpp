@@ -65,4 +65,39 @@ template <> struct Elem<bf16_t> {
   }
 };
 
+// ---- 3D rotary positions -------------------------------------------------
+// (cos a, sin a) for a = pos * theta^(-j/m), m > 0. The angle is formed and
+// reduced to [-pi, pi] in double precision, so the fp32 sincosf sees a small
+// argument at any position.
+__device__ inline float2 rope_cs(double pos, int j, int m, double log_theta) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  const double a = pos * exp(-((double)j / (double)m) * log_theta);
+  const double r = a - kTwoPi * rint(a * (1.0 / kTwoPi));
+  float s, c;
+  sincosf((float)r, &s, &c);
+  return make_float2(c, s);
+}
+
+// (y, x) = (l / gw, l % gw) for 0 <= l < 2^31: the double quotient is off by
+// at most one, which the remainder test corrects.
+__device__ __forceinline__ void grid_pos(int l, int gw, double inv_gw, int &y, int &x) {
+  int yy = (int)((double)l * inv_gw);
+  int xx = l - yy * gw;
+  if (xx < 0) {
+    --yy;
+    xx += gw;
+  } else if (xx >= gw) {
+    ++yy;
+    xx -= gw;
+  }
+  y = yy;
+  x = xx;
+}
+
+// Rotate the feature pair (a, b) by the angle whose (cos, sin) is cs:
+// (a, b) -> (a cos - b sin, a sin + b cos).
+__device__ __forceinline__ float2 rotate_pair(float a, float b, float2 cs) {
+  return make_float2(fmaf(a, cs.x, -b * cs.y), fmaf(a, cs.y, b * cs.x));
+}
+
 }  // namespace gla

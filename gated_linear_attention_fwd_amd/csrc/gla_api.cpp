@@ -153,57 +153,160 @@ hipError_t timed(Kind k, hipStream_t s, Fn &&fn) {
     if (_st != GLA_OK) return _st;        \
   } while (0)
 
-// Shared body of gla_fwd_framecausal (with outputs) and gla_state_carry.
-gla_status run_framecausal(const void *q, const void *k, const void *v, const void *g,
-                           const float *gamma, const float *S_in, const float *z_in, void *o,
-                           float *S_out, float *z_out, int B, int H, int F, int T, int d,
-                           gla_dtype dt, float eps, void *ws, size_t ws_bytes, void *stream,
-                           bool outputs) {
+constexpr int kMaxRopeEntries = 3072;  // LDS table of 24 KiB: with the kernels' own LDS (up to 57 KiB) it leaves two workgroups per CU
+
+// A [B][H][N][d] tensor argument: validated view plus its address span.
+gla_status check_view(const gla_tensor *t, const char *name, int64_t B, int64_t H, int64_t N,
+                      int d, size_t es, bool output, View *view, Range *span) {
+  *view = View{nullptr, 0, 0, 0};
+  *span = Range{nullptr, 0, name};
+  if (!t || !t->data) return GLA_OK;
+  if (t->stride_b < 0 || t->stride_h < 0 || t->stride_n < 0)
+    return fail(GLA_ERR_SHAPE, "%s has a negative stride", name);
+  const int64_t q = (int64_t)(16 / es);  // elements per 16 bytes
+  if (!aligned(t->data, 16)) return fail(GLA_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (t->stride_b % q || t->stride_h % q || t->stride_n % q)
+    return fail(GLA_ERR_ALIGN, "%s strides must be multiples of 16 bytes (%lld elements)", name,
+                (long long)q);
+  *view = View{t->data, t->stride_b, t->stride_h, t->stride_n};
+  if (B == 0 || H == 0 || N == 0) return GLA_OK;
+  // last element + 1, in elements (each term checked against overflow)
+  const __int128 ext = (__int128)(B - 1) * t->stride_b + (__int128)(H - 1) * t->stride_h +
+                       (__int128)(N - 1) * t->stride_n + d;
+  if (ext * (__int128)es > ((__int128)1 << 62))
+    return fail(GLA_ERR_SHAPE, "%s spans more than 2^62 bytes", name);
+  *span = Range{t->data, (size_t)(ext * (__int128)es), name};
+  if (output) {
+    // distinct (b, h, n) must be distinct rows: with the axes of size > 1 in
+    // increasing stride order, each stride must clear what the smaller ones span
+    int64_t st[3] = {t->stride_n, t->stride_h, t->stride_b}, sz[3] = {N, H, B};
+    for (int a = 0; a < 3; ++a)
+      for (int b = a + 1; b < 3; ++b)
+        if (st[b] < st[a]) {
+          std::swap(st[a], st[b]);
+          std::swap(sz[a], sz[b]);
+        }
+    __int128 extent = d;
+    for (int a = 0; a < 3; ++a) {
+      if (sz[a] <= 1) continue;
+      if ((__int128)st[a] < extent)
+        return fail(GLA_ERR_ALIAS, "%s rows overlap one another (strides %lld, %lld, %lld)",
+                    name, (long long)t->stride_b, (long long)t->stride_h,
+                    (long long)t->stride_n);
+      extent += (__int128)st[a] * (sz[a] - 1);
+    }
+  }
+  return GLA_OK;
+}
+
+gla_status make_rope(const gla_rope3d *r, int F, int64_t T, int d, RopeK *out) {
+  *out = RopeK{};
+  if (!r) return GLA_OK;
+  if (r->grid_h < 1 || r->grid_w < 1 || (int64_t)r->grid_h * r->grid_w != T)
+    return fail(GLA_ERR_SHAPE, "rope grid %d x %d must be >= 1 and hold the T=%lld tokens of a frame",
+                r->grid_h, r->grid_w, (long long)T);
+  if (r->dim_t < 0 || r->dim_h < 0 || r->dim_w < 0 || (r->dim_t | r->dim_h | r->dim_w) & 1 ||
+      (int64_t)r->dim_t + r->dim_h + r->dim_w != d)
+    return fail(GLA_ERR_SHAPE, "rope sections (%d, %d, %d) must be even, >= 0 and sum to d=%d",
+                r->dim_t, r->dim_h, r->dim_w, d);
+  if (!std::isfinite(r->theta) || !(r->theta > 0.0))
+    return fail(GLA_ERR_VALUE, "rope theta=%g must be finite and > 0", r->theta);
+  if (r->frame_offset <= -(1 << 30) || r->frame_offset >= (1 << 30) || F >= (1 << 30))
+    return fail(GLA_ERR_VALUE, "rope frame_offset=%d and F=%d must be below 2^30 in magnitude",
+                r->frame_offset, F);
+  RopeK k;
+  k.on = 1;
+  k.grid_h = r->grid_h;
+  k.grid_w = r->grid_w;
+  k.frame_offset = r->frame_offset;
+  k.Pt = r->dim_t / 2;
+  k.Ph = r->dim_h / 2;
+  k.Pw = r->dim_w / 2;
+  k.inv_gw = 1.0 / r->grid_w;
+  k.log_theta = std::log(r->theta);
+  k.frames = (int)kMaxGroupFrames;
+  *out = k;
+  return GLA_OK;
+}
+
+enum class Mode { kBidir, kFrameCausal, kStateCarry };
+
+// The body of every entry point. Bidirectional calls take F frames of T tokens
+// (N = F * T); without rotary positions the frames do not matter and the
+// sequence runs as one frame of N tokens, with them it runs on the frame
+// structure with no decay and every frame reading the last frame's state.
+gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_tensor *v,
+               const gla_tensor *g, const float *gamma, const float *S_in, const float *z_in,
+               const gla_tensor *o, float *S_out, float *z_out, int B, int H, int F, int64_t T,
+               int d, gla_dtype dt, float eps, const gla_rope3d *rope, void *ws,
+               size_t ws_bytes, void *stream) {
+  const bool outputs = mode != Mode::kStateCarry;
+  const bool bidir = mode == Mode::kBidir;
   GLA_TRY(check_dims(B, H, d, dt));
-  if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%d must be >= 0", F, T);
+  if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%lld must be >= 0", F, (long long)T);
   if (outputs) GLA_TRY(check_eps(eps));
   if ((S_in == nullptr) != (z_in == nullptr))
     return fail(GLA_ERR_NULL, "S_in and z_in must both be given or both be NULL");
   if ((S_out == nullptr) != (z_out == nullptr))
     return fail(GLA_ERR_NULL, "S_out and z_out must both be given or both be NULL");
   if (!outputs && !S_out) return fail(GLA_ERR_NULL, "S_out and z_out are required");
+  if (T > 0 && F > INT64_MAX / T) return fail(GLA_ERR_SHAPE, "F * T overflows");
 
   const int64_t BH = (int64_t)B * H;
   const int64_t N = (int64_t)F * T;
   const size_t es = dt == GLA_F32 ? 4 : 2;
-  const size_t tensor_bytes = (size_t)(BH * N * d) * es;
+  View vq, vk, vv, vg, vo;
+  Range rq, rk, rv, rg, ro;
+  GLA_TRY(check_view(k, "k", B, H, N, d, es, false, &vk, &rk));
+  GLA_TRY(check_view(v, "v", B, H, N, d, es, false, &vv, &rv));
+  if (outputs) {
+    GLA_TRY(check_view(q, "q", B, H, N, d, es, false, &vq, &rq));
+    GLA_TRY(check_view(g, "g", B, H, N, d, es, false, &vg, &rg));
+    GLA_TRY(check_view(o, "o", B, H, N, d, es, true, &vo, &ro));
+  } else {
+    vq = vg = vo = View{nullptr, 0, 0, 0};
+    rq = Range{nullptr, 0, "q"};
+    rg = Range{nullptr, 0, "g"};
+    ro = Range{nullptr, 0, "o"};
+  }
   const bool have_tokens = BH > 0 && N > 0;
   if (have_tokens) {
-    if (!k || !v) return fail(GLA_ERR_NULL, "k and v are required");
-    if (outputs && (!q || !g || !o)) return fail(GLA_ERR_NULL, "q, g and o are required");
+    if (!vk.data || !vv.data) return fail(GLA_ERR_NULL, "k and v are required");
+    if (outputs && (!vq.data || !vg.data || !vo.data))
+      return fail(GLA_ERR_NULL, "q, g and o are required");
   }
-  if (BH > 0 && F > 0 && !gamma) return fail(GLA_ERR_NULL, "gamma is required when F > 0");
-  GLA_TRY(check_tensor_align(q, "q"));
-  GLA_TRY(check_tensor_align(k, "k"));
-  GLA_TRY(check_tensor_align(v, "v"));
-  GLA_TRY(check_tensor_align(g, "g"));
-  GLA_TRY(check_tensor_align(o, "o"));
+  if (!bidir && BH > 0 && F > 0 && !gamma) return fail(GLA_ERR_NULL, "gamma is required when F > 0");
   GLA_TRY(check_tensor_align(S_in, "S_in"));
   GLA_TRY(check_tensor_align(z_in, "z_in"));
   GLA_TRY(check_tensor_align(S_out, "S_out"));
   GLA_TRY(check_tensor_align(z_out, "z_out"));
   if (gamma && !aligned(gamma, 4)) return fail(GLA_ERR_ALIGN, "gamma is not 4-byte aligned");
+  RopeK rk_;
+  GLA_TRY(make_rope(rope, F, T, d, &rk_));
 
+  // bidirectional without positions: one frame of all N tokens
+  const bool flat = bidir && !rk_.on;
   Plan p;
-  if (!make_plan(BH, F, T, d, &p)) return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
-  if (BH == 0) return GLA_OK;
+  if (!make_plan(BH, flat ? (N > 0 ? 1 : 0) : F, flat ? N : T, d, &p))
+    return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
+  if (BH == 0 || (bidir && N == 0)) return GLA_OK;
   GLA_TRY(check_ws(p, ws, ws_bytes));
+  const Path path = select_path(dt, d);
+  if (rk_.on && path == Path::kMfma && rk_.entries() > kMaxRopeEntries)
+    return fail(GLA_ERR_UNSUPPORTED,
+                "rope table of %d entries exceeds %d (1 + grid_h*dim_h/2 + grid_w*dim_w/2 + "
+                "8*dim_t/2)",
+                rk_.entries(), kMaxRopeEntries);
 
   const size_t sbytes = (size_t)(BH * d * d) * 4, zbytes = (size_t)(BH * d) * 4;
-  const Range all[] = {{q, tensor_bytes, "q"},       {k, tensor_bytes, "k"},
-                       {v, tensor_bytes, "v"},       {g, tensor_bytes, "g"},
-                       {gamma, (size_t)(BH * F) * 4, "gamma"},
-                       {S_in, sbytes, "S_in"},       {z_in, zbytes, "z_in"},
-                       {o, outputs ? tensor_bytes : 0, "o"},
-                       {S_out, sbytes, "S_out"},     {z_out, zbytes, "z_out"},
+  const Range all[] = {rq, rk, rv, rg,
+                       {gamma, bidir ? 0 : (size_t)(BH * F) * 4, "gamma"},
+                       {S_in, sbytes, "S_in"},   {z_in, zbytes, "z_in"},
+                       ro,
+                       {S_out, sbytes, "S_out"}, {z_out, zbytes, "z_out"},
                        {ws, p.ws_bytes, "workspace"}};
   // S_out may be S_in exactly (and z_out z_in): compare them without the inputs.
-  const Range outs_o[] = {{o, outputs ? tensor_bytes : 0, "o"}, {ws, p.ws_bytes, "workspace"}};
+  const Range outs_o[] = {ro, {ws, p.ws_bytes, "workspace"}};
   GLA_TRY(check_no_overlap(outs_o, 2, all, 11));
   const Range outs_s[] = {{S_out, sbytes, "S_out"}, {z_out, zbytes, "z_out"}};
   const Range others[] = {all[0], all[1], all[2], all[3], all[4], all[7], all[8], all[9], all[10]};
@@ -216,21 +319,27 @@ gla_status run_framecausal(const void *q, const void *k, const void *v, const vo
   if (z_out && overlap(outs_s[1], all[5])) return fail(GLA_ERR_ALIAS, "z_out overlaps S_in");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Path path = select_path(dt, d);
   float *wsf = static_cast<float *>(ws);
-  if (F > 0)
-    GLA_TRY(launched(
-        timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, gamma, wsf}, s); }), "kv"));
-  const CarryArgs sa{wsf, gamma, S_in, z_in, S_out, z_out, outputs ? 1 : 0};
-  GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, sa, s); }), "carry"));
-  if (outputs && have_tokens)
-    GLA_TRY(launched(timed(kKindReadout, s,
+  const float *gm = bidir ? nullptr : gamma;
+  if (p.F > 0)
+    GLA_TRY(launched(timed(kKindKv, s,
                            [&] {
-                             return launch_readout(p, dt, path,
-                                                   ReadoutArgs{q, g, o, gamma, wsf, eps}, s);
+                             return launch_kv(p, dt, path, KvArgs{vk, vv, H, gm, wsf, rk_}, s);
                            }),
+                     "kv"));
+  const CarryArgs sa{wsf,   gm,    bidir ? nullptr : S_in, bidir ? nullptr : z_in,
+                     S_out, z_out, outputs ? 1 : 0};
+  GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, sa, s); }), "carry"));
+  if (outputs && have_tokens) {
+    const ReadoutArgs ra{vq, vg, vo, H, gm, wsf, eps, (bidir && !flat) ? p.F - 1 : -1, rk_};
+    GLA_TRY(launched(timed(kKindReadout, s, [&] { return launch_readout(p, dt, path, ra, s); }),
                      "readout"));
+  }
   return GLA_OK;
+}
+
+gla_tensor contiguous(const void *p, int H, int64_t N, int d) {
+  return gla_tensor{const_cast<void *>(p), (int64_t)H * N * d, N * d, (int64_t)d};
 }
 
 }  // namespace
@@ -318,46 +427,31 @@ GLA_EXPORT size_t gla_state_carry_workspace(int B, int H, int F, int T, int d) {
   return gla_fwd_framecausal_workspace(B, H, F, T, d);
 }
 
+GLA_EXPORT size_t gla_fwd_bidir_ex_workspace(int B, int H, int F, int T, int d,
+                                              const gla_rope3d *rope) {
+  if (B < 0 || H < 0 || F < 0 || T < 0 || d <= 0) return 0;
+  if (rope) return gla_fwd_framecausal_workspace(B, H, F, T, d);
+  return gla_fwd_bidir_workspace(B, H, (int64_t)F * T, d);
+}
+
 GLA_EXPORT gla_status gla_fwd_bidir(const void *q, const void *k, const void *v, const void *g,
                                     void *o, int B, int H, int64_t N, int d, gla_dtype dt,
                                     float eps, void *ws, size_t ws_bytes, void *stream) {
   if (N < 0) return fail(GLA_ERR_SHAPE, "N=%lld must be >= 0", (long long)N);
-  // One frame holding the whole sequence, no decay and no carried state.
-  const int F = N > 0 ? 1 : 0;
-  GLA_TRY(check_dims(B, H, d, dt));
-  GLA_TRY(check_eps(eps));
-  const int64_t BH = (int64_t)B * H;
-  if (BH == 0 || N == 0) return GLA_OK;
-  if (!q || !k || !v || !g || !o) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
-  GLA_TRY(check_tensor_align(q, "q"));
-  GLA_TRY(check_tensor_align(k, "k"));
-  GLA_TRY(check_tensor_align(v, "v"));
-  GLA_TRY(check_tensor_align(g, "g"));
-  GLA_TRY(check_tensor_align(o, "o"));
-  Plan p;
-  if (!make_plan(BH, F, N, d, &p)) return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
-  GLA_TRY(check_ws(p, ws, ws_bytes));
-  const size_t tb = (size_t)(BH * N * d) * (dt == GLA_F32 ? 4 : 2);
-  const Range all[] = {{q, tb, "q"}, {k, tb, "k"}, {v, tb, "v"}, {g, tb, "g"},
-                       {o, tb, "o"}, {ws, p.ws_bytes, "workspace"}};
-  const Range outs[] = {all[4], all[5]};
-  GLA_TRY(check_no_overlap(outs, 2, all, 6));
+  const gla_tensor tq = contiguous(q, H, N, d), tk = contiguous(k, H, N, d),
+                   tv = contiguous(v, H, N, d), tg = contiguous(g, H, N, d),
+                   to = contiguous(o, H, N, d);
+  return run(Mode::kBidir, &tq, &tk, &tv, &tg, nullptr, nullptr, nullptr, &to, nullptr, nullptr,
+             B, H, N > 0 ? 1 : 0, N, d, dt, eps, nullptr, ws, ws_bytes, stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Path path = select_path(dt, d);
-  float *wsf = static_cast<float *>(ws);
-  GLA_TRY(launched(
-      timed(kKindKv, s, [&] { return launch_kv(p, dt, path, KvArgs{k, v, nullptr, wsf}, s); }),
-      "kv"));
-  const CarryArgs sa{wsf, nullptr, nullptr, nullptr, nullptr, nullptr, 1};
-  GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, sa, s); }), "carry"));
-  GLA_TRY(launched(
-      timed(kKindReadout, s,
-            [&] {
-              return launch_readout(p, dt, path, ReadoutArgs{q, g, o, nullptr, wsf, eps}, s);
-            }),
-      "readout"));
-  return GLA_OK;
+GLA_EXPORT gla_status gla_fwd_bidir_ex(const gla_tensor *q, const gla_tensor *k,
+                                       const gla_tensor *v, const gla_tensor *g,
+                                       const gla_tensor *o, int B, int H, int F, int T, int d,
+                                       gla_dtype dt, float eps, const gla_rope3d *rope, void *ws,
+                                       size_t ws_bytes, void *stream) {
+  return run(Mode::kBidir, q, k, v, g, nullptr, nullptr, nullptr, o, nullptr, nullptr, B, H, F,
+             T, d, dt, eps, rope, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_fwd_framecausal(const void *q, const void *k, const void *v,
@@ -365,16 +459,44 @@ GLA_EXPORT gla_status gla_fwd_framecausal(const void *q, const void *k, const vo
                                           const float *z_in, void *o, float *S_out, float *z_out,
                                           int B, int H, int F, int T, int d, gla_dtype dt,
                                           float eps, void *ws, size_t ws_bytes, void *stream) {
-  return run_framecausal(q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d, dt, eps,
-                         ws, ws_bytes, stream, true);
+  const int64_t N = (int64_t)std::max(F, 0) * std::max(T, 0);
+  const gla_tensor tq = contiguous(q, H, N, d), tk = contiguous(k, H, N, d),
+                   tv = contiguous(v, H, N, d), tg = contiguous(g, H, N, d),
+                   to = contiguous(o, H, N, d);
+  return run(Mode::kFrameCausal, &tq, &tk, &tv, &tg, gamma, S_in, z_in, &to, S_out, z_out, B, H,
+             F, T, d, dt, eps, nullptr, ws, ws_bytes, stream);
+}
+
+GLA_EXPORT gla_status gla_fwd_framecausal_ex(const gla_tensor *q, const gla_tensor *k,
+                                             const gla_tensor *v, const gla_tensor *g,
+                                             const float *gamma, const float *S_in,
+                                             const float *z_in, const gla_tensor *o,
+                                             float *S_out, float *z_out, int B, int H, int F,
+                                             int T, int d, gla_dtype dt, float eps,
+                                             const gla_rope3d *rope, void *ws, size_t ws_bytes,
+                                             void *stream) {
+  return run(Mode::kFrameCausal, q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d,
+             dt, eps, rope, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_state_carry(const void *k, const void *v, const float *gamma,
                                       const float *S_in, const float *z_in, float *S_out,
                                       float *z_out, int B, int H, int F, int T, int d,
                                       gla_dtype dt, void *ws, size_t ws_bytes, void *stream) {
-  return run_framecausal(nullptr, k, v, nullptr, gamma, S_in, z_in, nullptr, S_out, z_out, B, H,
-                         F, T, d, dt, 0.f, ws, ws_bytes, stream, false);
+  const int64_t N = (int64_t)std::max(F, 0) * std::max(T, 0);
+  const gla_tensor tk = contiguous(k, H, N, d), tv = contiguous(v, H, N, d);
+  return run(Mode::kStateCarry, nullptr, &tk, &tv, nullptr, gamma, S_in, z_in, nullptr, S_out,
+             z_out, B, H, F, T, d, dt, 0.f, nullptr, ws, ws_bytes, stream);
+}
+
+GLA_EXPORT gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *v,
+                                         const float *gamma, const float *S_in,
+                                         const float *z_in, float *S_out, float *z_out, int B,
+                                         int H, int F, int T, int d, gla_dtype dt,
+                                         const gla_rope3d *rope, void *ws, size_t ws_bytes,
+                                         void *stream) {
+  return run(Mode::kStateCarry, nullptr, k, v, nullptr, gamma, S_in, z_in, nullptr, S_out, z_out,
+             B, H, F, T, d, dt, 0.f, rope, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT const char *gla_status_string(gla_status s) {
@@ -394,7 +516,7 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
 
 GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
 
-GLA_EXPORT int gla_version(void) { return 10000; }
+GLA_EXPORT int gla_version(void) { return 10100; }
 
 GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
   if (max_launches < 1 || max_launches > 65536)

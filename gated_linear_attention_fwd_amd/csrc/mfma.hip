@@ -118,6 +118,82 @@ __device__ __forceinline__ bf16x8 tr_fragment(const lds_char *tile, int row, int
   return __builtin_bit_cast(bf16x8, ab);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 (v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// ---------------------------------------------------------------------------
+// 3D rotary positions
+//
+// Temporal and spatial sections turn disjoint feature pairs, so the rotation
+// of a token factors as R = R_t(frame) R_s(y, x), and R_t is shared by every
+// token of a frame. The kernels therefore turn each token by R_s only, and
+// apply R_t once per frame to a d x d operand: kv turns the rows of the
+// frame's sum U_f (U = sum R_t R_s phi(k) v^T = R_t sum R_s phi(k) v^T), the
+// readout turns the rows of S_f by R_t^T ((R_t R_s phi(q))^T S = (R_s phi(q))^T
+// R_t^T S). The (cos, sin) values come from an LDS table (RopeK::entries()),
+// filled once per workgroup.
+// ---------------------------------------------------------------------------
+__device__ void fill_rope_table(float2 *tab, const RopeK &r, int f0) {
+  const int n = r.entries();
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    float2 cs = make_float2(1.f, 0.f);
+    if (e >= r.t_base()) {
+      const int i = e - r.t_base(), fi = i / r.Pt;
+      cs = rope_cs((double)r.frame_offset + f0 + fi, i - fi * r.Pt, r.Pt, r.log_theta);
+    } else if (e >= r.x_base()) {
+      const int i = e - r.x_base(), x = i / r.Pw;
+      cs = rope_cs((double)x, i - x * r.Pw, r.Pw, r.log_theta);
+    } else if (e >= r.y_base()) {
+      const int i = e - r.y_base(), y = i / r.Ph;
+      cs = rope_cs((double)y, i - y * r.Ph, r.Ph, r.log_theta);
+    }
+    tab[e] = cs;
+  }
+}
+
+// The spatial turn of one 16-byte piece (8 bf16 = feature pairs 4c .. 4c+3) of
+// the token at in-frame index l. is_t / is_h mark which of the four pairs are
+// temporal (not turned here) or in the height section.
+struct PieceRope {
+  bool is_t[4], is_h[4];
+  int c4;
+  __device__ PieceRope(const RopeK &r, int c) : c4(4 * c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      is_t[e] = c4 + e < r.Pt;
+      is_h[e] = c4 + e < r.Pt + r.Ph;
+    }
+  }
+  // The turned features as hi + lo, both bf16 (hi = bf16(x), lo = bf16(x - hi):
+  // together 16 significant bits, like the state's split in the readout).
+  __device__ __forceinline__ void turn(uint4 w, int l, const RopeK &r, const float2 *tab,
+                                       uint4 &hi, uint4 &lo) const {
+    int y, x;
+    grid_pos(l, r.grid_w, r.inv_gw, y, x);
+    // entry of pair 4c + e: by + e in the height section, bx + e in the width one
+    const int by = r.y_base() + y * r.Ph - r.Pt + c4;
+    const int bx = r.x_base() + x * r.Pw - r.Pt - r.Ph + c4;
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    uint32_t hv[4], lv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = is_t[e] ? -e : (is_h[e] ? by : bx);
+      const float2 cs = tab[idx + e];
+      const float2 ab = rotate_pair(lo_bf16(wv[e]), hi_bf16(wv[e]), cs);
+      hv[e] = pack_bf16x2(ab.x, ab.y);
+      lv[e] = pack_bf16x2(ab.x - lo_bf16(hv[e]), ab.y - hi_bf16(hv[e]));
+    }
+    hi = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+    lo = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // KV sums
 // ---------------------------------------------------------------------------
@@ -143,6 +219,8 @@ struct KvCfg {
   static constexpr int RED_BYTES = kSplitTokens ? 4 * 1024 * 4 : 0;  // 4 waves x 32x32 fp32
   static constexpr int U_RED_BYTES = 4 * D * 4;                       // 4 waves x D fp32
   static constexpr int SMEM = (2 * TILE_BYTES > RED_BYTES ? 2 * TILE_BYTES : RED_BYTES);
+  // with rotary positions a third tile holds the low bf16 parts of turned phi(k)
+  static constexpr int SMEM_ROPE = (3 * TILE_BYTES > RED_BYTES ? 3 * TILE_BYTES : RED_BYTES);
 };
 
 // One workgroup per (slab, group of G frames, part). Per frame the MFMA
@@ -152,18 +230,20 @@ struct KvCfg {
 // registers per lane) and runs one frame per workgroup. Chunks are numbered
 // across the group's frames so that the next chunk's loads (possibly the next
 // frame's) overlap the MFMAs and the write-out of the current one.
-template <int D>
-__global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__restrict__ k,
-                                                           const uint16_t *__restrict__ v,
+template <int D, bool kRope>
+__global__ __launch_bounds__(kThreads) void kv_mfma_kernel(View kview, View vview, int H,
                                                            const float *__restrict__ gamma,
                                                            float *__restrict__ ws, int F,
                                                            int64_t T, int P, int G,
-                                                           int64_t part_len) {
+                                                           int64_t part_len, RopeK rope) {
   using C = KvCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM + C::U_RED_BYTES];
+  constexpr int kSmem = kRope ? C::SMEM_ROPE : C::SMEM;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem + C::U_RED_BYTES];
+  extern __shared__ float2 rope_tab[];  // kRope: RopeK::entries() (cos, sin) pairs
   lds_char *const sbase = (lds_char *)smem;
   lds_char *const tk = sbase;
   lds_char *const tv = sbase + C::TILE_BYTES;
+  lds_char *const tk_lo = sbase + 2 * C::TILE_BYTES;  // kRope only
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -181,13 +261,20 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
   const int nf = C::kGroups ? min(F, f_begin + G) - f_begin : 1;  // d = 128: G == 1
   const int ncf = (L + C::CH - 1) / C::CH;  // chunks per frame
   const int total = nf * ncf;
-  const uint4 *kb = reinterpret_cast<const uint4 *>(k + (bh * N + (int64_t)f_begin * T + t0) * D);
-  const uint4 *vb = reinterpret_cast<const uint4 *>(v + (bh * N + (int64_t)f_begin * T + t0) * D);
-  const int64_t frame_pieces = T * C::ROW_CHUNKS;  // 16-byte pieces per frame
+  (void)N;
+  // row strides in 16-byte pieces (host-checked multiples of 8 elements)
+  const int64_t snk = kview.sn / 8, snv = vview.sn / 8;
+  const uint4 *kb = reinterpret_cast<const uint4 *>(
+      static_cast<const uint16_t *>(kview.data) + kview.slab(bh, H) +
+      ((int64_t)f_begin * T + t0) * kview.sn);
+  const uint4 *vb = reinterpret_cast<const uint4 *>(
+      static_cast<const uint16_t *>(vview.data) + vview.slab(bh, H) +
+      ((int64_t)f_begin * T + t0) * vview.sn);
 
   // this thread's 16-byte pieces: fixed column piece c, rows r0 + i * ROWS_PER_PASS
   const int c = tid % C::ROW_CHUNKS;
   const int r0 = tid / C::ROW_CHUNKS;
+  [[maybe_unused]] const PieceRope prope(rope, c);
   uint4 rk[C::CPT], rv[C::CPT];
   auto load = [&](int chunk) {
     const int fi = chunk / ncf;
@@ -196,9 +283,9 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
     for (int i = 0; i < C::CPT; ++i) {
       const int row = base + r0 + i * C::ROWS_PER_PASS;
       if (row < L) {
-        const int64_t off = fi * frame_pieces + (int64_t)row * C::ROW_CHUNKS + c;
-        rk[i] = ld_stream16<GLA_KV_NT_LOADS>(kb + off);
-        rv[i] = ld_stream16<GLA_KV_NT_LOADS>(vb + off);
+        const int64_t trow = (int64_t)fi * T + row;
+        rk[i] = ld_stream16<GLA_KV_NT_LOADS>(kb + trow * snk + c);
+        rv[i] = ld_stream16<GLA_KV_NT_LOADS>(vb + trow * snv + c);
       } else {
         rk[i] = make_uint4(0, 0, 0, 0);
         rv[i] = make_uint4(0, 0, 0, 0);
@@ -226,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
   const int wm = C::kSplitTokens ? 0 : (wave >> 1);
   const int wn = C::kSplitTokens ? 0 : (wave & 1);
   float *red = (float *)smem;                 // [wave][r][lane], aliases the tiles
-  float *ured = (float *)(smem + C::SMEM);    // [wave][D]
+  float *ured = (float *)(smem + kSmem);      // [wave][D]
 
   // running state of the group: accumulator layout (d = 64) or the layout of
   // the cross-wave sum (d = 32)
@@ -241,7 +328,33 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
   float gms[C::kGroups ? kMaxGroup : 1];
 #pragma unroll
   for (int e = 0; e < (C::kGroups ? kMaxGroup : 1); ++e)
-    gms[e] = (e > 0 && e < nf) ? gamma[bh * F + f_begin + e] : 0.f;
+    gms[e] = (e > 0 && e < nf) ? (gamma ? gamma[bh * F + f_begin + e] : 1.f) : 0.f;
+
+  if constexpr (kRope) {
+    fill_rope_table(rope_tab, rope, f_begin);
+    sync_lds();
+  }
+  // U_f's rows (key features) turn with the frame: rows 2p and 2p+1 of a C
+  // block sit in one lane (elements r and r+1, r even)
+  auto turn_rows = [&](int fi) {
+    if constexpr (kRope) {
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a) {
+        const int rb = C::kSplitTokens ? a : wm * C::TM + a;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int pr = 16 * rb + 4 * (r >> 2) + 2 * h + ((r & 3) >> 1);
+          const float2 cs = rope_tab[pr < rope.Pt ? rope.t_base() + fi * rope.Pt + pr : 0];
+#pragma unroll
+          for (int b = 0; b < C::TM; ++b) {
+            const float2 ab = rotate_pair(acc[a][b][r], acc[a][b][r + 1], cs);
+            acc[a][b][r] = ab.x;
+            acc[a][b][r + 1] = ab.y;
+          }
+        }
+      }
+    }
+  };
 
   // After a frame's last chunk, frame_close() folds U_f into the running state
   // (registers; z through an LDS sum), and store_state() writes the slot. The
@@ -249,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
   // been waited for: vmcnt counts loads and stores alike, so stores issued
   // behind an outstanding prefetch would make its wait include them.
   auto frame_close = [&](int fi) {
+    turn_rows(fi);
     float gm = 0.f;
 #pragma unroll
     for (int e = 1; e < (C::kGroups ? kMaxGroup : 1); ++e) gm = (fi == e) ? gms[e] : gm;
@@ -352,7 +466,17 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
       for (int i = 0; i < C::CPT; ++i) {
         const int row = r0 + i * C::ROWS_PER_PASS;
         const uint4 kk = relu8(rk[i]);
-        *reinterpret_cast<uint4 *>(smem + row * C::PITCH + c * 16) = kk;
+        if constexpr (kRope) {
+          // z takes phi(k) unturned; S the spatially turned one (rows past the
+          // part are zeros: any in-frame position does)
+          const int l = (int)min(t0 + cc * C::CH + row, T - 1);
+          uint4 khi, klo;
+          prope.turn(kk, l, rope, rope_tab, khi, klo);
+          *reinterpret_cast<uint4 *>(smem + row * C::PITCH + c * 16) = khi;
+          *reinterpret_cast<uint4 *>(smem + 2 * C::TILE_BYTES + row * C::PITCH + c * 16) = klo;
+        } else {
+          *reinterpret_cast<uint4 *>(smem + row * C::PITCH + c * 16) = kk;
+        }
         *reinterpret_cast<uint4 *>(smem + C::TILE_BYTES + row * C::PITCH + c * 16) = rv[i];
         uacc[0] += lo_bf16(kk.x);
         uacc[1] += hi_bf16(kk.x);
@@ -384,6 +508,16 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(const uint16_t *__res
         for (int a = 0; a < C::TM; ++a)
 #pragma unroll
           for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_32x32x16(fa[a], fb[b], acc[a][b]);
+        if constexpr (kRope) {
+          // low parts of the turned keys
+#pragma unroll
+          for (int a = 0; a < C::TM; ++a) {
+            const bf16x8 fl =
+                tr_fragment(tk_lo, ks * 16 + frag_row, 32 * (wm * C::TM + a) + frag_col, C::PITCH);
+#pragma unroll
+            for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma_32x32x16(fl, fb[b], acc[a][b]);
+          }
+        }
       }
     }
     frame_close(fi);
@@ -416,16 +550,18 @@ struct RoCfg {
 //   2. acc = S_f^T phi(q)^T over the input features (hi and lo parts of S_f)
 //   3. o = sigmoid(g) * acc / (den + eps) -> bf16, written over g in LDS
 //   4. o rows -> global memory
-template <int D>
+template <int D, bool kRope>
 __global__ __launch_bounds__(kThreads) void readout_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ g, uint16_t *__restrict__ o,
-    const float *__restrict__ gamma, const float *__restrict__ ws, int F, int64_t T, int P,
-    int G, int64_t carry_offset, int R, int64_t read_len, float eps) {
+    View qview, View gview, View oview, int H, const float *__restrict__ gamma,
+    const float *__restrict__ ws, int F, int64_t T, int P, int G, int64_t carry_offset, int R,
+    int64_t read_len, float eps, int state_frame, RopeK rope) {
   using C = RoCfg<D>;
   constexpr int GP = 2 * D + 16;  // bytes per LDS row of g / o
   __shared__ __attribute__((aligned(16))) char qtile[C::BLK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) char qtile_lo[kRope ? C::BLK * C::PITCH : 16];
   __shared__ __attribute__((aligned(16))) char gtile[C::BLK * GP];
   __shared__ float den_s[C::BLK];
+  extern __shared__ float2 rope_tab[];  // kRope: RopeK::entries() (cos, sin) pairs
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -437,21 +573,26 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
   const int r = (int)(wg % R);
   const int f = (int)((wg / R) % F);
   const int64_t bh = wg / ((int64_t)R * F);
-  const int64_t N = (int64_t)F * T;
   const int64_t t0 = min((int64_t)r * read_len, T);
   const int64_t t1 = min(t0 + read_len, T);
   const int L = (int)(t1 - t0);
   if (L <= 0) return;
-  const int64_t row0 = bh * N + (int64_t)f * T + t0;
+  const int64_t trow0 = (int64_t)f * T + t0;  // first token row of the slab
 
-  // S_f = S_loc_f + w_f * carry of the frame's group, as bf16 hi/lo A fragments
+  // S_fs = S_loc_fs + w * carry of the group, as bf16 hi/lo A fragments (fs is
+  // the frame's own state, or the one all frames share)
+  const int fs = state_frame >= 0 ? state_frame : f;
   constexpr int64_t E = (int64_t)D * D + D;
   const int NG = (F + G - 1) / G;
-  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;
+  const float *Sg = ws + ((bh * F + fs) * (int64_t)P) * E;
   // G == 1: the carry kernel has completed S_f in place (no carries kept)
   const bool has_carry = G > 1;
-  const float *Cg = ws + carry_offset + (bh * NG + f / G) * E;
-  const float w = carry_weight(gamma ? gamma + bh * F : nullptr, f, G);
+  const float *Cg = ws + carry_offset + (bh * NG + fs / G) * E;
+  const float w = carry_weight(gamma ? gamma + bh * F : nullptr, fs, G);
+  if constexpr (kRope) {
+    fill_rope_table(rope_tab, rope, f);
+    sync_lds();
+  }
   bf16x8 ahi[C::KS], alo[C::KS];
   // S = hi + lo, both bf16: returns hi in the low half, lo in the high half
   auto split = [&](float sv) -> uint32_t {
@@ -463,7 +604,29 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       i16x8 hv, lv;
-      if (has_carry) {
+      if constexpr (kRope) {
+        // rows i = 16ks + 8h + e of S turned by R_t(f)^T: pair (i, i+1) for even e
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int idx = (16 * ks + 8 * h + e) * D + jcol;
+          sv[e] = has_carry ? fmaf(w, Cg[idx], Sg[idx]) : Sg[idx];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int pr = 8 * ks + 4 * h + e / 2;
+          const float2 cs = rope_tab[pr < rope.Pt ? rope.t_base() + pr : 0];
+          const float2 ab = rotate_pair(sv[e], sv[e + 1], make_float2(cs.x, -cs.y));
+          sv[e] = ab.x;
+          sv[e + 1] = ab.y;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t hl = split(sv[e]);
+          hv[e] = (short)(hl & 0xFFFFu);
+          lv[e] = (short)(hl >> 16);
+        }
+      } else if (has_carry) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int idx = (16 * ks + 8 * h + e) * D + jcol;
@@ -491,18 +654,24 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
   for (int e = 0; e < 8; ++e)
     zc[e] = has_carry ? fmaf(w, Cg[D * D + 8 * c + e], Sg[D * D + 8 * c + e]) : Sg[D * D + 8 * c + e];
 
-  const uint4 *qb = reinterpret_cast<const uint4 *>(q + row0 * D);
-  const uint4 *gb = reinterpret_cast<const uint4 *>(g + row0 * D);
-  uint4 *ob = reinterpret_cast<uint4 *>(o + row0 * D);
+  // row strides in 16-byte pieces (host-checked multiples of 8 elements)
+  const int64_t snq = qview.sn / 8, sng = gview.sn / 8, sno = oview.sn / 8;
+  const uint4 *qb = reinterpret_cast<const uint4 *>(
+      static_cast<const uint16_t *>(qview.data) + qview.slab(bh, H) + trow0 * qview.sn);
+  const uint4 *gb = reinterpret_cast<const uint4 *>(
+      static_cast<const uint16_t *>(gview.data) + gview.slab(bh, H) + trow0 * gview.sn);
+  uint4 *ob = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(
+      static_cast<const uint16_t *>(oview.data) + oview.slab(bh, H) + trow0 * oview.sn));
+  [[maybe_unused]] const PieceRope prope(rope, c);
   uint4 rq[C::CPT], rgv[C::CPT];
   auto load = [&](int blk) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = blk * C::BLK + r0 + i * C::ROWS_PER_PASS;
       const bool ok = row < L;
-      rq[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(qb + (int64_t)row * C::ROW_CHUNKS + c)
+      rq[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(qb + (int64_t)row * snq + c)
                  : make_uint4(0, 0, 0, 0);
-      rgv[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(gb + (int64_t)row * C::ROW_CHUNKS + c)
+      rgv[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(gb + (int64_t)row * sng + c)
                   : make_uint4(0, 0, 0, 0);
     }
   };
@@ -516,7 +685,16 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
     for (int i = 0; i < C::CPT; ++i) {
       const int row = r0 + i * C::ROWS_PER_PASS;
       const uint4 w = relu8(rq[i]);
-      *reinterpret_cast<uint4 *>(qtile + row * C::PITCH + c * 16) = w;
+      if constexpr (kRope) {
+        // the numerator takes phi(q) spatially turned, the normaliser unturned
+        const int l = (int)min(t0 + blk * C::BLK + row, T - 1);
+        uint4 qhi, qlo;
+        prope.turn(w, l, rope, rope_tab, qhi, qlo);
+        *reinterpret_cast<uint4 *>(qtile + row * C::PITCH + c * 16) = qhi;
+        *reinterpret_cast<uint4 *>(qtile_lo + row * C::PITCH + c * 16) = qlo;
+      } else {
+        *reinterpret_cast<uint4 *>(qtile + row * C::PITCH + c * 16) = w;
+      }
       *reinterpret_cast<uint4 *>(gtile + row * GP + c * 16) = rgv[i];
       float dp = lo_bf16(w.x) * zc[0];
       dp = fmaf(hi_bf16(w.x), zc[1], dp);
@@ -543,6 +721,12 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
       const bf16x8 bf = __builtin_bit_cast(bf16x8, bw);
       acc = mfma_32x32x16(ahi[ks], bf, acc);
       acc = mfma_32x32x16(alo[ks], bf, acc);
+      if constexpr (kRope) {
+        // low parts of the turned queries (times S_hi; S_lo x q_lo is below fp32 rounding)
+        const uint4 bl =
+            *reinterpret_cast<const uint4 *>(qtile_lo + tl * C::PITCH + (16 * ks + 8 * h) * 2);
+        acc = mfma_32x32x16(ahi[ks], __builtin_bit_cast(bf16x8, bl), acc);
+      }
     }
     const float inv = 1.f / (den_s[tl] + eps);
 #pragma unroll
@@ -567,13 +751,29 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
         const uint4 ov = *reinterpret_cast<const uint4 *>(gtile + row * GP + c * 16);
         if constexpr (GLA_RO_NT_STORES != 0) {
           const u32x4 x = {ov.x, ov.y, ov.z, ov.w};
-          __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(ob + (int64_t)tok * C::ROW_CHUNKS + c));
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(ob + (int64_t)tok * sno + c));
         } else {
-          ob[(int64_t)tok * C::ROW_CHUNKS + c] = ov;
+          ob[(int64_t)tok * sno + c] = ov;
         }
       }
     }
   }
+}
+
+template <int D, bool kRope>
+void kv_launch(const Plan &p, const KvArgs &a, RopeK rope, int64_t grid, hipStream_t s) {
+  const size_t lds = kRope ? (size_t)rope.entries() * sizeof(float2) : 0;
+  hipLaunchKernelGGL((kv_mfma_kernel<D, kRope>), dim3((unsigned)grid), dim3(kThreads), lds, s,
+                     a.k, a.v, a.H, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len, rope);
+}
+
+template <int D, bool kRope>
+void readout_launch(const Plan &p, const ReadoutArgs &a, RopeK rope, int64_t grid,
+                    hipStream_t s) {
+  const size_t lds = kRope ? (size_t)rope.entries() * sizeof(float2) : 0;
+  hipLaunchKernelGGL((readout_kernel<D, kRope>), dim3((unsigned)grid), dim3(kThreads), lds, s,
+                     a.q, a.g, a.o, a.H, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(),
+                     p.R, p.read_len, a.eps, a.state_frame, rope);
 }
 
 }  // namespace
@@ -583,21 +783,13 @@ bool mfma_supports(int d) { return d == 32 || d == 64 || d == 128; }
 hipError_t launch_kv_mfma(const Plan &p, const KvArgs &a, hipStream_t s) {
   const int64_t grid = p.BH * p.NG * p.P;
   if (grid == 0) return hipSuccess;
-  const uint16_t *k = static_cast<const uint16_t *>(a.k);
-  const uint16_t *v = static_cast<const uint16_t *>(a.v);
+  RopeK rope = a.rope;
+  rope.frames = p.G;  // temporal table rows: the group's frames
+  const bool r = rope.on != 0;
   switch (p.d) {
-    case 32:
-      hipLaunchKernelGGL(kv_mfma_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
-                         a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len);
-      break;
-    case 64:
-      hipLaunchKernelGGL(kv_mfma_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
-                         a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len);
-      break;
-    case 128:
-      hipLaunchKernelGGL(kv_mfma_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, k, v,
-                         a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len);
-      break;
+    case 32: r ? kv_launch<32, true>(p, a, rope, grid, s) : kv_launch<32, false>(p, a, rope, grid, s); break;
+    case 64: r ? kv_launch<64, true>(p, a, rope, grid, s) : kv_launch<64, false>(p, a, rope, grid, s); break;
+    case 128: r ? kv_launch<128, true>(p, a, rope, grid, s) : kv_launch<128, false>(p, a, rope, grid, s); break;
     default:
       return hipErrorInvalidValue;
   }
@@ -607,25 +799,13 @@ hipError_t launch_kv_mfma(const Plan &p, const KvArgs &a, hipStream_t s) {
 hipError_t launch_readout_mfma(const Plan &p, const ReadoutArgs &a, hipStream_t s) {
   const int64_t grid = p.BH * p.F * p.R;
   if (grid == 0 || p.T == 0) return hipSuccess;
-  const uint16_t *q = static_cast<const uint16_t *>(a.q);
-  const uint16_t *g = static_cast<const uint16_t *>(a.g);
-  uint16_t *o = static_cast<uint16_t *>(a.o);
+  RopeK rope = a.rope;
+  rope.frames = 1;  // a readout workgroup covers one frame
+  const bool r = rope.on != 0;
   switch (p.d) {
-    case 32:
-      hipLaunchKernelGGL(readout_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
-                         g, o, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(), p.R,
-                         p.read_len, a.eps);
-      break;
-    case 64:
-      hipLaunchKernelGGL(readout_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
-                         g, o, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(), p.R,
-                         p.read_len, a.eps);
-      break;
-    case 128:
-      hipLaunchKernelGGL(readout_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, s, q,
-                         g, o, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(), p.R,
-                         p.read_len, a.eps);
-      break;
+    case 32: r ? readout_launch<32, true>(p, a, rope, grid, s) : readout_launch<32, false>(p, a, rope, grid, s); break;
+    case 64: r ? readout_launch<64, true>(p, a, rope, grid, s) : readout_launch<64, false>(p, a, rope, grid, s); break;
+    case 128: r ? readout_launch<128, true>(p, a, rope, grid, s) : readout_launch<128, false>(p, a, rope, grid, s); break;
     default:
       return hipErrorInvalidValue;
   }

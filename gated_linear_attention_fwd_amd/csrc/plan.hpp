@@ -58,11 +58,50 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan);
 enum class Path { kValu = 0, kMfma = 1 };
 Path select_path(int dtype, int d);
 
+// A strided [B][H][N][d] tensor: element (b, h, n, c) sits at
+// data + b * sb + h * sh + n * sn + c (element units; the feature stride is 1).
+// Slab bh = b * H + h.
+struct View {
+  const void *data;
+  int64_t sb, sh, sn;
+  // bh < 2^31 (the grid limits keep it far below): 32-bit division
+  __host__ __device__ int64_t slab(int64_t bh, int H) const {
+    const int b = (int)bh / H;
+    return b * sb + ((int)bh - b * H) * sh;
+  }
+};
+
+__host__ __device__ inline View contiguous_view(const void *p, int H, int64_t N, int d) {
+  return View{p, (int64_t)H * N * d, N * d, (int64_t)d};
+}
+
+// 3D rotary positions (host-validated). Token l of frame f sits at
+// (t, y, x) = (frame_offset + f, l / grid_w, l % grid_w); feature pairs
+// (2p, 2p+1) form three consecutive sections of Pt, Ph and Pw pairs that turn
+// with t, y and x, pair j of an m-pair section by pos * theta^(-j/m).
+struct RopeK {
+  int on = 0;
+  int grid_h = 1, grid_w = 1;
+  int frame_offset = 0;
+  int Pt = 0, Ph = 0, Pw = 0;
+  double inv_gw = 1.0;      // 1 / grid_w, for the position decode
+  double log_theta = 0.0;   // ln(theta)
+  int frames = 1;           // temporal rows in a workgroup's table (frames per kv group)
+  // LDS table of (cos, sin): [0] identity, then [grid_h][Ph], [grid_w][Pw],
+  // [frames][Pt]
+  __host__ __device__ int y_base() const { return 1; }
+  __host__ __device__ int x_base() const { return 1 + grid_h * Ph; }
+  __host__ __device__ int t_base() const { return 1 + grid_h * Ph + grid_w * Pw; }
+  __host__ __device__ int entries() const { return t_base() + frames * Pt; }
+};
+
 struct KvArgs {
-  const void *k;
-  const void *v;
-  const float *gamma;  // NULL: no decay (bidirectional; then G == 1)
+  View k;
+  View v;
+  int H;
+  const float *gamma;  // NULL: no decay
   float *ws;
+  RopeK rope;
 };
 
 struct CarryArgs {
@@ -76,12 +115,15 @@ struct CarryArgs {
 };
 
 struct ReadoutArgs {
-  const void *q;
-  const void *g;
-  void *o;
+  View q;
+  View g;
+  View o;  // written
+  int H;
   const float *gamma;  // NULL: no decay
   const float *ws;
   float eps;
+  int state_frame;     // -1: every frame reads its own state; else all read this one
+  RopeK rope;
 };
 
 // Decay weight of a frame's carry-in: prod_{m = first frame of f's group}^{f} gamma_m.

@@ -14,24 +14,35 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKvTile = 32;  // tokens staged in LDS per step
 
+// (cos, sin) of feature pair p of token l in frame f: the whole turn, temporal
+// or spatial, computed directly (these kernels keep no tables, unlike the
+// matrix-core path).
+__device__ float2 token_rope_cs(const RopeK &r, int f, int l, int p) {
+  if (p < r.Pt) return rope_cs((double)r.frame_offset + f, p, r.Pt, r.log_theta);
+  int y, x;
+  grid_pos(l, r.grid_w, r.inv_gw, y, x);
+  if (p < r.Pt + r.Ph) return rope_cs((double)y, p - r.Pt, r.Ph, r.log_theta);
+  return rope_cs((double)x, p - r.Pt - r.Ph, r.Pw, r.log_theta);
+}
+
 // One workgroup per (slab, group of frames, part). Thread layout: key feature
 // i = tid % D, value columns j = tid / D + (256 / D) * c for c < D*D/256. Each
 // token adds phi(k[i]) * v[j] to the thread's entries; u[i] is kept by threads
 // with tid < D. Entering each frame after the group's first, the running sums
 // are scaled by that frame's gamma; after each frame they are written to the
 // frame's slot (S_loc_f, z_loc_f).
-template <typename TIn, int D>
-__global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict__ k,
-                                                           const TIn *__restrict__ v,
+template <typename TIn, int D, bool kRope>
+__global__ __launch_bounds__(kThreads) void kv_valu_kernel(View kview, View vview, int H,
                                                            const float *__restrict__ gamma,
                                                            float *__restrict__ ws, int F,
                                                            int64_t T, int P, int G,
-                                                           int64_t part_len) {
+                                                           int64_t part_len, RopeK rope) {
   static_assert(D * D >= kThreads && (D * D) % kThreads == 0, "D must be 16..128");
   constexpr int EPT = D * D / kThreads;
   constexpr int JS = kThreads / D;
-  __shared__ float sk[kKvTile][D];
+  __shared__ float sk[kKvTile][D];                  // phi(k), turned with kRope
   __shared__ float sv[kKvTile][D];
+  __shared__ float su[kRope ? kKvTile : 1][D];      // kRope: phi(k) unturned (for z)
 
   const int tid = threadIdx.x;
   const int NG = (F + G - 1) / G;
@@ -39,11 +50,12 @@ __global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict
   const int p = (int)(wg % P);
   const int grp = (int)((wg / P) % NG);
   const int64_t bh = wg / ((int64_t)P * NG);
-  const int64_t N = (int64_t)F * T;
   const int64_t t0 = min((int64_t)p * part_len, T);
   const int64_t t1 = min(t0 + part_len, T);
   const int f_begin = grp * G;
   const int f_end = min(F, f_begin + G);
+  const TIn *kslab = static_cast<const TIn *>(kview.data) + kview.slab(bh, H);
+  const TIn *vslab = static_cast<const TIn *>(vview.data) + vview.slab(bh, H);
 
   const int i = tid % D;
   const int jc = tid / D;
@@ -54,13 +66,13 @@ __global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict
 
   for (int f = f_begin; f < f_end; ++f) {
     if (f > f_begin) {
-      const float gm = gamma[bh * F + f];
+      const float gm = gamma ? gamma[bh * F + f] : 1.f;
 #pragma unroll
       for (int c = 0; c < EPT; ++c) acc[c] *= gm;
       uacc *= gm;
     }
-    const TIn *kb = k + (bh * N + (int64_t)f * T) * D;
-    const TIn *vb = v + (bh * N + (int64_t)f * T) * D;
+    const TIn *kb = kslab + (int64_t)f * T * kview.sn;
+    const TIn *vb = vslab + (int64_t)f * T * vview.sn;
     for (int64_t c0 = t0; c0 < t1; c0 += kKvTile) {
       const int n = (int)min((int64_t)kKvTile, t1 - c0);
       __syncthreads();
@@ -68,16 +80,30 @@ __global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict
         const int tt = e / D, ii = e % D;
         float kk = 0.f, vv = 0.f;
         if (tt < n) {
-          kk = relu(Elem<TIn>::load(kb, (c0 + tt) * D + ii));
-          vv = Elem<TIn>::load(vb, (c0 + tt) * D + ii);
+          kk = relu(Elem<TIn>::load(kb, (c0 + tt) * kview.sn + ii));
+          vv = Elem<TIn>::load(vb, (c0 + tt) * vview.sn + ii);
         }
         sk[tt][ii] = kk;
         sv[tt][ii] = vv;
       }
+      if constexpr (kRope) {
+        __syncthreads();
+        // turn each pair of phi(k) by its token's full rotation; keep the
+        // unturned copy for z
+        for (int e = tid; e < kKvTile * (D / 2); e += kThreads) {
+          const int tt = e / (D / 2), pp = e % (D / 2);
+          const float a = sk[tt][2 * pp], b = sk[tt][2 * pp + 1];
+          su[tt][2 * pp] = a;
+          su[tt][2 * pp + 1] = b;
+          const float2 ab = rotate_pair(a, b, token_rope_cs(rope, f, (int)(c0 + tt), pp));
+          sk[tt][2 * pp] = ab.x;
+          sk[tt][2 * pp + 1] = ab.y;
+        }
+      }
       __syncthreads();
       for (int tt = 0; tt < n; ++tt) {
         const float kk = sk[tt][i];
-        uacc += kk;
+        uacc += kRope ? su[tt][i] : kk;
 #pragma unroll
         for (int c = 0; c < EPT; ++c) acc[c] = fmaf(kk, sv[tt][jc + JS * c], acc[c]);
       }
@@ -92,40 +118,45 @@ __global__ __launch_bounds__(kThreads) void kv_valu_kernel(const TIn *__restrict
 // One workgroup per (slab, frame, split). Thread layout: 4 value columns
 // j = 4 * (tid % (D/4)) .. +3 of token tid / (D/4) of the current tile. phi(q)
 // of the tile is staged in LDS; S_f comes from LDS (D <= 64) or global memory.
-template <typename TIn, int D>
+template <typename TIn, int D, bool kRope>
 __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
-    const TIn *__restrict__ q, const TIn *__restrict__ g, TIn *__restrict__ o,
-    const float *__restrict__ gamma, const float *__restrict__ ws, int F, int64_t T, int P,
-    int G, int64_t carry_offset, int R, int64_t read_len, float eps) {
+    View qview, View gview, View oview, int H, const float *__restrict__ gamma,
+    const float *__restrict__ ws, int F, int64_t T, int P, int G, int64_t carry_offset, int R,
+    int64_t read_len, float eps, int state_frame, RopeK rope) {
   constexpr int CG = D / 4;             // column groups
   constexpr int TT = kThreads / CG;     // tokens per tile
   constexpr bool kSInLds = (D <= 64);
   __shared__ float sS[kSInLds ? D * D : 1];
   __shared__ float sz[D];
-  __shared__ float sq[TT][D];
+  __shared__ float sq[TT][D];                  // phi(q), turned with kRope (numerator)
+  __shared__ float sqd[kRope ? TT : 1][D];     // kRope: phi(q) unturned (normaliser)
 
   const int tid = threadIdx.x;
   const int64_t wg = blockIdx.x;
   const int r = (int)(wg % R);
   const int f = (int)((wg / R) % F);
   const int64_t bh = wg / ((int64_t)R * F);
-  const int64_t N = (int64_t)F * T;
   const int64_t t0 = min((int64_t)r * read_len, T);
   const int64_t t1 = min(t0 + read_len, T);
   if (t0 >= t1) return;
 
-  // S_f = S_loc_f + w_f * carry of the frame's group
+  // S_fs = S_loc_fs + w * carry of the group (fs: the frame's own state, or
+  // the one all frames share)
+  const int fs = state_frame >= 0 ? state_frame : f;
   constexpr int64_t E = (int64_t)D * D + D;
   const int NG = (F + G - 1) / G;
-  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;
+  const float *Sg = ws + ((bh * F + fs) * (int64_t)P) * E;
   // G == 1: the carry kernel has completed S_f in place (no carries kept)
-  const float *Cg = G > 1 ? ws + carry_offset + (bh * NG + f / G) * E : Sg;
-  const float w = G > 1 ? carry_weight(gamma ? gamma + bh * F : nullptr, f, G) : 0.f;
+  const float *Cg = G > 1 ? ws + carry_offset + (bh * NG + fs / G) * E : Sg;
+  const float w = G > 1 ? carry_weight(gamma ? gamma + bh * F : nullptr, fs, G) : 0.f;
   if (kSInLds)
     for (int e = tid; e < D * D; e += kThreads) sS[e] = fmaf(w, Cg[e], Sg[e]);
   for (int e = tid; e < D; e += kThreads) sz[e] = fmaf(w, Cg[D * D + e], Sg[D * D + e]);
 
-  const int64_t row0 = bh * N + (int64_t)f * T;
+  const int64_t trow0 = (int64_t)f * T;
+  const TIn *qs = static_cast<const TIn *>(qview.data) + qview.slab(bh, H);
+  const TIn *gs = static_cast<const TIn *>(gview.data) + gview.slab(bh, H);
+  TIn *os = const_cast<TIn *>(static_cast<const TIn *>(oview.data)) + oview.slab(bh, H);
   const int cg = tid % CG;
   const int tl = tid / CG;
 
@@ -134,7 +165,20 @@ __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
     __syncthreads();
     for (int e = tid; e < TT * D; e += kThreads) {
       const int tt = e / D, ii = e % D;
-      sq[tt][ii] = (tt < n) ? relu(Elem<TIn>::load(q, (row0 + c0 + tt) * D + ii)) : 0.f;
+      sq[tt][ii] =
+          (tt < n) ? relu(Elem<TIn>::load(qs, (trow0 + c0 + tt) * qview.sn + ii)) : 0.f;
+    }
+    if constexpr (kRope) {
+      __syncthreads();
+      for (int e = tid; e < TT * (D / 2); e += kThreads) {
+        const int tt = e / (D / 2), pp = e % (D / 2);
+        const float a = sq[tt][2 * pp], b = sq[tt][2 * pp + 1];
+        sqd[tt][2 * pp] = a;
+        sqd[tt][2 * pp + 1] = b;
+        const float2 ab = rotate_pair(a, b, token_rope_cs(rope, f, (int)(c0 + tt), pp));
+        sq[tt][2 * pp] = ab.x;
+        sq[tt][2 * pp + 1] = ab.y;
+      }
     }
     __syncthreads();
     if (tl < n) {
@@ -142,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
       float den = 0.f;
       for (int ii = 0; ii < D; ++ii) {
         const float qi = sq[tl][ii];
-        den = fmaf(qi, sz[ii], den);
+        den = fmaf(kRope ? sqd[tl][ii] : qi, sz[ii], den);
         float4 s4;
         if (kSInLds) {
           s4 = *reinterpret_cast<const float4 *>(sS + ii * D + 4 * cg);
@@ -158,61 +202,65 @@ __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
         num.w = fmaf(qi, s4.w, num.w);
       }
       const float inv = 1.f / (den + eps);
-      const int64_t off = (row0 + c0 + tl) * D + 4 * cg;
-      const float4 gg = Elem<TIn>::load4(g, off);
+      const int64_t row = trow0 + c0 + tl;
+      const float4 gg = Elem<TIn>::load4(gs, row * gview.sn + 4 * cg);
       float4 out;
       out.x = sigmoid(gg.x) * (num.x * inv);
       out.y = sigmoid(gg.y) * (num.y * inv);
       out.z = sigmoid(gg.z) * (num.z * inv);
       out.w = sigmoid(gg.w) * (num.w * inv);
-      Elem<TIn>::store4(o, off, out);
+      Elem<TIn>::store4(os, row * oview.sn + 4 * cg, out);
     }
   }
+}
+
+template <typename TIn, int D>
+void kv_valu_launch(const Plan &p, const KvArgs &a, int64_t grid, hipStream_t s) {
+  if (a.rope.on)
+    hipLaunchKernelGGL((kv_valu_kernel<TIn, D, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       s, a.k, a.v, a.H, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len, a.rope);
+  else
+    hipLaunchKernelGGL((kv_valu_kernel<TIn, D, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       s, a.k, a.v, a.H, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len, a.rope);
 }
 
 template <typename TIn>
 hipError_t kv_valu_dispatch(const Plan &p, const KvArgs &a, hipStream_t s) {
   const int64_t grid = p.BH * p.NG * p.P;
-  const TIn *k = static_cast<const TIn *>(a.k);
-  const TIn *v = static_cast<const TIn *>(a.v);
-#define GLA_KV_CASE(DD)                                                                   \
-  case DD:                                                                                \
-    hipLaunchKernelGGL((kv_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), 0, \
-                       s, k, v, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.part_len);           \
-    break;
   switch (p.d) {
-    GLA_KV_CASE(16)
-    GLA_KV_CASE(32)
-    GLA_KV_CASE(64)
-    GLA_KV_CASE(128)
+    case 16: kv_valu_launch<TIn, 16>(p, a, grid, s); break;
+    case 32: kv_valu_launch<TIn, 32>(p, a, grid, s); break;
+    case 64: kv_valu_launch<TIn, 64>(p, a, grid, s); break;
+    case 128: kv_valu_launch<TIn, 128>(p, a, grid, s); break;
     default:
       return hipErrorInvalidValue;
   }
-#undef GLA_KV_CASE
   return hipGetLastError();
+}
+
+template <typename TIn, int D>
+void readout_valu_launch(const Plan &p, const ReadoutArgs &a, int64_t grid, hipStream_t s) {
+  if (a.rope.on)
+    hipLaunchKernelGGL((readout_valu_kernel<TIn, D, true>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, s, a.q, a.g, a.o, a.H, a.gamma, a.ws, p.F, p.T, p.P,
+                       p.G, p.carry_offset(), p.R, p.read_len, a.eps, a.state_frame, a.rope);
+  else
+    hipLaunchKernelGGL((readout_valu_kernel<TIn, D, false>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, s, a.q, a.g, a.o, a.H, a.gamma, a.ws, p.F, p.T, p.P,
+                       p.G, p.carry_offset(), p.R, p.read_len, a.eps, a.state_frame, a.rope);
 }
 
 template <typename TIn>
 hipError_t readout_valu_dispatch(const Plan &p, const ReadoutArgs &a, hipStream_t s) {
   const int64_t grid = p.BH * p.F * p.R;
-  const TIn *q = static_cast<const TIn *>(a.q);
-  const TIn *g = static_cast<const TIn *>(a.g);
-  TIn *o = static_cast<TIn *>(a.o);
-#define GLA_RO_CASE(DD)                                                                     \
-  case DD:                                                                                  \
-    hipLaunchKernelGGL((readout_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), \
-                       0, s, q, g, o, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(), \
-                       p.R, p.read_len, a.eps);                                             \
-    break;
   switch (p.d) {
-    GLA_RO_CASE(16)
-    GLA_RO_CASE(32)
-    GLA_RO_CASE(64)
-    GLA_RO_CASE(128)
+    case 16: readout_valu_launch<TIn, 16>(p, a, grid, s); break;
+    case 32: readout_valu_launch<TIn, 32>(p, a, grid, s); break;
+    case 64: readout_valu_launch<TIn, 64>(p, a, grid, s); break;
+    case 128: readout_valu_launch<TIn, 128>(p, a, grid, s); break;
     default:
       return hipErrorInvalidValue;
   }
-#undef GLA_RO_CASE
   return hipGetLastError();
 }
 

@@ -101,6 +101,93 @@ gla_status gla_state_carry(const void *k, const void *v, const float *gamma, con
                            const float *z_in, float *S_out, float *z_out, int B, int H, int F,
                            int T, int d, gla_dtype dt, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- strided tensors and fused 3D rotary positions ------------------------
+ *
+ * The *_ex entry points compute the same operation as the plain ones, with
+ * two additions:
+ *
+ * 1. Any layout whose feature axis is contiguous. A gla_tensor describes a
+ *    [B][H][N][d] tensor whose element (b, h, n, c) sits at
+ *      data + b * stride_b + h * stride_h + n * stride_n + c
+ *    (strides in elements, >= 0). Examples: [B][N][H][d] is stride_b = N*H*d,
+ *    stride_h = d, stride_n = H*d; the q, k, v of a fused [B][N][3][H][d]
+ *    projection are three such views with stride_n = 3*H*d, 1 apart in the
+ *    "3" axis. Every row must start 16-byte aligned: data 16-byte aligned and
+ *    each stride a multiple of 16 bytes. Inputs may share memory and may
+ *    broadcast (a zero stride). The output may overlap no input, state or the
+ *    workspace (checked on the address span of each view: GLA_ERR_ALIAS), and
+ *    distinct (b, h, n) of it must be distinct rows (GLA_ERR_ALIAS). A NULL
+ *    gla_tensor pointer, or a NULL data, is an absent tensor.
+ *
+ * 2. Optional 3D rotary positions (rope != NULL). The SANA-Video ICLR 2026
+ *    oral talk (passage on temporal modeling) adds 3D RoPE to the linear
+ *    attention without saying where it acts; this library takes the rotary
+ *    linear attention of RoFormer (section 3.3): the numerator uses turned
+ *    features, the normaliser does not,
+ *      o_n = sigma(g_n) (.) (sum_s (R_n phi(q_n))^T (R_s phi(k_s)) v_s^T) /
+ *            (phi(q_n)^T sum_s phi(k_s) + eps),
+ *    with the sums running over the keys that token n sees (all keys, or the
+ *    decayed frame-causal prefix) and R_n the rotation of token n's position.
+ *    Token l of frame f sits at (t, y, x) = (frame_offset + f, l / grid_w,
+ *    l % grid_w); T must equal grid_h * grid_w. Feature pairs (2p, 2p+1) form
+ *    three consecutive sections of dim_t / 2, dim_h / 2 and dim_w / 2 pairs
+ *    (dim_* even, >= 0, summing to d) that turn with t, y and x respectively;
+ *    pair j of an m-pair section turns by the angle pos * theta^(-j / m):
+ *    (a, b) -> (a cos - b sin, a sin + b cos). theta must be finite and > 0;
+ *    |frame_offset| and F must be below 2^30. The carried state S of the
+ *    frame-causal mode then holds turned keys at their absolute positions, so
+ *    a stream continued block by block passes each block's first frame as its
+ *    frame_offset. With the matrix-core kernels (bf16, d in {32, 64, 128})
+ *    the per-workgroup table of turns must fit:
+ *    1 + grid_h * dim_h / 2 + grid_w * dim_w / 2 + 8 * dim_t / 2 <= 3072,
+ *    else GLA_ERR_UNSUPPORTED; there the turned features are rounded to bf16
+ *    for the matrix cores.
+ */
+typedef struct gla_tensor {
+  void *data;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_n;
+} gla_tensor;
+
+typedef struct gla_rope3d {
+  int32_t grid_h;       /* token rows per frame */
+  int32_t grid_w;       /* tokens per row */
+  int32_t frame_offset; /* temporal position of the call's frame 0 */
+  int32_t dim_t;        /* features turning with the frame */
+  int32_t dim_h;        /* features turning with the row */
+  int32_t dim_w;        /* features turning with the column */
+  double theta;         /* frequency base */
+} gla_rope3d;
+
+/* Workspace of gla_fwd_bidir_ex: with rope, that of gla_fwd_framecausal for
+ * (B, H, F, T, d) (the positions need the frame structure); without, that of
+ * gla_fwd_bidir for N = F * T. The other two *_ex calls take the workspace
+ * of their plain counterparts. */
+size_t gla_fwd_bidir_ex_workspace(int B, int H, int F, int T, int d, const gla_rope3d *rope);
+
+/* gla_fwd_bidir over N = F * T tokens (F frames of T tokens: the frames only
+ * place the rotary positions). */
+gla_status gla_fwd_bidir_ex(const gla_tensor *q, const gla_tensor *k, const gla_tensor *v,
+                            const gla_tensor *g, const gla_tensor *o, int B, int H, int F, int T,
+                            int d, gla_dtype dt, float eps, const gla_rope3d *rope, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* gla_fwd_framecausal with strided tensors and optional rotary positions. */
+gla_status gla_fwd_framecausal_ex(const gla_tensor *q, const gla_tensor *k, const gla_tensor *v,
+                                  const gla_tensor *g, const float *gamma, const float *S_in,
+                                  const float *z_in, const gla_tensor *o, float *S_out,
+                                  float *z_out, int B, int H, int F, int T, int d, gla_dtype dt,
+                                  float eps, const gla_rope3d *rope, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/* gla_state_carry with strided tensors and optional rotary positions (the
+ * state then holds turned keys: it matches gla_fwd_framecausal_ex's S_out). */
+gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *v, const float *gamma,
+                              const float *S_in, const float *z_in, float *S_out, float *z_out,
+                              int B, int H, int F, int T, int d, gla_dtype dt,
+                              const gla_rope3d *rope, void *ws, size_t ws_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *gla_status_string(gla_status s);
 
@@ -108,7 +195,7 @@ const char *gla_status_string(gla_status s);
 const char *gla_last_error(void);
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
-int gla_version(void);
+int gla_version(void); /* 10100: adds the *_ex entry points */
 
 /* ---- kernel timing for measurement tools ---------------------------------
  * Between gla_profile_begin and gla_profile_end, every kernel launched by the

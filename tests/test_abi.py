@@ -51,7 +51,7 @@ def test_status_strings(lib):
     for s in range(9):
         assert lib.gla_status_string(s).decode()
     assert lib.gla_status_string(99).decode() == "unknown status"
-    assert lib.gla_version() == 10000
+    assert lib.gla_version() == 10100
 
 
 def test_workspace_sizes(lib):
@@ -161,3 +161,67 @@ def test_python_binding_refuses_cpu_tensors():
         gla.gla_fwd_bidir(x, x, x, x)
     with pytest.raises(TypeError):
         gla.gla_fwd_bidir(x.double(), x.double(), x.double(), x.double())
+
+
+def tview(data, sb, sh, sn):
+    return ctypes.byref(gla._Tensor(data or None, sb, sh, sn))
+
+
+def rope3d(gh=4, gw=8, off=0, dt_=16, dh=24, dw=24, theta=10000.0):
+    return ctypes.byref(gla.Rope3D(gh, gw, dt_, dh, dw, theta, off))
+
+
+def fc_ex(lib, q=None, k=None, v=None, g=None, o=None, rope="default", B=1, H=2, F=2, T=32,
+          d=64, dt=BF16, ws=FAKE + 0x8000000, wsb=1 << 30):
+    """framecausal_ex on [B][N][H][d] views (contiguous strides of that layout)"""
+    N = F * T
+    lay = (N * H * d, d, H * d)
+    q = q or tview(FAKE, *lay)
+    k = k or tview(FAKE + 0x1000000, *lay)
+    v = v or tview(FAKE + 0x2000000, *lay)
+    g = g or tview(FAKE + 0x3000000, *lay)
+    o = o or tview(FAKE + 0x4000000, *lay)
+    r = rope3d() if rope == "default" else rope
+    return lib.gla_fwd_framecausal_ex(q, k, v, g, p(FAKE + 0x5000000), None, None, o, None, None,
+                                      B, H, F, T, d, dt, 1e-6, r, p(ws), wsb, None)
+
+
+def test_ex_validation(lib):
+    N, H, d = 64, 2, 64
+    # rotary parameters
+    assert fc_ex(lib, rope=rope3d(gh=3)) == SHAPE  # grid does not hold T tokens
+    assert fc_ex(lib, rope=rope3d(dt_=15, dh=25)) == SHAPE  # odd sections
+    assert fc_ex(lib, rope=rope3d(dw=16)) == SHAPE  # sections do not sum to d
+    assert fc_ex(lib, rope=rope3d(dt_=-2, dh=42)) == SHAPE
+    assert fc_ex(lib, rope=rope3d(theta=0.0)) == VALUE
+    assert fc_ex(lib, rope=rope3d(theta=float("nan"))) == VALUE
+    assert fc_ex(lib, rope=rope3d(off=1 << 30)) == VALUE
+    # the matrix-core table: 1 + 1024 * 12 + 1 * 12 + 8 * 8 entries > 3072
+    assert fc_ex(lib, T=1024, rope=rope3d(gh=1024, gw=1)) == UNSUP
+    assert "rope table" in lib.gla_last_error().decode()
+    # strides
+    lay = (N * H * d, d, H * d)
+    assert fc_ex(lib, k=tview(FAKE + 0x1000000, lay[0], -d, lay[2])) == SHAPE
+    assert fc_ex(lib, v=tview(FAKE + 0x2000000, lay[0], d + 4, lay[2])) == ALIGN  # 8 bytes
+    assert fc_ex(lib, g=tview(FAKE + 0x3000008, *lay)) == ALIGN
+    # output rows that coincide, or an output reaching into an input
+    assert fc_ex(lib, o=tview(FAKE + 0x4000000, lay[0], d, 0)) == ALIAS
+    assert "rows overlap" in lib.gla_last_error().decode()
+    assert fc_ex(lib, o=tview(FAKE + 0x4000000, lay[0], 0, lay[2])) == ALIAS
+    assert fc_ex(lib, o=tview(FAKE + 0x100, *lay)) == ALIAS
+    # absent tensors
+    assert fc_ex(lib, q=tview(0, *lay)) == NULL
+    # empty problems pass validation and launch nothing
+    assert fc_ex(lib, B=0) == OK
+    # without rotary positions the same checks apply
+    assert fc_ex(lib, rope=None, o=tview(FAKE + 0x4000000, lay[0], d, 0)) == ALIAS
+
+
+def test_ex_workspace(lib):
+    r = gla.Rope3D(23, 40, 24, 20, 20, 10000.0)
+    # positions need the frame structure: the frame-causal workspace
+    assert gla.gla_fwd_bidir_ex_workspace(1, 32, 241, 920, 64, r) == \
+        gla.gla_fwd_framecausal_workspace(1, 32, 241, 920, 64)
+    # without them the sequence is one frame of F * T tokens
+    assert gla.gla_fwd_bidir_ex_workspace(1, 32, 21, 920, 64) == \
+        gla.gla_fwd_bidir_workspace(1, 32, 21 * 920, 64)
