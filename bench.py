@@ -39,6 +39,11 @@ def parse():
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5],
                     help="2 small, 3 720p/5s, 4 720p/60s (default), 5 streamed 8 blocks")
     ap.add_argument("--mode", default="framecausal", choices=["framecausal", "bidir"])
+    ap.add_argument("--layout", default="bhnd", choices=["bhnd", "fused"],
+                    help="bhnd: contiguous [B,H,N,d] tensors; fused: q, k, v as slices of one "
+                         "[B,N,3,H,d] projection, g and o [B,N,H,d] (the *_ex entry points)")
+    ap.add_argument("--rope", action="store_true",
+                    help="fused 3D rotary positions over the latent grid (the *_ex entry points)")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -132,9 +137,27 @@ def main():
     d = w.d
     S = torch.zeros((w.B, w.H, d, d), dtype=torch.float32, device=dev)
     z = torch.zeros((w.B, w.H, d), dtype=torch.float32, device=dev)
-    outs = [torch.empty_like(b["q"]) for b in blocks]
+    ex = args.layout != "bhnd" or args.rope
+    if args.layout == "fused":
+        # q, k, v as slices of one [B, N, 3, H, d] projection; g and o [B, N, H, d]
+        for b in blocks:
+            X = torch.stack([b.pop("q"), b.pop("k"), b.pop("v")], dim=0)
+            X = X.permute(1, 3, 0, 2, 4).contiguous()
+            b["q"], b["k"], b["v"] = (X[:, :, i].transpose(1, 2) for i in range(3))
+            b["g"] = b["g"].transpose(1, 2).contiguous().transpose(1, 2)
+        outs = [torch.empty((w.B, b["q"].shape[2], w.H, d), dtype=b["q"].dtype,
+                            device=dev).transpose(1, 2) for b in blocks]
+    else:
+        outs = [torch.empty_like(b["q"]) for b in blocks]
+    grid = synth.LATENT_GRID_720P if w.T == synth.LATENT_TOKENS_720P else None
+    if args.rope and grid is None:
+        print("bench.py: --rope needs the 720p latent grid", file=sys.stderr)
+        sys.exit(2)
+    bounds = synth.stream_block_bounds(w) if len(blocks) > 1 else [(0, w.F)]
+    ropes = [gla.Rope3D.video(grid[0], grid[1], d, frame_offset=f0) if args.rope else None
+             for f0, _ in bounds]
     if mode == "bidir":
-        wsb = gla.gla_fwd_bidir_workspace(w.B, w.H, w.N, d)
+        wsb = gla.gla_fwd_bidir_ex_workspace(w.B, w.H, w.F, w.T, d, ropes[0])
     else:
         wsb = max(gla.gla_fwd_framecausal_workspace(w.B, w.H, b["gamma"].shape[-1], w.T, d)
                   for b in blocks)
@@ -143,16 +166,27 @@ def main():
     def step():
         if mode == "bidir":
             b = blocks[0]
-            gla.gla_fwd_bidir(b["q"], b["k"], b["v"], b["g"], eps=w.eps, out=outs[0], workspace=ws)
+            if ex:
+                gla.gla_fwd_bidir_ex(b["q"], b["k"], b["v"], b["g"], eps=w.eps, rope=ropes[0],
+                                     frames=w.F, out=outs[0], workspace=ws)
+            else:
+                gla.gla_fwd_bidir(b["q"], b["k"], b["v"], b["g"], eps=w.eps, out=outs[0],
+                                  workspace=ws)
             return
         carry = len(blocks) > 1
         if carry:
             S.zero_()
             z.zero_()
-        for b, o in zip(blocks, outs):
-            gla.gla_fwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"],
-                                    S if carry else None, z if carry else None, eps=w.eps,
-                                    out=o, S_out=S, z_out=z, workspace=ws)
+        for b, o, r in zip(blocks, outs, ropes):
+            if ex:
+                gla.gla_fwd_framecausal_ex(b["q"], b["k"], b["v"], b["g"], b["gamma"],
+                                           S if carry else None, z if carry else None,
+                                           eps=w.eps, rope=r, out=o, S_out=S, z_out=z,
+                                           workspace=ws)
+            else:
+                gla.gla_fwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"],
+                                        S if carry else None, z if carry else None, eps=w.eps,
+                                        out=o, S_out=S, z_out=z, workspace=ws)
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -194,7 +228,9 @@ def main():
     dom = max(prof, key=lambda k: prof[k][1])
     dk = kernels[dom]
     achieved = dk["alg_bytes_per_launch"] / (dk["avg_ms"] / 1e3)
-    traffic_rec = committed_traffic(dom, w.name + "/" + mode)
+    variant = w.name + "/" + mode + ("/fused" if args.layout == "fused" else "") + \
+        ("/rope" if args.rope else "")
+    traffic_rec = committed_traffic(dom, variant)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                 "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
@@ -209,7 +245,8 @@ def main():
     cpu = None
     parity = None
     if not args.no_cpu and args.cpu_heads > 0:
-        cpu, parity = cpu_baseline(args, w, mode, blocks, outs, value)
+        cpu, parity = cpu_baseline(args, w, mode, blocks, outs, value,
+                                   ropes[0].as_dict() if args.rope else None)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -217,17 +254,20 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded normal draws in the latent-video shape; no dataset)",
         "config": {"workload": w.name, "mode": mode, "B": w.B, "H": w.H, "d": d, "F": w.F,
-                   "T": w.T, "N": w.N, "blocks": list(w.blocks) or [w.F], "eps": w.eps},
+                   "T": w.T, "N": w.N, "blocks": list(w.blocks) or [w.F], "eps": w.eps,
+                   "layout": ("q, k, v slices of [B,N,3,H,d]; g, o [B,N,H,d]"
+                              if args.layout == "fused" else "[B,H,N,d] contiguous"),
+                   "rope": ropes[0].as_dict() if args.rope else None},
         "roofline": roofline, "call": call, "kernels": kernels, "cpu_baseline": cpu,
         "parity": parity, "wall_s": round(wall, 3), "source_hash": source_hash(),
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(args, w, mode, blocks, outs, gpu_value):
-    """Time the fp64 oracle (recurrent form) on a bounded sample of heads of the
-    same workload, scale to tokens/s of the whole workload, and check the GPU
-    output of those heads against it."""
+def cpu_baseline(args, w, mode, blocks, outs, gpu_value, rope=None):
+    """Time the fp64 oracle (recurrent form, with rotary positions if rope) on a
+    bounded sample of heads of the same workload, scale to tokens/s of the whole
+    workload, and check the GPU output of those heads against it."""
     import numpy as np
     import torch
 
@@ -252,7 +292,16 @@ def cpu_baseline(args, w, mode, blocks, outs, gpu_value):
     print("bench: CPU oracle on %d heads, %d threads" % (nh, min(threads, ntask)),
           file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    if mode == "bidir":
+    if rope is not None:
+        # the whole stream from frame 0 (each block passed its first frame as offset)
+        r0 = dict(rope, frame_offset=0)
+        if mode == "bidir":
+            ref, _, _ = oracle.rope_recurrent(oracle.BIDIR, x["q"], x["k"], x["v"], x["g"],
+                                              F=w.F, T=w.T, eps=w.eps, rope=r0)
+        else:
+            ref, _, _ = oracle.rope_recurrent(oracle.FRAMECAUSAL, x["q"], x["k"], x["v"],
+                                              x["g"], gamma, eps=w.eps, rope=r0)
+    elif mode == "bidir":
         ref, _, _ = oracle.recurrent(oracle.BIDIR, x["q"], x["k"], x["v"], x["g"], eps=w.eps)
     else:
         ref, _, _ = oracle.recurrent(oracle.FRAMECAUSAL, x["q"], x["k"], x["v"], x["g"], gamma,
@@ -262,8 +311,10 @@ def cpu_baseline(args, w, mode, blocks, outs, gpu_value):
     cpu_tokens_per_s = nh * w.N / el / w.H
     cpu = {"value": round(cpu_tokens_per_s, 1), "unit": "tokens/s",
            "cores": int(min(threads, ntask)), "kind": "oracle",
-           "sample": "%d of %d heads (all %d tokens each), recurrent fp64 form, %.1f s; "
-                     "tokens/s = head-tokens/s / H" % (nh, w.B * w.H, w.N, el),
+           "sample": "%d of %d heads (all %d tokens each), recurrent fp64 form%s, %.1f s; "
+                     "tokens/s = head-tokens/s / H" % (nh, w.B * w.H, w.N,
+                                                       " with rotary positions" if rope else "",
+                                                       el),
            "host_cpu": host_cpu_model(), "gpu_over_cpu": round(gpu_value / cpu_tokens_per_s, 1)}
     o64 = oracle.bf16_to_f64(got) if got.dtype == np.uint16 else got.astype(np.float64)
     r2 = ref.reshape(1, nh, -1)

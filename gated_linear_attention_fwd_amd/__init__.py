@@ -81,6 +81,17 @@ class Rope3D(ctypes.Structure):
                  theta: float = 10000.0, frame_offset: int = 0):
         super().__init__(grid_h, grid_w, frame_offset, dim_t, dim_h, dim_w, theta)
 
+    @classmethod
+    def video(cls, grid_h: int, grid_w: int, d: int, theta: float = 10000.0,
+              frame_offset: int = 0) -> "Rope3D":
+        """The common video split of a head: 2 * (d // 6) features each for the
+        row and column axes, the rest (a multiple of 4) for the frame axis."""
+        s = 2 * (d // 6)
+        return cls(grid_h, grid_w, d - 2 * s, s, s, theta, frame_offset)
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
 
 def library_path() -> str:
     return _LIB_PATH

@@ -40,6 +40,12 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = 8;  // most frames per kv workgroup (the plan's limit)
 
+// Waves per SIMD the compiler must allow. The rotary variants at d <= 64 would
+// otherwise take 3 (accumulators in AGPRs on top of ~120 VGPRs); with all
+// registers in one file they fit 4, without spills. 1: no constraint.
+template <int D, bool kRope>
+constexpr int kMinWaves = (kRope && D <= 64) ? 4 : 1;
+
 // q, k, v and g are read exactly once and o is written once: nontemporal
 // loads and stores keep that stream from displacing lines the next kernel
 // reuses (measured on the 720p/60s shape: kv -10%, readout -7%). Every such
@@ -104,6 +110,13 @@ __device__ __forceinline__ uint32_t relu2(uint32_t w) {
 
 __device__ __forceinline__ uint4 relu8(uint4 x) {
   return make_uint4(relu2(x.x), relu2(x.y), relu2(x.z), relu2(x.w));
+}
+
+// Gate and normaliser of the epilogue with the hardware reciprocal (v_rcp_f32,
+// 1 ulp) rather than an IEEE division (~10 instructions each): the result is
+// rounded to bf16 right after. exp overflow still gives sigmoid = 0 exactly.
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -231,7 +244,8 @@ struct KvCfg {
 // across the group's frames so that the next chunk's loads (possibly the next
 // frame's) overlap the MFMAs and the write-out of the current one.
 template <int D, bool kRope>
-__global__ __launch_bounds__(kThreads) void kv_mfma_kernel(View kview, View vview, int H,
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(View kview, View vview, int H,
                                                            const float *__restrict__ gamma,
                                                            float *__restrict__ ws, int F,
                                                            int64_t T, int P, int G,
@@ -276,20 +290,33 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(View kview, View vvie
   const int r0 = tid / C::ROW_CHUNKS;
   [[maybe_unused]] const PieceRope prope(rope, c);
   uint4 rk[C::CPT], rv[C::CPT];
-  auto load = [&](int chunk) {
-    const int fi = chunk / ncf;
-    const int base = (chunk - fi * ncf) * C::CH;
+  // Chunks are loaded in order (frame by frame): the addresses of this
+  // thread's pieces advance by additions only.
+  const uint4 *kp = kb + (int64_t)r0 * snk + c, *vp = vb + (int64_t)r0 * snv + c;
+  const int64_t k_pass = C::ROWS_PER_PASS * snk, v_pass = C::ROWS_PER_PASS * snv;
+  // from a frame's last chunk to the next frame's first: T - (ncf - 1) * CH rows
+  const int64_t jump_rows = T - (int64_t)(ncf > 0 ? ncf - 1 : 0) * C::CH;
+  int lcc = 0;  // chunk index within its frame of the next load
+  auto load = [&]() {
+    const int base = lcc * C::CH;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = base + r0 + i * C::ROWS_PER_PASS;
       if (row < L) {
-        const int64_t trow = (int64_t)fi * T + row;
-        rk[i] = ld_stream16<GLA_KV_NT_LOADS>(kb + trow * snk + c);
-        rv[i] = ld_stream16<GLA_KV_NT_LOADS>(vb + trow * snv + c);
+        rk[i] = ld_stream16<GLA_KV_NT_LOADS>(kp + i * k_pass);
+        rv[i] = ld_stream16<GLA_KV_NT_LOADS>(vp + i * v_pass);
       } else {
         rk[i] = make_uint4(0, 0, 0, 0);
         rv[i] = make_uint4(0, 0, 0, 0);
       }
+    }
+    if (++lcc == ncf) {  // on to the next frame's first chunk
+      lcc = 0;
+      kp += jump_rows * snk;
+      vp += jump_rows * snv;
+    } else {
+      kp += C::CH * snk;
+      vp += C::CH * snv;
     }
   };
 
@@ -447,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(View kview, View vvie
   };
 
   int pending = -1;  // frame whose slot is still to be written
-  if (total > 0) load(0);
+  if (total > 0) load();
   for (int fi = 0; fi < nf; ++fi) {
     if (fi > 0) {
 #pragma unroll
@@ -492,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void kv_mfma_kernel(View kview, View vvie
         store_state(pending);
         pending = -1;
       }
-      if (ch + 1 < total) load(ch + 1);
+      if (ch + 1 < total) load();
 
       constexpr int KS_PER_WAVE = C::kSplitTokens ? 1 : 4;
 #pragma unroll
@@ -551,7 +578,8 @@ struct RoCfg {
 //   3. o = sigmoid(g) * acc / (den + eps) -> bf16, written over g in LDS
 //   4. o rows -> global memory
 template <int D, bool kRope>
-__global__ __launch_bounds__(kThreads) void readout_kernel(
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
     View qview, View gview, View oview, int H, const float *__restrict__ gamma,
     const float *__restrict__ ws, int F, int64_t T, int P, int G, int64_t carry_offset, int R,
     int64_t read_len, float eps, int state_frame, RopeK rope) {
@@ -663,18 +691,25 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
   uint4 *ob = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(
       static_cast<const uint16_t *>(oview.data) + oview.slab(bh, H) + trow0 * oview.sn));
   [[maybe_unused]] const PieceRope prope(rope, c);
+  // this thread's piece of its first row in the block; blocks are visited in
+  // order, so the addresses advance by additions only
+  const uint4 *qp = qb + (int64_t)r0 * snq + c;
+  const uint4 *gp = gb + (int64_t)r0 * sng + c;
+  const int64_t q_pass = C::ROWS_PER_PASS * snq, g_pass = C::ROWS_PER_PASS * sng;
   uint4 rq[C::CPT], rgv[C::CPT];
   auto load = [&](int blk) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = blk * C::BLK + r0 + i * C::ROWS_PER_PASS;
       const bool ok = row < L;
-      rq[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(qb + (int64_t)row * snq + c)
-                 : make_uint4(0, 0, 0, 0);
-      rgv[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(gb + (int64_t)row * sng + c)
-                  : make_uint4(0, 0, 0, 0);
+      rq[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(qp + i * q_pass) : make_uint4(0, 0, 0, 0);
+      rgv[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(gp + i * g_pass) : make_uint4(0, 0, 0, 0);
     }
+    qp += C::BLK * snq;
+    gp += C::BLK * sng;
   };
+  uint4 *op = ob + (int64_t)r0 * sno + c;
+  const int64_t o_pass = C::ROWS_PER_PASS * sno;
 
   const int tl = 32 * tg + (lane & 31);
   const int nblk = (L + C::BLK - 1) / C::BLK;
@@ -728,15 +763,15 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
         acc = mfma_32x32x16(ahi[ks], __builtin_bit_cast(bf16x8, bl), acc);
       }
     }
-    const float inv = 1.f / (den_s[tl] + eps);
+    const float inv = __builtin_amdgcn_rcpf(den_s[tl] + eps);
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       uint2 *cell = reinterpret_cast<uint2 *>(gtile + tl * GP + (32 * mb + 8 * rg + 4 * h) * 2);
       const uint2 gv = *cell;
-      const float o0 = sigmoid(lo_bf16(gv.x)) * (acc[4 * rg + 0] * inv);
-      const float o1 = sigmoid(hi_bf16(gv.x)) * (acc[4 * rg + 1] * inv);
-      const float o2 = sigmoid(lo_bf16(gv.y)) * (acc[4 * rg + 2] * inv);
-      const float o3 = sigmoid(hi_bf16(gv.y)) * (acc[4 * rg + 3] * inv);
+      const float o0 = fast_sigmoid(lo_bf16(gv.x)) * (acc[4 * rg + 0] * inv);
+      const float o1 = fast_sigmoid(hi_bf16(gv.x)) * (acc[4 * rg + 1] * inv);
+      const float o2 = fast_sigmoid(lo_bf16(gv.y)) * (acc[4 * rg + 2] * inv);
+      const float o3 = fast_sigmoid(hi_bf16(gv.y)) * (acc[4 * rg + 3] * inv);
       uint2 ow;
       ow.x = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
       ow.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
@@ -751,12 +786,13 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(
         const uint4 ov = *reinterpret_cast<const uint4 *>(gtile + row * GP + c * 16);
         if constexpr (GLA_RO_NT_STORES != 0) {
           const u32x4 x = {ov.x, ov.y, ov.z, ov.w};
-          __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(ob + (int64_t)tok * sno + c));
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(op + i * o_pass));
         } else {
-          ob[(int64_t)tok * sno + c] = ov;
+          op[i * o_pass] = ov;
         }
       }
     }
+    op += C::BLK * sno;
   }
 }
 

@@ -27,7 +27,8 @@ from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
-LATENT_TOKENS_720P = 23 * 40  # 736 x 1280 at 32x spatial compression
+LATENT_GRID_720P = (23, 40)  # latent rows x columns of a 736 x 1280 frame at 32x compression
+LATENT_TOKENS_720P = LATENT_GRID_720P[0] * LATENT_GRID_720P[1]
 
 
 @dataclass(frozen=True)
