@@ -229,6 +229,13 @@ gla_status make_rope(const gla_rope3d *r, int F, int64_t T, int d, RopeK *out) {
   return GLA_OK;
 }
 
+// Work order of the matrix-core kernels for a view: slab fastest when heads sit
+// closer together than tokens. GLA_HEADS_FASTEST=0/1 overrides (measurement).
+int heads_fastest(const View &v) {
+  if (const char *e = getenv("GLA_HEADS_FASTEST")) return atoi(e) != 0;
+  return v.sh < v.sn ? 1 : 0;
+}
+
 enum class Mode { kBidir, kFrameCausal, kStateCarry };
 
 // The body of every entry point. Bidirectional calls take F frames of T tokens
@@ -321,6 +328,10 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
   hipStream_t s = static_cast<hipStream_t>(stream);
   float *wsf = static_cast<float *>(ws);
   const float *gm = bidir ? nullptr : gamma;
+  // Heads side by side within a token (head stride below the token stride, as
+  // in [B][N][H][d] or a fused projection): the readout orders its work with
+  // the slab fastest so that concurrent workgroups read neighbouring lines.
+  const int ro_heads = heads_fastest(vq);
   if (p.F > 0)
     GLA_TRY(launched(timed(kKindKv, s,
                            [&] {
@@ -331,7 +342,8 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
                      S_out, z_out, outputs ? 1 : 0};
   GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, sa, s); }), "carry"));
   if (outputs && have_tokens) {
-    const ReadoutArgs ra{vq, vg, vo, H, gm, wsf, eps, (bidir && !flat) ? p.F - 1 : -1, rk_};
+    const ReadoutArgs ra{vq, vg, vo, H, gm, wsf, eps, (bidir && !flat) ? p.F - 1 : -1, rk_,
+                         ro_heads};
     GLA_TRY(launched(timed(kKindReadout, s, [&] { return launch_readout(p, dt, path, ra, s); }),
                      "readout"));
   }

@@ -582,7 +582,7 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
     View qview, View gview, View oview, int H, const float *__restrict__ gamma,
     const float *__restrict__ ws, int F, int64_t T, int P, int G, int64_t carry_offset, int R,
-    int64_t read_len, float eps, int state_frame, RopeK rope) {
+    int64_t read_len, float eps, int state_frame, RopeK rope, int heads_fastest) {
   using C = RoCfg<D>;
   constexpr int GP = 2 * D + 16;  // bytes per LDS row of g / o
   __shared__ __attribute__((aligned(16))) char qtile[C::BLK * C::PITCH];
@@ -597,10 +597,24 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
   const int h = lane >> 5;
   const int mb = wave % C::MB;
   const int tg = wave / C::MB;
-  const int64_t wg = GLA_RO_XCD_REMAP ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int r = (int)(wg % R);
-  const int f = (int)((wg / R) % F);
-  const int64_t bh = wg / ((int64_t)R * F);
+  // work item order (after the XCD renumbering): (slab slowest, frame, split
+  // fastest), or with heads_fastest (frame slowest, split, slab fastest) -- for
+  // layouts whose heads sit side by side within a token: concurrent workgroups
+  // then read neighbouring lines (720p/60s, fused [B,N,3,H,d] q: readout -6%;
+  // the same order for kv measured neutral at d = 64 and slower at d = 128)
+  const int wg = (int)(GLA_RO_XCD_REMAP ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x);
+  int r, f, bhi;
+  if (heads_fastest) {
+    const int nbh = (int)gridDim.x / (R * F);
+    bhi = wg % nbh;
+    r = (wg / nbh) % R;
+    f = wg / (nbh * R);
+  } else {
+    r = wg % R;
+    f = (wg / R) % F;
+    bhi = wg / (R * F);
+  }
+  const int64_t bh = bhi;
   const int64_t t0 = min((int64_t)r * read_len, T);
   const int64_t t1 = min(t0 + read_len, T);
   const int L = (int)(t1 - t0);
@@ -809,7 +823,7 @@ void readout_launch(const Plan &p, const ReadoutArgs &a, RopeK rope, int64_t gri
   const size_t lds = kRope ? (size_t)rope.entries() * sizeof(float2) : 0;
   hipLaunchKernelGGL((readout_kernel<D, kRope>), dim3((unsigned)grid), dim3(kThreads), lds, s,
                      a.q, a.g, a.o, a.H, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(),
-                     p.R, p.read_len, a.eps, a.state_frame, rope);
+                     p.R, p.read_len, a.eps, a.state_frame, rope, a.heads_fastest);
 }
 
 }  // namespace

@@ -124,6 +124,7 @@ struct ReadoutArgs {
   float eps;
   int state_frame;     // -1: every frame reads its own state; else all read this one
   RopeK rope;
+  int heads_fastest;   // 1: work items ordered with the slab fastest (matrix-core kernels)
 };
 
 // Decay weight of a frame's carry-in: prod_{m = first frame of f's group}^{f} gamma_m.
