@@ -89,6 +89,9 @@ def _load():
     lib.gla_oracle_rope_quadratic.argtypes = common[:10] + common[12:] + [
         ctypes.POINTER(Rope), ctypes.c_int]
     lib.gla_oracle_rope_quadratic.restype = ctypes.c_int
+    lib.gla_oracle_backward.argtypes = [ctypes.c_int, ctypes.c_int] + [vp] * 17 + [
+        ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_int]
+    lib.gla_oracle_backward.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -228,6 +231,42 @@ def rope_quadratic(mode, q, k, v, g, gamma=None, S_in=None, z_in=None, F=None, T
                                   _ptr(S_in), _ptr(z_in), _ptr(o), B, H, F, T, d, float(eps),
                                   ctypes.byref(r), int(nthreads))
     return o
+
+
+def backward(mode, q, k, v, g, dO, gamma=None, S_in=None, z_in=None, dS_out=None,
+             dz_out=None, F=None, T=None, eps=1e-6, nthreads=0):
+    """Gradients of the forward definition (chain rule, fp64) for
+    dL/do = dO and, in frame-causal mode, dL/dS_out = dS_out, dL/dz_out = dz_out.
+
+    Returns a dict with dq, dk, dv, dg ([B, H, N, d] float64) and, in
+    frame-causal mode, dgamma [B, H, F], dS_in [B, H, d, d], dz_in [B, H, d]."""
+    (q, k, v, g, gamma, S_in, z_in, _, _, _, B, H, F, T, d, dt) = _prep(
+        mode, q, k, v, g, gamma, S_in, z_in, F, T, True)
+    dO = np.ascontiguousarray(bf16_to_f64(dO) if np.asarray(dO).dtype == np.uint16
+                              else np.asarray(dO, np.float64))
+    if dO.shape != (B, H, F * T, d):
+        raise ValueError("dO must be [B, H, N, d]")
+    causal = mode == FRAMECAUSAL
+    if causal and dS_out is not None:
+        dS_out = np.ascontiguousarray(np.asarray(dS_out, np.float64).reshape(B, H, d, d))
+    else:
+        dS_out = None
+    if causal and dz_out is not None:
+        dz_out = np.ascontiguousarray(np.asarray(dz_out, np.float64).reshape(B, H, d))
+    else:
+        dz_out = None
+    shape = (B, H, F * T, d)
+    out = {n: np.empty(shape, np.float64) for n in ("dq", "dk", "dv", "dg")}
+    if causal:
+        out["dgamma"] = np.empty((B, H, F), np.float64)
+        out["dS_in"] = np.empty((B, H, d, d), np.float64)
+        out["dz_in"] = np.empty((B, H, d), np.float64)
+    _load().gla_oracle_backward(
+        mode, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in),
+        _ptr(dO), _ptr(dS_out), _ptr(dz_out), _ptr(out["dq"]), _ptr(out["dk"]),
+        _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out.get("dgamma")), _ptr(out.get("dS_in")),
+        _ptr(out.get("dz_in")), B, H, F, T, d, float(eps), int(nthreads))
+    return out
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -517,3 +517,145 @@ int gla_oracle_rope_quadratic(int mode, int dt, const void *q, const void *k, co
   }
   return used;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward: gradients of the definition above                               */
+/* ------------------------------------------------------------------------ */
+/*
+ * The pages state the forward pass only; these are the chain rule through its
+ * definition, taken in reverse order of the forward steps. With
+ *   h_t = num_t / (den_t + eps),  o_t = sigma(g_t) (.) h_t,
+ * for a loss L whose gradients are dO = dL/do, dS_out = dL/dS_out and
+ * dz_out = dL/dz_out:
+ *   dg_t   = dO_t (.) h_t (.) sigma(g_t) (1 - sigma(g_t))
+ *   dnum_t = dO_t (.) sigma(g_t) / (den_t + eps)
+ *   dden_t = -((dO_t (.) sigma(g_t)) . h_t) / (den_t + eps)
+ *   dq_t   = [q_t > 0] (.) (S_f dnum_t + dden_t z_f)              t in frame f
+ *   adjoint of S_f:  Sh_f = sum_{t in f} phi(q_t) dnum_t^T + gamma_{f+1} Sh_{f+1}
+ *                    (Sh_{F-1} = its frame's sum + dS_out); zh_f likewise,
+ *                    with dden_t phi(q_t) and dz_out
+ *   dk_t   = [k_t > 0] (.) (Sh_f v_t + zh_f),   dv_t = Sh_f^T phi(k_t)
+ *   dgamma_f = <Sh_f, S_{f-1}> + <zh_f, z_{f-1}>   (Frobenius products)
+ *   dS_in  = gamma_0 Sh_0,  dz_in = gamma_0 zh_0
+ * The derivative of ReLU is taken as 0 at 0. Bidirectional mode is one frame
+ * of all N tokens with no decay and no carried state (dgamma, dS_in, dz_in
+ * are then not written).
+ *
+ * dO, dS_out, dz_out are float64 (dS_out/dz_out may be NULL: zero); dq, dk,
+ * dv, dg are float64 [B][H][N][d]; dgamma [B][H][F]; dS_in [B][H][d][d] and
+ * dz_in [B][H][d] may be NULL. OpenMP over slabs.
+ */
+int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const void *v,
+                        const void *g, const double *gamma, const double *S_in,
+                        const double *z_in, const double *dO, const double *dS_out,
+                        const double *dz_out, double *dq, double *dk, double *dv, double *dg,
+                        double *dgamma, double *dS_in, double *dz_in, int B, int H, int F, int T,
+                        int d, double eps, int nthreads) {
+  const long nslab = (long)B * H;
+  const size_t N = (size_t)F * T, dd = (size_t)d * d;
+  const int used = set_threads(nthreads);
+  const int causal = mode == ORC_FRAMECAUSAL;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < nslab; ++bh) {
+    double *S = (double *)calloc((size_t)(F + 1) * dd, sizeof(double)); /* S[f+1] = S_f */
+    double *z = (double *)calloc((size_t)(F + 1) * d, sizeof(double));
+    double *G = (double *)calloc((size_t)F * dd + 1, sizeof(double));   /* readout sums */
+    double *gz = (double *)calloc((size_t)F * d + 1, sizeof(double));
+    double *A = (double *)calloc(dd, sizeof(double));                   /* incoming adjoint */
+    double *az = (double *)calloc((size_t)d, sizeof(double));
+    double *Sh = (double *)malloc(dd * sizeof(double));
+    double *zh = (double *)malloc((size_t)d * sizeof(double));
+    double *fq = (double *)malloc((size_t)d * sizeof(double));
+    double *h = (double *)malloc((size_t)d * sizeof(double));
+    double *dn = (double *)malloc((size_t)d * sizeof(double));
+    const size_t base = (size_t)bh * N * d;
+
+    /* forward states S_{-1} .. S_{F-1} */
+    if (causal && S_in) memcpy(S, S_in + (size_t)bh * dd, dd * sizeof(double));
+    if (causal && z_in) memcpy(z, z_in + (size_t)bh * d, (size_t)d * sizeof(double));
+    for (int f = 0; f < F; ++f) {
+      const double gm = causal ? gamma[(size_t)bh * F + f] : 1.0;
+      double *Sc = S + (size_t)(f + 1) * dd, *zc = z + (size_t)(f + 1) * d;
+      for (size_t e = 0; e < dd; ++e) Sc[e] = gm * S[(size_t)f * dd + e];
+      for (int i = 0; i < d; ++i) zc[i] = gm * z[(size_t)f * d + i];
+      for (int t = 0; t < T; ++t) {
+        const size_t row = base + ((size_t)f * T + t) * d;
+        for (int i = 0; i < d; ++i) {
+          const double ki = relu(ld(k, dt, row + i));
+          zc[i] += ki;
+          for (int j = 0; j < d; ++j) Sc[(size_t)i * d + j] += ki * ld(v, dt, row + j);
+        }
+      }
+    }
+
+    /* readout side: dg, dq and the per-frame sums that feed the adjoints */
+    for (int f = 0; f < F; ++f) {
+      const double *Sc = S + (size_t)(f + 1) * dd, *zc = z + (size_t)(f + 1) * d;
+      double *Gf = G + (size_t)f * dd, *gzf = gz + (size_t)f * d;
+      for (int t = 0; t < T; ++t) {
+        const size_t row = base + ((size_t)f * T + t) * d;
+        double den = 0.0;
+        for (int i = 0; i < d; ++i) {
+          fq[i] = relu(ld(q, dt, row + i));
+          den += fq[i] * zc[i];
+        }
+        const double inv = 1.0 / (den + eps);
+        double dden = 0.0;
+        for (int j = 0; j < d; ++j) {
+          double num = 0.0;
+          for (int i = 0; i < d; ++i) num += fq[i] * Sc[(size_t)i * d + j];
+          const double sg = sigm(ld(g, dt, row + j));
+          h[j] = num * inv;
+          const double dh = dO[row + j] * sg;
+          dg[row + j] = dO[row + j] * h[j] * sg * (1.0 - sg);
+          dn[j] = dh * inv;
+          dden -= dh * h[j] * inv;
+        }
+        for (int i = 0; i < d; ++i) {
+          double acc = dden * zc[i];
+          for (int j = 0; j < d; ++j) acc += Sc[(size_t)i * d + j] * dn[j];
+          dq[row + i] = ld(q, dt, row + i) > 0.0 ? acc : 0.0;
+          for (int j = 0; j < d; ++j) Gf[(size_t)i * d + j] += fq[i] * dn[j];
+          gzf[i] += dden * fq[i];
+        }
+      }
+    }
+
+    /* reverse scan of the adjoints, and the key side */
+    if (causal && dS_out) memcpy(A, dS_out + (size_t)bh * dd, dd * sizeof(double));
+    if (causal && dz_out) memcpy(az, dz_out + (size_t)bh * d, (size_t)d * sizeof(double));
+    for (int f = F - 1; f >= 0; --f) {
+      for (size_t e = 0; e < dd; ++e) Sh[e] = G[(size_t)f * dd + e] + A[e];
+      for (int i = 0; i < d; ++i) zh[i] = gz[(size_t)f * d + i] + az[i];
+      if (causal && dgamma) {
+        double s = 0.0;
+        for (size_t e = 0; e < dd; ++e) s += Sh[e] * S[(size_t)f * dd + e];
+        for (int i = 0; i < d; ++i) s += zh[i] * z[(size_t)f * d + i];
+        dgamma[(size_t)bh * F + f] = s;
+      }
+      for (int t = 0; t < T; ++t) {
+        const size_t row = base + ((size_t)f * T + t) * d;
+        for (int i = 0; i < d; ++i) {
+          double acc = zh[i];
+          for (int j = 0; j < d; ++j) acc += Sh[(size_t)i * d + j] * ld(v, dt, row + j);
+          dk[row + i] = ld(k, dt, row + i) > 0.0 ? acc : 0.0;
+        }
+        for (int j = 0; j < d; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < d; ++i) acc += Sh[(size_t)i * d + j] * relu(ld(k, dt, row + i));
+          dv[row + j] = acc;
+        }
+      }
+      const double gm = causal ? gamma[(size_t)bh * F + f] : 1.0;
+      for (size_t e = 0; e < dd; ++e) A[e] = gm * Sh[e];
+      for (int i = 0; i < d; ++i) az[i] = gm * zh[i];
+    }
+    if (causal && dS_in) memcpy(dS_in + (size_t)bh * dd, A, dd * sizeof(double));
+    if (causal && dz_in) memcpy(dz_in + (size_t)bh * d, az, (size_t)d * sizeof(double));
+
+    free(S); free(z); free(G); free(gz); free(A); free(az); free(Sh); free(zh);
+    free(fq); free(h); free(dn);
+  }
+  return used;
+}
