@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
   feature axis is contiguous (e.g. ``x.transpose(1, 2)`` of a [B, N, H, d]
   tensor, or slices of a fused [B, N, 3, H, d] projection), with optional 3D
   rotary positions (:class:`Rope3D`)
+* :func:`gla_bwd_framecausal`, :func:`gla_bwd_bidir` -- the backward pass
+  (dq, dk, dv, dg, dgamma and the carried-state gradients)
 * ``gla_*_workspace`` -- workspace sizes in bytes
 
 The operation is the gated linear attention token mixer of "SANA-Video 2.0:
@@ -37,8 +39,9 @@ __all__ = [
     "GlaError", "Rope3D", "gla_fwd_bidir", "gla_fwd_framecausal", "gla_state_carry",
     "gla_fwd_bidir_ex", "gla_fwd_framecausal_ex", "gla_state_carry_ex",
     "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace", "gla_state_carry_workspace",
-    "gla_fwd_bidir_ex_workspace", "library_path", "load_library", "profile_begin",
-    "profile_end",
+    "gla_fwd_bidir_ex_workspace", "gla_bwd_framecausal", "gla_bwd_bidir",
+    "gla_bwd_framecausal_workspace", "gla_bwd_bidir_workspace", "library_path", "load_library",
+    "profile_begin", "profile_end",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -134,6 +137,14 @@ def load_library():
     lib.gla_state_carry_ex.argtypes = [tp, tp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                        rp, vp, sz, vp]
     lib.gla_state_carry_ex.restype = i32
+    lib.gla_bwd_framecausal_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.gla_bwd_framecausal_workspace.restype = sz
+    lib.gla_bwd_bidir_workspace.argtypes = [i32, i32, i64, i32]
+    lib.gla_bwd_bidir_workspace.restype = sz
+    lib.gla_bwd_framecausal.argtypes = [vp] * 17 + [i32] * 6 + [f32, vp, sz, vp]
+    lib.gla_bwd_framecausal.restype = i32
+    lib.gla_bwd_bidir.argtypes = [vp] * 9 + [i32, i32, i64, i32, i32, f32, vp, sz, vp]
+    lib.gla_bwd_bidir.restype = i32
     lib.gla_status_string.argtypes = [i32]
     lib.gla_status_string.restype = ctypes.c_char_p
     lib.gla_last_error.argtypes = []
@@ -438,6 +449,70 @@ def gla_state_carry_ex(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
                                   _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt, _rope(rope),
                                   _ptr(ws), wsb, _stream_handle(stream, dev)))
     return S_out, z_out
+
+
+def gla_bwd_framecausal_workspace(B: int, H: int, F: int, T: int, d: int) -> int:
+    return int(load_library().gla_bwd_framecausal_workspace(B, H, F, T, d))
+
+
+def gla_bwd_bidir_workspace(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().gla_bwd_bidir_workspace(B, H, N, d))
+
+
+def gla_bwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        gamma: torch.Tensor, dO: torch.Tensor,
+                        S_in: Optional[torch.Tensor] = None, z_in: Optional[torch.Tensor] = None,
+                        dS_out: Optional[torch.Tensor] = None,
+                        dz_out: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                        need_state_grad: Optional[bool] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of gla_fwd_framecausal for dL/do = dO (and dL/dS_out, dL/dz_out).
+
+    Returns {"dq", "dk", "dv", "dg", "dgamma"} and, when ``need_state_grad``
+    (default: S_in or dS_out given), "dS_in" and "dz_in"."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g, dO)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    if need_state_grad is None:
+        need_state_grad = S_in is not None or dS_out is not None
+    out = {n: torch.empty_like(ref) for n in ("dq", "dk", "dv", "dg")}
+    out["dgamma"] = torch.empty((B, H, F), dtype=torch.float32, device=ref.device)
+    if need_state_grad:
+        out["dS_in"] = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
+        out["dz_in"] = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    dev = _require_device(q, k, v, g, gamma, dO, S_in, z_in, dS_out, dz_out, workspace,
+                          *out.values())
+    ws, wsb = _workspace(lib.gla_bwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
+    _check(lib.gla_bwd_framecausal(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _ptr(dO),
+        _ptr(dS_out), _ptr(dz_out), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(out["dg"]), _ptr(out["dgamma"]), _ptr(out.get("dS_in")), _ptr(out.get("dz_in")),
+        B, H, F, T, d, dt, eps, _ptr(ws), wsb, _stream_handle(stream, dev)))
+    return out
+
+
+def gla_bwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  dO: torch.Tensor, eps: float = 1e-6, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> dict:
+    """Gradients of gla_fwd_bidir for dL/do = dO: {"dq", "dk", "dv", "dg"}."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g, dO)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    out = {n: torch.empty_like(ref) for n in ("dq", "dk", "dv", "dg")}
+    dev = _require_device(q, k, v, g, dO, workspace, *out.values())
+    ws, wsb = _workspace(lib.gla_bwd_bidir_workspace(B, H, N, d), dev, workspace)
+    _check(lib.gla_bwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dO), _ptr(out["dq"]),
+                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), B, H, N, d, dt,
+                             eps, _ptr(ws), wsb, _stream_handle(stream, dev)))
+    return out
 
 
 def profile_begin(max_launches: int = 4096) -> None:

@@ -1,0 +1,382 @@
+// bwd.hip -- backward pass of the gated linear attention: vector-ALU kernels,
+// the reverse scan of the state adjoints and the dgamma reduction.
+//
+// The gradients are the chain rule through the forward definition (taken in
+// reverse order of its steps). Per slab, with h_t = num_t / (den_t + eps) and
+// o_t = sigmoid(g_t) (.) h_t:
+//   dg_t   = dO_t (.) h_t (.) sigmoid'(g_t)
+//   dnum_t = dO_t (.) sigmoid(g_t) / (den_t + eps)
+//   dden_t = -((dO_t (.) sigmoid(g_t)) . h_t) / (den_t + eps)
+//   dq_t   = [q_t > 0] (.) (S_f dnum_t + dden_t z_f)                t in frame f
+//   Sh_f   = sum_{t in f} phi(q_t) dnum_t^T + gamma_{f+1} Sh_{f+1},  Sh_{F-1} adds dS_out
+//   zh_f   = sum_{t in f} dden_t phi(q_t) + gamma_{f+1} zh_{f+1},    zh_{F-1} adds dz_out
+//   dk_t   = [k_t > 0] (.) (Sh_f v_t + zh_f),   dv_t = Sh_f^T phi(k_t)
+//   dgamma_f = <Sh_f, S_{f-1}> + <zh_f, z_{f-1}>,   dS_in = gamma_0 Sh_0
+// (S_f, z_f: the forward states, recomputed by the forward kv and carry
+// kernels before these run.)
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace gla {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One workgroup per (slab, frame, split). Token tiles of TT tokens: thread
+// (cg, tl) owns value columns j = 4cg .. 4cg+3 of token tl for num, dg and
+// dnum, and key features i = 4cg .. 4cg+3 for dq. The split's sums
+// G = sum phi(q) dnum^T use the kv layout (thread: key feature i, value
+// columns jc + JS c) and gz = sum dden phi(q) the threads with jc == 0.
+template <typename TIn, int D>
+__global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
+    View qv, View gv, View dov, View dqv, View dgv, int H, const float *__restrict__ ws,
+    float *__restrict__ gs, int F, int64_t T, int P, int R, int64_t read_len, float eps) {
+  constexpr int CG = D / 4;
+  constexpr int TT = kThreads / CG;
+  constexpr bool kSInLds = (D <= 64);
+  constexpr int EPT = D * D / kThreads;
+  constexpr int JS = kThreads / D;
+  constexpr int64_t E = (int64_t)D * D + D;
+  __shared__ float sS[kSInLds ? D * D : 1];
+  __shared__ float sz[D];
+  __shared__ float sq[TT][D];   // phi(q)
+  __shared__ float sdn[TT][D];  // dnum
+  __shared__ float sred[TT][CG];
+  __shared__ float sdd[TT];     // dden
+
+  const int tid = threadIdx.x;
+  const int64_t wg = blockIdx.x;
+  const int r = (int)(wg % R);
+  const int f = (int)((wg / R) % F);
+  const int64_t bh = wg / ((int64_t)R * F);
+  const int64_t t0 = min((int64_t)r * read_len, T);
+  const int64_t t1 = min(t0 + read_len, T);
+
+  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;  // S_f (the carry left it in place)
+  if (kSInLds)
+    for (int e = tid; e < D * D; e += kThreads) sS[e] = Sg[e];
+  for (int e = tid; e < D; e += kThreads) sz[e] = Sg[D * D + e];
+
+  const TIn *qs = static_cast<const TIn *>(qv.data) + qv.slab(bh, H);
+  const TIn *gsl = static_cast<const TIn *>(gv.data) + gv.slab(bh, H);
+  const TIn *dos = static_cast<const TIn *>(dov.data) + dov.slab(bh, H);
+  TIn *dqs = const_cast<TIn *>(static_cast<const TIn *>(dqv.data)) + dqv.slab(bh, H);
+  TIn *dgs = const_cast<TIn *>(static_cast<const TIn *>(dgv.data)) + dgv.slab(bh, H);
+  const int64_t trow0 = (int64_t)f * T;
+  const int cg = tid % CG, tl = tid / CG;
+  const int ig = tid % D, jc = tid / D;
+  float Gacc[EPT];
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) Gacc[c] = 0.f;
+  float gzacc = 0.f;
+
+  for (int64_t c0 = t0; c0 < t1; c0 += TT) {
+    const int n = (int)min((int64_t)TT, t1 - c0);
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kThreads) {
+      const int tt = e / D, ii = e % D;
+      sq[tt][ii] =
+          (tt < n) ? relu(Elem<TIn>::load(qs, (trow0 + c0 + tt) * qv.sn + ii)) : 0.f;
+    }
+    __syncthreads();
+    const int64_t row = trow0 + c0 + tl;
+    float inv = 0.f;
+    if (tl < n) {
+      float num[4] = {0.f, 0.f, 0.f, 0.f};
+      float den = 0.f;
+      for (int ii = 0; ii < D; ++ii) {
+        const float qi = sq[tl][ii];
+        den = fmaf(qi, sz[ii], den);
+        const float *Srow = kSInLds ? sS + ii * D : Sg + ii * D;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) num[c] = fmaf(qi, Srow[4 * cg + c], num[c]);
+      }
+      inv = 1.f / (den + eps);
+      const float4 gg = Elem<TIn>::load4(gsl, row * gv.sn + 4 * cg);
+      const float4 dd = Elem<TIn>::load4(dos, row * dov.sn + 4 * cg);
+      const float ga[4] = {gg.x, gg.y, gg.z, gg.w}, da[4] = {dd.x, dd.y, dd.z, dd.w};
+      float dgo[4], part = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float sg = sigmoid(ga[c]);
+        const float hh = num[c] * inv;
+        const float dh = da[c] * sg;
+        dgo[c] = da[c] * hh * sg * (1.f - sg);
+        part = fmaf(dh, hh, part);
+        sdn[tl][4 * cg + c] = dh * inv;
+      }
+      Elem<TIn>::store4(dgs, row * dgv.sn + 4 * cg, make_float4(dgo[0], dgo[1], dgo[2], dgo[3]));
+      sred[tl][cg] = part;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sdn[tl][4 * cg + c] = 0.f;
+      sred[tl][cg] = 0.f;
+    }
+    __syncthreads();
+    if (tl < n) {
+      float tot = 0.f;
+      for (int c = 0; c < CG; ++c) tot += sred[tl][c];
+      const float dden = -tot * inv;
+      if (cg == 0) sdd[tl] = dden;
+      float dqo[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * cg + c;
+        const float *Srow = kSInLds ? sS + i * D : Sg + i * D;
+        float acc = dden * sz[i];
+        for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sdn[tl][j], acc);
+        dqo[c] = sq[tl][i] > 0.f ? acc : 0.f;
+      }
+      Elem<TIn>::store4(dqs, row * dqv.sn + 4 * cg, make_float4(dqo[0], dqo[1], dqo[2], dqo[3]));
+    } else if (cg == 0) {
+      sdd[tl] = 0.f;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < n; ++tt) {
+      const float qi = sq[tt][ig];
+#pragma unroll
+      for (int c = 0; c < EPT; ++c) Gacc[c] = fmaf(qi, sdn[tt][jc + JS * c], Gacc[c]);
+      gzacc = fmaf(sdd[tt], qi, gzacc);
+    }
+  }
+  float *out = gs + ((bh * F + f) * (int64_t)R + r) * E;
+#pragma unroll
+  for (int c = 0; c < EPT; ++c) out[ig * D + jc + JS * c] = Gacc[c];
+  if (jc == 0) out[D * D + ig] = gzacc;
+}
+
+// One workgroup per (slab, frame, part). Thread (cg, tl): dk for key features
+// i = 4cg .. 4cg+3 and dv for value features j = 4cg .. 4cg+3 of token tl.
+template <typename TIn, int D>
+__global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
+    View kv, View vv, View dkv, View dvv, int H, const float *__restrict__ gs, int F, int64_t T,
+    int P, int R, int64_t part_len) {
+  constexpr int CG = D / 4;
+  constexpr int TT = kThreads / CG;
+  constexpr bool kSInLds = (D <= 64);
+  constexpr int64_t E = (int64_t)D * D + D;
+  __shared__ float sSh[kSInLds ? D * D : 1];
+  __shared__ float szh[D];
+  __shared__ float sk[TT][D];  // phi(k)
+  __shared__ float sv[TT][D];
+
+  const int tid = threadIdx.x;
+  const int64_t wg = blockIdx.x;
+  const int p = (int)(wg % P);
+  const int f = (int)((wg / P) % F);
+  const int64_t bh = wg / ((int64_t)P * F);
+  const int64_t t0 = min((int64_t)p * part_len, T);
+  const int64_t t1 = min(t0 + part_len, T);
+  if (t0 >= t1) return;
+
+  const float *Sh = gs + ((bh * F + f) * (int64_t)R) * E;  // adjoint of S_f
+  if (kSInLds)
+    for (int e = tid; e < D * D; e += kThreads) sSh[e] = Sh[e];
+  for (int e = tid; e < D; e += kThreads) szh[e] = Sh[D * D + e];
+
+  const TIn *ks = static_cast<const TIn *>(kv.data) + kv.slab(bh, H);
+  const TIn *vs = static_cast<const TIn *>(vv.data) + vv.slab(bh, H);
+  TIn *dks = const_cast<TIn *>(static_cast<const TIn *>(dkv.data)) + dkv.slab(bh, H);
+  TIn *dvs = const_cast<TIn *>(static_cast<const TIn *>(dvv.data)) + dvv.slab(bh, H);
+  const int64_t trow0 = (int64_t)f * T;
+  const int cg = tid % CG, tl = tid / CG;
+
+  for (int64_t c0 = t0; c0 < t1; c0 += TT) {
+    const int n = (int)min((int64_t)TT, t1 - c0);
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kThreads) {
+      const int tt = e / D, ii = e % D;
+      const bool ok = tt < n;
+      const int64_t rr = trow0 + c0 + tt;
+      sk[tt][ii] = ok ? relu(Elem<TIn>::load(ks, rr * kv.sn + ii)) : 0.f;
+      sv[tt][ii] = ok ? Elem<TIn>::load(vs, rr * vv.sn + ii) : 0.f;
+    }
+    __syncthreads();
+    if (tl < n) {
+      const int64_t row = trow0 + c0 + tl;
+      float dko[4], dvo[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * cg + c;
+        const float *Srow = kSInLds ? sSh + i * D : Sh + i * D;
+        float acc = szh[i];
+        for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sv[tl][j], acc);
+        dko[c] = sk[tl][i] > 0.f ? acc : 0.f;
+      }
+      for (int i = 0; i < D; ++i) {
+        const float ki = sk[tl][i];
+        const float *Srow = kSInLds ? sSh + i * D : Sh + i * D;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dvo[c] = fmaf(Srow[4 * cg + c], ki, dvo[c]);
+      }
+      Elem<TIn>::store4(dks, row * dkv.sn + 4 * cg, make_float4(dko[0], dko[1], dko[2], dko[3]));
+      Elem<TIn>::store4(dvs, row * dvv.sn + 4 * cg, make_float4(dvo[0], dvo[1], dvo[2], dvo[3]));
+    }
+  }
+}
+
+// One thread per (slab, state element), frames walked last to first. Loads of
+// a batch of frames are issued before the serial chain folds them in. Per
+// frame, the block sums Sh_f[e] * S_{f-1}[e] over its elements (waves by
+// shuffles, then LDS), into dgp[(slab, frame)][block].
+constexpr int kScanThreads = 256;
+constexpr int kScanBatch = 8;
+
+__global__ __launch_bounds__(kScanThreads) void rev_scan_kernel(
+    const float *__restrict__ ws, float *__restrict__ gs, const float *__restrict__ gamma,
+    const float *S_in, const float *z_in, const float *dS_out, const float *dz_out, float *dS_in,
+    float *dz_in, float *__restrict__ dgp, int F, int P, int R, int d, int NB) {
+  const int64_t dd = (int64_t)d * d;
+  const int64_t E = dd + d;
+  const int64_t bh = blockIdx.x / NB;
+  const int blk = blockIdx.x % NB;
+  const int tid = threadIdx.x;
+  const int64_t e = (int64_t)blk * kScanThreads + tid;
+  const bool valid = e < E;
+  const bool is_S = e < dd;
+  __shared__ float red[kScanBatch][kScanThreads / 64];
+
+  float a = 0.f;  // incoming adjoint: gamma_{f+1} Sh_{f+1}
+  if (valid) {
+    if (is_S && dS_out) a = dS_out[bh * dd + e];
+    if (!is_S && dz_out) a = dz_out[bh * d + (e - dd)];
+  }
+  for (int fb = F - 1; fb >= 0; fb -= kScanBatch) {
+    float x[kScanBatch], prev[kScanBatch], gm[kScanBatch];
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) {
+      const int f = fb - j;
+      x[j] = 0.f;
+      prev[j] = 0.f;
+      gm[j] = 1.f;
+      if (f >= 0 && valid) {
+        const float *src = gs + ((bh * F + f) * (int64_t)R) * E + e;
+        float s = src[0];
+        for (int r = 1; r < R; ++r) s += src[(int64_t)r * E];
+        x[j] = s;
+        if (dgp) {
+          if (f > 0)
+            prev[j] = ws[((bh * F + f - 1) * (int64_t)P) * E + e];
+          else if (is_S && S_in)
+            prev[j] = S_in[bh * dd + e];
+          else if (!is_S && z_in)
+            prev[j] = z_in[bh * d + (e - dd)];
+        }
+        if (gamma) gm[j] = gamma[bh * F + f];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) {
+      const int f = fb - j;
+      if (f < 0) break;
+      const float sh = x[j] + a;
+      if (valid) gs[((bh * F + f) * (int64_t)R) * E + e] = sh;
+      if (dgp) {
+        float pr = valid ? sh * prev[j] : 0.f;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) pr += __shfl_xor(pr, off);
+        if ((tid & 63) == 0) red[j][tid >> 6] = pr;
+      }
+      a = gm[j] * sh;
+    }
+    if (dgp) {
+      __syncthreads();
+      if (tid < kScanBatch && fb - tid >= 0) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kScanThreads / 64; ++w) sum += red[tid][w];
+        dgp[(bh * F + (fb - tid)) * (int64_t)NB + blk] = sum;
+      }
+      __syncthreads();
+    }
+  }
+  if (valid) {
+    if (is_S && dS_in) dS_in[bh * dd + e] = a;
+    if (!is_S && dz_in) dz_in[bh * d + (e - dd)] = a;
+  }
+}
+
+__global__ __launch_bounds__(256) void dgamma_kernel(const float *__restrict__ dgp,
+                                                     float *__restrict__ dgamma, int64_t n,
+                                                     int NB) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int b = 0; b < NB; ++b) s += dgp[i * NB + b];
+  dgamma[i] = s;
+}
+
+template <typename TIn>
+hipError_t bwd_q_valu_dispatch(const BwdPlan &bp, const BwdQArgs &a, hipStream_t s) {
+  const Plan &p = bp.f;
+  const int64_t grid = p.BH * p.F * p.R;
+  float *gs = a.gs;
+#define GLA_BQ_CASE(DD)                                                                       \
+  case DD:                                                                                    \
+    hipLaunchKernelGGL((bwd_q_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), 0, \
+                       s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.ws, gs, p.F, p.T, p.P, p.R,       \
+                       p.read_len, a.eps);                                                    \
+    break;
+  switch (p.d) {
+    GLA_BQ_CASE(16)
+    GLA_BQ_CASE(32)
+    GLA_BQ_CASE(64)
+    GLA_BQ_CASE(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef GLA_BQ_CASE
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t bwd_k_valu_dispatch(const BwdPlan &bp, const BwdKArgs &a, hipStream_t s) {
+  const Plan &p = bp.f;
+  const int64_t grid = p.BH * p.F * p.P;
+#define GLA_BK_CASE(DD)                                                                       \
+  case DD:                                                                                    \
+    hipLaunchKernelGGL((bwd_k_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), 0, \
+                       s, a.k, a.v, a.dk, a.dv, a.H, a.gs, p.F, p.T, p.P, p.R, p.part_len);    \
+    break;
+  switch (p.d) {
+    GLA_BK_CASE(16)
+    GLA_BK_CASE(32)
+    GLA_BK_CASE(64)
+    GLA_BK_CASE(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef GLA_BK_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_q_valu(const BwdPlan &p, int dtype, const BwdQArgs &a, hipStream_t s) {
+  if (p.f.BH * p.f.F * p.f.R == 0) return hipSuccess;
+  return dtype == 0 ? bwd_q_valu_dispatch<float>(p, a, s) : bwd_q_valu_dispatch<bf16_t>(p, a, s);
+}
+
+hipError_t launch_bwd_k_valu(const BwdPlan &p, int dtype, const BwdKArgs &a, hipStream_t s) {
+  if (p.f.BH * p.f.F * p.f.P == 0 || p.f.T == 0) return hipSuccess;
+  return dtype == 0 ? bwd_k_valu_dispatch<float>(p, a, s) : bwd_k_valu_dispatch<bf16_t>(p, a, s);
+}
+
+hipError_t launch_rev_scan(const BwdPlan &p, const RevScanArgs &a, hipStream_t s) {
+  const int64_t grid = p.f.BH * p.NB;
+  if (grid == 0) return hipSuccess;  // F == 0 still runs: dS_in = dS_out
+  hipLaunchKernelGGL(rev_scan_kernel, dim3((unsigned)grid), dim3(kScanThreads), 0, s, a.ws, a.gs,
+                     a.gamma, a.S_in, a.z_in, a.dS_out, a.dz_out, a.dS_in, a.dz_in, a.dgp, p.f.F,
+                     p.f.P, p.f.R, p.f.d, p.NB);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgamma(const BwdPlan &p, const float *dgp, float *dgamma, hipStream_t s) {
+  const int64_t n = p.f.BH * p.f.F;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dgp,
+                     dgamma, n, p.NB);
+  return hipGetLastError();
+}
+
+}  // namespace gla

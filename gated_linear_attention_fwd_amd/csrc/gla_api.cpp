@@ -25,6 +25,8 @@ hipError_t launch_kv_valu(const Plan &p, int dtype, const KvArgs &a, hipStream_t
 hipError_t launch_readout_valu(const Plan &p, int dtype, const ReadoutArgs &a, hipStream_t s);
 hipError_t launch_kv_mfma(const Plan &p, const KvArgs &a, hipStream_t s);
 hipError_t launch_readout_mfma(const Plan &p, const ReadoutArgs &a, hipStream_t s);
+hipError_t launch_bwd_q_valu(const BwdPlan &p, int dtype, const BwdQArgs &a, hipStream_t s);
+hipError_t launch_bwd_k_valu(const BwdPlan &p, int dtype, const BwdKArgs &a, hipStream_t s);
 bool mfma_supports(int d);
 
 namespace {
@@ -118,8 +120,18 @@ gla_status launched(hipError_t e, const char *what) {
 }
 
 // ---- optional event timing of every launch (gla_profile_begin/end) ----
-enum Kind { kKindKv = 0, kKindCarry = 1, kKindReadout = 2, kNumKinds = 3 };
-const char *const kKindNames[kNumKinds] = {"kv", "carry", "readout"};
+enum Kind {
+  kKindKv = 0,
+  kKindCarry = 1,
+  kKindReadout = 2,
+  kKindBwdQ = 3,
+  kKindRevScan = 4,
+  kKindBwdK = 5,
+  kKindDgamma = 6,
+  kNumKinds = 7
+};
+const char *const kKindNames[kNumKinds] = {"kv", "carry", "readout", "bwd_q", "rev_scan",
+                                           "bwd_k", "dgamma"};
 
 struct Profiler {
   std::mutex mu;
@@ -354,6 +366,122 @@ gla_tensor contiguous(const void *p, int H, int64_t N, int d) {
   return gla_tensor{const_cast<void *>(p), (int64_t)H * N * d, N * d, (int64_t)d};
 }
 
+// The body of the two backward entry points (contiguous [B][H][N][d] tensors).
+gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, const void *g,
+                   const float *gamma, const float *S_in, const float *z_in, const void *dO,
+                   const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
+                   void *dg, float *dgamma, float *dS_in, float *dz_in, int B, int H, int F,
+                   int64_t T, int d, gla_dtype dt, float eps, void *ws, size_t ws_bytes,
+                   void *stream) {
+  GLA_TRY(check_dims(B, H, d, dt));
+  if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%lld must be >= 0", F, (long long)T);
+  GLA_TRY(check_eps(eps));
+  if ((S_in == nullptr) != (z_in == nullptr))
+    return fail(GLA_ERR_NULL, "S_in and z_in must both be given or both be NULL");
+  if ((dS_out == nullptr) != (dz_out == nullptr))
+    return fail(GLA_ERR_NULL, "dS_out and dz_out must both be given or both be NULL");
+  if ((dS_in == nullptr) != (dz_in == nullptr))
+    return fail(GLA_ERR_NULL, "dS_in and dz_in must both be given or both be NULL");
+  if (T > 0 && F > INT64_MAX / T) return fail(GLA_ERR_SHAPE, "F * T overflows");
+  const int64_t BH = (int64_t)B * H;
+  const int64_t N = (int64_t)F * T;
+  const bool have_tokens = BH > 0 && N > 0;
+  if (have_tokens && (!q || !k || !v || !g || !dO))
+    return fail(GLA_ERR_NULL, "q, k, v, g and dO are required");
+  if (have_tokens && (!dq || !dk || !dv || !dg))
+    return fail(GLA_ERR_NULL, "dq, dk, dv and dg are required");
+  if (!bidir && BH > 0 && F > 0 && !gamma) return fail(GLA_ERR_NULL, "gamma is required when F > 0");
+  const void *tens[] = {q, k, v, g, dO, dq, dk, dv, dg};
+  const char *tnames[] = {"q", "k", "v", "g", "dO", "dq", "dk", "dv", "dg"};
+  for (int i = 0; i < 9; ++i) GLA_TRY(check_tensor_align(tens[i], tnames[i]));
+  const float *st[] = {S_in, z_in, dS_out, dz_out, dS_in, dz_in};
+  const char *snames[] = {"S_in", "z_in", "dS_out", "dz_out", "dS_in", "dz_in"};
+  for (int i = 0; i < 6; ++i) GLA_TRY(check_tensor_align(st[i], snames[i]));
+  if (gamma && !aligned(gamma, 4)) return fail(GLA_ERR_ALIGN, "gamma is not 4-byte aligned");
+  if (dgamma && !aligned(dgamma, 4)) return fail(GLA_ERR_ALIGN, "dgamma is not 4-byte aligned");
+
+  BwdPlan bp;
+  if (!make_bwd_plan(BH, bidir ? (N > 0 ? 1 : 0) : F, bidir ? N : T, d, &bp))
+    return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
+  if (BH == 0 || (bidir && N == 0)) return GLA_OK;
+  if (bp.ws_bytes) {
+    if (!ws) return fail(GLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", bp.ws_bytes);
+    if (ws_bytes < bp.ws_bytes)
+      return fail(GLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, bp.ws_bytes);
+    if (!aligned(ws, 256)) return fail(GLA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  }
+  const size_t es = dt == GLA_F32 ? 4 : 2;
+  const size_t tb = (size_t)(BH * N * d) * es;
+  const size_t sbytes = (size_t)(BH * d * d) * 4, zbytes = (size_t)(BH * d) * 4;
+  const bool causal = !bidir;
+  const Range all[] = {{q, tb, "q"},
+                       {k, tb, "k"},
+                       {v, tb, "v"},
+                       {g, tb, "g"},
+                       {dO, tb, "dO"},
+                       {gamma, causal ? (size_t)(BH * F) * 4 : 0, "gamma"},
+                       {S_in, causal ? sbytes : 0, "S_in"},
+                       {z_in, causal ? zbytes : 0, "z_in"},
+                       {dS_out, causal ? sbytes : 0, "dS_out"},
+                       {dz_out, causal ? zbytes : 0, "dz_out"},
+                       {dq, tb, "dq"},
+                       {dk, tb, "dk"},
+                       {dv, tb, "dv"},
+                       {dg, tb, "dg"},
+                       {dgamma, causal ? (size_t)(BH * F) * 4 : 0, "dgamma"},
+                       {dS_in, causal ? sbytes : 0, "dS_in"},
+                       {dz_in, causal ? zbytes : 0, "dz_in"},
+                       {ws, bp.ws_bytes, "workspace"}};
+  GLA_TRY(check_no_overlap(all + 10, 8, all, 18));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Path path = select_path(dt, d);
+  float *wsf = static_cast<float *>(ws);
+  float *gsf = wsf + bp.gslot_offset;
+  const Plan &p = bp.f;
+  const float *gm = causal ? gamma : nullptr;
+  const View vq = contiguous_view(q, H, N, d), vk = contiguous_view(k, H, N, d),
+             vv = contiguous_view(v, H, N, d), vg = contiguous_view(g, H, N, d),
+             vdo = contiguous_view(dO, H, N, d), vdq = contiguous_view(dq, H, N, d),
+             vdk = contiguous_view(dk, H, N, d), vdv = contiguous_view(dv, H, N, d),
+             vdg = contiguous_view(dg, H, N, d);
+  if (p.F > 0) {
+    GLA_TRY(launched(timed(kKindKv, s,
+                           [&] {
+                             return launch_kv(p, dt, path, KvArgs{vk, vv, H, gm, wsf, RopeK{}}, s);
+                           }),
+                     "kv"));
+    const CarryArgs ca{wsf, gm, causal ? S_in : nullptr, causal ? z_in : nullptr,
+                       nullptr, nullptr, 1};
+    GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, ca, s); }), "carry"));
+    const BwdQArgs qa{vq, vg, vdo, vdq, vdg, H, wsf, gsf, eps};
+    GLA_TRY(launched(timed(kKindBwdQ, s, [&] { return launch_bwd_q(bp, dt, path, qa, s); }),
+                     "bwd_q"));
+  }
+  float *dgp = (causal && dgamma && p.F > 0) ? wsf + bp.dgp_offset : nullptr;
+  const RevScanArgs ra{wsf,
+                       gsf,
+                       gm,
+                       causal ? S_in : nullptr,
+                       causal ? z_in : nullptr,
+                       causal ? dS_out : nullptr,
+                       causal ? dz_out : nullptr,
+                       causal ? dS_in : nullptr,
+                       causal ? dz_in : nullptr,
+                       dgp};
+  GLA_TRY(launched(timed(kKindRevScan, s, [&] { return launch_rev_scan(bp, ra, s); }),
+                   "rev_scan"));
+  if (have_tokens) {
+    const BwdKArgs ka{vk, vv, vdk, vdv, H, gsf};
+    GLA_TRY(launched(timed(kKindBwdK, s, [&] { return launch_bwd_k(bp, dt, path, ka, s); }),
+                     "bwd_k"));
+  }
+  if (dgp)
+    GLA_TRY(launched(timed(kKindDgamma, s, [&] { return launch_dgamma(bp, dgp, dgamma, s); }),
+                     "dgamma"));
+  return GLA_OK;
+}
+
 }  // namespace
 
 bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
@@ -397,6 +525,35 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
   p.ws_bytes = (size_t)round_up((units * p.P + (p.G > 1 ? BH * p.NG : 0)) * E * 4, 256);
   *plan = p;
   return true;
+}
+
+bool make_bwd_plan(int64_t BH, int F, int64_t T, int d, BwdPlan *plan) {
+  BwdPlan b;
+  if (!make_plan(BH, F, T, d, &b.f)) return false;
+  Plan &p = b.f;
+  p.G = 1;  // one frame per group: the carry leaves S_f in place in its slot
+  p.NG = F;
+  const int64_t E = p.state_elems();
+  const int64_t slots = BH * F * (int64_t)p.P * E;
+  p.ws_bytes = (size_t)slots * 4;
+  b.NB = (int)ceil_div(E, 256);
+  b.gslot_offset = slots;
+  b.dgp_offset = slots + BH * F * (int64_t)p.R * E;
+  b.ws_bytes = (size_t)round_up((b.dgp_offset + BH * F * b.NB) * 4, 256);
+  *plan = b;
+  return true;
+}
+
+hipError_t launch_bwd_q(const BwdPlan &p, int dtype, Path path, const BwdQArgs &a,
+                        hipStream_t s) {
+  (void)path;
+  return launch_bwd_q_valu(p, dtype, a, s);
+}
+
+hipError_t launch_bwd_k(const BwdPlan &p, int dtype, Path path, const BwdKArgs &a,
+                        hipStream_t s) {
+  (void)path;
+  return launch_bwd_k_valu(p, dtype, a, s);
 }
 
 Path select_path(int dtype, int d) {
@@ -511,6 +668,41 @@ GLA_EXPORT gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *
              B, H, F, T, d, dt, 0.f, rope, ws, ws_bytes, stream);
 }
 
+GLA_EXPORT size_t gla_bwd_framecausal_workspace(int B, int H, int F, int T, int d) {
+  BwdPlan p;
+  if (B < 0 || H < 0 || F < 0 || T < 0 || d <= 0) return 0;
+  if (!make_bwd_plan((int64_t)B * H, F, T, d, &p)) return 0;
+  return p.ws_bytes;
+}
+
+GLA_EXPORT size_t gla_bwd_bidir_workspace(int B, int H, int64_t N, int d) {
+  BwdPlan p;
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return 0;
+  if (!make_bwd_plan((int64_t)B * H, N > 0 ? 1 : 0, N, d, &p)) return 0;
+  return p.ws_bytes;
+}
+
+GLA_EXPORT gla_status gla_bwd_framecausal(const void *q, const void *k, const void *v,
+                                          const void *g, const float *gamma, const float *S_in,
+                                          const float *z_in, const void *dO, const float *dS_out,
+                                          const float *dz_out, void *dq, void *dk, void *dv,
+                                          void *dg, float *dgamma, float *dS_in, float *dz_in,
+                                          int B, int H, int F, int T, int d, gla_dtype dt,
+                                          float eps, void *ws, size_t ws_bytes, void *stream) {
+  return run_bwd(false, q, k, v, g, gamma, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dg, dgamma,
+                 dS_in, dz_in, B, H, F, T, d, dt, eps, ws, ws_bytes, stream);
+}
+
+GLA_EXPORT gla_status gla_bwd_bidir(const void *q, const void *k, const void *v, const void *g,
+                                    const void *dO, void *dq, void *dk, void *dv, void *dg, int B,
+                                    int H, int64_t N, int d, gla_dtype dt, float eps, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  if (N < 0) return fail(GLA_ERR_SHAPE, "N=%lld must be >= 0", (long long)N);
+  return run_bwd(true, q, k, v, g, nullptr, nullptr, nullptr, dO, nullptr, nullptr, dq, dk, dv,
+                 dg, nullptr, nullptr, nullptr, B, H, N > 0 ? 1 : 0, N, d, dt, eps, ws, ws_bytes,
+                 stream);
+}
+
 GLA_EXPORT const char *gla_status_string(gla_status s) {
   switch (s) {
     case GLA_OK: return "ok";
@@ -554,8 +746,8 @@ GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
 GLA_EXPORT gla_status gla_profile_end(gla_kernel_time *out, int max_out, int *n_out) {
   std::lock_guard<std::mutex> lock(g_prof.mu);
   if (!g_prof.on) return fail(GLA_ERR_VALUE, "no profiling session is open");
-  double total[kNumKinds] = {0, 0, 0};
-  int count[kNumKinds] = {0, 0, 0};
+  double total[kNumKinds] = {};
+  int count[kNumKinds] = {};
   gla_status st = GLA_OK;
   for (int i = 0; i < g_prof.used; ++i) {
     float ms = 0.f;

@@ -135,6 +135,60 @@ __device__ __forceinline__ float carry_weight(const float *gamma_slab, int f, in
   return w;
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass. Launches on the caller's stream:
+//   1. kv + carry of the forward (one frame per group: after the carry, slot
+//      (f, part 0) holds S_f itself);
+//   2. bwd_q    one workgroup per (slab, frame, split): recomputes num, den,
+//               writes dg and dq, and the split's sums G = sum phi(q) dnum^T,
+//               gz = sum dden phi(q) into its "gslot";
+//   3. rev_scan one thread per (slab, state element): Sh_f = sum of the frame's
+//               gslots + gamma_{f+1} Sh_{f+1} (from dS_out), stored in place in
+//               gslot (f, 0); per-block partial sums of Sh_f . S_{f-1} for
+//               dgamma; dS_in = gamma_0 Sh_0;
+//   4. bwd_k    one workgroup per (slab, frame, part): dk = [k > 0] (Sh_f v + zh_f),
+//               dv = Sh_f^T phi(k);
+//   5. dgamma   one thread per (slab, frame): the partial sums in fixed order.
+// ---------------------------------------------------------------------------
+struct BwdPlan {
+  Plan f;                    // forward recompute (G == 1), its slots first in the workspace
+  int64_t gslot_offset = 0;  // floats: BH * F * R states of d*d + d
+  int64_t dgp_offset = 0;    // floats: BH * F * NB partial sums of dgamma
+  int NB = 0;                // reverse-scan blocks per slab, ceil((d*d + d) / 256)
+  size_t ws_bytes = 0;
+};
+
+bool make_bwd_plan(int64_t BH, int F, int64_t T, int d, BwdPlan *plan);
+
+struct BwdQArgs {
+  View q, g, dO, dq, dg;  // dq, dg written
+  int H;
+  const float *ws;        // forward slots (S_f)
+  float *gs;              // gslots
+  float eps;
+};
+
+struct RevScanArgs {
+  const float *ws;        // forward slots (S_f)
+  float *gs;              // gslots: in the frame's sums, out the adjoints in (f, 0)
+  const float *gamma;     // NULL: no decay (bidirectional)
+  const float *S_in, *z_in;      // NULL: zero
+  const float *dS_out, *dz_out;  // NULL: zero
+  float *dS_in, *dz_in;          // NULL: not written
+  float *dgp;             // partial sums of dgamma; NULL: not computed
+};
+
+struct BwdKArgs {
+  View k, v, dk, dv;      // dk, dv written
+  int H;
+  const float *gs;        // adjoints Sh_f, zh_f in gslot (f, 0)
+};
+
+hipError_t launch_bwd_q(const BwdPlan &p, int dtype, Path path, const BwdQArgs &a, hipStream_t s);
+hipError_t launch_rev_scan(const BwdPlan &p, const RevScanArgs &a, hipStream_t s);
+hipError_t launch_bwd_k(const BwdPlan &p, int dtype, Path path, const BwdKArgs &a, hipStream_t s);
+hipError_t launch_dgamma(const BwdPlan &p, const float *dgp, float *dgamma, hipStream_t s);
+
 hipError_t launch_kv(const Plan &p, int dtype, Path path, const KvArgs &a, hipStream_t s);
 hipError_t launch_carry(const Plan &p, const CarryArgs &a, hipStream_t s);
 hipError_t launch_readout(const Plan &p, int dtype, Path path, const ReadoutArgs &a,

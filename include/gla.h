@@ -101,6 +101,40 @@ gla_status gla_state_carry(const void *k, const void *v, const float *gamma, con
                            const float *z_in, float *S_out, float *z_out, int B, int H, int F,
                            int T, int d, gla_dtype dt, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- backward pass ---------------------------------------------------------
+ *
+ * Gradients of the forward operation above for a loss L, given
+ * dO = dL/do [B][H][N][d] (the input dtype) and, frame-causal only, the
+ * optional dS_out = dL/dS_out and dz_out = dL/dz_out (fp32, both or neither;
+ * NULL: zero). The pages state the forward only; these are its chain rule
+ * (the derivative of ReLU taken as 0 at 0):
+ *   dq, dk, dv, dg  [B][H][N][d], the input dtype, rounded from fp32;
+ *   dgamma          [B][H][F] fp32 (frame-causal; NULL: not computed);
+ *   dS_in, dz_in    fp32, dL/dS_in and dL/dz_in (frame-causal; both or neither;
+ *                   with S_in NULL they are the gradients of a zero state).
+ * For a stream run block by block, the backward of the last block is called
+ * first with the final dS_out; its dS_in is the previous block's dS_out.
+ *
+ * The forward states are recomputed inside the call (q, k, v, g, gamma,
+ * S_in, z_in are the forward's inputs). The workspace (the *_workspace
+ * queries) holds one fp32 state per (slab, frame, part) twice over. Outputs
+ * may overlap no input, other output or the workspace (GLA_ERR_ALIAS).
+ * Conventions otherwise as above. */
+size_t gla_bwd_framecausal_workspace(int B, int H, int F, int T, int d);
+size_t gla_bwd_bidir_workspace(int B, int H, int64_t N, int d);
+
+gla_status gla_bwd_framecausal(const void *q, const void *k, const void *v, const void *g,
+                               const float *gamma, const float *S_in, const float *z_in,
+                               const void *dO, const float *dS_out, const float *dz_out,
+                               void *dq, void *dk, void *dv, void *dg, float *dgamma,
+                               float *dS_in, float *dz_in, int B, int H, int F, int T, int d,
+                               gla_dtype dt, float eps, void *ws, size_t ws_bytes, void *stream);
+
+gla_status gla_bwd_bidir(const void *q, const void *k, const void *v, const void *g,
+                         const void *dO, void *dq, void *dk, void *dv, void *dg, int B, int H,
+                         int64_t N, int d, gla_dtype dt, float eps, void *ws, size_t ws_bytes,
+                         void *stream);
+
 /* ---- strided tensors and fused 3D rotary positions ------------------------
  *
  * The *_ex entry points compute the same operation as the plain ones, with
@@ -201,7 +235,8 @@ int gla_version(void); /* 10100: adds the *_ex entry points */
  * Between gla_profile_begin and gla_profile_end, every kernel launched by the
  * entry points (on any stream, from any thread) is bracketed by a pair of HIP
  * events recorded on its stream. gla_profile_end waits for those events and
- * returns, per kernel kind ("kv", "carry", "readout"), the number of launches
+ * returns, per kernel kind ("kv", "carry", "readout", and for the backward
+ * "bwd_q", "rev_scan", "bwd_k", "dgamma"), the number of launches
  * and their summed event time. At most max_launches launches are timed; later
  * ones run untimed. Not meant to overlap with itself: one session at a time.
  * gla_profile_begin creates 2 * max_launches HIP events (max_launches must be
