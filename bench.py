@@ -27,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GLA fwd tokens/s at 720p/60s shape; % HBM/MFMA roofline vs CPU oracle"
+METRIC_BWD = "GLA bwd tokens/s at 720p/60s shape; % HBM/MFMA roofline vs CPU oracle"
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 BF16_MFMA_PEAK = 2.5e15  # dense bf16 matrix-core peak, flop/s
 
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--layout", default="bhnd", choices=["bhnd", "fused"],
                     help="bhnd: contiguous [B,H,N,d] tensors; fused: q, k, v as slices of one "
                          "[B,N,3,H,d] projection, g and o [B,N,H,d] (the *_ex entry points)")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="fwd: the forward call (the headline); bwd: the backward call "
+                         "(gradients of the forward for a random dL/do)")
     ap.add_argument("--rope", action="store_true",
                     help="fused 3D rotary positions over the latent grid (the *_ex entry points)")
     ap.add_argument("--cpu-heads", type=int, default=32,
@@ -161,9 +165,58 @@ def main():
     else:
         wsb = max(gla.gla_fwd_framecausal_workspace(w.B, w.H, b["gamma"].shape[-1], w.T, d)
                   for b in blocks)
+    bwd = args.which == "bwd"
+    if bwd and ex:
+        print("bench.py: the backward takes contiguous tensors without rotary positions",
+              file=sys.stderr)
+        sys.exit(2)
+    if bwd:
+        # dL/do drawn on the device; for a stream, the forward states at the block
+        # boundaries (the S_in of each block) are computed once, before timing
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed * 1000 + 7)
+        for b in blocks:
+            b["dO"] = torch.randn(b["q"].shape, generator=gen, device=dev).to(b["q"].dtype)
+        grads = [{n: torch.empty_like(b["q"]) for n in ("dq", "dk", "dv", "dg")} for b in blocks]
+        for gd, b in zip(grads, blocks):
+            gd["dgamma"] = torch.empty_like(b["gamma"])
+        s_in = [None] * len(blocks)
+        if len(blocks) > 1:
+            Sb = torch.zeros_like(S)
+            zb = torch.zeros_like(z)
+            for i, b in enumerate(blocks):
+                s_in[i] = (Sb.clone(), zb.clone())
+                _, Sb, zb = gla.gla_fwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"],
+                                                    Sb, zb, eps=w.eps, return_state=True)
+            for gd in grads:
+                gd["dS_in"] = torch.empty_like(S)
+                gd["dz_in"] = torch.empty_like(z)
+        if mode == "bidir":
+            wsb = gla.gla_bwd_bidir_workspace(w.B, w.H, w.N, d)
+        else:
+            wsb = max(gla.gla_bwd_framecausal_workspace(w.B, w.H, b["gamma"].shape[-1], w.T, d)
+                      for b in blocks)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
+    def step_bwd():
+        if mode == "bidir":
+            b = blocks[0]
+            gla.gla_bwd_bidir(b["q"], b["k"], b["v"], b["g"], b["dO"], eps=w.eps, out=grads[0],
+                              workspace=ws)
+            return
+        dS = dz = None  # the stream's last block first
+        for i in reversed(range(len(blocks))):
+            b, si = blocks[i], s_in[i]
+            r = gla.gla_bwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"], b["dO"],
+                                        S_in=si[0] if si else None, z_in=si[1] if si else None,
+                                        dS_out=dS, dz_out=dz, eps=w.eps, out=grads[i],
+                                        workspace=ws)
+            dS, dz = r.get("dS_in"), r.get("dz_in")
+
     def step():
+        if bwd:
+            step_bwd()
+            return
         if mode == "bidir":
             b = blocks[0]
             if ex:
@@ -209,13 +262,15 @@ def main():
     value = tokens / (ms_per_step / 1e3)
 
     # ---------------------------------------------------------------- per-kernel times
-    launches_per_step = 3 * len(blocks)
+    launches_per_step = (6 if bwd else 3) * len(blocks)
     gla.profile_begin(launches_per_step * args.steps)
     for _ in range(args.steps):
         step()
     prof = gla.profile_end()
     torch.cuda.synchronize()
-    per_unit = {"kv": 2 * d * es, "readout": 3 * d * es, "carry": 0}  # bytes per token-head
+    # algorithmic bytes per token-head of each kernel
+    per_unit = {"kv": 2 * d * es, "readout": 3 * d * es, "carry": 0,
+                "bwd_q": 5 * d * es, "bwd_k": 4 * d * es}
     token_heads = w.B * w.H * w.N
     kernels = {}
     for name, (n, total) in prof.items():
@@ -229,27 +284,33 @@ def main():
     dk = kernels[dom]
     achieved = dk["alg_bytes_per_launch"] / (dk["avg_ms"] / 1e3)
     variant = w.name + "/" + mode + ("/fused" if args.layout == "fused" else "") + \
-        ("/rope" if args.rope else "")
+        ("/rope" if args.rope else "") + ("/bwd" if bwd else "")
     traffic_rec = committed_traffic(dom, variant)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                 "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
-    call_bytes = w.io_bytes()
+    # forward: read q, k, v, g, write o; backward: read q, k, v, g, dO, write dq,
+    # dk, dv, dg (the recompute's second read of k and v is not counted)
+    call_bytes = w.io_bytes() * 9 // 5 if bwd else w.io_bytes()
+    flops = (12 if bwd else 4) * d * d * token_heads
     call = {"alg_bytes": call_bytes, "GBps": round(call_bytes / (ms_per_step / 1e3) / 1e9, 1),
             "frac_of_hbm_peak": round(call_bytes / (ms_per_step / 1e3) / HBM_PEAK, 4),
-            "flops": 4 * d * d * token_heads,
-            "frac_of_bf16_mfma_peak": round(4 * d * d * token_heads / (ms_per_step / 1e3)
-                                            / BF16_MFMA_PEAK, 4)}
+            "flops": flops,
+            "frac_of_bf16_mfma_peak": round(flops / (ms_per_step / 1e3) / BF16_MFMA_PEAK, 4)}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     parity = None
     if not args.no_cpu and args.cpu_heads > 0:
-        cpu, parity = cpu_baseline(args, w, mode, blocks, outs, value,
-                                   ropes[0].as_dict() if args.rope else None)
+        if bwd:
+            cpu, parity = cpu_baseline_bwd(args, w, mode, blocks, grads, value)
+        else:
+            cpu, parity = cpu_baseline(args, w, mode, blocks, outs, value,
+                                       ropes[0].as_dict() if args.rope else None)
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_BWD if bwd else METRIC, "value": round(value, 1), "unit": "tokens/s",
+        "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded normal draws in the latent-video shape; no dataset)",
@@ -257,7 +318,9 @@ def main():
                    "T": w.T, "N": w.N, "blocks": list(w.blocks) or [w.F], "eps": w.eps,
                    "layout": ("q, k, v slices of [B,N,3,H,d]; g, o [B,N,H,d]"
                               if args.layout == "fused" else "[B,H,N,d] contiguous"),
-                   "rope": ropes[0].as_dict() if args.rope else None},
+                   "rope": ropes[0].as_dict() if args.rope else None,
+                   "pass": "backward (dq, dk, dv, dg, dgamma for a random dL/do)" if bwd
+                   else "forward"},
         "roofline": roofline, "call": call, "kernels": kernels, "cpu_baseline": cpu,
         "parity": parity, "wall_s": round(wall, 3), "source_hash": source_hash(),
     }
@@ -321,6 +384,57 @@ def cpu_baseline(args, w, mode, blocks, outs, gpu_value, rope=None):
     rms = np.sqrt(np.mean(r2 * r2, axis=-1, keepdims=True))
     err = np.abs(o64.reshape(r2.shape) - r2) / np.maximum(np.maximum(np.abs(r2), rms), 1e-300)
     parity = {"heads": nh, "max_slab_rel_err": float(err.max()),
+              "bar": 1e-4 if w.dtype == "f32" else 2e-2}
+    return cpu, parity
+
+
+def cpu_baseline_bwd(args, w, mode, blocks, grads, gpu_value):
+    """Time the fp64 backward oracle on a bounded sample of heads (the whole
+    stream at once), scale to tokens/s, and check dq, dk, dv, dg of those heads."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    nh = min(args.cpu_heads, w.B * w.H)
+    heads = [(i // w.H, i % w.H) for i in range(nh)]
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.contiguous().cpu().numpy()
+
+    def sel(t):
+        return np.concatenate([host(t[b:b + 1, h:h + 1]) for (b, h) in heads], axis=1)
+
+    x = {n: np.concatenate([sel(b[n]) for b in blocks], axis=2) for n in ("q", "k", "v", "g", "dO")}
+    gamma = np.concatenate([sel(b["gamma"]) for b in blocks], axis=2)
+    threads = min(oracle.max_threads(), nh)
+    print("bench: CPU backward oracle on %d heads, %d threads" % (nh, threads), file=sys.stderr,
+          flush=True)
+    t0 = time.perf_counter()
+    if mode == "bidir":
+        ref = oracle.backward(oracle.BIDIR, x["q"], x["k"], x["v"], x["g"], x["dO"], eps=w.eps)
+    else:
+        ref = oracle.backward(oracle.FRAMECAUSAL, x["q"], x["k"], x["v"], x["g"], x["dO"],
+                              gamma=gamma, eps=w.eps)
+    el = time.perf_counter() - t0
+    cpu_tokens_per_s = nh * w.N / el / w.H
+    cpu = {"value": round(cpu_tokens_per_s, 1), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": "%d of %d heads (all %d tokens each), fp64 backward oracle, %.1f s; "
+                     "tokens/s = head-tokens/s / H" % (nh, w.B * w.H, w.N, el),
+           "host_cpu": host_cpu_model(), "gpu_over_cpu": round(gpu_value / cpu_tokens_per_s, 1)}
+    worst = 0.0
+    for n in ("dq", "dk", "dv", "dg"):
+        got = np.concatenate([sel(gd[n]) for gd in grads], axis=2)
+        o64 = oracle.bf16_to_f64(got) if got.dtype == np.uint16 else got.astype(np.float64)
+        r2 = ref[n].reshape(1, nh, -1)
+        rms = np.sqrt(np.mean(r2 * r2, axis=-1, keepdims=True))
+        err = np.abs(o64.reshape(r2.shape) - r2) / np.maximum(np.maximum(np.abs(r2), rms),
+                                                               1e-300)
+        worst = max(worst, float(err.max()))
+    parity = {"heads": nh, "max_slab_rel_err": worst, "over": "dq, dk, dv, dg",
               "bar": 1e-4 if w.dtype == "f32" else 2e-2}
     return cpu, parity
 

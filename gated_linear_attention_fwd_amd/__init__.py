@@ -464,12 +464,13 @@ def gla_bwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
                         S_in: Optional[torch.Tensor] = None, z_in: Optional[torch.Tensor] = None,
                         dS_out: Optional[torch.Tensor] = None,
                         dz_out: Optional[torch.Tensor] = None, eps: float = 1e-6,
-                        need_state_grad: Optional[bool] = None,
+                        need_state_grad: Optional[bool] = None, out: Optional[dict] = None,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Gradients of gla_fwd_framecausal for dL/do = dO (and dL/dS_out, dL/dz_out).
 
     Returns {"dq", "dk", "dv", "dg", "dgamma"} and, when ``need_state_grad``
-    (default: S_in or dS_out given), "dS_in" and "dz_in"."""
+    (default: S_in or dS_out given), "dS_in" and "dz_in". ``out`` may supply
+    any of these tensors to be written."""
     lib = load_library()
     ref = _qkvg(q, k, v, g, dO)
     dt = _dtype_code(ref)
@@ -482,11 +483,13 @@ def gla_bwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     T = N // F if F else 0
     if need_state_grad is None:
         need_state_grad = S_in is not None or dS_out is not None
-    out = {n: torch.empty_like(ref) for n in ("dq", "dk", "dv", "dg")}
-    out["dgamma"] = torch.empty((B, H, F), dtype=torch.float32, device=ref.device)
+    out = dict(out or {})
+    for n in ("dq", "dk", "dv", "dg"):
+        out.setdefault(n, torch.empty_like(ref))
+    out.setdefault("dgamma", torch.empty((B, H, F), dtype=torch.float32, device=ref.device))
     if need_state_grad:
-        out["dS_in"] = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
-        out["dz_in"] = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+        out.setdefault("dS_in", torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device))
+        out.setdefault("dz_in", torch.empty((B, H, d), dtype=torch.float32, device=ref.device))
     dev = _require_device(q, k, v, g, gamma, dO, S_in, z_in, dS_out, dz_out, workspace,
                           *out.values())
     ws, wsb = _workspace(lib.gla_bwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
@@ -499,14 +502,16 @@ def gla_bwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
 
 
 def gla_bwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                  dO: torch.Tensor, eps: float = 1e-6, workspace: Optional[torch.Tensor] = None,
-                  stream=None) -> dict:
+                  dO: torch.Tensor, eps: float = 1e-6, out: Optional[dict] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Gradients of gla_fwd_bidir for dL/do = dO: {"dq", "dk", "dv", "dg"}."""
     lib = load_library()
     ref = _qkvg(q, k, v, g, dO)
     dt = _dtype_code(ref)
     B, H, N, d = ref.shape
-    out = {n: torch.empty_like(ref) for n in ("dq", "dk", "dv", "dg")}
+    out = dict(out or {})
+    for n in ("dq", "dk", "dv", "dg"):
+        out.setdefault(n, torch.empty_like(ref))
     dev = _require_device(q, k, v, g, dO, workspace, *out.values())
     ws, wsb = _workspace(lib.gla_bwd_bidir_workspace(B, H, N, d), dev, workspace)
     _check(lib.gla_bwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dO), _ptr(out["dq"]),

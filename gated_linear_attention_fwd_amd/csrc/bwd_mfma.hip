@@ -1,0 +1,611 @@
+// bwd_mfma.hip -- bf16 matrix-core (MFMA) kernels of the backward pass (gfx950).
+//
+// Key side, per (slab, frame, part), with Sh_f, zh_f the adjoints of the
+// frame's state (fp32, split into bf16 hi + lo as the forward readout does
+// with S_f):
+//   dv^T = Sh_f^T phi(K)^T                    (d x d times d x C)
+//   dk^T = [K > 0]^T (.) (Sh_f V^T + zh_f)    (d x d times d x C)
+// Query side, per (slab, frame, split):
+//   num^T = S_f^T phi(Q)^T, den = phi(Q) z_f       (the forward readout again)
+//   dg = dO (.) h (.) sigmoid'(g), dnum = dO (.) sigmoid(g) / (den + eps),
+//   dden = -((dO (.) sigmoid(g)) . h) / (den + eps)     with h = num / (den + eps)
+//   dq^T = [Q > 0]^T (.) (S_f dnum^T + z_f dden^T)
+//   G += phi(Q)^T dnum, gz += phi(Q)^T dden     (the split's share of Sh_f, zh_f)
+// dnum is fp32; it enters the matrix cores as a bf16 hi + lo pair.
+#include "common.hpp"
+#include "mfma_util.hpp"
+#include "plan.hpp"
+
+namespace gla {
+namespace {
+
+// x = hi + lo, both bf16: returns hi in the low half, lo in the high half
+__device__ __forceinline__ uint32_t split_hl(float x) {
+  const uint16_t h = f32_to_bf16_rne(x);
+  return (uint32_t)h | ((uint32_t)f32_to_bf16_rne(x - bf16_to_f32(h)) << 16);
+}
+
+// A fragments (hi, lo) of M^T for output block mb: A[m = j][k = i] = M[i][j]
+template <int D>
+__device__ __forceinline__ void frag_transposed(const float *M, int mb, int lane, bf16x8 *hi,
+                                                bf16x8 *lo) {
+  const int h = lane >> 5, col = 32 * mb + (lane & 31);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    i16x8 hv, lv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t x = split_hl(M[(16 * ks + 8 * h + e) * D + col]);
+      hv[e] = (short)(x & 0xFFFFu);
+      lv[e] = (short)(x >> 16);
+    }
+    hi[ks] = __builtin_bit_cast(bf16x8, hv);
+    lo[ks] = __builtin_bit_cast(bf16x8, lv);
+    asm volatile("" ::: "memory");  // one k-step of loads in flight at a time (registers)
+  }
+}
+
+// A fragments (hi, lo) of M for output block mb: A[m = i][k = j] = M[i][j]
+// (each lane reads 8 consecutive floats of a row)
+template <int D>
+__device__ __forceinline__ void frag_direct(const float *M, int mb, int lane, bf16x8 *hi,
+                                            bf16x8 *lo) {
+  const int h = lane >> 5, row = 32 * mb + (lane & 31);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const float4 a = *reinterpret_cast<const float4 *>(M + row * D + 16 * ks + 8 * h);
+    const float4 b = *reinterpret_cast<const float4 *>(M + row * D + 16 * ks + 8 * h + 4);
+    const float xs[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    i16x8 hv, lv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t x = split_hl(xs[e]);
+      hv[e] = (short)(x & 0xFFFFu);
+      lv[e] = (short)(x >> 16);
+    }
+    hi[ks] = __builtin_bit_cast(bf16x8, hv);
+    lo[ks] = __builtin_bit_cast(bf16x8, lv);
+  }
+}
+
+__device__ __forceinline__ void st_stream16(uint4 *p, uint4 v) {
+  const u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Key side: one workgroup of 8 waves per (slab, frame, part). The 2 MB
+// (role, feature block) pairs -- role dv (A = Sh^T) or dk (A = Sh) -- are
+// spread over the waves, WPP = 8 / (2 MB) waves per pair, each wave taking 32
+// of the block's BLK = 32 WPP tokens: a wave holds one set of A fragments.
+// k and v rows are staged in LDS (phi(k) and v, the B operands); the outputs
+// go back through LDS as whole rows.
+// ---------------------------------------------------------------------------
+constexpr int kBwThreads = 512;
+
+template <int D>
+struct BkCfg {
+  static constexpr int MB = D / 32;
+  static constexpr int WPP = 8 / (2 * MB);     // waves per (role, block) pair
+  static constexpr int BLK = 32 * WPP;         // tokens per iteration
+  static constexpr int KS = D / 16;
+  static constexpr int PITCH = 2 * D + 16;
+  static constexpr int ROW_CHUNKS = D / 8;
+  static constexpr int CPT = BLK * ROW_CHUNKS / kBwThreads;  // 16-byte pieces per thread
+  static constexpr int ROWS_PER_PASS = kBwThreads / ROW_CHUNKS;
+};
+
+template <int D>
+__global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
+    View kview, View vview, View dkview, View dvview, int H, const float *__restrict__ gs, int F,
+    int64_t T, int P, int R, int64_t part_len) {
+  using C = BkCfg<D>;
+  static_assert(C::CPT >= 1, "tile too small for the workgroup");
+  __shared__ __attribute__((aligned(16))) char ktile[C::BLK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) char vtile[C::BLK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) char dktile[C::BLK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) char dvtile[C::BLK * C::PITCH];
+  __shared__ float szh[D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int pair = wave / C::WPP;
+  const int tg = wave % C::WPP;
+  const bool role_dk = pair >= C::MB;
+  const int mb = pair % C::MB;
+  const int64_t wg = blockIdx.x;
+  const int p = (int)(wg % P);
+  const int f = (int)((wg / P) % F);
+  const int64_t bh = wg / ((int64_t)P * F);
+  const int64_t t0 = min((int64_t)p * part_len, T);
+  const int64_t t1 = min(t0 + part_len, T);
+  const int L = (int)(t1 - t0);
+  if (L <= 0) return;
+
+  constexpr int64_t E = (int64_t)D * D + D;
+  const float *Sh = gs + ((bh * F + f) * (int64_t)R) * E;
+  if (tid < D) szh[tid] = Sh[D * D + tid];
+  bf16x8 ahi[C::KS], alo[C::KS];
+  if (role_dk)
+    frag_direct<D>(Sh, mb, lane, ahi, alo);
+  else
+    frag_transposed<D>(Sh, mb, lane, ahi, alo);
+
+  const int c = tid % C::ROW_CHUNKS;
+  const int r0 = tid / C::ROW_CHUNKS;
+  const int64_t trow0 = (int64_t)f * T + t0;
+  const int64_t snk = kview.sn / 8, snv = vview.sn / 8, sdk = dkview.sn / 8, sdv = dvview.sn / 8;
+  const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(kview.data) +
+                                                    kview.slab(bh, H) + trow0 * kview.sn) +
+                    (int64_t)r0 * snk + c;
+  const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(vview.data) +
+                                                    vview.slab(bh, H) + trow0 * vview.sn) +
+                    (int64_t)r0 * snv + c;
+  uint4 *dkp = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(
+                   static_cast<const uint16_t *>(dkview.data) + dkview.slab(bh, H) +
+                   trow0 * dkview.sn)) +
+               (int64_t)r0 * sdk + c;
+  uint4 *dvp = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(
+                   static_cast<const uint16_t *>(dvview.data) + dvview.slab(bh, H) +
+                   trow0 * dvview.sn)) +
+               (int64_t)r0 * sdv + c;
+  uint4 rk[C::CPT], rv[C::CPT];
+  auto load = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const bool ok = blk * C::BLK + r0 + i * C::ROWS_PER_PASS < L;
+      rk[i] = ok ? ld_stream16<true>(kp + i * C::ROWS_PER_PASS * snk) : make_uint4(0, 0, 0, 0);
+      rv[i] = ok ? ld_stream16<true>(vp + i * C::ROWS_PER_PASS * snv) : make_uint4(0, 0, 0, 0);
+    }
+    kp += C::BLK * snk;
+    vp += C::BLK * snv;
+  };
+
+  const int tl = 32 * tg + (lane & 31);
+  // role dv multiplies phi(k) rows, role dk multiplies v rows
+  const char *btile = role_dk ? vtile : ktile;
+  char *otile = role_dk ? dktile : dvtile;
+  const int nblk = (L + C::BLK - 1) / C::BLK;
+  load(0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    sync_lds();  // the previous block's output rows have been read
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = r0 + i * C::ROWS_PER_PASS;
+      *reinterpret_cast<uint4 *>(ktile + row * C::PITCH + c * 16) = relu8(rk[i]);
+      *reinterpret_cast<uint4 *>(vtile + row * C::PITCH + c * 16) = rv[i];
+    }
+    sync_lds();
+    if (blk + 1 < nblk) load(blk + 1);
+
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 b = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4 *>(btile + tl * C::PITCH + (16 * ks + 8 * h) * 2));
+      acc = mfma_32x32x16(ahi[ks], b, acc);
+      acc = mfma_32x32x16(alo[ks], b, acc);
+    }
+    // C layout: element 4rg + e is feature 32mb + 8rg + 4h + e of token tl
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int fo = 32 * mb + 8 * rg + 4 * h;
+      const int off = tl * C::PITCH + fo * 2;
+      float o4[4] = {acc[4 * rg], acc[4 * rg + 1], acc[4 * rg + 2], acc[4 * rg + 3]};
+      if (role_dk) {
+        const uint2 kk = *reinterpret_cast<const uint2 *>(ktile + off);  // phi(k) > 0 <=> k > 0
+        const float k4[4] = {lo_bf16(kk.x), hi_bf16(kk.x), lo_bf16(kk.y), hi_bf16(kk.y)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = k4[e] > 0.f ? o4[e] + szh[fo + e] : 0.f;
+      }
+      *reinterpret_cast<uint2 *>(otile + off) =
+          make_uint2(pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3]));
+    }
+    sync_lds();
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = r0 + i * C::ROWS_PER_PASS;
+      if (blk * C::BLK + row < L) {
+        st_stream16(dkp + i * C::ROWS_PER_PASS * sdk,
+                    *reinterpret_cast<const uint4 *>(dktile + row * C::PITCH + c * 16));
+        st_stream16(dvp + i * C::ROWS_PER_PASS * sdv,
+                    *reinterpret_cast<const uint4 *>(dvtile + row * C::PITCH + c * 16));
+      }
+    }
+    dkp += C::BLK * sdk;
+    dvp += C::BLK * sdv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query side: one workgroup of 8 waves per (slab, frame, split). Per block of
+// BLK tokens:
+//   1. phi(q) rows -> LDS (den = phi(q) . z_f on the way), g and dO rows -> LDS;
+//   2. waves 0-3 ("N"): num^T = S^T phi(Q)^T (hi + lo of S), then in the C
+//      layout h, dg (written over g), dnum (bf16 hi + lo tiles) and the per-token
+//      partial sums of dh . h;
+//   3. waves 4-7 ("Q"): dphi(q)^T = S dnum^T (hi + lo of both, less lo x lo),
+//      + dden z, times [q > 0] -> dq tile; meanwhile waves 0-3 accumulate
+//      G = phi(Q)^T dnum over the block (transposed LDS reads, as in kv), and
+//      every thread adds dden phi(q) of its staged rows to gz;
+//   4. dq and dg rows -> global memory.
+// Wave w of a role takes feature block mb = w % MB and tokens 32 (w / MB)..
+// After the last block, G (reduced over the waves that split its k-steps) and
+// gz (reduced over the threads of a column piece) go to the split's gslot.
+// ---------------------------------------------------------------------------
+template <int D>
+struct BqCfg {
+  static constexpr int MB = D / 32;
+  static constexpr int TG = 4 / MB;            // token groups of 32 per role
+  static constexpr int BLK = 32 * TG;
+  static constexpr int KS = D / 16;            // k-steps over features
+  static constexpr int KT = BLK / 16;          // k-steps over the block's tokens
+  static constexpr int PITCH = 2 * D + 16;
+  static constexpr int ROW_CHUNKS = D / 8;
+  static constexpr int CPT = BLK * ROW_CHUNKS / kBwThreads;
+  static constexpr int ROWS_PER_PASS = kBwThreads / ROW_CHUNKS;
+  static constexpr int GB = MB * MB;           // 32 x 32 blocks of G
+  static constexpr int GPW = GB >= 4 ? GB / 4 : 1;   // G blocks per N wave
+  static constexpr int KSPLIT = GB >= 4 ? 1 : 4 / GB;  // N waves sharing a G block
+};
+
+template <int D>
+__global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
+    View qview, View gview, View doview, View dqview, View dgview, int H,
+    const float *__restrict__ ws, float *__restrict__ gs, int F, int64_t T, int P, int R,
+    int64_t read_len, float eps) {
+  using C = BqCfg<D>;
+  static_assert(C::CPT >= 1, "tile too small for the workgroup");
+  // six row tiles in one array; after the last block it holds the G reduction
+  constexpr int TILE = C::BLK * C::PITCH;
+  static_assert(6 * TILE >= 4 * 16 * 64 * 4, "LDS too small for the G reduction");
+  __shared__ __attribute__((aligned(16))) char smem[6 * TILE];
+  char *const qtile = smem;              // phi(q)
+  char *const gtile = smem + TILE;       // g, then dg
+  char *const otile = smem + 2 * TILE;   // dO
+  char *const dnhi = smem + 3 * TILE;    // dnum, hi
+  char *const dnlo = smem + 4 * TILE;    // dnum, lo
+  char *const dqtile = smem + 5 * TILE;  // dq
+  __shared__ float szf[D];
+  __shared__ float inv_s[C::BLK];
+  __shared__ float ddp[C::MB][C::BLK];  // per feature block: sum of dh . h
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const bool role_q = wave >= 4;
+  const int rw = wave & 3;            // wave index within its role
+  const int mb = rw % C::MB;
+  const int tg = rw / C::MB;
+  const int64_t wg = blockIdx.x;
+  const int r = (int)(wg % R);
+  const int f = (int)((wg / R) % F);
+  const int64_t bh = wg / ((int64_t)R * F);
+  const int64_t t0 = min((int64_t)r * read_len, T);
+  const int64_t t1 = min(t0 + read_len, T);
+  const int L = (int)max(t1 - t0, (int64_t)0);
+
+  constexpr int64_t E = (int64_t)D * D + D;
+  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;  // S_f (left in place by the carry)
+  if (tid < D) szf[tid] = Sg[D * D + tid];
+  bf16x8 ahi[C::KS], alo[C::KS];
+  if (role_q)
+    frag_direct<D>(Sg, mb, lane, ahi, alo);
+  else
+    frag_transposed<D>(Sg, mb, lane, ahi, alo);
+
+  // G accumulators of an N wave: blocks gb = rw * GPW + u (GPW > 1), or the
+  // single block of its KSPLIT group taking k-steps ks % KSPLIT == rw % KSPLIT
+  f32x16 gacc[C::GPW];
+#pragma unroll
+  for (int u = 0; u < C::GPW; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) gacc[u][e] = 0.f;
+  const int grp16 = (lane >> 4) & 1;
+  const int jj = lane & 15;
+  const int frag_row = 8 * h + (jj >> 2);
+  const int frag_col = 16 * grp16 + 4 * (jj & 3);
+
+  const int c = tid % C::ROW_CHUNKS;
+  const int r0 = tid / C::ROW_CHUNKS;
+  float gz8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gz8[e] = 0.f;
+  float zc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zc[e] = Sg[D * D + 8 * c + e];
+
+  const int64_t trow0 = (int64_t)f * T + t0;
+  const int64_t snq = qview.sn / 8, sng = gview.sn / 8, sno = doview.sn / 8;
+  const int64_t sdq = dqview.sn / 8, sdg = dgview.sn / 8;
+  const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(qview.data) +
+                                                    qview.slab(bh, H) + trow0 * qview.sn) +
+                    (int64_t)r0 * snq + c;
+  const uint4 *gp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(gview.data) +
+                                                    gview.slab(bh, H) + trow0 * gview.sn) +
+                    (int64_t)r0 * sng + c;
+  const uint4 *op = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(doview.data) +
+                                                    doview.slab(bh, H) + trow0 * doview.sn) +
+                    (int64_t)r0 * sno + c;
+  uint4 *dqp = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(
+                   static_cast<const uint16_t *>(dqview.data) + dqview.slab(bh, H) +
+                   trow0 * dqview.sn)) +
+               (int64_t)r0 * sdq + c;
+  uint4 *dgp = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(
+                   static_cast<const uint16_t *>(dgview.data) + dgview.slab(bh, H) +
+                   trow0 * dgview.sn)) +
+               (int64_t)r0 * sdg + c;
+  uint4 rq[C::CPT], rg[C::CPT], ro[C::CPT];
+  auto load = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const bool ok = blk * C::BLK + r0 + i * C::ROWS_PER_PASS < L;
+      const int64_t pass = (int64_t)i * C::ROWS_PER_PASS;
+      rq[i] = ok ? ld_stream16<true>(qp + pass * snq) : make_uint4(0, 0, 0, 0);
+      rg[i] = ok ? ld_stream16<true>(gp + pass * sng) : make_uint4(0, 0, 0, 0);
+      ro[i] = ok ? ld_stream16<true>(op + pass * sno) : make_uint4(0, 0, 0, 0);
+    }
+    qp += C::BLK * snq;
+    gp += C::BLK * sng;
+    op += C::BLK * sno;
+  };
+
+  const int tl = 32 * tg + (lane & 31);
+  const int nblk = (L + C::BLK - 1) / C::BLK;
+  uint4 qkeep[C::CPT];  // this thread's phi(q) pieces, for gz
+  if (nblk > 0) load(0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    sync_lds();  // the previous block's tiles are consumed
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = r0 + i * C::ROWS_PER_PASS;
+      const uint4 w = relu8(rq[i]);
+      qkeep[i] = w;
+      *reinterpret_cast<uint4 *>(qtile + row * C::PITCH + c * 16) = w;
+      *reinterpret_cast<uint4 *>(gtile + row * C::PITCH + c * 16) = rg[i];
+      *reinterpret_cast<uint4 *>(otile + row * C::PITCH + c * 16) = ro[i];
+      float dp = lo_bf16(w.x) * zc[0];
+      dp = fmaf(hi_bf16(w.x), zc[1], dp);
+      dp = fmaf(lo_bf16(w.y), zc[2], dp);
+      dp = fmaf(hi_bf16(w.y), zc[3], dp);
+      dp = fmaf(lo_bf16(w.z), zc[4], dp);
+      dp = fmaf(hi_bf16(w.z), zc[5], dp);
+      dp = fmaf(lo_bf16(w.w), zc[6], dp);
+      dp = fmaf(hi_bf16(w.w), zc[7], dp);
+#pragma unroll
+      for (int off = 1; off < C::ROW_CHUNKS; off <<= 1) dp += __shfl_xor(dp, off);
+      // rows past the split: 0, so that they add nothing (even with eps = 0)
+      if (c == 0) inv_s[row] = blk * C::BLK + row < L ? 1.f / (dp + eps) : 0.f;
+    }
+    sync_lds();
+    if (blk + 1 < nblk) load(blk + 1);
+
+    if (!role_q) {
+      // num^T for features 32mb.., tokens 32tg..
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4 *>(qtile + tl * C::PITCH + (16 * ks + 8 * h) * 2));
+        acc = mfma_32x32x16(ahi[ks], b, acc);
+        acc = mfma_32x32x16(alo[ks], b, acc);
+      }
+      const float inv = inv_s[tl];
+      float part = 0.f;
+#pragma unroll
+      for (int rgp = 0; rgp < 4; ++rgp) {
+        const int off = tl * C::PITCH + (32 * mb + 8 * rgp + 4 * h) * 2;
+        const uint2 gv = *reinterpret_cast<const uint2 *>(gtile + off);
+        const uint2 ov = *reinterpret_cast<const uint2 *>(otile + off);
+        const float g4[4] = {lo_bf16(gv.x), hi_bf16(gv.x), lo_bf16(gv.y), hi_bf16(gv.y)};
+        const float o4[4] = {lo_bf16(ov.x), hi_bf16(ov.x), lo_bf16(ov.y), hi_bf16(ov.y)};
+        float dg4[4], dh4[4], hl4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = fast_sigmoid(g4[e]);
+          const float hh = acc[4 * rgp + e] * inv;
+          dh4[e] = o4[e] * sg;
+          dg4[e] = o4[e] * hh * sg * (1.f - sg);
+          part = fmaf(dh4[e], hh, part);
+          hl4[e] = dh4[e] * inv;  // dnum
+        }
+        *reinterpret_cast<uint2 *>(gtile + off) =
+            make_uint2(pack_bf16x2(dg4[0], dg4[1]), pack_bf16x2(dg4[2], dg4[3]));
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const uint32_t a = split_hl(hl4[2 * e2]), b = split_hl(hl4[2 * e2 + 1]);
+          hw[e2] = (a & 0xFFFFu) | (b << 16);
+          lw[e2] = (a >> 16) | (b & 0xFFFF0000u);
+        }
+        *reinterpret_cast<uint2 *>(dnhi + off) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2 *>(dnlo + off) = make_uint2(lw[0], lw[1]);
+      }
+      part += __shfl_xor(part, 32);  // the other half of the block's features, same token
+      if (h == 0) ddp[mb][tl] = part;
+    }
+    sync_lds();
+
+    if (role_q) {
+      // dphi(q)^T for features 32mb.., tokens 32tg..
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int off = tl * C::PITCH + (16 * ks + 8 * h) * 2;
+        const bf16x8 bh_ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(dnhi + off));
+        const bf16x8 bl_ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(dnlo + off));
+        acc = mfma_32x32x16(ahi[ks], bh_, acc);
+        acc = mfma_32x32x16(alo[ks], bh_, acc);
+        acc = mfma_32x32x16(ahi[ks], bl_, acc);
+      }
+      float dsum = 0.f;
+#pragma unroll
+      for (int m = 0; m < C::MB; ++m) dsum += ddp[m][tl];
+      const float dden = -dsum * inv_s[tl];
+#pragma unroll
+      for (int rgp = 0; rgp < 4; ++rgp) {
+        const int fo = 32 * mb + 8 * rgp + 4 * h;
+        const int off = tl * C::PITCH + fo * 2;
+        const uint2 qv = *reinterpret_cast<const uint2 *>(qtile + off);
+        const float q4[4] = {lo_bf16(qv.x), hi_bf16(qv.x), lo_bf16(qv.y), hi_bf16(qv.y)};
+        float d4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d4[e] = q4[e] > 0.f ? fmaf(dden, szf[fo + e], acc[4 * rgp + e]) : 0.f;
+        *reinterpret_cast<uint2 *>(dqtile + off) =
+            make_uint2(pack_bf16x2(d4[0], d4[1]), pack_bf16x2(d4[2], d4[3]));
+      }
+    } else {
+      // G += phi(Q)^T dnum over the block's tokens
+#pragma unroll
+      for (int u = 0; u < C::GPW; ++u) {
+        const int gb = C::KSPLIT > 1 ? 0 : rw * C::GPW + u;
+        const int bi = gb / C::MB, bj = gb % C::MB;
+#pragma unroll
+        for (int kt = 0; kt < C::KT; ++kt) {
+          if (C::KSPLIT > 1 && kt % C::KSPLIT != rw % C::KSPLIT) continue;
+          const bf16x8 fa = tr_fragment((const lds_char *)qtile, kt * 16 + frag_row,
+                                        32 * bi + frag_col, C::PITCH);
+          const bf16x8 fh = tr_fragment((const lds_char *)dnhi, kt * 16 + frag_row,
+                                        32 * bj + frag_col, C::PITCH);
+          const bf16x8 fl = tr_fragment((const lds_char *)dnlo, kt * 16 + frag_row,
+                                        32 * bj + frag_col, C::PITCH);
+          gacc[u] = mfma_32x32x16(fa, fh, gacc[u]);
+          gacc[u] = mfma_32x32x16(fa, fl, gacc[u]);
+        }
+      }
+    }
+    // gz += dden phi(q) over this thread's staged rows
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = r0 + i * C::ROWS_PER_PASS;
+      float dsum = 0.f;
+#pragma unroll
+      for (int m = 0; m < C::MB; ++m) dsum += ddp[m][row];
+      const float dden = -dsum * inv_s[row];
+      const uint4 w = qkeep[i];
+      gz8[0] = fmaf(dden, lo_bf16(w.x), gz8[0]);
+      gz8[1] = fmaf(dden, hi_bf16(w.x), gz8[1]);
+      gz8[2] = fmaf(dden, lo_bf16(w.y), gz8[2]);
+      gz8[3] = fmaf(dden, hi_bf16(w.y), gz8[3]);
+      gz8[4] = fmaf(dden, lo_bf16(w.z), gz8[4]);
+      gz8[5] = fmaf(dden, hi_bf16(w.z), gz8[5]);
+      gz8[6] = fmaf(dden, lo_bf16(w.w), gz8[6]);
+      gz8[7] = fmaf(dden, hi_bf16(w.w), gz8[7]);
+    }
+    sync_lds();
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int row = r0 + i * C::ROWS_PER_PASS;
+      if (blk * C::BLK + row < L) {
+        const int64_t pass = (int64_t)i * C::ROWS_PER_PASS;
+        st_stream16(dqp + pass * sdq, *reinterpret_cast<const uint4 *>(dqtile + row * C::PITCH + c * 16));
+        st_stream16(dgp + pass * sdg, *reinterpret_cast<const uint4 *>(gtile + row * C::PITCH + c * 16));
+      }
+    }
+    dqp += C::BLK * sdq;
+    dgp += C::BLK * sdg;
+  }
+
+  // ---- the split's G and gz -> its gslot (the tiles are free now) ----
+  float *out = gs + ((bh * F + f) * (int64_t)R + r) * E;
+  sync_lds();
+  float *red = reinterpret_cast<float *>(smem);  // [wave][16][64] partial G blocks
+  if (C::KSPLIT > 1) {
+    if (!role_q) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(rw * 16 + e) * 64 + lane] = gacc[0][e];
+    }
+    sync_lds();
+    if (!role_q && rw == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float sum = 0.f;
+        for (int w2 = 0; w2 < C::KSPLIT; ++w2) sum += red[(w2 * 16 + e) * 64 + lane];
+        gacc[0][e] = sum;
+      }
+    }
+  }
+  if (!role_q && (C::KSPLIT == 1 || rw == 0)) {
+#pragma unroll
+    for (int u = 0; u < C::GPW; ++u) {
+      const int gb = C::KSPLIT > 1 ? 0 : rw * C::GPW + u;
+      const int bi = gb / C::MB, bj = gb % C::MB;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = 8 * (e >> 2) + 4 * h + (e & 3);
+        out[(32 * bi + m) * D + 32 * bj + (lane & 31)] = gacc[u][e];
+      }
+    }
+  }
+  // gz: sum over the lanes of a column piece, then over the waves
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int off = C::ROW_CHUNKS; off < 64; off <<= 1) gz8[e] += __shfl_xor(gz8[e], off);
+  sync_lds();
+  float *gzr = reinterpret_cast<float *>(smem + 5 * TILE);  // [wave][D], clear of red
+  if (lane < C::ROW_CHUNKS) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gzr[wave * D + 8 * lane + e] = gz8[e];
+  }
+  sync_lds();
+  if (tid < D) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kBwThreads / 64; ++w2) sum += gzr[w2 * D + tid];
+    out[D * D + tid] = sum;
+  }
+}
+
+template <int D>
+void bwd_q_launch(const BwdPlan &bp, const BwdQArgs &a, hipStream_t s) {
+  const Plan &p = bp.f;
+  hipLaunchKernelGGL((bwd_q_mfma_kernel<D>), dim3((unsigned)(p.BH * p.F * p.R)),
+                     dim3(kBwThreads), 0, s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.ws, a.gs, p.F,
+                     p.T, p.P, p.R, p.read_len, a.eps);
+}
+
+template <int D>
+void bwd_k_launch(const BwdPlan &bp, const BwdKArgs &a, hipStream_t s) {
+  const Plan &p = bp.f;
+  hipLaunchKernelGGL((bwd_k_mfma_kernel<D>), dim3((unsigned)(p.BH * p.F * p.P)),
+                     dim3(kBwThreads), 0, s, a.k, a.v, a.dk, a.dv, a.H, a.gs, p.F, p.T, p.P, p.R,
+                     p.part_len);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_q_mfma(const BwdPlan &p, const BwdQArgs &a, hipStream_t s) {
+  if (p.f.BH * p.f.F * p.f.R == 0) return hipSuccess;
+  switch (p.f.d) {
+    case 32: bwd_q_launch<32>(p, a, s); break;
+    case 64: bwd_q_launch<64>(p, a, s); break;
+    case 128: bwd_q_launch<128>(p, a, s); break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_k_mfma(const BwdPlan &p, const BwdKArgs &a, hipStream_t s) {
+  if (p.f.BH * p.f.F * p.f.P == 0 || p.f.T == 0) return hipSuccess;
+  switch (p.f.d) {
+    case 32: bwd_k_launch<32>(p, a, s); break;
+    case 64: bwd_k_launch<64>(p, a, s); break;
+    case 128: bwd_k_launch<128>(p, a, s); break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gla

@@ -27,6 +27,8 @@ hipError_t launch_kv_mfma(const Plan &p, const KvArgs &a, hipStream_t s);
 hipError_t launch_readout_mfma(const Plan &p, const ReadoutArgs &a, hipStream_t s);
 hipError_t launch_bwd_q_valu(const BwdPlan &p, int dtype, const BwdQArgs &a, hipStream_t s);
 hipError_t launch_bwd_k_valu(const BwdPlan &p, int dtype, const BwdKArgs &a, hipStream_t s);
+hipError_t launch_bwd_k_mfma(const BwdPlan &p, const BwdKArgs &a, hipStream_t s);
+hipError_t launch_bwd_q_mfma(const BwdPlan &p, const BwdQArgs &a, hipStream_t s);
 bool mfma_supports(int d);
 
 namespace {
@@ -546,13 +548,13 @@ bool make_bwd_plan(int64_t BH, int F, int64_t T, int d, BwdPlan *plan) {
 
 hipError_t launch_bwd_q(const BwdPlan &p, int dtype, Path path, const BwdQArgs &a,
                         hipStream_t s) {
-  (void)path;
+  if (path == Path::kMfma) return launch_bwd_q_mfma(p, a, s);
   return launch_bwd_q_valu(p, dtype, a, s);
 }
 
 hipError_t launch_bwd_k(const BwdPlan &p, int dtype, Path path, const BwdKArgs &a,
                         hipStream_t s) {
-  (void)path;
+  if (path == Path::kMfma) return launch_bwd_k_mfma(p, a, s);
   return launch_bwd_k_valu(p, dtype, a, s);
 }
 

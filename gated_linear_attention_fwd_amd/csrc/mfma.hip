@@ -11,11 +11,7 @@
 // The state is fp32; for the readout it is split as S = S_hi + S_lo with both
 // parts bf16 (S_lo = bf16(S - S_hi)), so the product keeps ~16 bits of S.
 //
-// MFMA 32x32x16 bf16 operand layout (lane l, half h = l / 32):
-//   A[m][k]: lane holds m = l % 32, k = 8h .. 8h+7
-//   B[k][n]: lane holds n = l % 32, k = 8h .. 8h+7
-//   C[m][n]: element r holds m = 8(r/4) + 4h + r%4, n = l % 32
-// Any consistent relabelling of k between A and B gives the same sum.
+// (MFMA operand layouts: mfma_util.hpp.)
 //
 // KV: the contraction runs over tokens, the slow axis of the [N][d] layout, so
 // both operands are read transposed out of row-major LDS tiles with
@@ -23,19 +19,11 @@
 // the address of 4 consecutive bf16 in row j/4 (columns 4(j%4)..) of a 4 x 16
 // block and receives column j of that block (rows 0..3).
 #include "common.hpp"
+#include "mfma_util.hpp"
 #include "plan.hpp"
 
 namespace gla {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
 constexpr int kMaxGroup = 8;  // most frames per kv workgroup (the plan's limit)
@@ -62,83 +50,6 @@ constexpr int kMinWaves = (kRope && D <= 64) ? 4 : 1;
 #ifndef GLA_RO_XCD_REMAP
 #define GLA_RO_XCD_REMAP 1
 #endif
-
-// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
-// Renumbering so that XCD x runs a contiguous range of work items keeps
-// neighbouring frames (which share their group's carried state) on one L2.
-// A bijection on [0, n): the first 8 * floor(n / 8) ids are remapped, the
-// remainder keep their id.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_contiguous(int64_t w, int64_t n) {
-  const int64_t per = n / kXcds;
-  if (w >= per * kXcds) return w;
-  return (w % kXcds) * per + w / kXcds;
-}
-
-template <bool kNt>
-__device__ __forceinline__ uint4 ld_stream16(const uint4 *p) {
-  if constexpr (kNt) {
-    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(x.x, x.y, x.z, x.w);
-  } else {
-    return *p;
-  }
-}
-
-// Workgroup barrier for data exchanged through LDS only. __syncthreads() also
-// fences global memory, which on this architecture waits for every
-// outstanding global load and store (vmcnt(0)) -- including the prefetch of
-// the next tile and the stores of the previous one -- before the barrier.
-// Waiting for LDS operations alone (lgkmcnt(0)) is enough for LDS data.
-__device__ __forceinline__ void sync_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// ReLU of two packed bf16: as signed 16-bit integers every negative bf16
-// (including -0) is negative, so max(x, 0) in int16 is max(x, +0) in bf16.
-__device__ __forceinline__ uint32_t relu2(uint32_t w) {
-  i16x2 v = __builtin_bit_cast(i16x2, w);
-  v = __builtin_elementwise_max(v, (i16x2){0, 0});
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ uint4 relu8(uint4 x) {
-  return make_uint4(relu2(x.x), relu2(x.y), relu2(x.z), relu2(x.w));
-}
-
-// Gate and normaliser of the epilogue with the hardware reciprocal (v_rcp_f32,
-// 1 ulp) rather than an IEEE division (~10 instructions each): the result is
-// rounded to bf16 right after. exp overflow still gives sigmoid = 0 exactly.
-__device__ __forceinline__ float fast_sigmoid(float x) {
-  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ bf16x8 tr_fragment(const lds_char *tile, int row, int col, int pitch) {
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4 *)(tile + row * pitch + col * 2));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4 *)(tile + (row + 4) * pitch + col * 2));
-  const i16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, ab);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// two floats -> packed bf16 (v_cvt_pk_bf16_f32, round to nearest even)
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const f32x2 x = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-}
 
 // ---------------------------------------------------------------------------
 // 3D rotary positions
