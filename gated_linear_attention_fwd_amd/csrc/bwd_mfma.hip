@@ -25,6 +25,13 @@ __device__ __forceinline__ uint32_t split_hl(float x) {
   return (uint32_t)h | ((uint32_t)f32_to_bf16_rne(x - bf16_to_f32(h)) << 16);
 }
 
+// (x0, x1) = hi + lo with both parts bf16, as packed pairs: v_cvt_pk_bf16_f32
+// rounds to nearest even, like split_hl, two values per instruction
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - lo_bf16(hi), x1 - hi_bf16(hi));
+}
+
 // A fragments (hi, lo) of M^T for output block mb: A[m = j][k = i] = M[i][j]
 template <int D>
 __device__ __forceinline__ void frag_transposed(const float *M, int mb, int lane, bf16x8 *hi,
@@ -224,14 +231,15 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
 // ---------------------------------------------------------------------------
 // Query side: one workgroup of 8 waves per (slab, frame, split). Per block of
 // BLK tokens:
-//   1. phi(q) rows -> LDS (den = phi(q) . z_f on the way), g and dO rows -> LDS;
-//   2. waves 0-3 ("N"): num^T = S^T phi(Q)^T (hi + lo of S), then in the C
-//      layout h, dg (written over g), dnum (bf16 hi + lo tiles) and the per-token
-//      partial sums of dh . h;
-//   3. waves 4-7 ("Q"): dphi(q)^T = S dnum^T (hi + lo of both, less lo x lo),
-//      + dden z, times [q > 0] -> dq tile; meanwhile waves 0-3 accumulate
-//      G = phi(Q)^T dnum over the block (transposed LDS reads, as in kv), and
-//      every thread adds dden phi(q) of its staged rows to gz;
+//   1. all threads: phi(q), g and dO rows -> LDS; den = phi(q) . z_f; and
+//      dnum = dO (.) sigmoid(g) / (den + eps) (it needs den, not num) -> bf16
+//      hi + lo tiles;
+//   2. at once: waves 0-3 ("N") num^T = S^T phi(Q)^T (hi + lo of S), then in
+//      the C layout dg (written over g) and the per-token sums of dh . h;
+//      waves 4-7 ("Q") S dnum^T (hi + lo of both, less lo x lo);
+//   3. waves 4-7: dq = [q > 0] (.) (S dnum^T + dden z) -> LDS; waves 0-3:
+//      G += phi(Q)^T dnum (transposed LDS reads, as in kv); every thread adds
+//      dden phi(q) of its staged rows to gz;
 //   4. dq and dg rows -> global memory.
 // Wave w of a role takes feature block mb = w % MB and tokens 32 (w / MB)..
 // After the last block, G (reduced over the waves that split its k-steps) and
@@ -251,6 +259,10 @@ struct BqCfg {
   static constexpr int GB = MB * MB;           // 32 x 32 blocks of G
   static constexpr int GPW = GB >= 4 ? GB / 4 : 1;   // G blocks per N wave
   static constexpr int KSPLIT = GB >= 4 ? 1 : 4 / GB;  // N waves sharing a G block
+  // d <= 64: G accumulates in LDS (fp32, one image per k-step split), which
+  // keeps its registers free between blocks; d = 128 keeps 4 blocks in registers
+  static constexpr bool kGInLds = D <= 64;
+  static constexpr int GL_FLOATS = kGInLds ? KSPLIT * D * D : 1;
 };
 
 template <int D>
@@ -271,6 +283,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
   char *const dnlo = smem + 4 * TILE;    // dnum, lo
   char *const dqtile = smem + 5 * TILE;  // dq
   __shared__ float szf[D];
+  __shared__ __attribute__((aligned(16))) float gl[C::GL_FLOATS];  // G^T images [n][m]
   __shared__ float inv_s[C::BLK];
   __shared__ float ddp[C::MB][C::BLK];  // per feature block: sum of dh . h
 
@@ -301,11 +314,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 
   // G accumulators of an N wave: blocks gb = rw * GPW + u (GPW > 1), or the
   // single block of its KSPLIT group taking k-steps ks % KSPLIT == rw % KSPLIT
-  f32x16 gacc[C::GPW];
+  constexpr int NACC = C::kGInLds ? 1 : C::GPW;
+  f32x16 gacc[NACC];
 #pragma unroll
-  for (int u = 0; u < C::GPW; ++u)
+  for (int u = 0; u < NACC; ++u)
 #pragma unroll
     for (int e = 0; e < 16; ++e) gacc[u][e] = 0.f;
+  if constexpr (C::kGInLds)
+    for (int e = tid; e < C::GL_FLOATS; e += kBwThreads) gl[e] = 0.f;
   const int grp16 = (lane >> 4) & 1;
   const int jj = lane & 15;
   const int frag_row = 8 * h + (jj >> 2);
@@ -316,9 +332,16 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
   float gz8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) gz8[e] = 0.f;
-  float zc[8];
+  // d <= 64 re-reads z and its staged phi(q) pieces from LDS (registers are
+  // what limits its occupancy); d = 128 keeps them (its occupancy is set by the
+  // fragments either way)
+  constexpr bool kKeep = !C::kGInLds;
+  float zk[kKeep ? 8 : 1];
+  uint4 qkeep[kKeep ? C::CPT : 1];
+  if constexpr (kKeep) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zc[e] = Sg[D * D + 8 * c + e];
+    for (int e = 0; e < 8; ++e) zk[e] = Sg[D * D + 8 * c + e];
+  }
 
   const int64_t trow0 = (int64_t)f * T + t0;
   const int64_t snq = qview.sn / 8, sng = gview.sn / 8, sno = doview.sn / 8;
@@ -357,16 +380,27 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 
   const int tl = 32 * tg + (lane & 31);
   const int nblk = (L + C::BLK - 1) / C::BLK;
-  uint4 qkeep[C::CPT];  // this thread's phi(q) pieces, for gz
   if (nblk > 0) load(0);
   for (int blk = 0; blk < nblk; ++blk) {
     sync_lds();  // the previous block's tiles are consumed
+    // staging, all threads: phi(q), g and dO rows; den; and dnum, which needs
+    // only den: dnum = dO (.) sigmoid(g) / (den + eps)
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = r0 + i * C::ROWS_PER_PASS;
       const uint4 w = relu8(rq[i]);
-      qkeep[i] = w;
       *reinterpret_cast<uint4 *>(qtile + row * C::PITCH + c * 16) = w;
+      float zc[8];
+      if constexpr (kKeep) {
+        qkeep[i] = w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zc[e] = zk[e];
+      } else {
+        const float4 za = *reinterpret_cast<const float4 *>(szf + 8 * c);
+        const float4 zb = *reinterpret_cast<const float4 *>(szf + 8 * c + 4);
+        zc[0] = za.x; zc[1] = za.y; zc[2] = za.z; zc[3] = za.w;
+        zc[4] = zb.x; zc[5] = zb.y; zc[6] = zb.z; zc[7] = zb.w;
+      }
       *reinterpret_cast<uint4 *>(gtile + row * C::PITCH + c * 16) = rg[i];
       *reinterpret_cast<uint4 *>(otile + row * C::PITCH + c * 16) = ro[i];
       float dp = lo_bf16(w.x) * zc[0];
@@ -380,16 +414,28 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 #pragma unroll
       for (int off = 1; off < C::ROW_CHUNKS; off <<= 1) dp += __shfl_xor(dp, off);
       // rows past the split: 0, so that they add nothing (even with eps = 0)
-      if (c == 0) inv_s[row] = blk * C::BLK + row < L ? 1.f / (dp + eps) : 0.f;
+      const float inv = blk * C::BLK + row < L ? 1.f / (dp + eps) : 0.f;
+      if (c == 0) inv_s[row] = inv;
+      const uint32_t gw[4] = {rg[i].x, rg[i].y, rg[i].z, rg[i].w};
+      const uint32_t ow[4] = {ro[i].x, ro[i].y, ro[i].z, ro[i].w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float d0 = lo_bf16(ow[e2]) * fast_sigmoid(lo_bf16(gw[e2])) * inv;
+        const float d1 = hi_bf16(ow[e2]) * fast_sigmoid(hi_bf16(gw[e2])) * inv;
+        split2(d0, d1, hw[e2], lw[e2]);
+      }
+      *reinterpret_cast<uint4 *>(dnhi + row * C::PITCH + c * 16) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4 *>(dnlo + row * C::PITCH + c * 16) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
     sync_lds();
     if (blk + 1 < nblk) load(blk + 1);
 
-    if (!role_q) {
-      // num^T for features 32mb.., tokens 32tg..
-      f32x16 acc;
+    f32x16 acc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    if (!role_q) {
+      // num^T for features 32mb.., tokens 32tg..; then dg and the sums dh . h
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const bf16x8 b = __builtin_bit_cast(
@@ -399,45 +445,31 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       }
       const float inv = inv_s[tl];
       float part = 0.f;
-#pragma unroll
+      // one row group at a time: unrolled, the four groups' temporaries would
+      // hold 20 more registers
+#pragma unroll 1
       for (int rgp = 0; rgp < 4; ++rgp) {
         const int off = tl * C::PITCH + (32 * mb + 8 * rgp + 4 * h) * 2;
         const uint2 gv = *reinterpret_cast<const uint2 *>(gtile + off);
         const uint2 ov = *reinterpret_cast<const uint2 *>(otile + off);
         const float g4[4] = {lo_bf16(gv.x), hi_bf16(gv.x), lo_bf16(gv.y), hi_bf16(gv.y)};
         const float o4[4] = {lo_bf16(ov.x), hi_bf16(ov.x), lo_bf16(ov.y), hi_bf16(ov.y)};
-        float dg4[4], dh4[4], hl4[4];
+        float dg4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float sg = fast_sigmoid(g4[e]);
           const float hh = acc[4 * rgp + e] * inv;
-          dh4[e] = o4[e] * sg;
-          dg4[e] = o4[e] * hh * sg * (1.f - sg);
-          part = fmaf(dh4[e], hh, part);
-          hl4[e] = dh4[e] * inv;  // dnum
+          const float dh = o4[e] * sg;
+          dg4[e] = dh * hh * (1.f - sg);
+          part = fmaf(dh, hh, part);
         }
         *reinterpret_cast<uint2 *>(gtile + off) =
             make_uint2(pack_bf16x2(dg4[0], dg4[1]), pack_bf16x2(dg4[2], dg4[3]));
-        uint32_t hw[2], lw[2];
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          const uint32_t a = split_hl(hl4[2 * e2]), b = split_hl(hl4[2 * e2 + 1]);
-          hw[e2] = (a & 0xFFFFu) | (b << 16);
-          lw[e2] = (a >> 16) | (b & 0xFFFF0000u);
-        }
-        *reinterpret_cast<uint2 *>(dnhi + off) = make_uint2(hw[0], hw[1]);
-        *reinterpret_cast<uint2 *>(dnlo + off) = make_uint2(lw[0], lw[1]);
       }
       part += __shfl_xor(part, 32);  // the other half of the block's features, same token
       if (h == 0) ddp[mb][tl] = part;
-    }
-    sync_lds();
-
-    if (role_q) {
-      // dphi(q)^T for features 32mb.., tokens 32tg..
-      f32x16 acc;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    } else {
+      // dphi(q)^T without dden z: S dnum^T for features 32mb.., tokens 32tg..
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const int off = tl * C::PITCH + (16 * ks + 8 * h) * 2;
@@ -447,11 +479,15 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
         acc = mfma_32x32x16(alo[ks], bh_, acc);
         acc = mfma_32x32x16(ahi[ks], bl_, acc);
       }
+    }
+    sync_lds();  // the sums dh . h of every feature block are in ddp
+
+    if (role_q) {
       float dsum = 0.f;
 #pragma unroll
       for (int m = 0; m < C::MB; ++m) dsum += ddp[m][tl];
       const float dden = -dsum * inv_s[tl];
-#pragma unroll
+#pragma unroll 1
       for (int rgp = 0; rgp < 4; ++rgp) {
         const int fo = 32 * mb + 8 * rgp + 4 * h;
         const int off = tl * C::PITCH + fo * 2;
@@ -463,12 +499,20 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
         *reinterpret_cast<uint2 *>(dqtile + off) =
             make_uint2(pack_bf16x2(d4[0], d4[1]), pack_bf16x2(d4[2], d4[3]));
       }
-    } else {
-      // G += phi(Q)^T dnum over the block's tokens
+    }
+    if (!role_q) {
+      // G += phi(Q)^T dnum over the block's tokens (waves 0-3, their accumulators free)
 #pragma unroll
       for (int u = 0; u < C::GPW; ++u) {
         const int gb = C::KSPLIT > 1 ? 0 : rw * C::GPW + u;
         const int bi = gb / C::MB, bj = gb % C::MB;
+        f32x16 blk_acc;
+        if constexpr (C::kGInLds) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) blk_acc[e] = 0.f;
+        } else {
+          blk_acc = gacc[u];
+        }
 #pragma unroll
         for (int kt = 0; kt < C::KT; ++kt) {
           if (C::KSPLIT > 1 && kt % C::KSPLIT != rw % C::KSPLIT) continue;
@@ -478,8 +522,25 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
                                         32 * bj + frag_col, C::PITCH);
           const bf16x8 fl = tr_fragment((const lds_char *)dnlo, kt * 16 + frag_row,
                                         32 * bj + frag_col, C::PITCH);
-          gacc[u] = mfma_32x32x16(fa, fh, gacc[u]);
-          gacc[u] = mfma_32x32x16(fa, fl, gacc[u]);
+          blk_acc = mfma_32x32x16(fa, fh, blk_acc);
+          blk_acc = mfma_32x32x16(fa, fl, blk_acc);
+        }
+        if constexpr (C::kGInLds) {
+          // add into this wave's image (rows m = 8(e/4) + 4h + e%4 of column n)
+          float *img = gl + (C::KSPLIT > 1 ? rw % C::KSPLIT : 0) * D * D;
+          const int n = 32 * bj + (lane & 31);
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            float4 *cell = reinterpret_cast<float4 *>(img + n * D + 32 * bi + 8 * e4 + 4 * h);
+            float4 v = *cell;
+            v.x += blk_acc[4 * e4];
+            v.y += blk_acc[4 * e4 + 1];
+            v.z += blk_acc[4 * e4 + 2];
+            v.w += blk_acc[4 * e4 + 3];
+            *cell = v;
+          }
+        } else {
+          gacc[u] = blk_acc;
         }
       }
     }
@@ -491,7 +552,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 #pragma unroll
       for (int m = 0; m < C::MB; ++m) dsum += ddp[m][row];
       const float dden = -dsum * inv_s[row];
-      const uint4 w = qkeep[i];
+      uint4 w;
+      if constexpr (kKeep)
+        w = qkeep[i];
+      else
+        w = *reinterpret_cast<const uint4 *>(qtile + row * C::PITCH + c * 16);
       gz8[0] = fmaf(dden, lo_bf16(w.x), gz8[0]);
       gz8[1] = fmaf(dden, hi_bf16(w.x), gz8[1]);
       gz8[2] = fmaf(dden, lo_bf16(w.y), gz8[2]);
@@ -518,8 +583,18 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
   // ---- the split's G and gz -> its gslot (the tiles are free now) ----
   float *out = gs + ((bh * F + f) * (int64_t)R + r) * E;
   sync_lds();
+  if constexpr (C::kGInLds) {
+    // sum the images, transpose back: out[m * D + n] = sum_img gl[img][n][m]
+    for (int e = tid; e < D * D; e += kBwThreads) {
+      const int m = e / D, n = e % D;
+      float sum = 0.f;
+#pragma unroll
+      for (int im = 0; im < C::KSPLIT; ++im) sum += gl[im * D * D + n * D + m];
+      out[e] = sum;
+    }
+  }
   float *red = reinterpret_cast<float *>(smem);  // [wave][16][64] partial G blocks
-  if (C::KSPLIT > 1) {
+  if (!C::kGInLds && C::KSPLIT > 1) {
     if (!role_q) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) red[(rw * 16 + e) * 64 + lane] = gacc[0][e];
@@ -534,7 +609,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       }
     }
   }
-  if (!role_q && (C::KSPLIT == 1 || rw == 0)) {
+  if (!C::kGInLds && !role_q && (C::KSPLIT == 1 || rw == 0)) {
 #pragma unroll
     for (int u = 0; u < C::GPW; ++u) {
       const int gb = C::KSPLIT > 1 ? 0 : rw * C::GPW + u;
