@@ -92,6 +92,9 @@ def _load():
     lib.gla_oracle_backward.argtypes = [ctypes.c_int, ctypes.c_int] + [vp] * 17 + [
         ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_int]
     lib.gla_oracle_backward.restype = ctypes.c_int
+    lib.gla_oracle_gdn.argtypes = [ctypes.c_int] + [vp] * 8 + [ctypes.c_int] * 5 + [
+        ctypes.c_double, ctypes.c_int]
+    lib.gla_oracle_gdn.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -267,6 +270,43 @@ def backward(mode, q, k, v, g, dO, gamma=None, S_in=None, z_in=None, dS_out=None
         _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out.get("dgamma")), _ptr(out.get("dS_in")),
         _ptr(out.get("dz_in")), B, H, F, T, d, float(eps), int(nthreads))
     return out
+
+
+def gdn(q, k, v, beta, gamma, S_in=None, key_scale=None, T=None, outputs=True, nthreads=0):
+    """Frame-wise Gated DeltaNet (block delta rule per frame); returns (o, S_out).
+
+    q, k, v [B, H, N, d]; beta [B, H, N] (write strengths); gamma [B, H, F]
+    (frame decays, F = gamma.shape[-1], T = N / F); key_scale defaults to
+    1 / sqrt(d T)."""
+    k = np.ascontiguousarray(k)
+    B, H, N, d = k.shape
+    dt = _DT.get(k.dtype)
+    if dt is None:
+        raise TypeError("unsupported input dtype %s" % k.dtype)
+    v = np.ascontiguousarray(v)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must share shape and dtype")
+    if outputs:
+        q = np.ascontiguousarray(q)
+        if q.shape != k.shape or q.dtype != k.dtype:
+            raise ValueError("q must match k")
+    else:
+        q = None
+    gamma = np.ascontiguousarray(np.asarray(gamma, np.float64))
+    F = gamma.shape[-1]
+    T = N // F if T is None else T
+    if F * T != N or gamma.shape != (B, H, F):
+        raise ValueError("gamma must be [B, H, F] with N = F * T")
+    beta = np.ascontiguousarray(np.broadcast_to(np.asarray(beta, np.float64), (B, H, N)))
+    if S_in is not None:
+        S_in = np.ascontiguousarray(np.asarray(S_in, np.float64).reshape(B, H, d, d))
+    if key_scale is None:
+        key_scale = 1.0 / np.sqrt(d * T)
+    o = np.empty((B, H, N, d), np.float64) if outputs else None
+    S_out = np.empty((B, H, d, d), np.float64)
+    _load().gla_oracle_gdn(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma), _ptr(S_in),
+                           _ptr(o), _ptr(S_out), B, H, F, T, d, float(key_scale), int(nthreads))
+    return o, S_out
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -659,3 +659,74 @@ int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const vo
   }
   return used;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Frame-wise Gated DeltaNet                                                 */
+/* ------------------------------------------------------------------------ */
+/*
+ * The SANA-WM analysis page (method components) names its linear mixer a
+ * frame-wise Gated DeltaNet: decay gates plus a delta-rule correction of the
+ * recurrent state, with keys scaled by 1/sqrt(D S), the only scaling that
+ * trains stably (claim checks). Reading taken: the state is updated once per
+ * frame, every token of the frame measuring its prediction error against the
+ * same decayed prior (a block delta rule; S = tokens per frame, which is what
+ * makes the frame's summed key norms, and with them the update's contraction,
+ * independent of the frame size):
+ *
+ *   k~_t = c k_t                     (c = key_scale, 1/sqrt(d T) by default)
+ *   P_f  = gamma_f S_{f-1}           (S_{-1} = S_in or 0)
+ *   e_t  = v_t - P_f^T k~_t          (t in frame f)
+ *   S_f  = P_f + sum_{t in f} beta_t k~_t e_t^T
+ *   o_t  = S_f^T q_t                 (every token of frame f reads S_f)
+ *
+ * beta [B][H][N] and gamma [B][H][F] are float64; S_in, S_out [B][H][d][d]
+ * (S[i][j]: i = key feature, j = value feature). q may be NULL (state only).
+ * OpenMP over slabs.
+ */
+int gla_oracle_gdn(int dt, const void *q, const void *k, const void *v, const double *beta,
+                   const double *gamma, const double *S_in, double *o, double *S_out, int B,
+                   int H, int F, int T, int d, double key_scale, int nthreads) {
+  const long nslab = (long)B * H;
+  const size_t N = (size_t)F * T, dd = (size_t)d * d;
+  const int used = set_threads(nthreads);
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < nslab; ++bh) {
+    double *S = (double *)calloc(dd, sizeof(double));
+    double *Pr = (double *)malloc(dd * sizeof(double));
+    double *kt = (double *)malloc((size_t)d * sizeof(double));
+    double *e = (double *)malloc((size_t)d * sizeof(double));
+    const size_t base = (size_t)bh * N * d;
+    if (S_in) memcpy(S, S_in + (size_t)bh * dd, dd * sizeof(double));
+    for (int f = 0; f < F; ++f) {
+      const double gm = gamma[(size_t)bh * F + f];
+      for (size_t x = 0; x < dd; ++x) Pr[x] = gm * S[x];
+      for (size_t x = 0; x < dd; ++x) S[x] = Pr[x];
+      for (int t = 0; t < T; ++t) {
+        const size_t row = base + ((size_t)f * T + t) * d;
+        const double bt = beta[(size_t)bh * N + (size_t)f * T + t];
+        for (int i = 0; i < d; ++i) kt[i] = key_scale * ld(k, dt, row + i);
+        for (int j = 0; j < d; ++j) {
+          double pred = 0.0;
+          for (int i = 0; i < d; ++i) pred += Pr[(size_t)i * d + j] * kt[i];
+          e[j] = ld(v, dt, row + j) - pred;
+        }
+        for (int i = 0; i < d; ++i)
+          for (int j = 0; j < d; ++j) S[(size_t)i * d + j] += bt * kt[i] * e[j];
+      }
+      if (q && o) {
+        for (int t = 0; t < T; ++t) {
+          const size_t row = base + ((size_t)f * T + t) * d;
+          for (int j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += S[(size_t)i * d + j] * ld(q, dt, row + i);
+            o[row + j] = acc;
+          }
+        }
+      }
+    }
+    if (S_out) memcpy(S_out + (size_t)bh * dd, S, dd * sizeof(double));
+    free(S); free(Pr); free(kt); free(e);
+  }
+  return used;
+}
