@@ -19,6 +19,8 @@ Entry points (same names as the C ABI):
   rotary positions (:class:`Rope3D`)
 * :func:`gla_bwd_framecausal`, :func:`gla_bwd_bidir` -- the backward pass
   (dq, dk, dv, dg, dgamma and the carried-state gradients)
+* :func:`gla_gdn_framecausal` -- the frame-wise Gated DeltaNet mixer (a block
+  delta-rule update per frame, keys scaled by 1/sqrt(d T))
 * ``gla_*_workspace`` -- workspace sizes in bytes
 
 The operation is the gated linear attention token mixer of "SANA-Video 2.0:
@@ -40,7 +42,8 @@ __all__ = [
     "gla_fwd_bidir_ex", "gla_fwd_framecausal_ex", "gla_state_carry_ex",
     "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace", "gla_state_carry_workspace",
     "gla_fwd_bidir_ex_workspace", "gla_bwd_framecausal", "gla_bwd_bidir",
-    "gla_bwd_framecausal_workspace", "gla_bwd_bidir_workspace", "library_path", "load_library",
+    "gla_bwd_framecausal_workspace", "gla_bwd_bidir_workspace", "gla_gdn_framecausal",
+    "gla_gdn_framecausal_workspace", "library_path", "load_library",
     "profile_begin", "profile_end",
 ]
 
@@ -145,6 +148,10 @@ def load_library():
     lib.gla_bwd_framecausal.restype = i32
     lib.gla_bwd_bidir.argtypes = [vp] * 9 + [i32, i32, i64, i32, i32, f32, vp, sz, vp]
     lib.gla_bwd_bidir.restype = i32
+    lib.gla_gdn_framecausal_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.gla_gdn_framecausal_workspace.restype = sz
+    lib.gla_gdn_framecausal.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp, sz, vp]
+    lib.gla_gdn_framecausal.restype = i32
     lib.gla_status_string.argtypes = [i32]
     lib.gla_status_string.restype = ctypes.c_char_p
     lib.gla_last_error.argtypes = []
@@ -518,6 +525,48 @@ def gla_bwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                              _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), B, H, N, d, dt,
                              eps, _ptr(ws), wsb, _stream_handle(stream, dev)))
     return out
+
+
+def gla_gdn_framecausal_workspace(B: int, H: int, F: int, T: int, d: int) -> int:
+    return int(load_library().gla_gdn_framecausal_workspace(B, H, F, T, d))
+
+
+def gla_gdn_framecausal(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
+                        beta: torch.Tensor, gamma: torch.Tensor,
+                        S_in: Optional[torch.Tensor] = None, key_scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None, S_out: Optional[torch.Tensor] = None,
+                        return_state: bool = False, workspace: Optional[torch.Tensor] = None,
+                        stream=None):
+    """Frame-wise Gated DeltaNet: F = gamma.shape[-1], T = N / F; beta [B, H, N]
+    fp32. key_scale defaults to 1/sqrt(d T). q None computes the state only.
+
+    Returns o, or (o, S_out) with ``return_state`` or S_out given."""
+    lib = load_library()
+    ref = _qkvg(*(t for t in (q, k, v) if t is not None))
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if beta.shape != (B, H, N) or beta.dtype != torch.float32:
+        raise ValueError("beta must be float32 [B, H, N]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    if key_scale is None:
+        key_scale = 1.0 / (d * T) ** 0.5 if T else 1.0
+    want_state = return_state or S_out is not None or q is None
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
+    o = None if q is None else (torch.empty_like(ref) if out is None else out)
+    dev = _require_device(q, k, v, beta, gamma, S_in, o, S_out, workspace)
+    ws, wsb = _workspace(lib.gla_gdn_framecausal_workspace(B, H, F, T, d), dev, workspace)
+    _check(lib.gla_gdn_framecausal(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma),
+                                   _ptr(S_in), _ptr(o), _ptr(S_out), B, H, F, T, d, dt,
+                                   float(key_scale), _ptr(ws), wsb, _stream_handle(stream, dev)))
+    if q is None:
+        return S_out
+    return (o, S_out) if want_state else o
 
 
 def profile_begin(max_launches: int = 4096) -> None:

@@ -29,6 +29,9 @@ hipError_t launch_bwd_q_valu(const BwdPlan &p, int dtype, const BwdQArgs &a, hip
 hipError_t launch_bwd_k_valu(const BwdPlan &p, int dtype, const BwdKArgs &a, hipStream_t s);
 hipError_t launch_bwd_k_mfma(const BwdPlan &p, const BwdKArgs &a, hipStream_t s);
 hipError_t launch_bwd_q_mfma(const BwdPlan &p, const BwdQArgs &a, hipStream_t s);
+hipError_t launch_gdn_kv_valu(const Plan &p, int dtype, const GdnKvArgs &a, hipStream_t s);
+hipError_t launch_gdn_readout_valu(const Plan &p, int dtype, const GdnReadoutArgs &a,
+                                   hipStream_t s);
 bool mfma_supports(int d);
 
 namespace {
@@ -130,10 +133,14 @@ enum Kind {
   kKindRevScan = 4,
   kKindBwdK = 5,
   kKindDgamma = 6,
-  kNumKinds = 7
+  kKindGdnKv = 7,
+  kKindGdnScan = 8,
+  kKindGdnReadout = 9,
+  kNumKinds = 10
 };
-const char *const kKindNames[kNumKinds] = {"kv", "carry", "readout", "bwd_q", "rev_scan",
-                                           "bwd_k", "dgamma"};
+const char *const kKindNames[kNumKinds] = {"kv",     "carry",  "readout",  "bwd_q",
+                                           "rev_scan", "bwd_k", "dgamma", "gdn_kv",
+                                           "gdn_scan", "gdn_readout"};
 
 struct Profiler {
   std::mutex mu;
@@ -484,7 +491,112 @@ gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, cons
   return GLA_OK;
 }
 
+// The body of gla_gdn_framecausal (contiguous [B][H][N][d] tensors).
+gla_status run_gdn(const void *q, const void *k, const void *v, const float *beta,
+                   const float *gamma, const float *S_in, void *o, float *S_out, int B, int H,
+                   int F, int T, int d, gla_dtype dt, float key_scale, void *ws,
+                   size_t ws_bytes, void *stream) {
+  GLA_TRY(check_dims(B, H, d, dt));
+  if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%d must be >= 0", F, T);
+  if (!std::isfinite(key_scale) || !(key_scale > 0.f))
+    return fail(GLA_ERR_VALUE, "key_scale=%g must be finite and > 0", (double)key_scale);
+  if ((q == nullptr) != (o == nullptr))
+    return fail(GLA_ERR_NULL, "q and o must both be given (outputs) or both be NULL (state only)");
+  if (!o && !S_out) return fail(GLA_ERR_NULL, "nothing to compute: o and S_out are both NULL");
+  const int64_t BH = (int64_t)B * H;
+  const int64_t N = (int64_t)F * T;
+  const bool have_tokens = BH > 0 && N > 0;
+  if (have_tokens && (!k || !v || !beta)) return fail(GLA_ERR_NULL, "k, v and beta are required");
+  if (BH > 0 && F > 0 && !gamma) return fail(GLA_ERR_NULL, "gamma is required when F > 0");
+  const void *tens[] = {q, k, v, o};
+  const char *tn[] = {"q", "k", "v", "o"};
+  for (int i = 0; i < 4; ++i) GLA_TRY(check_tensor_align(tens[i], tn[i]));
+  GLA_TRY(check_tensor_align(S_in, "S_in"));
+  GLA_TRY(check_tensor_align(S_out, "S_out"));
+  if (beta && !aligned(beta, 4)) return fail(GLA_ERR_ALIGN, "beta is not 4-byte aligned");
+  if (gamma && !aligned(gamma, 4)) return fail(GLA_ERR_ALIGN, "gamma is not 4-byte aligned");
+  Plan p;
+  if (!make_gdn_plan(BH, F, T, d, &p)) return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
+  if (BH == 0) return GLA_OK;
+  GLA_TRY(check_ws(p, ws, ws_bytes));
+  const size_t es = dt == GLA_F32 ? 4 : 2;
+  const size_t tb = (size_t)(BH * N * d) * es;
+  const size_t sbytes = (size_t)(BH * d * d) * 4;
+  const Range all[] = {{q, tb, "q"},
+                       {k, tb, "k"},
+                       {v, tb, "v"},
+                       {beta, (size_t)(BH * N) * 4, "beta"},
+                       {gamma, (size_t)(BH * F) * 4, "gamma"},
+                       {S_in, sbytes, "S_in"},
+                       {o, tb, "o"},
+                       {S_out, sbytes, "S_out"},
+                       {ws, p.ws_bytes, "workspace"}};
+  const Range outs[] = {all[6], all[7], all[8]};
+  // S_out may be S_in (in-place carry): compare it without S_in
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 9; ++j) {
+      if (!strcmp(outs[i].name, all[j].name)) continue;
+      if (i == 1 && j == 5 && S_out == S_in) continue;
+      if (overlap(outs[i], all[j]))
+        return fail(GLA_ERR_ALIAS, "%s overlaps %s", outs[i].name, all[j].name);
+    }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Path path = select_path(dt, d);
+  float *wsf = static_cast<float *>(ws);
+  // (T == 0 still launches it: every frame's sums are then written as zeros)
+  if (p.F > 0)
+    GLA_TRY(launched(timed(kKindGdnKv, s,
+                           [&] {
+                             return launch_gdn_kv(p, dt, path,
+                                                  GdnKvArgs{contiguous_view(k, H, N, d),
+                                                            contiguous_view(v, H, N, d), H, beta,
+                                                            wsf},
+                                                  s);
+                           }),
+                     "gdn_kv"));
+  GLA_TRY(launched(timed(kKindGdnScan, s,
+                         [&] {
+                           return launch_gdn_scan(
+                               p, GdnScanArgs{wsf, gamma, S_in, S_out, key_scale}, s);
+                         }),
+                   "gdn_scan"));
+  if (o && have_tokens)
+    GLA_TRY(launched(timed(kKindGdnReadout, s,
+                           [&] {
+                             return launch_gdn_readout(
+                                 p, dt, path,
+                                 GdnReadoutArgs{contiguous_view(q, H, N, d),
+                                                contiguous_view(o, H, N, d), H, wsf},
+                                 s);
+                           }),
+                     "gdn_readout"));
+  return GLA_OK;
+}
+
 }  // namespace
+
+bool make_gdn_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
+  Plan p;
+  if (!make_plan(BH, F, T, d, &p)) return false;
+  p.G = 1;
+  p.NG = F;
+  p.ws_bytes = (size_t)round_up(BH * F * (int64_t)p.P * 2 * d * d * 4, 256);
+  *plan = p;
+  return true;
+}
+
+hipError_t launch_gdn_kv(const Plan &p, int dtype, Path path, const GdnKvArgs &a,
+                         hipStream_t s) {
+  (void)path;
+  return launch_gdn_kv_valu(p, dtype, a, s);
+}
+
+hipError_t launch_gdn_readout(const Plan &p, int dtype, Path path, const GdnReadoutArgs &a,
+                              hipStream_t s) {
+  (void)path;
+  return launch_gdn_readout_valu(p, dtype, a, s);
+}
 
 bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
   Plan p;
@@ -703,6 +815,22 @@ GLA_EXPORT gla_status gla_bwd_bidir(const void *q, const void *k, const void *v,
   return run_bwd(true, q, k, v, g, nullptr, nullptr, nullptr, dO, nullptr, nullptr, dq, dk, dv,
                  dg, nullptr, nullptr, nullptr, B, H, N > 0 ? 1 : 0, N, d, dt, eps, ws, ws_bytes,
                  stream);
+}
+
+GLA_EXPORT size_t gla_gdn_framecausal_workspace(int B, int H, int F, int T, int d) {
+  Plan p;
+  if (B < 0 || H < 0 || F < 0 || T < 0 || d <= 0) return 0;
+  if (!make_gdn_plan((int64_t)B * H, F, T, d, &p)) return 0;
+  return p.ws_bytes;
+}
+
+GLA_EXPORT gla_status gla_gdn_framecausal(const void *q, const void *k, const void *v,
+                                          const float *beta, const float *gamma,
+                                          const float *S_in, void *o, float *S_out, int B, int H,
+                                          int F, int T, int d, gla_dtype dt, float key_scale,
+                                          void *ws, size_t ws_bytes, void *stream) {
+  return run_gdn(q, k, v, beta, gamma, S_in, o, S_out, B, H, F, T, d, dt, key_scale, ws,
+                 ws_bytes, stream);
 }
 
 GLA_EXPORT const char *gla_status_string(gla_status s) {

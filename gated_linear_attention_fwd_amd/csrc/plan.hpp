@@ -189,6 +189,39 @@ hipError_t launch_rev_scan(const BwdPlan &p, const RevScanArgs &a, hipStream_t s
 hipError_t launch_bwd_k(const BwdPlan &p, int dtype, Path path, const BwdKArgs &a, hipStream_t s);
 hipError_t launch_dgamma(const BwdPlan &p, const float *dgp, float *dgamma, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Frame-wise Gated DeltaNet: gdn_kv (per slab, frame, part: U = sum beta k v^T,
+// A = sum beta k k^T into a slot of 2 d^2 floats), gdn_scan (per slab and
+// block of state columns: S_f = gamma_f (S_{f-1} - c^2 A_f S_{f-1}) + c U_f,
+// left in part 0's U area), gdn_readout (o = S_f^T q). One frame per group.
+// ---------------------------------------------------------------------------
+struct GdnKvArgs {
+  View k, v;
+  int H;
+  const float *beta;  // [B][H][N]
+  float *ws;
+};
+
+struct GdnScanArgs {
+  float *ws;
+  const float *gamma;  // [B][H][F]
+  const float *S_in;   // NULL: zero
+  float *S_out;        // NULL: not written
+  float key_scale;
+};
+
+struct GdnReadoutArgs {
+  View q, o;  // o written
+  int H;
+  const float *ws;
+};
+
+bool make_gdn_plan(int64_t BH, int F, int64_t T, int d, Plan *plan);
+hipError_t launch_gdn_kv(const Plan &p, int dtype, Path path, const GdnKvArgs &a, hipStream_t s);
+hipError_t launch_gdn_scan(const Plan &p, const GdnScanArgs &a, hipStream_t s);
+hipError_t launch_gdn_readout(const Plan &p, int dtype, Path path, const GdnReadoutArgs &a,
+                              hipStream_t s);
+
 hipError_t launch_kv(const Plan &p, int dtype, Path path, const KvArgs &a, hipStream_t s);
 hipError_t launch_carry(const Plan &p, const CarryArgs &a, hipStream_t s);
 hipError_t launch_readout(const Plan &p, int dtype, Path path, const ReadoutArgs &a,

@@ -135,6 +135,32 @@ gla_status gla_bwd_bidir(const void *q, const void *k, const void *v, const void
                          int64_t N, int d, gla_dtype dt, float eps, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* ---- frame-wise Gated DeltaNet ----------------------------------------------
+ *
+ * The other linear mixer of the pages: the SANA-WM analysis page (method
+ * components; claim checks) describes a frame-wise Gated DeltaNet -- decay
+ * gates plus a delta-rule correction of the recurrent state, with keys scaled
+ * by 1/sqrt(D S) -- and gives no equations. This library reads it as one block
+ * delta-rule update per frame, every token of the frame measuring its
+ * prediction error against the same decayed prior (S = tokens per frame):
+ *   P_f = gamma_f S_{f-1}                 (S_{-1} = S_in, or 0)
+ *   e_t = v_t - P_f^T (c k_t)             c = key_scale (1/sqrt(d T) reads the pages)
+ *   S_f = P_f + sum_{t in f} beta_t (c k_t) e_t^T
+ *   o_t = S_f^T q_t                       every token of frame f
+ * There is no feature map, normaliser or gate: q, k, v are used as given.
+ * q, k, v, o [B][H][F*T][d] (GLA_F32 or GLA_BF16, rounded to nearest even);
+ * beta [B][H][F*T] fp32 write strengths (typically in [0, 1]); gamma [B][H][F]
+ * fp32; S_in, S_out [B][H][d][d] fp32 (either may be NULL; S_out may be S_in).
+ * q and o both NULL: the state only (a block-cache commit). key_scale must be
+ * finite and > 0. Conventions otherwise as above; the workspace holds 2 d^2
+ * floats per (slab, frame, part). */
+size_t gla_gdn_framecausal_workspace(int B, int H, int F, int T, int d);
+
+gla_status gla_gdn_framecausal(const void *q, const void *k, const void *v, const float *beta,
+                               const float *gamma, const float *S_in, void *o, float *S_out,
+                               int B, int H, int F, int T, int d, gla_dtype dt, float key_scale,
+                               void *ws, size_t ws_bytes, void *stream);
+
 /* ---- strided tensors and fused 3D rotary positions ------------------------
  *
  * The *_ex entry points compute the same operation as the plain ones, with
@@ -236,7 +262,8 @@ int gla_version(void); /* 10100: adds the *_ex entry points */
  * entry points (on any stream, from any thread) is bracketed by a pair of HIP
  * events recorded on its stream. gla_profile_end waits for those events and
  * returns, per kernel kind ("kv", "carry", "readout", and for the backward
- * "bwd_q", "rev_scan", "bwd_k", "dgamma"), the number of launches
+ * "bwd_q", "rev_scan", "bwd_k", "dgamma", and for the Gated DeltaNet "gdn_kv",
+ * "gdn_scan", "gdn_readout"), the number of launches
  * and their summed event time. At most max_launches launches are timed; later
  * ones run untimed. Not meant to overlap with itself: one session at a time.
  * gla_profile_begin creates 2 * max_launches HIP events (max_launches must be
