@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "GLA fwd tokens/s at 720p/60s shape; % HBM/MFMA roofline vs CPU oracle"
 METRIC_BWD = "GLA bwd tokens/s at 720p/60s shape; % HBM/MFMA roofline vs CPU oracle"
+METRIC_GDN = "Gated DeltaNet fwd tokens/s at 720p/60s shape; % HBM roofline vs CPU oracle"
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 BF16_MFMA_PEAK = 2.5e15  # dense bf16 matrix-core peak, flop/s
 
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="fwd: the forward call (the headline); bwd: the backward call "
                          "(gradients of the forward for a random dL/do)")
+    ap.add_argument("--mixer", default="gla", choices=["gla", "gdn"],
+                    help="gla: gated linear attention (the headline); gdn: the frame-wise "
+                         "Gated DeltaNet (beta = sigmoid of a normal draw per token)")
     ap.add_argument("--rope", action="store_true",
                     help="fused 3D rotary positions over the latent grid (the *_ex entry points)")
     ap.add_argument("--cpu-heads", type=int, default=32,
@@ -166,6 +170,18 @@ def main():
         wsb = max(gla.gla_fwd_framecausal_workspace(w.B, w.H, b["gamma"].shape[-1], w.T, d)
                   for b in blocks)
     bwd = args.which == "bwd"
+    gdn = args.mixer == "gdn"
+    if gdn and (bwd or ex or mode != "framecausal"):
+        print("bench.py: the Gated DeltaNet runs frame-causal, forward, contiguous",
+              file=sys.stderr)
+        sys.exit(2)
+    if gdn:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed * 1000 + 11)
+        for b in blocks:
+            b["beta"] = torch.sigmoid(torch.randn(b["q"].shape[:3], generator=gen, device=dev))
+        wsb = max(gla.gla_gdn_framecausal_workspace(w.B, w.H, b["gamma"].shape[-1], w.T, d)
+                  for b in blocks)
     if bwd and ex:
         print("bench.py: the backward takes contiguous tensors without rotary positions",
               file=sys.stderr)
@@ -213,7 +229,18 @@ def main():
                                         workspace=ws)
             dS, dz = r.get("dS_in"), r.get("dz_in")
 
+    def step_gdn():
+        carry = len(blocks) > 1
+        if carry:
+            S.zero_()
+        for b, o in zip(blocks, outs):
+            gla.gla_gdn_framecausal(b["q"], b["k"], b["v"], b["beta"], b["gamma"],
+                                    S if carry else None, out=o, S_out=S, workspace=ws)
+
     def step():
+        if gdn:
+            step_gdn()
+            return
         if bwd:
             step_bwd()
             return
@@ -270,7 +297,8 @@ def main():
     torch.cuda.synchronize()
     # algorithmic bytes per token-head of each kernel
     per_unit = {"kv": 2 * d * es, "readout": 3 * d * es, "carry": 0,
-                "bwd_q": 5 * d * es, "bwd_k": 4 * d * es}
+                "bwd_q": 5 * d * es, "bwd_k": 4 * d * es,
+                "gdn_kv": 2 * d * es + 4, "gdn_readout": 2 * d * es}
     token_heads = w.B * w.H * w.N
     kernels = {}
     for name, (n, total) in prof.items():
@@ -284,15 +312,19 @@ def main():
     dk = kernels[dom]
     achieved = dk["alg_bytes_per_launch"] / (dk["avg_ms"] / 1e3)
     variant = w.name + "/" + mode + ("/fused" if args.layout == "fused" else "") + \
-        ("/rope" if args.rope else "") + ("/bwd" if bwd else "")
+        ("/rope" if args.rope else "") + ("/bwd" if bwd else "") + ("/gdn" if gdn else "")
     traffic_rec = committed_traffic(dom, variant)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                 "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
     # forward: read q, k, v, g, write o; backward: read q, k, v, g, dO, write dq,
     # dk, dv, dg (the recompute's second read of k and v is not counted)
-    call_bytes = w.io_bytes() * 9 // 5 if bwd else w.io_bytes()
-    flops = (12 if bwd else 4) * d * d * token_heads
+    if gdn:  # read q, k, v, beta, write o
+        call_bytes = w.io_bytes() * 4 // 5 + 4 * token_heads
+        flops = 6 * d * d * token_heads  # U, A, readout
+    else:
+        call_bytes = w.io_bytes() * 9 // 5 if bwd else w.io_bytes()
+        flops = (12 if bwd else 4) * d * d * token_heads
     call = {"alg_bytes": call_bytes, "GBps": round(call_bytes / (ms_per_step / 1e3) / 1e9, 1),
             "frac_of_hbm_peak": round(call_bytes / (ms_per_step / 1e3) / HBM_PEAK, 4),
             "flops": flops,
@@ -302,14 +334,17 @@ def main():
     cpu = None
     parity = None
     if not args.no_cpu and args.cpu_heads > 0:
-        if bwd:
+        if gdn:
+            cpu, parity = cpu_baseline_gdn(args, w, blocks, outs, value)
+        elif bwd:
             cpu, parity = cpu_baseline_bwd(args, w, mode, blocks, grads, value)
         else:
             cpu, parity = cpu_baseline(args, w, mode, blocks, outs, value,
                                        ropes[0].as_dict() if args.rope else None)
 
     line = {
-        "metric": METRIC_BWD if bwd else METRIC, "value": round(value, 1), "unit": "tokens/s",
+        "metric": METRIC_GDN if gdn else (METRIC_BWD if bwd else METRIC), "value": round(value, 1),
+        "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
@@ -320,7 +355,9 @@ def main():
                               if args.layout == "fused" else "[B,H,N,d] contiguous"),
                    "rope": ropes[0].as_dict() if args.rope else None,
                    "pass": "backward (dq, dk, dv, dg, dgamma for a random dL/do)" if bwd
-                   else "forward"},
+                   else "forward",
+                   "mixer": ("frame-wise Gated DeltaNet (block delta rule per frame, key "
+                             "scale 1/sqrt(d T))" if gdn else "gated linear attention")},
         "roofline": roofline, "call": call, "kernels": kernels, "cpu_baseline": cpu,
         "parity": parity, "wall_s": round(wall, 3), "source_hash": source_hash(),
     }
@@ -378,6 +415,50 @@ def cpu_baseline(args, w, mode, blocks, outs, gpu_value, rope=None):
                      "tokens/s = head-tokens/s / H" % (nh, w.B * w.H, w.N,
                                                        " with rotary positions" if rope else "",
                                                        el),
+           "host_cpu": host_cpu_model(), "gpu_over_cpu": round(gpu_value / cpu_tokens_per_s, 1)}
+    o64 = oracle.bf16_to_f64(got) if got.dtype == np.uint16 else got.astype(np.float64)
+    r2 = ref.reshape(1, nh, -1)
+    rms = np.sqrt(np.mean(r2 * r2, axis=-1, keepdims=True))
+    err = np.abs(o64.reshape(r2.shape) - r2) / np.maximum(np.maximum(np.abs(r2), rms), 1e-300)
+    parity = {"heads": nh, "max_slab_rel_err": float(err.max()),
+              "bar": 1e-4 if w.dtype == "f32" else 2e-2}
+    return cpu, parity
+
+
+def cpu_baseline_gdn(args, w, blocks, outs, gpu_value):
+    """Time oracle.gdn on a bounded sample of heads (the whole stream at once)
+    and check o of those heads."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    nh = min(args.cpu_heads, w.B * w.H)
+    heads = [(i // w.H, i % w.H) for i in range(nh)]
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.contiguous().cpu().numpy()
+
+    def sel(t):
+        return np.concatenate([host(t[b:b + 1, h:h + 1]) for (b, h) in heads], axis=1)
+
+    x = {n: np.concatenate([sel(b[n]) for b in blocks], axis=2)
+         for n in ("q", "k", "v", "beta", "gamma")}
+    got = np.concatenate([sel(o) for o in outs], axis=2)
+    threads = min(oracle.max_threads(), nh)
+    print("bench: CPU Gated DeltaNet oracle on %d heads, %d threads" % (nh, threads),
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ref, _ = oracle.gdn(x["q"], x["k"], x["v"], x["beta"], x["gamma"],
+                        key_scale=1.0 / np.sqrt(w.d * w.T))
+    el = time.perf_counter() - t0
+    cpu_tokens_per_s = nh * w.N / el / w.H
+    cpu = {"value": round(cpu_tokens_per_s, 1), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": "%d of %d heads (all %d tokens each), fp64 Gated DeltaNet oracle, %.1f s; "
+                     "tokens/s = head-tokens/s / H" % (nh, w.B * w.H, w.N, el),
            "host_cpu": host_cpu_model(), "gpu_over_cpu": round(gpu_value / cpu_tokens_per_s, 1)}
     o64 = oracle.bf16_to_f64(got) if got.dtype == np.uint16 else got.astype(np.float64)
     r2 = ref.reshape(1, nh, -1)
