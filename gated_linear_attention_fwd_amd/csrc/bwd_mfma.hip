@@ -19,67 +19,6 @@
 namespace gla {
 namespace {
 
-// x = hi + lo, both bf16: returns hi in the low half, lo in the high half
-__device__ __forceinline__ uint32_t split_hl(float x) {
-  const uint16_t h = f32_to_bf16_rne(x);
-  return (uint32_t)h | ((uint32_t)f32_to_bf16_rne(x - bf16_to_f32(h)) << 16);
-}
-
-// (x0, x1) = hi + lo with both parts bf16, as packed pairs: v_cvt_pk_bf16_f32
-// rounds to nearest even, like split_hl, two values per instruction
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
-  hi = pack_bf16x2(x0, x1);
-  lo = pack_bf16x2(x0 - lo_bf16(hi), x1 - hi_bf16(hi));
-}
-
-// A fragments (hi, lo) of M^T for output block mb: A[m = j][k = i] = M[i][j]
-template <int D>
-__device__ __forceinline__ void frag_transposed(const float *M, int mb, int lane, bf16x8 *hi,
-                                                bf16x8 *lo) {
-  const int h = lane >> 5, col = 32 * mb + (lane & 31);
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    i16x8 hv, lv;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t x = split_hl(M[(16 * ks + 8 * h + e) * D + col]);
-      hv[e] = (short)(x & 0xFFFFu);
-      lv[e] = (short)(x >> 16);
-    }
-    hi[ks] = __builtin_bit_cast(bf16x8, hv);
-    lo[ks] = __builtin_bit_cast(bf16x8, lv);
-    asm volatile("" ::: "memory");  // one k-step of loads in flight at a time (registers)
-  }
-}
-
-// A fragments (hi, lo) of M for output block mb: A[m = i][k = j] = M[i][j]
-// (each lane reads 8 consecutive floats of a row)
-template <int D>
-__device__ __forceinline__ void frag_direct(const float *M, int mb, int lane, bf16x8 *hi,
-                                            bf16x8 *lo) {
-  const int h = lane >> 5, row = 32 * mb + (lane & 31);
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const float4 a = *reinterpret_cast<const float4 *>(M + row * D + 16 * ks + 8 * h);
-    const float4 b = *reinterpret_cast<const float4 *>(M + row * D + 16 * ks + 8 * h + 4);
-    const float xs[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    i16x8 hv, lv;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t x = split_hl(xs[e]);
-      hv[e] = (short)(x & 0xFFFFu);
-      lv[e] = (short)(x >> 16);
-    }
-    hi[ks] = __builtin_bit_cast(bf16x8, hv);
-    lo[ks] = __builtin_bit_cast(bf16x8, lv);
-  }
-}
-
-__device__ __forceinline__ void st_stream16(uint4 *p, uint4 v) {
-  const u32x4 x = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(p));
-}
-
 // ---------------------------------------------------------------------------
 // Key side: one workgroup of 8 waves per (slab, frame, part). The 2 MB
 // (role, feature block) pairs -- role dv (A = Sh^T) or dk (A = Sh) -- are
