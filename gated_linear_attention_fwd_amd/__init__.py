@@ -577,7 +577,9 @@ def profile_begin(max_launches: int = 4096) -> None:
 def profile_end() -> dict:
     """Stop timing; returns {kernel kind: (launches, summed milliseconds)}."""
     lib = load_library()
-    out = (_KernelTime * 8)()
+    cap = 16  # more than the library's kernel kinds
+    out = (_KernelTime * cap)()
     n = ctypes.c_int(0)
-    _check(lib.gla_profile_end(out, 8, ctypes.byref(n)))
-    return {out[i].name.decode(): (out[i].launches, out[i].total_ms) for i in range(min(n.value, 8))}
+    _check(lib.gla_profile_end(out, cap, ctypes.byref(n)))
+    return {out[i].name.decode(): (out[i].launches, out[i].total_ms)
+            for i in range(min(n.value, cap))}

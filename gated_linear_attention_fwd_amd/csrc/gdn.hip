@@ -286,7 +286,7 @@ hipError_t launch_gdn_readout_valu(const Plan &p, int dtype, const GdnReadoutArg
                     : gdn_readout_valu_dispatch<bf16_t>(p, a, s);
 }
 
-hipError_t launch_gdn_scan(const Plan &p, const GdnScanArgs &a, hipStream_t s) {
+hipError_t launch_gdn_scan_valu(const Plan &p, const GdnScanArgs &a, hipStream_t s) {
   if (p.BH == 0) return hipSuccess;
   switch (p.d) {
     case 16: gdn_scan_launch<16>(p, a, s); break;

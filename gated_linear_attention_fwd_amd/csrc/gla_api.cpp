@@ -30,6 +30,10 @@ hipError_t launch_bwd_k_valu(const BwdPlan &p, int dtype, const BwdKArgs &a, hip
 hipError_t launch_bwd_k_mfma(const BwdPlan &p, const BwdKArgs &a, hipStream_t s);
 hipError_t launch_bwd_q_mfma(const BwdPlan &p, const BwdQArgs &a, hipStream_t s);
 hipError_t launch_gdn_kv_valu(const Plan &p, int dtype, const GdnKvArgs &a, hipStream_t s);
+hipError_t launch_gdn_kv_mfma(const Plan &p, const GdnKvArgs &a, hipStream_t s);
+hipError_t launch_gdn_scan_valu(const Plan &p, const GdnScanArgs &a, hipStream_t s);
+hipError_t launch_gdn_scan_mfma(const Plan &p, const GdnScanArgs &a, hipStream_t s);
+hipError_t launch_gdn_readout_mfma(const Plan &p, const GdnReadoutArgs &a, hipStream_t s);
 hipError_t launch_gdn_readout_valu(const Plan &p, int dtype, const GdnReadoutArgs &a,
                                    hipStream_t s);
 bool mfma_supports(int d);
@@ -558,7 +562,7 @@ gla_status run_gdn(const void *q, const void *k, const void *v, const float *bet
   GLA_TRY(launched(timed(kKindGdnScan, s,
                          [&] {
                            return launch_gdn_scan(
-                               p, GdnScanArgs{wsf, gamma, S_in, S_out, key_scale}, s);
+                               p, path, GdnScanArgs{wsf, gamma, S_in, S_out, key_scale}, s);
                          }),
                    "gdn_scan"));
   if (o && have_tokens)
@@ -588,13 +592,18 @@ bool make_gdn_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
 
 hipError_t launch_gdn_kv(const Plan &p, int dtype, Path path, const GdnKvArgs &a,
                          hipStream_t s) {
-  (void)path;
+  if (path == Path::kMfma) return launch_gdn_kv_mfma(p, a, s);
   return launch_gdn_kv_valu(p, dtype, a, s);
+}
+
+hipError_t launch_gdn_scan(const Plan &p, Path path, const GdnScanArgs &a, hipStream_t s) {
+  if (path == Path::kMfma) return launch_gdn_scan_mfma(p, a, s);
+  return launch_gdn_scan_valu(p, a, s);
 }
 
 hipError_t launch_gdn_readout(const Plan &p, int dtype, Path path, const GdnReadoutArgs &a,
                               hipStream_t s) {
-  (void)path;
+  if (path == Path::kMfma) return launch_gdn_readout_mfma(p, a, s);
   return launch_gdn_readout_valu(p, dtype, a, s);
 }
 

@@ -15,6 +15,7 @@ namespace gla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
@@ -57,6 +58,13 @@ __device__ __forceinline__ void sync_lds() {
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 bf16 (lane l, g = l / 16):
+//   A[m][k]: m = l % 16, k = 8g .. 8g+7;  B[k][n]: n = l % 16, k = 8g .. 8g+7
+//   C[m][n]: element r holds m = 4g + r, n = l % 16
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // ReLU of two packed bf16: as signed 16-bit integers every negative bf16

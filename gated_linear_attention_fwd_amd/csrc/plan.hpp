@@ -218,7 +218,7 @@ struct GdnReadoutArgs {
 
 bool make_gdn_plan(int64_t BH, int F, int64_t T, int d, Plan *plan);
 hipError_t launch_gdn_kv(const Plan &p, int dtype, Path path, const GdnKvArgs &a, hipStream_t s);
-hipError_t launch_gdn_scan(const Plan &p, const GdnScanArgs &a, hipStream_t s);
+hipError_t launch_gdn_scan(const Plan &p, Path path, const GdnScanArgs &a, hipStream_t s);
 hipError_t launch_gdn_readout(const Plan &p, int dtype, Path path, const GdnReadoutArgs &a,
                               hipStream_t s);
 

@@ -263,7 +263,8 @@ int gla_version(void); /* 10100: adds the *_ex entry points */
  * events recorded on its stream. gla_profile_end waits for those events and
  * returns, per kernel kind ("kv", "carry", "readout", and for the backward
  * "bwd_q", "rev_scan", "bwd_k", "dgamma", and for the Gated DeltaNet "gdn_kv",
- * "gdn_scan", "gdn_readout"), the number of launches
+ * "gdn_scan", "gdn_readout"; "gdn_scan" includes the summing of a frame's parts
+ * where the frame is split over several workgroups), the number of launches
  * and their summed event time. At most max_launches launches are timed; later
  * ones run untimed. Not meant to overlap with itself: one session at a time.
  * gla_profile_begin creates 2 * max_launches HIP events (max_launches must be

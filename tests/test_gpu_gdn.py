@@ -79,6 +79,9 @@ CASES = [
     ("bf16", 2, 2, 32, 6, 61, True),
     ("bf16", 1, 2, 128, 3, 100, True),
     ("bf16", 1, 3, 16, 4, 33, False),
+    ("bf16", 1, 2, 64, 1, 40, True),     # a single frame
+    ("bf16", 1, 2, 64, 2, 300, False),   # three parts per frame, ragged last part
+    ("bf16", 1, 2, 128, 4, 520, True),   # five parts per frame at d = 128
 ]
 
 
@@ -157,6 +160,22 @@ def test_gdn_no_writes():
     w = np.repeat(np.cumprod(x["gamma"].astype(np.float64), axis=-1), T, axis=-1)[..., None]
     want = np.einsum("bhnd,bhde->bhne", x["q"].astype(np.float64), S_in.astype(np.float64)) * w
     assert slab_rel_err(o.cpu().numpy(), want) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64), ("bf16", 128)])
+def test_gdn_no_tokens(dtype, d):
+    """T = 0: every frame only decays the state, S_out = (prod gamma) S_in."""
+    B, H, F = 1, 2, 3
+    rng = np.random.default_rng(d)
+    S_in = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.0, (B, H, F)).astype(np.float32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    e = torch.empty((B, H, 0, d), dtype=tdt, device=DEV)
+    o, S = gla.gla_gdn_framecausal(e, e, e, torch.empty((B, H, 0), device=DEV), dev(gamma),
+                                   dev(S_in), key_scale=0.5, return_state=True)
+    want = S_in.astype(np.float64) * np.prod(gamma.astype(np.float64), axis=-1)[..., None, None]
+    assert o.numel() == 0
+    assert max_abs_over_max(S.cpu().numpy(), want) <= STATE_TOL
 
 
 def test_gdn_720p_60s_sampled_heads():
