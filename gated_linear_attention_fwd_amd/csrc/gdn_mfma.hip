@@ -334,9 +334,13 @@ struct GsCfg {
   static constexpr int KS = D / 32;                   // k-steps of 32 rows
   static constexpr int PITCH = 2 * D + 16;            // bytes per LDS row of a plane
   static constexpr int APT = D * D / (4 * THREADS);   // float4 pieces of A_f per thread
-  // loads two frames ahead (d <= 64; at d = 128 a second buffer would not fit
-  // beside the state in registers)
-  static constexpr bool kAhead2 = D <= 64;
+  // frames loaded ahead (at d = 128 a second buffer would not fit beside the
+  // state in registers)
+#ifdef GLA_SCAN_AHEAD
+  static constexpr int AHEAD = D == 128 ? 1 : GLA_SCAN_AHEAD;
+#else
+  static constexpr int AHEAD = D == 128 ? 1 : 2;
+#endif
 };
 
 // LDS position (in elements) of column col of a plane row
@@ -450,19 +454,15 @@ __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
       }
   };
 
-  if constexpr (C::kAhead2) {
-    // two frames in flight: frame f + 2 is requested as frame f is staged
-    Frame b0, b1;
-    if (F > 0) load_frame(0, b0);
-    if (F > 1) load_frame(1, b1);
-    for (int f = 0; f < F; f += 2) {
-      step(f, b0, f + 2);
-      if (f + 1 < F) step(f + 1, b1, f + 3);
-    }
-  } else {
-    Frame b0;
-    if (F > 0) load_frame(0, b0);
-    for (int f = 0; f < F; ++f) step(f, b0, f + 1);
+  // AHEAD frames in flight: frame f + AHEAD is requested as frame f is staged
+  Frame buf[C::AHEAD];
+#pragma unroll
+  for (int i = 0; i < C::AHEAD; ++i)
+    if (i < F) load_frame(i, buf[i]);
+  for (int f = 0; f < F; f += C::AHEAD) {
+#pragma unroll
+    for (int i = 0; i < C::AHEAD; ++i)
+      if (f + i < F) step(f + i, buf[i], f + i + C::AHEAD);
   }
   if (S_out) {
 #pragma unroll
