@@ -13,6 +13,10 @@ Formulations (each function returns ``(o, S_out, z_out)`` as float64 arrays):
 * :func:`quadratic` -- explicit weighted sum over key tokens (O(N^2 d)).
 * :func:`chunked`   -- chunk sums of phi(k) v^T, per-frame sum, scan, readout.
 
+Also :func:`backward` (gradients of the same forward), :func:`gdn` (the
+frame-wise Gated DeltaNet) and :func:`softmax_anchor` (gated softmax attention
+over whole frames with sink frames and a local window).
+
 Definitions followed: the gated linear attention token mixer of "SANA-Video
 2.0: Hybrid Linear Attention with Attention Residuals for Efficient Video
 Generation" (section "Hybrid Linear-Softmax Attention"), its fixed D x D state
@@ -95,6 +99,9 @@ def _load():
     lib.gla_oracle_gdn.argtypes = [ctypes.c_int] + [vp] * 8 + [ctypes.c_int] * 5 + [
         ctypes.c_double, ctypes.c_int]
     lib.gla_oracle_gdn.restype = ctypes.c_int
+    lib.gla_oracle_softmax_anchor.argtypes = [ctypes.c_int] + [vp] * 5 + [ctypes.c_int] * 9 + [
+        ctypes.c_double, ctypes.c_int]
+    lib.gla_oracle_softmax_anchor.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -307,6 +314,39 @@ def gdn(q, k, v, beta, gamma, S_in=None, key_scale=None, T=None, outputs=True, n
     _load().gla_oracle_gdn(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma), _ptr(S_in),
                            _ptr(o), _ptr(S_out), B, H, F, T, d, float(key_scale), int(nthreads))
     return o, S_out
+
+
+def softmax_anchor(q, k, v, g, T, causal=True, n_sink=0, window=0, scale=None, nthreads=0):
+    """Gated softmax attention over whole frames; returns o (float64, shaped like q).
+
+    k, v [B, H, F*T, d] (F key frames of T tokens); q, g [B, H, Fq*T, d], the
+    tokens of the last Fq key frames. Full mode (causal False): every key is
+    visible. Frame-causal: query frame f sees key frames i <= f with
+    i < n_sink (sinks) or i > f - window (window <= 0: no limit). scale
+    defaults to 1/sqrt(d)."""
+    k = np.ascontiguousarray(k)
+    B, H, Nk, d = k.shape
+    dt = _DT.get(k.dtype)
+    if dt is None:
+        raise TypeError("unsupported input dtype %s" % k.dtype)
+    v = np.ascontiguousarray(v)
+    q = np.ascontiguousarray(q)
+    g = np.ascontiguousarray(g)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must share shape and dtype")
+    if q.shape[:2] != (B, H) or q.shape[3] != d or q.dtype != k.dtype or g.shape != q.shape \
+            or g.dtype != q.dtype:
+        raise ValueError("q and g must be [B, H, Nq, d] in k's dtype")
+    Nq = q.shape[2]
+    if T <= 0 or Nk % T or Nq % T or Nq > Nk:
+        raise ValueError("Nq and Nk must be multiples of T with Nq <= Nk")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((B, H, Nq, d), np.float64)
+    _load().gla_oracle_softmax_anchor(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), B, H,
+                                      Nq // T, Nk // T, T, d, int(bool(causal)), int(n_sink),
+                                      int(window), float(scale), int(nthreads))
+    return o
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -730,3 +730,77 @@ int gla_oracle_gdn(int dt, const void *q, const void *k, const void *v, const do
   }
   return used;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Gated softmax anchor: sink frames and a local temporal window             */
+/* ------------------------------------------------------------------------ */
+/*
+ * The SANA-Video 2.0 project page ("Hybrid Linear-Softmax Attention") puts a
+ * gated-softmax anchor in one layer of every four, to restore full-rank token
+ * interactions; the SANA-WM analysis page (deployment) gives the softmax
+ * layers attention-sink tokens and a local temporal window, so that their
+ * memory and per-chunk latency stay constant along the rollout. Neither page
+ * prints the formula. Reading taken (the gate as in the linear layers):
+ *
+ *   o_t = sigma(g_t) (.) sum_{s in V(t)} w_ts v_s
+ *   w_ts = exp(scale q_t.k_s) / sum_{s' in V(t)} exp(scale q_t.k_s')
+ *
+ * Keys and values are F frames of T tokens; queries (and g, o) are the tokens
+ * of the last Fq of those frames: query frame j is key frame f = F - Fq + j
+ * (a streaming call passes [kept frames | new frames] as keys and the new
+ * frames as queries). V(t) is every key in full mode; in frame-causal mode it
+ * is the tokens of key frames i with i <= f and (i < n_sink or i > f - window):
+ * the sink frames plus a window of `window` frames that ends with the query's
+ * own frame (window <= 0: unlimited). The query's own frame is always in V(t).
+ * scale is given by the caller (the usual choice is 1/sqrt(d)). The maximum
+ * score over V(t) is subtracted before exp, which leaves w unchanged.
+ * q, k, v, g in the input dtype, o float64; OpenMP over (slab, query frame).
+ */
+static int anchor_visible(int i, int f, int causal, int n_sink, int window) {
+  if (!causal) return 1;
+  if (i > f) return 0;
+  return i < n_sink || window <= 0 || i > f - window;
+}
+
+int gla_oracle_softmax_anchor(int dt, const void *q, const void *k, const void *v,
+                              const void *g, double *o, int B, int H, int Fq, int F, int T,
+                              int d, int causal, int n_sink, int window, double scale,
+                              int nthreads) {
+  const long nslab = (long)B * H;
+  const size_t Nq = (size_t)Fq * T, Nk = (size_t)F * T;
+  const int used = set_threads(nthreads);
+  const long tasks = nslab * Fq;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long task = 0; task < tasks; ++task) {
+    const long bh = task / Fq;
+    const int j = (int)(task % Fq), f = F - Fq + j;
+    double *w = (double *)malloc((Nk ? Nk : 1) * sizeof(double));
+    double *acc = (double *)malloc((size_t)d * sizeof(double));
+    for (int t = 0; t < T; ++t) {
+      const size_t qrow = ((size_t)bh * Nq + (size_t)j * T + t) * d;
+      double mx = -INFINITY;
+      for (size_t s = 0; s < Nk; ++s) {
+        if (!anchor_visible((int)(s / T), f, causal, n_sink, window)) continue;
+        const size_t krow = ((size_t)bh * Nk + s) * d;
+        double dot = 0.0;
+        for (int x = 0; x < d; ++x) dot += ld(q, dt, qrow + x) * ld(k, dt, krow + x);
+        w[s] = scale * dot;
+        if (w[s] > mx) mx = w[s];
+      }
+      double den = 0.0;
+      for (int x = 0; x < d; ++x) acc[x] = 0.0;
+      for (size_t s = 0; s < Nk; ++s) {
+        if (!anchor_visible((int)(s / T), f, causal, n_sink, window)) continue;
+        const double e = exp(w[s] - mx);
+        const size_t vrow = ((size_t)bh * Nk + s) * d;
+        den += e;
+        for (int x = 0; x < d; ++x) acc[x] += e * ld(v, dt, vrow + x);
+      }
+      for (int x = 0; x < d; ++x) o[qrow + x] = sigm(ld(g, dt, qrow + x)) * acc[x] / den;
+    }
+    free(w);
+    free(acc);
+  }
+  return used;
+}
