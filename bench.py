@@ -29,6 +29,8 @@ if ROOT not in sys.path:
 METRIC = "GLA fwd tokens/s at 720p/60s shape; % HBM/MFMA roofline vs CPU oracle"
 METRIC_BWD = "GLA bwd tokens/s at 720p/60s shape; % HBM/MFMA roofline vs CPU oracle"
 METRIC_GDN = "Gated DeltaNet fwd tokens/s at 720p/60s shape; % HBM roofline vs CPU oracle"
+METRIC_ANCHOR = ("Gated softmax anchor fwd tokens/s at 720p/60s shape (sink frames + local "
+                 "window); % bf16 MFMA roofline vs CPU oracle")
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 BF16_MFMA_PEAK = 2.5e15  # dense bf16 matrix-core peak, flop/s
 
@@ -47,9 +49,14 @@ def parse():
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="fwd: the forward call (the headline); bwd: the backward call "
                          "(gradients of the forward for a random dL/do)")
-    ap.add_argument("--mixer", default="gla", choices=["gla", "gdn"],
+    ap.add_argument("--mixer", default="gla", choices=["gla", "gdn", "anchor"],
                     help="gla: gated linear attention (the headline); gdn: the frame-wise "
-                         "Gated DeltaNet (beta = sigmoid of a normal draw per token)")
+                         "Gated DeltaNet (beta = sigmoid of a normal draw per token); anchor: "
+                         "the gated softmax anchor (frame-causal with --sink and --window, "
+                         "or over every key with --mode bidir)")
+    ap.add_argument("--sink", type=int, default=1, help="anchor: sink frames")
+    ap.add_argument("--window", type=int, default=4,
+                    help="anchor: frames in the local window, the query's own included")
     ap.add_argument("--rope", action="store_true",
                     help="fused 3D rotary positions over the latent grid (the *_ex entry points)")
     ap.add_argument("--cpu-heads", type=int, default=32,
@@ -175,6 +182,11 @@ def main():
         print("bench.py: the Gated DeltaNet runs frame-causal, forward, contiguous",
               file=sys.stderr)
         sys.exit(2)
+    anchor = args.mixer == "anchor"
+    if anchor and (bwd or ex or len(blocks) > 1):
+        print("bench.py: the anchor runs forward, contiguous, in one call (workloads 2-4)",
+              file=sys.stderr)
+        sys.exit(2)
     if gdn:
         gen = torch.Generator(device=dev)
         gen.manual_seed(w.seed * 1000 + 11)
@@ -237,7 +249,16 @@ def main():
             gla.gla_gdn_framecausal(b["q"], b["k"], b["v"], b["beta"], b["gamma"],
                                     S if carry else None, out=o, S_out=S, workspace=ws)
 
+    def step_anchor():
+        b = blocks[0]
+        gla.gla_softmax_anchor(b["q"], b["k"], b["v"], b["g"], T=w.T,
+                               causal=mode == "framecausal", n_sink=args.sink,
+                               window=args.window, out=outs[0])
+
     def step():
+        if anchor:
+            step_anchor()
+            return
         if gdn:
             step_gdn()
             return
@@ -300,6 +321,9 @@ def main():
                 "bwd_q": 5 * d * es, "bwd_k": 4 * d * es,
                 "gdn_kv": 2 * d * es + 4, "gdn_readout": 2 * d * es}
     token_heads = w.B * w.H * w.N
+    # anchor: 4 d flops per (query, visible key) pair (scores and P V)
+    pairs = anchor_pairs(w, mode == "framecausal", args.sink, args.window) if anchor else 0
+    anchor_flops = 4 * d * pairs * w.B * w.H
     kernels = {}
     for name, (n, total) in prof.items():
         avg_ms = total / n
@@ -308,18 +332,32 @@ def main():
         kernels[name] = {"avg_ms": round(avg_ms, 5), "launches_per_step": launches_per_call,
                          "alg_bytes_per_launch": int(alg),
                          "alg_GBps": round(alg / (avg_ms / 1e3) / 1e9, 1) if alg else 0.0}
+        if name == "anchor":
+            fl = anchor_flops / launches_per_call
+            kernels[name]["alg_flops_per_launch"] = int(fl)
+            kernels[name]["alg_TFLOPs"] = round(fl / (avg_ms / 1e3) / 1e12, 1)
     dom = max(prof, key=lambda k: prof[k][1])
     dk = kernels[dom]
     achieved = dk["alg_bytes_per_launch"] / (dk["avg_ms"] / 1e3)
     variant = w.name + "/" + mode + ("/fused" if args.layout == "fused" else "") + \
-        ("/rope" if args.rope else "") + ("/bwd" if bwd else "") + ("/gdn" if gdn else "")
+        ("/rope" if args.rope else "") + ("/bwd" if bwd else "") + ("/gdn" if gdn else "") + \
+        ("/anchor" if anchor else "")
     traffic_rec = committed_traffic(dom, variant)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                 "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
+    if anchor:  # a dense contraction: the bf16 matrix-core peak bounds it
+        fl = dk["alg_flops_per_launch"] / (dk["avg_ms"] / 1e3)
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(fl / 1e12, 1),
+                    "peak": BF16_MFMA_PEAK / 1e12, "unit": "TFLOP/s",
+                    "frac": round(fl / BF16_MFMA_PEAK, 4),
+                    "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
     # forward: read q, k, v, g, write o; backward: read q, k, v, g, dO, write dq,
     # dk, dv, dg (the recompute's second read of k and v is not counted)
-    if gdn:  # read q, k, v, beta, write o
+    if anchor:  # read q, k, v, g, write o (re-reads of k and v from cache not counted)
+        call_bytes = w.io_bytes()
+        flops = anchor_flops
+    elif gdn:  # read q, k, v, beta, write o
         call_bytes = w.io_bytes() * 4 // 5 + 4 * token_heads
         flops = 6 * d * d * token_heads  # U, A, readout
     else:
@@ -334,7 +372,9 @@ def main():
     cpu = None
     parity = None
     if not args.no_cpu and args.cpu_heads > 0:
-        if gdn:
+        if anchor:
+            cpu, parity = cpu_baseline_anchor(args, w, mode, blocks, outs, value)
+        elif gdn:
             cpu, parity = cpu_baseline_gdn(args, w, blocks, outs, value)
         elif bwd:
             cpu, parity = cpu_baseline_bwd(args, w, mode, blocks, grads, value)
@@ -343,7 +383,8 @@ def main():
                                        ropes[0].as_dict() if args.rope else None)
 
     line = {
-        "metric": METRIC_GDN if gdn else (METRIC_BWD if bwd else METRIC), "value": round(value, 1),
+        "metric": METRIC_ANCHOR if anchor else (METRIC_GDN if gdn else (
+            METRIC_BWD if bwd else METRIC)), "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -357,7 +398,12 @@ def main():
                    "pass": "backward (dq, dk, dv, dg, dgamma for a random dL/do)" if bwd
                    else "forward",
                    "mixer": ("frame-wise Gated DeltaNet (block delta rule per frame, key "
-                             "scale 1/sqrt(d T))" if gdn else "gated linear attention")},
+                             "scale 1/sqrt(d T))" if gdn else (
+                                 "gated softmax anchor (%s)" % (
+                                     "every key" if mode == "bidir" else
+                                     "%d sink frame(s), window of %d frames" % (
+                                         args.sink, args.window)) if anchor
+                                 else "gated linear attention"))},
         "roofline": roofline, "call": call, "kernels": kernels, "cpu_baseline": cpu,
         "parity": parity, "wall_s": round(wall, 3), "source_hash": source_hash(),
     }
@@ -421,6 +467,79 @@ def cpu_baseline(args, w, mode, blocks, outs, gpu_value, rope=None):
     rms = np.sqrt(np.mean(r2 * r2, axis=-1, keepdims=True))
     err = np.abs(o64.reshape(r2.shape) - r2) / np.maximum(np.maximum(np.abs(r2), rms), 1e-300)
     parity = {"heads": nh, "max_slab_rel_err": float(err.max()),
+              "bar": 1e-4 if w.dtype == "f32" else 2e-2}
+    return cpu, parity
+
+
+def anchor_visible_frames(F, f, causal, n_sink, window):
+    """Key frames query frame f sees (full mode: all F)."""
+    if not causal:
+        return F
+    lo = 0 if window <= 0 else max(0, f - window + 1)
+    return len(set(range(min(n_sink, f + 1))) | set(range(lo, f + 1)))
+
+
+def anchor_pairs(w, causal, n_sink, window):
+    """(query, visible key) pairs of one slab."""
+    return sum(w.T * w.T * anchor_visible_frames(w.F, f, causal, n_sink, window)
+               for f in range(w.F))
+
+
+def cpu_baseline_anchor(args, w, mode, blocks, outs, gpu_value):
+    """Time oracle.softmax_anchor on a bounded sample -- a few heads, the last
+    query frames (each a streaming call over the frames up to it; full mode:
+    one frame of queries over every key) -- and check o there."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    causal = mode == "framecausal"
+    nh = min(args.cpu_heads, 4, w.B * w.H)
+    nf = min(w.F, 4 if causal else 1)
+    heads = [(i // w.H, i % w.H) for i in range(nh)]
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.contiguous().cpu().numpy()
+
+    def sel(t, rows):
+        return np.concatenate([host(t[b:b + 1, h:h + 1, rows]) for (b, h) in heads], axis=1)
+
+    b0, T = blocks[0], w.T
+    frames = list(range(w.F - nf, w.F))
+    threads = min(oracle.max_threads(), nh)
+    print("bench: CPU anchor oracle on %d heads x %d query frames, %d threads" % (nh, nf, threads),
+          file=sys.stderr, flush=True)
+    el, pairs, worst = 0.0, 0, 0.0
+    for f in frames:
+        q_rows = slice(f * T, (f + 1) * T)
+        k_rows = slice(0, (f + 1) * T) if causal else slice(0, w.F * T)
+        q, g = sel(b0["q"], q_rows), sel(b0["g"], q_rows)
+        k, v = sel(b0["k"], k_rows), sel(b0["v"], k_rows)
+        t0 = time.perf_counter()
+        ref = oracle.softmax_anchor(q, k, v, g, T=T, causal=causal, n_sink=args.sink,
+                                    window=args.window)
+        el += time.perf_counter() - t0
+        pairs += T * T * anchor_visible_frames(w.F, f, causal, args.sink, args.window)
+        got = sel(outs[0], q_rows)
+        o64 = oracle.bf16_to_f64(got) if got.dtype == np.uint16 else got.astype(np.float64)
+        r2 = ref.reshape(1, nh, -1)
+        rms = np.sqrt(np.mean(r2 * r2, axis=-1, keepdims=True))
+        err = np.abs(o64.reshape(r2.shape) - r2) / np.maximum(np.maximum(np.abs(r2), rms), 1e-300)
+        worst = max(worst, float(err.max()))
+    # scaled by work: the whole call's (query, key) pairs over the sample's
+    total_pairs = anchor_pairs(w, causal, args.sink, args.window) * w.B * w.H
+    call_s = el * total_pairs / (pairs * nh)
+    cpu_tokens_per_s = w.B * w.N / call_s
+    cpu = {"value": round(cpu_tokens_per_s, 1), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": "%d of %d heads x the last %d query frames (%d tokens each), fp64 softmax "
+                     "anchor oracle, %.1f s; scaled to the call by (query, key) pairs"
+                     % (nh, w.B * w.H, nf, T, el),
+           "host_cpu": host_cpu_model(), "gpu_over_cpu": round(gpu_value / cpu_tokens_per_s, 1)}
+    parity = {"heads": nh, "frames": frames, "max_slab_rel_err": worst,
               "bar": 1e-4 if w.dtype == "f32" else 2e-2}
     return cpu, parity
 

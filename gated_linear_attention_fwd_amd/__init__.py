@@ -43,7 +43,7 @@ __all__ = [
     "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace", "gla_state_carry_workspace",
     "gla_fwd_bidir_ex_workspace", "gla_bwd_framecausal", "gla_bwd_bidir",
     "gla_bwd_framecausal_workspace", "gla_bwd_bidir_workspace", "gla_gdn_framecausal",
-    "gla_gdn_framecausal_workspace", "library_path", "load_library",
+    "gla_gdn_framecausal_workspace", "gla_softmax_anchor", "library_path", "load_library",
     "profile_begin", "profile_end",
 ]
 
@@ -152,6 +152,8 @@ def load_library():
     lib.gla_gdn_framecausal_workspace.restype = sz
     lib.gla_gdn_framecausal.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp, sz, vp]
     lib.gla_gdn_framecausal.restype = i32
+    lib.gla_softmax_anchor.argtypes = [vp] * 5 + [i32] * 10 + [f32, vp]
+    lib.gla_softmax_anchor.restype = i32
     lib.gla_status_string.argtypes = [i32]
     lib.gla_status_string.restype = ctypes.c_char_p
     lib.gla_last_error.argtypes = []
@@ -567,6 +569,36 @@ def gla_gdn_framecausal(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Ten
     if q is None:
         return S_out
     return (o, S_out) if want_state else o
+
+
+def gla_softmax_anchor(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                       T: int, causal: bool = True, n_sink: int = 0, window: int = 0,
+                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Gated softmax attention over whole frames: o = sigmoid(g) * softmax(scale q k^T) v.
+
+    k, v [B, H, F*T, d]; q, g [B, H, Fq*T, d], the tokens of the last Fq key
+    frames. causal False: every key visible. causal True: query frame f sees
+    key frames i <= f with i < n_sink or i > f - window (window <= 0: no
+    limit). scale defaults to 1/sqrt(d)."""
+    lib = load_library()
+    if k.dim() != 4 or v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must be [B, H, F*T, d] of one dtype")
+    if q.dim() != 4 or g.shape != q.shape or q.dtype != k.dtype or g.dtype != k.dtype \
+            or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q and g must be [B, H, Fq*T, d] in k's dtype")
+    B, H, Nk, d = k.shape
+    Nq = q.shape[2]
+    if T <= 0 or Nk % T or Nq % T or Nq > Nk:
+        raise ValueError("Nq=%d and Nk=%d must be multiples of T=%d with Nq <= Nk" % (Nq, Nk, T))
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    o = torch.empty_like(q) if out is None else out
+    dev = _require_device(q, k, v, g, o)
+    _check(lib.gla_softmax_anchor(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), B, H, Nq // T,
+                                  Nk // T, T, d, _dtype_code(k), int(bool(causal)), int(n_sink),
+                                  int(window), float(scale), _stream_handle(stream, dev)))
+    return o
 
 
 def profile_begin(max_launches: int = 4096) -> None:

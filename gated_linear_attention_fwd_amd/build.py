@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgla.so")
 ARCH = "gfx950"
 
-SOURCES = ["gla_api.cpp", "carry.hip", "valu.hip", "mfma.hip", "bwd.hip", "bwd_mfma.hip", "gdn.hip", "gdn_mfma.hip"]
+SOURCES = ["gla_api.cpp", "anchor.hip", "carry.hip", "valu.hip", "mfma.hip", "bwd.hip", "bwd_mfma.hip", "gdn.hip", "gdn_mfma.hip"]
 
 # Packed fp32 arithmetic is switched off for the device code (the compiler then
 # emits plain v_fma_f32 / v_add_f32 / v_mul_f32).

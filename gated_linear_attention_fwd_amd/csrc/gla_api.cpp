@@ -140,11 +140,12 @@ enum Kind {
   kKindGdnKv = 7,
   kKindGdnScan = 8,
   kKindGdnReadout = 9,
-  kNumKinds = 10
+  kKindAnchor = 10,
+  kNumKinds = 11
 };
 const char *const kKindNames[kNumKinds] = {"kv",     "carry",  "readout",  "bwd_q",
                                            "rev_scan", "bwd_k", "dgamma", "gdn_kv",
-                                           "gdn_scan", "gdn_readout"};
+                                           "gdn_scan", "gdn_readout", "anchor"};
 
 struct Profiler {
   std::mutex mu;
@@ -578,6 +579,41 @@ gla_status run_gdn(const void *q, const void *k, const void *v, const float *bet
   return GLA_OK;
 }
 
+// The body of gla_softmax_anchor (contiguous tensors; no workspace).
+gla_status run_anchor(const void *q, const void *k, const void *v, const void *g, void *o, int B,
+                      int H, int Fq, int F, int T, int d, gla_dtype dt, int causal, int n_sink,
+                      int window, float scale, void *stream) {
+  GLA_TRY(check_dims(B, H, d, dt));
+  if (F < 0 || Fq < 0 || T < 0 || Fq > F)
+    return fail(GLA_ERR_SHAPE, "need 0 <= Fq <= F and T >= 0 (Fq=%d F=%d T=%d)", Fq, F, T);
+  if (causal != 0 && causal != 1) return fail(GLA_ERR_VALUE, "causal=%d must be 0 or 1", causal);
+  if (n_sink < 0) return fail(GLA_ERR_VALUE, "n_sink=%d must be >= 0", n_sink);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(GLA_ERR_VALUE, "scale=%g must be finite and > 0", (double)scale);
+  const int64_t BH = (int64_t)B * H;
+  const int64_t Nq = (int64_t)Fq * T, Nk = (int64_t)F * T;
+  if (BH == 0 || Nq == 0) return GLA_OK;
+  if (!q || !k || !v || !g || !o) return fail(GLA_ERR_NULL, "q, k, v, g and o are required");
+  const void *tens[] = {q, k, v, g, o};
+  const char *tn[] = {"q", "k", "v", "g", "o"};
+  for (int i = 0; i < 5; ++i) GLA_TRY(check_tensor_align(tens[i], tn[i]));
+  if (Nk > (int64_t(1) << 62) / BH / d) return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
+  const size_t es = dt == GLA_F32 ? 4 : 2;
+  const size_t qb = (size_t)(BH * Nq * d) * es, kb = (size_t)(BH * Nk * d) * es;
+  const Range ins[] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {g, qb, "g"}};
+  const Range out{o, qb, "o"};
+  for (const Range &r : ins)
+    if (overlap(out, r)) return fail(GLA_ERR_ALIAS, "o overlaps %s", r.name);
+  const Path path = select_path(dt, d);
+  const AnchorArgs a{q, k, v, g, o, BH, Fq, F, T, d, causal, n_sink, window, scale};
+  if (anchor_tiles(a, path) >= (int64_t(1) << 31))
+    return fail(GLA_ERR_SHAPE, "sizes overflow the grid");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GLA_TRY(launched(timed(kKindAnchor, s, [&] { return launch_anchor(a, dt, path, s); }),
+                   "anchor"));
+  return GLA_OK;
+}
+
 }  // namespace
 
 bool make_gdn_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
@@ -842,6 +878,13 @@ GLA_EXPORT gla_status gla_gdn_framecausal(const void *q, const void *k, const vo
                  ws_bytes, stream);
 }
 
+GLA_EXPORT gla_status gla_softmax_anchor(const void *q, const void *k, const void *v,
+                                         const void *g, void *o, int B, int H, int Fq, int F,
+                                         int T, int d, gla_dtype dt, int causal, int n_sink,
+                                         int window, float scale, void *stream) {
+  return run_anchor(q, k, v, g, o, B, H, Fq, F, T, d, dt, causal, n_sink, window, scale, stream);
+}
+
 GLA_EXPORT const char *gla_status_string(gla_status s) {
   switch (s) {
     case GLA_OK: return "ok";
@@ -859,7 +902,7 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
 
 GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
 
-GLA_EXPORT int gla_version(void) { return 10100; }
+GLA_EXPORT int gla_version(void) { return 10200; }
 
 GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
   if (max_launches < 1 || max_launches > 65536)

@@ -222,6 +222,23 @@ hipError_t launch_gdn_scan(const Plan &p, Path path, const GdnScanArgs &a, hipSt
 hipError_t launch_gdn_readout(const Plan &p, int dtype, Path path, const GdnReadoutArgs &a,
                               hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Gated softmax anchor (no workspace): k, v [BH][F*T][d]; q, g, o [BH][Fq*T][d],
+// the tokens of the last Fq key frames. causal = 0: every key visible; 1: key
+// frames i <= f with i < n_sink or i > f - window (window <= 0: unlimited).
+// ---------------------------------------------------------------------------
+struct AnchorArgs {
+  const void *q, *k, *v, *g;
+  void *o;
+  int64_t BH;
+  int Fq, F, T, d;
+  int causal, n_sink, window;
+  float scale;
+};
+
+int64_t anchor_tiles(const AnchorArgs &a, Path path);  // workgroups of one launch
+hipError_t launch_anchor(const AnchorArgs &a, int dtype, Path path, hipStream_t s);
+
 hipError_t launch_kv(const Plan &p, int dtype, Path path, const KvArgs &a, hipStream_t s);
 hipError_t launch_carry(const Plan &p, const CarryArgs &a, hipStream_t s);
 hipError_t launch_readout(const Plan &p, int dtype, Path path, const ReadoutArgs &a,

@@ -161,6 +161,30 @@ gla_status gla_gdn_framecausal(const void *q, const void *k, const void *v, cons
                                int B, int H, int F, int T, int d, gla_dtype dt, float key_scale,
                                void *ws, size_t ws_bytes, void *stream);
 
+/* ---- gated softmax anchor ------------------------------------------------------
+ *
+ * The layer the linear mixers alternate with. The SANA-Video 2.0 project page
+ * ("Hybrid Linear-Softmax Attention") places a gated-softmax anchor in one
+ * layer of every four, to restore full-rank token interactions; the SANA-WM
+ * analysis page (deployment) gives the softmax layers attention-sink tokens
+ * and a local temporal window, so that their memory and per-chunk latency stay
+ * constant along a rollout. Neither page prints a formula. This library
+ * computes, with whole frames visible and the gate of the linear layers,
+ *   o_t = sigmoid(g_t) (.) sum_{s in V(t)} softmax_s(scale q_t . k_s) v_s
+ * k, v: [B][H][F*T][d], F frames of T tokens. q, g, o: [B][H][Fq*T][d], the
+ * tokens of the last Fq <= F key frames: query frame j is key frame
+ * f = F - Fq + j (a streaming call passes [kept frames | new frames] as keys
+ * and the new frames as queries). causal = 0: V(t) is every key. causal = 1:
+ * V(t) is the key frames i <= f with i < n_sink (the sink frames) or
+ * i > f - window (the local window, which ends with the query's own frame;
+ * window <= 0: no limit). scale must be finite and > 0 (1/sqrt(d) is the
+ * usual choice); n_sink >= 0. GLA_F32 or GLA_BF16 (o rounded to nearest even),
+ * softmax and sums in fp32. No workspace. o may overlap no input
+ * (GLA_ERR_ALIAS). Conventions otherwise as above. */
+gla_status gla_softmax_anchor(const void *q, const void *k, const void *v, const void *g, void *o,
+                              int B, int H, int Fq, int F, int T, int d, gla_dtype dt, int causal,
+                              int n_sink, int window, float scale, void *stream);
+
 /* ---- strided tensors and fused 3D rotary positions ------------------------
  *
  * The *_ex entry points compute the same operation as the plain ones, with
@@ -255,7 +279,7 @@ const char *gla_status_string(gla_status s);
 const char *gla_last_error(void);
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
-int gla_version(void); /* 10100: adds the *_ex entry points */
+int gla_version(void); /* 10200: adds gla_softmax_anchor (10100: the *_ex entry points) */
 
 /* ---- kernel timing for measurement tools ---------------------------------
  * Between gla_profile_begin and gla_profile_end, every kernel launched by the
@@ -264,7 +288,8 @@ int gla_version(void); /* 10100: adds the *_ex entry points */
  * returns, per kernel kind ("kv", "carry", "readout", and for the backward
  * "bwd_q", "rev_scan", "bwd_k", "dgamma", and for the Gated DeltaNet "gdn_kv",
  * "gdn_scan", "gdn_readout"; "gdn_scan" includes the summing of a frame's parts
- * where the frame is split over several workgroups), the number of launches
+ * where the frame is split over several workgroups; and "anchor"), the number
+ * of launches
  * and their summed event time. At most max_launches launches are timed; later
  * ones run untimed. Not meant to overlap with itself: one session at a time.
  * gla_profile_begin creates 2 * max_launches HIP events (max_launches must be

@@ -51,7 +51,7 @@ def test_status_strings(lib):
     for s in range(9):
         assert lib.gla_status_string(s).decode()
     assert lib.gla_status_string(99).decode() == "unknown status"
-    assert lib.gla_version() == 10100
+    assert lib.gla_version() == 10200
 
 
 def test_workspace_sizes(lib):
@@ -225,3 +225,34 @@ def test_ex_workspace(lib):
     # without them the sequence is one frame of F * T tokens
     assert gla.gla_fwd_bidir_ex_workspace(1, 32, 21, 920, 64) == \
         gla.gla_fwd_bidir_workspace(1, 32, 21 * 920, 64)
+
+
+def test_anchor_validation(lib):
+    """gla_softmax_anchor rejects bad arguments before any launch; empty
+    problems return OK without touching the device."""
+    f = lib.gla_softmax_anchor
+    A = FAKE
+    B = FAKE + 0x100000  # a second, disjoint aligned address
+
+    def call(q=A, k=B, v=B + 0x100000, g=B + 0x200000, o=B + 0x300000, Bn=1, H=2, Fq=2, F=3,
+             T=8, d=64, dt=BF16, causal=1, n_sink=1, window=2, scale=0.125):
+        return f(p(q), p(k), p(v), p(g), p(o), Bn, H, Fq, F, T, d, dt, causal, n_sink, window,
+                 ctypes.c_float(scale), None)
+
+    assert call(d=48) == UNSUP
+    assert call(dt=7) == UNSUP
+    assert call(Fq=4) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert call(causal=2) == VALUE
+    assert call(n_sink=-1) == VALUE
+    assert call(scale=0.0) == VALUE
+    assert call(scale=float("nan")) == VALUE
+    assert call(q=0) == NULL
+    assert call(o=0) == NULL
+    assert call(q=A + 8) == ALIGN
+    assert call(o=A) == ALIAS         # o is q
+    assert call(o=B + 64) == ALIAS    # o inside k
+    # nothing to do: no query tokens, or no heads
+    assert call(Fq=0, q=0, g=0, o=0) == OK
+    assert call(T=0, q=0, k=0, v=0, g=0, o=0) == OK
+    assert call(Bn=0) == OK

@@ -1,0 +1,150 @@
+"""GPU parity of the gated softmax anchor (gla_softmax_anchor, through the C
+ABI) against the fp64 oracle (oracle.softmax_anchor, pinned in
+test_oracle_anchor.py).
+
+Bar: slab-normalised error (gla_testutil.slab_rel_err) of o at most 1e-4 for
+float32 inputs and 2e-2 for bfloat16 inputs (fp32 softmax and sums; the
+matrix-core path rounds the probabilities to bf16 for the P V product).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gated_linear_attention_fwd_amd as gla
+import oracle
+from gated_linear_attention_fwd_amd import synth
+from gla_testutil import TOL, slab_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gla.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(params=["auto", "valu"])
+def path(request, monkeypatch):
+    if request.param == "valu":
+        monkeypatch.setenv("GLA_PATH", "valu")
+    else:
+        monkeypatch.delenv("GLA_PATH", raising=False)
+    return request.param
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    h = host(t)
+    return oracle.bf16_to_f64(h) if h.dtype == np.uint16 else h.astype(np.float64)
+
+
+def inputs(B, H, Fq, F, T, d, dtype, seed, qk_scale=1.0):
+    rng = np.random.default_rng(seed)
+    cast = synth.bf16_bits if dtype == "bf16" else (lambda a: a)
+    q = cast((qk_scale * rng.standard_normal((B, H, Fq * T, d))).astype(np.float32))
+    k = cast((qk_scale * rng.standard_normal((B, H, F * T, d))).astype(np.float32))
+    v = cast(rng.standard_normal((B, H, F * T, d)).astype(np.float32))
+    g = cast(rng.standard_normal((B, H, Fq * T, d)).astype(np.float32))
+    return q, k, v, g
+
+
+def report(name, e):
+    print(name, "o=%.3e" % e, flush=True)
+
+
+CASES = [
+    # (dtype, B, H, d, Fq, F, T, causal, n_sink, window)
+    ("f32", 1, 2, 16, 4, 4, 8, 1, 1, 2),
+    ("f32", 1, 2, 32, 3, 3, 20, 0, 0, 0),
+    ("f32", 1, 1, 64, 2, 5, 33, 1, 1, 2),
+    ("bf16", 1, 2, 64, 5, 5, 300, 1, 1, 2),    # 3 query tiles per frame, ragged key blocks
+    ("bf16", 1, 2, 64, 1, 1, 700, 0, 0, 0),    # full mode, one segment of 700 queries
+    ("bf16", 1, 2, 128, 2, 6, 150, 1, 2, 3),   # streaming: the last 2 of 6 frames
+    ("bf16", 2, 1, 32, 3, 3, 97, 1, 0, 0),     # no sinks, no window limit
+    ("bf16", 1, 2, 16, 3, 3, 40, 1, 1, 1),
+    ("bf16", 1, 1, 64, 6, 6, 64, 1, 4, 1),     # sinks reach past the window
+    ("bf16", 1, 1, 128, 3, 3, 1, 1, 0, 2),     # one token per frame
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-B%dH%d-d%d-Fq%dF%dT%d-c%d-s%d-w%d" % c)
+def test_anchor(case, path):
+    dtype, B, H, d, Fq, F, T, causal, n_sink, window = case
+    q, k, v, g = inputs(B, H, Fq, F, T, d, dtype, seed=700 + d + T)
+    o = gla.gla_softmax_anchor(dev(q), dev(k), dev(v), dev(g), T=T, causal=bool(causal),
+                               n_sink=n_sink, window=window)
+    ref = oracle.softmax_anchor(q, k, v, g, T=T, causal=bool(causal), n_sink=n_sink,
+                               window=window)
+    e = slab_rel_err(f64(o), ref)
+    report("anchor %s %s" % (case, path), e)
+    assert e <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64), ("bf16", 128)])
+def test_anchor_peaked_scores(dtype, d):
+    """scale = 1 with unit-variance q, k: scores of standard deviation sqrt(d),
+    nearly one-hot softmax (exercises the running-max rescaling)."""
+    q, k, v, g = inputs(1, 2, 4, 4, 70, d, dtype, seed=5)
+    o = gla.gla_softmax_anchor(dev(q), dev(k), dev(v), dev(g), T=70, n_sink=1, window=2,
+                               scale=1.0)
+    ref = oracle.softmax_anchor(q, k, v, g, T=70, n_sink=1, window=2, scale=1.0)
+    e = slab_rel_err(f64(o), ref)
+    report("anchor peaked %s d=%d" % (dtype, d), e)
+    assert e <= TOL[dtype]
+
+
+def test_anchor_streaming_equals_one_call():
+    """The last frames as queries over [all frames] give the same rows as the
+    call with every frame as queries, bit for bit (one tile never spans frames)."""
+    q, k, v, g = inputs(1, 2, 6, 6, 200, 64, "bf16", seed=6)
+    t = {n: dev(x) for n, x in zip("qkvg", (q, k, v, g))}
+    full = gla.gla_softmax_anchor(t["q"], t["k"], t["v"], t["g"], T=200, n_sink=1, window=3)
+    last = gla.gla_softmax_anchor(t["q"][:, :, 800:].contiguous(), t["k"], t["v"],
+                                  t["g"][:, :, 800:].contiguous(), T=200, n_sink=1, window=3)
+    assert torch.equal(last, full[:, :, 800:])
+
+
+def test_anchor_deterministic():
+    q, k, v, g = inputs(1, 2, 3, 3, 500, 64, "bf16", seed=7)
+    args = [dev(x) for x in (q, k, v, g)]
+    a = gla.gla_softmax_anchor(*args, T=500, causal=False)
+    b = gla.gla_softmax_anchor(*args, T=500, causal=False)
+    assert torch.equal(a, b)
+
+
+def test_anchor_720p_60s_sampled_frames():
+    """The 720p/60s streaming shape (B=1, H=32, d=64, 241 frames of 920 tokens,
+    bf16, one sink frame, a window of 4 frames): three query frames of two heads
+    against the oracle, each as a streaming call over the frames up to it."""
+    w = synth.WORKLOADS[4]
+    xd = synth.device_inputs(w, DEV)
+    o = gla.gla_softmax_anchor(xd["q"], xd["k"], xd["v"], xd["g"], T=w.T, n_sink=1, window=4)
+    torch.cuda.synchronize()
+    T = w.T
+    for h in (0, 19):
+        for f in (0, 3, 240):
+            rows = slice(f * T, (f + 1) * T)
+            sel = lambda t, s: host(t[:, h:h + 1, s])  # noqa: E731
+            ref = oracle.softmax_anchor(sel(xd["q"], rows), sel(xd["k"], slice(0, (f + 1) * T)),
+                                        sel(xd["v"], slice(0, (f + 1) * T)), sel(xd["g"], rows),
+                                        T=T, n_sink=1, window=4)
+            e = slab_rel_err(f64(o[:, h:h + 1, rows]), ref)
+            report("anchor 720p/60s head %d frame %d" % (h, f), e)
+            assert e <= TOL["bf16"]
