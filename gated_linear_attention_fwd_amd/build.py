@@ -26,6 +26,13 @@ SOURCES = ["gla_api.cpp", "anchor.hip", "carry.hip", "valu.hip", "mfma.hip", "bw
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
           "--offload-arch=" + ARCH, "-I" + os.path.join(ROOT, "include")]
+# Per-source additions. The softmax kernels run with the IEEE mode bit off and
+# no NaN handling (their inputs are finite by precondition): the running max is
+# then a single v_max_f32 per score instead of two (NaN canonicalisation), and
+# the MFMA accumulators, which the softmax reads and rescales every block, stay
+# in ordinary VGPRs rather than moving through AGPRs.
+EXTRA_FLAGS = {"anchor.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans",
+                              "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -37,7 +44,8 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compiling %s failed:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

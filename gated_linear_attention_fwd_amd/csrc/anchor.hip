@@ -26,6 +26,8 @@
 //
 // Vector-ALU kernel (fp32 inputs, other d, or forced): one query per thread,
 // blocks of 32 keys through LDS.
+#include <type_traits>
+
 #include "common.hpp"
 #include "mfma_util.hpp"
 #include "plan.hpp"
@@ -181,36 +183,55 @@ __global__ __launch_bounds__(256) void anchor_mfma_kernel(AnchorArgs a, int tile
         s[kb] = mfma_32x32x16(kf, qf[kk], s[kb]);
       }
     }
-    // online softmax over the block (keys past nv are not there)
-    float mx = -1e30f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (key < nv) mx = fmaxf(mx, s[kb][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * cl2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
+    // online softmax over the block (keys past nv are not there; only the
+    // last block of a range is partial)
     uint32_t pw[2][8];  // probabilities as packed bf16 pairs, per 32-key block
+    auto softmax = [&](auto masked) {
+      constexpr bool kMasked = decltype(masked)::value;
+      float mx = -1e30f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float p0 = key < nv ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], cl2, -m_new)) : 0.f;
-        const float p1 = key + 1 < nv ? __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], cl2, -m_new)) : 0.f;
-        psum += p0 + p1;
-        pw[kb][r >> 1] = pack_bf16x2(p0, p1);
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (!kMasked || key < nv) mx = fmaxf(mx, s[kb][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * cl2;
+      // Lazy rescaling: the reference m_run moves (and O, l are rescaled)
+      // only when some query's maximum exceeds it by more than 8 (a factor
+      // 256): the probabilities stay below 2^8 and O, l keep one reference,
+      // so the result is unchanged.
+      if (__builtin_amdgcn_read_exec() & __ballot(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int jb = 0; jb < C::JB; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[jb][r] *= alpha;
       }
-    l_run = fmaf(l_run, alpha, psum);
+      float psum = 0.f;
 #pragma unroll
-    for (int jb = 0; jb < C::JB; ++jb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[jb][r] *= alpha;
+        for (int r = 0; r < 16; r += 2) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cl2, -m_run));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], cl2, -m_run));
+          if (kMasked) {
+            p0 = key < nv ? p0 : 0.f;
+            p1 = key + 1 < nv ? p1 : 0.f;
+          }
+          psum += p0 + p1;
+          pw[kb][r >> 1] = pack_bf16x2(p0, p1);
+        }
+      l_run += psum;
+    };
+    if (nv == C::BN)
+      softmax(std::false_type{});
+    else
+      softmax(std::true_type{});
 
     // O^T += V^T P^T over the block's 4 k-steps of 16 keys
 #pragma unroll
