@@ -67,23 +67,43 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash() -> str:
+# The sources each family's kernels are built from (besides the shared headers,
+# the API file and the build flags): a counter record stays valid while these
+# are unchanged.
+KERNEL_SOURCES = {
+    "gla": ["mfma.hip", "valu.hip", "carry.hip"],
+    "bwd": ["bwd.hip", "bwd_mfma.hip", "mfma.hip", "valu.hip", "carry.hip"],
+    "gdn": ["gdn.hip", "gdn_mfma.hip"],
+    "anchor": ["anchor.hip"],
+}
+SHARED_SOURCES = ["common.hpp", "mfma_util.hpp", "plan.hpp", "gla_api.cpp"]
+
+
+def source_hash(family=None) -> str:
+    """Hash of the kernel sources (all of them, or one family's with the shared
+    files and the build script)."""
+    csrc = os.path.join(ROOT, "gated_linear_attention_fwd_amd", "csrc")
+    if family is None:
+        paths = sorted(glob.glob(os.path.join(csrc, "*")))
+    else:
+        paths = [os.path.join(csrc, n) for n in sorted(SHARED_SOURCES + KERNEL_SOURCES[family])]
+        paths.append(os.path.join(ROOT, "gated_linear_attention_fwd_amd", "build.py"))
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "gated_linear_attention_fwd_amd", "csrc", "*"))):
+    for p in paths:
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel: str, workload: str):
+def committed_traffic(kernel: str, workload: str, family: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the current sources of the kernel's family; else None."""
     for p in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
         txt = open(p).read()
         for m in re.finditer(r"<!-- traffic (\{.*?\}) -->", txt):
             rec = json.loads(m.group(1))
             if (rec.get("kernel") == kernel and rec.get("workload") == workload
-                    and rec.get("source_hash") == source_hash()):
+                    and rec.get("source_hash") == source_hash(family)):
                 return rec
     return None
 
@@ -342,7 +362,8 @@ def main():
     variant = w.name + "/" + mode + ("/fused" if args.layout == "fused" else "") + \
         ("/rope" if args.rope else "") + ("/bwd" if bwd else "") + ("/gdn" if gdn else "") + \
         ("/anchor" if anchor else "")
-    traffic_rec = committed_traffic(dom, variant)
+    family = "anchor" if anchor else ("gdn" if gdn else ("bwd" if bwd else "gla"))
+    traffic_rec = committed_traffic(dom, variant, family)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                 "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
@@ -406,6 +427,7 @@ def main():
                                  else "gated linear attention"))},
         "roofline": roofline, "call": call, "kernels": kernels, "cpu_baseline": cpu,
         "parity": parity, "wall_s": round(wall, 3), "source_hash": source_hash(),
+        "kernel_family": family, "family_source_hash": source_hash(family),
     }
     print(json.dumps(line), flush=True)
 
