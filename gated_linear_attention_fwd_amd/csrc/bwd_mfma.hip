@@ -201,7 +201,11 @@ struct BqCfg {
   // d <= 64: G accumulates in LDS (fp32, one image per k-step split), which
   // keeps its registers free between blocks; d = 128 keeps 4 blocks in registers
   static constexpr bool kGInLds = D <= 64;
-  static constexpr int GL_FLOATS = kGInLds ? KSPLIT * D * D : 1;
+  // image rows padded by 4 floats: the 32 lanes of a half-wave update 32
+  // consecutive rows n at one column, which an unpadded D-float stride would
+  // put on the same 4 banks
+  static constexpr int GLP = D + 4;
+  static constexpr int GL_FLOATS = kGInLds ? KSPLIT * D * GLP : 1;
 };
 
 template <int D>
@@ -466,11 +470,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
         }
         if constexpr (C::kGInLds) {
           // add into this wave's image (rows m = 8(e/4) + 4h + e%4 of column n)
-          float *img = gl + (C::KSPLIT > 1 ? rw % C::KSPLIT : 0) * D * D;
+          float *img = gl + (C::KSPLIT > 1 ? rw % C::KSPLIT : 0) * D * C::GLP;
           const int n = 32 * bj + (lane & 31);
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
-            float4 *cell = reinterpret_cast<float4 *>(img + n * D + 32 * bi + 8 * e4 + 4 * h);
+            float4 *cell = reinterpret_cast<float4 *>(img + n * C::GLP + 32 * bi + 8 * e4 + 4 * h);
             float4 v = *cell;
             v.x += blk_acc[4 * e4];
             v.y += blk_acc[4 * e4 + 1];
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       const int m = e / D, n = e % D;
       float sum = 0.f;
 #pragma unroll
-      for (int im = 0; im < C::KSPLIT; ++im) sum += gl[im * D * D + n * D + m];
+      for (int im = 0; im < C::KSPLIT; ++im) sum += gl[(im * D + n) * C::GLP + m];
       out[e] = sum;
     }
   }
