@@ -349,30 +349,76 @@ __device__ __forceinline__ int scan_perm(int col) {
   return (col & ~31) + 8 * ((c32 & 15) >> 2) + 4 * (c32 >> 4) + (c32 & 3);
 }
 
-template <int D>
+// The scan runs in one of four modes, each a sequence of steps
+//   X <- g0 X + g1 (A X) + g2 U     (A d x d; X, U d x ncols)
+// with X kept in registers as above:
+//   kWhole:    one pass over the F frames of a slab: A = A_f, U = U_f,
+//              (g0, g1, g2) = (gamma_f, -gamma_f c^2, c); S_f stored after each step.
+//   kTransfer: per chunk of frames, from [0 | I] on d x 2d columns: the chunk's
+//              local end state (left d columns) and its transfer matrix
+//              M = prod_f gamma_f (I - c^2 A_f) (right d columns, U = 0).
+//   kChain:    per slab, over the chunks in order: A = M_c, U = L_c (the local
+//              end state), (g0, g1, g2) = (0, 1, 1); X before each step is the
+//              chunk's start state.
+//   kApply:    per chunk, kWhole's steps from the chunk's start state.
+// The chunked form cuts the chain of dependent steps from F to about
+// 2 Fc + F / Fc; the products are the same matrix-core steps.
+enum ScanMode { kWhole = 0, kTransfer = 1, kChain = 2, kApply = 3 };
+
+template <int D, int kMode>
+struct ScanJob {
+  static constexpr int AHEAD = kMode == kWhole ? GsCfg<D>::AHEAD : 1;
+  static constexpr int COLS = kMode == kTransfer ? 2 * D : D;
+  static constexpr int NWG = COLS / (16 * GsCfg<D>::NW);  // workgroups per item
+};
+
+template <int D, int kMode>
 __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
     float *__restrict__ ws, const float *__restrict__ gamma, const float *S_in, float *S_out,
-    int F, int P, float key_scale) {
+    int F, int P, float key_scale, int Fc, int nc, float *__restrict__ tws,
+    float *__restrict__ sws) {
   using C = GsCfg<D>;
+  using J = ScanJob<D, kMode>;
   __shared__ __attribute__((aligned(16))) char planes[2 * D * C::PITCH];  // hi, then lo
   constexpr int64_t SLOT = 2 * (int64_t)D * D;
+  constexpr int64_t DD = (int64_t)D * D;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
-  const int64_t bh = blockIdx.x / C::NWG;
-  const int col = 16 * ((int)(blockIdx.x % C::NWG) * C::NW + wave) + n;  // the lane's column
+  const int cb = (int)(blockIdx.x % J::NWG);
+  const int64_t item = blockIdx.x / J::NWG;
+  const bool per_chunk = kMode == kTransfer || kMode == kApply;
+  const int64_t bh = per_chunk ? item / nc : item;
+  const int chunk = per_chunk ? (int)(item % nc) : 0;
+  const int f0 = per_chunk ? chunk * Fc : 0;
+  const int nsteps = kMode == kChain ? nc : (per_chunk ? min(Fc, F - f0) : F);
+  const int cx = 16 * (cb * C::NW + wave) + n;  // the lane's column of X (< COLS)
+  const bool right = kMode == kTransfer && cx >= D;  // a column of the transfer matrix
+  const int col = cx % D;                            // its column within a d x d matrix
   const float c1 = key_scale, c2 = key_scale * key_scale;
   float *slab = ws + bh * (int64_t)F * P * SLOT;  // part 0 of each frame holds the whole sums
+  float *tw = tws + bh * (int64_t)nc * 2 * DD;    // per chunk: L_c, then M_c
+  float *sw = sws + bh * (int64_t)nc * DD;        // per chunk: its start state
 
   f32x4 s[C::RB];
 #pragma unroll
   for (int ib = 0; ib < C::RB; ++ib)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      s[ib][r] = S_in ? S_in[bh * D * D + (16 * ib + 4 * g + r) * D + col] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * ib + 4 * g + r;
+      float x = 0.f;
+      if constexpr (kMode == kWhole || kMode == kChain) {
+        if (S_in) x = S_in[bh * DD + row * D + col];
+      } else if constexpr (kMode == kTransfer) {
+        x = right && row == col ? 1.f : 0.f;
+      } else {
+        x = sw[(int64_t)chunk * DD + row * D + col];
+      }
+      s[ib][r] = x;
+    }
 
-  // a frame's A_f (this thread's pieces), U_f (the lane's values) and gamma_f
+  // a step's A (this thread's pieces), U (the lane's values) and gamma
   struct Frame {
     float4 a[C::APT];
     f32x4 u[C::RB];
@@ -383,23 +429,31 @@ __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
   // (lgkmcnt(0)), a few instructions after its issue
   int vzero = 0;
   asm volatile("" : "+v"(vzero));
-  auto load_frame = [&](int f, Frame &b) {
-    const float *src = slab + (int64_t)f * P * SLOT;
+  auto load_step = [&](int t, Frame &b) {
+    const float *amat, *umat;
+    if constexpr (kMode == kChain) {
+      umat = tw + (int64_t)t * 2 * DD;
+      amat = umat + DD;
+    } else {
+      umat = slab + (int64_t)(f0 + t) * P * SLOT;
+      amat = umat + DD;
+    }
 #pragma unroll
     for (int it = 0; it < C::APT; ++it) {
       const int x = tid + C::THREADS * it;
-      b.a[it] = *reinterpret_cast<const float4 *>(src + D * D + (x / (D / 4)) * D + 4 * (x % (D / 4)));
+      b.a[it] = *reinterpret_cast<const float4 *>(amat + (x / (D / 4)) * D + 4 * (x % (D / 4)));
     }
 #pragma unroll
     for (int ib = 0; ib < C::RB; ++ib)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) b.u[ib][r] = src[(16 * ib + 4 * g + r) * D + col];
-    b.g = gamma[bh * F + f + vzero];
+      for (int r = 0; r < 4; ++r)
+        b.u[ib][r] = right ? 0.f : umat[(16 * ib + 4 * g + r) * D + col];
+    if constexpr (kMode != kChain) b.g = gamma[bh * F + f0 + t + vzero];
   };
 
-  // frame f from the loaded buffer b, which then receives frame f_next
-  auto step = [&](int f, Frame &b, int f_next) {
-    sync_lds();  // the previous frame's A reads are done
+  // step t from the loaded buffer b, which then receives step t_next
+  auto step = [&](int t, Frame &b, int t_next) {
+    sync_lds();  // the previous step's A reads are done
 #pragma unroll
     for (int it = 0; it < C::APT; ++it) {
       const int x = tid + C::THREADS * it;
@@ -413,9 +467,16 @@ __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
     f32x4 u[C::RB];
 #pragma unroll
     for (int ib = 0; ib < C::RB; ++ib) u[ib] = b.u[ib];
-    const float gm = b.g;
+    const float gm = kMode == kChain ? 0.f : b.g;
     sync_lds();
-    if (f_next < F) load_frame(f_next, b);
+    if (t_next < nsteps) load_step(t_next, b);
+    if constexpr (kMode == kChain) {
+      // the chunk's start state, before its step
+#pragma unroll
+      for (int ib = 0; ib < C::RB; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sw[(int64_t)t * DD + (16 * ib + 4 * g + r) * D + col] = s[ib][r];
+    }
 
     f32x4 acc[C::RB];
 #pragma unroll
@@ -444,31 +505,39 @@ __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
 #pragma unroll
       for (int ib = 0; ib < C::RB; ++ib) acc[ib] = mfma_16x16x32(alo[ib], bhi, acc[ib]);
     }
-    float *dst = slab + (int64_t)f * P * SLOT;  // S_f, over part 0's U
+    float *dst = slab + (int64_t)(f0 + t) * P * SLOT;  // S_f, over part 0's U
 #pragma unroll
     for (int ib = 0; ib < C::RB; ++ib)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[ib][r] = fmaf(gm, fmaf(-c2, acc[ib][r], s[ib][r]), c1 * u[ib][r]);
-        dst[(16 * ib + 4 * g + r) * D + col] = s[ib][r];
+        if constexpr (kMode == kChain) {
+          s[ib][r] = acc[ib][r] + u[ib][r];
+        } else {
+          s[ib][r] = fmaf(gm, fmaf(-c2, acc[ib][r], s[ib][r]), c1 * u[ib][r]);
+          if constexpr (kMode != kTransfer) dst[(16 * ib + 4 * g + r) * D + col] = s[ib][r];
+        }
       }
   };
 
-  // AHEAD frames in flight: frame f + AHEAD is requested as frame f is staged
-  Frame buf[C::AHEAD];
+  // AHEAD steps in flight: step t + AHEAD is requested as step t is staged
+  Frame buf[J::AHEAD];
 #pragma unroll
-  for (int i = 0; i < C::AHEAD; ++i)
-    if (i < F) load_frame(i, buf[i]);
-  for (int f = 0; f < F; f += C::AHEAD) {
+  for (int i = 0; i < J::AHEAD; ++i)
+    if (i < nsteps) load_step(i, buf[i]);
+  for (int t = 0; t < nsteps; t += J::AHEAD) {
 #pragma unroll
-    for (int i = 0; i < C::AHEAD; ++i)
-      if (f + i < F) step(f + i, buf[i], f + i + C::AHEAD);
+    for (int i = 0; i < J::AHEAD; ++i)
+      if (t + i < nsteps) step(t + i, buf[i], t + i + J::AHEAD);
   }
-  if (S_out) {
+  float *fin = nullptr;  // where the final state goes
+  if constexpr (kMode == kWhole) fin = S_out ? S_out + bh * DD : nullptr;
+  if constexpr (kMode == kApply) fin = (S_out && chunk == nc - 1) ? S_out + bh * DD : nullptr;
+  if constexpr (kMode == kTransfer) fin = tw + ((int64_t)chunk * 2 + (right ? 1 : 0)) * DD;
+  if (fin) {
 #pragma unroll
     for (int ib = 0; ib < C::RB; ++ib)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S_out[bh * D * D + (16 * ib + 4 * g + r) * D + col] = s[ib][r];
+      for (int r = 0; r < 4; ++r) fin[(16 * ib + 4 * g + r) * D + col] = s[ib][r];
   }
 }
 
@@ -491,17 +560,30 @@ __global__ __launch_bounds__(kThreads) void gdn_sum_parts_kernel(float *__restri
   w[0] = a;
 }
 
+template <int D, int kMode>
+void gdn_scan_run(const Plan &p, const GdnScanArgs &a, int64_t items, hipStream_t s) {
+  using C = GsCfg<D>;
+  float *tws = a.ws + p.scan_tws, *sws = a.ws + p.scan_sws;
+  hipLaunchKernelGGL((gdn_scan_mfma_kernel<D, kMode>),
+                     dim3((unsigned)(items * ScanJob<D, kMode>::NWG)), dim3(C::THREADS), 0, s,
+                     a.ws, a.gamma, a.S_in, a.S_out, p.F, p.P, a.key_scale, p.scan_fc, p.scan_nc,
+                     tws, sws);
+}
+
 template <int D>
 void gdn_scan_launch(const Plan &p, const GdnScanArgs &a, hipStream_t s) {
-  using C = GsCfg<D>;
   if (p.P > 1) {
     const int64_t slots = p.BH * p.F, E4 = (int64_t)D * D / 2;
     hipLaunchKernelGGL(gdn_sum_parts_kernel, dim3((unsigned)((slots * E4 + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, s, a.ws, slots, p.P, (int)E4);
   }
-  hipLaunchKernelGGL((gdn_scan_mfma_kernel<D>), dim3((unsigned)(p.BH * C::NWG)),
-                     dim3(C::THREADS), 0, s, a.ws, a.gamma, a.S_in, a.S_out, p.F, p.P,
-                     a.key_scale);
+  if (p.scan_nc > 1) {  // chunks of frames: transfer, chain, apply
+    gdn_scan_run<D, kTransfer>(p, a, p.BH * p.scan_nc, s);
+    gdn_scan_run<D, kChain>(p, a, p.BH, s);
+    gdn_scan_run<D, kApply>(p, a, p.BH * p.scan_nc, s);
+  } else {
+    gdn_scan_run<D, kWhole>(p, a, p.BH, s);
+  }
 }
 
 template <int D>

@@ -48,6 +48,8 @@ constexpr int64_t kMaxGroupFrames = 8;  // the kv kernels hold up to 8 decays
 // kv workgroups resident at once on 256 CUs (4 per CU at d <= 64): grouping
 // frames down to about this many workgroups removes the tail of a second wave.
 constexpr int64_t kResidentKvWorkgroups = 1024;
+constexpr int kChunkedScanMinFrames = 64;  // Gated DeltaNet: scan in chunks from here on
+constexpr int kScanChunkFrames = 32;  // transfer and apply stay memory-bound (16..32 measured)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -621,7 +623,20 @@ bool make_gdn_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
   if (!make_plan(BH, F, T, d, &p)) return false;
   p.G = 1;
   p.NG = F;
-  p.ws_bytes = (size_t)round_up(BH * F * (int64_t)p.P * 2 * d * d * 4, 256);
+  int64_t floats = BH * F * (int64_t)p.P * 2 * d * d;
+  // long sequences scan in chunks of frames (matrix-core path): the chain of
+  // dependent steps drops from F to about 2 Fc + F / Fc
+  int fc = kScanChunkFrames;
+  if (const char *e = getenv("GLA_SCAN_CHUNK"))  // testing knob
+    if (atoi(e) >= 1) fc = atoi(e);
+  if (F >= kChunkedScanMinFrames && fc < F) {
+    p.scan_fc = fc;
+    p.scan_nc = (F + p.scan_fc - 1) / p.scan_fc;
+    p.scan_tws = floats;
+    p.scan_sws = floats + BH * p.scan_nc * 2 * (int64_t)d * d;
+    floats = p.scan_sws + BH * p.scan_nc * (int64_t)d * d;
+  }
+  p.ws_bytes = (size_t)round_up(floats * 4, 256);
   *plan = p;
   return true;
 }

@@ -42,6 +42,11 @@ struct Plan {
   int64_t read_len = 0;  // tokens per readout split (a multiple of 32)
   int G = 1;             // frames per kv group (G > 1 only with P == 1)
   int NG = 0;            // groups per slab, ceil(F / G)
+  // Gated DeltaNet scan in chunks of frames (scan_nc > 1): scan_fc frames per
+  // chunk; float offsets of the per-chunk local states and transfer matrices
+  // (BH * nc * 2 d^2) and of the chunk start states (BH * nc * d^2)
+  int scan_fc = 0, scan_nc = 0;
+  int64_t scan_tws = 0, scan_sws = 0;
   size_t ws_bytes = 0;   // workspace bytes, 256-byte rounded:
                          //   slots  BH * F * P  states of d*d + d floats
                          //   carry  BH * NG     states of d*d + d floats (G > 1 only)

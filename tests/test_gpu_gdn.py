@@ -82,6 +82,10 @@ CASES = [
     ("bf16", 1, 2, 64, 1, 40, True),     # a single frame
     ("bf16", 1, 2, 64, 2, 300, False),   # three parts per frame, ragged last part
     ("bf16", 1, 2, 128, 4, 520, True),   # five parts per frame at d = 128
+    ("bf16", 1, 2, 64, 70, 24, True),    # scan in chunks of 32 frames, a ragged last chunk
+    ("bf16", 1, 2, 32, 64, 16, True),    # exactly two chunks
+    ("bf16", 1, 1, 128, 65, 20, True),   # a last chunk of one frame
+    ("f32", 1, 2, 64, 66, 8, True),      # the vector-ALU scan at the same length
 ]
 
 
