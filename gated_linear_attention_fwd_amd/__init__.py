@@ -247,10 +247,24 @@ def _qkvg(*ts: Optional[torch.Tensor]):
     return ref
 
 
-def _stream_handle(stream, device):
+def _stream_handle(stream, device, *tensors):
+    """The raw stream the kernels are launched on (the current stream if None).
+
+    When it is another stream, every tensor of the call (inputs, outputs and
+    the workspace, which the binding may have allocated on the current stream)
+    is recorded as in use by it, so that torch's caching allocator does not
+    hand their memory out again while the kernels still run there."""
+    current = torch.cuda.current_stream(device)
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        stream = current
+    elif not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    if stream != current:
+        for t in tensors:
+            for x in (t.values() if isinstance(t, dict) else (t,)):
+                if isinstance(x, torch.Tensor) and x.is_cuda and x.numel():
+                    x.record_stream(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
@@ -285,7 +299,8 @@ def gla_fwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     B, H, N, d = ref.shape
     ws, wsb = _workspace(lib.gla_fwd_bidir_workspace(B, H, N, d), dev, workspace)
     _check(lib.gla_fwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), B, H, N, d,
-                             dt, eps, _ptr(ws), wsb, _stream_handle(stream, dev)))
+                             dt, eps, _ptr(ws), wsb,
+                             _stream_handle(stream, dev, q, k, v, g, o, ws)))
     return o
 
 
@@ -321,7 +336,9 @@ def gla_fwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     _check(lib.gla_fwd_framecausal(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in),
                                    _ptr(z_in), _ptr(o), _ptr(S_out), _ptr(z_out), B, H, F, T, d,
                                    dt, eps, _ptr(ws), wsb,
-                                   _stream_handle(stream, dev)))
+
+                                   _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in, o,
+                                                  S_out, z_out, ws)))
     return (o, S_out, z_out) if want_state else o
 
 
@@ -349,7 +366,9 @@ def gla_state_carry(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
     ws, wsb = _workspace(lib.gla_state_carry_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_state_carry(_ptr(k), _ptr(v), _ptr(gamma), _ptr(S_in), _ptr(z_in),
                                _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt,
-                               _ptr(ws), wsb, _stream_handle(stream, dev)))
+                               _ptr(ws), wsb,
+                               _stream_handle(stream, dev, k, v, gamma, S_in, z_in, S_out, z_out,
+                                              ws)))
     return S_out, z_out
 
 
@@ -391,7 +410,8 @@ def gla_fwd_bidir_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     ws, wsb = _workspace(lib.gla_fwd_bidir_ex_workspace(B, H, F, T, d, _rope(rope)), dev,
                          workspace)
     _check(lib.gla_fwd_bidir_ex(_view(q), _view(k), _view(v), _view(g), _view(o), B, H, F, T, d,
-                                dt, eps, _rope(rope), _ptr(ws), wsb, _stream_handle(stream, dev)))
+                                dt, eps, _rope(rope), _ptr(ws), wsb,
+                                _stream_handle(stream, dev, q, k, v, g, o, ws)))
     return o
 
 
@@ -428,7 +448,9 @@ def gla_fwd_framecausal_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     _check(lib.gla_fwd_framecausal_ex(_view(q), _view(k), _view(v), _view(g), _ptr(gamma),
                                       _ptr(S_in), _ptr(z_in), _view(o), _ptr(S_out), _ptr(z_out),
                                       B, H, F, T, d, dt, eps, _rope(rope), _ptr(ws), wsb,
-                                      _stream_handle(stream, dev)))
+
+                                      _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in,
+                                                     o, S_out, z_out, ws)))
     return (o, S_out, z_out) if want_state else o
 
 
@@ -456,7 +478,9 @@ def gla_state_carry_ex(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
     ws, wsb = _workspace(lib.gla_state_carry_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_state_carry_ex(_view(k), _view(v), _ptr(gamma), _ptr(S_in), _ptr(z_in),
                                   _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt, _rope(rope),
-                                  _ptr(ws), wsb, _stream_handle(stream, dev)))
+                                  _ptr(ws), wsb,
+                                  _stream_handle(stream, dev, k, v, gamma, S_in, z_in, S_out,
+                                                 z_out, ws)))
     return S_out, z_out
 
 
@@ -506,7 +530,8 @@ def gla_bwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _ptr(dO),
         _ptr(dS_out), _ptr(dz_out), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
         _ptr(out["dg"]), _ptr(out["dgamma"]), _ptr(out.get("dS_in")), _ptr(out.get("dz_in")),
-        B, H, F, T, d, dt, eps, _ptr(ws), wsb, _stream_handle(stream, dev)))
+        B, H, F, T, d, dt, eps, _ptr(ws), wsb,
+        _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in, dO, dS_out, dz_out, out, ws)))
     return out
 
 
@@ -525,7 +550,8 @@ def gla_bwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     ws, wsb = _workspace(lib.gla_bwd_bidir_workspace(B, H, N, d), dev, workspace)
     _check(lib.gla_bwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dO), _ptr(out["dq"]),
                              _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), B, H, N, d, dt,
-                             eps, _ptr(ws), wsb, _stream_handle(stream, dev)))
+                             eps, _ptr(ws), wsb,
+                             _stream_handle(stream, dev, q, k, v, g, dO, out, ws)))
     return out
 
 
@@ -565,7 +591,9 @@ def gla_gdn_framecausal(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Ten
     ws, wsb = _workspace(lib.gla_gdn_framecausal_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_gdn_framecausal(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma),
                                    _ptr(S_in), _ptr(o), _ptr(S_out), B, H, F, T, d, dt,
-                                   float(key_scale), _ptr(ws), wsb, _stream_handle(stream, dev)))
+                                   float(key_scale), _ptr(ws), wsb,
+                                   _stream_handle(stream, dev, q, k, v, beta, gamma, S_in, o,
+                                                  S_out, ws)))
     if q is None:
         return S_out
     return (o, S_out) if want_state else o
@@ -597,7 +625,8 @@ def gla_softmax_anchor(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: tor
     dev = _require_device(q, k, v, g, o)
     _check(lib.gla_softmax_anchor(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), B, H, Nq // T,
                                   Nk // T, T, d, _dtype_code(k), int(bool(causal)), int(n_sink),
-                                  int(window), float(scale), _stream_handle(stream, dev)))
+                                  int(window), float(scale),
+                                  _stream_handle(stream, dev, q, k, v, g, o)))
     return o
 
 
