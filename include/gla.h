@@ -35,8 +35,13 @@
  *  - Pointers are device memory of the current HIP device, owned by the
  *    caller. The entry points never allocate, free or synchronise; all work is
  *    enqueued asynchronously on `stream` (a hipStream_t; NULL is the default
- *    stream). Tensor pointers must be 16-byte aligned, gamma 4-byte aligned,
- *    the workspace 256-byte aligned.
+ *    stream). A call enqueues kernel launches only (no memset, copy or
+ *    synchronisation), so it can be captured into a HIP graph and replayed.
+ *    The library keeps no state between calls (apart from the optional
+ *    timing session below): calls from several threads or on several
+ *    streams may run at once when their outputs and workspaces are disjoint.
+ *    Tensor pointers must be 16-byte aligned, gamma 4-byte aligned, the
+ *    workspace 256-byte aligned.
  *  - Aliasing: S_out may equal S_in and z_out may equal z_in (in-place
  *    update). No other overlap is allowed (checked: GLA_ERR_ALIAS).
  *  - Errors: every argument is validated on the host before anything is
