@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="fwd: the forward call (the headline); bwd: the backward call "
                          "(gradients of the forward for a random dL/do)")
+    ap.add_argument("--saved-states", action="store_true",
+                    help="--pass fwd: the forward that records every frame's state "
+                         "(gla_fwd_framecausal_states); --pass bwd: the backward given that "
+                         "record (no recompute of the states)")
     ap.add_argument("--mixer", default="gla", choices=["gla", "gdn", "anchor"],
                     help="gla: gated linear attention (the headline); gdn: the frame-wise "
                          "Gated DeltaNet (beta = sigmoid of a normal draw per token); anchor: "
@@ -218,6 +222,14 @@ def main():
         print("bench.py: the backward takes contiguous tensors without rotary positions",
               file=sys.stderr)
         sys.exit(2)
+    saved = args.saved_states
+    if saved and (ex or mode != "framecausal" or args.mixer != "gla"):
+        print("bench.py: --saved-states goes with the contiguous frame-causal linear mixer",
+              file=sys.stderr)
+        sys.exit(2)
+    if saved and not bwd:
+        rec = [torch.empty((w.B, w.H, b["gamma"].shape[-1], d * d + d), dtype=torch.float32,
+                           device=dev) for b in blocks]
     if bwd:
         # dL/do drawn on the device; for a stream, the forward states at the block
         # boundaries (the S_in of each block) are computed once, before timing
@@ -239,8 +251,16 @@ def main():
             for gd in grads:
                 gd["dS_in"] = torch.empty_like(S)
                 gd["dz_in"] = torch.empty_like(z)
+        if saved:  # the forward's record of every frame's state, made before timing
+            for b, si in zip(blocks, s_in):
+                _, b["states"] = gla.gla_fwd_framecausal_states(
+                    b["q"], b["k"], b["v"], b["g"], b["gamma"], si[0] if si else None,
+                    si[1] if si else None, eps=w.eps)
         if mode == "bidir":
             wsb = gla.gla_bwd_bidir_workspace(w.B, w.H, w.N, d)
+        elif saved:
+            wsb = max(gla.gla_bwd_framecausal_states_workspace(
+                w.B, w.H, b["gamma"].shape[-1], w.T, d) for b in blocks)
         else:
             wsb = max(gla.gla_bwd_framecausal_workspace(w.B, w.H, b["gamma"].shape[-1], w.T, d)
                       for b in blocks)
@@ -255,10 +275,14 @@ def main():
         dS = dz = None  # the stream's last block first
         for i in reversed(range(len(blocks))):
             b, si = blocks[i], s_in[i]
-            r = gla.gla_bwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"], b["dO"],
-                                        S_in=si[0] if si else None, z_in=si[1] if si else None,
-                                        dS_out=dS, dz_out=dz, eps=w.eps, out=grads[i],
-                                        workspace=ws)
+            kw = dict(S_in=si[0] if si else None, z_in=si[1] if si else None, dS_out=dS,
+                      dz_out=dz, eps=w.eps, out=grads[i], workspace=ws)
+            if saved:
+                r = gla.gla_bwd_framecausal_states(b["q"], b["k"], b["v"], b["g"], b["gamma"],
+                                                   b["states"], b["dO"], **kw)
+            else:
+                r = gla.gla_bwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"], b["dO"],
+                                            **kw)
             dS, dz = r.get("dS_in"), r.get("dz_in")
 
     def step_gdn():
@@ -298,12 +322,17 @@ def main():
         if carry:
             S.zero_()
             z.zero_()
-        for b, o, r in zip(blocks, outs, ropes):
+        for i, (b, o, r) in enumerate(zip(blocks, outs, ropes)):
             if ex:
                 gla.gla_fwd_framecausal_ex(b["q"], b["k"], b["v"], b["g"], b["gamma"],
                                            S if carry else None, z if carry else None,
                                            eps=w.eps, rope=r, out=o, S_out=S, z_out=z,
                                            workspace=ws)
+            elif saved:
+                gla.gla_fwd_framecausal_states(b["q"], b["k"], b["v"], b["g"], b["gamma"],
+                                               S if carry else None, z if carry else None,
+                                               eps=w.eps, out=o, states=rec[i],
+                                               S_out=S, z_out=z, workspace=ws)
             else:
                 gla.gla_fwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"],
                                         S if carry else None, z if carry else None, eps=w.eps,
@@ -330,7 +359,7 @@ def main():
     value = tokens / (ms_per_step / 1e3)
 
     # ---------------------------------------------------------------- per-kernel times
-    launches_per_step = (6 if bwd else 3) * len(blocks)
+    launches_per_step = ((4 if saved else 6) if bwd else 3) * len(blocks)
     gla.profile_begin(launches_per_step * args.steps)
     for _ in range(args.steps):
         step()
@@ -360,7 +389,8 @@ def main():
     dk = kernels[dom]
     achieved = dk["alg_bytes_per_launch"] / (dk["avg_ms"] / 1e3)
     variant = w.name + "/" + mode + ("/fused" if args.layout == "fused" else "") + \
-        ("/rope" if args.rope else "") + ("/bwd" if bwd else "") + ("/gdn" if gdn else "") + \
+        ("/rope" if args.rope else "") + ("/bwd" if bwd else "") + \
+        ("/states" if saved else "") + ("/gdn" if gdn else "") + \
         ("/anchor" if anchor else "")
     family = "anchor" if anchor else ("gdn" if gdn else ("bwd" if bwd else "gla"))
     traffic_rec = committed_traffic(dom, variant, family)
@@ -374,7 +404,8 @@ def main():
                     "frac": round(fl / BF16_MFMA_PEAK, 4),
                     "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
     # forward: read q, k, v, g, write o; backward: read q, k, v, g, dO, write dq,
-    # dk, dv, dg (the recompute's second read of k and v is not counted)
+    # dk, dv, dg (the recompute's second read of k and v is not counted; with
+    # saved states there is none)
     if anchor:  # read q, k, v, g, write o (re-reads of k and v from cache not counted)
         call_bytes = w.io_bytes()
         flops = anchor_flops
@@ -416,8 +447,9 @@ def main():
                    "layout": ("q, k, v slices of [B,N,3,H,d]; g, o [B,N,H,d]"
                               if args.layout == "fused" else "[B,H,N,d] contiguous"),
                    "rope": ropes[0].as_dict() if args.rope else None,
-                   "pass": "backward (dq, dk, dv, dg, dgamma for a random dL/do)" if bwd
-                   else "forward",
+                   "pass": ("backward (dq, dk, dv, dg, dgamma for a random dL/do)" + (
+                       ", given the forward's per-frame states" if saved else "")) if bwd
+                   else ("forward, recording every frame's state" if saved else "forward"),
                    "mixer": ("frame-wise Gated DeltaNet (block delta rule per frame, key "
                              "scale 1/sqrt(d T))" if gdn else (
                                  "gated softmax anchor (%s)" % (

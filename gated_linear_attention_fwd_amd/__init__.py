@@ -148,6 +148,12 @@ def load_library():
     lib.gla_bwd_framecausal.restype = i32
     lib.gla_bwd_bidir.argtypes = [vp] * 9 + [i32, i32, i64, i32, i32, f32, vp, sz, vp]
     lib.gla_bwd_bidir.restype = i32
+    lib.gla_fwd_framecausal_states.argtypes = [vp] * 11 + [i32] * 6 + [f32, vp, sz, vp]
+    lib.gla_fwd_framecausal_states.restype = i32
+    lib.gla_bwd_framecausal_states_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.gla_bwd_framecausal_states_workspace.restype = sz
+    lib.gla_bwd_framecausal_states.argtypes = [vp] * 18 + [i32] * 6 + [f32, vp, sz, vp]
+    lib.gla_bwd_framecausal_states.restype = i32
     lib.gla_gdn_framecausal_workspace.argtypes = [i32, i32, i32, i32, i32]
     lib.gla_gdn_framecausal_workspace.restype = sz
     lib.gla_gdn_framecausal.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp, sz, vp]
@@ -342,6 +348,50 @@ def gla_fwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     return (o, S_out, z_out) if want_state else o
 
 
+def gla_fwd_framecausal_states(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               g: torch.Tensor, gamma: torch.Tensor,
+                               S_in: Optional[torch.Tensor] = None,
+                               z_in: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                               out: Optional[torch.Tensor] = None,
+                               states: Optional[torch.Tensor] = None,
+                               S_out: Optional[torch.Tensor] = None,
+                               z_out: Optional[torch.Tensor] = None, return_state: bool = False,
+                               workspace: Optional[torch.Tensor] = None, stream=None):
+    """gla_fwd_framecausal that also records every frame's state for the backward.
+
+    ``states`` is float32 [B, H, F, d*d + d]: S_f (row-major) then z_f per frame.
+    Returns ``(o, states)``, or ``(o, states, S_out, z_out)`` when
+    ``return_state`` is set or S_out/z_out are given."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    want_state = return_state or S_out is not None or z_out is not None
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
+    if want_state and z_out is None:
+        z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    if states is None:
+        states = torch.empty((B, H, F, d * d + d), dtype=torch.float32, device=ref.device)
+    elif states.shape != (B, H, F, d * d + d) or states.dtype != torch.float32:
+        raise ValueError("states must be float32 [B, H, F, d*d + d]")
+    o = torch.empty_like(ref) if out is None else out
+    dev = _require_device(q, k, v, g, gamma, S_in, z_in, o, states, S_out, z_out, workspace)
+    ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
+    _check(lib.gla_fwd_framecausal_states(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _ptr(o),
+        _ptr(S_out), _ptr(z_out), _ptr(states), B, H, F, T, d, dt, eps, _ptr(ws), wsb,
+        _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in, o, states, S_out, z_out,
+                       ws)))
+    return (o, states, S_out, z_out) if want_state else (o, states)
+
+
 def gla_state_carry(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
                     S_in: Optional[torch.Tensor] = None, z_in: Optional[torch.Tensor] = None,
                     S_out: Optional[torch.Tensor] = None, z_out: Optional[torch.Tensor] = None,
@@ -504,6 +554,31 @@ def gla_bwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     Returns {"dq", "dk", "dv", "dg", "dgamma"} and, when ``need_state_grad``
     (default: S_in or dS_out given), "dS_in" and "dz_in". ``out`` may supply
     any of these tensors to be written."""
+    return _bwd_framecausal(q, k, v, g, gamma, None, dO, S_in, z_in, dS_out, dz_out, eps,
+                            need_state_grad, out, workspace, stream)
+
+
+def gla_bwd_framecausal_states(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               g: torch.Tensor, gamma: torch.Tensor, states: torch.Tensor,
+                               dO: torch.Tensor, S_in: Optional[torch.Tensor] = None,
+                               z_in: Optional[torch.Tensor] = None,
+                               dS_out: Optional[torch.Tensor] = None,
+                               dz_out: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                               need_state_grad: Optional[bool] = None,
+                               out: Optional[dict] = None,
+                               workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """gla_bwd_framecausal given the states recorded by gla_fwd_framecausal_states
+    for the same inputs (no recompute; bitwise the same gradients)."""
+    return _bwd_framecausal(q, k, v, g, gamma, states, dO, S_in, z_in, dS_out, dz_out, eps,
+                            need_state_grad, out, workspace, stream)
+
+
+def gla_bwd_framecausal_states_workspace(B: int, H: int, F: int, T: int, d: int) -> int:
+    return int(load_library().gla_bwd_framecausal_states_workspace(B, H, F, T, d))
+
+
+def _bwd_framecausal(q, k, v, g, gamma, states, dO, S_in, z_in, dS_out, dz_out, eps,
+                     need_state_grad, out, workspace, stream) -> dict:
     lib = load_library()
     ref = _qkvg(q, k, v, g, dO)
     dt = _dtype_code(ref)
@@ -514,6 +589,9 @@ def gla_bwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     if (F == 0 and N != 0) or (F and N % F):
         raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
     T = N // F if F else 0
+    if states is not None and (states.shape != (B, H, F, d * d + d)
+                               or states.dtype != torch.float32):
+        raise ValueError("states must be float32 [B, H, F, d*d + d]")
     if need_state_grad is None:
         need_state_grad = S_in is not None or dS_out is not None
     out = dict(out or {})
@@ -523,15 +601,26 @@ def gla_bwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     if need_state_grad:
         out.setdefault("dS_in", torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device))
         out.setdefault("dz_in", torch.empty((B, H, d), dtype=torch.float32, device=ref.device))
-    dev = _require_device(q, k, v, g, gamma, dO, S_in, z_in, dS_out, dz_out, workspace,
+    dev = _require_device(q, k, v, g, gamma, states, dO, S_in, z_in, dS_out, dz_out, workspace,
                           *out.values())
-    ws, wsb = _workspace(lib.gla_bwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
-    _check(lib.gla_bwd_framecausal(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _ptr(dO),
-        _ptr(dS_out), _ptr(dz_out), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-        _ptr(out["dg"]), _ptr(out["dgamma"]), _ptr(out.get("dS_in")), _ptr(out.get("dz_in")),
-        B, H, F, T, d, dt, eps, _ptr(ws), wsb,
-        _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in, dO, dS_out, dz_out, out, ws)))
+    grads = (_ptr(dO), _ptr(dS_out), _ptr(dz_out), _ptr(out["dq"]), _ptr(out["dk"]),
+             _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dgamma"]), _ptr(out.get("dS_in")),
+             _ptr(out.get("dz_in")))
+    if states is None:
+        nbytes = lib.gla_bwd_framecausal_workspace(B, H, F, T, d)
+    else:
+        nbytes = lib.gla_bwd_framecausal_states_workspace(B, H, F, T, d)
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    handle = _stream_handle(stream, dev, q, k, v, g, gamma, states, S_in, z_in, dO, dS_out,
+                            dz_out, out, ws)
+    if states is None:
+        _check(lib.gla_bwd_framecausal(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), *grads,
+            B, H, F, T, d, dt, eps, _ptr(ws), wsb, handle))
+    else:
+        _check(lib.gla_bwd_framecausal_states(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in),
+            _ptr(states), *grads, B, H, F, T, d, dt, eps, _ptr(ws), wsb, handle))
     return out
 
 

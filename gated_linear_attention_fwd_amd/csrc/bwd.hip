@@ -29,8 +29,9 @@ constexpr int kThreads = 256;
 // columns jc + JS c) and gz = sum dden phi(q) the threads with jc == 0.
 template <typename TIn, int D>
 __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
-    View qv, View gv, View dov, View dqv, View dgv, int H, const float *__restrict__ ws,
-    float *__restrict__ gs, int F, int64_t T, int P, int R, int64_t read_len, float eps) {
+    View qv, View gv, View dov, View dqv, View dgv, int H, const float *__restrict__ st,
+    int64_t sstride, float *__restrict__ gs, int F, int64_t T, int R, int64_t read_len,
+    float eps) {
   constexpr int CG = D / 4;
   constexpr int TT = kThreads / CG;
   constexpr bool kSInLds = (D <= 64);
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
   const int64_t t0 = min((int64_t)r * read_len, T);
   const int64_t t1 = min(t0 + read_len, T);
 
-  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;  // S_f (the carry left it in place)
+  const float *Sg = st + (bh * F + f) * sstride;  // S_f
   if (kSInLds)
     for (int e = tid; e < D * D; e += kThreads) sS[e] = Sg[e];
   for (int e = tid; e < D; e += kThreads) sz[e] = Sg[D * D + e];
@@ -223,9 +224,10 @@ constexpr int kScanThreads = 256;
 constexpr int kScanBatch = 8;
 
 __global__ __launch_bounds__(kScanThreads) void rev_scan_kernel(
-    const float *__restrict__ ws, float *__restrict__ gs, const float *__restrict__ gamma,
-    const float *S_in, const float *z_in, const float *dS_out, const float *dz_out, float *dS_in,
-    float *dz_in, float *__restrict__ dgp, int F, int P, int R, int d, int NB) {
+    const float *__restrict__ st, int64_t sstride, float *__restrict__ gs,
+    const float *__restrict__ gamma, const float *S_in, const float *z_in, const float *dS_out,
+    const float *dz_out, float *dS_in, float *dz_in, float *__restrict__ dgp, int F, int R, int d,
+    int NB) {
   const int64_t dd = (int64_t)d * d;
   const int64_t E = dd + d;
   const int64_t bh = blockIdx.x / NB;
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kScanThreads) void rev_scan_kernel(
         x[j] = s;
         if (dgp) {
           if (f > 0)
-            prev[j] = ws[((bh * F + f - 1) * (int64_t)P) * E + e];
+            prev[j] = st[(bh * F + f - 1) * sstride + e];
           else if (is_S && S_in)
             prev[j] = S_in[bh * dd + e];
           else if (!is_S && z_in)
@@ -314,8 +316,8 @@ hipError_t bwd_q_valu_dispatch(const BwdPlan &bp, const BwdQArgs &a, hipStream_t
 #define GLA_BQ_CASE(DD)                                                                       \
   case DD:                                                                                    \
     hipLaunchKernelGGL((bwd_q_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), 0, \
-                       s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.ws, gs, p.F, p.T, p.P, p.R,       \
-                       p.read_len, a.eps);                                                    \
+                       s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.st.base, a.st.stride, gs, p.F,    \
+                       p.T, p.R, p.read_len, a.eps);                                          \
     break;
   switch (p.d) {
     GLA_BQ_CASE(16)
@@ -365,9 +367,9 @@ hipError_t launch_bwd_k_valu(const BwdPlan &p, int dtype, const BwdKArgs &a, hip
 hipError_t launch_rev_scan(const BwdPlan &p, const RevScanArgs &a, hipStream_t s) {
   const int64_t grid = p.f.BH * p.NB;
   if (grid == 0) return hipSuccess;  // F == 0 still runs: dS_in = dS_out
-  hipLaunchKernelGGL(rev_scan_kernel, dim3((unsigned)grid), dim3(kScanThreads), 0, s, a.ws, a.gs,
-                     a.gamma, a.S_in, a.z_in, a.dS_out, a.dz_out, a.dS_in, a.dz_in, a.dgp, p.f.F,
-                     p.f.P, p.f.R, p.f.d, p.NB);
+  hipLaunchKernelGGL(rev_scan_kernel, dim3((unsigned)grid), dim3(kScanThreads), 0, s, a.st.base,
+                     a.st.stride, a.gs, a.gamma, a.S_in, a.z_in, a.dS_out, a.dz_out, a.dS_in,
+                     a.dz_in, a.dgp, p.f.F, p.f.R, p.f.d, p.NB);
   return hipGetLastError();
 }
 

@@ -211,8 +211,8 @@ struct BqCfg {
 template <int D>
 __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
     View qview, View gview, View doview, View dqview, View dgview, int H,
-    const float *__restrict__ ws, float *__restrict__ gs, int F, int64_t T, int P, int R,
-    int64_t read_len, float eps) {
+    const float *__restrict__ st, int64_t sstride, float *__restrict__ gs, int F, int64_t T,
+    int R, int64_t read_len, float eps) {
   using C = BqCfg<D>;
   static_assert(C::CPT >= 1, "tile too small for the workgroup");
   // six row tiles in one array; after the last block it holds the G reduction
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
   const int L = (int)max(t1 - t0, (int64_t)0);
 
   constexpr int64_t E = (int64_t)D * D + D;
-  const float *Sg = ws + ((bh * F + f) * (int64_t)P) * E;  // S_f (left in place by the carry)
+  const float *Sg = st + (bh * F + f) * sstride;  // S_f
   if (tid < D) szf[tid] = Sg[D * D + tid];
   bf16x8 ahi[C::KS], alo[C::KS];
   if (role_q)
@@ -588,8 +588,8 @@ template <int D>
 void bwd_q_launch(const BwdPlan &bp, const BwdQArgs &a, hipStream_t s) {
   const Plan &p = bp.f;
   hipLaunchKernelGGL((bwd_q_mfma_kernel<D>), dim3((unsigned)(p.BH * p.F * p.R)),
-                     dim3(kBwThreads), 0, s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.ws, a.gs, p.F,
-                     p.T, p.P, p.R, p.read_len, a.eps);
+                     dim3(kBwThreads), 0, s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.st.base,
+                     a.st.stride, a.gs, p.F, p.T, p.R, p.read_len, a.eps);
 }
 
 template <int D>

@@ -12,10 +12,11 @@
 //   carry_{g+1} = S_loc_{last frame of g} + (prod_{m in g} gamma_m) * carry_g
 //
 // and S_out = carry_{NG}. With one frame per group (G = 1) no carries are
-// kept: the walk is the plain scan S_f = gamma_f S_{f-1} + U_f, and S_f is
-// written in place over the frame's slot (part 0, after summing the frame's
-// parts in a fixed order), which is all the readout needs. Bidirectional mode
-// is that walk with one frame and no decay.
+// kept: the walk is the plain scan S_f = gamma_f S_{f-1} + U_f (the frame's
+// parts summed in a fixed order), and S_f is written where the readout will
+// read it: in place over the frame's slot (part 0), or into a caller's record
+// of the per-frame states. Bidirectional mode is that walk with one frame and
+// no decay.
 //
 // One thread owns one of the d*d + d state elements of one slab. The chain of
 // FMAs is serial, the loads are not: a batch of groups is loaded first, then
@@ -32,7 +33,8 @@ constexpr int kGroupBatch = 16;
 __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     float *__restrict__ ws, const float *__restrict__ gamma, const float *S_in,
     const float *z_in, float *S_out, float *z_out, int F, int P, int G, int NG, int d,
-    int64_t blocks_per_slab, int64_t carry_offset, int keep_frames) {
+    int64_t blocks_per_slab, int64_t carry_offset, int keep_frames, float *frames,
+    int64_t frames_stride) {
   const int64_t dd = (int64_t)d * d;
   const int64_t E = dd + d;
   const int64_t bh = blockIdx.x / blocks_per_slab;
@@ -45,6 +47,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   const int64_t frame_stride = (int64_t)P * E;
   float *slots = ws + bh * (int64_t)F * frame_stride + e;
   float *carry = ws + carry_offset + bh * (int64_t)NG * E + e;
+  float *dst = frames + bh * (int64_t)F * frames_stride + e;  // G == 1: S_f of frame f
   const float *gm_slab = gamma ? gamma + bh * F : nullptr;
 
   for (int g0 = 0; g0 < NG; g0 += kGroupBatch) {
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       if (grp < NG) {
         if (keep_frames && G > 1) carry[(int64_t)grp * E] = s;
         s = fmaf(w[j], s, x[j]);
-        if (keep_frames && G == 1) slots[(int64_t)grp * frame_stride] = s;
+        if (keep_frames && G == 1) dst[(int64_t)grp * frames_stride] = s;
       }
     }
   }
@@ -93,7 +96,8 @@ hipError_t launch_carry(const Plan &p, const CarryArgs &a, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(carry_kernel, dim3((unsigned)grid), dim3(kCarryThreads), 0, stream, a.ws,
                      a.gamma, a.S_in, a.z_in, a.S_out, a.z_out, p.F, p.P, p.G, p.NG, p.d,
-                     blocks_per_slab, p.carry_offset(), a.keep_frames);
+                     blocks_per_slab, p.carry_offset(), a.keep_frames, a.frames.base,
+                     a.frames.stride);
   return hipGetLastError();
 }
 

@@ -273,7 +273,7 @@ enum class Mode { kBidir, kFrameCausal, kStateCarry };
 gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_tensor *v,
                const gla_tensor *g, const float *gamma, const float *S_in, const float *z_in,
                const gla_tensor *o, float *S_out, float *z_out, int B, int H, int F, int64_t T,
-               int d, gla_dtype dt, float eps, const gla_rope3d *rope, void *ws,
+               int d, gla_dtype dt, float eps, const gla_rope3d *rope, float *states, void *ws,
                size_t ws_bytes, void *stream) {
   const bool outputs = mode != Mode::kStateCarry;
   const bool bidir = mode == Mode::kBidir;
@@ -316,6 +316,7 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
   GLA_TRY(check_tensor_align(S_out, "S_out"));
   GLA_TRY(check_tensor_align(z_out, "z_out"));
   if (gamma && !aligned(gamma, 4)) return fail(GLA_ERR_ALIGN, "gamma is not 4-byte aligned");
+  GLA_TRY(check_tensor_align(states, "states"));
   RopeK rk_;
   GLA_TRY(make_rope(rope, F, T, d, &rk_));
 
@@ -324,6 +325,9 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
   Plan p;
   if (!make_plan(BH, flat ? (N > 0 ? 1 : 0) : F, flat ? N : T, d, &p))
     return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
+  // a record of every frame's state: the scan runs frame by frame and writes
+  // S_f there, where the readout then reads it
+  if (states) single_frame_groups(&p);
   if (BH == 0 || (bidir && N == 0)) return GLA_OK;
   GLA_TRY(check_ws(p, ws, ws_bytes));
   const Path path = select_path(dt, d);
@@ -339,13 +343,15 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
                        {S_in, sbytes, "S_in"},   {z_in, zbytes, "z_in"},
                        ro,
                        {S_out, sbytes, "S_out"}, {z_out, zbytes, "z_out"},
-                       {ws, p.ws_bytes, "workspace"}};
+                       {ws, p.ws_bytes, "workspace"},
+                       {states, (size_t)(BH * F * p.state_elems()) * 4, "states"}};
   // S_out may be S_in exactly (and z_out z_in): compare them without the inputs.
-  const Range outs_o[] = {ro, {ws, p.ws_bytes, "workspace"}};
-  GLA_TRY(check_no_overlap(outs_o, 2, all, 11));
+  const Range outs_o[] = {ro, all[10], all[11]};
+  GLA_TRY(check_no_overlap(outs_o, 3, all, 12));
   const Range outs_s[] = {{S_out, sbytes, "S_out"}, {z_out, zbytes, "z_out"}};
-  const Range others[] = {all[0], all[1], all[2], all[3], all[4], all[7], all[8], all[9], all[10]};
-  GLA_TRY(check_no_overlap(outs_s, 2, others, 9));
+  const Range others[] = {all[0], all[1], all[2], all[3], all[4],
+                          all[7], all[8], all[9], all[10], all[11]};
+  GLA_TRY(check_no_overlap(outs_s, 2, others, 10));
   if (S_out && S_in && S_out != S_in && overlap(outs_s[0], all[5]))
     return fail(GLA_ERR_ALIAS, "S_out partially overlaps S_in");
   if (z_out && z_in && z_out != z_in && overlap(outs_s[1], all[6]))
@@ -366,12 +372,14 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
                              return launch_kv(p, dt, path, KvArgs{vk, vv, H, gm, wsf, rk_}, s);
                            }),
                      "kv"));
+  const FrameStates fs = states ? FrameStates{states, p.state_elems()}
+                                : FrameStates{wsf, p.slot_stride()};
   const CarryArgs sa{wsf,   gm,    bidir ? nullptr : S_in, bidir ? nullptr : z_in,
-                     S_out, z_out, outputs ? 1 : 0};
+                     S_out, z_out, (outputs || states) ? 1 : 0, fs};
   GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, sa, s); }), "carry"));
   if (outputs && have_tokens) {
-    const ReadoutArgs ra{vq, vg, vo, H, gm, wsf, eps, (bidir && !flat) ? p.F - 1 : -1, rk_,
-                         ro_heads};
+    const ReadoutArgs ra{vq,  vg, vo, H, gm, wsf, fs, eps, (bidir && !flat) ? p.F - 1 : -1,
+                         rk_, ro_heads};
     GLA_TRY(launched(timed(kKindReadout, s, [&] { return launch_readout(p, dt, path, ra, s); }),
                      "readout"));
   }
@@ -386,9 +394,9 @@ gla_tensor contiguous(const void *p, int H, int64_t N, int d) {
 gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, const void *g,
                    const float *gamma, const float *S_in, const float *z_in, const void *dO,
                    const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                   void *dg, float *dgamma, float *dS_in, float *dz_in, int B, int H, int F,
-                   int64_t T, int d, gla_dtype dt, float eps, void *ws, size_t ws_bytes,
-                   void *stream) {
+                   void *dg, float *dgamma, float *dS_in, float *dz_in, bool want_states,
+                   const float *states, int B, int H, int F, int64_t T, int d, gla_dtype dt,
+                   float eps, void *ws, size_t ws_bytes, void *stream) {
   GLA_TRY(check_dims(B, H, d, dt));
   if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%lld must be >= 0", F, (long long)T);
   GLA_TRY(check_eps(eps));
@@ -415,9 +423,11 @@ gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, cons
   for (int i = 0; i < 6; ++i) GLA_TRY(check_tensor_align(st[i], snames[i]));
   if (gamma && !aligned(gamma, 4)) return fail(GLA_ERR_ALIGN, "gamma is not 4-byte aligned");
   if (dgamma && !aligned(dgamma, 4)) return fail(GLA_ERR_ALIGN, "dgamma is not 4-byte aligned");
+  GLA_TRY(check_tensor_align(states, "states"));
+  if (want_states && BH > 0 && F > 0 && !states) return fail(GLA_ERR_NULL, "states is required");
 
   BwdPlan bp;
-  if (!make_bwd_plan(BH, bidir ? (N > 0 ? 1 : 0) : F, bidir ? N : T, d, &bp))
+  if (!make_bwd_plan(BH, bidir ? (N > 0 ? 1 : 0) : F, bidir ? N : T, d, &bp, !want_states))
     return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
   if (BH == 0 || (bidir && N == 0)) return GLA_OK;
   if (bp.ws_bytes) {
@@ -447,8 +457,9 @@ gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, cons
                        {dgamma, causal ? (size_t)(BH * F) * 4 : 0, "dgamma"},
                        {dS_in, causal ? sbytes : 0, "dS_in"},
                        {dz_in, causal ? zbytes : 0, "dz_in"},
-                       {ws, bp.ws_bytes, "workspace"}};
-  GLA_TRY(check_no_overlap(all + 10, 8, all, 18));
+                       {ws, bp.ws_bytes, "workspace"},
+                       {states, causal ? (size_t)(BH * F * bp.f.state_elems()) * 4 : 0, "states"}};
+  GLA_TRY(check_no_overlap(all + 10, 8, all, 19));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Path path = select_path(dt, d);
@@ -461,21 +472,28 @@ gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, cons
              vdo = contiguous_view(dO, H, N, d), vdq = contiguous_view(dq, H, N, d),
              vdk = contiguous_view(dk, H, N, d), vdv = contiguous_view(dv, H, N, d),
              vdg = contiguous_view(dg, H, N, d);
+  // the forward's S_f: recomputed into the workspace slots, or the caller's record
+  const FrameStates fst = want_states
+                              ? FrameStates{const_cast<float *>(states), p.state_elems()}
+                              : FrameStates{wsf, p.slot_stride()};
   if (p.F > 0) {
-    GLA_TRY(launched(timed(kKindKv, s,
-                           [&] {
-                             return launch_kv(p, dt, path, KvArgs{vk, vv, H, gm, wsf, RopeK{}}, s);
-                           }),
-                     "kv"));
-    const CarryArgs ca{wsf, gm, causal ? S_in : nullptr, causal ? z_in : nullptr,
-                       nullptr, nullptr, 1};
-    GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, ca, s); }), "carry"));
-    const BwdQArgs qa{vq, vg, vdo, vdq, vdg, H, wsf, gsf, eps};
+    if (!want_states) {
+      GLA_TRY(launched(timed(kKindKv, s,
+                             [&] {
+                               return launch_kv(p, dt, path, KvArgs{vk, vv, H, gm, wsf, RopeK{}},
+                                                s);
+                             }),
+                       "kv"));
+      const CarryArgs ca{wsf, gm, causal ? S_in : nullptr, causal ? z_in : nullptr,
+                         nullptr, nullptr, 1, fst};
+      GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, ca, s); }), "carry"));
+    }
+    const BwdQArgs qa{vq, vg, vdo, vdq, vdg, H, fst, gsf, eps};
     GLA_TRY(launched(timed(kKindBwdQ, s, [&] { return launch_bwd_q(bp, dt, path, qa, s); }),
                      "bwd_q"));
   }
   float *dgp = (causal && dgamma && p.F > 0) ? wsf + bp.dgp_offset : nullptr;
-  const RevScanArgs ra{wsf,
+  const RevScanArgs ra{fst,
                        gsf,
                        gm,
                        causal ? S_in : nullptr,
@@ -701,14 +719,20 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
   return true;
 }
 
-bool make_bwd_plan(int64_t BH, int F, int64_t T, int d, BwdPlan *plan) {
+void single_frame_groups(Plan *plan) {
+  Plan &p = *plan;
+  p.G = 1;
+  p.NG = p.F;
+  p.ws_bytes = (size_t)round_up(p.BH * p.F * (int64_t)p.P * p.state_elems() * 4, 256);
+}
+
+bool make_bwd_plan(int64_t BH, int F, int64_t T, int d, BwdPlan *plan, bool with_slots) {
   BwdPlan b;
   if (!make_plan(BH, F, T, d, &b.f)) return false;
   Plan &p = b.f;
-  p.G = 1;  // one frame per group: the carry leaves S_f in place in its slot
-  p.NG = F;
+  single_frame_groups(&p);  // the carry leaves S_f in place in its slot
   const int64_t E = p.state_elems();
-  const int64_t slots = BH * F * (int64_t)p.P * E;
+  const int64_t slots = with_slots ? BH * F * (int64_t)p.P * E : 0;
   p.ws_bytes = (size_t)slots * 4;
   b.NB = (int)ceil_div(E, 256);
   b.gslot_offset = slots;
@@ -785,7 +809,7 @@ GLA_EXPORT gla_status gla_fwd_bidir(const void *q, const void *k, const void *v,
                    tv = contiguous(v, H, N, d), tg = contiguous(g, H, N, d),
                    to = contiguous(o, H, N, d);
   return run(Mode::kBidir, &tq, &tk, &tv, &tg, nullptr, nullptr, nullptr, &to, nullptr, nullptr,
-             B, H, N > 0 ? 1 : 0, N, d, dt, eps, nullptr, ws, ws_bytes, stream);
+             B, H, N > 0 ? 1 : 0, N, d, dt, eps, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_fwd_bidir_ex(const gla_tensor *q, const gla_tensor *k,
@@ -794,7 +818,7 @@ GLA_EXPORT gla_status gla_fwd_bidir_ex(const gla_tensor *q, const gla_tensor *k,
                                        gla_dtype dt, float eps, const gla_rope3d *rope, void *ws,
                                        size_t ws_bytes, void *stream) {
   return run(Mode::kBidir, q, k, v, g, nullptr, nullptr, nullptr, o, nullptr, nullptr, B, H, F,
-             T, d, dt, eps, rope, ws, ws_bytes, stream);
+             T, d, dt, eps, rope, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_fwd_framecausal(const void *q, const void *k, const void *v,
@@ -807,7 +831,7 @@ GLA_EXPORT gla_status gla_fwd_framecausal(const void *q, const void *k, const vo
                    tv = contiguous(v, H, N, d), tg = contiguous(g, H, N, d),
                    to = contiguous(o, H, N, d);
   return run(Mode::kFrameCausal, &tq, &tk, &tv, &tg, gamma, S_in, z_in, &to, S_out, z_out, B, H,
-             F, T, d, dt, eps, nullptr, ws, ws_bytes, stream);
+             F, T, d, dt, eps, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_fwd_framecausal_ex(const gla_tensor *q, const gla_tensor *k,
@@ -819,7 +843,7 @@ GLA_EXPORT gla_status gla_fwd_framecausal_ex(const gla_tensor *q, const gla_tens
                                              const gla_rope3d *rope, void *ws, size_t ws_bytes,
                                              void *stream) {
   return run(Mode::kFrameCausal, q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d,
-             dt, eps, rope, ws, ws_bytes, stream);
+             dt, eps, rope, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_state_carry(const void *k, const void *v, const float *gamma,
@@ -829,7 +853,7 @@ GLA_EXPORT gla_status gla_state_carry(const void *k, const void *v, const float 
   const int64_t N = (int64_t)std::max(F, 0) * std::max(T, 0);
   const gla_tensor tk = contiguous(k, H, N, d), tv = contiguous(v, H, N, d);
   return run(Mode::kStateCarry, nullptr, &tk, &tv, nullptr, gamma, S_in, z_in, nullptr, S_out,
-             z_out, B, H, F, T, d, dt, 0.f, nullptr, ws, ws_bytes, stream);
+             z_out, B, H, F, T, d, dt, 0.f, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *v,
@@ -839,7 +863,7 @@ GLA_EXPORT gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *
                                          const gla_rope3d *rope, void *ws, size_t ws_bytes,
                                          void *stream) {
   return run(Mode::kStateCarry, nullptr, k, v, nullptr, gamma, S_in, z_in, nullptr, S_out, z_out,
-             B, H, F, T, d, dt, 0.f, rope, ws, ws_bytes, stream);
+             B, H, F, T, d, dt, 0.f, rope, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT size_t gla_bwd_framecausal_workspace(int B, int H, int F, int T, int d) {
@@ -864,7 +888,7 @@ GLA_EXPORT gla_status gla_bwd_framecausal(const void *q, const void *k, const vo
                                           int B, int H, int F, int T, int d, gla_dtype dt,
                                           float eps, void *ws, size_t ws_bytes, void *stream) {
   return run_bwd(false, q, k, v, g, gamma, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dg, dgamma,
-                 dS_in, dz_in, B, H, F, T, d, dt, eps, ws, ws_bytes, stream);
+                 dS_in, dz_in, false, nullptr, B, H, F, T, d, dt, eps, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_bwd_bidir(const void *q, const void *k, const void *v, const void *g,
@@ -873,8 +897,41 @@ GLA_EXPORT gla_status gla_bwd_bidir(const void *q, const void *k, const void *v,
                                     size_t ws_bytes, void *stream) {
   if (N < 0) return fail(GLA_ERR_SHAPE, "N=%lld must be >= 0", (long long)N);
   return run_bwd(true, q, k, v, g, nullptr, nullptr, nullptr, dO, nullptr, nullptr, dq, dk, dv,
-                 dg, nullptr, nullptr, nullptr, B, H, N > 0 ? 1 : 0, N, d, dt, eps, ws, ws_bytes,
-                 stream);
+                 dg, nullptr, nullptr, nullptr, false, nullptr, B, H, N > 0 ? 1 : 0, N, d, dt, eps,
+                 ws, ws_bytes, stream);
+}
+
+GLA_EXPORT gla_status gla_fwd_framecausal_states(const void *q, const void *k, const void *v,
+                                                 const void *g, const float *gamma,
+                                                 const float *S_in, const float *z_in, void *o,
+                                                 float *S_out, float *z_out, float *states, int B,
+                                                 int H, int F, int T, int d, gla_dtype dt,
+                                                 float eps, void *ws, size_t ws_bytes,
+                                                 void *stream) {
+  if ((int64_t)B * H > 0 && F > 0 && !states) return fail(GLA_ERR_NULL, "states is required");
+  const int64_t N = (int64_t)std::max(F, 0) * std::max(T, 0);
+  const gla_tensor tq = contiguous(q, H, N, d), tk = contiguous(k, H, N, d),
+                   tv = contiguous(v, H, N, d), tg = contiguous(g, H, N, d),
+                   to = contiguous(o, H, N, d);
+  return run(Mode::kFrameCausal, &tq, &tk, &tv, &tg, gamma, S_in, z_in, &to, S_out, z_out, B, H,
+             F, T, d, dt, eps, nullptr, F > 0 ? states : nullptr, ws, ws_bytes, stream);
+}
+
+GLA_EXPORT size_t gla_bwd_framecausal_states_workspace(int B, int H, int F, int T, int d) {
+  BwdPlan p;
+  if (B < 0 || H < 0 || F < 0 || T < 0 || d <= 0) return 0;
+  if (!make_bwd_plan((int64_t)B * H, F, T, d, &p, false)) return 0;
+  return p.ws_bytes;
+}
+
+GLA_EXPORT gla_status gla_bwd_framecausal_states(
+    const void *q, const void *k, const void *v, const void *g, const float *gamma,
+    const float *S_in, const float *z_in, const float *states, const void *dO,
+    const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, void *dg,
+    float *dgamma, float *dS_in, float *dz_in, int B, int H, int F, int T, int d, gla_dtype dt,
+    float eps, void *ws, size_t ws_bytes, void *stream) {
+  return run_bwd(false, q, k, v, g, gamma, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dg, dgamma,
+                 dS_in, dz_in, true, states, B, H, F, T, d, dt, eps, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT size_t gla_gdn_framecausal_workspace(int B, int H, int F, int T, int d) {
@@ -917,7 +974,7 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
 
 GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
 
-GLA_EXPORT int gla_version(void) { return 10200; }
+GLA_EXPORT int gla_version(void) { return 10300; }
 
 GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
   if (max_launches < 1 || max_launches > 65536)

@@ -492,8 +492,8 @@ template <int D, bool kRope>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
     View qview, View gview, View oview, int H, const float *__restrict__ gamma,
-    const float *__restrict__ ws, int F, int64_t T, int P, int G, int64_t carry_offset, int R,
-    int64_t read_len, float eps, int state_frame, RopeK rope, int heads_fastest) {
+    const float *__restrict__ ws, const float *__restrict__ st, int64_t sstride, int F, int64_t T,
+    int G, int64_t carry_offset, int R, int64_t read_len, float eps, int state_frame, RopeK rope, int heads_fastest) {
   using C = RoCfg<D>;
   constexpr int GP = 2 * D + 16;  // bytes per LDS row of g / o
   __shared__ __attribute__((aligned(16))) char qtile[C::BLK * C::PITCH];
@@ -537,8 +537,8 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
   const int fs = state_frame >= 0 ? state_frame : f;
   constexpr int64_t E = (int64_t)D * D + D;
   const int NG = (F + G - 1) / G;
-  const float *Sg = ws + ((bh * F + fs) * (int64_t)P) * E;
-  // G == 1: the carry kernel has completed S_f in place (no carries kept)
+  const float *Sg = st + (bh * F + fs) * sstride;
+  // G == 1: the carry kernel has written S_f itself (no carries kept)
   const bool has_carry = G > 1;
   const float *Cg = ws + carry_offset + (bh * NG + fs / G) * E;
   const float w = carry_weight(gamma ? gamma + bh * F : nullptr, fs, G);
@@ -733,8 +733,9 @@ void readout_launch(const Plan &p, const ReadoutArgs &a, RopeK rope, int64_t gri
                     hipStream_t s) {
   const size_t lds = kRope ? (size_t)rope.entries() * sizeof(float2) : 0;
   hipLaunchKernelGGL((readout_kernel<D, kRope>), dim3((unsigned)grid), dim3(kThreads), lds, s,
-                     a.q, a.g, a.o, a.H, a.gamma, a.ws, p.F, p.T, p.P, p.G, p.carry_offset(),
-                     p.R, p.read_len, a.eps, a.state_frame, rope, a.heads_fastest);
+                     a.q, a.g, a.o, a.H, a.gamma, a.ws, a.states.base, a.states.stride, p.F,
+                     p.T, p.G, p.carry_offset(), p.R, p.read_len, a.eps, a.state_frame, rope,
+                     a.heads_fastest);
 }
 
 }  // namespace

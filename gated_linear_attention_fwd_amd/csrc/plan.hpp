@@ -53,10 +53,23 @@ struct Plan {
 
   int64_t state_elems() const { return (int64_t)d * d + d; }
   int64_t carry_offset() const { return BH * F * (int64_t)P * state_elems(); }  // floats
+  int64_t slot_stride() const { return (int64_t)P * state_elems(); }  // floats per frame
+};
+
+// Where the per-frame states S_f, z_f (d*d + d floats each) are read or
+// written: frame f of slab bh at base + (bh * F + f) * stride. The workspace
+// slots (part 0 of each frame, stride P (d*d + d)), or a caller's state record
+// ([B][H][F][d*d + d], stride d*d + d).
+struct FrameStates {
+  float *base;
+  int64_t stride;
 };
 
 // Cut sizes into a plan. Returns false if the sizes overflow the indexing.
 bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan);
+// One frame per kv group (no carries): the carry then writes S_f of every
+// frame. The workspace shrinks to the slots.
+void single_frame_groups(Plan *plan);
 
 // Which kernel family runs a (dtype, d) pair; the choice is a pure function of
 // them so that parity tests know what they exercise.
@@ -117,6 +130,7 @@ struct CarryArgs {
   float *S_out;        // NULL: not written
   float *z_out;
   int keep_frames;     // 1: leave what the readout needs (carries, summed parts)
+  FrameStates frames;  // G == 1 with keep_frames: where S_f goes (the slots: in place)
 };
 
 struct ReadoutArgs {
@@ -125,7 +139,8 @@ struct ReadoutArgs {
   View o;  // written
   int H;
   const float *gamma;  // NULL: no decay
-  const float *ws;
+  const float *ws;     // carries (G > 1)
+  FrameStates states;  // S_loc_f (G > 1) or S_f (G == 1)
   float eps;
   int state_frame;     // -1: every frame reads its own state; else all read this one
   RopeK rope;
@@ -157,24 +172,26 @@ __device__ __forceinline__ float carry_weight(const float *gamma_slab, int f, in
 // ---------------------------------------------------------------------------
 struct BwdPlan {
   Plan f;                    // forward recompute (G == 1), its slots first in the workspace
+                             // (none when the caller gives the states)
   int64_t gslot_offset = 0;  // floats: BH * F * R states of d*d + d
   int64_t dgp_offset = 0;    // floats: BH * F * NB partial sums of dgamma
   int NB = 0;                // reverse-scan blocks per slab, ceil((d*d + d) / 256)
   size_t ws_bytes = 0;
 };
 
-bool make_bwd_plan(int64_t BH, int F, int64_t T, int d, BwdPlan *plan);
+// with_slots false: the forward's states come from the caller (no recompute).
+bool make_bwd_plan(int64_t BH, int F, int64_t T, int d, BwdPlan *plan, bool with_slots = true);
 
 struct BwdQArgs {
   View q, g, dO, dq, dg;  // dq, dg written
   int H;
-  const float *ws;        // forward slots (S_f)
+  FrameStates st;         // the forward's S_f
   float *gs;              // gslots
   float eps;
 };
 
 struct RevScanArgs {
-  const float *ws;        // forward slots (S_f)
+  FrameStates st;         // the forward's S_f
   float *gs;              // gslots: in the frame's sums, out the adjoints in (f, 0)
   const float *gamma;     // NULL: no decay (bidirectional)
   const float *S_in, *z_in;      // NULL: zero

@@ -121,8 +121,8 @@ __global__ __launch_bounds__(kThreads) void kv_valu_kernel(View kview, View vvie
 template <typename TIn, int D, bool kRope>
 __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
     View qview, View gview, View oview, int H, const float *__restrict__ gamma,
-    const float *__restrict__ ws, int F, int64_t T, int P, int G, int64_t carry_offset, int R,
-    int64_t read_len, float eps, int state_frame, RopeK rope) {
+    const float *__restrict__ ws, const float *__restrict__ st, int64_t sstride, int F, int64_t T,
+    int G, int64_t carry_offset, int R, int64_t read_len, float eps, int state_frame, RopeK rope) {
   constexpr int CG = D / 4;             // column groups
   constexpr int TT = kThreads / CG;     // tokens per tile
   constexpr bool kSInLds = (D <= 64);
@@ -145,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void readout_valu_kernel(
   const int fs = state_frame >= 0 ? state_frame : f;
   constexpr int64_t E = (int64_t)D * D + D;
   const int NG = (F + G - 1) / G;
-  const float *Sg = ws + ((bh * F + fs) * (int64_t)P) * E;
-  // G == 1: the carry kernel has completed S_f in place (no carries kept)
+  const float *Sg = st + (bh * F + fs) * sstride;
+  // G == 1: the carry kernel has written S_f itself (no carries kept)
   const float *Cg = G > 1 ? ws + carry_offset + (bh * NG + fs / G) * E : Sg;
   const float w = G > 1 ? carry_weight(gamma ? gamma + bh * F : nullptr, fs, G) : 0.f;
   if (kSInLds)
@@ -242,12 +242,14 @@ template <typename TIn, int D>
 void readout_valu_launch(const Plan &p, const ReadoutArgs &a, int64_t grid, hipStream_t s) {
   if (a.rope.on)
     hipLaunchKernelGGL((readout_valu_kernel<TIn, D, true>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, s, a.q, a.g, a.o, a.H, a.gamma, a.ws, p.F, p.T, p.P,
-                       p.G, p.carry_offset(), p.R, p.read_len, a.eps, a.state_frame, a.rope);
+                       dim3(kThreads), 0, s, a.q, a.g, a.o, a.H, a.gamma, a.ws, a.states.base,
+                       a.states.stride, p.F, p.T, p.G, p.carry_offset(), p.R, p.read_len, a.eps,
+                       a.state_frame, a.rope);
   else
     hipLaunchKernelGGL((readout_valu_kernel<TIn, D, false>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, s, a.q, a.g, a.o, a.H, a.gamma, a.ws, p.F, p.T, p.P,
-                       p.G, p.carry_offset(), p.R, p.read_len, a.eps, a.state_frame, a.rope);
+                       dim3(kThreads), 0, s, a.q, a.g, a.o, a.H, a.gamma, a.ws, a.states.base,
+                       a.states.stride, p.F, p.T, p.G, p.carry_offset(), p.R, p.read_len, a.eps,
+                       a.state_frame, a.rope);
 }
 
 template <typename TIn>

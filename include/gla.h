@@ -140,6 +140,45 @@ gla_status gla_bwd_bidir(const void *q, const void *k, const void *v, const void
                          int64_t N, int d, gla_dtype dt, float eps, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* ---- per-frame state record (training) -------------------------------------
+ *
+ * The frame-causal forward can record the state every frame reads, so that
+ * its backward need not recompute the states from k, v and gamma (it skips
+ * the kv and carry launches: about a sixth of the backward at 720p/60s).
+ *
+ * states [B][H][F][d*d + d] float32: for frame f, S_f (d x d row-major, rows
+ * the key features) followed by z_f -- the state of the frame-causal
+ * definition above, as the tokens of frame f read it.
+ *
+ * gla_fwd_framecausal_states: gla_fwd_framecausal that also writes states
+ * (required when B*H*F > 0). The scan runs one frame at a time (the plain
+ * call folds frames in groups), so o may differ from gla_fwd_framecausal's in
+ * the last bits. Its workspace need is at most gla_fwd_framecausal_workspace.
+ *
+ * gla_bwd_framecausal_states: gla_bwd_framecausal given the states written by
+ * gla_fwd_framecausal_states for the same q, k, v, g, gamma, S_in, z_in (S_in,
+ * z_in are still read for dgamma of the first frame). The results are bitwise
+ * those of gla_bwd_framecausal. The workspace holds the adjoint sums only
+ * (gla_bwd_framecausal_states_workspace). states is an input: outputs may
+ * not overlap it. Conventions otherwise as above. */
+gla_status gla_fwd_framecausal_states(const void *q, const void *k, const void *v,
+                                      const void *g, const float *gamma, const float *S_in,
+                                      const float *z_in, void *o, float *S_out, float *z_out,
+                                      float *states, int B, int H, int F, int T, int d,
+                                      gla_dtype dt, float eps, void *ws, size_t ws_bytes,
+                                      void *stream);
+
+size_t gla_bwd_framecausal_states_workspace(int B, int H, int F, int T, int d);
+
+gla_status gla_bwd_framecausal_states(const void *q, const void *k, const void *v,
+                                      const void *g, const float *gamma, const float *S_in,
+                                      const float *z_in, const float *states, const void *dO,
+                                      const float *dS_out, const float *dz_out, void *dq,
+                                      void *dk, void *dv, void *dg, float *dgamma, float *dS_in,
+                                      float *dz_in, int B, int H, int F, int T, int d,
+                                      gla_dtype dt, float eps, void *ws, size_t ws_bytes,
+                                      void *stream);
+
 /* ---- frame-wise Gated DeltaNet ----------------------------------------------
  *
  * The other linear mixer of the pages: the SANA-WM analysis page (method
@@ -284,7 +323,8 @@ const char *gla_status_string(gla_status s);
 const char *gla_last_error(void);
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
-int gla_version(void); /* 10200: adds gla_softmax_anchor (10100: the *_ex entry points) */
+int gla_version(void); /* 10300: adds the *_states calls (10200: gla_softmax_anchor;
+                        10100: the *_ex entry points) */
 
 /* ---- kernel timing for measurement tools ---------------------------------
  * Between gla_profile_begin and gla_profile_end, every kernel launched by the

@@ -51,7 +51,7 @@ def test_status_strings(lib):
     for s in range(9):
         assert lib.gla_status_string(s).decode()
     assert lib.gla_status_string(99).decode() == "unknown status"
-    assert lib.gla_version() == 10200
+    assert lib.gla_version() == 10300
 
 
 def test_workspace_sizes(lib):
@@ -256,3 +256,52 @@ def test_anchor_validation(lib):
     assert call(Fq=0, q=0, g=0, o=0) == OK
     assert call(T=0, q=0, k=0, v=0, g=0, o=0) == OK
     assert call(Bn=0) == OK
+
+
+def test_states_workspace_sizes(lib):
+    # the backward given the states keeps only the adjoint sums: the recomputed
+    # slots (one state per slab and frame at 720p/60s) are not needed
+    E = 64 * 64 + 64
+    full = gla.gla_bwd_framecausal_workspace(1, 32, 241, 920, 64)
+    given = gla.gla_bwd_framecausal_states_workspace(1, 32, 241, 920, 64)
+    assert full - given == 32 * 241 * E * 4
+    assert gla.gla_bwd_framecausal_states_workspace(0, 32, 241, 920, 64) == 0
+    assert gla.gla_bwd_framecausal_states_workspace(1, 1, -1, 4, 64) == 0
+
+
+def test_states_validation(lib):
+    """The *_states calls: states required, aligned, and disjoint from the
+    other tensors (an output in the forward, an input in the backward)."""
+    st = FAKE + 0x9000000
+    t = [FAKE + i * 0x1000000 for i in range(9)]  # q k v g o/dO dq dk dv dg
+    gam = FAKE + 0xA000000
+    dgam = FAKE + 0xB000000
+    ws = FAKE + 0xC000000
+
+    def fwd(q=t[0], o=t[4], states=st, B=1, H=1, F=2, T=32, d=64, ws=ws, wsb=1 << 30):
+        return lib.gla_fwd_framecausal_states(
+            p(q), p(t[1]), p(t[2]), p(t[3]), p(gam), None, None, p(o), None, None, p(states),
+            B, H, F, T, d, BF16, ctypes.c_float(1e-6), p(ws), wsb, None)
+
+    def bwd(states=st, dq=t[5], B=1, H=1, F=2, T=32, d=64, ws=ws, wsb=1 << 30):
+        return lib.gla_bwd_framecausal_states(
+            p(t[0]), p(t[1]), p(t[2]), p(t[3]), p(gam), None, None, p(states), p(t[4]), None,
+            None, p(dq), p(t[6]), p(t[7]), p(t[8]), p(dgam), None, None, B, H, F, T, d, BF16,
+            ctypes.c_float(1e-6), p(ws), wsb, None)
+
+    assert fwd(states=0) == NULL
+    assert "states" in lib.gla_last_error().decode()
+    assert fwd(states=st + 8) == ALIGN
+    assert fwd(states=t[0] + 256) == ALIAS      # inside q
+    assert fwd(states=ws) == ALIAS              # the workspace
+    assert fwd(o=st) == ALIAS                   # o over the states
+    assert fwd(d=48) == UNSUP
+    assert fwd(wsb=0) == WS
+    assert fwd(B=0) == OK
+    assert bwd(states=0) == NULL
+    assert bwd(states=st + 4) == ALIGN
+    assert bwd(dq=st) == ALIAS                  # an output over the states
+    assert bwd(states=ws) == ALIAS              # the workspace over the states
+    assert bwd(wsb=16) == WS
+    assert bwd(T=-1) == SHAPE
+    assert bwd(B=0) == OK

@@ -34,6 +34,8 @@ def draw(seed, F=4, T=150, d=64):
     t["dO"] = bf(synth.bf16_bits(rng.standard_normal((1, 4, F * T, d)).astype(np.float32)))
     t["S"] = torch.from_numpy(rng.standard_normal((1, 4, d, d)).astype(np.float32)).to(DEV)
     t["z"] = torch.from_numpy(np.abs(rng.standard_normal((1, 4, d))).astype(np.float32)).to(DEV)
+    t["states"] = torch.from_numpy(
+        rng.standard_normal((1, 4, F, d * d + d)).astype(np.float32)).to(DEV)
     return t
 
 
@@ -43,6 +45,11 @@ CALLS = {
     "bidir": lambda t: gla.gla_fwd_bidir(t["q"], t["k"], t["v"], t["g"]),
     "bwd": lambda t: gla.gla_bwd_framecausal(t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"],
                                              S_in=t["S"], z_in=t["z"], need_state_grad=True),
+    "fwd_states": lambda t: gla.gla_fwd_framecausal_states(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["S"], t["z"], return_state=True),
+    "bwd_states": lambda t: gla.gla_bwd_framecausal_states(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["states"], t["dO"], S_in=t["S"], z_in=t["z"],
+        need_state_grad=True),
     "gdn": lambda t: gla.gla_gdn_framecausal(t["q"], t["k"], t["v"], t["beta"], t["gamma"],
                                              t["S"], return_state=True),
     "anchor": lambda t: gla.gla_softmax_anchor(t["q"], t["k"], t["v"], t["g"], T=150, n_sink=1,

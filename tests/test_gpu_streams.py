@@ -37,6 +37,7 @@ def inputs(F=5, T=200, d=64, seed=3):
     t["dO"] = dev(synth.bf16_bits(rng.standard_normal((1, 4, F * T, d)).astype(np.float32)))
     t["S"] = dev(rng.standard_normal((1, 4, d, d)).astype(np.float32))
     t["z"] = dev(np.abs(rng.standard_normal((1, 4, d))).astype(np.float32))
+    t["states"] = dev(rng.standard_normal((1, 4, F, d * d + d)).astype(np.float32))
     return t
 
 
@@ -52,6 +53,11 @@ CALLS = {
     "bwd": lambda t, s: gla.gla_bwd_framecausal(t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"],
                                                 S_in=t["S"], z_in=t["z"], need_state_grad=True,
                                                 stream=s),
+    "fwd_states": lambda t, s: gla.gla_fwd_framecausal_states(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["S"], t["z"], return_state=True, stream=s),
+    "bwd_states": lambda t, s: gla.gla_bwd_framecausal_states(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["states"], t["dO"], S_in=t["S"],
+        z_in=t["z"], need_state_grad=True, stream=s),
     "gdn": lambda t, s: gla.gla_gdn_framecausal(t["q"], t["k"], t["v"], t["beta"], t["gamma"],
                                                 t["S"], return_state=True, stream=s),
     "anchor": lambda t, s: gla.gla_softmax_anchor(t["q"], t["k"], t["v"], t["g"], T=200,
