@@ -31,7 +31,7 @@ constexpr int kCarryThreads = 256;
 constexpr int kGroupBatch = 16;
 
 __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
-    float *__restrict__ ws, const float *__restrict__ gamma, const float *S_in,
+    float *ws, const float *__restrict__ gamma, const float *S_in,
     const float *z_in, float *S_out, float *z_out, int F, int P, int G, int NG, int d,
     int64_t blocks_per_slab, int64_t carry_offset, int keep_frames, float *frames,
     int64_t frames_stride) {
@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   const int64_t frame_stride = (int64_t)P * E;
   float *slots = ws + bh * (int64_t)F * frame_stride + e;
   float *carry = ws + carry_offset + bh * (int64_t)NG * E + e;
-  float *dst = frames + bh * (int64_t)F * frames_stride + e;  // G == 1: S_f of frame f
+  // G == 1: S_f of frame f (may be the slots themselves: ws is not restrict)
+  float *dst = frames + bh * (int64_t)F * frames_stride + e;
   const float *gm_slab = gamma ? gamma + bh * F : nullptr;
 
   for (int g0 = 0; g0 < NG; g0 += kGroupBatch) {

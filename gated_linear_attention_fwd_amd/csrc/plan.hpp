@@ -158,7 +158,8 @@ __device__ __forceinline__ float carry_weight(const float *gamma_slab, int f, in
 // ---------------------------------------------------------------------------
 // Backward pass. Launches on the caller's stream:
 //   1. kv + carry of the forward (one frame per group: after the carry, slot
-//      (f, part 0) holds S_f itself);
+//      (f, part 0) holds S_f itself), unless the caller hands over the record
+//      of every frame's state that the forward wrote;
 //   2. bwd_q    one workgroup per (slab, frame, split): recomputes num, den,
 //               writes dg and dq, and the split's sums G = sum phi(q) dnum^T,
 //               gz = sum dden phi(q) into its "gslot";
