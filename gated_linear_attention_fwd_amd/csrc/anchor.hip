@@ -175,12 +175,10 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
   }
   int nv = nv_next;
   sync_lds();
-  // Every load issued so far (the query fragments, the first block) has
-  // landed: said explicitly, so that no path into the loop carries a pending
-  // load and the compiler does not wait for one -- by count, which would take
-  // the next block's prefetch with it -- inside the loop (720p/60s window of
-  // 4: 11.39 -> 11.2 ms; every key at 720p/5s: 3.57 -> 3.50 ms).
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt(7), lgkmcnt(15): no other wait
+  // the query fragments and the first block have landed (otherwise the wait
+  // for them sits inside the loop and takes the next block's prefetch with it:
+  // 720p/60s window of 4 11.39 -> 11.2 ms; every key at 720p/5s 3.57 -> 3.50)
+  wait_vmem_all();
   for (int b = 0; b < nb; ++b) {
     const int buf = b & 1;
     if (b + 1 < nb) load_block(b + 1);

@@ -98,12 +98,17 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
                    trow0 * dvview.sn)) +
                (int64_t)r0 * sdv + c;
   uint4 rk[C::CPT], rv[C::CPT];
+  // Rows past the part load (and later store) its last row again: every
+  // output row depends on its own token alone, and a row stored twice gets the
+  // same value. Without branches the compiler can count these loads and
+  // stores, and waits for the loads alone (the counter covers both).
   auto load = [&](int blk) {
+    const int last = L - 1 - blk * C::BLK;  // the block's last row, >= 0
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const bool ok = blk * C::BLK + r0 + i * C::ROWS_PER_PASS < L;
-      rk[i] = ok ? ld_stream16<true>(kp + i * C::ROWS_PER_PASS * snk) : make_uint4(0, 0, 0, 0);
-      rv[i] = ok ? ld_stream16<true>(vp + i * C::ROWS_PER_PASS * snv) : make_uint4(0, 0, 0, 0);
+      const int64_t row = min(r0 + i * C::ROWS_PER_PASS, last) - r0;
+      rk[i] = ld_stream16<true>(kp + row * snk);
+      rv[i] = ld_stream16<true>(vp + row * snv);
     }
     kp += C::BLK * snk;
     vp += C::BLK * snv;
@@ -115,6 +120,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
   char *otile = role_dk ? dktile : dvtile;
   const int nblk = (L + C::BLK - 1) / C::BLK;
   load(0);
+  wait_vmem_all();  // no load outstanding into the loop: its waits count its own
   for (int blk = 0; blk < nblk; ++blk) {
     sync_lds();  // the previous block's output rows have been read
 #pragma unroll
@@ -152,13 +158,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
           make_uint2(pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3]));
     }
     sync_lds();
+    {
+      const int last = L - 1 - blk * C::BLK;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int row = r0 + i * C::ROWS_PER_PASS;
-      if (blk * C::BLK + row < L) {
-        st_stream16(dkp + i * C::ROWS_PER_PASS * sdk,
+      for (int i = 0; i < C::CPT; ++i) {
+        const int row = min(r0 + i * C::ROWS_PER_PASS, last);
+        st_stream16(dkp + (int64_t)(row - r0) * sdk,
                     *reinterpret_cast<const uint4 *>(dktile + row * C::PITCH + c * 16));
-        st_stream16(dvp + i * C::ROWS_PER_PASS * sdv,
+        st_stream16(dvp + (int64_t)(row - r0) * sdv,
                     *reinterpret_cast<const uint4 *>(dvtile + row * C::PITCH + c * 16));
       }
     }
@@ -307,14 +314,19 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
                    trow0 * dgview.sn)) +
                (int64_t)r0 * sdg + c;
   uint4 rq[C::CPT], rg[C::CPT], ro[C::CPT];
+  // Rows past the split load (and later store) its last row again: their
+  // 1 / (den + eps) is set to 0 below, which zeroes dnum and dden and with
+  // them their share of G and gz, and a row stored twice gets the same value.
+  // Without branches the compiler can count these loads and stores, and waits
+  // for the loads alone (the counter covers both).
   auto load = [&](int blk) {
+    const int last = L - 1 - blk * C::BLK;  // the block's last row, >= 0
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const bool ok = blk * C::BLK + r0 + i * C::ROWS_PER_PASS < L;
-      const int64_t pass = (int64_t)i * C::ROWS_PER_PASS;
-      rq[i] = ok ? ld_stream16<true>(qp + pass * snq) : make_uint4(0, 0, 0, 0);
-      rg[i] = ok ? ld_stream16<true>(gp + pass * sng) : make_uint4(0, 0, 0, 0);
-      ro[i] = ok ? ld_stream16<true>(op + pass * sno) : make_uint4(0, 0, 0, 0);
+      const int64_t pass = min(r0 + i * C::ROWS_PER_PASS, last) - r0;
+      rq[i] = ld_stream16<true>(qp + pass * snq);
+      rg[i] = ld_stream16<true>(gp + pass * sng);
+      ro[i] = ld_stream16<true>(op + pass * sno);
     }
     qp += C::BLK * snq;
     gp += C::BLK * sng;
@@ -324,6 +336,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
   const int tl = 32 * tg + (lane & 31);
   const int nblk = (L + C::BLK - 1) / C::BLK;
   if (nblk > 0) load(0);
+  wait_vmem_all();  // no load outstanding into the loop: its waits count its own
   for (int blk = 0; blk < nblk; ++blk) {
     sync_lds();  // the previous block's tiles are consumed
     // staging, all threads: phi(q), g and dO rows; den; and dnum, which needs
@@ -510,11 +523,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       gz8[7] = fmaf(dden, hi_bf16(w.w), gz8[7]);
     }
     sync_lds();
+    {
+      const int last = L - 1 - blk * C::BLK;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int row = r0 + i * C::ROWS_PER_PASS;
-      if (blk * C::BLK + row < L) {
-        const int64_t pass = (int64_t)i * C::ROWS_PER_PASS;
+      for (int i = 0; i < C::CPT; ++i) {
+        const int row = min(r0 + i * C::ROWS_PER_PASS, last);
+        const int64_t pass = row - r0;
         st_stream16(dqp + pass * sdq, *reinterpret_cast<const uint4 *>(dqtile + row * C::PITCH + c * 16));
         st_stream16(dgp + pass * sdg, *reinterpret_cast<const uint4 *>(gtile + row * C::PITCH + c * 16));
       }

@@ -260,13 +260,17 @@ __global__ __launch_bounds__(kThreads) void gdn_readout_mfma_kernel(
                   static_cast<const uint16_t *>(oview.data) + oview.slab(bh, H) +
                   trow0 * oview.sn)) +
               (int64_t)r0 * sno + c;
-  const int64_t q_pass = C::ROWS_PER_PASS * snq, o_pass = C::ROWS_PER_PASS * sno;
   uint4 rq[C::CPT];
+  // Rows past the split load (and later store) its last row again: each o row
+  // depends on its own q row alone, and a row stored twice gets the same
+  // value. Without branches the compiler can count these loads and stores,
+  // and waits for the loads alone (the counter covers both).
   auto load = [&](int blk) {
+    const int last = L - 1 - blk * C::BLK;  // the block's last row, >= 0
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int row = blk * C::BLK + r0 + i * C::ROWS_PER_PASS;
-      rq[i] = row < L ? ld_stream16<true>(qp + i * q_pass) : make_uint4(0, 0, 0, 0);
+      const int64_t row = min(r0 + i * C::ROWS_PER_PASS, last) - r0;
+      rq[i] = ld_stream16<true>(qp + row * snq);
     }
     qp += C::BLK * snq;
   };
@@ -274,6 +278,7 @@ __global__ __launch_bounds__(kThreads) void gdn_readout_mfma_kernel(
   const int tl = 32 * tg + (lane & 31);
   const int nblk = (L + C::BLK - 1) / C::BLK;
   load(0);
+  wait_vmem_all();  // no load outstanding into the loop: its waits count its own
   for (int blk = 0; blk < nblk; ++blk) {
     sync_lds();  // the previous block's q fragments and o rows have been read
 #pragma unroll
@@ -300,11 +305,14 @@ __global__ __launch_bounds__(kThreads) void gdn_readout_mfma_kernel(
       *reinterpret_cast<uint2 *>(otile + tl * C::PITCH + (32 * mb + 8 * rg + 4 * h) * 2) = ow;
     }
     sync_lds();
+    {
+      const int last = L - 1 - blk * C::BLK;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int row = r0 + i * C::ROWS_PER_PASS;
-      if (blk * C::BLK + row < L)
-        st_stream16(op + i * o_pass, *reinterpret_cast<const uint4 *>(otile + row * C::PITCH + c * 16));
+      for (int i = 0; i < C::CPT; ++i) {
+        const int row = min(r0 + i * C::ROWS_PER_PASS, last);
+        st_stream16(op + (int64_t)(row - r0) * sno,
+                    *reinterpret_cast<const uint4 *>(otile + row * C::PITCH + c * 16));
+      }
     }
     op += C::BLK * sno;
   }

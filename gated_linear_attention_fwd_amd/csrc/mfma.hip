@@ -620,25 +620,30 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
   // order, so the addresses advance by additions only
   const uint4 *qp = qb + (int64_t)r0 * snq + c;
   const uint4 *gp = gb + (int64_t)r0 * sng + c;
-  const int64_t q_pass = C::ROWS_PER_PASS * snq, g_pass = C::ROWS_PER_PASS * sng;
   uint4 rq[C::CPT], rgv[C::CPT];
+  // Rows past the split load (and later store) its last row again: each o row
+  // depends on its own q and g rows alone, and a row stored twice gets the
+  // same value. Without branches the compiler can count these loads and
+  // stores and waits at the next block's staging for its loads alone, not for
+  // the stores too (the counter covers both): 720p/60s readout -0.5%, d = 128
+  // streaming -2%.
   auto load = [&](int blk) {
+    const int last = L - 1 - blk * C::BLK;  // the block's last row, >= 0
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int row = blk * C::BLK + r0 + i * C::ROWS_PER_PASS;
-      const bool ok = row < L;
-      rq[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(qp + i * q_pass) : make_uint4(0, 0, 0, 0);
-      rgv[i] = ok ? ld_stream16<GLA_RO_NT_LOADS>(gp + i * g_pass) : make_uint4(0, 0, 0, 0);
+      const int64_t row = min(r0 + i * C::ROWS_PER_PASS, last) - r0;
+      rq[i] = ld_stream16<GLA_RO_NT_LOADS>(qp + row * snq);
+      rgv[i] = ld_stream16<GLA_RO_NT_LOADS>(gp + row * sng);
     }
     qp += C::BLK * snq;
     gp += C::BLK * sng;
   };
   uint4 *op = ob + (int64_t)r0 * sno + c;
-  const int64_t o_pass = C::ROWS_PER_PASS * sno;
 
   const int tl = 32 * tg + (lane & 31);
   const int nblk = (L + C::BLK - 1) / C::BLK;
   load(0);
+  wait_vmem_all();  // no load outstanding into the loop: its waits count its own
   for (int blk = 0; blk < nblk; ++blk) {
     sync_lds();  // the previous block's o rows have been read out of gtile
 #pragma unroll
@@ -703,17 +708,18 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
       *cell = ow;
     }
     sync_lds();
+    {
+      const int last = L - 1 - blk * C::BLK;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int row = r0 + i * C::ROWS_PER_PASS;
-      const int tok = blk * C::BLK + row;
-      if (tok < L) {
+      for (int i = 0; i < C::CPT; ++i) {
+        const int row = min(r0 + i * C::ROWS_PER_PASS, last);
         const uint4 ov = *reinterpret_cast<const uint4 *>(gtile + row * GP + c * 16);
+        uint4 *dst = op + (int64_t)(row - r0) * sno;
         if constexpr (GLA_RO_NT_STORES != 0) {
           const u32x4 x = {ov.x, ov.y, ov.z, ov.w};
-          __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(op + i * o_pass));
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(dst));
         } else {
-          op[i * o_pass] = ov;
+          *dst = ov;
         }
       }
     }

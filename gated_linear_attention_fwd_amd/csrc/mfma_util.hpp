@@ -56,6 +56,15 @@ __device__ __forceinline__ void sync_lds() {
   asm volatile("" ::: "memory");
 }
 
+// Wait for every global load and store issued so far (vmcnt(0); expcnt and
+// lgkmcnt at their maximum: no wait). Placed in front of a tile loop whose
+// first tile was loaded ahead of it: then no path enters the loop with a load
+// outstanding. Otherwise the compiler, which counts loads and stores on one
+// counter, waits inside the loop for that load by count -- vmcnt(0) -- and so
+// each iteration waits for the previous tile's stores, or for the next tile's
+// prefetch, as well.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
