@@ -30,6 +30,10 @@ namespace {
 constexpr int kCarryThreads = 256;
 constexpr int kGroupBatch = 16;
 
+// kP > 0: frames of kP parts, their loads unrolled so that a batch's loads
+// are all in flight at once; kP == 0: any P, in a loop (720p/5s: 21 frames of
+// 4 parts took 30 us with the loop alone).
+template <int kP>
 __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     float *ws, const float *__restrict__ gamma, const float *S_in,
     const float *z_in, float *S_out, float *z_out, int F, int P, int G, int NG, int d,
@@ -56,18 +60,25 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     float w[kGroupBatch];
 #pragma unroll
     for (int j = 0; j < kGroupBatch; ++j) {
+      // groups past the end load the last group again (no branch around the
+      // loads) and are dropped
       const int grp = g0 + j;
-      x[j] = 0.f;
-      w[j] = 1.f;
-      if (grp < NG) {
-        const int last = min(F, (grp + 1) * G) - 1;
-        const float *src = slots + (int64_t)last * frame_stride;
-        float a = src[0];
+      const bool ok = grp < NG;
+      const int gc = ok ? grp : NG - 1;
+      const int last = min(F, (gc + 1) * G) - 1;
+      const float *src = slots + (int64_t)last * frame_stride;
+      float a = src[0];
+      if constexpr (kP > 0) {
+#pragma unroll
+        for (int p = 1; p < kP; ++p) a += src[(int64_t)p * E];
+      } else {
         for (int p = 1; p < P; ++p) a += src[(int64_t)p * E];
-        x[j] = a;
-        if (gm_slab)
-          for (int m = grp * G; m <= last; ++m) w[j] *= gm_slab[m];
       }
+      float wj = 1.f;
+      if (gm_slab)
+        for (int m = gc * G; m <= last; ++m) wj *= gm_slab[m];
+      x[j] = ok ? a : 0.f;
+      w[j] = ok ? wj : 1.f;
     }
 #pragma unroll
     for (int j = 0; j < kGroupBatch; ++j) {
@@ -95,10 +106,19 @@ hipError_t launch_carry(const Plan &p, const CarryArgs &a, hipStream_t stream) {
   const int64_t blocks_per_slab = (E + kCarryThreads - 1) / kCarryThreads;
   const int64_t grid = p.BH * blocks_per_slab;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)grid), dim3(kCarryThreads), 0, stream, a.ws,
-                     a.gamma, a.S_in, a.z_in, a.S_out, a.z_out, p.F, p.P, p.G, p.NG, p.d,
-                     blocks_per_slab, p.carry_offset(), a.keep_frames, a.frames.base,
-                     a.frames.stride);
+#define GLA_CARRY_LAUNCH(KP)                                                                  \
+  hipLaunchKernelGGL(carry_kernel<KP>, dim3((unsigned)grid), dim3(kCarryThreads), 0, stream,   \
+                     a.ws, a.gamma, a.S_in, a.z_in, a.S_out, a.z_out, p.F, p.P, p.G, p.NG, p.d, \
+                     blocks_per_slab, p.carry_offset(), a.keep_frames, a.frames.base,         \
+                     a.frames.stride)
+  switch (p.P) {
+    case 1: GLA_CARRY_LAUNCH(1); break;
+    case 2: GLA_CARRY_LAUNCH(2); break;
+    case 3: GLA_CARRY_LAUNCH(3); break;
+    case 4: GLA_CARRY_LAUNCH(4); break;
+    default: GLA_CARRY_LAUNCH(0); break;
+  }
+#undef GLA_CARRY_LAUNCH
   return hipGetLastError();
 }
 
