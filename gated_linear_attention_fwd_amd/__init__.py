@@ -19,6 +19,10 @@ Entry points (same names as the C ABI):
   rotary positions (:class:`Rope3D`)
 * :func:`gla_bwd_framecausal`, :func:`gla_bwd_bidir` -- the backward pass
   (dq, dk, dv, dg, dgamma and the carried-state gradients)
+* :func:`gla_fwd_framecausal_states`, :func:`gla_bwd_framecausal_states` -- the
+  forward keeping every frame's state and the backward that reads it
+* :mod:`.autograd` -- the two modes as ``torch.autograd`` functions (forward and
+  backward both through the calls above)
 * :func:`gla_gdn_framecausal` -- the frame-wise Gated DeltaNet mixer (a block
   delta-rule update per frame, keys scaled by 1/sqrt(d T))
 * ``gla_*_workspace`` -- workspace sizes in bytes
@@ -42,7 +46,8 @@ __all__ = [
     "gla_fwd_bidir_ex", "gla_fwd_framecausal_ex", "gla_state_carry_ex",
     "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace", "gla_state_carry_workspace",
     "gla_fwd_bidir_ex_workspace", "gla_bwd_framecausal", "gla_bwd_bidir",
-    "gla_bwd_framecausal_workspace", "gla_bwd_bidir_workspace", "gla_gdn_framecausal",
+    "gla_bwd_framecausal_workspace", "gla_bwd_bidir_workspace", "gla_fwd_framecausal_states",
+    "gla_bwd_framecausal_states", "gla_bwd_framecausal_states_workspace", "gla_gdn_framecausal",
     "gla_gdn_framecausal_workspace", "gla_softmax_anchor", "library_path", "load_library",
     "profile_begin", "profile_end",
 ]

@@ -305,3 +305,13 @@ def test_states_validation(lib):
     assert bwd(wsb=16) == WS
     assert bwd(T=-1) == SHAPE
     assert bwd(B=0) == OK
+
+
+def test_autograd_functions_refuse_cpu_tensors():
+    import torch
+    from gated_linear_attention_fwd_amd import autograd as ga
+    x = torch.zeros(1, 1, 32, 16, requires_grad=True)
+    with pytest.raises(ValueError, match="GPU"):
+        ga.gla_bidir(x, x, x, x)
+    with pytest.raises(ValueError, match="GPU"):
+        ga.gla_framecausal(x, x, x, x, torch.zeros(1, 1, 2))
