@@ -211,13 +211,16 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
           const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
           if (!kMasked || key < nv) mx = fmaxf(mx, s[kb][r]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * cl2;
+      mx *= cl2;
       // Lazy rescaling: the reference m_run moves (and O, l are rescaled)
       // only when some query's maximum exceeds it by more than 8 (a factor
       // 256): the probabilities stay below 2^8 and O, l keep one reference,
-      // so the result is unchanged.
+      // so the result is unchanged. The test takes each lane half's own
+      // maximum (if neither half's passes, the query's cannot), so the
+      // exchange between the halves (an LDS round trip) is needed only in the
+      // rare branch, which the whole wave takes together.
       if (__builtin_amdgcn_read_exec() & __ballot(mx > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, mx);
+        const float m_new = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)));
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
