@@ -367,8 +367,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       dp = fmaf(hi_bf16(w.z), zc[5], dp);
       dp = fmaf(lo_bf16(w.w), zc[6], dp);
       dp = fmaf(hi_bf16(w.w), zc[7], dp);
-#pragma unroll
-      for (int off = 1; off < C::ROW_CHUNKS; off <<= 1) dp += __shfl_xor(dp, off);
+      dp = group_sum<C::ROW_CHUNKS>(dp);  // over the row's pieces
       // rows past the split: 0, so that they add nothing (even with eps = 0)
       const float inv = blk * C::BLK + row < L ? 1.f / (dp + eps) : 0.f;
       if (c == 0) inv_s[row] = inv;

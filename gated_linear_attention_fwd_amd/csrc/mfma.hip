@@ -669,8 +669,7 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
       dp = fmaf(hi_bf16(w.z), zc[5], dp);
       dp = fmaf(lo_bf16(w.w), zc[6], dp);
       dp = fmaf(hi_bf16(w.w), zc[7], dp);
-#pragma unroll
-      for (int off = 1; off < C::ROW_CHUNKS; off <<= 1) dp += __shfl_xor(dp, off);
+      dp = group_sum<C::ROW_CHUNKS>(dp);  // over the row's pieces
       if (c == 0) den_s[row] = dp;
     }
     sync_lds();

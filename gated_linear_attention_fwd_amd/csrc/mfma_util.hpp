@@ -65,6 +65,27 @@ __device__ __forceinline__ void sync_lds() {
 // prefetch, as well.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                          0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of kLanes lanes (2, 4, 8 or 16), in every lane of
+// the group, by DPP moves on the vector ALU: swap neighbours and pairs within
+// quads, then mirror half-rows (lane i of 8 takes 7 - i) and rows (i of 16
+// takes 15 - i). A shuffle (__shfl_xor) goes through the LDS crossbar instead,
+// a round trip per step.
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(kLanes == 2 || kLanes == 4 || kLanes == 8 || kLanes == 16, "group of 2 to 16");
+  x = dpp_add<0xB1>(x);                           // quad_perm [1, 0, 3, 2]
+  if constexpr (kLanes >= 4) x = dpp_add<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  if constexpr (kLanes >= 8) x = dpp_add<0x141>(x);  // row_half_mirror
+  if constexpr (kLanes >= 16) x = dpp_add<0x140>(x); // row_mirror
+  return x;
+}
+
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
