@@ -191,6 +191,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
 // After the last block, G (reduced over the waves that split its k-steps) and
 // gz (reduced over the threads of a column piece) go to the split's gslot.
 // ---------------------------------------------------------------------------
+#define GLA_BQ_GROUP_BARRIER() __builtin_amdgcn_sched_barrier(0)
+
 template <int D>
 struct BqCfg {
   static constexpr int MB = D / 32;
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       dp = fmaf(hi_bf16(w.w), zc[7], dp);
       dp = group_sum<C::ROW_CHUNKS>(dp);  // over the row's pieces
       // rows past the split: 0, so that they add nothing (even with eps = 0)
-      const float inv = blk * C::BLK + row < L ? 1.f / (dp + eps) : 0.f;
+      const float inv = blk * C::BLK + row < L ? __builtin_amdgcn_rcpf(dp + eps) : 0.f;
       if (c == 0) inv_s[row] = inv;
       const uint32_t gw[4] = {rg[i].x, rg[i].y, rg[i].z, rg[i].w};
       const uint32_t ow[4] = {ro[i].x, ro[i].y, ro[i].z, ro[i].w};
@@ -400,10 +402,13 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       }
       const float inv = inv_s[tl];
       float part = 0.f;
-      // one row group at a time: unrolled, the four groups' temporaries would
-      // hold 20 more registers
-#pragma unroll 1
+      // Unrolled (a loop would index the accumulator at run time, which takes
+      // indexed register moves); a scheduling barrier after each row group
+      // keeps only one group's temporaries live, so the kernel stays within
+      // the 128 registers of 4 waves per SIMD.
+#pragma unroll
       for (int rgp = 0; rgp < 4; ++rgp) {
+        GLA_BQ_GROUP_BARRIER();
         const int off = tl * C::PITCH + (32 * mb + 8 * rgp + 4 * h) * 2;
         const uint2 gv = *reinterpret_cast<const uint2 *>(gtile + off);
         const uint2 ov = *reinterpret_cast<const uint2 *>(otile + off);
@@ -442,8 +447,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 #pragma unroll
       for (int m = 0; m < C::MB; ++m) dsum += ddp[m][tl];
       const float dden = -dsum * inv_s[tl];
-#pragma unroll 1
-      for (int rgp = 0; rgp < 4; ++rgp) {
+#pragma unroll
+      for (int rgp = 0; rgp < 4; ++rgp) {  // unrolled as above
+        GLA_BQ_GROUP_BARRIER();
         const int fo = 32 * mb + 8 * rgp + 4 * h;
         const int off = tl * C::PITCH + fo * 2;
         const uint2 qv = *reinterpret_cast<const uint2 *>(qtile + off);
