@@ -377,11 +377,23 @@ template <int D, int kMode>
 struct ScanJob {
   static constexpr int AHEAD = kMode == kWhole ? GsCfg<D>::AHEAD : 1;
   static constexpr int COLS = kMode == kTransfer ? 2 * D : D;
-  static constexpr int NWG = COLS / (16 * GsCfg<D>::NW);  // workgroups per item
+  // At d <= 64 the transfer's d x 2d columns go to twice the waves rather
+  // than to twice the workgroups: every workgroup stages each frame's A from
+  // HBM, so one workgroup per chunk reads it once (720p/60s: 379 -> 253 MB).
+  // At d = 128, 8 waves of 128 rows would spill; it keeps two workgroups.
+#ifndef GLA_SCAN_WIDE_TRANSFER
+#define GLA_SCAN_WIDE_TRANSFER 1
+#endif
+  static constexpr int NW = (kMode == kTransfer && GLA_SCAN_WIDE_TRANSFER && D <= 64)
+                                ? 2 * GsCfg<D>::NW
+                                : GsCfg<D>::NW;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int APT = D * D / (4 * THREADS);  // float4 pieces of A_f per thread
+  static constexpr int NWG = COLS / (16 * NW);       // workgroups per item
 };
 
 template <int D, int kMode>
-__global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
+__global__ __launch_bounds__((ScanJob<D, kMode>::THREADS)) void gdn_scan_mfma_kernel(
     float *__restrict__ ws, const float *__restrict__ gamma, const float *S_in, float *S_out,
     int F, int P, float key_scale, int Fc, int nc, float *__restrict__ tws,
     float *__restrict__ sws) {
@@ -401,7 +413,7 @@ __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
   const int chunk = per_chunk ? (int)(item % nc) : 0;
   const int f0 = per_chunk ? chunk * Fc : 0;
   const int nsteps = kMode == kChain ? nc : (per_chunk ? min(Fc, F - f0) : F);
-  const int cx = 16 * (cb * C::NW + wave) + n;  // the lane's column of X (< COLS)
+  const int cx = 16 * (cb * J::NW + wave) + n;  // the lane's column of X (< COLS)
   const bool right = kMode == kTransfer && cx >= D;  // a column of the transfer matrix
   const int col = cx % D;                            // its column within a d x d matrix
   const float c1 = key_scale, c2 = key_scale * key_scale;
@@ -428,7 +440,7 @@ __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
 
   // a step's A (this thread's pieces), U (the lane's values) and gamma
   struct Frame {
-    float4 a[C::APT];
+    float4 a[J::APT];
     f32x4 u[C::RB];
     float g;
   };
@@ -447,8 +459,8 @@ __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
       amat = umat + DD;
     }
 #pragma unroll
-    for (int it = 0; it < C::APT; ++it) {
-      const int x = tid + C::THREADS * it;
+    for (int it = 0; it < J::APT; ++it) {
+      const int x = tid + J::THREADS * it;
       b.a[it] = *reinterpret_cast<const float4 *>(amat + (x / (D / 4)) * D + 4 * (x % (D / 4)));
     }
 #pragma unroll
@@ -463,8 +475,8 @@ __global__ __launch_bounds__(GsCfg<D>::THREADS) void gdn_scan_mfma_kernel(
   auto step = [&](int t, Frame &b, int t_next) {
     sync_lds();  // the previous step's A reads are done
 #pragma unroll
-    for (int it = 0; it < C::APT; ++it) {
-      const int x = tid + C::THREADS * it;
+    for (int it = 0; it < J::APT; ++it) {
+      const int x = tid + J::THREADS * it;
       const int off = (x / (D / 4)) * C::PITCH + 2 * scan_perm(4 * (x % (D / 4)));
       uint32_t h0, l0, h1, l1;
       split2(b.a[it].x, b.a[it].y, h0, l0);
@@ -570,10 +582,10 @@ __global__ __launch_bounds__(kThreads) void gdn_sum_parts_kernel(float *__restri
 
 template <int D, int kMode>
 void gdn_scan_run(const Plan &p, const GdnScanArgs &a, int64_t items, hipStream_t s) {
-  using C = GsCfg<D>;
   float *tws = a.ws + p.scan_tws, *sws = a.ws + p.scan_sws;
   hipLaunchKernelGGL((gdn_scan_mfma_kernel<D, kMode>),
-                     dim3((unsigned)(items * ScanJob<D, kMode>::NWG)), dim3(C::THREADS), 0, s,
+                     dim3((unsigned)(items * ScanJob<D, kMode>::NWG)),
+                     dim3(ScanJob<D, kMode>::THREADS), 0, s,
                      a.ws, a.gamma, a.S_in, a.S_out, p.F, p.P, a.key_scale, p.scan_fc, p.scan_nc,
                      tws, sws);
 }
