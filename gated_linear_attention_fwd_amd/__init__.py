@@ -47,7 +47,8 @@ __all__ = [
     "gla_fwd_bidir_workspace", "gla_fwd_framecausal_workspace", "gla_state_carry_workspace",
     "gla_fwd_bidir_ex_workspace", "gla_bwd_framecausal", "gla_bwd_bidir",
     "gla_bwd_framecausal_workspace", "gla_bwd_bidir_workspace", "gla_fwd_framecausal_states",
-    "gla_bwd_framecausal_states", "gla_bwd_framecausal_states_workspace", "gla_gdn_framecausal",
+    "gla_bwd_framecausal_states", "gla_bwd_framecausal_states_workspace",
+    "gla_fwd_framecausal_states_ex", "gla_bwd_framecausal_ex", "gla_gdn_framecausal",
     "gla_gdn_framecausal_workspace", "gla_softmax_anchor", "library_path", "load_library",
     "profile_begin", "profile_end",
 ]
@@ -159,6 +160,12 @@ def load_library():
     lib.gla_bwd_framecausal_states_workspace.restype = sz
     lib.gla_bwd_framecausal_states.argtypes = [vp] * 18 + [i32] * 6 + [f32, vp, sz, vp]
     lib.gla_bwd_framecausal_states.restype = i32
+    lib.gla_fwd_framecausal_states_ex.argtypes = [tp, tp, tp, tp, vp, vp, vp, tp, vp, vp, vp] + \
+        [i32] * 6 + [f32, vp, sz, vp]
+    lib.gla_fwd_framecausal_states_ex.restype = i32
+    lib.gla_bwd_framecausal_ex.argtypes = [tp, tp, tp, tp, vp, vp, vp, vp, tp, vp, vp, tp, tp, tp,
+                                           tp, vp, vp, vp] + [i32] * 6 + [f32, vp, sz, vp]
+    lib.gla_bwd_framecausal_ex.restype = i32
     lib.gla_gdn_framecausal_workspace.argtypes = [i32, i32, i32, i32, i32]
     lib.gla_gdn_framecausal_workspace.restype = sz
     lib.gla_gdn_framecausal.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp, sz, vp]
@@ -509,6 +516,51 @@ def gla_fwd_framecausal_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     return (o, S_out, z_out) if want_state else o
 
 
+def gla_fwd_framecausal_states_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  g: torch.Tensor, gamma: torch.Tensor,
+                                  S_in: Optional[torch.Tensor] = None,
+                                  z_in: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                                  out: Optional[torch.Tensor] = None,
+                                  states: Optional[torch.Tensor] = None,
+                                  S_out: Optional[torch.Tensor] = None,
+                                  z_out: Optional[torch.Tensor] = None,
+                                  return_state: bool = False,
+                                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """gla_fwd_framecausal_states on views of any layout with a contiguous
+    feature axis (no rotary positions). Returns ``(o, states)`` or
+    ``(o, states, S_out, z_out)``."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    want_state = return_state or S_out is not None or z_out is not None
+    if want_state and S_out is None:
+        S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
+    if want_state and z_out is None:
+        z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    if states is None:
+        states = torch.empty((B, H, F, d * d + d), dtype=torch.float32, device=ref.device)
+    elif states.shape != (B, H, F, d * d + d) or states.dtype != torch.float32:
+        raise ValueError("states must be float32 [B, H, F, d*d + d]")
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != ref.shape or o.dtype != ref.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    dev = _require_device_any_layout(q, k, v, g, gamma, S_in, z_in, o, states, S_out, z_out,
+                                     workspace)
+    ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
+    _check(lib.gla_fwd_framecausal_states_ex(
+        _view(q), _view(k), _view(v), _view(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _view(o),
+        _ptr(S_out), _ptr(z_out), _ptr(states), B, H, F, T, d, dt, eps, _ptr(ws), wsb,
+        _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in, o, states, S_out, z_out, ws)))
+    return (o, states, S_out, z_out) if want_state else (o, states)
+
+
 def gla_state_carry_ex(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
                        S_in: Optional[torch.Tensor] = None, z_in: Optional[torch.Tensor] = None,
                        S_out: Optional[torch.Tensor] = None, z_out: Optional[torch.Tensor] = None,
@@ -576,6 +628,62 @@ def gla_bwd_framecausal_states(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     for the same inputs (no recompute; bitwise the same gradients)."""
     return _bwd_framecausal(q, k, v, g, gamma, states, dO, S_in, z_in, dS_out, dz_out, eps,
                             need_state_grad, out, workspace, stream)
+
+
+def gla_bwd_framecausal_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                           gamma: torch.Tensor, dO: torch.Tensor,
+                           states: Optional[torch.Tensor] = None,
+                           S_in: Optional[torch.Tensor] = None,
+                           z_in: Optional[torch.Tensor] = None,
+                           dS_out: Optional[torch.Tensor] = None,
+                           dz_out: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                           need_state_grad: Optional[bool] = None, out: Optional[dict] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """The frame-causal backward on views of any layout with a contiguous
+    feature axis (e.g. q, k, v slices of a fused [B, N, 3, H, d] projection);
+    ``states``: the record of gla_fwd_framecausal_states(_ex), or None to
+    recompute. ``out`` may supply dq, dk, dv, dg (views too; they may not
+    overlap one another) and the fp32 gradients; missing ones are allocated
+    contiguous."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g, dO)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    if states is not None and (states.shape != (B, H, F, d * d + d)
+                               or states.dtype != torch.float32):
+        raise ValueError("states must be float32 [B, H, F, d*d + d]")
+    if need_state_grad is None:
+        need_state_grad = S_in is not None or dS_out is not None
+    out = dict(out or {})
+    for n in ("dq", "dk", "dv", "dg"):
+        out.setdefault(n, torch.empty(ref.shape, dtype=ref.dtype, device=ref.device))
+        if out[n].shape != ref.shape or out[n].dtype != ref.dtype:
+            raise ValueError("%s must match q's shape and dtype" % n)
+    out.setdefault("dgamma", torch.empty((B, H, F), dtype=torch.float32, device=ref.device))
+    if need_state_grad:
+        out.setdefault("dS_in", torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device))
+        out.setdefault("dz_in", torch.empty((B, H, d), dtype=torch.float32, device=ref.device))
+    dev = _require_device_any_layout(q, k, v, g, gamma, states, dO, S_in, z_in, dS_out, dz_out,
+                                     workspace, *out.values())
+    if states is None:
+        nbytes = lib.gla_bwd_framecausal_workspace(B, H, F, T, d)
+    else:
+        nbytes = lib.gla_bwd_framecausal_states_workspace(B, H, F, T, d)
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    _check(lib.gla_bwd_framecausal_ex(
+        _view(q), _view(k), _view(v), _view(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _ptr(states),
+        _view(dO), _ptr(dS_out), _ptr(dz_out), _view(out["dq"]), _view(out["dk"]),
+        _view(out["dv"]), _view(out["dg"]), _ptr(out["dgamma"]), _ptr(out.get("dS_in")),
+        _ptr(out.get("dz_in")), B, H, F, T, d, dt, eps, _ptr(ws), wsb,
+        _stream_handle(stream, dev, q, k, v, g, gamma, states, S_in, z_in, dO, dS_out, dz_out,
+                       out, ws)))
+    return out
 
 
 def gla_bwd_framecausal_states_workspace(B: int, H: int, F: int, T: int, d: int) -> int:

@@ -1,10 +1,12 @@
 """The gated linear-attention mixer as ``torch.autograd`` functions.
 
 Both directions run in ``libgla.so``: the forward through
-:func:`gla_fwd_framecausal_states` (or :func:`gla_fwd_framecausal`) and
-:func:`gla_fwd_bidir`, the backward through :func:`gla_bwd_framecausal_states`
-(or :func:`gla_bwd_framecausal`) and :func:`gla_bwd_bidir`. These classes only
-route tensors between autograd and those calls.
+:func:`gla_fwd_framecausal_states_ex` (or :func:`gla_fwd_framecausal_ex`) and
+:func:`gla_fwd_bidir`, the backward through :func:`gla_bwd_framecausal_ex` and
+:func:`gla_bwd_bidir`. These classes only route tensors between autograd and
+those calls. Frame-causal q, k, v, g may be any [B, H, N, d] views with a
+contiguous feature axis (e.g. slices of a fused projection): neither direction
+copies them.
 
 Frame-causal mode keeps, by default, every frame's state from the forward
 ([B, H, F, d*d + d] float32, 128 MB per call at the 720p/60s shape with
@@ -17,8 +19,8 @@ from typing import Optional
 
 import torch
 
-from . import (gla_bwd_bidir, gla_bwd_framecausal, gla_bwd_framecausal_states, gla_fwd_bidir,
-               gla_fwd_framecausal, gla_fwd_framecausal_states)
+from . import (gla_bwd_bidir, gla_bwd_framecausal_ex, gla_fwd_bidir, gla_fwd_framecausal_ex,
+               gla_fwd_framecausal_states_ex)
 
 __all__ = ["FrameCausal", "Bidirectional", "gla_framecausal", "gla_bidir"]
 
@@ -29,11 +31,14 @@ class FrameCausal(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, gamma, S_in, z_in, eps: float, save_states: bool):
         if save_states:
-            o, states, S_out, z_out = gla_fwd_framecausal_states(
-                q, k, v, g, gamma, S_in, z_in, eps=eps, return_state=True)
+            o, states, S_out, z_out = gla_fwd_framecausal_states_ex(
+                q, k, v, g, gamma, S_in, z_in, eps=eps, out=torch.empty(q.shape, dtype=q.dtype,
+                                                                        device=q.device),
+                return_state=True)
         else:
-            o, S_out, z_out = gla_fwd_framecausal(q, k, v, g, gamma, S_in, z_in, eps=eps,
-                                                  return_state=True)
+            o, S_out, z_out = gla_fwd_framecausal_ex(
+                q, k, v, g, gamma, S_in, z_in, eps=eps,
+                out=torch.empty(q.shape, dtype=q.dtype, device=q.device), return_state=True)
             states = None
         ctx.save_for_backward(q, k, v, g, gamma, S_in, z_in, states)
         ctx.eps = eps
@@ -52,13 +57,9 @@ class FrameCausal(torch.autograd.Function):
         if dz_out is None and dS_out is not None:
             dz_out = torch.zeros((B, H, d), dtype=torch.float32, device=q.device)
         need_state = S_in is not None and (ctx.needs_input_grad[5] or ctx.needs_input_grad[6])
-        args = (q, k, v, g, gamma)
-        kw = dict(S_in=S_in, z_in=z_in, dS_out=dS_out, dz_out=dz_out, eps=ctx.eps,
-                  need_state_grad=need_state)
-        if states is not None:
-            grads = gla_bwd_framecausal_states(*args, states, dO.contiguous(), **kw)
-        else:
-            grads = gla_bwd_framecausal(*args, dO.contiguous(), **kw)
+        grads = gla_bwd_framecausal_ex(q, k, v, g, gamma, dO.contiguous(), states=states,
+                                       S_in=S_in, z_in=z_in, dS_out=dS_out, dz_out=dz_out,
+                                       eps=ctx.eps, need_state_grad=need_state)
         return (grads["dq"], grads["dk"], grads["dv"], grads["dg"], grads["dgamma"],
                 grads.get("dS_in"), grads.get("dz_in"), None, None)
 
@@ -83,8 +84,9 @@ def gla_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
                     gamma: torch.Tensor, S_in: Optional[torch.Tensor] = None,
                     z_in: Optional[torch.Tensor] = None, eps: float = 1e-6,
                     save_states: bool = True, return_state: bool = False):
-    """Differentiable frame-causal gated linear attention ([B, H, F*T, d] contiguous
-    q, k, v, g; gamma float32 [B, H, F]; optional carried S_in, z_in).
+    """Differentiable frame-causal gated linear attention (q, k, v, g any
+    [B, H, F*T, d] views with a contiguous feature axis; gamma float32
+    [B, H, F]; optional carried S_in, z_in).
 
     Returns o, or (o, S_out, z_out) with ``return_state``; gradients reach q,
     k, v, g, gamma and S_in, z_in."""

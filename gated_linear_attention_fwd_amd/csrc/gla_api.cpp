@@ -391,12 +391,13 @@ gla_tensor contiguous(const void *p, int H, int64_t N, int d) {
 }
 
 // The body of the two backward entry points (contiguous [B][H][N][d] tensors).
-gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, const void *g,
-                   const float *gamma, const float *S_in, const float *z_in, const void *dO,
-                   const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv,
-                   void *dg, float *dgamma, float *dS_in, float *dz_in, bool want_states,
-                   const float *states, int B, int H, int F, int64_t T, int d, gla_dtype dt,
-                   float eps, void *ws, size_t ws_bytes, void *stream) {
+gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const gla_tensor *v,
+                   const gla_tensor *g, const float *gamma, const float *S_in, const float *z_in,
+                   const gla_tensor *dO, const float *dS_out, const float *dz_out,
+                   const gla_tensor *dq, const gla_tensor *dk, const gla_tensor *dv,
+                   const gla_tensor *dg, float *dgamma, float *dS_in, float *dz_in,
+                   bool want_states, const float *states, int B, int H, int F, int64_t T, int d,
+                   gla_dtype dt, float eps, void *ws, size_t ws_bytes, void *stream) {
   GLA_TRY(check_dims(B, H, d, dt));
   if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%lld must be >= 0", F, (long long)T);
   GLA_TRY(check_eps(eps));
@@ -410,14 +411,25 @@ gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, cons
   const int64_t BH = (int64_t)B * H;
   const int64_t N = (int64_t)F * T;
   const bool have_tokens = BH > 0 && N > 0;
-  if (have_tokens && (!q || !k || !v || !g || !dO))
+  const size_t es = dt == GLA_F32 ? 4 : 2;
+  // token tensors: any [B][H][N][d] view with unit feature stride (outputs
+  // may not overlap themselves); each view's span enters the overlap checks
+  View vq, vk, vv, vg, vdo, vdq, vdk, vdv, vdg;
+  Range rq, rk, rv, rg, rdo, rdq, rdk, rdv, rdg;
+  GLA_TRY(check_view(q, "q", B, H, N, d, es, false, &vq, &rq));
+  GLA_TRY(check_view(k, "k", B, H, N, d, es, false, &vk, &rk));
+  GLA_TRY(check_view(v, "v", B, H, N, d, es, false, &vv, &rv));
+  GLA_TRY(check_view(g, "g", B, H, N, d, es, false, &vg, &rg));
+  GLA_TRY(check_view(dO, "dO", B, H, N, d, es, false, &vdo, &rdo));
+  GLA_TRY(check_view(dq, "dq", B, H, N, d, es, true, &vdq, &rdq));
+  GLA_TRY(check_view(dk, "dk", B, H, N, d, es, true, &vdk, &rdk));
+  GLA_TRY(check_view(dv, "dv", B, H, N, d, es, true, &vdv, &rdv));
+  GLA_TRY(check_view(dg, "dg", B, H, N, d, es, true, &vdg, &rdg));
+  if (have_tokens && (!vq.data || !vk.data || !vv.data || !vg.data || !vdo.data))
     return fail(GLA_ERR_NULL, "q, k, v, g and dO are required");
-  if (have_tokens && (!dq || !dk || !dv || !dg))
+  if (have_tokens && (!vdq.data || !vdk.data || !vdv.data || !vdg.data))
     return fail(GLA_ERR_NULL, "dq, dk, dv and dg are required");
   if (!bidir && BH > 0 && F > 0 && !gamma) return fail(GLA_ERR_NULL, "gamma is required when F > 0");
-  const void *tens[] = {q, k, v, g, dO, dq, dk, dv, dg};
-  const char *tnames[] = {"q", "k", "v", "g", "dO", "dq", "dk", "dv", "dg"};
-  for (int i = 0; i < 9; ++i) GLA_TRY(check_tensor_align(tens[i], tnames[i]));
   const float *st[] = {S_in, z_in, dS_out, dz_out, dS_in, dz_in};
   const char *snames[] = {"S_in", "z_in", "dS_out", "dz_out", "dS_in", "dz_in"};
   for (int i = 0; i < 6; ++i) GLA_TRY(check_tensor_align(st[i], snames[i]));
@@ -436,24 +448,22 @@ gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, cons
       return fail(GLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, bp.ws_bytes);
     if (!aligned(ws, 256)) return fail(GLA_ERR_ALIGN, "workspace is not 256-byte aligned");
   }
-  const size_t es = dt == GLA_F32 ? 4 : 2;
-  const size_t tb = (size_t)(BH * N * d) * es;
   const size_t sbytes = (size_t)(BH * d * d) * 4, zbytes = (size_t)(BH * d) * 4;
   const bool causal = !bidir;
-  const Range all[] = {{q, tb, "q"},
-                       {k, tb, "k"},
-                       {v, tb, "v"},
-                       {g, tb, "g"},
-                       {dO, tb, "dO"},
+  const Range all[] = {rq,
+                       rk,
+                       rv,
+                       rg,
+                       rdo,
                        {gamma, causal ? (size_t)(BH * F) * 4 : 0, "gamma"},
                        {S_in, causal ? sbytes : 0, "S_in"},
                        {z_in, causal ? zbytes : 0, "z_in"},
                        {dS_out, causal ? sbytes : 0, "dS_out"},
                        {dz_out, causal ? zbytes : 0, "dz_out"},
-                       {dq, tb, "dq"},
-                       {dk, tb, "dk"},
-                       {dv, tb, "dv"},
-                       {dg, tb, "dg"},
+                       rdq,
+                       rdk,
+                       rdv,
+                       rdg,
                        {dgamma, causal ? (size_t)(BH * F) * 4 : 0, "dgamma"},
                        {dS_in, causal ? sbytes : 0, "dS_in"},
                        {dz_in, causal ? zbytes : 0, "dz_in"},
@@ -467,11 +477,6 @@ gla_status run_bwd(bool bidir, const void *q, const void *k, const void *v, cons
   float *gsf = wsf + bp.gslot_offset;
   const Plan &p = bp.f;
   const float *gm = causal ? gamma : nullptr;
-  const View vq = contiguous_view(q, H, N, d), vk = contiguous_view(k, H, N, d),
-             vv = contiguous_view(v, H, N, d), vg = contiguous_view(g, H, N, d),
-             vdo = contiguous_view(dO, H, N, d), vdq = contiguous_view(dq, H, N, d),
-             vdk = contiguous_view(dk, H, N, d), vdv = contiguous_view(dv, H, N, d),
-             vdg = contiguous_view(dg, H, N, d);
   // the forward's S_f: recomputed into the workspace slots, or the caller's record
   const FrameStates fst = want_states
                               ? FrameStates{const_cast<float *>(states), p.state_elems()}
@@ -887,8 +892,13 @@ GLA_EXPORT gla_status gla_bwd_framecausal(const void *q, const void *k, const vo
                                           void *dg, float *dgamma, float *dS_in, float *dz_in,
                                           int B, int H, int F, int T, int d, gla_dtype dt,
                                           float eps, void *ws, size_t ws_bytes, void *stream) {
-  return run_bwd(false, q, k, v, g, gamma, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dg, dgamma,
-                 dS_in, dz_in, false, nullptr, B, H, F, T, d, dt, eps, ws, ws_bytes, stream);
+  const int64_t N = (int64_t)std::max(F, 0) * std::max(T, 0);
+  const gla_tensor t[9] = {contiguous(q, H, N, d),  contiguous(k, H, N, d),  contiguous(v, H, N, d),
+                           contiguous(g, H, N, d),  contiguous(dO, H, N, d), contiguous(dq, H, N, d),
+                           contiguous(dk, H, N, d), contiguous(dv, H, N, d), contiguous(dg, H, N, d)};
+  return run_bwd(false, &t[0], &t[1], &t[2], &t[3], gamma, S_in, z_in, &t[4], dS_out, dz_out,
+                 &t[5], &t[6], &t[7], &t[8], dgamma, dS_in, dz_in, false, nullptr, B, H, F, T, d,
+                 dt, eps, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_bwd_bidir(const void *q, const void *k, const void *v, const void *g,
@@ -896,9 +906,12 @@ GLA_EXPORT gla_status gla_bwd_bidir(const void *q, const void *k, const void *v,
                                     int H, int64_t N, int d, gla_dtype dt, float eps, void *ws,
                                     size_t ws_bytes, void *stream) {
   if (N < 0) return fail(GLA_ERR_SHAPE, "N=%lld must be >= 0", (long long)N);
-  return run_bwd(true, q, k, v, g, nullptr, nullptr, nullptr, dO, nullptr, nullptr, dq, dk, dv,
-                 dg, nullptr, nullptr, nullptr, false, nullptr, B, H, N > 0 ? 1 : 0, N, d, dt, eps,
-                 ws, ws_bytes, stream);
+  const gla_tensor t[9] = {contiguous(q, H, N, d),  contiguous(k, H, N, d),  contiguous(v, H, N, d),
+                           contiguous(g, H, N, d),  contiguous(dO, H, N, d), contiguous(dq, H, N, d),
+                           contiguous(dk, H, N, d), contiguous(dv, H, N, d), contiguous(dg, H, N, d)};
+  return run_bwd(true, &t[0], &t[1], &t[2], &t[3], nullptr, nullptr, nullptr, &t[4], nullptr,
+                 nullptr, &t[5], &t[6], &t[7], &t[8], nullptr, nullptr, nullptr, false, nullptr, B,
+                 H, N > 0 ? 1 : 0, N, d, dt, eps, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_fwd_framecausal_states(const void *q, const void *k, const void *v,
@@ -930,8 +943,35 @@ GLA_EXPORT gla_status gla_bwd_framecausal_states(
     const float *dS_out, const float *dz_out, void *dq, void *dk, void *dv, void *dg,
     float *dgamma, float *dS_in, float *dz_in, int B, int H, int F, int T, int d, gla_dtype dt,
     float eps, void *ws, size_t ws_bytes, void *stream) {
+  const int64_t N = (int64_t)std::max(F, 0) * std::max(T, 0);
+  const gla_tensor t[9] = {contiguous(q, H, N, d),  contiguous(k, H, N, d),  contiguous(v, H, N, d),
+                           contiguous(g, H, N, d),  contiguous(dO, H, N, d), contiguous(dq, H, N, d),
+                           contiguous(dk, H, N, d), contiguous(dv, H, N, d), contiguous(dg, H, N, d)};
+  return run_bwd(false, &t[0], &t[1], &t[2], &t[3], gamma, S_in, z_in, &t[4], dS_out, dz_out,
+                 &t[5], &t[6], &t[7], &t[8], dgamma, dS_in, dz_in, true, states, B, H, F, T, d, dt,
+                 eps, ws, ws_bytes, stream);
+}
+
+GLA_EXPORT gla_status gla_fwd_framecausal_states_ex(
+    const gla_tensor *q, const gla_tensor *k, const gla_tensor *v, const gla_tensor *g,
+    const float *gamma, const float *S_in, const float *z_in, const gla_tensor *o, float *S_out,
+    float *z_out, float *states, int B, int H, int F, int T, int d, gla_dtype dt, float eps,
+    void *ws, size_t ws_bytes, void *stream) {
+  if ((int64_t)B * H > 0 && F > 0 && !states) return fail(GLA_ERR_NULL, "states is required");
+  return run(Mode::kFrameCausal, q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d,
+             dt, eps, nullptr, F > 0 ? states : nullptr, ws, ws_bytes, stream);
+}
+
+GLA_EXPORT gla_status gla_bwd_framecausal_ex(
+    const gla_tensor *q, const gla_tensor *k, const gla_tensor *v, const gla_tensor *g,
+    const float *gamma, const float *S_in, const float *z_in, const float *states,
+    const gla_tensor *dO, const float *dS_out, const float *dz_out, const gla_tensor *dq,
+    const gla_tensor *dk, const gla_tensor *dv, const gla_tensor *dg, float *dgamma,
+    float *dS_in, float *dz_in, int B, int H, int F, int T, int d, gla_dtype dt, float eps,
+    void *ws, size_t ws_bytes, void *stream) {
   return run_bwd(false, q, k, v, g, gamma, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dg, dgamma,
-                 dS_in, dz_in, true, states, B, H, F, T, d, dt, eps, ws, ws_bytes, stream);
+                 dS_in, dz_in, states != nullptr, states, B, H, F, T, d, dt, eps, ws, ws_bytes,
+                 stream);
 }
 
 GLA_EXPORT size_t gla_gdn_framecausal_workspace(int B, int H, int F, int T, int d) {
@@ -974,7 +1014,7 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
 
 GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
 
-GLA_EXPORT int gla_version(void) { return 10300; }
+GLA_EXPORT int gla_version(void) { return 10400; }
 
 GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
   if (max_launches < 1 || max_launches > 65536)

@@ -316,6 +316,40 @@ gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *v, const fl
                               int B, int H, int F, int T, int d, gla_dtype dt,
                               const gla_rope3d *rope, void *ws, size_t ws_bytes, void *stream);
 
+/* Training on strided tensors (no rotary positions): gla_fwd_framecausal_states
+ * and the frame-causal backward on views, e.g. q, k, v read straight from a
+ * fused [B, N, 3, H, d] projection without copies.
+ *
+ * gla_fwd_framecausal_states_ex: gla_fwd_framecausal_states with q, k, v, g,
+ * o as views (o may not overlap itself or any input); the workspace of
+ * gla_fwd_framecausal_workspace suffices.
+ *
+ * gla_bwd_framecausal_ex: the backward on views -- q, k, v, g, dO inputs; dq,
+ * dk, dv, dg outputs, which may not overlap themselves, one another (each
+ * view's span from its first to its last element counts, so gradients
+ * interleaved in one fused buffer are refused with GLA_ERR_ALIAS), any input
+ * or the workspace. states NULL: the states are recomputed (workspace
+ * gla_bwd_framecausal_workspace); else the record written by
+ * gla_fwd_framecausal_states(_ex) for the same inputs (workspace
+ * gla_bwd_framecausal_states_workspace). Results are bitwise those of the
+ * contiguous calls on copies of the same tensors. */
+gla_status gla_fwd_framecausal_states_ex(const gla_tensor *q, const gla_tensor *k,
+                                         const gla_tensor *v, const gla_tensor *g,
+                                         const float *gamma, const float *S_in, const float *z_in,
+                                         const gla_tensor *o, float *S_out, float *z_out,
+                                         float *states, int B, int H, int F, int T, int d,
+                                         gla_dtype dt, float eps, void *ws, size_t ws_bytes,
+                                         void *stream);
+
+gla_status gla_bwd_framecausal_ex(const gla_tensor *q, const gla_tensor *k, const gla_tensor *v,
+                                  const gla_tensor *g, const float *gamma, const float *S_in,
+                                  const float *z_in, const float *states, const gla_tensor *dO,
+                                  const float *dS_out, const float *dz_out, const gla_tensor *dq,
+                                  const gla_tensor *dk, const gla_tensor *dv,
+                                  const gla_tensor *dg, float *dgamma, float *dS_in,
+                                  float *dz_in, int B, int H, int F, int T, int d, gla_dtype dt,
+                                  float eps, void *ws, size_t ws_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *gla_status_string(gla_status s);
 
@@ -323,8 +357,9 @@ const char *gla_status_string(gla_status s);
 const char *gla_last_error(void);
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
-int gla_version(void); /* 10300: adds the *_states calls (10200: gla_softmax_anchor;
-                        10100: the *_ex entry points) */
+int gla_version(void); /* 10400: adds gla_fwd_framecausal_states_ex and
+                        gla_bwd_framecausal_ex (10300: the *_states calls; 10200:
+                        gla_softmax_anchor; 10100: the *_ex entry points) */
 
 /* ---- kernel timing for measurement tools ---------------------------------
  * Between gla_profile_begin and gla_profile_end, every kernel launched by the

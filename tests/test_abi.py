@@ -51,7 +51,7 @@ def test_status_strings(lib):
     for s in range(9):
         assert lib.gla_status_string(s).decode()
     assert lib.gla_status_string(99).decode() == "unknown status"
-    assert lib.gla_version() == 10300
+    assert lib.gla_version() == 10400
 
 
 def test_workspace_sizes(lib):
@@ -315,3 +315,39 @@ def test_autograd_functions_refuse_cpu_tensors():
         ga.gla_bidir(x, x, x, x)
     with pytest.raises(ValueError, match="GPU"):
         ga.gla_framecausal(x, x, x, x, torch.zeros(1, 1, 2))
+
+
+def test_strided_training_validation(lib):
+    """The strided training calls: gradients may not overlap one another, also
+    when interleaved in one fused buffer (their spans overlap)."""
+    H, N, d = 2, 64, 64
+    es = 2
+    fused = FAKE + 0x1000000  # a [1, N, 3, H, d] buffer: three interleaved views
+
+    def view(base, off, sb, sh, sn):
+        return ctypes.byref(gla._Tensor(base + off * es, sb, sh, sn))
+
+    contig = lambda base: view(base, 0, H * N * d, N * d, d)  # noqa: E731
+    inter = lambda i: view(fused, i * H * d, N * 3 * H * d, d, 3 * H * d)  # noqa: E731
+
+    def bwd(dq, dk, states=None, wsb=1 << 30):
+        return lib.gla_bwd_framecausal_ex(
+            inter(0), inter(1), inter(2), contig(FAKE + 0x2000000), p(FAKE + 0x3000000), None,
+            None, p(states), contig(FAKE + 0x4000000), None, None, dq, dk,
+            contig(FAKE + 0x5000000), contig(FAKE + 0x6000000), None, None, None, 1, H, 2, N // 2,
+            d, BF16, ctypes.c_float(1e-6), p(FAKE + 0x8000000), wsb, None)
+
+    # inputs interleaved in one fused buffer are fine (only outputs are checked)
+    assert bwd(contig(FAKE + 0x7000000), contig(FAKE + 0x7100000), wsb=0) == WS
+    # gradients interleaved in one buffer overlap by span
+    g2 = FAKE + 0x9000000
+    assert bwd(view(g2, 0, N * 3 * H * d, d, 3 * H * d),
+               view(g2, H * d, N * 3 * H * d, d, 3 * H * d)) == ALIAS
+    # an output view overlapping itself
+    assert bwd(view(FAKE + 0x7000000, 0, 0, 0, d), contig(FAKE + 0x7100000)) == ALIAS
+    # a misaligned record
+    assert bwd(contig(FAKE + 0x7000000), contig(FAKE + 0x7100000), states=FAKE + 0xA000004) == ALIGN
+    f = lib.gla_fwd_framecausal_states_ex
+    assert f(inter(0), inter(1), inter(2), contig(FAKE + 0x2000000), p(FAKE + 0x3000000), None,
+             None, contig(FAKE + 0x4000000), None, None, None, 1, H, 2, N // 2, d, BF16,
+             ctypes.c_float(1e-6), p(FAKE + 0x8000000), 1 << 30, None) == NULL

@@ -84,3 +84,24 @@ def test_bidir_grads_equal_direct_backward():
     want = gla.gla_bwd_bidir(*(t[n].detach() for n in "qkvg"), w)
     for x, n in zip(got, ("dq", "dk", "dv", "dg")):
         assert torch.equal(x, want[n]), n
+
+
+def test_framecausal_on_a_fused_projection():
+    """q, k, v as slices of one fused [B, N, 3, H, d] leaf: the gradient that
+    reaches the fused tensor holds the three gradients, bit for bit those of
+    the contiguous call."""
+    B, H, F, T, d = 1, 2, 3, 64, 64
+    N = F * T
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(21)
+    qkv = torch.randn((B, N, 3, H, d), generator=gen, device=DEV).to(torch.bfloat16)
+    qkv.requires_grad_()
+    g = torch.randn((B, H, N, d), generator=gen, device=DEV).to(torch.bfloat16).requires_grad_()
+    gamma = torch.sigmoid(torch.randn((B, H, F), generator=gen, device=DEV) + 2)
+    q, k, v = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+    o = ga.gla_framecausal(q, k, v, g, gamma)
+    w = torch.randn(o.shape, generator=gen, device=DEV).to(torch.bfloat16)
+    (dqkv,) = torch.autograd.grad((o.float() * w.float()).sum(), [qkv])
+    want = gla.gla_bwd_framecausal(*(x.detach().contiguous() for x in (q, k, v, g)), gamma, w)
+    for i, n in enumerate(("dq", "dk", "dv")):
+        assert torch.equal(dqkv[:, :, i].transpose(1, 2), want[n]), n

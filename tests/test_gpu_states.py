@@ -164,3 +164,41 @@ def test_720p_60s_backward_from_states_equals_recompute():
     for n in want:
         assert torch.equal(got[n], want[n]), n
     assert slab_rel_err(f64(o[:, :4]), f64(o_plain[:, :4])) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_strided_training_calls_equal_contiguous(d):
+    """q, k, v read from a fused [B, N, 3, H, d] projection, g and dO as
+    [B, N, H, d] views, gradients written into [B, N, H, d] views: the same
+    bits as the contiguous calls on copies, with and without the record."""
+    B, H, F, T = 1, 3, 4, 96
+    N = F * T
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(d)
+    qkv = torch.randn((B, N, 3, H, d), generator=gen, device=DEV).to(torch.bfloat16)
+    gbnhd = torch.randn((B, N, H, d), generator=gen, device=DEV).to(torch.bfloat16)
+    dobnhd = torch.randn((B, N, H, d), generator=gen, device=DEV).to(torch.bfloat16)
+    gamma = torch.sigmoid(torch.randn((B, H, F), generator=gen, device=DEV) + 2)
+    S_in = torch.randn((B, H, d, d), generator=gen, device=DEV)
+    z_in = torch.rand((B, H, d), generator=gen, device=DEV)
+    q, k, v = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+    g, dO = gbnhd.transpose(1, 2), dobnhd.transpose(1, 2)
+    cq, ck, cv, cg, cdO = (x.contiguous() for x in (q, k, v, g, dO))
+
+    o, st = gla.gla_fwd_framecausal_states_ex(q, k, v, g, gamma, S_in, z_in)
+    o_ref, st_ref = gla.gla_fwd_framecausal_states(cq, ck, cv, cg, gamma, S_in, z_in)
+    assert torch.equal(o, o_ref) and torch.equal(st, st_ref)
+
+    outs = {n: torch.empty((B, N, H, d), dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+            for n in ("dq", "dk", "dv", "dg")}
+    for states in (st, None):
+        got = gla.gla_bwd_framecausal_ex(q, k, v, g, gamma, dO, states=states, S_in=S_in,
+                                         z_in=z_in, need_state_grad=True, out=dict(outs))
+        if states is None:
+            want = gla.gla_bwd_framecausal(cq, ck, cv, cg, gamma, cdO, S_in=S_in, z_in=z_in,
+                                           need_state_grad=True)
+        else:
+            want = gla.gla_bwd_framecausal_states(cq, ck, cv, cg, gamma, st_ref, cdO, S_in=S_in,
+                                                  z_in=z_in, need_state_grad=True)
+        for n in want:
+            assert torch.equal(got[n], want[n]), (n, states is None)
