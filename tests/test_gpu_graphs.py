@@ -50,6 +50,11 @@ CALLS = {
     "bwd_states": lambda t: gla.gla_bwd_framecausal_states(
         t["q"], t["k"], t["v"], t["g"], t["gamma"], t["states"], t["dO"], S_in=t["S"], z_in=t["z"],
         need_state_grad=True),
+    "fwd_states_ex": lambda t: gla.gla_fwd_framecausal_states_ex(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["S"], t["z"], return_state=True),
+    "bwd_ex": lambda t: gla.gla_bwd_framecausal_ex(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"], states=t["states"], S_in=t["S"],
+        z_in=t["z"], need_state_grad=True),
     "gdn": lambda t: gla.gla_gdn_framecausal(t["q"], t["k"], t["v"], t["beta"], t["gamma"],
                                              t["S"], return_state=True),
     "anchor": lambda t: gla.gla_softmax_anchor(t["q"], t["k"], t["v"], t["g"], T=150, n_sink=1,

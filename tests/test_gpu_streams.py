@@ -58,6 +58,11 @@ CALLS = {
     "bwd_states": lambda t, s: gla.gla_bwd_framecausal_states(
         t["q"], t["k"], t["v"], t["g"], t["gamma"], t["states"], t["dO"], S_in=t["S"],
         z_in=t["z"], need_state_grad=True, stream=s),
+    "fwd_states_ex": lambda t, s: gla.gla_fwd_framecausal_states_ex(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["S"], t["z"], return_state=True, stream=s),
+    "bwd_ex": lambda t, s: gla.gla_bwd_framecausal_ex(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"], states=None, S_in=t["S"],
+        z_in=t["z"], need_state_grad=True, stream=s),
     "gdn": lambda t, s: gla.gla_gdn_framecausal(t["q"], t["k"], t["v"], t["beta"], t["gamma"],
                                                 t["S"], return_state=True, stream=s),
     "anchor": lambda t, s: gla.gla_softmax_anchor(t["q"], t["k"], t["v"], t["g"], T=200,
