@@ -94,7 +94,7 @@ def _load():
         ctypes.POINTER(Rope), ctypes.c_int]
     lib.gla_oracle_rope_quadratic.restype = ctypes.c_int
     lib.gla_oracle_backward.argtypes = [ctypes.c_int, ctypes.c_int] + [vp] * 17 + [
-        ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_int]
+        ctypes.c_int] * 5 + [ctypes.c_double, ctypes.POINTER(Rope), ctypes.c_int, ctypes.c_int]
     lib.gla_oracle_backward.restype = ctypes.c_int
     lib.gla_oracle_gdn.argtypes = [ctypes.c_int] + [vp] * 8 + [ctypes.c_int] * 5 + [
         ctypes.c_double, ctypes.c_int]
@@ -244,14 +244,28 @@ def rope_quadratic(mode, q, k, v, g, gamma=None, S_in=None, z_in=None, F=None, T
 
 
 def backward(mode, q, k, v, g, dO, gamma=None, S_in=None, z_in=None, dS_out=None,
-             dz_out=None, F=None, T=None, eps=1e-6, nthreads=0):
+             dz_out=None, F=None, T=None, eps=1e-6, rope=None, nthreads=0):
     """Gradients of the forward definition (chain rule, fp64) for
     dL/do = dO and, in frame-causal mode, dL/dS_out = dS_out, dL/dz_out = dz_out.
 
+    With ``rope`` the gradients are those of the rotary form
+    (:func:`rope_recurrent`); in bidirectional mode F and T then give the
+    positions (N = F * T), as there.
+
     Returns a dict with dq, dk, dv, dg ([B, H, N, d] float64) and, in
     frame-causal mode, dgamma [B, H, F], dS_in [B, H, d, d], dz_in [B, H, d]."""
+    pos_T = None
+    if rope is not None and mode == BIDIR:
+        pos_T = T if F else np.shape(k)[2]
+        F = T = None
     (q, k, v, g, gamma, S_in, z_in, _, _, _, B, H, F, T, d, dt) = _prep(
         mode, q, k, v, g, gamma, S_in, z_in, F, T, True)
+    r = None
+    if rope is not None:
+        pos_T = T if pos_T is None else pos_T
+        r = _rope(rope, pos_T, d)
+        if (F * T) % pos_T:
+            raise ValueError("the positions need whole frames of grid_h * grid_w tokens")
     dO = np.ascontiguousarray(bf16_to_f64(dO) if np.asarray(dO).dtype == np.uint16
                               else np.asarray(dO, np.float64))
     if dO.shape != (B, H, F * T, d):
@@ -275,7 +289,8 @@ def backward(mode, q, k, v, g, dO, gamma=None, S_in=None, z_in=None, dS_out=None
         mode, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in),
         _ptr(dO), _ptr(dS_out), _ptr(dz_out), _ptr(out["dq"]), _ptr(out["dk"]),
         _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out.get("dgamma")), _ptr(out.get("dS_in")),
-        _ptr(out.get("dz_in")), B, H, F, T, d, float(eps), int(nthreads))
+        _ptr(out.get("dz_in")), B, H, F, T, d, float(eps),
+        ctypes.byref(r) if r is not None else None, int(pos_T or T), int(nthreads))
     return out
 
 

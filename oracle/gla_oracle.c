@@ -374,7 +374,9 @@ typedef struct orc_rope {
   double theta;
 } orc_rope;
 
-static void rope_rotate(double *x, int d, int T, size_t n, const orc_rope *r) {
+/* Turns the pairs of x, the features of token n (T tokens per frame), by
+ * dir times their angles: dir = +1 is R_n, dir = -1 its transpose. */
+static void rope_turn(double *x, int d, int T, size_t n, const orc_rope *r, double dir) {
   const int f = (int)(n / (size_t)T);
   const int l = (int)(n % (size_t)T);
   const double pt = (double)(r->frame_offset + f);
@@ -391,12 +393,16 @@ static void rope_rotate(double *x, int d, int T, size_t n, const orc_rope *r) {
     } else {
       pos = px; j = p - Pt - Ph; m = Pw;
     }
-    const double ang = pos * pow(r->theta, -(double)j / (double)m);
+    const double ang = dir * (pos * pow(r->theta, -(double)j / (double)m));
     const double c = cos(ang), s = sin(ang);
     const double a = x[2 * p], b = x[2 * p + 1];
     x[2 * p] = a * c - b * s;
     x[2 * p + 1] = a * s + b * c;
   }
+}
+
+static void rope_rotate(double *x, int d, int T, size_t n, const orc_rope *r) {
+  rope_turn(x, d, T, n, r, 1.0);
 }
 
 /* Recurrent form with rotation: the state collects rotated keys, the
@@ -541,6 +547,16 @@ int gla_oracle_rope_quadratic(int mode, int dt, const void *q, const void *k, co
  * of all N tokens with no decay and no carried state (dgamma, dS_in, dz_in
  * are then not written).
  *
+ * With rotary positions (rope != NULL; the rotary form above) the numerator
+ * takes turned features a~_t = R_t phi(q_t), b~_s = R_s phi(k_s) and the
+ * normaliser the unturned ones, so S_f collects b~_s v_s^T and z_f phi(k_s):
+ *   dq_t = [q_t > 0] (.) (R_t^T S_f dnum_t + dden_t z_f)
+ *   Sh_f collects a~_t dnum_t^T, zh_f still dden_t phi(q_t)
+ *   dk_t = [k_t > 0] (.) (R_t^T Sh_f v_t + zh_f),   dv_t = Sh_f^T b~_t
+ * Token n = f T + t turns by the position (n / pos_T, n % pos_T) of a frame of
+ * pos_T tokens (pos_T = T in frame-causal mode; in bidirectional mode the
+ * positions keep the frames of pos_T tokens while the sums run over all N).
+ *
  * dO, dS_out, dz_out are float64 (dS_out/dz_out may be NULL: zero); dq, dk,
  * dv, dg are float64 [B][H][N][d]; dgamma [B][H][F]; dS_in [B][H][d][d] and
  * dz_in [B][H][d] may be NULL. OpenMP over slabs.
@@ -550,7 +566,7 @@ int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const vo
                         const double *z_in, const double *dO, const double *dS_out,
                         const double *dz_out, double *dq, double *dk, double *dv, double *dg,
                         double *dgamma, double *dS_in, double *dz_in, int B, int H, int F, int T,
-                        int d, double eps, int nthreads) {
+                        int d, double eps, const orc_rope *rope, int pos_T, int nthreads) {
   const long nslab = (long)B * H;
   const size_t N = (size_t)F * T, dd = (size_t)d * d;
   const int used = set_threads(nthreads);
@@ -567,6 +583,9 @@ int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const vo
     double *Sh = (double *)malloc(dd * sizeof(double));
     double *zh = (double *)malloc((size_t)d * sizeof(double));
     double *fq = (double *)malloc((size_t)d * sizeof(double));
+    double *rq = (double *)malloc((size_t)d * sizeof(double)); /* turned phi(q) (= fq without rope) */
+    double *rk = (double *)malloc((size_t)d * sizeof(double)); /* turned phi(k) */
+    double *u = (double *)malloc((size_t)d * sizeof(double));
     double *h = (double *)malloc((size_t)d * sizeof(double));
     double *dn = (double *)malloc((size_t)d * sizeof(double));
     const size_t base = (size_t)bh * N * d;
@@ -580,11 +599,12 @@ int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const vo
       for (size_t e = 0; e < dd; ++e) Sc[e] = gm * S[(size_t)f * dd + e];
       for (int i = 0; i < d; ++i) zc[i] = gm * z[(size_t)f * d + i];
       for (int t = 0; t < T; ++t) {
-        const size_t row = base + ((size_t)f * T + t) * d;
+        const size_t n = (size_t)f * T + t, row = base + n * d;
+        for (int i = 0; i < d; ++i) rk[i] = relu(ld(k, dt, row + i));
+        if (rope) rope_turn(rk, d, pos_T, n, rope, 1.0);
         for (int i = 0; i < d; ++i) {
-          const double ki = relu(ld(k, dt, row + i));
-          zc[i] += ki;
-          for (int j = 0; j < d; ++j) Sc[(size_t)i * d + j] += ki * ld(v, dt, row + j);
+          zc[i] += relu(ld(k, dt, row + i));
+          for (int j = 0; j < d; ++j) Sc[(size_t)i * d + j] += rk[i] * ld(v, dt, row + j);
         }
       }
     }
@@ -594,17 +614,18 @@ int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const vo
       const double *Sc = S + (size_t)(f + 1) * dd, *zc = z + (size_t)(f + 1) * d;
       double *Gf = G + (size_t)f * dd, *gzf = gz + (size_t)f * d;
       for (int t = 0; t < T; ++t) {
-        const size_t row = base + ((size_t)f * T + t) * d;
+        const size_t n = (size_t)f * T + t, row = base + n * d;
         double den = 0.0;
         for (int i = 0; i < d; ++i) {
-          fq[i] = relu(ld(q, dt, row + i));
+          rq[i] = fq[i] = relu(ld(q, dt, row + i));
           den += fq[i] * zc[i];
         }
+        if (rope) rope_turn(rq, d, pos_T, n, rope, 1.0);
         const double inv = 1.0 / (den + eps);
         double dden = 0.0;
         for (int j = 0; j < d; ++j) {
           double num = 0.0;
-          for (int i = 0; i < d; ++i) num += fq[i] * Sc[(size_t)i * d + j];
+          for (int i = 0; i < d; ++i) num += rq[i] * Sc[(size_t)i * d + j];
           const double sg = sigm(ld(g, dt, row + j));
           h[j] = num * inv;
           const double dh = dO[row + j] * sg;
@@ -613,10 +634,14 @@ int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const vo
           dden -= dh * h[j] * inv;
         }
         for (int i = 0; i < d; ++i) {
-          double acc = dden * zc[i];
+          double acc = 0.0;
           for (int j = 0; j < d; ++j) acc += Sc[(size_t)i * d + j] * dn[j];
-          dq[row + i] = ld(q, dt, row + i) > 0.0 ? acc : 0.0;
-          for (int j = 0; j < d; ++j) Gf[(size_t)i * d + j] += fq[i] * dn[j];
+          u[i] = acc;
+        }
+        if (rope) rope_turn(u, d, pos_T, n, rope, -1.0);
+        for (int i = 0; i < d; ++i) {
+          dq[row + i] = ld(q, dt, row + i) > 0.0 ? u[i] + dden * zc[i] : 0.0;
+          for (int j = 0; j < d; ++j) Gf[(size_t)i * d + j] += rq[i] * dn[j];
           gzf[i] += dden * fq[i];
         }
       }
@@ -635,15 +660,21 @@ int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const vo
         dgamma[(size_t)bh * F + f] = s;
       }
       for (int t = 0; t < T; ++t) {
-        const size_t row = base + ((size_t)f * T + t) * d;
+        const size_t n = (size_t)f * T + t, row = base + n * d;
         for (int i = 0; i < d; ++i) {
-          double acc = zh[i];
+          double acc = 0.0;
           for (int j = 0; j < d; ++j) acc += Sh[(size_t)i * d + j] * ld(v, dt, row + j);
-          dk[row + i] = ld(k, dt, row + i) > 0.0 ? acc : 0.0;
+          u[i] = acc;
+          rk[i] = relu(ld(k, dt, row + i));
         }
+        if (rope) {
+          rope_turn(u, d, pos_T, n, rope, -1.0);
+          rope_turn(rk, d, pos_T, n, rope, 1.0);
+        }
+        for (int i = 0; i < d; ++i) dk[row + i] = ld(k, dt, row + i) > 0.0 ? u[i] + zh[i] : 0.0;
         for (int j = 0; j < d; ++j) {
           double acc = 0.0;
-          for (int i = 0; i < d; ++i) acc += Sh[(size_t)i * d + j] * relu(ld(k, dt, row + i));
+          for (int i = 0; i < d; ++i) acc += Sh[(size_t)i * d + j] * rk[i];
           dv[row + j] = acc;
         }
       }
@@ -655,7 +686,7 @@ int gla_oracle_backward(int mode, int dt, const void *q, const void *k, const vo
     if (causal && dz_in) memcpy(dz_in + (size_t)bh * d, az, (size_t)d * sizeof(double));
 
     free(S); free(z); free(G); free(gz); free(A); free(az); free(Sh); free(zh);
-    free(fq); free(h); free(dn);
+    free(fq); free(rq); free(rk); free(u); free(h); free(dn);
   }
   return used;
 }
