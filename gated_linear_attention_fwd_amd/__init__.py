@@ -48,7 +48,8 @@ __all__ = [
     "gla_fwd_bidir_ex_workspace", "gla_bwd_framecausal", "gla_bwd_bidir",
     "gla_bwd_framecausal_workspace", "gla_bwd_bidir_workspace", "gla_fwd_framecausal_states",
     "gla_bwd_framecausal_states", "gla_bwd_framecausal_states_workspace",
-    "gla_fwd_framecausal_states_ex", "gla_bwd_framecausal_ex", "gla_gdn_framecausal",
+    "gla_fwd_framecausal_states_ex", "gla_bwd_framecausal_ex", "gla_bwd_bidir_ex",
+    "gla_bwd_bidir_ex_workspace", "gla_gdn_framecausal",
     "gla_gdn_framecausal_workspace", "gla_softmax_anchor", "library_path", "load_library",
     "profile_begin", "profile_end",
 ]
@@ -161,11 +162,15 @@ def load_library():
     lib.gla_bwd_framecausal_states.argtypes = [vp] * 18 + [i32] * 6 + [f32, vp, sz, vp]
     lib.gla_bwd_framecausal_states.restype = i32
     lib.gla_fwd_framecausal_states_ex.argtypes = [tp, tp, tp, tp, vp, vp, vp, tp, vp, vp, vp] + \
-        [i32] * 6 + [f32, vp, sz, vp]
+        [i32] * 6 + [f32, rp, vp, sz, vp]
     lib.gla_fwd_framecausal_states_ex.restype = i32
     lib.gla_bwd_framecausal_ex.argtypes = [tp, tp, tp, tp, vp, vp, vp, vp, tp, vp, vp, tp, tp, tp,
-                                           tp, vp, vp, vp] + [i32] * 6 + [f32, vp, sz, vp]
+                                           tp, vp, vp, vp] + [i32] * 6 + [f32, rp, vp, sz, vp]
     lib.gla_bwd_framecausal_ex.restype = i32
+    lib.gla_bwd_bidir_ex_workspace.argtypes = [i32, i32, i32, i32, i32, rp]
+    lib.gla_bwd_bidir_ex_workspace.restype = sz
+    lib.gla_bwd_bidir_ex.argtypes = [tp] * 9 + [i32] * 6 + [f32, rp, vp, sz, vp]
+    lib.gla_bwd_bidir_ex.restype = i32
     lib.gla_gdn_framecausal_workspace.argtypes = [i32, i32, i32, i32, i32]
     lib.gla_gdn_framecausal_workspace.restype = sz
     lib.gla_gdn_framecausal.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp, sz, vp]
@@ -520,14 +525,15 @@ def gla_fwd_framecausal_states_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
                                   g: torch.Tensor, gamma: torch.Tensor,
                                   S_in: Optional[torch.Tensor] = None,
                                   z_in: Optional[torch.Tensor] = None, eps: float = 1e-6,
-                                  out: Optional[torch.Tensor] = None,
+                                  rope=None, out: Optional[torch.Tensor] = None,
                                   states: Optional[torch.Tensor] = None,
                                   S_out: Optional[torch.Tensor] = None,
                                   z_out: Optional[torch.Tensor] = None,
                                   return_state: bool = False,
                                   workspace: Optional[torch.Tensor] = None, stream=None):
     """gla_fwd_framecausal_states on views of any layout with a contiguous
-    feature axis (no rotary positions). Returns ``(o, states)`` or
+    feature axis, optionally with 3D rotary positions (the record then holds
+    the turned-key states). Returns ``(o, states)`` or
     ``(o, states, S_out, z_out)``."""
     lib = load_library()
     ref = _qkvg(q, k, v, g)
@@ -556,7 +562,8 @@ def gla_fwd_framecausal_states_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_fwd_framecausal_states_ex(
         _view(q), _view(k), _view(v), _view(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _view(o),
-        _ptr(S_out), _ptr(z_out), _ptr(states), B, H, F, T, d, dt, eps, _ptr(ws), wsb,
+        _ptr(S_out), _ptr(z_out), _ptr(states), B, H, F, T, d, dt, eps, _rope(rope), _ptr(ws),
+        wsb,
         _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in, o, states, S_out, z_out, ws)))
     return (o, states, S_out, z_out) if want_state else (o, states)
 
@@ -637,11 +644,14 @@ def gla_bwd_framecausal_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
                            z_in: Optional[torch.Tensor] = None,
                            dS_out: Optional[torch.Tensor] = None,
                            dz_out: Optional[torch.Tensor] = None, eps: float = 1e-6,
-                           need_state_grad: Optional[bool] = None, out: Optional[dict] = None,
-                           workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+                           rope=None, need_state_grad: Optional[bool] = None,
+                           out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> dict:
     """The frame-causal backward on views of any layout with a contiguous
-    feature axis (e.g. q, k, v slices of a fused [B, N, 3, H, d] projection);
-    ``states``: the record of gla_fwd_framecausal_states(_ex), or None to
+    feature axis (e.g. q, k, v slices of a fused [B, N, 3, H, d] projection),
+    optionally with 3D rotary positions (the gradients of
+    gla_fwd_framecausal_ex with the same ``rope``); ``states``: the record of
+    gla_fwd_framecausal_states(_ex) for the same inputs and rope, or None to
     recompute. ``out`` may supply dq, dk, dv, dg (views too; they may not
     overlap one another) and the fp32 gradients; missing ones are allocated
     contiguous."""
@@ -680,9 +690,40 @@ def gla_bwd_framecausal_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
         _view(q), _view(k), _view(v), _view(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _ptr(states),
         _view(dO), _ptr(dS_out), _ptr(dz_out), _view(out["dq"]), _view(out["dk"]),
         _view(out["dv"]), _view(out["dg"]), _ptr(out["dgamma"]), _ptr(out.get("dS_in")),
-        _ptr(out.get("dz_in")), B, H, F, T, d, dt, eps, _ptr(ws), wsb,
+        _ptr(out.get("dz_in")), B, H, F, T, d, dt, eps, _rope(rope), _ptr(ws), wsb,
         _stream_handle(stream, dev, q, k, v, g, gamma, states, S_in, z_in, dO, dS_out, dz_out,
                        out, ws)))
+    return out
+
+
+def gla_bwd_bidir_ex_workspace(B: int, H: int, F: int, T: int, d: int, rope=None) -> int:
+    return int(load_library().gla_bwd_bidir_ex_workspace(B, H, F, T, d, _rope(rope)))
+
+
+def gla_bwd_bidir_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     dO: torch.Tensor, eps: float = 1e-6, rope=None,
+                     frames: Optional[int] = None, out: Optional[dict] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of gla_fwd_bidir_ex (same ``rope`` and ``frames``) for
+    dL/do = dO on views of any layout with a contiguous feature axis:
+    {"dq", "dk", "dv", "dg"}; ``out`` may supply any of them (views too)."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g, dO)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F, T = _frames_of(N, rope, frames)
+    out = dict(out or {})
+    for n in ("dq", "dk", "dv", "dg"):
+        out.setdefault(n, torch.empty(ref.shape, dtype=ref.dtype, device=ref.device))
+        if out[n].shape != ref.shape or out[n].dtype != ref.dtype:
+            raise ValueError("%s must match q's shape and dtype" % n)
+    dev = _require_device_any_layout(q, k, v, g, dO, workspace, *out.values())
+    ws, wsb = _workspace(lib.gla_bwd_bidir_ex_workspace(B, H, F, T, d, _rope(rope)), dev,
+                         workspace)
+    _check(lib.gla_bwd_bidir_ex(_view(q), _view(k), _view(v), _view(g), _view(dO),
+                                _view(out["dq"]), _view(out["dk"]), _view(out["dv"]),
+                                _view(out["dg"]), B, H, F, T, d, dt, eps, _rope(rope), _ptr(ws),
+                                wsb, _stream_handle(stream, dev, q, k, v, g, dO, out, ws)))
     return out
 
 

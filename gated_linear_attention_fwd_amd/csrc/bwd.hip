@@ -28,11 +28,14 @@ constexpr int kThreads = 256;
 // dnum, and key features i = 4cg .. 4cg+3 for dq. The split's sums
 // G = sum phi(q) dnum^T use the kv layout (thread: key feature i, value
 // columns jc + JS c) and gz = sum dden phi(q) the threads with jc == 0.
-template <typename TIn, int D>
+// kRope: num and G take the turned phi(q), den, gz and the ReLU mask the
+// unturned one, and S_f dnum turns back (R^T) before dden z_f is added; a
+// thread's four key features are two whole pairs.
+template <typename TIn, int D, bool kRope>
 __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
     View qv, View gv, View dov, View dqv, View dgv, int H, const float *__restrict__ st,
     int64_t sstride, float *__restrict__ gs, int F, int64_t T, int R, int64_t read_len,
-    float eps) {
+    float eps, int state_frame, RopeK rope) {
   constexpr int CG = D / 4;
   constexpr int TT = kThreads / CG;
   constexpr bool kSInLds = (D <= 64);
@@ -41,7 +44,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
   constexpr int64_t E = (int64_t)D * D + D;
   __shared__ float sS[kSInLds ? D * D : 1];
   __shared__ float sz[D];
-  __shared__ float sq[TT][D];   // phi(q)
+  __shared__ float sq[TT][D];   // phi(q), turned with kRope
+  __shared__ float sqd[kRope ? TT : 1][D];  // kRope: phi(q) unturned
   __shared__ float sdn[TT][D];  // dnum
   __shared__ float sred[TT][CG];
   __shared__ float sdd[TT];     // dden
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
   const int64_t t0 = min((int64_t)r * read_len, T);
   const int64_t t1 = min(t0 + read_len, T);
 
-  const float *Sg = st + (bh * F + f) * sstride;  // S_f
+  const float *Sg = st + (bh * F + (state_frame >= 0 ? state_frame : f)) * sstride;  // S_f
   if (kSInLds)
     for (int e = tid; e < D * D; e += kThreads) sS[e] = Sg[e];
   for (int e = tid; e < D; e += kThreads) sz[e] = Sg[D * D + e];
@@ -75,10 +79,27 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
   for (int64_t c0 = t0; c0 < t1; c0 += TT) {
     const int n = (int)min((int64_t)TT, t1 - c0);
     __syncthreads();
-    for (int e = tid; e < TT * D; e += kThreads) {
-      const int tt = e / D, ii = e % D;
-      sq[tt][ii] =
-          (tt < n) ? relu(Elem<TIn>::load(qs, (trow0 + c0 + tt) * qv.sn + ii)) : 0.f;
+    if constexpr (kRope) {
+      for (int e = tid; e < TT * (D / 2); e += kThreads) {
+        const int tt = e / (D / 2), pp = e % (D / 2);
+        float a = 0.f, b = 0.f;
+        if (tt < n) {
+          const int64_t off = (trow0 + c0 + tt) * qv.sn + 2 * pp;
+          a = relu(Elem<TIn>::load(qs, off));
+          b = relu(Elem<TIn>::load(qs, off + 1));
+        }
+        sqd[tt][2 * pp] = a;
+        sqd[tt][2 * pp + 1] = b;
+        const float2 ab = rotate_pair(a, b, token_rope_cs(rope, f, (int)(c0 + tt), pp));
+        sq[tt][2 * pp] = ab.x;
+        sq[tt][2 * pp + 1] = ab.y;
+      }
+    } else {
+      for (int e = tid; e < TT * D; e += kThreads) {
+        const int tt = e / D, ii = e % D;
+        sq[tt][ii] =
+            (tt < n) ? relu(Elem<TIn>::load(qs, (trow0 + c0 + tt) * qv.sn + ii)) : 0.f;
+      }
     }
     __syncthreads();
     const int64_t row = trow0 + c0 + tl;
@@ -88,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
       float den = 0.f;
       for (int ii = 0; ii < D; ++ii) {
         const float qi = sq[tl][ii];
-        den = fmaf(qi, sz[ii], den);
+        den = fmaf(kRope ? sqd[tl][ii] : qi, sz[ii], den);
         const float *Srow = kSInLds ? sS + ii * D : Sg + ii * D;
 #pragma unroll
         for (int c = 0; c < 4; ++c) num[c] = fmaf(qi, Srow[4 * cg + c], num[c]);
@@ -121,13 +142,36 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
       const float dden = -tot * inv;
       if (cg == 0) sdd[tl] = dden;
       float dqo[4];
+      if constexpr (kRope) {
+        float u[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * cg + c;
-        const float *Srow = kSInLds ? sS + i * D : Sg + i * D;
-        float acc = dden * sz[i];
-        for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sdn[tl][j], acc);
-        dqo[c] = sq[tl][i] > 0.f ? acc : 0.f;
+        for (int c = 0; c < 4; ++c) {
+          const float *Srow = kSInLds ? sS + (4 * cg + c) * D : Sg + (4 * cg + c) * D;
+          float acc = 0.f;
+          for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sdn[tl][j], acc);
+          u[c] = acc;
+        }
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+          const float2 cs = token_rope_cs(rope, f, (int)(c0 + tl), 2 * cg + hp);
+          const float2 back = rotate_pair(u[2 * hp], u[2 * hp + 1], make_float2(cs.x, -cs.y));
+          u[2 * hp] = back.x;
+          u[2 * hp + 1] = back.y;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i = 4 * cg + c;
+          dqo[c] = sqd[tl][i] > 0.f ? fmaf(dden, sz[i], u[c]) : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i = 4 * cg + c;
+          const float *Srow = kSInLds ? sS + i * D : Sg + i * D;
+          float acc = dden * sz[i];
+          for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sdn[tl][j], acc);
+          dqo[c] = sq[tl][i] > 0.f ? acc : 0.f;
+        }
       }
       Elem<TIn>::store4(dqs, row * dqv.sn + 4 * cg, make_float4(dqo[0], dqo[1], dqo[2], dqo[3]));
     } else if (cg == 0) {
@@ -138,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
       const float qi = sq[tt][ig];
 #pragma unroll
       for (int c = 0; c < EPT; ++c) Gacc[c] = fmaf(qi, sdn[tt][jc + JS * c], Gacc[c]);
-      gzacc = fmaf(sdd[tt], qi, gzacc);
+      gzacc = fmaf(sdd[tt], kRope ? sqd[tt][ig] : qi, gzacc);
     }
   }
   float *out = gs + ((bh * F + f) * (int64_t)R + r) * E;
@@ -149,17 +193,20 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
 
 // One workgroup per (slab, frame, part). Thread (cg, tl): dk for key features
 // i = 4cg .. 4cg+3 and dv for value features j = 4cg .. 4cg+3 of token tl.
-template <typename TIn, int D>
+// kRope: dv takes the turned phi(k), the mask the unturned one, and Sh_f v
+// turns back (R^T) before zh_f is added.
+template <typename TIn, int D, bool kRope>
 __global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
     View kv, View vv, View dkv, View dvv, int H, const float *__restrict__ gs, int F, int64_t T,
-    int P, int R, int64_t part_len) {
+    int P, int R, int64_t part_len, int adj_frame, RopeK rope) {
   constexpr int CG = D / 4;
   constexpr int TT = kThreads / CG;
   constexpr bool kSInLds = (D <= 64);
   constexpr int64_t E = (int64_t)D * D + D;
   __shared__ float sSh[kSInLds ? D * D : 1];
   __shared__ float szh[D];
-  __shared__ float sk[TT][D];  // phi(k)
+  __shared__ float sk[TT][D];  // phi(k), turned with kRope
+  __shared__ float skd[kRope ? TT : 1][D];  // kRope: phi(k) unturned
   __shared__ float sv[TT][D];
 
   const int tid = threadIdx.x;
@@ -171,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
   const int64_t t1 = min(t0 + part_len, T);
   if (t0 >= t1) return;
 
-  const float *Sh = gs + ((bh * F + f) * (int64_t)R) * E;  // adjoint of S_f
+  const float *Sh = gs + ((bh * F + (adj_frame >= 0 ? adj_frame : f)) * (int64_t)R) * E;  // adjoint of S_f
   if (kSInLds)
     for (int e = tid; e < D * D; e += kThreads) sSh[e] = Sh[e];
   for (int e = tid; e < D; e += kThreads) szh[e] = Sh[D * D + e];
@@ -186,24 +233,68 @@ __global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
   for (int64_t c0 = t0; c0 < t1; c0 += TT) {
     const int n = (int)min((int64_t)TT, t1 - c0);
     __syncthreads();
-    for (int e = tid; e < TT * D; e += kThreads) {
-      const int tt = e / D, ii = e % D;
-      const bool ok = tt < n;
-      const int64_t rr = trow0 + c0 + tt;
-      sk[tt][ii] = ok ? relu(Elem<TIn>::load(ks, rr * kv.sn + ii)) : 0.f;
-      sv[tt][ii] = ok ? Elem<TIn>::load(vs, rr * vv.sn + ii) : 0.f;
+    if constexpr (kRope) {
+      for (int e = tid; e < TT * (D / 2); e += kThreads) {
+        const int tt = e / (D / 2), pp = e % (D / 2);
+        float a = 0.f, b = 0.f, va = 0.f, vb = 0.f;
+        if (tt < n) {
+          const int64_t rr = trow0 + c0 + tt;
+          a = relu(Elem<TIn>::load(ks, rr * kv.sn + 2 * pp));
+          b = relu(Elem<TIn>::load(ks, rr * kv.sn + 2 * pp + 1));
+          va = Elem<TIn>::load(vs, rr * vv.sn + 2 * pp);
+          vb = Elem<TIn>::load(vs, rr * vv.sn + 2 * pp + 1);
+        }
+        skd[tt][2 * pp] = a;
+        skd[tt][2 * pp + 1] = b;
+        const float2 ab = rotate_pair(a, b, token_rope_cs(rope, f, (int)(c0 + tt), pp));
+        sk[tt][2 * pp] = ab.x;
+        sk[tt][2 * pp + 1] = ab.y;
+        sv[tt][2 * pp] = va;
+        sv[tt][2 * pp + 1] = vb;
+      }
+    } else {
+      for (int e = tid; e < TT * D; e += kThreads) {
+        const int tt = e / D, ii = e % D;
+        const bool ok = tt < n;
+        const int64_t rr = trow0 + c0 + tt;
+        sk[tt][ii] = ok ? relu(Elem<TIn>::load(ks, rr * kv.sn + ii)) : 0.f;
+        sv[tt][ii] = ok ? Elem<TIn>::load(vs, rr * vv.sn + ii) : 0.f;
+      }
     }
     __syncthreads();
     if (tl < n) {
       const int64_t row = trow0 + c0 + tl;
       float dko[4], dvo[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kRope) {
+        float u[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * cg + c;
-        const float *Srow = kSInLds ? sSh + i * D : Sh + i * D;
-        float acc = szh[i];
-        for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sv[tl][j], acc);
-        dko[c] = sk[tl][i] > 0.f ? acc : 0.f;
+        for (int c = 0; c < 4; ++c) {
+          const float *Srow = kSInLds ? sSh + (4 * cg + c) * D : Sh + (4 * cg + c) * D;
+          float acc = 0.f;
+          for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sv[tl][j], acc);
+          u[c] = acc;
+        }
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+          const float2 cs = token_rope_cs(rope, f, (int)(c0 + tl), 2 * cg + hp);
+          const float2 back = rotate_pair(u[2 * hp], u[2 * hp + 1], make_float2(cs.x, -cs.y));
+          u[2 * hp] = back.x;
+          u[2 * hp + 1] = back.y;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i = 4 * cg + c;
+          dko[c] = skd[tl][i] > 0.f ? u[c] + szh[i] : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i = 4 * cg + c;
+          const float *Srow = kSInLds ? sSh + i * D : Sh + i * D;
+          float acc = szh[i];
+          for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sv[tl][j], acc);
+          dko[c] = sk[tl][i] > 0.f ? acc : 0.f;
+        }
       }
       for (int i = 0; i < D; ++i) {
         const float ki = sk[tl][i];
@@ -358,11 +449,18 @@ hipError_t bwd_q_valu_dispatch(const BwdPlan &bp, const BwdQArgs &a, hipStream_t
   const Plan &p = bp.f;
   const int64_t grid = p.BH * p.F * p.R;
   float *gs = a.gs;
-#define GLA_BQ_CASE(DD)                                                                       \
-  case DD:                                                                                    \
-    hipLaunchKernelGGL((bwd_q_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), 0, \
-                       s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.st.base, a.st.stride, gs, p.F,    \
-                       p.T, p.R, p.read_len, a.eps);                                          \
+#define GLA_BQ_CASE(DD)                                                                         \
+  case DD:                                                                                      \
+    if (a.rope.on)                                                                              \
+      hipLaunchKernelGGL((bwd_q_valu_kernel<TIn, DD, true>), dim3((unsigned)grid),              \
+                         dim3(kThreads), 0, s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.st.base,       \
+                         a.st.stride, gs, p.F, p.T, p.R, p.read_len, a.eps, a.state_frame,       \
+                         a.rope);                                                               \
+    else                                                                                        \
+      hipLaunchKernelGGL((bwd_q_valu_kernel<TIn, DD, false>), dim3((unsigned)grid),             \
+                         dim3(kThreads), 0, s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.st.base,       \
+                         a.st.stride, gs, p.F, p.T, p.R, p.read_len, a.eps, a.state_frame,       \
+                         a.rope);                                                               \
     break;
   switch (p.d) {
     GLA_BQ_CASE(16)
@@ -380,10 +478,16 @@ template <typename TIn>
 hipError_t bwd_k_valu_dispatch(const BwdPlan &bp, const BwdKArgs &a, hipStream_t s) {
   const Plan &p = bp.f;
   const int64_t grid = p.BH * p.F * p.P;
-#define GLA_BK_CASE(DD)                                                                       \
-  case DD:                                                                                    \
-    hipLaunchKernelGGL((bwd_k_valu_kernel<TIn, DD>), dim3((unsigned)grid), dim3(kThreads), 0, \
-                       s, a.k, a.v, a.dk, a.dv, a.H, a.gs, p.F, p.T, p.P, p.R, p.part_len);    \
+#define GLA_BK_CASE(DD)                                                                         \
+  case DD:                                                                                      \
+    if (a.rope.on)                                                                              \
+      hipLaunchKernelGGL((bwd_k_valu_kernel<TIn, DD, true>), dim3((unsigned)grid),              \
+                         dim3(kThreads), 0, s, a.k, a.v, a.dk, a.dv, a.H, a.gs, p.F, p.T, p.P,   \
+                         p.R, p.part_len, a.adj_frame, a.rope);                                 \
+    else                                                                                        \
+      hipLaunchKernelGGL((bwd_k_valu_kernel<TIn, DD, false>), dim3((unsigned)grid),             \
+                         dim3(kThreads), 0, s, a.k, a.v, a.dk, a.dv, a.H, a.gs, p.F, p.T, p.P,   \
+                         p.R, p.part_len, a.adj_frame, a.rope);                                 \
     break;
   switch (p.d) {
     GLA_BK_CASE(16)

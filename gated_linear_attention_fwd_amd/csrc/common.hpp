@@ -94,6 +94,18 @@ __device__ __forceinline__ void grid_pos(int l, int gw, double inv_gw, int &y, i
   x = xx;
 }
 
+// (cos, sin) of feature pair p of token l in frame f: the whole turn, temporal
+// or spatial, computed directly (the vector-ALU kernels keep no tables, unlike
+// the matrix-core path). R is the validated rotation record (RopeK).
+template <class R>
+__device__ float2 token_rope_cs(const R &r, int f, int l, int p) {
+  if (p < r.Pt) return rope_cs((double)r.frame_offset + f, p, r.Pt, r.log_theta);
+  int y, x;
+  grid_pos(l, r.grid_w, r.inv_gw, y, x);
+  if (p < r.Pt + r.Ph) return rope_cs((double)y, p - r.Pt, r.Ph, r.log_theta);
+  return rope_cs((double)x, p - r.Pt - r.Ph, r.Pw, r.log_theta);
+}
+
 // Rotate the feature pair (a, b) by the angle whose (cos, sin) is cs:
 // (a, b) -> (a cos - b sin, a sin + b cos).
 __device__ __forceinline__ float2 rotate_pair(float a, float b, float2 cs) {

@@ -397,7 +397,8 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
                    const gla_tensor *dq, const gla_tensor *dk, const gla_tensor *dv,
                    const gla_tensor *dg, float *dgamma, float *dS_in, float *dz_in,
                    bool want_states, const float *states, int B, int H, int F, int64_t T, int d,
-                   gla_dtype dt, float eps, void *ws, size_t ws_bytes, void *stream) {
+                   gla_dtype dt, float eps, const gla_rope3d *rope, void *ws, size_t ws_bytes,
+                   void *stream) {
   GLA_TRY(check_dims(B, H, d, dt));
   if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%lld must be >= 0", F, (long long)T);
   GLA_TRY(check_eps(eps));
@@ -437,9 +438,14 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
   if (dgamma && !aligned(dgamma, 4)) return fail(GLA_ERR_ALIGN, "dgamma is not 4-byte aligned");
   GLA_TRY(check_tensor_align(states, "states"));
   if (want_states && BH > 0 && F > 0 && !states) return fail(GLA_ERR_NULL, "states is required");
+  RopeK rk_;
+  GLA_TRY(make_rope(rope, F, T, d, &rk_));
 
+  // bidirectional without positions: one frame of all N tokens; with them the
+  // frames place the positions (no decay; every frame reads the sums over all)
+  const bool flat = bidir && !rk_.on;
   BwdPlan bp;
-  if (!make_bwd_plan(BH, bidir ? (N > 0 ? 1 : 0) : F, bidir ? N : T, d, &bp, !want_states))
+  if (!make_bwd_plan(BH, flat ? (N > 0 ? 1 : 0) : F, flat ? N : T, d, &bp, !want_states))
     return fail(GLA_ERR_SHAPE, "sizes overflow the indexing");
   if (BH == 0 || (bidir && N == 0)) return GLA_OK;
   if (bp.ws_bytes) {
@@ -473,6 +479,13 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Path path = select_path(dt, d);
+  if (rk_.on && !want_states && path == Path::kMfma && rk_.entries() > kMaxRopeEntries)
+    return fail(GLA_ERR_UNSUPPORTED,
+                "rope table of %d entries exceeds %d (1 + grid_h*dim_h/2 + grid_w*dim_w/2 + "
+                "8*dim_t/2)",
+                rk_.entries(), kMaxRopeEntries);
+  // the gradient kernels with rotary positions run on the vector ALU
+  const Path gpath = rk_.on ? Path::kValu : path;
   float *wsf = static_cast<float *>(ws);
   float *gsf = wsf + bp.gslot_offset;
   const Plan &p = bp.f;
@@ -485,16 +498,15 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
     if (!want_states) {
       GLA_TRY(launched(timed(kKindKv, s,
                              [&] {
-                               return launch_kv(p, dt, path, KvArgs{vk, vv, H, gm, wsf, RopeK{}},
-                                                s);
+                               return launch_kv(p, dt, path, KvArgs{vk, vv, H, gm, wsf, rk_}, s);
                              }),
                        "kv"));
       const CarryArgs ca{wsf, gm, causal ? S_in : nullptr, causal ? z_in : nullptr,
                          nullptr, nullptr, 1, fst};
       GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, ca, s); }), "carry"));
     }
-    const BwdQArgs qa{vq, vg, vdo, vdq, vdg, H, fst, gsf, eps};
-    GLA_TRY(launched(timed(kKindBwdQ, s, [&] { return launch_bwd_q(bp, dt, path, qa, s); }),
+    const BwdQArgs qa{vq, vg, vdo, vdq, vdg, H, fst, gsf, eps, rk_, (bidir && !flat) ? p.F - 1 : -1};
+    GLA_TRY(launched(timed(kKindBwdQ, s, [&] { return launch_bwd_q(bp, dt, gpath, qa, s); }),
                      "bwd_q"));
   }
   float *dgp = (causal && dgamma && p.F > 0) ? wsf + bp.dgp_offset : nullptr;
@@ -511,8 +523,8 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
   GLA_TRY(launched(timed(kKindRevScan, s, [&] { return launch_rev_scan(bp, ra, s); }),
                    "rev_scan"));
   if (have_tokens) {
-    const BwdKArgs ka{vk, vv, vdk, vdv, H, gsf};
-    GLA_TRY(launched(timed(kKindBwdK, s, [&] { return launch_bwd_k(bp, dt, path, ka, s); }),
+    const BwdKArgs ka{vk, vv, vdk, vdv, H, gsf, rk_, (bidir && !flat) ? 0 : -1};
+    GLA_TRY(launched(timed(kKindBwdK, s, [&] { return launch_bwd_k(bp, dt, gpath, ka, s); }),
                      "bwd_k"));
   }
   if (dgp)
@@ -898,7 +910,7 @@ GLA_EXPORT gla_status gla_bwd_framecausal(const void *q, const void *k, const vo
                            contiguous(dk, H, N, d), contiguous(dv, H, N, d), contiguous(dg, H, N, d)};
   return run_bwd(false, &t[0], &t[1], &t[2], &t[3], gamma, S_in, z_in, &t[4], dS_out, dz_out,
                  &t[5], &t[6], &t[7], &t[8], dgamma, dS_in, dz_in, false, nullptr, B, H, F, T, d,
-                 dt, eps, ws, ws_bytes, stream);
+                 dt, eps, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_bwd_bidir(const void *q, const void *k, const void *v, const void *g,
@@ -911,7 +923,7 @@ GLA_EXPORT gla_status gla_bwd_bidir(const void *q, const void *k, const void *v,
                            contiguous(dk, H, N, d), contiguous(dv, H, N, d), contiguous(dg, H, N, d)};
   return run_bwd(true, &t[0], &t[1], &t[2], &t[3], nullptr, nullptr, nullptr, &t[4], nullptr,
                  nullptr, &t[5], &t[6], &t[7], &t[8], nullptr, nullptr, nullptr, false, nullptr, B,
-                 H, N > 0 ? 1 : 0, N, d, dt, eps, ws, ws_bytes, stream);
+                 H, N > 0 ? 1 : 0, N, d, dt, eps, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_fwd_framecausal_states(const void *q, const void *k, const void *v,
@@ -949,17 +961,17 @@ GLA_EXPORT gla_status gla_bwd_framecausal_states(
                            contiguous(dk, H, N, d), contiguous(dv, H, N, d), contiguous(dg, H, N, d)};
   return run_bwd(false, &t[0], &t[1], &t[2], &t[3], gamma, S_in, z_in, &t[4], dS_out, dz_out,
                  &t[5], &t[6], &t[7], &t[8], dgamma, dS_in, dz_in, true, states, B, H, F, T, d, dt,
-                 eps, ws, ws_bytes, stream);
+                 eps, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_fwd_framecausal_states_ex(
     const gla_tensor *q, const gla_tensor *k, const gla_tensor *v, const gla_tensor *g,
     const float *gamma, const float *S_in, const float *z_in, const gla_tensor *o, float *S_out,
     float *z_out, float *states, int B, int H, int F, int T, int d, gla_dtype dt, float eps,
-    void *ws, size_t ws_bytes, void *stream) {
+    const gla_rope3d *rope, void *ws, size_t ws_bytes, void *stream) {
   if ((int64_t)B * H > 0 && F > 0 && !states) return fail(GLA_ERR_NULL, "states is required");
   return run(Mode::kFrameCausal, q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d,
-             dt, eps, nullptr, F > 0 ? states : nullptr, ws, ws_bytes, stream);
+             dt, eps, rope, F > 0 ? states : nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT gla_status gla_bwd_framecausal_ex(
@@ -968,10 +980,37 @@ GLA_EXPORT gla_status gla_bwd_framecausal_ex(
     const gla_tensor *dO, const float *dS_out, const float *dz_out, const gla_tensor *dq,
     const gla_tensor *dk, const gla_tensor *dv, const gla_tensor *dg, float *dgamma,
     float *dS_in, float *dz_in, int B, int H, int F, int T, int d, gla_dtype dt, float eps,
-    void *ws, size_t ws_bytes, void *stream) {
+    const gla_rope3d *rope, void *ws, size_t ws_bytes, void *stream) {
   return run_bwd(false, q, k, v, g, gamma, S_in, z_in, dO, dS_out, dz_out, dq, dk, dv, dg, dgamma,
-                 dS_in, dz_in, states != nullptr, states, B, H, F, T, d, dt, eps, ws, ws_bytes,
-                 stream);
+                 dS_in, dz_in, states != nullptr, states, B, H, F, T, d, dt, eps, rope, ws,
+                 ws_bytes, stream);
+}
+
+GLA_EXPORT size_t gla_bwd_bidir_ex_workspace(int B, int H, int F, int T, int d,
+                                             const gla_rope3d *rope) {
+  if (!rope) return gla_bwd_bidir_workspace(B, H, (int64_t)std::max(F, 0) * std::max(T, 0), d);
+  BwdPlan p;
+  if (B < 0 || H < 0 || F < 0 || T < 0 || d <= 0) return 0;
+  if (!make_bwd_plan((int64_t)B * H, F, T, d, &p)) return 0;
+  return p.ws_bytes;
+}
+
+GLA_EXPORT gla_status gla_bwd_bidir_ex(const gla_tensor *q, const gla_tensor *k,
+                                       const gla_tensor *v, const gla_tensor *g,
+                                       const gla_tensor *dO, const gla_tensor *dq,
+                                       const gla_tensor *dk, const gla_tensor *dv,
+                                       const gla_tensor *dg, int B, int H, int F, int T, int d,
+                                       gla_dtype dt, float eps, const gla_rope3d *rope, void *ws,
+                                       size_t ws_bytes, void *stream) {
+  if (F < 0 || T < 0) return fail(GLA_ERR_SHAPE, "F=%d and T=%d must be >= 0", F, T);
+  if (rope)
+    return run_bwd(true, q, k, v, g, nullptr, nullptr, nullptr, dO, nullptr, nullptr, dq, dk, dv,
+                   dg, nullptr, nullptr, nullptr, false, nullptr, B, H, F, T, d, dt, eps, rope,
+                   ws, ws_bytes, stream);
+  const int64_t N = (int64_t)F * T;
+  return run_bwd(true, q, k, v, g, nullptr, nullptr, nullptr, dO, nullptr, nullptr, dq, dk, dv,
+                 dg, nullptr, nullptr, nullptr, false, nullptr, B, H, N > 0 ? 1 : 0, N, d, dt,
+                 eps, nullptr, ws, ws_bytes, stream);
 }
 
 GLA_EXPORT size_t gla_gdn_framecausal_workspace(int B, int H, int F, int T, int d) {
@@ -1014,7 +1053,7 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
 
 GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
 
-GLA_EXPORT int gla_version(void) { return 10400; }
+GLA_EXPORT int gla_version(void) { return 10500; }
 
 GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
   if (max_launches < 1 || max_launches > 65536)

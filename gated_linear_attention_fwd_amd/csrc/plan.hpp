@@ -169,6 +169,11 @@ __device__ __forceinline__ float carry_weight(const float *gamma_slab, int f, in
 //               dgamma; dS_in = gamma_0 Sh_0;
 //   4. bwd_k    one workgroup per (slab, frame, part): dk = [k > 0] (Sh_f v + zh_f),
 //               dv = Sh_f^T phi(k);
+//      with rotary positions the numerator side takes turned features (S_f and
+//      Sh_f hold turned keys and queries) and its adjoints turn back before the
+//      normaliser's terms are added; bidirectional with positions runs on the
+//      frames with no decay, every frame reading the last frame's S and frame
+//      0's adjoint (the sums over all frames);
 //   5. dgamma   one thread per (slab, frame): the partial sums in fixed order.
 // ---------------------------------------------------------------------------
 struct BwdPlan {
@@ -189,6 +194,8 @@ struct BwdQArgs {
   FrameStates st;         // the forward's S_f
   float *gs;              // gslots
   float eps;
+  RopeK rope;             // on: vector-ALU kernel only
+  int state_frame;        // >= 0: every frame reads that frame's S (bidirectional with positions)
 };
 
 struct RevScanArgs {
@@ -205,6 +212,8 @@ struct BwdKArgs {
   View k, v, dk, dv;      // dk, dv written
   int H;
   const float *gs;        // adjoints Sh_f, zh_f in gslot (f, 0)
+  RopeK rope;             // on: vector-ALU kernel only
+  int adj_frame;          // >= 0: every frame reads that frame's adjoint (bidirectional with positions)
 };
 
 hipError_t launch_bwd_q(const BwdPlan &p, int dtype, Path path, const BwdQArgs &a, hipStream_t s);

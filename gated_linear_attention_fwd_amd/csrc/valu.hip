@@ -14,17 +14,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKvTile = 32;  // tokens staged in LDS per step
 
-// (cos, sin) of feature pair p of token l in frame f: the whole turn, temporal
-// or spatial, computed directly (these kernels keep no tables, unlike the
-// matrix-core path).
-__device__ float2 token_rope_cs(const RopeK &r, int f, int l, int p) {
-  if (p < r.Pt) return rope_cs((double)r.frame_offset + f, p, r.Pt, r.log_theta);
-  int y, x;
-  grid_pos(l, r.grid_w, r.inv_gw, y, x);
-  if (p < r.Pt + r.Ph) return rope_cs((double)y, p - r.Pt, r.Ph, r.log_theta);
-  return rope_cs((double)x, p - r.Pt - r.Ph, r.Pw, r.log_theta);
-}
-
 // One workgroup per (slab, group of frames, part). Thread layout: key feature
 // i = tid % D, value columns j = tid / D + (256 / D) * c for c < D*D/256. Each
 // token adds phi(k[i]) * v[j] to the thread's entries; u[i] is kept by threads

@@ -316,13 +316,14 @@ gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *v, const fl
                               int B, int H, int F, int T, int d, gla_dtype dt,
                               const gla_rope3d *rope, void *ws, size_t ws_bytes, void *stream);
 
-/* Training on strided tensors (no rotary positions): gla_fwd_framecausal_states
- * and the frame-causal backward on views, e.g. q, k, v read straight from a
- * fused [B, N, 3, H, d] projection without copies.
+/* Training on strided tensors, with optional rotary positions: the forward
+ * with its state record and the backward of both modes on views, e.g. q, k, v
+ * read straight from a fused [B, N, 3, H, d] projection without copies.
  *
  * gla_fwd_framecausal_states_ex: gla_fwd_framecausal_states with q, k, v, g,
- * o as views (o may not overlap itself or any input); the workspace of
- * gla_fwd_framecausal_workspace suffices.
+ * o as views (o may not overlap itself or any input) and rope as in
+ * gla_fwd_framecausal_ex (the record then holds the turned-key states); the
+ * workspace of gla_fwd_framecausal_workspace suffices.
  *
  * gla_bwd_framecausal_ex: the backward on views -- q, k, v, g, dO inputs; dq,
  * dk, dv, dg outputs, which may not overlap themselves, one another (each
@@ -330,16 +331,27 @@ gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *v, const fl
  * interleaved in one fused buffer are refused with GLA_ERR_ALIAS), any input
  * or the workspace. states NULL: the states are recomputed (workspace
  * gla_bwd_framecausal_workspace); else the record written by
- * gla_fwd_framecausal_states(_ex) for the same inputs (workspace
- * gla_bwd_framecausal_states_workspace). Results are bitwise those of the
- * contiguous calls on copies of the same tensors. */
+ * gla_fwd_framecausal_states(_ex) for the same inputs and rope (workspace
+ * gla_bwd_framecausal_states_workspace). Without rope, results are bitwise
+ * those of the contiguous calls on copies of the same tensors.
+ *
+ * gla_bwd_bidir_ex: the backward of gla_fwd_bidir_ex over N = F * T tokens
+ * (the frames only place the rotary positions), views as above; workspace
+ * gla_bwd_bidir_ex_workspace (that of gla_bwd_bidir for N without rope).
+ *
+ * Rotary positions (rope != NULL): the gradients of the rotary form of
+ * gla_fwd_framecausal_ex / gla_fwd_bidir_ex (the chain rule through it: the
+ * numerator's adjoints of phi(q) and phi(k) turn back by R^T before the
+ * normaliser's terms are added). With rope the gradient kernels run on the
+ * vector ALU in fp32 (the recompute of the states keeps the matrix cores and
+ * their table limit, GLA_ERR_UNSUPPORTED beyond it). */
 gla_status gla_fwd_framecausal_states_ex(const gla_tensor *q, const gla_tensor *k,
                                          const gla_tensor *v, const gla_tensor *g,
                                          const float *gamma, const float *S_in, const float *z_in,
                                          const gla_tensor *o, float *S_out, float *z_out,
                                          float *states, int B, int H, int F, int T, int d,
-                                         gla_dtype dt, float eps, void *ws, size_t ws_bytes,
-                                         void *stream);
+                                         gla_dtype dt, float eps, const gla_rope3d *rope,
+                                         void *ws, size_t ws_bytes, void *stream);
 
 gla_status gla_bwd_framecausal_ex(const gla_tensor *q, const gla_tensor *k, const gla_tensor *v,
                                   const gla_tensor *g, const float *gamma, const float *S_in,
@@ -348,7 +360,16 @@ gla_status gla_bwd_framecausal_ex(const gla_tensor *q, const gla_tensor *k, cons
                                   const gla_tensor *dk, const gla_tensor *dv,
                                   const gla_tensor *dg, float *dgamma, float *dS_in,
                                   float *dz_in, int B, int H, int F, int T, int d, gla_dtype dt,
-                                  float eps, void *ws, size_t ws_bytes, void *stream);
+                                  float eps, const gla_rope3d *rope, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+size_t gla_bwd_bidir_ex_workspace(int B, int H, int F, int T, int d, const gla_rope3d *rope);
+
+gla_status gla_bwd_bidir_ex(const gla_tensor *q, const gla_tensor *k, const gla_tensor *v,
+                            const gla_tensor *g, const gla_tensor *dO, const gla_tensor *dq,
+                            const gla_tensor *dk, const gla_tensor *dv, const gla_tensor *dg,
+                            int B, int H, int F, int T, int d, gla_dtype dt, float eps,
+                            const gla_rope3d *rope, void *ws, size_t ws_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *gla_status_string(gla_status s);
@@ -357,9 +378,11 @@ const char *gla_status_string(gla_status s);
 const char *gla_last_error(void);
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
-int gla_version(void); /* 10400: adds gla_fwd_framecausal_states_ex and
-                        gla_bwd_framecausal_ex (10300: the *_states calls; 10200:
-                        gla_softmax_anchor; 10100: the *_ex entry points) */
+int gla_version(void); /* 10500: rotary positions in the training calls
+                        (gla_fwd_framecausal_states_ex, gla_bwd_framecausal_ex take
+                        rope) and gla_bwd_bidir_ex (10400: the two training calls on
+                        views; 10300: the *_states calls; 10200: gla_softmax_anchor;
+                        10100: the *_ex entry points) */
 
 /* ---- kernel timing for measurement tools ---------------------------------
  * Between gla_profile_begin and gla_profile_end, every kernel launched by the

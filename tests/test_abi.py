@@ -51,7 +51,7 @@ def test_status_strings(lib):
     for s in range(9):
         assert lib.gla_status_string(s).decode()
     assert lib.gla_status_string(99).decode() == "unknown status"
-    assert lib.gla_version() == 10400
+    assert lib.gla_version() == 10500
 
 
 def test_workspace_sizes(lib):
@@ -335,7 +335,7 @@ def test_strided_training_validation(lib):
             inter(0), inter(1), inter(2), contig(FAKE + 0x2000000), p(FAKE + 0x3000000), None,
             None, p(states), contig(FAKE + 0x4000000), None, None, dq, dk,
             contig(FAKE + 0x5000000), contig(FAKE + 0x6000000), None, None, None, 1, H, 2, N // 2,
-            d, BF16, ctypes.c_float(1e-6), p(FAKE + 0x8000000), wsb, None)
+            d, BF16, ctypes.c_float(1e-6), None, p(FAKE + 0x8000000), wsb, None)
 
     # inputs interleaved in one fused buffer are fine (only outputs are checked)
     assert bwd(contig(FAKE + 0x7000000), contig(FAKE + 0x7100000), wsb=0) == WS
@@ -350,4 +350,42 @@ def test_strided_training_validation(lib):
     f = lib.gla_fwd_framecausal_states_ex
     assert f(inter(0), inter(1), inter(2), contig(FAKE + 0x2000000), p(FAKE + 0x3000000), None,
              None, contig(FAKE + 0x4000000), None, None, None, 1, H, 2, N // 2, d, BF16,
-             ctypes.c_float(1e-6), p(FAKE + 0x8000000), 1 << 30, None) == NULL
+             ctypes.c_float(1e-6), None, p(FAKE + 0x8000000), 1 << 30, None) == NULL
+
+
+def test_rotary_training_validation(lib):
+    """Rotary positions in the training calls: the same checks as the forward
+    (grid, sections, the matrix-core table of the states' recompute), before
+    any launch; gla_bwd_bidir_ex's workspace follows the frames with them."""
+    H, F, T, d = 2, 2, 32, 64
+    N = F * T
+    lay = (N * H * d, d, H * d)
+    t = lambda off: tview(FAKE + off, *lay)  # noqa: E731
+
+    def bwd(rope, T_=T, F_=F):
+        return lib.gla_bwd_framecausal_ex(
+            t(0), t(0x1000000), t(0x2000000), t(0x3000000), p(FAKE + 0x5000000), None, None,
+            None, t(0x4000000), None, None, t(0x6000000), t(0x7000000), t(0x9000000),
+            t(0xA000000), None, None, None, 1, H, F_, T_, d, BF16, ctypes.c_float(1e-6), rope,
+            p(FAKE + 0xB000000), 1 << 30, None)
+
+    assert bwd(rope3d(gh=3)) == SHAPE
+    assert bwd(rope3d(dw=16)) == SHAPE
+    assert bwd(rope3d(theta=-1.0)) == VALUE
+    assert bwd(rope3d(gh=1024, gw=1), T_=1024) == UNSUP
+    assert "rope table" in lib.gla_last_error().decode()
+
+    def bidir_bwd(rope, F_=F, T_=T):
+        return lib.gla_bwd_bidir_ex(
+            t(0), t(0x1000000), t(0x2000000), t(0x3000000), t(0x4000000), t(0x6000000),
+            t(0x7000000), t(0x9000000), t(0xA000000), 1, H, F_, T_, d, BF16,
+            ctypes.c_float(1e-6), rope, p(FAKE + 0xB000000), 1 << 30, None)
+
+    assert bidir_bwd(rope3d(gh=3)) == SHAPE
+    assert bidir_bwd(rope3d(), F_=-1) == SHAPE
+    assert bidir_bwd(rope3d(), F_=0, T_=T) == OK  # no tokens
+    r = gla.Rope3D(23, 40, 24, 20, 20, 10000.0)
+    assert gla.gla_bwd_bidir_ex_workspace(1, 32, 21, 920, 64, r) == \
+        gla.gla_bwd_framecausal_workspace(1, 32, 21, 920, 64)
+    assert gla.gla_bwd_bidir_ex_workspace(1, 32, 21, 920, 64) == \
+        gla.gla_bwd_bidir_workspace(1, 32, 21 * 920, 64)
