@@ -218,13 +218,9 @@ def main():
             b["beta"] = torch.sigmoid(torch.randn(b["q"].shape[:3], generator=gen, device=dev))
         wsb = max(gla.gla_gdn_framecausal_workspace(w.B, w.H, b["gamma"].shape[-1], w.T, d)
                   for b in blocks)
-    if bwd and ex:
-        print("bench.py: the backward takes contiguous tensors without rotary positions",
-              file=sys.stderr)
-        sys.exit(2)
     saved = args.saved_states
-    if saved and (ex or mode != "framecausal" or args.mixer != "gla"):
-        print("bench.py: --saved-states goes with the contiguous frame-causal linear mixer",
+    if saved and (mode != "framecausal" or args.mixer != "gla"):
+        print("bench.py: --saved-states goes with the frame-causal linear mixer",
               file=sys.stderr)
         sys.exit(2)
     if saved and not bwd:
@@ -246,18 +242,19 @@ def main():
             zb = torch.zeros_like(z)
             for i, b in enumerate(blocks):
                 s_in[i] = (Sb.clone(), zb.clone())
-                _, Sb, zb = gla.gla_fwd_framecausal(b["q"], b["k"], b["v"], b["g"], b["gamma"],
-                                                    Sb, zb, eps=w.eps, return_state=True)
+                _, Sb, zb = gla.gla_fwd_framecausal_ex(b["q"], b["k"], b["v"], b["g"],
+                                                       b["gamma"], Sb, zb, eps=w.eps,
+                                                       rope=ropes[i], return_state=True)
             for gd in grads:
                 gd["dS_in"] = torch.empty_like(S)
                 gd["dz_in"] = torch.empty_like(z)
         if saved:  # the forward's record of every frame's state, made before timing
-            for b, si in zip(blocks, s_in):
-                _, b["states"] = gla.gla_fwd_framecausal_states(
+            for b, si, r in zip(blocks, s_in, ropes):
+                _, b["states"] = gla.gla_fwd_framecausal_states_ex(
                     b["q"], b["k"], b["v"], b["g"], b["gamma"], si[0] if si else None,
-                    si[1] if si else None, eps=w.eps)
+                    si[1] if si else None, eps=w.eps, rope=r)
         if mode == "bidir":
-            wsb = gla.gla_bwd_bidir_workspace(w.B, w.H, w.N, d)
+            wsb = gla.gla_bwd_bidir_ex_workspace(w.B, w.H, w.F, w.T, d, ropes[0])
         elif saved:
             wsb = max(gla.gla_bwd_framecausal_states_workspace(
                 w.B, w.H, b["gamma"].shape[-1], w.T, d) for b in blocks)
@@ -269,15 +266,23 @@ def main():
     def step_bwd():
         if mode == "bidir":
             b = blocks[0]
-            gla.gla_bwd_bidir(b["q"], b["k"], b["v"], b["g"], b["dO"], eps=w.eps, out=grads[0],
-                              workspace=ws)
+            if ex:
+                gla.gla_bwd_bidir_ex(b["q"], b["k"], b["v"], b["g"], b["dO"], eps=w.eps,
+                                     rope=ropes[0], frames=w.F, out=grads[0], workspace=ws)
+            else:
+                gla.gla_bwd_bidir(b["q"], b["k"], b["v"], b["g"], b["dO"], eps=w.eps,
+                                  out=grads[0], workspace=ws)
             return
         dS = dz = None  # the stream's last block first
         for i in reversed(range(len(blocks))):
             b, si = blocks[i], s_in[i]
             kw = dict(S_in=si[0] if si else None, z_in=si[1] if si else None, dS_out=dS,
                       dz_out=dz, eps=w.eps, out=grads[i], workspace=ws)
-            if saved:
+            if ex:  # views and/or rotary positions
+                r = gla.gla_bwd_framecausal_ex(b["q"], b["k"], b["v"], b["g"], b["gamma"],
+                                               b["dO"], states=b.get("states"), rope=ropes[i],
+                                               **kw)
+            elif saved:
                 r = gla.gla_bwd_framecausal_states(b["q"], b["k"], b["v"], b["g"], b["gamma"],
                                                    b["states"], b["dO"], **kw)
             else:
@@ -429,7 +434,8 @@ def main():
         elif gdn:
             cpu, parity = cpu_baseline_gdn(args, w, blocks, outs, value)
         elif bwd:
-            cpu, parity = cpu_baseline_bwd(args, w, mode, blocks, grads, value)
+            cpu, parity = cpu_baseline_bwd(args, w, mode, blocks, grads, value,
+                                           ropes[0].as_dict() if args.rope else None)
         else:
             cpu, parity = cpu_baseline(args, w, mode, blocks, outs, value,
                                        ropes[0].as_dict() if args.rope else None)
@@ -642,9 +648,10 @@ def cpu_baseline_gdn(args, w, blocks, outs, gpu_value):
     return cpu, parity
 
 
-def cpu_baseline_bwd(args, w, mode, blocks, grads, gpu_value):
-    """Time the fp64 backward oracle on a bounded sample of heads (the whole
-    stream at once), scale to tokens/s, and check dq, dk, dv, dg of those heads."""
+def cpu_baseline_bwd(args, w, mode, blocks, grads, gpu_value, rope=None):
+    """Time the fp64 backward oracle (with rotary positions if rope) on a
+    bounded sample of heads (the whole stream at once), scale to tokens/s, and
+    check dq, dk, dv, dg of those heads."""
     import numpy as np
     import torch
 
@@ -667,11 +674,14 @@ def cpu_baseline_bwd(args, w, mode, blocks, grads, gpu_value):
     print("bench: CPU backward oracle on %d heads, %d threads" % (nh, threads), file=sys.stderr,
           flush=True)
     t0 = time.perf_counter()
+    # the whole stream at once: its first frame sits at temporal position 0
+    r0 = dict(rope, frame_offset=0) if rope is not None else None
     if mode == "bidir":
-        ref = oracle.backward(oracle.BIDIR, x["q"], x["k"], x["v"], x["g"], x["dO"], eps=w.eps)
+        ref = oracle.backward(oracle.BIDIR, x["q"], x["k"], x["v"], x["g"], x["dO"], eps=w.eps,
+                              F=w.F if r0 else None, T=w.T if r0 else None, rope=r0)
     else:
         ref = oracle.backward(oracle.FRAMECAUSAL, x["q"], x["k"], x["v"], x["g"], x["dO"],
-                              gamma=gamma, eps=w.eps)
+                              gamma=gamma, eps=w.eps, rope=r0)
     el = time.perf_counter() - t0
     cpu_tokens_per_s = nh * w.N / el / w.H
     cpu = {"value": round(cpu_tokens_per_s, 1), "unit": "tokens/s", "cores": int(threads),
