@@ -44,9 +44,16 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
   constexpr int64_t E = (int64_t)D * D + D;
   __shared__ float sS[kSInLds ? D * D : 1];
   __shared__ float sz[D];
-  __shared__ float sq[TT][D];   // phi(q), turned with kRope
-  __shared__ float sqd[kRope ? TT : 1][D];  // kRope: phi(q) unturned
-  __shared__ float sdn[TT][D];  // dnum
+  // token rows padded by CG floats: the two token rows a half-wave reads sit
+  // 16 banks apart, so row reads that differ by column group do not collide
+  constexpr int PITCH = D + CG;
+  __shared__ float sq[TT][PITCH];   // phi(q), turned with kRope
+  __shared__ float sqd[kRope ? TT : 1][PITCH];  // kRope: phi(q) unturned
+  __shared__ float sdn[TT][PITCH];  // dnum
+  // kRope: the pairs' frequencies, and the tile's turns from the staging (used
+  // again to turn S_f dnum back)
+  __shared__ double sfreq[kRope ? D / 2 : 1];
+  __shared__ float2 scs[kRope ? TT : 1][kRope ? D / 2 : 1];
   __shared__ float sred[TT][CG];
   __shared__ float sdd[TT];     // dden
 
@@ -59,6 +66,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
   const int64_t t1 = min(t0 + read_len, T);
 
   const float *Sg = st + (bh * F + (state_frame >= 0 ? state_frame : f)) * sstride;  // S_f
+  if constexpr (kRope)
+    for (int pp = tid; pp < D / 2; pp += kThreads) sfreq[pp] = pair_freq(rope, pp);
   if (kSInLds)
     for (int e = tid; e < D * D; e += kThreads) sS[e] = Sg[e];
   for (int e = tid; e < D; e += kThreads) sz[e] = Sg[D * D + e];
@@ -90,7 +99,9 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
         }
         sqd[tt][2 * pp] = a;
         sqd[tt][2 * pp + 1] = b;
-        const float2 ab = rotate_pair(a, b, token_rope_cs(rope, f, (int)(c0 + tt), pp));
+        const float2 cs = token_rope_cs_freq(rope, f, (int)(c0 + tt), pp, sfreq[pp]);
+        scs[tt][pp] = cs;
+        const float2 ab = rotate_pair(a, b, cs);
         sq[tt][2 * pp] = ab.x;
         sq[tt][2 * pp + 1] = ab.y;
       }
@@ -148,12 +159,17 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
         for (int c = 0; c < 4; ++c) {
           const float *Srow = kSInLds ? sS + (4 * cg + c) * D : Sg + (4 * cg + c) * D;
           float acc = 0.f;
-          for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sdn[tl][j], acc);
+          // each column group starts its sweep at its own column: the rows
+          // 4cg + c of S (D floats apart) then fall in distinct banks
+          for (int jj = 0; jj < D; ++jj) {
+            const int j = (jj + cg) & (D - 1);
+            acc = fmaf(Srow[j], sdn[tl][j], acc);
+          }
           u[c] = acc;
         }
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
-          const float2 cs = token_rope_cs(rope, f, (int)(c0 + tl), 2 * cg + hp);
+          const float2 cs = scs[tl][2 * cg + hp];
           const float2 back = rotate_pair(u[2 * hp], u[2 * hp + 1], make_float2(cs.x, -cs.y));
           u[2 * hp] = back.x;
           u[2 * hp + 1] = back.y;
@@ -169,7 +185,12 @@ __global__ __launch_bounds__(kThreads) void bwd_q_valu_kernel(
           const int i = 4 * cg + c;
           const float *Srow = kSInLds ? sS + i * D : Sg + i * D;
           float acc = dden * sz[i];
-          for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sdn[tl][j], acc);
+          // each column group starts its sweep at its own column: the rows
+          // 4cg + c of S (D floats apart) then fall in distinct banks
+          for (int jj = 0; jj < D; ++jj) {
+            const int j = (jj + cg) & (D - 1);
+            acc = fmaf(Srow[j], sdn[tl][j], acc);
+          }
           dqo[c] = sq[tl][i] > 0.f ? acc : 0.f;
         }
       }
@@ -205,9 +226,12 @@ __global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
   constexpr int64_t E = (int64_t)D * D + D;
   __shared__ float sSh[kSInLds ? D * D : 1];
   __shared__ float szh[D];
-  __shared__ float sk[TT][D];  // phi(k), turned with kRope
-  __shared__ float skd[kRope ? TT : 1][D];  // kRope: phi(k) unturned
-  __shared__ float sv[TT][D];
+  constexpr int PITCH = D + CG;  // padded token rows, as in bwd_q_valu_kernel
+  __shared__ float sk[TT][PITCH];  // phi(k), turned with kRope
+  __shared__ float skd[kRope ? TT : 1][PITCH];  // kRope: phi(k) unturned
+  __shared__ float sv[TT][PITCH];
+  __shared__ double sfreq[kRope ? D / 2 : 1];  // kRope: as in bwd_q_valu_kernel
+  __shared__ float2 scs[kRope ? TT : 1][kRope ? D / 2 : 1];
 
   const int tid = threadIdx.x;
   const int64_t wg = blockIdx.x;
@@ -219,6 +243,8 @@ __global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
   if (t0 >= t1) return;
 
   const float *Sh = gs + ((bh * F + (adj_frame >= 0 ? adj_frame : f)) * (int64_t)R) * E;  // adjoint of S_f
+  if constexpr (kRope)
+    for (int pp = tid; pp < D / 2; pp += kThreads) sfreq[pp] = pair_freq(rope, pp);
   if (kSInLds)
     for (int e = tid; e < D * D; e += kThreads) sSh[e] = Sh[e];
   for (int e = tid; e < D; e += kThreads) szh[e] = Sh[D * D + e];
@@ -246,7 +272,9 @@ __global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
         }
         skd[tt][2 * pp] = a;
         skd[tt][2 * pp + 1] = b;
-        const float2 ab = rotate_pair(a, b, token_rope_cs(rope, f, (int)(c0 + tt), pp));
+        const float2 cs = token_rope_cs_freq(rope, f, (int)(c0 + tt), pp, sfreq[pp]);
+        scs[tt][pp] = cs;
+        const float2 ab = rotate_pair(a, b, cs);
         sk[tt][2 * pp] = ab.x;
         sk[tt][2 * pp + 1] = ab.y;
         sv[tt][2 * pp] = va;
@@ -271,12 +299,15 @@ __global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
         for (int c = 0; c < 4; ++c) {
           const float *Srow = kSInLds ? sSh + (4 * cg + c) * D : Sh + (4 * cg + c) * D;
           float acc = 0.f;
-          for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sv[tl][j], acc);
+          for (int jj = 0; jj < D; ++jj) {  // staggered start, as in bwd_q_valu_kernel
+            const int j = (jj + cg) & (D - 1);
+            acc = fmaf(Srow[j], sv[tl][j], acc);
+          }
           u[c] = acc;
         }
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
-          const float2 cs = token_rope_cs(rope, f, (int)(c0 + tl), 2 * cg + hp);
+          const float2 cs = scs[tl][2 * cg + hp];
           const float2 back = rotate_pair(u[2 * hp], u[2 * hp + 1], make_float2(cs.x, -cs.y));
           u[2 * hp] = back.x;
           u[2 * hp + 1] = back.y;
@@ -292,7 +323,10 @@ __global__ __launch_bounds__(kThreads) void bwd_k_valu_kernel(
           const int i = 4 * cg + c;
           const float *Srow = kSInLds ? sSh + i * D : Sh + i * D;
           float acc = szh[i];
-          for (int j = 0; j < D; ++j) acc = fmaf(Srow[j], sv[tl][j], acc);
+          for (int jj = 0; jj < D; ++jj) {  // staggered start, as in bwd_q_valu_kernel
+            const int j = (jj + cg) & (D - 1);
+            acc = fmaf(Srow[j], sv[tl][j], acc);
+          }
           dko[c] = sk[tl][i] > 0.f ? acc : 0.f;
         }
       }

@@ -66,16 +66,26 @@ template <> struct Elem<bf16_t> {
 };
 
 // ---- 3D rotary positions -------------------------------------------------
-// (cos a, sin a) for a = pos * theta^(-j/m), m > 0. The angle is formed and
-// reduced to [-pi, pi] in double precision, so the fp32 sincosf sees a small
-// argument at any position.
-__device__ inline float2 rope_cs(double pos, int j, int m, double log_theta) {
+// (cos a, sin a) for a = pos * freq (freq = theta^(-j/m), m > 0). The angle is
+// formed and reduced to [-pi, pi] in double precision, so the fp32 sincosf sees
+// a small argument at any position.
+__device__ inline float2 rope_cs_at(double pos, double freq) {
   constexpr double kTwoPi = 6.283185307179586476925286766559;
-  const double a = pos * exp(-((double)j / (double)m) * log_theta);
+  const double a = pos * freq;
   const double r = a - kTwoPi * rint(a * (1.0 / kTwoPi));
   float s, c;
   sincosf((float)r, &s, &c);
   return make_float2(c, s);
+}
+
+// theta^(-j/m), formed in double precision
+__device__ inline double rope_freq(int j, int m, double log_theta) {
+  return exp(-((double)j / (double)m) * log_theta);
+}
+
+// (cos a, sin a) for a = pos * theta^(-j/m)
+__device__ inline float2 rope_cs(double pos, int j, int m, double log_theta) {
+  return rope_cs_at(pos, rope_freq(j, m, log_theta));
 }
 
 // (y, x) = (l / gw, l % gw) for 0 <= l < 2^31: the double quotient is off by
@@ -104,6 +114,23 @@ __device__ float2 token_rope_cs(const R &r, int f, int l, int p) {
   grid_pos(l, r.grid_w, r.inv_gw, y, x);
   if (p < r.Pt + r.Ph) return rope_cs((double)y, p - r.Pt, r.Ph, r.log_theta);
   return rope_cs((double)x, p - r.Pt - r.Ph, r.Pw, r.log_theta);
+}
+
+// The frequency theta^(-j/m) of feature pair p (kernels that turn many tokens
+// keep these in a table and call token_rope_cs_freq: the same angles).
+template <class R>
+__device__ double pair_freq(const R &r, int p) {
+  if (p < r.Pt) return rope_freq(p, r.Pt, r.log_theta);
+  if (p < r.Pt + r.Ph) return rope_freq(p - r.Pt, r.Ph, r.log_theta);
+  return rope_freq(p - r.Pt - r.Ph, r.Pw, r.log_theta);
+}
+
+template <class R>
+__device__ float2 token_rope_cs_freq(const R &r, int f, int l, int p, double freq) {
+  if (p < r.Pt) return rope_cs_at((double)r.frame_offset + f, freq);
+  int y, x;
+  grid_pos(l, r.grid_w, r.inv_gw, y, x);
+  return rope_cs_at((double)(p < r.Pt + r.Ph ? y : x), freq);
 }
 
 // Rotate the feature pair (a, b) by the angle whose (cos, sin) is cs:
