@@ -75,8 +75,8 @@ def parse():
 # the API file and the build flags): a counter record stays valid while these
 # are unchanged.
 KERNEL_SOURCES = {
-    "gla": ["mfma.hip", "valu.hip", "carry.hip"],
-    "bwd": ["bwd.hip", "bwd_mfma.hip", "mfma.hip", "valu.hip", "carry.hip"],
+    "gla": ["mfma.hip", "valu.hip", "carry.hip", "rope_tab.hpp"],
+    "bwd": ["bwd.hip", "bwd_mfma.hip", "mfma.hip", "valu.hip", "carry.hip", "rope_tab.hpp"],
     "gdn": ["gdn.hip", "gdn_mfma.hip"],
     "anchor": ["anchor.hip"],
 }

@@ -15,6 +15,7 @@
 #include "common.hpp"
 #include "mfma_util.hpp"
 #include "plan.hpp"
+#include "rope_tab.hpp"
 
 namespace gla {
 namespace {
@@ -26,6 +27,11 @@ namespace {
 // of the block's BLK = 32 WPP tokens: a wave holds one set of A fragments.
 // k and v rows are staged in LDS (phi(k) and v, the B operands); the outputs
 // go back through LDS as whole rows.
+// kRope (3D rotary positions): dv = Sh^T R phi(k) takes the turned phi(k) as
+// bf16 hi + lo B operands (hi x hi, lo x hi, hi x lo), and dk's rows (a lane
+// holds both features of a pair) turn back by R^T before zh is added; phi(k)
+// unturned stays staged for the ReLU mask. The turns come from an LDS table
+// filled for the workgroup's frame.
 // ---------------------------------------------------------------------------
 constexpr int kBwThreads = 512;
 
@@ -41,17 +47,21 @@ struct BkCfg {
   static constexpr int ROWS_PER_PASS = kBwThreads / ROW_CHUNKS;
 };
 
-template <int D>
+template <int D, bool kRope>
 __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
     View kview, View vview, View dkview, View dvview, int H, const float *__restrict__ gs, int F,
-    int64_t T, int P, int R, int64_t part_len) {
+    int64_t T, int P, int R, int64_t part_len, int adj_frame, RopeK rope) {
   using C = BkCfg<D>;
   static_assert(C::CPT >= 1, "tile too small for the workgroup");
+  constexpr int kTurnBytes = kRope ? C::BLK * C::PITCH : 16;
   __shared__ __attribute__((aligned(16))) char ktile[C::BLK * C::PITCH];
   __shared__ __attribute__((aligned(16))) char vtile[C::BLK * C::PITCH];
   __shared__ __attribute__((aligned(16))) char dktile[C::BLK * C::PITCH];
   __shared__ __attribute__((aligned(16))) char dvtile[C::BLK * C::PITCH];
+  __shared__ __attribute__((aligned(16))) char khtile[kTurnBytes];  // kRope: turned phi(k), hi
+  __shared__ __attribute__((aligned(16))) char kltile[kTurnBytes];  // kRope: turned phi(k), lo
   __shared__ float szh[D];
+  extern __shared__ float2 rope_tab[];  // kRope: RopeK::entries() turns, one frame
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -71,8 +81,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
   if (L <= 0) return;
 
   constexpr int64_t E = (int64_t)D * D + D;
-  const float *Sh = gs + ((bh * F + f) * (int64_t)R) * E;
+  const float *Sh = gs + ((bh * F + (adj_frame >= 0 ? adj_frame : f)) * (int64_t)R) * E;
   if (tid < D) szh[tid] = Sh[D * D + tid];
+  if constexpr (kRope) fill_rope_table(rope_tab, rope, f);  // read after the loop's first barrier
   bf16x8 ahi[C::KS], alo[C::KS];
   if (role_dk)
     frag_direct<D>(Sh, mb, lane, ahi, alo);
@@ -81,6 +92,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
 
   const int c = tid % C::ROW_CHUNKS;
   const int r0 = tid / C::ROW_CHUNKS;
+  [[maybe_unused]] const PieceRope prope(rope, c);
   const int64_t trow0 = (int64_t)f * T + t0;
   const int64_t snk = kview.sn / 8, snv = vview.sn / 8, sdk = dkview.sn / 8, sdv = dvview.sn / 8;
   const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(kview.data) +
@@ -115,8 +127,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
   };
 
   const int tl = 32 * tg + (lane & 31);
-  // role dv multiplies phi(k) rows, role dk multiplies v rows
-  const char *btile = role_dk ? vtile : ktile;
+  // role dv multiplies phi(k) rows (turned with kRope), role dk multiplies v rows
+  const char *btile = role_dk ? vtile : (kRope ? khtile : ktile);
   char *otile = role_dk ? dktile : dvtile;
   const int nblk = (L + C::BLK - 1) / C::BLK;
   load(0);
@@ -126,8 +138,17 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = r0 + i * C::ROWS_PER_PASS;
-      *reinterpret_cast<uint4 *>(ktile + row * C::PITCH + c * 16) = relu8(rk[i]);
+      const uint4 kk = relu8(rk[i]);
+      *reinterpret_cast<uint4 *>(ktile + row * C::PITCH + c * 16) = kk;
       *reinterpret_cast<uint4 *>(vtile + row * C::PITCH + c * 16) = rv[i];
+      if constexpr (kRope) {
+        // the token whose row was loaded (rows past the part repeat the last)
+        const int l = (int)t0 + blk * C::BLK + min(row, L - 1 - blk * C::BLK);
+        uint4 hi, lo;
+        prope.turn_whole(kk, l, rope, rope_tab, hi, lo);
+        *reinterpret_cast<uint4 *>(khtile + row * C::PITCH + c * 16) = hi;
+        *reinterpret_cast<uint4 *>(kltile + row * C::PITCH + c * 16) = lo;
+      }
     }
     sync_lds();
     if (blk + 1 < nblk) load(blk + 1);
@@ -141,6 +162,19 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
           bf16x8, *reinterpret_cast<const uint4 *>(btile + tl * C::PITCH + (16 * ks + 8 * h) * 2));
       acc = mfma_32x32x16(ahi[ks], b, acc);
       acc = mfma_32x32x16(alo[ks], b, acc);
+      if constexpr (kRope) {
+        if (!role_dk) {  // the low parts of the turned keys
+          const bf16x8 bl = __builtin_bit_cast(
+              bf16x8,
+              *reinterpret_cast<const uint4 *>(kltile + tl * C::PITCH + (16 * ks + 8 * h) * 2));
+          acc = mfma_32x32x16(ahi[ks], bl, acc);
+        }
+      }
+    }
+    [[maybe_unused]] int ty = 0, tx = 0;  // kRope: the position of token tl
+    if constexpr (kRope) {
+      const int l = (int)t0 + blk * C::BLK + min(tl, L - 1 - blk * C::BLK);
+      grid_pos(l, rope.grid_w, rope.inv_gw, ty, tx);
     }
     // C layout: element 4rg + e is feature 32mb + 8rg + 4h + e of token tl
 #pragma unroll
@@ -149,6 +183,15 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
       const int off = tl * C::PITCH + fo * 2;
       float o4[4] = {acc[4 * rg], acc[4 * rg + 1], acc[4 * rg + 2], acc[4 * rg + 3]};
       if (role_dk) {
+        if constexpr (kRope) {  // Sh v turns back: features fo .. fo+3 are pairs fo/2, fo/2+1
+#pragma unroll
+          for (int hp = 0; hp < 2; ++hp) {
+            const float2 cs = pair_turn(rope, rope_tab, ty, tx, (fo >> 1) + hp);
+            const float2 back = rotate_pair(o4[2 * hp], o4[2 * hp + 1], make_float2(cs.x, -cs.y));
+            o4[2 * hp] = back.x;
+            o4[2 * hp + 1] = back.y;
+          }
+        }
         const uint2 kk = *reinterpret_cast<const uint2 *>(ktile + off);  // phi(k) > 0 <=> k > 0
         const float k4[4] = {lo_bf16(kk.x), hi_bf16(kk.x), lo_bf16(kk.y), hi_bf16(kk.y)};
 #pragma unroll
@@ -614,9 +657,18 @@ void bwd_q_launch(const BwdPlan &bp, const BwdQArgs &a, hipStream_t s) {
 template <int D>
 void bwd_k_launch(const BwdPlan &bp, const BwdKArgs &a, hipStream_t s) {
   const Plan &p = bp.f;
-  hipLaunchKernelGGL((bwd_k_mfma_kernel<D>), dim3((unsigned)(p.BH * p.F * p.P)),
-                     dim3(kBwThreads), 0, s, a.k, a.v, a.dk, a.dv, a.H, a.gs, p.F, p.T, p.P, p.R,
-                     p.part_len);
+  const dim3 grid((unsigned)(p.BH * p.F * p.P));
+  if (a.rope.on) {
+    RopeK r = a.rope;
+    r.frames = 1;  // a workgroup covers one frame
+    hipLaunchKernelGGL((bwd_k_mfma_kernel<D, true>), grid, dim3(kBwThreads),
+                       (unsigned)(r.entries() * sizeof(float2)), s, a.k, a.v, a.dk, a.dv, a.H,
+                       a.gs, p.F, p.T, p.P, p.R, p.part_len, a.adj_frame, r);
+  } else {
+    hipLaunchKernelGGL((bwd_k_mfma_kernel<D, false>), grid, dim3(kBwThreads), 0, s, a.k, a.v,
+                       a.dk, a.dv, a.H, a.gs, p.F, p.T, p.P, p.R, p.part_len, a.adj_frame,
+                       a.rope);
+  }
 }
 
 }  // namespace

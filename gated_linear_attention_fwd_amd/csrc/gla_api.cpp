@@ -479,13 +479,13 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Path path = select_path(dt, d);
-  if (rk_.on && !want_states && path == Path::kMfma && rk_.entries() > kMaxRopeEntries)
+  if (rk_.on && path == Path::kMfma && rk_.entries() > kMaxRopeEntries)
     return fail(GLA_ERR_UNSUPPORTED,
                 "rope table of %d entries exceeds %d (1 + grid_h*dim_h/2 + grid_w*dim_w/2 + "
                 "8*dim_t/2)",
                 rk_.entries(), kMaxRopeEntries);
-  // the gradient kernels with rotary positions run on the vector ALU
-  const Path gpath = rk_.on ? Path::kValu : path;
+  // with rotary positions the query side runs on the vector ALU
+  const Path qpath = rk_.on ? Path::kValu : path;
   float *wsf = static_cast<float *>(ws);
   float *gsf = wsf + bp.gslot_offset;
   const Plan &p = bp.f;
@@ -506,7 +506,7 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
       GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, ca, s); }), "carry"));
     }
     const BwdQArgs qa{vq, vg, vdo, vdq, vdg, H, fst, gsf, eps, rk_, (bidir && !flat) ? p.F - 1 : -1};
-    GLA_TRY(launched(timed(kKindBwdQ, s, [&] { return launch_bwd_q(bp, dt, gpath, qa, s); }),
+    GLA_TRY(launched(timed(kKindBwdQ, s, [&] { return launch_bwd_q(bp, dt, qpath, qa, s); }),
                      "bwd_q"));
   }
   float *dgp = (causal && dgamma && p.F > 0) ? wsf + bp.dgp_offset : nullptr;
@@ -524,7 +524,7 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
                    "rev_scan"));
   if (have_tokens) {
     const BwdKArgs ka{vk, vv, vdk, vdv, H, gsf, rk_, (bidir && !flat) ? 0 : -1};
-    GLA_TRY(launched(timed(kKindBwdK, s, [&] { return launch_bwd_k(bp, dt, gpath, ka, s); }),
+    GLA_TRY(launched(timed(kKindBwdK, s, [&] { return launch_bwd_k(bp, dt, path, ka, s); }),
                      "bwd_k"));
   }
   if (dgp)
