@@ -233,6 +233,10 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
 // Wave w of a role takes feature block mb = w % MB and tokens 32 (w / MB)..
 // After the last block, G (reduced over the waves that split its k-steps) and
 // gz (reduced over the threads of a column piece) go to the split's gslot.
+// kRope (3D rotary positions): num and G take the turned phi(q), staged as
+// bf16 hi + lo tiles (three MFMAs per step instead of two); den, gz and the
+// ReLU mask the unturned one; S dnum^T's rows (a lane holds both features of
+// a pair) turn back by R^T before dden z is added.
 // ---------------------------------------------------------------------------
 #define GLA_BQ_GROUP_BARRIER() __builtin_amdgcn_sched_barrier(0)
 
@@ -260,17 +264,21 @@ struct BqCfg {
   static constexpr int GL_FLOATS = kGInLds ? KSPLIT * D * GLP : 1;
 };
 
-template <int D>
+template <int D, bool kRope>
 __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
     View qview, View gview, View doview, View dqview, View dgview, int H,
     const float *__restrict__ st, int64_t sstride, float *__restrict__ gs, int F, int64_t T,
-    int R, int64_t read_len, float eps) {
+    int R, int64_t read_len, float eps, int state_frame, RopeK rope) {
   using C = BqCfg<D>;
   static_assert(C::CPT >= 1, "tile too small for the workgroup");
-  // six row tiles in one array; after the last block it holds the G reduction
+  // six row tiles in one array (eight with kRope); after the last block it
+  // holds the G reduction
   constexpr int TILE = C::BLK * C::PITCH;
   static_assert(6 * TILE >= 4 * 16 * 64 * 4, "LDS too small for the G reduction");
-  __shared__ __attribute__((aligned(16))) char smem[6 * TILE];
+  __shared__ __attribute__((aligned(16))) char smem[(kRope ? 8 : 6) * TILE];
+  [[maybe_unused]] char *const qhi = smem + 6 * TILE;  // kRope: turned phi(q), hi
+  [[maybe_unused]] char *const qlo = smem + 7 * TILE;  // kRope: turned phi(q), lo
+  extern __shared__ float2 rope_tab[];                 // kRope: turns of one frame
   char *const qtile = smem;              // phi(q)
   char *const gtile = smem + TILE;       // g, then dg
   char *const otile = smem + 2 * TILE;   // dO
@@ -299,8 +307,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
   const int L = (int)max(t1 - t0, (int64_t)0);
 
   constexpr int64_t E = (int64_t)D * D + D;
-  const float *Sg = st + (bh * F + f) * sstride;  // S_f
+  const float *Sg = st + (bh * F + (state_frame >= 0 ? state_frame : f)) * sstride;  // S_f
   if (tid < D) szf[tid] = Sg[D * D + tid];
+  if constexpr (kRope) fill_rope_table(rope_tab, rope, f);  // read after the loop's first barrier
   bf16x8 ahi[C::KS], alo[C::KS];
   if (role_q)
     frag_direct<D>(Sg, mb, lane, ahi, alo);
@@ -324,6 +333,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 
   const int c = tid % C::ROW_CHUNKS;
   const int r0 = tid / C::ROW_CHUNKS;
+  [[maybe_unused]] const PieceRope prope(rope, c);
+  // the turned phi(q) tiles: B operands of num, A operands of G
+  const char *const qnum = kRope ? qhi : qtile;
   float gz8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) gz8[e] = 0.f;
@@ -391,6 +403,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       const int row = r0 + i * C::ROWS_PER_PASS;
       const uint4 w = relu8(rq[i]);
       *reinterpret_cast<uint4 *>(qtile + row * C::PITCH + c * 16) = w;
+      if constexpr (kRope) {
+        // the token whose row was loaded (rows past the split repeat the last)
+        const int l = (int)t0 + blk * C::BLK + min(row, L - 1 - blk * C::BLK);
+        uint4 th, tlo;
+        prope.turn_whole(w, l, rope, rope_tab, th, tlo);
+        *reinterpret_cast<uint4 *>(qhi + row * C::PITCH + c * 16) = th;
+        *reinterpret_cast<uint4 *>(qlo + row * C::PITCH + c * 16) = tlo;
+      }
       float zc[8];
       if constexpr (kKeep) {
         qkeep[i] = w;
@@ -438,10 +458,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       // num^T for features 32mb.., tokens 32tg..; then dg and the sums dh . h
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 b = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4 *>(qtile + tl * C::PITCH + (16 * ks + 8 * h) * 2));
+        const int boff = tl * C::PITCH + (16 * ks + 8 * h) * 2;
+        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qnum + boff));
         acc = mfma_32x32x16(ahi[ks], b, acc);
         acc = mfma_32x32x16(alo[ks], b, acc);
+        if constexpr (kRope) {
+          const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qlo + boff));
+          acc = mfma_32x32x16(ahi[ks], bl, acc);
+        }
       }
       const float inv = inv_s[tl];
       float part = 0.f;
@@ -490,6 +514,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 #pragma unroll
       for (int m = 0; m < C::MB; ++m) dsum += ddp[m][tl];
       const float dden = -dsum * inv_s[tl];
+      [[maybe_unused]] int ty = 0, tx = 0;  // kRope: the position of token tl
+      if constexpr (kRope) {
+        const int l = (int)t0 + blk * C::BLK + min(tl, L - 1 - blk * C::BLK);
+        grid_pos(l, rope.grid_w, rope.inv_gw, ty, tx);
+      }
 #pragma unroll
       for (int rgp = 0; rgp < 4; ++rgp) {  // unrolled as above
         GLA_BQ_GROUP_BARRIER();
@@ -497,9 +526,19 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
         const int off = tl * C::PITCH + fo * 2;
         const uint2 qv = *reinterpret_cast<const uint2 *>(qtile + off);
         const float q4[4] = {lo_bf16(qv.x), hi_bf16(qv.x), lo_bf16(qv.y), hi_bf16(qv.y)};
+        float a4[4] = {acc[4 * rgp], acc[4 * rgp + 1], acc[4 * rgp + 2], acc[4 * rgp + 3]};
+        if constexpr (kRope) {  // features fo .. fo+3 are pairs fo/2, fo/2 + 1: turn back
+#pragma unroll
+          for (int hp = 0; hp < 2; ++hp) {
+            const float2 cs = pair_turn(rope, rope_tab, ty, tx, (fo >> 1) + hp);
+            const float2 back = rotate_pair(a4[2 * hp], a4[2 * hp + 1], make_float2(cs.x, -cs.y));
+            a4[2 * hp] = back.x;
+            a4[2 * hp + 1] = back.y;
+          }
+        }
         float d4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d4[e] = q4[e] > 0.f ? fmaf(dden, szf[fo + e], acc[4 * rgp + e]) : 0.f;
+        for (int e = 0; e < 4; ++e) d4[e] = q4[e] > 0.f ? fmaf(dden, szf[fo + e], a4[e]) : 0.f;
         *reinterpret_cast<uint2 *>(dqtile + off) =
             make_uint2(pack_bf16x2(d4[0], d4[1]), pack_bf16x2(d4[2], d4[3]));
       }
@@ -520,7 +559,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 #pragma unroll
         for (int kt = 0; kt < C::KT; ++kt) {
           if (C::KSPLIT > 1 && kt % C::KSPLIT != rw % C::KSPLIT) continue;
-          const bf16x8 fa = tr_fragment((const lds_char *)qtile, kt * 16 + frag_row,
+          const bf16x8 fa = tr_fragment((const lds_char *)qnum, kt * 16 + frag_row,
                                         32 * bi + frag_col, C::PITCH);
           const bf16x8 fh = tr_fragment((const lds_char *)dnhi, kt * 16 + frag_row,
                                         32 * bj + frag_col, C::PITCH);
@@ -528,6 +567,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
                                         32 * bj + frag_col, C::PITCH);
           blk_acc = mfma_32x32x16(fa, fh, blk_acc);
           blk_acc = mfma_32x32x16(fa, fl, blk_acc);
+          if constexpr (kRope) {  // the low parts of the turned queries
+            const bf16x8 fal = tr_fragment((const lds_char *)qlo, kt * 16 + frag_row,
+                                           32 * bi + frag_col, C::PITCH);
+            blk_acc = mfma_32x32x16(fal, fh, blk_acc);
+          }
         }
         if constexpr (C::kGInLds) {
           // add into this wave's image (rows m = 8(e/4) + 4h + e%4 of column n)
@@ -649,9 +693,19 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
 template <int D>
 void bwd_q_launch(const BwdPlan &bp, const BwdQArgs &a, hipStream_t s) {
   const Plan &p = bp.f;
-  hipLaunchKernelGGL((bwd_q_mfma_kernel<D>), dim3((unsigned)(p.BH * p.F * p.R)),
-                     dim3(kBwThreads), 0, s, a.q, a.g, a.dO, a.dq, a.dg, a.H, a.st.base,
-                     a.st.stride, a.gs, p.F, p.T, p.R, p.read_len, a.eps);
+  const dim3 grid((unsigned)(p.BH * p.F * p.R));
+  if (a.rope.on) {
+    RopeK r = a.rope;
+    r.frames = 1;  // a workgroup covers one frame
+    hipLaunchKernelGGL((bwd_q_mfma_kernel<D, true>), grid, dim3(kBwThreads),
+                       (unsigned)(r.entries() * sizeof(float2)), s, a.q, a.g, a.dO, a.dq, a.dg,
+                       a.H, a.st.base, a.st.stride, a.gs, p.F, p.T, p.R, p.read_len, a.eps,
+                       a.state_frame, r);
+  } else {
+    hipLaunchKernelGGL((bwd_q_mfma_kernel<D, false>), grid, dim3(kBwThreads), 0, s, a.q, a.g,
+                       a.dO, a.dq, a.dg, a.H, a.st.base, a.st.stride, a.gs, p.F, p.T, p.R,
+                       p.read_len, a.eps, a.state_frame, a.rope);
+  }
 }
 
 template <int D>

@@ -484,8 +484,6 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
                 "rope table of %d entries exceeds %d (1 + grid_h*dim_h/2 + grid_w*dim_w/2 + "
                 "8*dim_t/2)",
                 rk_.entries(), kMaxRopeEntries);
-  // with rotary positions the query side runs on the vector ALU
-  const Path qpath = rk_.on ? Path::kValu : path;
   float *wsf = static_cast<float *>(ws);
   float *gsf = wsf + bp.gslot_offset;
   const Plan &p = bp.f;
@@ -506,7 +504,7 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
       GLA_TRY(launched(timed(kKindCarry, s, [&] { return launch_carry(p, ca, s); }), "carry"));
     }
     const BwdQArgs qa{vq, vg, vdo, vdq, vdg, H, fst, gsf, eps, rk_, (bidir && !flat) ? p.F - 1 : -1};
-    GLA_TRY(launched(timed(kKindBwdQ, s, [&] { return launch_bwd_q(bp, dt, qpath, qa, s); }),
+    GLA_TRY(launched(timed(kKindBwdQ, s, [&] { return launch_bwd_q(bp, dt, path, qa, s); }),
                      "bwd_q"));
   }
   float *dgp = (causal && dgamma && p.F > 0) ? wsf + bp.dgp_offset : nullptr;

@@ -171,7 +171,7 @@ __device__ __forceinline__ float carry_weight(const float *gamma_slab, int f, in
 //               dv = Sh_f^T phi(k);
 //      with rotary positions the numerator side takes turned features (S_f and
 //      Sh_f hold turned keys and queries) and its adjoints turn back before the
-//      normaliser's terms are added (bwd_q then on the vector ALU); bidirectional with positions runs on the
+//      normaliser's terms are added; bidirectional with positions runs on the
 //      frames with no decay, every frame reading the last frame's S and frame
 //      0's adjoint (the sums over all frames);
 //   5. dgamma   one thread per (slab, frame): the partial sums in fixed order.
@@ -194,7 +194,7 @@ struct BwdQArgs {
   FrameStates st;         // the forward's S_f
   float *gs;              // gslots
   float eps;
-  RopeK rope;             // on: vector-ALU kernel only
+  RopeK rope;             // on: turned queries (both kernels)
   int state_frame;        // >= 0: every frame reads that frame's S (bidirectional with positions)
 };
 
