@@ -342,9 +342,9 @@ gla_status gla_state_carry_ex(const gla_tensor *k, const gla_tensor *v, const fl
  * Rotary positions (rope != NULL): the gradients of the rotary form of
  * gla_fwd_framecausal_ex / gla_fwd_bidir_ex (the chain rule through it: the
  * numerator's adjoints of phi(q) and phi(k) turn back by R^T before the
- * normaliser's terms are added). With rope the gradient kernels run on the
- * vector ALU in fp32 (the recompute of the states keeps the matrix cores and
- * their table limit, GLA_ERR_UNSUPPORTED beyond it). */
+ * normaliser's terms are added). The matrix-core kernels take the turned
+ * features as bf16 hi + lo pairs and the same table limit as the forward
+ * (GLA_ERR_UNSUPPORTED beyond it). */
 gla_status gla_fwd_framecausal_states_ex(const gla_tensor *q, const gla_tensor *k,
                                          const gla_tensor *v, const gla_tensor *g,
                                          const float *gamma, const float *S_in, const float *z_in,
