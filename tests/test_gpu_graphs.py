@@ -55,6 +55,11 @@ CALLS = {
     "bwd_ex": lambda t: gla.gla_bwd_framecausal_ex(
         t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"], states=t["states"], S_in=t["S"],
         z_in=t["z"], need_state_grad=True),
+    "bwd_rope": lambda t: gla.gla_bwd_framecausal_ex(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"], S_in=t["S"], z_in=t["z"],
+        rope=gla.Rope3D.video(10, 15, 64, frame_offset=2), need_state_grad=True),
+    "bidir_bwd_rope": lambda t: gla.gla_bwd_bidir_ex(
+        t["q"], t["k"], t["v"], t["g"], t["dO"], rope=gla.Rope3D.video(10, 15, 64)),
     "gdn": lambda t: gla.gla_gdn_framecausal(t["q"], t["k"], t["v"], t["beta"], t["gamma"],
                                              t["S"], return_state=True),
     "anchor": lambda t: gla.gla_softmax_anchor(t["q"], t["k"], t["v"], t["g"], T=150, n_sink=1,

@@ -217,3 +217,39 @@ def test_autograd_with_rotary_positions_equals_direct_calls(save_states):
     wb = gla.gla_bwd_bidir_ex(*(leaf[n].detach() for n in "qkvg"), w, rope=rope)
     for a, n in zip(gb, ("dq", "dk", "dv", "dg")):
         assert torch.equal(a, wb[n]), n
+
+
+def draw_sweep(n, seed):
+    """Irregular shapes, drawn once from a fixed seed: head dimension, dtype,
+    batch, heads, frames, the latent grid (tokens per frame), frame offset,
+    carried state."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        d = int(rng.choice([16, 32, 64, 128]))
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        cases.append((dtype, int(rng.integers(1, 3)), int(rng.integers(1, 4)), d,
+                      int(rng.integers(1, 6)), int(rng.integers(1, 13)), int(rng.integers(1, 23)),
+                      int(rng.integers(-3, 9)), bool(rng.random() < 0.5)))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_sweep(10, seed=909), ids=ident)
+def test_sweep_of_irregular_shapes(case):
+    """Both modes, against the rotary backward oracle, at the drawn shapes."""
+    dtype, B, H, d, F, gh, gw, off, carry = case
+    x, rope = inputs(case, seed=3900 + d + gh * gw)
+    t = {n: dev(a) for n, a in x.items()}
+    opt = {n: t.get(n) for n in ("S_in", "z_in", "dS_out", "dz_out")}
+    got = gla.gla_bwd_framecausal_ex(t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"],
+                                     rope=rope, need_state_grad=True, **opt)
+    ref = oracle.backward(oracle.FRAMECAUSAL, x["q"], x["k"], x["v"], x["g"], x["dO"],
+                          gamma=x["gamma"], S_in=x.get("S_in"), z_in=x.get("z_in"),
+                          dS_out=x.get("dS_out"), dz_out=x.get("dz_out"), rope=rope)
+    errs = {n: slab_rel_err(f64(got[n]), ref[n]) for n in ("dq", "dk", "dv", "dg")}
+    errs.update({n: max_abs_over_max(f64(got[n]), ref[n]) for n in ("dgamma", "dS_in", "dz_in")})
+    gb = gla.gla_bwd_bidir_ex(t["q"], t["k"], t["v"], t["g"], t["dO"], rope=rope)
+    rb = oracle.backward(oracle.BIDIR, x["q"], x["k"], x["v"], x["g"], x["dO"], F=F, T=gh * gw,
+                         rope=rope)
+    errs.update({"bidir_" + n: slab_rel_err(f64(gb[n]), rb[n]) for n in ("dq", "dk", "dv", "dg")})
+    check(errs, dtype, "rope bwd sweep %s" % ident(case))

@@ -63,6 +63,9 @@ CALLS = {
     "bwd_ex": lambda t, s: gla.gla_bwd_framecausal_ex(
         t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"], states=None, S_in=t["S"],
         z_in=t["z"], need_state_grad=True, stream=s),
+    "bwd_rope": lambda t, s: gla.gla_bwd_framecausal_ex(
+        t["q"], t["k"], t["v"], t["g"], t["gamma"], t["dO"], S_in=t["S"], z_in=t["z"],
+        rope=gla.Rope3D.video(10, 20, 64, frame_offset=1), need_state_grad=True, stream=s),
     "gdn": lambda t, s: gla.gla_gdn_framecausal(t["q"], t["k"], t["v"], t["beta"], t["gamma"],
                                                 t["S"], return_state=True, stream=s),
     "anchor": lambda t, s: gla.gla_softmax_anchor(t["q"], t["k"], t["v"], t["g"], T=200,
