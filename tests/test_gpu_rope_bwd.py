@@ -75,6 +75,8 @@ CASES = [
     ("bf16", 2, 2, 64, 5, 8, 16, 0, False),
     ("bf16", 1, 2, 128, 3, 6, 11, 7, True),
     ("bf16", 1, 2, 32, 2, 16, 16, 1, True),
+    # one token per frame, a temporal position near the 2^30 limit
+    ("bf16", 1, 2, 64, 4, 1, 1, (1 << 29) + 3, True),
 ]
 
 
