@@ -225,24 +225,60 @@ def _require_device(*ts: Optional[torch.Tensor]) -> torch.device:
     return dev
 
 
-def _require_device_any_layout(*ts: Optional[torch.Tensor]) -> torch.device:
-    """Like _require_device, for the strided entry points: any layout whose
-    last (feature) axis has unit stride."""
+def _require_device_any_layout(*views: Optional[torch.Tensor],
+                               dense=()) -> torch.device:
+    """Like _require_device, for the strided entry points: the token tensors
+    (``views``, [B, H, N, d]) may have any layout whose last (feature) axis has
+    unit stride; every other tensor (``dense``: gamma, states, the state
+    record, fp32 gradients, the workspace) reaches the library as a bare
+    pointer and must be contiguous."""
     dev = None
-    for t in ts:
+    for t in views:
+        if t is None:
+            continue
+        if t.dim() != 4:
+            raise ValueError("token tensors must be [B, H, N, d] views")
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("the feature axis must have unit stride")
+    for t in dense:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("gamma, the states, the state record, the fp32 gradients and the "
+                             "workspace must be contiguous")
+    for t in (*views, *dense):
         if t is None:
             continue
         if not t.is_cuda:
             raise ValueError("libgla runs on the GPU only; got a tensor on %s" % t.device)
-        if t.dim() == 4 and t.shape[-1] > 1 and t.stride(-1) != 1:
-            raise ValueError("the feature axis must have unit stride")
-        if t.dim() != 4 and not t.is_contiguous():
-            raise ValueError("gamma and the states must be contiguous")
         if dev is None:
             dev = t.device
         elif t.device != dev:
             raise ValueError("all tensors must be on one device")
     return dev
+
+
+def _dense(t: Optional[torch.Tensor], shape, name: str) -> None:
+    """A float32 tensor the library reads or writes through a bare pointer
+    (states, normalisers, their gradients): exact shape, dense layout."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32:
+        raise ValueError("%s must be float32 %s, got %s %s"
+                         % (name, list(shape), t.dtype, list(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _states(B: int, H: int, d: int, **ts: Optional[torch.Tensor]) -> None:
+    """_dense for S-like ([B, H, d, d]: names starting with S or dS) and
+    z-like ([B, H, d]) tensors."""
+    for name, t in ts.items():
+        square = name.startswith("S") or name.startswith("dS")
+        _dense(t, (B, H, d, d) if square else (B, H, d), name)
+
+
+def _like(t: torch.Tensor, ref: torch.Tensor, name: str) -> None:
+    if t.shape != ref.shape or t.dtype != ref.dtype:
+        raise ValueError("%s must match q's shape and dtype" % name)
 
 
 def _view(t: Optional[torch.Tensor]):
@@ -318,6 +354,7 @@ def gla_fwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     ref = _qkvg(q, k, v, g)
     dt = _dtype_code(ref)
     o = torch.empty_like(ref) if out is None else out
+    _like(o, ref, "out")
     dev = _require_device(q, k, v, g, o, workspace)
     B, H, N, d = ref.shape
     ws, wsb = _workspace(lib.gla_fwd_bidir_workspace(B, H, N, d), dev, workspace)
@@ -354,6 +391,8 @@ def gla_fwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     if want_state and z_out is None:
         z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
     o = torch.empty_like(ref) if out is None else out
+    _like(o, ref, "out")
+    _states(B, H, d, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
     dev = _require_device(q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, workspace)
     ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_fwd_framecausal(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in),
@@ -399,6 +438,8 @@ def gla_fwd_framecausal_states(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     elif states.shape != (B, H, F, d * d + d) or states.dtype != torch.float32:
         raise ValueError("states must be float32 [B, H, F, d*d + d]")
     o = torch.empty_like(ref) if out is None else out
+    _like(o, ref, "out")
+    _states(B, H, d, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
     dev = _require_device(q, k, v, g, gamma, S_in, z_in, o, states, S_out, z_out, workspace)
     ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_fwd_framecausal_states(
@@ -429,6 +470,7 @@ def gla_state_carry(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
         S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
     if z_out is None:
         z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
+    _states(B, H, d, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
     dev = _require_device(k, v, gamma, S_in, z_in, S_out, z_out, workspace)
     ws, wsb = _workspace(lib.gla_state_carry_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_state_carry(_ptr(k), _ptr(v), _ptr(gamma), _ptr(S_in), _ptr(z_in),
@@ -473,7 +515,7 @@ def gla_fwd_bidir_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     o = torch.empty_like(q) if out is None else out
     if o.shape != ref.shape or o.dtype != ref.dtype:
         raise ValueError("out must match q's shape and dtype")
-    dev = _require_device_any_layout(q, k, v, g, o, workspace)
+    dev = _require_device_any_layout(q, k, v, g, o, dense=(workspace,))
     ws, wsb = _workspace(lib.gla_fwd_bidir_ex_workspace(B, H, F, T, d, _rope(rope)), dev,
                          workspace)
     _check(lib.gla_fwd_bidir_ex(_view(q), _view(k), _view(v), _view(g), _view(o), B, H, F, T, d,
@@ -510,7 +552,9 @@ def gla_fwd_framecausal_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     o = torch.empty_like(q) if out is None else out
     if o.shape != ref.shape or o.dtype != ref.dtype:
         raise ValueError("out must match q's shape and dtype")
-    dev = _require_device_any_layout(q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, workspace)
+    _states(B, H, d, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
+    dev = _require_device_any_layout(q, k, v, g, o,
+                                     dense=(gamma, S_in, z_in, S_out, z_out, workspace))
     ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_fwd_framecausal_ex(_view(q), _view(k), _view(v), _view(g), _ptr(gamma),
                                       _ptr(S_in), _ptr(z_in), _view(o), _ptr(S_out), _ptr(z_out),
@@ -557,8 +601,9 @@ def gla_fwd_framecausal_states_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     o = torch.empty_like(q) if out is None else out
     if o.shape != ref.shape or o.dtype != ref.dtype:
         raise ValueError("out must match q's shape and dtype")
-    dev = _require_device_any_layout(q, k, v, g, gamma, S_in, z_in, o, states, S_out, z_out,
-                                     workspace)
+    _states(B, H, d, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
+    dev = _require_device_any_layout(q, k, v, g, o, dense=(gamma, S_in, z_in, states, S_out,
+                                                           z_out, workspace))
     ws, wsb = _workspace(lib.gla_fwd_framecausal_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_fwd_framecausal_states_ex(
         _view(q), _view(k), _view(v), _view(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _view(o),
@@ -588,7 +633,8 @@ def gla_state_carry_ex(k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
         S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
     if z_out is None:
         z_out = torch.empty((B, H, d), dtype=torch.float32, device=ref.device)
-    dev = _require_device_any_layout(k, v, gamma, S_in, z_in, S_out, z_out, workspace)
+    _states(B, H, d, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
+    dev = _require_device_any_layout(k, v, dense=(gamma, S_in, z_in, S_out, z_out, workspace))
     ws, wsb = _workspace(lib.gla_state_carry_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_state_carry_ex(_view(k), _view(v), _ptr(gamma), _ptr(S_in), _ptr(z_in),
                                   _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt, _rope(rope),
@@ -679,8 +725,13 @@ def gla_bwd_framecausal_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     if need_state_grad:
         out.setdefault("dS_in", torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device))
         out.setdefault("dz_in", torch.empty((B, H, d), dtype=torch.float32, device=ref.device))
-    dev = _require_device_any_layout(q, k, v, g, gamma, states, dO, S_in, z_in, dS_out, dz_out,
-                                     workspace, *out.values())
+    _states(B, H, d, S_in=S_in, z_in=z_in, dS_out=dS_out, dz_out=dz_out,
+            dS_in=out.get("dS_in"), dz_in=out.get("dz_in"))
+    _dense(out["dgamma"], (B, H, F), "dgamma")
+    dev = _require_device_any_layout(
+        q, k, v, g, dO, out["dq"], out["dk"], out["dv"], out["dg"],
+        dense=(gamma, states, S_in, z_in, dS_out, dz_out, out["dgamma"], out.get("dS_in"),
+               out.get("dz_in"), workspace))
     if states is None:
         nbytes = lib.gla_bwd_framecausal_workspace(B, H, F, T, d)
     else:
@@ -717,7 +768,8 @@ def gla_bwd_bidir_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
         out.setdefault(n, torch.empty(ref.shape, dtype=ref.dtype, device=ref.device))
         if out[n].shape != ref.shape or out[n].dtype != ref.dtype:
             raise ValueError("%s must match q's shape and dtype" % n)
-    dev = _require_device_any_layout(q, k, v, g, dO, workspace, *out.values())
+    dev = _require_device_any_layout(q, k, v, g, dO, out["dq"], out["dk"], out["dv"],
+                                     out["dg"], dense=(workspace,))
     ws, wsb = _workspace(lib.gla_bwd_bidir_ex_workspace(B, H, F, T, d, _rope(rope)), dev,
                          workspace)
     _check(lib.gla_bwd_bidir_ex(_view(q), _view(k), _view(v), _view(g), _view(dO),
@@ -755,6 +807,11 @@ def _bwd_framecausal(q, k, v, g, gamma, states, dO, S_in, z_in, dS_out, dz_out, 
     if need_state_grad:
         out.setdefault("dS_in", torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device))
         out.setdefault("dz_in", torch.empty((B, H, d), dtype=torch.float32, device=ref.device))
+    for n in ("dq", "dk", "dv", "dg"):
+        _like(out[n], ref, n)
+    _states(B, H, d, S_in=S_in, z_in=z_in, dS_out=dS_out, dz_out=dz_out,
+            dS_in=out.get("dS_in"), dz_in=out.get("dz_in"))
+    _dense(out["dgamma"], (B, H, F), "dgamma")
     dev = _require_device(q, k, v, g, gamma, states, dO, S_in, z_in, dS_out, dz_out, workspace,
                           *out.values())
     grads = (_ptr(dO), _ptr(dS_out), _ptr(dz_out), _ptr(out["dq"]), _ptr(out["dk"]),
@@ -789,6 +846,8 @@ def gla_bwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     out = dict(out or {})
     for n in ("dq", "dk", "dv", "dg"):
         out.setdefault(n, torch.empty_like(ref))
+    for n in ("dq", "dk", "dv", "dg"):
+        _like(out[n], ref, n)
     dev = _require_device(q, k, v, g, dO, workspace, *out.values())
     ws, wsb = _workspace(lib.gla_bwd_bidir_workspace(B, H, N, d), dev, workspace)
     _check(lib.gla_bwd_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dO), _ptr(out["dq"]),
@@ -830,6 +889,10 @@ def gla_gdn_framecausal(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Ten
     if want_state and S_out is None:
         S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=ref.device)
     o = None if q is None else (torch.empty_like(ref) if out is None else out)
+    if o is not None:
+        _like(o, ref, "out")
+    _dense(S_in, (B, H, d, d), "S_in")
+    _dense(S_out, (B, H, d, d), "S_out")
     dev = _require_device(q, k, v, beta, gamma, S_in, o, S_out, workspace)
     ws, wsb = _workspace(lib.gla_gdn_framecausal_workspace(B, H, F, T, d), dev, workspace)
     _check(lib.gla_gdn_framecausal(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma),
@@ -865,6 +928,7 @@ def gla_softmax_anchor(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: tor
     if scale is None:
         scale = 1.0 / d ** 0.5
     o = torch.empty_like(q) if out is None else out
+    _like(o, q, "out")
     dev = _require_device(q, k, v, g, o)
     _check(lib.gla_softmax_anchor(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), B, H, Nq // T,
                                   Nk // T, T, d, _dtype_code(k), int(bool(causal)), int(n_sink),

@@ -57,6 +57,10 @@ class FrameCausal(torch.autograd.Function):
             dS_out = torch.zeros((B, H, d, d), dtype=torch.float32, device=q.device)
         if dz_out is None and dS_out is not None:
             dz_out = torch.zeros((B, H, d), dtype=torch.float32, device=q.device)
+        # a loss that reduces the state (S_out.sum(), z_out.mean()) hands over
+        # expanded gradients with zero strides; the call reads dense arrays
+        if dS_out is not None:
+            dS_out, dz_out = dS_out.contiguous(), dz_out.contiguous()
         need_state = S_in is not None and (ctx.needs_input_grad[5] or ctx.needs_input_grad[6])
         grads = gla_bwd_framecausal_ex(q, k, v, g, gamma, dO.contiguous(), states=states,
                                        S_in=S_in, z_in=z_in, dS_out=dS_out, dz_out=dz_out,

@@ -30,9 +30,28 @@ namespace {
 constexpr int kCarryThreads = 256;
 constexpr int kGroupBatch = 16;
 
+// Sum of a frame's P parts (P > 4), left to right as in the unrolled case:
+// loads go out eight at a time so that they overlap, the additions keep their
+// order (bidirectional 720p/5s: 61 parts per slab).
+__device__ __forceinline__ float sum_parts(const float *src, int P, int64_t E) {
+  constexpr int kBatch = 8;
+  float a = src[0];
+  for (int p0 = 1; p0 < P; p0 += kBatch) {
+    float x[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) x[j] = src[(int64_t)min(p0 + j, P - 1) * E];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (p0 + j < P) a += x[j];
+  }
+  return a;
+}
+
 // kP > 0: frames of kP parts, their loads unrolled so that a batch's loads
-// are all in flight at once; kP == 0: any P, in a loop (720p/5s: 21 frames of
-// 4 parts took 30 us with the loop alone).
+// are all in flight at once; kP == 0: more parts, summed by sum_parts, for
+// the groups that exist only (a frame of many parts is typically the one
+// frame of a bidirectional call, where reloading it for every slot of the
+// batch cost 16 times its reads).
 template <int kP>
 __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
     float *ws, const float *__restrict__ gamma, const float *S_in,
@@ -67,12 +86,13 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       const int gc = ok ? grp : NG - 1;
       const int last = min(F, (gc + 1) * G) - 1;
       const float *src = slots + (int64_t)last * frame_stride;
-      float a = src[0];
+      float a = 0.f;
       if constexpr (kP > 0) {
+        a = src[0];
 #pragma unroll
         for (int p = 1; p < kP; ++p) a += src[(int64_t)p * E];
       } else {
-        for (int p = 1; p < P; ++p) a += src[(int64_t)p * E];
+        if (ok) a = sum_parts(src, P, E);
       }
       float wj = 1.f;
       if (gm_slab)

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -242,6 +243,13 @@ gla_status make_rope(const gla_rope3d *r, int F, int64_t T, int d, RopeK *out) {
   if (r->frame_offset <= -(1 << 30) || r->frame_offset >= (1 << 30) || F >= (1 << 30))
     return fail(GLA_ERR_VALUE, "rope frame_offset=%d and F=%d must be below 2^30 in magnitude",
                 r->frame_offset, F);
+  // the table offsets (RopeK::x_base, t_base, entries) are int: bound the
+  // entry count in 64 bits first
+  const int64_t entries = 1 + (int64_t)r->grid_h * (r->dim_h / 2) +
+                          (int64_t)r->grid_w * (r->dim_w / 2) + kMaxGroupFrames * (r->dim_t / 2);
+  if (entries > INT32_MAX)
+    return fail(GLA_ERR_SHAPE, "rope grid %d x %d gives a turn table of %lld entries (over 2^31)",
+                r->grid_h, r->grid_w, (long long)entries);
   RopeK k;
   k.on = 1;
   k.grid_h = r->grid_h;

@@ -85,14 +85,29 @@ size_t gla_fwd_framecausal_workspace(int B, int H, int F, int T, int d);
 size_t gla_state_carry_workspace(int B, int H, int F, int T, int d);
 
 /* Bidirectional (whole-sequence, non-causal) gated linear attention.
- * Reads q, k, v, g [B][H][N][d]; writes o [B][H][N][d]. */
+ * Defining passages: the O(N) gated linear-attention mixer of the hybrid DiT
+ * ("SANA-Video 2.0" project page, section "Hybrid Linear-Softmax Attention"),
+ * in the form a denoising DiT applies it to a clip it diffuses as a whole:
+ * every token reads the one state summed over all tokens ("SANA-Video" ICLR
+ * 2026 oral talk: the video model's linear-attention DiT is the image model's,
+ * and a block is diffused jointly, all of its tokens seeing one another).
+ * Equals the frame-causal mode's last frame with gamma = 1 (no decay).
+ * Reads q, k, v, g [B][H][N][d]; writes o [B][H][N][d]. The workspace holds
+ * one fp32 state of d*d + d floats per (slab, part); nothing in it needs to
+ * be initialised. */
 gla_status gla_fwd_bidir(const void *q, const void *k, const void *v, const void *g, void *o,
                          int B, int H, int64_t N, int d, gla_dtype dt, float eps, void *ws,
                          size_t ws_bytes, void *stream);
 
 /* Frame-causal gated linear attention with per-frame decay gamma [B][H][F].
+ * Defining passages: block-causal linear attention over video frames with a
+ * constant-size carried state ("SANA-Video" ICLR 2026 oral talk, block-causal
+ * linear attention and block KV cache passages), gated by a per-frame decay
+ * ("SANA-WM" analysis page, method components: frame-wise decay gates).
  * S_in/z_in: carried-in state (both NULL: zero state). S_out/z_out: state after
- * the last frame (both NULL: not written). o [B][H][F*T][d]. */
+ * the last frame (both NULL: not written). o [B][H][F*T][d]. The workspace
+ * holds fp32 states of d*d + d floats per (slab, frame, part) plus one per
+ * (slab, group of frames); nothing in it needs to be initialised. */
 gla_status gla_fwd_framecausal(const void *q, const void *k, const void *v, const void *g,
                                const float *gamma, const float *S_in, const float *z_in,
                                void *o, float *S_out, float *z_out, int B, int H, int F, int T,
@@ -100,8 +115,13 @@ gla_status gla_fwd_framecausal(const void *q, const void *k, const void *v, cons
                                void *stream);
 
 /* Block-cache commit: the state after F more frames, from k, v and gamma only
- * (no queries, no output). Equals the S_out/z_out of gla_fwd_framecausal on the
- * same inputs. S_out and z_out are required. */
+ * (no queries, no output). Defining passage: the block KV cache of the
+ * "SANA-Video" ICLR 2026 oral talk (block KV cache passage): the D x D state
+ * of a finished block is cached and the next block's KV contribution is added
+ * to it; with the frame-wise decay of the "SANA-WM" analysis page (method
+ * components), S_out = S_{F-1} of the frame-causal recurrence above, started
+ * from S_in. Equals the S_out/z_out of gla_fwd_framecausal on the same
+ * inputs. S_out and z_out are required (S_out may be S_in). */
 gla_status gla_state_carry(const void *k, const void *v, const float *gamma, const float *S_in,
                            const float *z_in, float *S_out, float *z_out, int B, int H, int F,
                            int T, int d, gla_dtype dt, void *ws, size_t ws_bytes, void *stream);

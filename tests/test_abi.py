@@ -389,3 +389,74 @@ def test_rotary_training_validation(lib):
         gla.gla_bwd_framecausal_workspace(1, 32, 21, 920, 64)
     assert gla.gla_bwd_bidir_ex_workspace(1, 32, 21, 920, 64) == \
         gla.gla_bwd_bidir_workspace(1, 32, 21 * 920, 64)
+
+
+def test_bindings_refuse_non_dense_states():
+    """The state tensors (S, z, their gradients, gamma and the state record)
+    reach the library as bare pointers: the bindings refuse views that are not
+    dense or of the wrong shape, also on the strided (_ex) entry points, whose
+    token tensors may be any view with a unit feature stride. (CPU tensors: the
+    checks run before the device check.)"""
+    import torch
+    B, H, F, T, d = 2, 2, 2, 32, 16
+    x = torch.zeros(B, H, F * T, d)
+    gamma = torch.ones(B, H, F)
+    S = torch.zeros(B, H, d, d)
+    z = torch.zeros(B, H, d)
+    buf = torch.zeros(B, H, d, 2 * d)
+    S_all = torch.zeros(B, 2 * H, d, d)
+    bad_S = {"a column slice": buf[..., :d], "a head slice with B > 1": S_all[:, 1:1 + H],
+             "a transposed view": S.transpose(2, 3)}
+    for what, S_bad in bad_S.items():
+        assert not S_bad.is_contiguous(), what
+        for fn in (gla.gla_fwd_framecausal_ex, gla.gla_fwd_framecausal):
+            with pytest.raises(ValueError, match="contiguous"):
+                fn(x, x, x, x, gamma, S_bad, z)
+            with pytest.raises(ValueError, match="contiguous"):
+                fn(x, x, x, x, gamma, S, z, S_out=S_bad, z_out=z)
+        with pytest.raises(ValueError, match="contiguous"):
+            gla.gla_state_carry_ex(x, x, gamma, S_bad, z)
+        with pytest.raises(ValueError, match="contiguous"):
+            gla.gla_bwd_framecausal_ex(x, x, x, x, gamma, x, S_in=S, z_in=z, dS_out=S_bad,
+                                       dz_out=z)
+    with pytest.raises(ValueError, match="contiguous"):
+        gla.gla_fwd_framecausal_ex(x, x, x, x, gamma, S, torch.zeros(B, H, 2 * d)[..., ::2])
+    rec = torch.zeros(B, H, d * d + d, F).transpose(2, 3)  # [B, H, F, d*d + d], not dense
+    with pytest.raises(ValueError, match="contiguous"):
+        gla.gla_fwd_framecausal_states_ex(x, x, x, x, gamma, states=rec)
+    with pytest.raises(ValueError, match="contiguous"):
+        gla.gla_bwd_framecausal_ex(x, x, x, x, gamma, x, states=rec)
+    with pytest.raises(ValueError, match="contiguous"):
+        gla.gla_fwd_framecausal_ex(x, x, x, x, torch.ones(B, H, 2 * F)[..., ::2])
+    # shapes: a state for fewer slabs would be read past its end
+    with pytest.raises(ValueError, match=r"S_in must be float32 \[2, 2, 16, 16\]"):
+        gla.gla_fwd_framecausal_ex(x, x, x, x, gamma, S[:1], z[:1])
+    with pytest.raises(ValueError, match="z_out must be float32"):
+        gla.gla_fwd_framecausal(x, x, x, x, gamma, S_out=S, z_out=torch.zeros(B, H, d + 1))
+    with pytest.raises(ValueError, match="dS_out must be float32"):
+        gla.gla_bwd_framecausal(x, x, x, x, gamma, x, dS_out=S.double(), dz_out=z)
+    with pytest.raises(ValueError, match="S_in must be float32"):
+        gla.gla_gdn_framecausal(x, x, x, torch.zeros(B, H, F * T), gamma, S_in=S[:, :1])
+    # outputs of the contiguous calls must match the inputs' shape
+    with pytest.raises(ValueError, match="out must match"):
+        gla.gla_fwd_framecausal(x, x, x, x, gamma, out=torch.zeros(B, H, F * T - 1, d))
+    with pytest.raises(ValueError, match="out must match"):
+        gla.gla_fwd_bidir(x, x, x, x, out=torch.zeros(B, H, F * T, d, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="dq must match"):
+        gla.gla_bwd_bidir(x, x, x, x, x, out={"dq": torch.zeros(B, H, 1, d)})
+    # the token views themselves may be strided: only their feature axis counts
+    xt = torch.zeros(B, F * T, H, d).transpose(1, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        gla.gla_fwd_framecausal_ex(xt, xt, xt, xt, gamma, S, z)
+    with pytest.raises(ValueError, match="unit stride"):
+        gla.gla_fwd_framecausal_ex(torch.zeros(B, H, d, F * T).transpose(2, 3), x, x, x, gamma)
+
+
+def test_rope_table_size_overflow(lib):
+    """A latent grid so large that the rotary table's entry count overflows
+    32-bit arithmetic is refused before any launch (the count is formed in
+    64 bits)."""
+    T = 1 << 26
+    r = rope3d(gh=T, gw=1, dt_=0, dh=128, dw=0)  # grid_h * dim_h / 2 = 2^32 entries
+    assert fc_ex(lib, T=T, F=1, H=1, d=128, rope=r) == SHAPE
+    assert "rope" in lib.gla_last_error().decode()

@@ -105,3 +105,25 @@ def test_framecausal_on_a_fused_projection():
     want = gla.gla_bwd_framecausal(*(x.detach().contiguous() for x in (q, k, v, g)), gamma, w)
     for i, n in enumerate(("dq", "dk", "dv")):
         assert torch.equal(dqkv[:, :, i].transpose(1, 2), want[n]), n
+
+
+@pytest.mark.parametrize("save_states", [True, False])
+def test_framecausal_loss_reducing_the_state(save_states):
+    """A loss that reduces the carried state (S_out.sum() + z_out.mean())
+    hands the backward expanded gradients with zero strides: they reach the
+    call as dense arrays, and the gradients equal the direct call's for
+    dS_out = 1 and dz_out = 1 / (B H d)."""
+    t = leaves(seed=13)
+    o, S, z = ga.gla_framecausal(t["q"], t["k"], t["v"], t["g"], t["gamma"], t["S_in"],
+                                 t["z_in"], save_states=save_states, return_state=True)
+    loss = o.float().sum() + S.sum() + z.mean()
+    names = ["q", "k", "v", "g", "gamma", "S_in", "z_in"]
+    got = dict(zip(names, torch.autograd.grad(loss, [t[n] for n in names])))
+    dz = torch.full(t["z_in"].shape, 1.0 / t["z_in"].numel(), device=DEV)
+    want = gla.gla_bwd_framecausal(
+        *(t[n].detach() for n in ("q", "k", "v", "g", "gamma")), torch.ones_like(o),
+        S_in=t["S_in"].detach(), z_in=t["z_in"].detach(), dS_out=torch.ones_like(S),
+        dz_out=dz, need_state_grad=True)
+    for n, m in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("gamma", "dgamma"),
+                 ("S_in", "dS_in"), ("z_in", "dz_in")):
+        assert torch.equal(got[n], want[m]), n
