@@ -50,7 +50,8 @@ __all__ = [
     "gla_bwd_framecausal_states", "gla_bwd_framecausal_states_workspace",
     "gla_fwd_framecausal_states_ex", "gla_bwd_framecausal_ex", "gla_bwd_bidir_ex",
     "gla_bwd_bidir_ex_workspace", "gla_gdn_framecausal",
-    "gla_gdn_framecausal_workspace", "gla_softmax_anchor", "library_path", "load_library",
+    "gla_gdn_framecausal_workspace", "gla_softmax_anchor", "gla_fwd_framecausal_noalloc",
+    "NOALLOC_SCRATCH_BYTES", "library_path", "load_library",
     "profile_begin", "profile_end",
 ]
 
@@ -60,6 +61,8 @@ _lib = None
 
 GLA_F32 = 0
 GLA_BF16 = 1
+# the static device scratch of gla_fwd_framecausal_noalloc (GLA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 192 << 20
 
 
 class GlaError(RuntimeError):
@@ -135,6 +138,8 @@ def load_library():
     lib.gla_state_carry.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
                                     sz, vp]
     lib.gla_state_carry.restype = i32
+    lib.gla_fwd_framecausal_noalloc.argtypes = [vp] * 10 + [i32] * 6 + [f32, vp]
+    lib.gla_fwd_framecausal_noalloc.restype = i32
     tp, rp = ctypes.POINTER(_Tensor), ctypes.POINTER(Rope3D)
     lib.gla_fwd_bidir_ex_workspace.argtypes = [i32, i32, i32, i32, i32, rp]
     lib.gla_fwd_bidir_ex_workspace.restype = sz
@@ -402,6 +407,36 @@ def gla_fwd_framecausal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
                                    _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in, o,
                                                   S_out, z_out, ws)))
     return (o, S_out, z_out) if want_state else o
+
+
+def gla_fwd_framecausal_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                g: torch.Tensor, gamma: torch.Tensor, out: torch.Tensor,
+                                S_in: Optional[torch.Tensor] = None,
+                                z_in: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                                S_out: Optional[torch.Tensor] = None,
+                                z_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """gla_fwd_framecausal with its workspace in the library's static device
+    scratch (NOALLOC_SCRATCH_BYTES per GPU): neither this binding nor the call
+    allocates, so the caller passes ``out`` (and S_out, z_out for the state).
+    Calls that overlap in time on one GPU race on the scratch."""
+    lib = load_library()
+    ref = _qkvg(q, k, v, g)
+    dt = _dtype_code(ref)
+    B, H, N, d = ref.shape
+    F = int(gamma.shape[-1])
+    if gamma.shape != (B, H, F) or gamma.dtype != torch.float32:
+        raise ValueError("gamma must be float32 [B, H, F]")
+    if (F == 0 and N != 0) or (F and N % F):
+        raise ValueError("N=%d is not a multiple of F=%d" % (N, F))
+    T = N // F if F else 0
+    _like(out, ref, "out")
+    _states(B, H, d, S_in=S_in, z_in=z_in, S_out=S_out, z_out=z_out)
+    dev = _require_device(q, k, v, g, gamma, S_in, z_in, out, S_out, z_out)
+    _check(lib.gla_fwd_framecausal_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(S_in), _ptr(z_in), _ptr(out),
+        _ptr(S_out), _ptr(z_out), B, H, F, T, d, dt, eps,
+        _stream_handle(stream, dev, q, k, v, g, gamma, S_in, z_in, out, S_out, z_out)))
+    return out
 
 
 def gla_fwd_framecausal_states(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

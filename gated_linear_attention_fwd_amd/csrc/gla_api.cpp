@@ -38,6 +38,7 @@ hipError_t launch_gdn_readout_mfma(const Plan &p, const GdnReadoutArgs &a, hipSt
 hipError_t launch_gdn_readout_valu(const Plan &p, int dtype, const GdnReadoutArgs &a,
                                    hipStream_t s);
 bool mfma_supports(int d);
+void *noalloc_scratch(hipError_t *err);  // noalloc.hip
 
 namespace {
 
@@ -857,6 +858,29 @@ GLA_EXPORT gla_status gla_fwd_framecausal(const void *q, const void *k, const vo
              F, T, d, dt, eps, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
+GLA_EXPORT gla_status gla_fwd_framecausal_noalloc(const void *q, const void *k, const void *v,
+                                                  const void *g, const float *gamma,
+                                                  const float *S_in, const float *z_in, void *o,
+                                                  float *S_out, float *z_out, int B, int H, int F,
+                                                  int T, int d, gla_dtype dt, float eps,
+                                                  void *stream) {
+  // the size check needs no GPU: refuse before the scratch lookup
+  Plan p;
+  if (B >= 0 && H >= 0 && F >= 0 && T >= 0 && make_plan((int64_t)B * H, F, T, d, &p) &&
+      p.ws_bytes > GLA_NOALLOC_SCRATCH_BYTES)
+    return fail(GLA_ERR_WORKSPACE,
+                "these sizes need %zu bytes of workspace; the static scratch of the no-alloc "
+                "call holds %zu (GLA_NOALLOC_SCRATCH_BYTES): use gla_fwd_framecausal with a "
+                "workspace",
+                p.ws_bytes, (size_t)GLA_NOALLOC_SCRATCH_BYTES);
+  hipError_t e = hipSuccess;
+  void *ws = noalloc_scratch(&e);
+  if (!ws)
+    return fail(GLA_ERR_HIP, "device address of the static scratch: %s", hipGetErrorString(e));
+  return gla_fwd_framecausal(q, k, v, g, gamma, S_in, z_in, o, S_out, z_out, B, H, F, T, d, dt,
+                             eps, ws, GLA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 GLA_EXPORT gla_status gla_fwd_framecausal_ex(const gla_tensor *q, const gla_tensor *k,
                                              const gla_tensor *v, const gla_tensor *g,
                                              const float *gamma, const float *S_in,
@@ -1059,7 +1083,7 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
 
 GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
 
-GLA_EXPORT int gla_version(void) { return 10500; }
+GLA_EXPORT int gla_version(void) { return 10600; }
 
 GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
   if (max_launches < 1 || max_launches > 65536)

@@ -126,6 +126,36 @@ gla_status gla_state_carry(const void *k, const void *v, const float *gamma, con
                            const float *z_in, float *S_out, float *z_out, int B, int H, int F,
                            int T, int d, gla_dtype dt, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- the frame-causal forward without a workspace argument ------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * gla_fwd_framecausal_noalloc computes exactly gla_fwd_framecausal (the same
+ * kernels and plan: the results are bitwise those of gla_fwd_framecausal), with
+ * its workspace in a static device array of GLA_NOALLOC_SCRATCH_BYTES inside the
+ * library instead of a caller's buffer. The call allocates and frees nothing.
+ *  - Limit: sizes whose gla_fwd_framecausal_workspace exceeds
+ *    GLA_NOALLOC_SCRATCH_BYTES (192 MiB: the 720p/60s shape with H = 32,
+ *    d = 64 needs 138 MiB; a 31-frame block at B = 2, H = 40, d = 128, 156 MiB)
+ *    are refused with GLA_ERR_WORKSPACE before any HIP call.
+ *  - Memory: every GPU the library runs this call on holds its own copy of the
+ *    array until the process ends. The first call on a device looks up the
+ *    array's device address there (hipGetSymbolAddress) and keeps it; a
+ *    failure of that lookup returns GLA_ERR_HIP.
+ *  - Concurrency: every call on one GPU uses that GPU's one array. Calls that
+ *    overlap in time on one GPU (other threads, other streams) race on it and
+ *    give undefined results: serialise them, e.g. on one stream. Nothing in the
+ *    array needs to start at zero, and a call leaves it holding that call's
+ *    per-frame states.
+ *  - Arguments, validation and errors otherwise as gla_fwd_framecausal. */
+#define GLA_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+
+gla_status gla_fwd_framecausal_noalloc(const void *q, const void *k, const void *v,
+                                       const void *g, const float *gamma, const float *S_in,
+                                       const float *z_in, void *o, float *S_out, float *z_out,
+                                       int B, int H, int F, int T, int d, gla_dtype dt,
+                                       float eps, void *stream);
+
 /* ---- backward pass ---------------------------------------------------------
  *
  * Gradients of the forward operation above for a loss L, given
@@ -398,11 +428,12 @@ const char *gla_status_string(gla_status s);
 const char *gla_last_error(void);
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
-int gla_version(void); /* 10500: rotary positions in the training calls
+int gla_version(void); /* 10600: gla_fwd_framecausal_noalloc (10500: rotary
+                        positions in the training calls
                         (gla_fwd_framecausal_states_ex, gla_bwd_framecausal_ex take
                         rope) and gla_bwd_bidir_ex (10400: the two training calls on
                         views; 10300: the *_states calls; 10200: gla_softmax_anchor;
-                        10100: the *_ex entry points) */
+                        10100: the *_ex entry points)) */
 
 /* ---- kernel timing for measurement tools ---------------------------------
  * Between gla_profile_begin and gla_profile_end, every kernel launched by the

@@ -51,7 +51,7 @@ def test_status_strings(lib):
     for s in range(9):
         assert lib.gla_status_string(s).decode()
     assert lib.gla_status_string(99).decode() == "unknown status"
-    assert lib.gla_version() == 10500
+    assert lib.gla_version() == 10600
 
 
 def test_workspace_sizes(lib):
@@ -460,3 +460,18 @@ def test_rope_table_size_overflow(lib):
     r = rope3d(gh=T, gw=1, dt_=0, dh=128, dw=0)  # grid_h * dim_h / 2 = 2^32 entries
     assert fc_ex(lib, T=T, F=1, H=1, d=128, rope=r) == SHAPE
     assert "rope" in lib.gla_last_error().decode()
+
+
+def test_noalloc_refuses_sizes_beyond_its_scratch(lib):
+    """gla_fwd_framecausal_noalloc checks the workspace its sizes need against
+    the static scratch before any HIP call (so this runs without a GPU)."""
+    assert gla.NOALLOC_SCRATCH_BYTES == 192 << 20
+    # 720p/60s at H = 32, d = 64 fits; four times the heads does not
+    assert gla.gla_fwd_framecausal_workspace(1, 32, 241, 920, 64) <= gla.NOALLOC_SCRATCH_BYTES
+    assert gla.gla_fwd_framecausal_workspace(2, 40, 31, 920, 128) <= gla.NOALLOC_SCRATCH_BYTES
+    assert gla.gla_fwd_framecausal_workspace(1, 128, 241, 920, 64) > gla.NOALLOC_SCRATCH_BYTES
+    f = lib.gla_fwd_framecausal_noalloc
+    st = f(p(FAKE), p(FAKE), p(FAKE), p(FAKE), p(FAKE), None, None, p(FAKE + 0x100000), None,
+           None, 1, 128, 241, 920, 64, BF16, ctypes.c_float(1e-6), None)
+    assert st == WS
+    assert "static scratch" in lib.gla_last_error().decode()
