@@ -52,7 +52,7 @@ __all__ = [
     "gla_bwd_bidir_ex_workspace", "gla_gdn_framecausal",
     "gla_gdn_framecausal_workspace", "gla_softmax_anchor", "gla_fwd_framecausal_noalloc",
     "NOALLOC_SCRATCH_BYTES", "library_path", "load_library",
-    "profile_begin", "profile_end",
+    "profile_begin", "profile_end", "stream_probe", "PROBE_KINDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -187,6 +187,8 @@ def load_library():
     lib.gla_last_error.argtypes = []
     lib.gla_last_error.restype = ctypes.c_char_p
     lib.gla_version.restype = i32
+    lib.gla_stream_probe.argtypes = [i32, vp, vp, vp, sz, vp]
+    lib.gla_stream_probe.restype = i32
     lib.gla_profile_begin.argtypes = [i32]
     lib.gla_profile_begin.restype = i32
     lib.gla_profile_end.argtypes = [ctypes.POINTER(_KernelTime), i32, ctypes.POINTER(i32)]
@@ -970,6 +972,24 @@ def gla_softmax_anchor(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: tor
                                   int(window), float(scale),
                                   _stream_handle(stream, dev, q, k, v, g, o)))
     return o
+
+
+PROBE_KINDS = ("read", "read_nt", "write", "write_nt", "copy", "copy_nt", "read2_write1",
+               "read2_write1_nt")
+
+
+def stream_probe(kind: str, out: torch.Tensor, a: Optional[torch.Tensor] = None,
+                 b: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One launch of the library's bandwidth probe (``gla_stream_probe``) over
+    ``out.numel() * out.element_size()`` bytes; kind is one of PROBE_KINDS."""
+    lib = load_library()
+    nbytes = out.numel() * out.element_size()
+    for t in (a, b):
+        if t is not None and t.numel() * t.element_size() != nbytes:
+            raise ValueError("probe buffers must have equal sizes")
+    dev = _require_device(out, a, b)
+    _check(lib.gla_stream_probe(PROBE_KINDS.index(kind), _ptr(a), _ptr(b), _ptr(out), nbytes,
+                                _stream_handle(stream, dev, out, a, b)))
 
 
 def profile_begin(max_launches: int = 4096) -> None:

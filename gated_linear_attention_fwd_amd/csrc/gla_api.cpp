@@ -39,6 +39,9 @@ hipError_t launch_gdn_readout_valu(const Plan &p, int dtype, const GdnReadoutArg
                                    hipStream_t s);
 bool mfma_supports(int d);
 void *noalloc_scratch(hipError_t *err);  // noalloc.hip
+hipError_t launch_probe(int kind, const void *a, const void *b, void *out, size_t bytes,
+                        hipStream_t s);  // probe.hip
+int probe_kinds();
 
 namespace {
 
@@ -1084,6 +1087,26 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
 GLA_EXPORT const char *gla_last_error(void) { return g_last_error; }
 
 GLA_EXPORT int gla_version(void) { return 10600; }
+
+GLA_EXPORT gla_status gla_stream_probe(int kind, const void *a, const void *b, void *out,
+                                      size_t bytes, void *stream) {
+  if (kind < 0 || kind >= probe_kinds())
+    return fail(GLA_ERR_VALUE, "probe kind %d not in 0..%d", kind, probe_kinds() - 1);
+  constexpr size_t kRange = size_t(256) << 10;
+  if (bytes == 0 || bytes % kRange)
+    return fail(GLA_ERR_SHAPE, "probe size %zu must be a positive multiple of 256 KiB", bytes);
+  const bool reads_a = kind != 2 && kind != 3, reads_b = kind >= 6;
+  if (!out || (reads_a && !a) || (reads_b && !b))
+    return fail(GLA_ERR_NULL, "probe kind %d needs out%s%s", kind, reads_a ? ", a" : "",
+                reads_b ? ", b" : "");
+  if (!aligned(out, 16) || (a && !aligned(a, 16)) || (b && !aligned(b, 16)))
+    return fail(GLA_ERR_ALIGN, "probe buffers must be 16-byte aligned");
+  const Range ro{out, bytes, "out"};
+  const Range ra{reads_a ? a : nullptr, bytes, "a"}, rb{reads_b ? b : nullptr, bytes, "b"};
+  if (overlap(ro, ra) || overlap(ro, rb)) return fail(GLA_ERR_ALIAS, "probe out overlaps a or b");
+  return launched(launch_probe(kind, a, b, out, bytes, static_cast<hipStream_t>(stream)),
+                  "probe");
+}
 
 GLA_EXPORT gla_status gla_profile_begin(int max_launches) {
   if (max_launches < 1 || max_launches > 65536)

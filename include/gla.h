@@ -459,6 +459,20 @@ typedef struct gla_kernel_time {
 gla_status gla_profile_begin(int max_launches);
 gla_status gla_profile_end(gla_kernel_time *out, int max_out, int *n_out);
 
+/* Streaming bandwidth probe: one launch that moves `bytes` through HBM in the
+ * access pattern of the mixer's kernels (16-byte loads and stores per lane,
+ * whole 1 KiB runs per wave), for measuring the practical ceilings those
+ * kernels are held against. kind: 0 read a, 1 read a nontemporal, 2 write
+ * out, 3 write out nontemporal, 4 copy a to out, 5 the copy nontemporal,
+ * 6 out = a ^ b (two reads and one write, the readout's pattern), 7 that
+ * nontemporal. a, b, out: device buffers of `bytes` bytes each (as the kind
+ * uses them; out is required for every kind: the read kinds may write a few
+ * words into it), 16-byte aligned, out overlapping neither a nor b; `bytes` a
+ * positive multiple of 256 KiB. Errors: GLA_ERR_VALUE (kind), GLA_ERR_SHAPE,
+ * GLA_ERR_NULL, GLA_ERR_ALIGN, GLA_ERR_ALIAS, GLA_ERR_HIP (launch). */
+gla_status gla_stream_probe(int kind, const void *a, const void *b, void *out, size_t bytes,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,3 +57,15 @@ def test_json_line_carries_the_contract_keys():
     # traffic: the committed counter record when the kernel sources match the
     # profiled build, else null
     assert roof["traffic"] is None or roof["traffic"] > 0
+    # per-step spread, the measured ceilings and the other configurations
+    st = d["ms_per_step_stats"]
+    assert st["min"] <= st["median"] <= st["max"] and st["reps"] == 2
+    peak = d["practical_peak"]
+    for k in ("read_GBps", "read_nt_GBps", "copy_GBps", "read2_write1_nt_GBps",
+              "torch_copy_GBps"):
+        assert 0 < peak[k] < 8000, k
+    for name in ("720p_5s_bidir", "720p_5s_framecausal", "720p_60s_stream_d128"):
+        wl = d["workloads"][name]
+        assert wl["ms"]["min"] <= wl["ms"]["median"] <= wl["ms"]["max"], name
+        assert wl["tokens_per_s"] > 0 and 0 < wl["frac_of_hbm_peak"] < 1, name
+        assert wl["parity"]["max_slab_rel_err"] <= wl["parity"]["bar"], name
