@@ -196,11 +196,21 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
   for (int e = 0; e < kSt; ++e) st[e] = 0.f;
 
   // the group's decays, loaded once up front (a load per frame would stall
-  // every frame's write-out for a full memory latency)
-  float gms[C::kGroups ? kMaxGroup : 1];
+  // every frame's write-out for a full memory latency); branch-free, frames
+  // past the group reloading its last one, so that all go out at once (with
+  // a test per load each was a memory round trip of its own)
+  constexpr int kNg = C::kGroups ? kMaxGroup : 1;
+  float gms[kNg];
+  if (gamma) {
+    const float *gsl = gamma + bh * F + f_begin;
 #pragma unroll
-  for (int e = 0; e < (C::kGroups ? kMaxGroup : 1); ++e)
-    gms[e] = (e > 0 && e < nf) ? (gamma ? gamma[bh * F + f_begin + e] : 1.f) : 0.f;
+    for (int e = 0; e < kNg; ++e) gms[e] = gsl[min(e, nf - 1)];
+  } else {
+#pragma unroll
+    for (int e = 0; e < kNg; ++e) gms[e] = 1.f;
+  }
+#pragma unroll
+  for (int e = 0; e < kNg; ++e) gms[e] = (e > 0 && e < nf) ? gms[e] : 0.f;
 
   if constexpr (kRope) {
     fill_rope_table(rope_tab, rope, f_begin);
@@ -480,67 +490,8 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
     fill_rope_table(rope_tab, rope, f);
     sync_lds();
   }
-  bf16x8 ahi[C::KS], alo[C::KS];
-  // S = hi + lo, both bf16: returns hi in the low half, lo in the high half
-  auto split = [&](float sv) -> uint32_t {
-    const uint16_t sh = f32_to_bf16_rne(sv);
-    return (uint32_t)sh | ((uint32_t)f32_to_bf16_rne(sv - bf16_to_f32(sh)) << 16);
-  };
-  {
-    const int jcol = 32 * mb + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      i16x8 hv, lv;
-      if constexpr (kRope) {
-        // rows i = 16ks + 8h + e of S turned by R_t(f)^T: pair (i, i+1) for even e
-        float sv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int idx = (16 * ks + 8 * h + e) * D + jcol;
-          sv[e] = has_carry ? fmaf(w, Cg[idx], Sg[idx]) : Sg[idx];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int pr = 8 * ks + 4 * h + e / 2;
-          const float2 cs = rope_tab[pr < rope.Pt ? rope.t_base() + pr : 0];
-          const float2 ab = rotate_pair(sv[e], sv[e + 1], make_float2(cs.x, -cs.y));
-          sv[e] = ab.x;
-          sv[e + 1] = ab.y;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t hl = split(sv[e]);
-          hv[e] = (short)(hl & 0xFFFFu);
-          lv[e] = (short)(hl >> 16);
-        }
-      } else if (has_carry) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int idx = (16 * ks + 8 * h + e) * D + jcol;
-          const uint32_t hl = split(fmaf(w, Cg[idx], Sg[idx]));
-          hv[e] = (short)(hl & 0xFFFFu);
-          lv[e] = (short)(hl >> 16);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t hl = split(Sg[(16 * ks + 8 * h + e) * D + jcol]);
-          hv[e] = (short)(hl & 0xFFFFu);
-          lv[e] = (short)(hl >> 16);
-        }
-      }
-      ahi[ks] = __builtin_bit_cast(bf16x8, hv);
-      alo[ks] = __builtin_bit_cast(bf16x8, lv);
-      asm volatile("" ::: "memory");  // one k-step of loads in flight at a time (registers)
-    }
-  }
   const int c = tid % C::ROW_CHUNKS;
   const int r0 = tid / C::ROW_CHUNKS;
-  float zc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    zc[e] = has_carry ? fmaf(w, Cg[D * D + 8 * c + e], Sg[D * D + 8 * c + e]) : Sg[D * D + 8 * c + e];
-
   // row strides in 16-byte pieces (host-checked multiples of 8 elements)
   const int64_t snq = qview.sn / 8, sng = gview.sn / 8, sno = oview.sn / 8;
   const uint4 *qb = reinterpret_cast<const uint4 *>(
@@ -572,11 +523,69 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
     qp += C::BLK * snq;
     gp += C::BLK * sng;
   };
+  // the first block's q and g go out before the state: their latency
+  // overlaps the state's
+  load(0);
+  bf16x8 ahi[C::KS], alo[C::KS];
+  // S = hi + lo, both bf16: returns hi in the low half, lo in the high half
+  auto split = [&](float sv) -> uint32_t {
+    const uint16_t sh = f32_to_bf16_rne(sv);
+    return (uint32_t)sh | ((uint32_t)f32_to_bf16_rne(sv - bf16_to_f32(sh)) << 16);
+  };
+  // The fragments are built in one straight run per case (the carry test is
+  // outside the k-step loop, and the normaliser's likewise below), so that the
+  // compiler issues every k-step's loads before it waits: with the test
+  // inside, each k-step and each of the eight normaliser loads was a memory
+  // round trip of its own, 13 (d = 64) to 17 (d = 128) of them before the
+  // first token (720p/5s readout 52 -> 50 us).
+  {
+    const int jcol = 32 * mb + (lane & 31);
+    auto build = [&](auto state_at) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        i16x8 hv, lv;
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[e] = state_at((16 * ks + 8 * h + e) * D + jcol);
+        if constexpr (kRope) {
+          // rows i = 16ks + 8h + e of S turned by R_t(f)^T: pair (i, i+1) for even e
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const int pr = 8 * ks + 4 * h + e / 2;
+            const float2 cs = rope_tab[pr < rope.Pt ? rope.t_base() + pr : 0];
+            const float2 ab = rotate_pair(sv[e], sv[e + 1], make_float2(cs.x, -cs.y));
+            sv[e] = ab.x;
+            sv[e + 1] = ab.y;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t hl = split(sv[e]);
+          hv[e] = (short)(hl & 0xFFFFu);
+          lv[e] = (short)(hl >> 16);
+        }
+        ahi[ks] = __builtin_bit_cast(bf16x8, hv);
+        alo[ks] = __builtin_bit_cast(bf16x8, lv);
+      }
+    };
+    if (has_carry)
+      build([&](int idx) { return fmaf(w, Cg[idx], Sg[idx]); });
+    else
+      build([&](int idx) { return Sg[idx]; });
+  }
+  float zc[8];
+  if (has_carry) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zc[e] = fmaf(w, Cg[D * D + 8 * c + e], Sg[D * D + 8 * c + e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zc[e] = Sg[D * D + 8 * c + e];
+  }
+
   uint4 *op = ob + (int64_t)r0 * sno + c;
 
   const int tl = 32 * tg + (lane & 31);
   const int nblk = (L + C::BLK - 1) / C::BLK;
-  load(0);
   wait_vmem_all();  // no load outstanding into the loop: its waits count its own
   for (int blk = 0; blk < nblk; ++blk) {
     sync_lds();  // the previous block's o rows have been read out of gtile
