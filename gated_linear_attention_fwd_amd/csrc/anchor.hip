@@ -85,10 +85,12 @@ struct AmCfg {
   static_assert(BM * PITCH <= SMEM, "the epilogue tile reuses the K/V buffers");
 };
 
-// Waves per SIMD the compiler must allow: at d = 64 it would take 2 (208
-// VGPRs); 3 fit without spills and measured 9% faster (720p/60s, window of 4).
+// Waves per SIMD the compiler must allow. With the probabilities split into
+// bf16 hi + lo for P V, d = 64 takes 222 VGPRs (2 waves; forcing 3 spills and
+// measured slower) and d = 128 would take 260 (1 wave): held to 2, it spills
+// 16 bytes and runs 20% faster than at 1.
 template <int D>
-constexpr int kAnchorWaves = D == 64 ? 3 : 1;
+constexpr int kAnchorWaves = D == 64 ? 2 : D == 128 ? 2 : 1;
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAnchorWaves<D>))) void
@@ -200,7 +202,14 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
     }
     // online softmax over the block (keys past nv are not there; only the
     // last block of a range is partial)
-    uint32_t pw[2][8];  // probabilities as packed bf16 pairs, per 32-key block
+    // probabilities as packed bf16 pairs, per 32-key block: p = hi + lo, both
+    // bf16, so that P V keeps ~16 bits of p. With one bf16 rounding (2^-9 per
+    // weight against the fp32 normaliser) the output reached 1.4e-2 of the
+    // slab-relative metric in the shape sweep; with the split it sits at the
+    // output's own bf16 rounding (3.9e-3), for one more MFMA per P V step
+    // (720p/60s, window of 4: 10.4 -> 14.7 ms; d = 128 every key at 720p/5s:
+    // 3.1 -> 4.1 ms)
+    uint32_t pw[2][8], pl[2][8];
     auto softmax = [&](auto masked) {
       constexpr bool kMasked = decltype(masked)::value;
       float mx = -1e30f;
@@ -242,7 +251,7 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
             p1 = key + 1 < nv ? p1 : 0.f;
           }
           psum += p0 + p1;
-          pw[kb][r >> 1] = pack_bf16x2(p0, p1);
+          split2(p0, p1, pw[kb][r >> 1], pl[kb][r >> 1]);
         }
       l_run += psum;
     };
@@ -257,6 +266,8 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
       const int kb = kk >> 1, g0 = 2 * (kk & 1);  // accumulator row groups g0, g0 + 1
       const bf16x8 pf = __builtin_bit_cast(
           bf16x8, make_uint4(pw[kb][2 * g0], pw[kb][2 * g0 + 1], pw[kb][2 * g0 + 2], pw[kb][2 * g0 + 3]));
+      const bf16x8 plf = __builtin_bit_cast(
+          bf16x8, make_uint4(pl[kb][2 * g0], pl[kb][2 * g0 + 1], pl[kb][2 * g0 + 2], pl[kb][2 * g0 + 3]));
       const int rowA = 16 * kk + 4 * h + (j16 >> 2);
 #pragma unroll
       for (int jb = 0; jb < C::JB; ++jb) {
@@ -267,6 +278,7 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
             (lds_i16x4 *)(vt + (rowA + 8) * C::VPITCH + col * 2));
         const i16x8 x = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         o[jb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, x), pf, o[jb]);
+        o[jb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, x), plf, o[jb]);
       }
     }
     if (b + 1 < nb) {
