@@ -398,8 +398,15 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
   return GLA_OK;
 }
 
+// Strides of a dense [B][H][N][d] tensor. They are formed before the sizes are
+// validated: a stride beyond 64 bits saturates, and the span check of the
+// view then refuses the sizes.
 gla_tensor contiguous(const void *p, int H, int64_t N, int d) {
-  return gla_tensor{const_cast<void *>(p), (int64_t)H * N * d, N * d, (int64_t)d};
+  const auto sat = [](__int128 x) {
+    return x > INT64_MAX ? INT64_MAX : x < INT64_MIN ? INT64_MIN : (int64_t)x;
+  };
+  return gla_tensor{const_cast<void *>(p), sat((__int128)H * N * d), sat((__int128)N * d),
+                    (int64_t)d};
 }
 
 // The body of the two backward entry points (contiguous [B][H][N][d] tensors).
@@ -676,7 +683,7 @@ bool make_gdn_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
     if (atoi(e) >= 1) fc = atoi(e);
   if (F >= kChunkedScanMinFrames && fc < F) {
     p.scan_fc = fc;
-    p.scan_nc = (F + p.scan_fc - 1) / p.scan_fc;
+    p.scan_nc = (int)ceil_div(F, p.scan_fc);
     p.scan_tws = floats;
     p.scan_sws = floats + BH * p.scan_nc * 2 * (int64_t)d * d;
     floats = p.scan_sws + BH * p.scan_nc * (int64_t)d * d;
@@ -710,7 +717,16 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
   p.T = T;
   p.d = d;
   if (BH < 0 || F < 0 || T < 0) return false;
+  // indexing limits, checked by division before any product is formed: 1-D
+  // grids of 256-thread workgroups (slab x frame units, the carry's slab x
+  // element blocks), 64-bit element offsets
+  const int64_t max_grid = (int64_t(1) << 31) / 256;
+  const int64_t E = p.state_elems();
+  if (d < 1 || BH > (max_grid - 1) / ceil_div(E, 256)) return false;
+  if (F > 0 && BH > (max_grid - 1) / F) return false;
+  if (T > (int64_t(1) << 62) / d) return false;
   const int64_t units = BH * F;
+  if (T > 0 && units > (int64_t(1) << 62) / T / d) return false;
   if (units > 0 && T > 0) {
     // kv parts fill about one round of resident kv workgroups (the carry then
     // sums fewer parts and each part streams more tokens: 720p/5s frame-causal
@@ -739,12 +755,7 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
     p.P = p.R = 1;
     p.part_len = p.read_len = round_up(T, kTokenAlign);
   }
-  // indexing limits: 1-D grids of 256-thread workgroups, 64-bit element offsets
-  const int64_t max_grid = (int64_t(1) << 31) / 256;
   if (units > 0 && (units * std::max(p.P, p.R) >= max_grid)) return false;
-  if (T > 0 && units > (int64_t(1) << 62) / T / std::max(d, 1)) return false;
-  const int64_t E = p.state_elems();
-  if (BH * ceil_div(E, 256) >= max_grid) return false;
   p.NG = (int)ceil_div(F, p.G);
   // carries are kept only for groups of several frames (G == 1 scans in place)
   p.ws_bytes = (size_t)round_up((units * p.P + (p.G > 1 ? BH * p.NG : 0)) * E * 4, 256);
@@ -1086,6 +1097,7 @@ GLA_EXPORT const char *gla_status_string(gla_status s) {
     case GLA_ERR_VALUE: return "invalid scalar argument";
     case GLA_ERR_HIP: return "HIP runtime error";
     case GLA_ERR_ALIAS: return "output overlaps another argument";
+    default: break;
   }
   return "unknown status";
 }

@@ -73,10 +73,23 @@ typedef enum gla_status {
   GLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the *_workspace query */
   GLA_ERR_VALUE = 6,       /* eps negative or not finite */
   GLA_ERR_HIP = 7,         /* the HIP runtime reported an error at launch */
-  GLA_ERR_ALIAS = 8        /* an output overlaps an input or the workspace */
+  GLA_ERR_ALIAS = 8,       /* an output overlaps an input or the workspace */
+  /* Not statuses: these two give the type the range of a 32-bit int, so that
+   * any int a C caller passes (gla_status_string) is a value of the type in
+   * the C++ implementation too, which then maps unknown values to a message. */
+  GLA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  GLA_STATUS_RANGE_MAX_ = 2147483647
 } gla_status;
 
-typedef enum gla_dtype { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+typedef enum gla_dtype {
+  GLA_F32 = 0,
+  GLA_BF16 = 1,
+  /* Not dtypes: the range of a 32-bit int, so that an unknown value a C caller
+   * passes is still a value of the type on the C++ side, where it is refused
+   * with GLA_ERR_UNSUPPORTED. */
+  GLA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  GLA_DTYPE_RANGE_MAX_ = 2147483647
+} gla_dtype;
 
 /* Workspace bytes needed by the matching call for these sizes (0 if none).
  * Returns 0 for invalid sizes as well; the call itself reports those. */
