@@ -99,6 +99,14 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
   constexpr int kSmem = kRope ? C::SMEM_ROPE : C::SMEM;
   __shared__ __attribute__((aligned(16))) char smem[kSmem + C::U_RED_BYTES];
   extern __shared__ float2 rope_tab[];  // kRope: RopeK::entries() (cos, sin) pairs
+  // the running state's elements per thread (d = 128 keeps none: 1 unused)
+  constexpr int kSt = !C::kGroups ? 1 : (C::kSplitTokens ? C::TM * C::TM * 4 : C::TM * C::TM * 16);
+  // an even frame's state and z, parked here until the next frame's slot is
+  // written with it (thread-private layout [element][thread]); not with
+  // rotary positions, whose turn table and third tile leave no room for it
+  // (and whose registers it would push to 3 waves per SIMD)
+  constexpr bool kStash = C::kGroups && !kRope;
+  __shared__ float stash[kStash ? (kSt + 1) * kThreads : 1];
   lds_char *const sbase = (lds_char *)smem;
   lds_char *const tk = sbase;
   lds_char *const tv = sbase + C::TILE_BYTES;
@@ -189,7 +197,6 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
 
   // running state of the group: accumulator layout (d = 64) or the layout of
   // the cross-wave sum (d = 32)
-  constexpr int kSt = !C::kGroups ? 1 : (C::kSplitTokens ? C::TM * C::TM * 4 : C::TM * C::TM * 16);
   float st[kSt];
   float zst = 0.f;
 #pragma unroll
@@ -239,10 +246,16 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
   };
 
   // After a frame's last chunk, frame_close() folds U_f into the running state
-  // (registers; z through an LDS sum), and store_state() writes the slot. The
-  // stores are issued one chunk later, right after that chunk's loads have
-  // been waited for: vmcnt counts loads and stores alike, so stores issued
-  // behind an outstanding prefetch would make its wait include them.
+  // (registers; z through an LDS sum), and the slot is written later:
+  //  - vmcnt counts loads and stores alike, and with a store outstanding the
+  //    wait for a load takes the store's completion with it. Stores are
+  //    therefore issued right after a chunk's loads have been waited for, one
+  //    chunk after the frame closed, so that they meet no outstanding prefetch.
+  //  - Each such write-out still costs the workgroup a store round trip before
+  //    its next load is consumed. An even frame's state therefore waits in LDS
+  //    and goes out together with the next frame's: half the write-outs
+  //    (720p/60s: kv 0.361 -> 0.351 ms; with all of a workgroup's states
+  //    written at its end, kv is 0.338 ms, but that needs LDS for G states).
   auto frame_close = [&](int fi) {
     turn_rows(fi);
     float gm = 0.f;
@@ -294,7 +307,9 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
       zst = fmaf(gm, zst, ured[tid] + ured[D + tid] + ured[2 * D + tid] + ured[3 * D + tid]);
   };
 
-  auto store_state = [&](int fi) {
+  // Writes frame fi's slot. src(e, tid) is element e of the running state in
+  // st's layout, z(tid) the normaliser sum (d = 128: the accumulators).
+  auto write_slot = [&](int fi, auto src, auto z) {
     float *out = ws + ((bh * F + f_begin + fi) * (int64_t)P + p) * ((int64_t)D * D + D);
     // Recompute the offsets from an opaque copy of the thread id: hoisted out
     // of the loop they would stay live in registers.
@@ -311,7 +326,7 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
             const int idx = tidv + kThreads * e4;
             const int r = idx >> 6, ln = idx & 63;
             const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-            out[(32 * a + m) * D + 32 * b + (ln & 31)] = st[(a * C::TM + b) * 4 + e4];
+            out[(32 * a + m) * D + 32 * b + (ln & 31)] = src((a * C::TM + b) * 4 + e4, tidv);
           }
     } else {
 #pragma unroll
@@ -320,15 +335,23 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
         for (int b = 0; b < C::TM; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float sv = C::kGroups ? st[(a * C::TM + b) * 16 + r] : acc[a][b][r];
+            const float sv = C::kGroups ? src((a * C::TM + b) * 16 + r, tidv) : acc[a][b][r];
             const int m = 8 * (r >> 2) + 4 * (lanev >> 5) + (r & 3);
             out[(32 * (wm * C::TM + a) + m) * D + 32 * (wn * C::TM + b) + (lanev & 31)] = sv;
           }
     }
-    if (tidv < D) out[D * D + tidv] = zst;
+    if (tidv < D) out[D * D + tidv] = z(tidv);
+  };
+  auto store_state = [&](int fi) {
+    write_slot(fi, [&](int e, int) { return st[e]; }, [&](int) { return zst; });
+  };
+  auto store_stash = [&](int fi) {
+    write_slot(fi, [&](int e, int t) { return stash[e * kThreads + t]; },
+               [&](int t) { return stash[kSt * kThreads + t]; });
   };
 
   int pending = -1;  // frame whose slot is still to be written
+  int stashed = -1;  // frame whose state waits in the stash
   if (total > 0) load();
   for (int fi = 0; fi < nf; ++fi) {
     if (fi > 0) {
@@ -371,6 +394,10 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
       }
       sync_lds();
       if (pending >= 0) {
+        if (stashed >= 0) {
+          store_stash(stashed);
+          stashed = -1;
+        }
         store_state(pending);
         pending = -1;
       }
@@ -403,9 +430,22 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
       }
     }
     frame_close(fi);
-    if (pending >= 0 || ncf == 0) store_state(fi);  // no chunk follows to carry the store
-    else pending = fi;
+    if (kStash && (fi & 1) == 0 && fi + 1 < nf && ncf > 0 && pending < 0) {
+#pragma unroll
+      for (int e = 0; e < kSt; ++e) stash[e * kThreads + tid] = st[e];
+      stash[kSt * kThreads + tid] = zst;
+      stashed = fi;
+    } else if (pending >= 0 || ncf == 0) {  // no chunk follows to carry the store
+      if (stashed >= 0) {
+        store_stash(stashed);
+        stashed = -1;
+      }
+      store_state(fi);
+    } else {
+      pending = fi;
+    }
   }
+  if (stashed >= 0) store_stash(stashed);
   if (pending >= 0) store_state(pending);
 }
 
