@@ -24,6 +24,18 @@
 // lane half h is key 16kk + 4h + e (e < 4) or 16kk + 8 + 4h + (e - 4); V^T is
 // read from LDS with ds_read_b64_tr_b16 in that same key order.
 //
+// P V runs on the fp16 matrix cores: V is converted from bf16 to fp16 as it is
+// staged (exact for magnitudes in [2^-14, 65504]) and the probabilities are
+// packed to fp16 (11 significant bits against bf16's 8; worst slab-relative
+// error on the shape sweep 5.2e-3 against 1.4e-2 with bf16 probabilities).
+// A workgroup also takes the largest |v| of the keys it staged. If that lies
+// outside [2^-6, 65504] (values fp16 cannot hold, or a V so small that fp16's
+// subnormals would cost it precision) it writes a marker instead of its
+// output, and a second launch recomputes exactly those tiles with bf16 P V,
+// the probabilities split into bf16 hi + lo pairs (about 16 significant
+// bits, 3.9e-3 on the sweep); every other workgroup of that launch reads one
+// element and exits.
+//
 // Vector-ALU kernel (fp32 inputs, other d, or forced): one query per thread,
 // blocks of 32 keys through LDS.
 #include <type_traits>
@@ -61,6 +73,35 @@ __device__ __forceinline__ KeyRanges anchor_ranges(const AnchorArgs &a, int seg)
 // ---------------------------------------------------------------------------
 // Matrix-core kernel
 // ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// two floats -> packed fp16, rounded toward zero (v_cvt_pkrtz_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// eight bf16 -> eight fp16, with the running maximum of their magnitudes
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v, float &vmax) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = lo_bf16(w[i]), hi = hi_bf16(w[i]);
+    vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+    w[i] = pack_f16x2_rtz(lo, hi);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x16_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// bf16 bits of a quiet NaN with payload 1: written by a workgroup of the fp16
+// pass at its tile's first output element when the tile is to be recomputed
+// (arithmetic never produces this payload: a NaN result is the canonical 0x7FC0)
+constexpr uint16_t kRedoMark = 0x7FC1;
+// |v| range in which fp16 P V is taken
+constexpr float kF16VMin = 0x1p-6f, kF16VMax = 65504.f;
 template <int D>
 struct AmCfg {
   static constexpr int BM = 128;               // queries per workgroup (32 per wave)
@@ -85,15 +126,20 @@ struct AmCfg {
   static_assert(BM * PITCH <= SMEM, "the epilogue tile reuses the K/V buffers");
 };
 
-// Waves per SIMD the compiler must allow. With the probabilities split into
-// bf16 hi + lo for P V, d = 64 takes 222 VGPRs (2 waves; forcing 3 spills and
-// measured slower) and d = 128 would take 260 (1 wave): held to 2, it spills
-// 16 bytes and runs 20% faster than at 1.
-template <int D>
-constexpr int kAnchorWaves = D == 64 ? 2 : D == 128 ? 2 : 1;
+// Waves per SIMD the compiler must allow.
+//  - fp16 P V: d = 64 fits 3 waves (168 VGPRs, 16 bytes spilled; 720p/60s
+//    window of 4: 12.6 ms at 2 waves -> 11.6 ms), d = 128 takes 256 VGPRs
+//    (2 waves).
+//  - bf16 hi + lo P V (the recomputed tiles): d = 64 takes 222 VGPRs (2 waves;
+//    forcing 3 spills and measured slower) and d = 128 would take 260 (1
+//    wave): held to 2, it spills 16 bytes and runs 20% faster than at 1.
+template <int D, bool kF16>
+constexpr int kAnchorWaves = D == 64 ? (kF16 ? 3 : 2) : D == 128 ? 2 : 1;
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAnchorWaves<D>))) void
+// kF16: the fp16 pass over every tile. Otherwise the bf16 hi + lo pass, which
+// computes only the tiles the fp16 pass marked.
+template <int D, bool kF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAnchorWaves<D, kF16>))) void
 anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
   using C = AmCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -110,6 +156,12 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
   const int64_t Nq = (int64_t)a.Fq * a.T, Nk = (int64_t)a.F * a.T;
   const int64_t q0 = (int64_t)seg * seg_len + (int64_t)tile * C::BM;  // first query row
   const int nq = (int)min((int64_t)C::BM, seg_len - (int64_t)tile * C::BM);
+  uint16_t *os = static_cast<uint16_t *>(a.o) + bh * Nq * D;
+  if constexpr (!kF16) {
+    // only the tiles the fp16 pass marked
+    const uint16_t mark = __builtin_nontemporal_load(os + q0 * D);
+    if (mark != kRedoMark) return;
+  }
   const KeyRanges kr = anchor_ranges(a, seg);
   const int nb_a = (int)((kr.a1 - kr.a0 + C::BN - 1) / C::BN);
   const int nb = nb_a + (int)((kr.b1 - kr.b0 + C::BN - 1) / C::BN);
@@ -149,13 +201,15 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
     }
     nv_next = nv;
   };
+  float vmax = 0.f;  // largest |v| staged by this thread (fp16 pass)
   auto store_block = [&](int buf) {
     char *kt = smem + buf * C::BUF;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int row = r0 + i * C::RPP;
       *reinterpret_cast<uint4 *>(kt + row * C::KPITCH + 16 * c) = rk[i];
-      *reinterpret_cast<uint4 *>(kt + C::KTILE + row * C::VPITCH + 16 * c) = rv[i];
+      *reinterpret_cast<uint4 *>(kt + C::KTILE + row * C::VPITCH + 16 * c) =
+          kF16 ? bf16x8_to_f16x8(rv[i], vmax) : rv[i];
     }
   };
 
@@ -202,14 +256,10 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
     }
     // online softmax over the block (keys past nv are not there; only the
     // last block of a range is partial)
-    // probabilities as packed bf16 pairs, per 32-key block: p = hi + lo, both
-    // bf16, so that P V keeps ~16 bits of p. With one bf16 rounding (2^-9 per
-    // weight against the fp32 normaliser) the output reached 1.4e-2 of the
-    // slab-relative metric in the shape sweep; with the split it sits at the
-    // output's own bf16 rounding (3.9e-3), for one more MFMA per P V step
-    // (720p/60s, window of 4: 10.4 -> 14.7 ms; d = 128 every key at 720p/5s:
-    // 3.1 -> 4.1 ms)
-    uint32_t pw[2][8], pl[2][8];
+    // probabilities as packed pairs, per 32-key block: fp16 (fp16 pass), or
+    // p = hi + lo with both bf16 (bf16 pass: one more MFMA per P V step)
+    uint32_t pw[2][8];
+    [[maybe_unused]] uint32_t pl[kF16 ? 1 : 2][8];
     auto softmax = [&](auto masked) {
       constexpr bool kMasked = decltype(masked)::value;
       float mx = -1e30f;
@@ -251,7 +301,10 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
             p1 = key + 1 < nv ? p1 : 0.f;
           }
           psum += p0 + p1;
-          split2(p0, p1, pw[kb][r >> 1], pl[kb][r >> 1]);
+          if constexpr (kF16)
+            pw[kb][r >> 1] = pack_f16x2_rtz(p0, p1);
+          else
+            split2(p0, p1, pw[kb][r >> 1], pl[kb][r >> 1]);
         }
       l_run += psum;
     };
@@ -264,10 +317,7 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int kb = kk >> 1, g0 = 2 * (kk & 1);  // accumulator row groups g0, g0 + 1
-      const bf16x8 pf = __builtin_bit_cast(
-          bf16x8, make_uint4(pw[kb][2 * g0], pw[kb][2 * g0 + 1], pw[kb][2 * g0 + 2], pw[kb][2 * g0 + 3]));
-      const bf16x8 plf = __builtin_bit_cast(
-          bf16x8, make_uint4(pl[kb][2 * g0], pl[kb][2 * g0 + 1], pl[kb][2 * g0 + 2], pl[kb][2 * g0 + 3]));
+      const uint4 pu = make_uint4(pw[kb][2 * g0], pw[kb][2 * g0 + 1], pw[kb][2 * g0 + 2], pw[kb][2 * g0 + 3]);
       const int rowA = 16 * kk + 4 * h + (j16 >> 2);
 #pragma unroll
       for (int jb = 0; jb < C::JB; ++jb) {
@@ -277,8 +327,14 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
         const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4 *)(vt + (rowA + 8) * C::VPITCH + col * 2));
         const i16x8 x = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        o[jb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, x), pf, o[jb]);
-        o[jb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, x), plf, o[jb]);
+        if constexpr (kF16) {
+          o[jb] = mfma_32x32x16_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, pu), o[jb]);
+        } else {
+          const uint4 lu = make_uint4(pl[kb][2 * g0], pl[kb][2 * g0 + 1], pl[kb][2 * g0 + 2],
+                                      pl[kb][2 * g0 + 3]);
+          o[jb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, pu), o[jb]);
+          o[jb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, lu), o[jb]);
+        }
       }
     }
     if (b + 1 < nb) {
@@ -288,12 +344,27 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
     sync_lds();
   }
 
+  if constexpr (kF16) {
+    // the workgroup's largest staged |v| (the K/V buffers are free after the
+    // loop's last barrier): out of the fp16 range, mark the tile for the bf16
+    // pass and write nothing else
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    float *wmax = reinterpret_cast<float *>(smem);
+    if (lane == 0) wmax[wave] = vmax;
+    sync_lds();
+    vmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    sync_lds();  // wmax is read before the epilogue reuses the LDS
+    if (nb > 0 && !(vmax >= kF16VMin && vmax <= kF16VMax)) {
+      if (tid == 0) os[q0 * D] = kRedoMark;
+      return;
+    }
+  }
   // epilogue: o = sigmoid(g) * O / l, through LDS so that g is read and o is
   // written as whole rows (the K/V buffers are free after the last barrier)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = nb > 0 ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
   const uint16_t *gs = static_cast<const uint16_t *>(a.g) + bh * Nq * D;
-  uint16_t *os = static_cast<uint16_t *>(a.o) + bh * Nq * D;
 #pragma unroll
   for (int i = 0; i < C::GPT; ++i) {
     const int row = r0 + i * C::RPP;
@@ -395,11 +466,14 @@ __global__ __launch_bounds__(kValuQ) void anchor_valu_kernel(AnchorArgs a, int t
 }
 
 template <int D>
-void anchor_mfma_launch(const AnchorArgs &a, int64_t seg_len, hipStream_t s) {
+void anchor_mfma_launch(const AnchorArgs &a, int64_t seg_len, bool f16, hipStream_t s) {
   const int nseg = a.causal ? a.Fq : 1;
   const int tiles = (int)((seg_len + AmCfg<D>::BM - 1) / AmCfg<D>::BM);
-  hipLaunchKernelGGL((anchor_mfma_kernel<D>), dim3((unsigned)(a.BH * nseg * tiles)), dim3(256), 0,
-                     s, a, tiles, seg_len);
+  const dim3 grid((unsigned)(a.BH * nseg * tiles));
+  if (f16)
+    hipLaunchKernelGGL((anchor_mfma_kernel<D, true>), grid, dim3(256), 0, s, a, tiles, seg_len);
+  else
+    hipLaunchKernelGGL((anchor_mfma_kernel<D, false>), grid, dim3(256), 0, s, a, tiles, seg_len);
 }
 
 template <typename TIn, int D>
@@ -431,21 +505,31 @@ int64_t anchor_tiles(const AnchorArgs &a, Path path) {
   return a.BH * (a.causal ? a.Fq : 1) * ((seg_len + per - 1) / per);
 }
 
+namespace {
+hipError_t anchor_mfma_dispatch(const AnchorArgs &a, int64_t seg_len, bool f16, hipStream_t s) {
+  switch (a.d) {
+    case 32: anchor_mfma_launch<32>(a, seg_len, f16, s); break;
+    case 64: anchor_mfma_launch<64>(a, seg_len, f16, s); break;
+    case 128: anchor_mfma_launch<128>(a, seg_len, f16, s); break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_anchor(const AnchorArgs &a, int dtype, Path path, hipStream_t s) {
   const int64_t seg_len = a.causal ? a.T : (int64_t)a.Fq * a.T;
   if (a.BH == 0 || seg_len == 0 || a.Fq == 0) return hipSuccess;
-  if (path == Path::kMfma) {
-    switch (a.d) {
-      case 32: anchor_mfma_launch<32>(a, seg_len, s); break;
-      case 64: anchor_mfma_launch<64>(a, seg_len, s); break;
-      case 128: anchor_mfma_launch<128>(a, seg_len, s); break;
-      default:
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
+  if (path == Path::kMfma) return anchor_mfma_dispatch(a, seg_len, true, s);
   return dtype == 0 ? anchor_valu_dispatch<float>(a, seg_len, s)
                     : anchor_valu_dispatch<bf16_t>(a, seg_len, s);
+}
+
+hipError_t launch_anchor_redo(const AnchorArgs &a, Path path, hipStream_t s) {
+  const int64_t seg_len = a.causal ? a.T : (int64_t)a.Fq * a.T;
+  if (a.BH == 0 || seg_len == 0 || a.Fq == 0 || path != Path::kMfma) return hipSuccess;
+  return anchor_mfma_dispatch(a, seg_len, false, s);
 }
 
 }  // namespace gla

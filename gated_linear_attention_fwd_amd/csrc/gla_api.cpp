@@ -148,11 +148,13 @@ enum Kind {
   kKindGdnScan = 8,
   kKindGdnReadout = 9,
   kKindAnchor = 10,
-  kNumKinds = 11
+  kKindAnchorRedo = 11,
+  kNumKinds = 12
 };
 const char *const kKindNames[kNumKinds] = {"kv",     "carry",  "readout",  "bwd_q",
                                            "rev_scan", "bwd_k", "dgamma", "gdn_kv",
-                                           "gdn_scan", "gdn_readout", "anchor"};
+                                           "gdn_scan", "gdn_readout", "anchor",
+                                           "anchor_redo"};
 
 struct Profiler {
   std::mutex mu;
@@ -665,6 +667,8 @@ gla_status run_anchor(const void *q, const void *k, const void *v, const void *g
   hipStream_t s = static_cast<hipStream_t>(stream);
   GLA_TRY(launched(timed(kKindAnchor, s, [&] { return launch_anchor(a, dt, path, s); }),
                    "anchor"));
+  GLA_TRY(launched(timed(kKindAnchorRedo, s, [&] { return launch_anchor_redo(a, path, s); }),
+                   "anchor_redo"));
   return GLA_OK;
 }
 
@@ -728,13 +732,16 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
   const int64_t units = BH * F;
   if (T > 0 && units > (int64_t(1) << 62) / T / d) return false;
   if (units > 0 && T > 0) {
-    // kv parts fill about one round of resident kv workgroups (the carry then
-    // sums fewer parts and each part streams more tokens: 720p/5s frame-causal
-    // 0.110 -> 0.102 ms, bidirectional 0.102 -> 0.093 ms against cutting to
-    // 2048); readout splits aim at 2048 workgroups
+    // kv parts fill at most one round of resident kv workgroups: the carry
+    // then sums fewer parts and each part streams more tokens (720p/5s:
+    // frame-causal 0.110 -> 0.102 ms, bidirectional 0.102 -> 0.093 ms against
+    // cutting to 2048), and a second, mostly empty round costs more than the
+    // idle slots of a partial first one (720p/5s frame-causal, 672 frames:
+    // 2 parts -> 1, kv 0.0386 -> 0.0348 ms). Readout splits aim at 2048
+    // workgroups.
     int64_t P = 1, R = 1;
     if (units < kResidentKvWorkgroups)
-      P = std::min(ceil_div(kResidentKvWorkgroups, units),
+      P = std::min(std::max<int64_t>(1, kResidentKvWorkgroups / units),
                    std::max<int64_t>(1, ceil_div(T, kMinPartTokens)));
     if (units < kTargetWorkgroups)
       R = std::min(ceil_div(kTargetWorkgroups, units),

@@ -270,6 +270,9 @@ struct AnchorArgs {
 
 int64_t anchor_tiles(const AnchorArgs &a, Path path);  // workgroups of one launch
 hipError_t launch_anchor(const AnchorArgs &a, int dtype, Path path, hipStream_t s);
+// Matrix-core path: recomputes the tiles launch_anchor marked (probabilities
+// as bf16 hi + lo); launches nothing on the vector-ALU path.
+hipError_t launch_anchor_redo(const AnchorArgs &a, Path path, hipStream_t s);
 
 hipError_t launch_kv(const Plan &p, int dtype, Path path, const KvArgs &a, hipStream_t s);
 hipError_t launch_carry(const Plan &p, const CarryArgs &a, hipStream_t s);

@@ -287,7 +287,16 @@ gla_status gla_gdn_framecausal(const void *q, const void *k, const void *v, cons
  * window <= 0: no limit). scale must be finite and > 0 (1/sqrt(d) is the
  * usual choice); n_sink >= 0. GLA_F32 or GLA_BF16 (o rounded to nearest even),
  * softmax and sums in fp32. No workspace. o may overlap no input
- * (GLA_ERR_ALIAS). Conventions otherwise as above. */
+ * (GLA_ERR_ALIAS). Conventions otherwise as above.
+ * Precision of the bf16 matrix-core path (d = 32, 64, 128): scores on bf16
+ * matrix cores with fp32 sums; P V on fp16 matrix cores, V converted from bf16
+ * (exact in fp16's range) and the probabilities rounded to fp16. A tile of
+ * 128 queries whose visible keys have a largest |v| outside [2^-6, 65504] is
+ * recomputed by a second launch with P V in bf16 and each probability split
+ * into a bf16 hi + lo pair; that launch costs the other tiles one load each.
+ * The first launch marks such a tile by writing a NaN with payload 1 (bf16
+ * 0x7FC1) at its first output element, so o holds that value between the two
+ * launches. */
 gla_status gla_softmax_anchor(const void *q, const void *k, const void *v, const void *g, void *o,
                               int B, int H, int Fq, int F, int T, int d, gla_dtype dt, int causal,
                               int n_sink, int window, float scale, void *stream);

@@ -3,10 +3,11 @@ ABI) against the fp64 oracle (oracle.softmax_anchor, pinned in
 test_oracle_anchor.py).
 
 Bar: slab-normalised error (gla_testutil.slab_rel_err) of o at most 1e-4 for
-float32 inputs and 2e-2 for bfloat16 inputs (fp32 softmax and sums; the
-matrix-core path splits the probabilities into bf16 hi + lo for the P V
-product, which keeps the bf16 error at the output's own rounding: a margin
-test below holds a sweep of shapes to 1e-2).
+float32 inputs and 2e-2 for bfloat16 inputs (fp32 softmax and sums). The
+matrix-core path runs P V on fp16 matrix cores (probabilities rounded to fp16,
+V converted from bf16), and recomputes with bf16 hi + lo probabilities the
+tiles whose V magnitudes lie outside [2^-6, 65504]: a margin test holds a
+sweep of shapes to 1e-2, and tests below drive V out of fp16's range.
 """
 from __future__ import annotations
 
@@ -154,9 +155,9 @@ def test_anchor_720p_60s_sampled_frames():
 
 def test_anchor_precision_margin():
     """The matrix-core anchor's bf16 error stays well inside the 2e-2 bar on a
-    seeded sweep of shapes, modes, sinks and windows: at most 1e-2 (the
-    probabilities reach P V as bf16 hi + lo pairs; with one bf16 rounding of
-    each probability this sweep reached 1.4e-2)."""
+    seeded sweep of shapes, modes, sinks and windows: at most 1e-2 (P V in
+    fp16 reaches 5.2e-3, bf16 hi + lo probabilities 3.9e-3; with one bf16
+    rounding of each probability this sweep reached 1.4e-2)."""
     rng0 = np.random.default_rng(123)
     worst = 0.0
     for c in range(16):
@@ -180,3 +181,58 @@ def test_anchor_precision_margin():
         o64 = oracle.bf16_to_f64(o.view(torch.int16).cpu().numpy().view(np.uint16))
         worst = max(worst, slab_rel_err(o64, ro))
     assert worst <= 1e-2, worst
+
+
+def scaled_v(v: np.ndarray, scale: float) -> np.ndarray:
+    return synth.bf16_bits((oracle.bf16_to_f64(v) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("scale_v,d", [(3e5, 64), (2e5, 128), (1e-5, 64), (1e-4, 32)],
+                         ids=["large-d64", "large-d128", "small-d64", "small-d32"])
+def test_anchor_v_outside_fp16_range(scale_v, d):
+    """V with magnitudes fp16 cannot hold (above 65504, which fp16 would
+    saturate) or would hold only as subnormals: the marked tiles are recomputed
+    with bf16 hi + lo probabilities and stay within 1e-2."""
+    q, k, v, g = inputs(1, 2, 3, 3, 150, d, "bf16", seed=11)
+    v = scaled_v(v, scale_v)
+    o = gla.gla_softmax_anchor(dev(q), dev(k), dev(v), dev(g), T=150, n_sink=1, window=2)
+    ref = oracle.softmax_anchor(q, k, v, g, T=150, n_sink=1, window=2)
+    e = slab_rel_err(f64(o), ref)
+    report("anchor V x %g d=%d" % (scale_v, d), e)
+    assert e <= 1e-2
+
+
+def test_anchor_recomputes_only_marked_tiles():
+    """Head 1's V exceeds fp16's range, head 0's does not: head 0's rows are bit
+    for bit those of a call where no head is out of range (its tiles kept the
+    fp16 result), and head 1 meets the bar against the oracle."""
+    q, k, v, g = inputs(1, 2, 2, 2, 200, 64, "bf16", seed=12)
+    v_big = v.copy()
+    v_big[:, 1] = scaled_v(v[:, 1], 1e5)
+    t = {n: dev(x) for n, x in zip("qkg", (q, k, g))}
+    plain = gla.gla_softmax_anchor(t["q"], t["k"], dev(v), t["g"], T=200, n_sink=1, window=1)
+    mixed = gla.gla_softmax_anchor(t["q"], t["k"], dev(v_big), t["g"], T=200, n_sink=1, window=1)
+    assert torch.equal(mixed[:, 0], plain[:, 0])
+    ref = oracle.softmax_anchor(q[:, 1:], k[:, 1:], v_big[:, 1:], g[:, 1:], T=200, n_sink=1,
+                                window=1)
+    e = slab_rel_err(f64(mixed[:, 1:]), ref)
+    report("anchor mixed heads, head 1", e)
+    assert e <= 1e-2
+
+
+def test_anchor_second_launch_idle_on_ordinary_inputs():
+    """With V in fp16's range no tile is marked: the recomputing launch only
+    reads each tile's first output element (measured with the library's
+    per-launch event timing)."""
+    q, k, v, g = inputs(1, 8, 4, 4, 920, 64, "bf16", seed=13)
+    args = [dev(x) for x in (q, k, v, g)]
+    gla.gla_softmax_anchor(*args, T=920, n_sink=1, window=2)
+    torch.cuda.synchronize()
+    gla.profile_begin(64)
+    for _ in range(3):
+        gla.gla_softmax_anchor(*args, T=920, n_sink=1, window=2)
+    prof = gla.profile_end()
+    main = prof["anchor"][1] / prof["anchor"][0]
+    redo = prof["anchor_redo"][1] / prof["anchor_redo"][0]
+    print("anchor %.4f ms, recomputing launch %.4f ms" % (main, redo), flush=True)
+    assert redo < 0.2 * main
