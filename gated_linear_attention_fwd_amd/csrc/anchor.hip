@@ -52,6 +52,13 @@ struct KeyRanges {
   int64_t a0, a1, b0, b1;
 };
 
+// a wave-uniform 64-bit value, read into scalar registers
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ KeyRanges anchor_ranges(const AnchorArgs &a, int seg) {
   const int64_t T = a.T;
   KeyRanges r{0, (int64_t)a.F * T, 0, 0};
@@ -74,6 +81,7 @@ __device__ __forceinline__ KeyRanges anchor_ranges(const AnchorArgs &a, int seg)
 // Matrix-core kernel
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // two floats -> packed fp16, rounded toward zero (v_cvt_pkrtz_f16_f32)
 __device__ __forceinline__ uint32_t pack_f16x2_rtz(float a, float b) {
@@ -150,9 +158,13 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
   const int n = lane & 31;
   const int nseg = a.causal ? a.Fq : 1;
   const int64_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int tile = (int)(wg % tiles_per_seg);
-  const int seg = (int)((wg / tiles_per_seg) % nseg);
-  const int64_t bh = wg / ((int64_t)tiles_per_seg * nseg);
+  // The work item is uniform, but 64-bit divisions leave it in vector
+  // registers: read it into scalars, so that the key ranges and the block
+  // addresses derived from it are scalar work (vector-ALU time is what bounds
+  // this kernel)
+  const int tile = __builtin_amdgcn_readfirstlane((int)(wg % tiles_per_seg));
+  const int seg = __builtin_amdgcn_readfirstlane((int)((wg / tiles_per_seg) % nseg));
+  const int bh = __builtin_amdgcn_readfirstlane((int)(wg / ((int64_t)tiles_per_seg * nseg)));
   const int64_t Nq = (int64_t)a.Fq * a.T, Nk = (int64_t)a.F * a.T;
   const int64_t q0 = (int64_t)seg * seg_len + (int64_t)tile * C::BM;  // first query row
   const int nq = (int)min((int64_t)C::BM, seg_len - (int64_t)tile * C::BM);
@@ -162,9 +174,10 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
     const uint16_t mark = __builtin_nontemporal_load(os + q0 * D);
     if (mark != kRedoMark) return;
   }
-  const KeyRanges kr = anchor_ranges(a, seg);
-  const int nb_a = (int)((kr.a1 - kr.a0 + C::BN - 1) / C::BN);
-  const int nb = nb_a + (int)((kr.b1 - kr.b0 + C::BN - 1) / C::BN);
+  KeyRanges kr = anchor_ranges(a, seg);
+  kr = KeyRanges{uniform64(kr.a0), uniform64(kr.a1), uniform64(kr.b0), uniform64(kr.b1)};
+  const int nb_a = __builtin_amdgcn_readfirstlane((int)((kr.a1 - kr.a0 + C::BN - 1) / C::BN));
+  const int nb = __builtin_amdgcn_readfirstlane(nb_a + (int)((kr.b1 - kr.b0 + C::BN - 1) / C::BN));
 
   const uint16_t *qs = static_cast<const uint16_t *>(a.q) + bh * Nq * D;
   const uint16_t *ks = static_cast<const uint16_t *>(a.k) + bh * Nk * D;
@@ -194,10 +207,11 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
       // rows past the range load its last key again (in bounds, finite): the
       // softmax gives them probability 0, so neither K nor V of them counts,
       // and the loads need no branch or zero fill
+      // a scalar block base plus a 32-bit offset within the block
       const int row = min(r0 + i * C::RPP, nv - 1);
-      const int64_t off = (start + row) * D + 8 * c;
-      rk[i] = ld_stream16<false>(reinterpret_cast<const uint4 *>(ks + off));
-      rv[i] = ld_stream16<false>(reinterpret_cast<const uint4 *>(vs + off));
+      const uint32_t off = (uint32_t)(row * D + 8 * c);
+      rk[i] = ld_stream16<false>(reinterpret_cast<const uint4 *>(ks + start * D + off));
+      rv[i] = ld_stream16<false>(reinterpret_cast<const uint4 *>(vs + start * D + off));
     }
     nv_next = nv;
   };
@@ -260,16 +274,25 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
     // p = hi + lo with both bf16 (bf16 pass: one more MFMA per P V step)
     uint32_t pw[2][8];
     [[maybe_unused]] uint32_t pl[kF16 ? 1 : 2][8];
-    auto softmax = [&](auto masked) {
-      constexpr bool kMasked = decltype(masked)::value;
-      float mx = -1e30f;
+    // the last block of a range: keys past nv get a score whose probability
+    // is 0 (one softmax path for every block: with a second, masked copy the
+    // two paths held the output accumulators in different registers and
+    // copied them at the join)
+    if (nv < C::BN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (!kMasked || key < nv) mx = fmaxf(mx, s[kb][r]);
+          s[kb][r] = key < nv ? s[kb][r] : -1e30f;
         }
+    }
+    {
+      float mx = -1e30f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx *= cl2;
       // Lazy rescaling: the reference m_run moves (and O, l are rescaled)
       // only when some query's maximum exceeds it by more than 8 (a factor
@@ -293,25 +316,21 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cl2, -m_run));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], cl2, -m_run));
-          if (kMasked) {
-            p0 = key < nv ? p0 : 0.f;
-            p1 = key + 1 < nv ? p1 : 0.f;
-          }
-          psum += p0 + p1;
-          if constexpr (kF16)
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cl2, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], cl2, -m_run));
+          if constexpr (kF16) {
+            // the normaliser sums the fp16 probabilities P V takes (one
+            // v_dot2_f32_f16 a pair instead of two additions)
             pw[kb][r >> 1] = pack_f16x2_rtz(p0, p1);
-          else
+            psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[kb][r >> 1]),
+                                          f16x2{(_Float16)1.f, (_Float16)1.f}, psum, false);
+          } else {
+            psum += p0 + p1;
             split2(p0, p1, pw[kb][r >> 1], pl[kb][r >> 1]);
+          }
         }
       l_run += psum;
-    };
-    if (nv == C::BN)
-      softmax(std::false_type{});
-    else
-      softmax(std::true_type{});
+    }
 
     // O^T += V^T P^T over the block's 4 k-steps of 16 keys
 #pragma unroll
