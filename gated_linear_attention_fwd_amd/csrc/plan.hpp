@@ -70,6 +70,9 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan);
 // One frame per kv group (no carries): the carry then writes S_f of every
 // frame. The workspace shrinks to the slots.
 void single_frame_groups(Plan *plan);
+// The forward readout's splits: a frame also cut into pieces of a few hundred
+// tokens (the backward keeps make_plan's).
+void forward_readout_splits(Plan *plan);
 
 // Which kernel family runs a (dtype, d) pair; the choice is a pure function of
 // them so that parity tests know what they exercise.
