@@ -607,7 +607,7 @@ def other_workloads(args, dev):
             def step():
                 gla.gla_fwd_framecausal(x["q"], x["k"], x["v"], x["g"], x["gamma"], eps=w.eps,
                                         out=o, workspace=ws)
-        st = timed(step, 3, 20, flush=True)
+        st = timed(step, 3, 50, flush=True)
         kern = kernel_avgs(step, 5)
         got = np.concatenate([host(o[:, h:h + 1]) for h in heads], axis=1)
         if mode == "bidir":
