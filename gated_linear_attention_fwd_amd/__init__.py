@@ -62,7 +62,7 @@ _lib = None
 GLA_F32 = 0
 GLA_BF16 = 1
 # the static device scratch of gla_fwd_framecausal_noalloc (GLA_NOALLOC_SCRATCH_BYTES)
-NOALLOC_SCRATCH_BYTES = 192 << 20
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class GlaError(RuntimeError):

@@ -31,8 +31,14 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
 # then a single v_max_f32 per score instead of two (NaN canonicalisation), and
 # the MFMA accumulators, which the softmax reads and rescales every block, stay
 # in ordinary VGPRs rather than moving through AGPRs.
+# The kv kernels scale their MFMA accumulators in place at d = 128 (the
+# running state of a frame group): with the accumulators in VGPRs that is plain
+# vector work; in AGPRs it would copy them through VGPRs (229 registers, 2
+# waves per SIMD, against 165 and 3). Measured neutral for the other kernels of
+# the file.
 EXTRA_FLAGS = {"anchor.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans",
-                              "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                              "-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

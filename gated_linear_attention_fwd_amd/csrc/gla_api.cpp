@@ -59,6 +59,8 @@ constexpr int64_t kTokenAlign = 32;
 // splits: each of its splits writes a partial sum of the state adjoint.
 constexpr int64_t kSplitTargetTokens = 320;
 constexpr int64_t kMaxGroupFrames = 8;  // the kv kernels hold up to 8 decays
+// d = 128: frame pairs from 2 x 768 frames (1.5 rounds of resident kv workgroups)
+constexpr int64_t kPairFramesMinUnits = 1536;
 // kv workgroups resident at once on 256 CUs (4 per CU at d <= 64): grouping
 // frames down to about this many workgroups removes the tail of a second wave.
 constexpr int64_t kResidentKvWorkgroups = 1024;
@@ -351,6 +353,9 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
   // a record of every frame's state: the scan runs frame by frame and writes
   // S_f there, where the readout then reads it
   if (states) single_frame_groups(&p);
+  // d = 128 carries a group's running sum in the accumulators, which the
+  // frame's rotary turn must not touch: one frame per group there
+  if (rk_.on && d == 128 && p.G > 1) single_frame_groups(&p);
   forward_readout_splits(&p);
   if (BH == 0 || (bidir && N == 0)) return GLA_OK;
   GLA_TRY(check_ws(p, ws, ws_bytes));
@@ -760,11 +765,20 @@ bool make_plan(int64_t BH, int F, int64_t T, int d, Plan *plan) {
     p.P = (int)ceil_div(T, p.part_len);
     p.read_len = round_up(ceil_div(T, R), kTokenAlign);
     p.R = (int)ceil_div(T, p.read_len);
-    // Enough frames for a full grid: group consecutive frames in one kv workgroup.
-    // (The d = 128 matrix-core kernel keeps no running state: one frame each.)
-    const bool can_group = p.P == 1 && d <= 64;
-    if (can_group && units >= 2 * kTargetWorkgroups)
+    // Enough frames for a full grid: group consecutive frames in one kv
+    // workgroup. d <= 64 keeps the running sum in registers of its own and
+    // groups up to 8 frames once the grid is twice the target. d = 128 keeps
+    // it in the accumulators and pairs frames while the pairs still fill 1.5
+    // rounds of its 768 resident workgroups: a mid-workgroup write-out of its
+    // 64 KB states costs more, so larger groups lost more in kv than the carry
+    // saved (the 720p/60s stream at B = 2, H = 40, per 30-frame block: G = 2
+    // carry 0.058 -> 0.038 ms, kv 0.229 -> 0.232, call 4.79 -> 4.72 ms for 8
+    // blocks; G = 3, 4, 8: 4.91, 4.82, 5.05 ms). Rotary positions keep G = 1
+    // at d = 128 (run() below).
+    const bool can_group = p.P == 1 && (d <= 64 || d == 128);
+    if (can_group && d <= 64 && units >= 2 * kTargetWorkgroups)
       p.G = (int)std::min<int64_t>(kMaxGroupFrames, ceil_div(units, kResidentKvWorkgroups));
+    if (can_group && d == 128 && units >= kPairFramesMinUnits) p.G = 2;
     if (const char *e = getenv("GLA_FRAMES_PER_GROUP"))
       if (can_group && atoi(e) >= 1)
         p.G = (int)std::min<int64_t>({(int64_t)atoi(e), (int64_t)std::max(F, 1), kMaxGroupFrames});

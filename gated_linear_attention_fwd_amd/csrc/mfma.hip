@@ -66,10 +66,14 @@ struct KvCfg {
   // its blocks outright and no cross-wave sum is needed.
   static constexpr bool kSplitTokens = (D == 32);
   static constexpr int TM = kSplitTokens ? MB : MB / 2;
-  // running decayed state kept across the frames of a group; at d = 128 it
-  // would need 64 more registers per lane (1 wave/SIMD), so d = 128 runs one
-  // frame per workgroup
+  // running decayed state kept across the frames of a group, in registers of
+  // its own (d <= 64); at d = 128 those would be 64 more registers per lane,
+  // so there the accumulators themselves carry it: after a frame's slot is
+  // written they are scaled by the next frame's decay (kInPlace; the file is
+  // built with MFMA accumulators in VGPRs, where that scaling is plain vector
+  // work: 165 VGPRs, 3 waves per SIMD)
   static constexpr bool kGroups = (D <= 64);
+  static constexpr bool kInPlace = (D == 128);
   static constexpr int ROW_CHUNKS = D / 8;                 // 16-byte pieces per row
   static constexpr int CPT = CH * ROW_CHUNKS / kThreads;   // pieces per thread per array
   static constexpr int ROWS_PER_PASS = kThreads / ROW_CHUNKS;
@@ -125,7 +129,11 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
   const int64_t t1 = min(t0 + part_len, T);
   const int L = (int)(t1 - t0);
   const int f_begin = grp * G;
-  const int nf = C::kGroups ? min(F, f_begin + G) - f_begin : 1;  // d = 128: G == 1
+  // in-place groups at d = 128 without rotary positions only (the frame's
+  // turn applies to U_f, not to the running sum; the plan keeps G = 1 there)
+  constexpr bool kInPlace = C::kInPlace && !kRope;
+  constexpr bool kAnyGroups = C::kGroups || kInPlace;
+  const int nf = kAnyGroups ? min(F, f_begin + G) - f_begin : 1;
   const int ncf = (L + C::CH - 1) / C::CH;  // chunks per frame
   const int total = nf * ncf;
   (void)N;
@@ -206,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
   // every frame's write-out for a full memory latency); branch-free, frames
   // past the group reloading its last one, so that all go out at once (with
   // a test per load each was a memory round trip of its own)
-  constexpr int kNg = C::kGroups ? kMaxGroup : 1;
+  constexpr int kNg = kAnyGroups ? kMaxGroup : 1;
   float gms[kNg];
   if (gamma) {
     const float *gsl = gamma + bh * F + f_begin;
@@ -260,7 +268,7 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
     turn_rows(fi);
     float gm = 0.f;
 #pragma unroll
-    for (int e = 1; e < (C::kGroups ? kMaxGroup : 1); ++e) gm = (fi == e) ? gms[e] : gm;
+    for (int e = 1; e < (kAnyGroups ? kMaxGroup : 1); ++e) gm = (fi == e) ? gms[e] : gm;
     if constexpr (C::kSplitTokens) {
 #pragma unroll
       for (int a = 0; a < C::TM; ++a)
@@ -355,12 +363,14 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
   if (total > 0) load();
   for (int fi = 0; fi < nf; ++fi) {
     if (fi > 0) {
+      if constexpr (!kInPlace) {
 #pragma unroll
-      for (int a = 0; a < C::TM; ++a)
+        for (int a = 0; a < C::TM; ++a)
 #pragma unroll
-        for (int b = 0; b < C::TM; ++b)
+          for (int b = 0; b < C::TM; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
     }
@@ -400,6 +410,19 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void kv_mfma_kernel(Vi
         }
         store_state(pending);
         pending = -1;
+      }
+      if constexpr (kInPlace) {
+        if (cc == 0 && fi > 0) {  // the previous frame's slot is written: decay the running sum
+          float gm = 0.f;
+#pragma unroll
+          for (int e = 1; e < kMaxGroup; ++e) gm = (fi == e) ? gms[e] : gm;
+#pragma unroll
+          for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+            for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[a][b][r] *= gm;
+        }
       }
       if (ch + 1 < total) load();
 

@@ -148,8 +148,8 @@ gla_status gla_state_carry(const void *k, const void *v, const float *gamma, con
  * its workspace in a static device array of GLA_NOALLOC_SCRATCH_BYTES inside the
  * library instead of a caller's buffer. The call allocates and frees nothing.
  *  - Limit: sizes whose gla_fwd_framecausal_workspace exceeds
- *    GLA_NOALLOC_SCRATCH_BYTES (192 MiB: the 720p/60s shape with H = 32,
- *    d = 64 needs 138 MiB; a 31-frame block at B = 2, H = 40, d = 128, 156 MiB)
+ *    GLA_NOALLOC_SCRATCH_BYTES (256 MiB: the 720p/60s shape with H = 32,
+ *    d = 64 needs 138 MiB; a 31-frame block at B = 2, H = 40, d = 128, 237 MiB)
  *    are refused with GLA_ERR_WORKSPACE before any HIP call.
  *  - Memory: every GPU the library runs this call on holds its own copy of the
  *    array until the process ends. The first call on a device looks up the
@@ -161,7 +161,7 @@ gla_status gla_state_carry(const void *k, const void *v, const float *gamma, con
  *    array needs to start at zero, and a call leaves it holding that call's
  *    per-frame states.
  *  - Arguments, validation and errors otherwise as gla_fwd_framecausal. */
-#define GLA_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+#define GLA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
 
 gla_status gla_fwd_framecausal_noalloc(const void *q, const void *k, const void *v,
                                        const void *g, const float *gamma, const float *S_in,

@@ -60,9 +60,12 @@ def test_workspace_sizes(lib):
     E = 64 * 64 + 64
     assert gla.gla_fwd_framecausal_workspace(1, 32, 241, 920, 64) == (32 * 241 + 32 * 31) * E * 4
     assert gla.gla_state_carry_workspace(1, 32, 241, 920, 64) == (32 * 241 + 32 * 31) * E * 4
-    # d = 128 runs one frame per group: the scan completes each state in place
+    # d = 128 pairs frames from 1536 frames on (a carried state per pair of the
+    # 30-frame block's 15), and below that runs one frame per group, the scan
+    # completing each state in place (480 frames: two parts per frame)
     E2 = 128 * 128 + 128
-    assert gla.gla_fwd_framecausal_workspace(2, 40, 30, 920, 128) == 80 * 30 * E2 * 4
+    assert gla.gla_fwd_framecausal_workspace(2, 40, 30, 920, 128) == (80 * 30 + 80 * 15) * E2 * 4
+    assert gla.gla_fwd_framecausal_workspace(1, 16, 30, 920, 128) == 16 * 30 * 2 * E2 * 4
     # small problems are cut into parts to fill the GPU: the size grows accordingly
     small = gla.gla_fwd_framecausal_workspace(1, 8, 5, 256, 64)
     assert small > 8 * 5 * 4160 * 4 and small % 256 == 0
@@ -465,7 +468,7 @@ def test_rope_table_size_overflow(lib):
 def test_noalloc_refuses_sizes_beyond_its_scratch(lib):
     """gla_fwd_framecausal_noalloc checks the workspace its sizes need against
     the static scratch before any HIP call (so this runs without a GPU)."""
-    assert gla.NOALLOC_SCRATCH_BYTES == 192 << 20
+    assert gla.NOALLOC_SCRATCH_BYTES == 256 << 20
     # 720p/60s at H = 32, d = 64 fits; four times the heads does not
     assert gla.gla_fwd_framecausal_workspace(1, 32, 241, 920, 64) <= gla.NOALLOC_SCRATCH_BYTES
     assert gla.gla_fwd_framecausal_workspace(2, 40, 31, 920, 128) <= gla.NOALLOC_SCRATCH_BYTES

@@ -328,10 +328,12 @@ def test_block_split_resume_and_determinism():
 
 
 @pytest.mark.parametrize("G", [2, 3, 8])
-@pytest.mark.parametrize("d,dt", [(64, "bf16"), (32, "bf16"), (64, "f32")])
+@pytest.mark.parametrize("d,dt", [(64, "bf16"), (32, "bf16"), (64, "f32"), (128, "bf16"),
+                                  (128, "f32")])
 def test_frame_groups_with_carry(G, d, dt, path, monkeypatch):
-    """kv workgroups that own G consecutive frames (running decayed sum in the
-    accumulators, chained by the carry kernel), with a ragged last group and a
+    """kv workgroups that own G consecutive frames (running decayed sum, in
+    registers of its own at d <= 64 and in the accumulators themselves at
+    d = 128, chained by the carry kernel), with a ragged last group and a
     carried-in state; T <= 128 keeps one part per frame so grouping applies."""
     monkeypatch.setenv("GLA_FRAMES_PER_GROUP", str(G))
     x = synth.random_inputs(1, 3, 7, 100, d, dt, seed=50 + G + d, gamma_mu=1.0)

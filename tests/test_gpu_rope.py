@@ -148,6 +148,7 @@ ROPE_CASES = [
     ("bf16", 64, 6, 9, 7, 3, None),            # groups of 3 frames with a carry chain
     ("bf16", 32, 4, 10, 5, 2, None),
     ("bf16", 128, 8, 8, 3, None, None),
+    ("bf16", 128, 8, 8, 3, 2, None),          # d = 128 asked for frame pairs: one frame per group
     ("bf16", 64, 4, 6, 3, None, (0, 32, 32)),  # no temporal section
     ("bf16", 64, 4, 6, 3, None, (64, 0, 0)),   # temporal only
     ("bf16", 16, 3, 5, 3, None, None),         # vector-ALU kernels (no matrix-core d = 16)
