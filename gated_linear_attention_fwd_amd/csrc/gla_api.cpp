@@ -56,7 +56,8 @@ constexpr int64_t kTokenAlign = 32;
 // 0.484 ms, call 0.887 -> 0.857 ms; the d = 128 stream at B = 2, H = 40:
 // 0.357 -> 0.319 ms per block; 2 and 4 splits measured slower than 3 on
 // both). A split changes no token's arithmetic. The backward keeps the plan's
-// splits: each of its splits writes a partial sum of the state adjoint.
+// splits: each of its splits writes a partial sum of the state adjoint. Calls
+// with rotary positions keep them too (see run()).
 constexpr int64_t kSplitTargetTokens = 320;
 constexpr int64_t kMaxGroupFrames = 8;  // the kv kernels hold up to 8 decays
 // d = 128: frame pairs from 2 x 768 frames (1.5 rounds of resident kv workgroups)
@@ -356,7 +357,9 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
   // d = 128 carries a group's running sum in the accumulators, which the
   // frame's rotary turn must not touch: one frame per group there
   if (rk_.on && d == 128 && p.G > 1) single_frame_groups(&p);
-  forward_readout_splits(&p);
+  // (not with rotary positions: each split builds the turn table and the
+  // turned state fragments again; 720p/60s readout 0.568 -> 0.590 ms at 3)
+  if (!rk_.on) forward_readout_splits(&p);
   if (BH == 0 || (bidir && N == 0)) return GLA_OK;
   GLA_TRY(check_ws(p, ws, ws_bytes));
   const Path path = select_path(dt, d);
