@@ -144,20 +144,19 @@ struct AmCfg {
 template <int D, bool kF16>
 constexpr int kAnchorWaves = D == 64 ? (kF16 ? 3 : 2) : D == 128 ? 2 : 1;
 
-// kF16: the fp16 pass over every tile. Otherwise the bf16 hi + lo pass, which
-// computes only the tiles the fp16 pass marked.
+// One tile of queries, work item wg = (slab, segment, tile), with the
+// workgroup's LDS. kF16: P V in fp16 (a tile whose V is out of range is marked
+// instead of computed); otherwise P V in bf16 with hi + lo probabilities.
 template <int D, bool kF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAnchorWaves<D, kF16>))) void
-anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
+__device__ __forceinline__ void anchor_tile(const AnchorArgs &a, int tiles_per_seg,
+                                            int64_t seg_len, int64_t wg, char *smem) {
   using C = AmCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = lane >> 5;
   const int n = lane & 31;
   const int nseg = a.causal ? a.Fq : 1;
-  const int64_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
   // The work item is uniform, but 64-bit divisions leave it in vector
   // registers: read it into scalars, so that the key ranges and the block
   // addresses derived from it are scalar work (vector-ALU time is what bounds
@@ -169,11 +168,6 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
   const int64_t q0 = (int64_t)seg * seg_len + (int64_t)tile * C::BM;  // first query row
   const int nq = (int)min((int64_t)C::BM, seg_len - (int64_t)tile * C::BM);
   uint16_t *os = static_cast<uint16_t *>(a.o) + bh * Nq * D;
-  if constexpr (!kF16) {
-    // only the tiles the fp16 pass marked
-    const uint16_t mark = __builtin_nontemporal_load(os + q0 * D);
-    if (mark != kRedoMark) return;
-  }
   KeyRanges kr = anchor_ranges(a, seg);
   kr = KeyRanges{uniform64(kr.a0), uniform64(kr.a1), uniform64(kr.b0), uniform64(kr.b1)};
   const int nb_a = __builtin_amdgcn_readfirstlane((int)((kr.a1 - kr.a0 + C::BN - 1) / C::BN));
@@ -415,6 +409,49 @@ anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
   }
 }
 
+// A redo workgroup checks this many tiles' marks and computes the marked ones
+// in turn: on ordinary inputs the launch is 8 times fewer workgroups that each
+// make 8 loads (one per tile: 125 us at 720p/60s), and with every tile marked
+// it still has thousands of workgroups.
+constexpr int kRedoBatch = 8;
+
+// kF16: the fp16 pass, one tile per workgroup. Otherwise the bf16 hi + lo pass
+// over the tiles the fp16 pass marked, kRedoBatch tiles per workgroup.
+template <int D, bool kF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAnchorWaves<D, kF16>))) void
+anchor_mfma_kernel(AnchorArgs a, int tiles_per_seg, int64_t seg_len) {
+  using C = AmCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  if constexpr (kF16) {
+    anchor_tile<D, true>(a, tiles_per_seg, seg_len, xcd_contiguous(blockIdx.x, gridDim.x), smem);
+  } else {
+    const int nseg = a.causal ? a.Fq : 1;
+    const int64_t total = a.BH * nseg * (int64_t)tiles_per_seg;
+    const int64_t Nq = (int64_t)a.Fq * a.T;
+    // the marks first, all loads in flight together (a tile's first output
+    // element, read as the aligned word that holds it: D is even)
+    uint32_t mark[kRedoBatch];
+#pragma unroll
+    for (int i = 0; i < kRedoBatch; ++i) {
+      const int64_t wg = min((int64_t)blockIdx.x * kRedoBatch + i, total - 1);
+      const int tile = (int)(wg % tiles_per_seg);
+      const int seg = (int)((wg / tiles_per_seg) % nseg);
+      const int64_t bh = wg / ((int64_t)tiles_per_seg * nseg);
+      const int64_t q0 = (int64_t)seg * seg_len + (int64_t)tile * C::BM;
+      const uint32_t *m = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.o) +
+                                                             (bh * Nq + q0) * D);
+      mark[i] = __builtin_nontemporal_load(m);
+    }
+#pragma unroll 1
+    for (int i = 0; i < kRedoBatch; ++i) {
+      const int64_t wg = (int64_t)blockIdx.x * kRedoBatch + i;
+      if (wg >= total || (mark[i] & 0xFFFFu) != kRedoMark) continue;
+      anchor_tile<D, false>(a, tiles_per_seg, seg_len, wg, smem);
+      sync_lds();  // the next marked tile reuses the LDS
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Vector-ALU kernel: one query per thread, 64 per workgroup
 // ---------------------------------------------------------------------------
@@ -488,11 +525,14 @@ template <int D>
 void anchor_mfma_launch(const AnchorArgs &a, int64_t seg_len, bool f16, hipStream_t s) {
   const int nseg = a.causal ? a.Fq : 1;
   const int tiles = (int)((seg_len + AmCfg<D>::BM - 1) / AmCfg<D>::BM);
-  const dim3 grid((unsigned)(a.BH * nseg * tiles));
+  const int64_t items = a.BH * nseg * tiles;
   if (f16)
-    hipLaunchKernelGGL((anchor_mfma_kernel<D, true>), grid, dim3(256), 0, s, a, tiles, seg_len);
+    hipLaunchKernelGGL((anchor_mfma_kernel<D, true>), dim3((unsigned)items), dim3(256), 0, s, a,
+                       tiles, seg_len);
   else
-    hipLaunchKernelGGL((anchor_mfma_kernel<D, false>), grid, dim3(256), 0, s, a, tiles, seg_len);
+    hipLaunchKernelGGL((anchor_mfma_kernel<D, false>),
+                       dim3((unsigned)((items + kRedoBatch - 1) / kRedoBatch)), dim3(256), 0, s, a,
+                       tiles, seg_len);
 }
 
 template <typename TIn, int D>
