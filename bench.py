@@ -32,7 +32,7 @@ METRIC_GDN = "Gated DeltaNet fwd tokens/s at 720p/60s shape; % HBM roofline vs C
 METRIC_ANCHOR = ("Gated softmax anchor fwd tokens/s at 720p/60s shape (sink frames + local "
                  "window); % bf16 MFMA roofline vs CPU oracle")
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
-BF16_MFMA_PEAK = 2.5e15  # dense bf16 matrix-core peak, flop/s
+BF16_MFMA_PEAK = 2.5e15  # dense bf16 (and fp16) matrix-core peak, flop/s
 
 
 def parse():
@@ -406,7 +406,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved / 1e9, 1),
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                 "traffic": traffic_rec["bytes_per_launch"] if traffic_rec else None}
-    if anchor:  # a dense contraction: the bf16 matrix-core peak bounds it
+    if anchor:  # dense contractions (scores on bf16, P V on fp16 matrix cores: one 2.5 PFLOP/s peak)
         fl = dk["alg_flops_per_launch"] / (dk["avg_ms"] / 1e3)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(fl / 1e12, 1),
                     "peak": BF16_MFMA_PEAK / 1e12, "unit": "TFLOP/s",
