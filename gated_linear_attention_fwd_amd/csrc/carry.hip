@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kCarryThreads = 256;
 constexpr int kGroupBatch = 16;
+constexpr int kMaxGroupFrames = 8;  // the plan's most frames per group
 
 // Sum of a frame's P parts (P > 4), left to right as in the unrolled case:
 // loads go out eight at a time so that they overlap, the additions keep their
@@ -61,8 +62,12 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   const int64_t dd = (int64_t)d * d;
   const int64_t E = dd + d;
   const int64_t bh = blockIdx.x / blocks_per_slab;
-  const int64_t e = (blockIdx.x % blocks_per_slab) * kCarryThreads + threadIdx.x;
-  if (e >= E) return;
+  const int tid = threadIdx.x;
+  const int64_t e_own = (blockIdx.x % blocks_per_slab) * kCarryThreads + tid;
+  // threads past the state walk its last element too (the workgroup meets at
+  // barriers) and store nothing
+  const bool valid = e_own < E;
+  const int64_t e = valid ? e_own : E - 1;
 
   float s = 0.f;
   if (S_in) s = (e < dd) ? S_in[bh * dd + e] : z_in[bh * d + (e - dd)];
@@ -73,8 +78,18 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
   // G == 1: S_f of frame f (may be the slots themselves: ws is not restrict)
   float *dst = frames + bh * (int64_t)F * frames_stride + e;
   const float *gm_slab = gamma ? gamma + bh * F : nullptr;
+  // The decays go through vector loads (an opaque zero in the index), all of
+  // a batch at once. A group's decay is the product of its frames' decays:
+  // one thread per group of the batch forms it (its loads issued together,
+  // frames past the group reloading the last one and counting as 1, so the
+  // product keeps its order) and shares it through LDS. Loaded and multiplied
+  // one frame at a time, each scalar load was a memory round trip on the
+  // critical path (720p/60s, 8-frame groups: 23 us per call).
+  int vzero = 0;
+  asm volatile("" : "+v"(vzero));
+  __shared__ float gdec[2][kGroupBatch];
 
-  for (int g0 = 0; g0 < NG; g0 += kGroupBatch) {
+  for (int g0 = 0, bi = 0; g0 < NG; g0 += kGroupBatch, bi ^= 1) {
     float x[kGroupBatch];
     float w[kGroupBatch];
 #pragma unroll
@@ -94,24 +109,45 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(
       } else {
         if (ok) a = sum_parts(src, P, E);
       }
-      float wj = 1.f;
-      if (gm_slab)
-        for (int m = gc * G; m <= last; ++m) wj *= gm_slab[m];
       x[j] = ok ? a : 0.f;
-      w[j] = ok ? wj : 1.f;
+      w[j] = 1.f;
+      if (gm_slab && G == 1) w[j] = ok ? gm_slab[gc + vzero] : 1.f;
+    }
+    if (gm_slab && G > 1) {
+      if (tid < kGroupBatch) {
+        const int gc = min(g0 + tid, NG - 1);
+        const int f0 = gc * G;
+        const int last = min(F, f0 + G) - 1;
+        float wj = 1.f;
+        if (G <= kMaxGroupFrames) {
+          float gv[kMaxGroupFrames];
+#pragma unroll
+          for (int m = 0; m < kMaxGroupFrames; ++m) gv[m] = gm_slab[min(f0 + m, last) + vzero];
+#pragma unroll
+          for (int m = 0; m < kMaxGroupFrames; ++m) wj *= f0 + m <= last ? gv[m] : 1.f;
+        } else {
+          for (int m = f0; m <= last; ++m) wj *= gm_slab[m + vzero];
+        }
+        gdec[bi][tid] = wj;
+      }
+      // one barrier per batch: the buffer written here was last read before
+      // the previous batch's barrier
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kGroupBatch; ++j) w[j] = g0 + j < NG ? gdec[bi][j] : 1.f;
     }
 #pragma unroll
     for (int j = 0; j < kGroupBatch; ++j) {
       const int grp = g0 + j;
       if (grp < NG) {
-        if (keep_frames && G > 1) carry[(int64_t)grp * E] = s;
+        if (valid && keep_frames && G > 1) carry[(int64_t)grp * E] = s;
         s = fmaf(w[j], s, x[j]);
-        if (keep_frames && G == 1) dst[(int64_t)grp * frames_stride] = s;
+        if (valid && keep_frames && G == 1) dst[(int64_t)grp * frames_stride] = s;
       }
     }
   }
 
-  if (S_out) {
+  if (S_out && valid) {
     if (e < dd)
       S_out[bh * dd + e] = s;
     else
