@@ -327,6 +327,23 @@ def test_block_split_resume_and_determinism():
     assert e_o <= 1e-6 and state_err(S, S1.cpu().numpy()) <= 1e-6
 
 
+@pytest.mark.parametrize("G,d,dt", [(2, 32, "bf16"), (3, 64, "bf16"), (8, 64, "bf16"),
+                                    (8, 16, "f32"), (2, 128, "bf16")])
+def test_carry_over_several_batches(G, d, dt, path, monkeypatch):
+    """The carry chains groups in batches of 16, the decay of each group (the
+    product of its frames' gammas) formed once per batch and shared in LDS
+    through two buffers used in turn: 34 groups take three batches, the last
+    one ragged, and the state's d*d + d elements leave the last workgroup of
+    each slab partly empty (those threads still meet the barriers)."""
+    monkeypatch.setenv("GLA_FRAMES_PER_GROUP", str(G))
+    F = 34 * G - 1  # 34 groups, the last one a frame short
+    x = synth.random_inputs(1, 3, F, 16, d, dt, seed=700 + G + d, gamma_mu=2.5)
+    rng = np.random.default_rng(G + d)
+    S_in = rng.standard_normal((1, 3, d, d))
+    z_in = np.abs(rng.standard_normal((1, 3, d))) * 4
+    check_framecausal(x, dt, S_in=S_in, z_in=z_in, name="carry batches G=%d d=%d %s %s" % (G, d, dt, path))
+
+
 @pytest.mark.parametrize("G", [2, 3, 8])
 @pytest.mark.parametrize("d,dt", [(64, "bf16"), (32, "bf16"), (64, "f32"), (128, "bf16"),
                                   (128, "f32")])
