@@ -178,8 +178,35 @@ struct Profiler {
 };
 Profiler g_prof;
 
+// ---- optional launch log: GLA_LOG=1 prints each call's plan (how the work is
+// cut into workgroups) and each launch, in order, on stderr ----
+bool log_on() {
+  static const bool on = [] {
+    const char *e = getenv("GLA_LOG");
+    return e != nullptr && atoi(e) != 0;
+  }();
+  return on;
+}
+
+const char *path_name(Path path) { return path == Path::kMfma ? "mfma" : "valu"; }
+
+// A plan's geometry: kv workgroups BH * NG * P (G frames each, P parts of a
+// frame), carry workgroups BH * ceil((d*d + d) / 256), readout workgroups
+// BH * F * R (R splits of a frame).
+void log_plan(const char *call, const Plan &p, Path path) {
+  if (!log_on()) return;
+  fprintf(stderr,
+          "gla: %s path=%s BH=%lld F=%d T=%lld d=%d P=%d part_len=%lld G=%d NG=%d R=%d "
+          "read_len=%lld kv_wgs=%lld carry_wgs=%lld readout_wgs=%lld ws_bytes=%zu\n",
+          call, path_name(path), (long long)p.BH, p.F, (long long)p.T, p.d, p.P,
+          (long long)p.part_len, p.G, p.NG, p.R, (long long)p.read_len,
+          (long long)(p.BH * p.NG * p.P), (long long)(p.BH * ((p.state_elems() + 255) / 256)),
+          (long long)(p.BH * p.F * p.R), p.ws_bytes);
+}
+
 template <class Fn>
 hipError_t timed(Kind k, hipStream_t s, Fn &&fn) {
+  if (log_on()) fprintf(stderr, "gla: launch %s\n", kKindNames[k]);
   int slot = -1;
   {
     std::lock_guard<std::mutex> lock(g_prof.mu);
@@ -363,6 +390,9 @@ gla_status run(Mode mode, const gla_tensor *q, const gla_tensor *k, const gla_te
   if (BH == 0 || (bidir && N == 0)) return GLA_OK;
   GLA_TRY(check_ws(p, ws, ws_bytes));
   const Path path = select_path(dt, d);
+  log_plan(bidir ? "forward (bidirectional)" : states ? "forward (frame-causal, state record)"
+                                                     : "forward (frame-causal)",
+           p, path);
   if (rk_.on && path == Path::kMfma && rk_.entries() > kMaxRopeEntries)
     return fail(GLA_ERR_UNSUPPORTED,
                 "rope table of %d entries exceeds %d (1 + grid_h*dim_h/2 + grid_w*dim_w/2 + "
@@ -518,6 +548,9 @@ gla_status run_bwd(bool bidir, const gla_tensor *q, const gla_tensor *k, const g
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Path path = select_path(dt, d);
+  log_plan(bidir ? "backward (bidirectional)" : states ? "backward (frame-causal, state record)"
+                                                      : "backward (frame-causal)",
+           bp.f, path);
   if (rk_.on && path == Path::kMfma && rk_.entries() > kMaxRopeEntries)
     return fail(GLA_ERR_UNSUPPORTED,
                 "rope table of %d entries exceeds %d (1 + grid_h*dim_h/2 + grid_w*dim_w/2 + "
@@ -622,6 +655,13 @@ gla_status run_gdn(const void *q, const void *k, const void *v, const float *bet
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Path path = select_path(dt, d);
+  if (log_on())
+    fprintf(stderr,
+            "gla: gated deltanet path=%s BH=%lld F=%d T=%lld d=%d P=%d part_len=%lld "
+            "scan_frames_per_chunk=%d scan_chunks=%d gdn_kv_wgs=%lld ws_bytes=%zu\n",
+            path_name(path), (long long)p.BH, p.F, (long long)p.T, p.d, p.P,
+            (long long)p.part_len, p.scan_fc, p.scan_nc, (long long)(p.BH * p.F * p.P),
+            p.ws_bytes);
   float *wsf = static_cast<float *>(ws);
   // (T == 0 still launches it: every frame's sums are then written as zeros)
   if (p.F > 0)
@@ -683,6 +723,12 @@ gla_status run_anchor(const void *q, const void *k, const void *v, const void *g
   if (anchor_tiles(a, path) >= (int64_t(1) << 31))
     return fail(GLA_ERR_SHAPE, "sizes overflow the grid");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (log_on())
+    fprintf(stderr,
+            "gla: softmax anchor path=%s BH=%lld Fq=%d F=%d T=%d d=%d causal=%d n_sink=%d "
+            "window=%d tiles=%lld\n",
+            path_name(path), (long long)BH, Fq, F, T, d, causal, n_sink, window,
+            (long long)anchor_tiles(a, path));
   GLA_TRY(launched(timed(kKindAnchor, s, [&] { return launch_anchor(a, dt, path, s); }),
                    "anchor"));
   GLA_TRY(launched(timed(kKindAnchorRedo, s, [&] { return launch_anchor_redo(a, path, s); }),

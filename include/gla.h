@@ -464,8 +464,8 @@ int gla_version(void); /* 10600: gla_fwd_framecausal_noalloc (10500: rotary
  * returns, per kernel kind ("kv", "carry", "readout", and for the backward
  * "bwd_q", "rev_scan", "bwd_k", "dgamma", and for the Gated DeltaNet "gdn_kv",
  * "gdn_scan", "gdn_readout"; "gdn_scan" includes the summing of a frame's parts
- * where the frame is split over several workgroups; and "anchor"), the number
- * of launches
+ * where the frame is split over several workgroups; and "anchor",
+ * "anchor_redo"), the number of launches
  * and their summed event time. At most max_launches launches are timed; later
  * ones run untimed. Not meant to overlap with itself: one session at a time.
  * gla_profile_begin creates 2 * max_launches HIP events (max_launches must be
@@ -480,6 +480,12 @@ typedef struct gla_kernel_time {
 
 gla_status gla_profile_begin(int max_launches);
 gla_status gla_profile_end(gla_kernel_time *out, int max_out, int *n_out);
+
+/* Launch log: with the environment variable GLA_LOG set to a nonzero integer
+ * when the library first checks it, every call that launches kernels prints
+ * one line with its plan (how the work is cut: kv parts P and frame groups G,
+ * readout splits R, workgroups per kernel, workspace bytes) and one line per
+ * launch, in order, to stderr, each starting "gla: ". */
 
 /* Streaming bandwidth probe: one launch that moves `bytes` through HBM in the
  * access pattern of the mixer's kernels (16-byte loads and stores per lane,

@@ -59,14 +59,46 @@ def test_oracle_under_address_and_undefined_sanitizers(tmp_path):
     assert int(out.split(" checks")[0].split()[-1]) >= 80
 
 
-@pytest.mark.skipif(shutil.which("g++") is None or not os.path.isdir("/opt/rocm/include"),
-                    reason="g++ and the ROCm headers are required")
-def test_c_abi_host_code_under_address_and_undefined_sanitizers(tmp_path):
+@pytest.fixture(scope="module")
+def abi_exe(tmp_path_factory):
+    if shutil.which("g++") is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("g++ and the ROCm headers are required")
+    tmp_path = tmp_path_factory.mktemp("abi_san")
     exe = str(tmp_path / "abi_san")
     _build(["g++", "-std=c++17", *SAN, "-Wall", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
             "-I" + os.path.join(ROOT, "include"),
             os.path.join(ROOT, "gated_linear_attention_fwd_amd", "csrc", "gla_api.cpp"),
             os.path.join(HERE, "abi_stubs.cpp"), os.path.join(HERE, "abi_driver.cpp"),
             "-o", exe], tmp_path)
-    out = _run(exe)
+    return exe
+
+
+def test_c_abi_host_code_under_address_and_undefined_sanitizers(abi_exe):
+    out = _run(abi_exe)
     assert int(out.split(" checks")[0].split()[-1]) >= 200
+
+
+def test_launch_log(abi_exe):
+    """GLA_LOG=1: every call prints its plan (the workgroup geometry) and each
+    launch, in order, on stderr; without it nothing is printed."""
+    r = subprocess.run([abi_exe], capture_output=True, text=True,
+                       env=dict(ENV, GLA_LOG="1"), timeout=600)
+    assert r.returncode == 0, r.stderr[-4000:]
+    log = [l for l in r.stderr.splitlines() if l.startswith("gla: ")]
+    plans = [l for l in log if not l.startswith("gla: launch ")]
+    assert any(l.startswith("gla: forward (frame-causal) path=") and " G=" in l and " R=" in l
+               and " kv_wgs=" in l and " readout_wgs=" in l for l in plans), plans[:5]
+    assert any(l.startswith("gla: forward (bidirectional) path=") for l in plans)
+    assert any(l.startswith("gla: backward (frame-causal") for l in plans)
+    assert any(l.startswith("gla: gated deltanet path=") for l in plans)
+    assert any(l.startswith("gla: softmax anchor path=") and " tiles=" in l for l in plans)
+    launches = [l[len("gla: launch "):] for l in log if l.startswith("gla: launch ")]
+    for k in ("kv", "carry", "readout", "bwd_q", "rev_scan", "bwd_k", "gdn_kv", "gdn_scan",
+              "gdn_readout", "anchor", "anchor_redo"):
+        assert k in launches, k
+    # a forward's launches follow its plan line in order: kv, carry, readout
+    i = next(n for n, l in enumerate(log) if l.startswith("gla: forward (frame-causal) path="))
+    nxt = [l for l in log[i + 1:i + 4]]
+    assert nxt[:3] == ["gla: launch kv", "gla: launch carry", "gla: launch readout"], nxt
+    quiet = subprocess.run([abi_exe], capture_output=True, text=True, env=ENV, timeout=600)
+    assert not any(l.startswith("gla: ") for l in quiet.stderr.splitlines())
