@@ -220,13 +220,16 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
 // ---------------------------------------------------------------------------
 // Query side: one workgroup of 8 waves per (slab, frame, split). Per block of
 // BLK tokens:
-//   1. all threads: phi(q), g and dO rows -> LDS; den = phi(q) . z_f; and
-//      dnum = dO (.) sigmoid(g) / (den + eps) (it needs den, not num) -> bf16
-//      hi + lo tiles;
+//   1. all threads: phi(q) rows -> LDS; den = phi(q) . z_f; from the g and dO
+//      rows in registers dh = dO (.) sigmoid(g) (an fp32 tile), 1 - sigmoid(g)
+//      (an fp16 tile) and dnum = dh / (den + eps) (it needs den, not num;
+//      bf16 hi + lo tiles);
 //   2. at once: waves 0-3 ("N") num^T = S^T phi(Q)^T (hi + lo of S), then in
-//      the C layout dg (written over g) and the per-token sums of dh . h;
+//      the C layout dg = dh (.) h (.) (1 - sigmoid(g)) (written over the fp16
+//      tile) and the per-token sums of dh . h;
 //      waves 4-7 ("Q") S dnum^T (hi + lo of both, less lo x lo);
-//   3. waves 4-7: dq = [q > 0] (.) (S dnum^T + dden z) -> LDS; waves 0-3:
+//   3. waves 4-7: dq = [q > 0] (.) (S dnum^T + dden z) -> LDS (over the dh
+//      tile); waves 0-3:
 //      G += phi(Q)^T dnum (transposed LDS reads, as in kv); every thread adds
 //      dden phi(q) of its staged rows to gz;
 //   4. dq and dg rows -> global memory.
@@ -239,6 +242,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
 // a pair) turn back by R^T before dden z is added.
 // ---------------------------------------------------------------------------
 #define GLA_BQ_GROUP_BARRIER() __builtin_amdgcn_sched_barrier(0)
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct BqCfg {
@@ -264,8 +268,14 @@ struct BqCfg {
   static constexpr int GL_FLOATS = kGInLds ? KSPLIT * D * GLP : 1;
 };
 
+// Waves per SIMD bwd_q is held to: 4 (128 registers) at d <= 64 without
+// rotary positions, which keeps two workgroups per CU
 template <int D, bool kRope>
-__global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
+constexpr int kBqWaves = (D <= 64 && !kRope) ? 4 : 1;
+
+template <int D, bool kRope>
+__global__ __launch_bounds__(kBwThreads)
+__attribute__((amdgpu_waves_per_eu(kBqWaves<D, kRope>))) void bwd_q_mfma_kernel(
     View qview, View gview, View doview, View dqview, View dgview, int H,
     const float *__restrict__ st, int64_t sstride, float *__restrict__ gs, int F, int64_t T,
     int R, int64_t read_len, float eps, int state_frame, RopeK rope) {
@@ -279,12 +289,18 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
   [[maybe_unused]] char *const qhi = smem + 6 * TILE;  // kRope: turned phi(q), hi
   [[maybe_unused]] char *const qlo = smem + 7 * TILE;  // kRope: turned phi(q), lo
   extern __shared__ float2 rope_tab[];                 // kRope: turns of one frame
+  // The dg epilogue takes dh = dO (.) sigmoid(g) in fp32 and 1 - sigmoid(g)
+  // as fp16, both formed once when the block is staged (dO and g themselves
+  // are read there only); dq then goes over the dh tile, which its last
+  // reader is done with.
+  constexpr int HPITCH = 4 * D + 16;  // bytes per fp32 row of the dh tile
+  static_assert(C::BLK * HPITCH <= 2 * TILE, "dh tile larger than two tiles");
   char *const qtile = smem;              // phi(q)
-  char *const gtile = smem + TILE;       // g, then dg
-  char *const otile = smem + 2 * TILE;   // dO
-  char *const dnhi = smem + 3 * TILE;    // dnum, hi
-  char *const dnlo = smem + 4 * TILE;    // dnum, lo
-  char *const dqtile = smem + 5 * TILE;  // dq
+  char *const gtile = smem + TILE;       // 1 - sigmoid(g) (fp16), then dg
+  char *const dnhi = smem + 2 * TILE;    // dnum, hi
+  char *const dnlo = smem + 3 * TILE;    // dnum, lo
+  char *const htile = smem + 4 * TILE;   // dh (fp32)
+  char *const dqtile = htile;            // dq
   __shared__ float szf[D];
   __shared__ __attribute__((aligned(16))) float gl[C::GL_FLOATS];  // G^T images [n][m]
   __shared__ float inv_s[C::BLK];
@@ -422,8 +438,6 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
         zc[0] = za.x; zc[1] = za.y; zc[2] = za.z; zc[3] = za.w;
         zc[4] = zb.x; zc[5] = zb.y; zc[6] = zb.z; zc[7] = zb.w;
       }
-      *reinterpret_cast<uint4 *>(gtile + row * C::PITCH + c * 16) = rg[i];
-      *reinterpret_cast<uint4 *>(otile + row * C::PITCH + c * 16) = ro[i];
       float dp = lo_bf16(w.x) * zc[0];
       dp = fmaf(hi_bf16(w.x), zc[1], dp);
       dp = fmaf(lo_bf16(w.y), zc[2], dp);
@@ -438,13 +452,20 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
       if (c == 0) inv_s[row] = inv;
       const uint32_t gw[4] = {rg[i].x, rg[i].y, rg[i].z, rg[i].w};
       const uint32_t ow[4] = {ro[i].x, ro[i].y, ro[i].z, ro[i].w};
-      uint32_t hw[4], lw[4];
+      uint32_t hw[4], lw[4], omw[4];
+      float dh8[8];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const float d0 = lo_bf16(ow[e2]) * fast_sigmoid(lo_bf16(gw[e2])) * inv;
-        const float d1 = hi_bf16(ow[e2]) * fast_sigmoid(hi_bf16(gw[e2])) * inv;
-        split2(d0, d1, hw[e2], lw[e2]);
+        const float s0 = fast_sigmoid(lo_bf16(gw[e2])), s1 = fast_sigmoid(hi_bf16(gw[e2]));
+        dh8[2 * e2] = lo_bf16(ow[e2]) * s0;
+        dh8[2 * e2 + 1] = hi_bf16(ow[e2]) * s1;
+        split2(dh8[2 * e2] * inv, dh8[2 * e2 + 1] * inv, hw[e2], lw[e2]);
+        const f16x2_t om = __builtin_convertvector(f32x2{1.f - s0, 1.f - s1}, f16x2_t);  // nearest
+        omw[e2] = __builtin_bit_cast(uint32_t, om);
       }
+      *reinterpret_cast<uint4 *>(gtile + row * C::PITCH + c * 16) = make_uint4(omw[0], omw[1], omw[2], omw[3]);
+      *reinterpret_cast<float4 *>(htile + row * HPITCH + c * 32) = make_float4(dh8[0], dh8[1], dh8[2], dh8[3]);
+      *reinterpret_cast<float4 *>(htile + row * HPITCH + c * 32 + 16) = make_float4(dh8[4], dh8[5], dh8[6], dh8[7]);
       *reinterpret_cast<uint4 *>(dnhi + row * C::PITCH + c * 16) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       *reinterpret_cast<uint4 *>(dnlo + row * C::PITCH + c * 16) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
@@ -478,17 +499,16 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_mfma_kernel(
         GLA_BQ_GROUP_BARRIER();
         const int off = tl * C::PITCH + (32 * mb + 8 * rgp + 4 * h) * 2;
         const uint2 gv = *reinterpret_cast<const uint2 *>(gtile + off);
-        const uint2 ov = *reinterpret_cast<const uint2 *>(otile + off);
-        const float g4[4] = {lo_bf16(gv.x), hi_bf16(gv.x), lo_bf16(gv.y), hi_bf16(gv.y)};
-        const float o4[4] = {lo_bf16(ov.x), hi_bf16(ov.x), lo_bf16(ov.y), hi_bf16(ov.y)};
+        const float4 hv = *reinterpret_cast<const float4 *>(htile + tl * HPITCH + (32 * mb + 8 * rgp + 4 * h) * 4);
+        const f16x2_t om01 = __builtin_bit_cast(f16x2_t, gv.x), om23 = __builtin_bit_cast(f16x2_t, gv.y);
+        const float om4[4] = {(float)om01[0], (float)om01[1], (float)om23[0], (float)om23[1]};
+        const float dh4[4] = {hv.x, hv.y, hv.z, hv.w};
         float dg4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float sg = fast_sigmoid(g4[e]);
           const float hh = acc[4 * rgp + e] * inv;
-          const float dh = o4[e] * sg;
-          dg4[e] = dh * hh * (1.f - sg);
-          part = fmaf(dh, hh, part);
+          dg4[e] = dh4[e] * hh * om4[e];
+          part = fmaf(dh4[e], hh, part);
         }
         *reinterpret_cast<uint2 *>(gtile + off) =
             make_uint2(pack_bf16x2(dg4[0], dg4[1]), pack_bf16x2(dg4[2], dg4[3]));

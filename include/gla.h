@@ -176,7 +176,9 @@ gla_status gla_fwd_framecausal_noalloc(const void *q, const void *k, const void 
  * optional dS_out = dL/dS_out and dz_out = dL/dz_out (fp32, both or neither;
  * NULL: zero). The pages state the forward only; these are its chain rule
  * (the derivative of ReLU taken as 0 at 0):
- *   dq, dk, dv, dg  [B][H][N][d], the input dtype, rounded from fp32;
+ *   dq, dk, dv, dg  [B][H][N][d], the input dtype, rounded from fp32 (on the
+ *                   bf16 matrix-core path dg takes 1 - sigmoid(g) rounded to
+ *                   fp16, about 11 significant bits, before the product);
  *   dgamma          [B][H][F] fp32 (frame-causal; NULL: not computed);
  *   dS_in, dz_in    fp32, dL/dS_in and dL/dz_in (frame-causal; both or neither;
  *                   with S_in NULL they are the gradients of a zero state).
