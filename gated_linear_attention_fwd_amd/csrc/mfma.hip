@@ -590,11 +590,6 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
   // overlaps the state's
   load(0);
   bf16x8 ahi[C::KS], alo[C::KS];
-  // S = hi + lo, both bf16: returns hi in the low half, lo in the high half
-  auto split = [&](float sv) -> uint32_t {
-    const uint16_t sh = f32_to_bf16_rne(sv);
-    return (uint32_t)sh | ((uint32_t)f32_to_bf16_rne(sv - bf16_to_f32(sh)) << 16);
-  };
   // The fragments are built in one straight run per case (the carry test is
   // outside the k-step loop, and the normaliser's likewise below), so that the
   // compiler issues every k-step's loads before it waits: with the test
@@ -606,7 +601,6 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
     auto build = [&](auto state_at) {
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        i16x8 hv, lv;
         float sv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) sv[e] = state_at((16 * ks + 8 * h + e) * D + jcol);
@@ -621,14 +615,12 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
             sv[e + 1] = ab.y;
           }
         }
+        // S = hi + lo, both bf16
+        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t hl = split(sv[e]);
-          hv[e] = (short)(hl & 0xFFFFu);
-          lv[e] = (short)(hl >> 16);
-        }
-        ahi[ks] = __builtin_bit_cast(bf16x8, hv);
-        alo[ks] = __builtin_bit_cast(bf16x8, lv);
+        for (int e = 0; e < 4; ++e) split2(sv[2 * e], sv[2 * e + 1], hw[e], lw[e]);
+        ahi[ks] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        alo[ks] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
     };
     if (has_carry)
@@ -707,10 +699,7 @@ __attribute__((amdgpu_waves_per_eu(kMinWaves<D, kRope>))) void readout_kernel(
       const float o1 = fast_sigmoid(hi_bf16(gv.x)) * (acc[4 * rg + 1] * inv);
       const float o2 = fast_sigmoid(lo_bf16(gv.y)) * (acc[4 * rg + 2] * inv);
       const float o3 = fast_sigmoid(hi_bf16(gv.y)) * (acc[4 * rg + 3] * inv);
-      uint2 ow;
-      ow.x = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
-      ow.y = (uint32_t)f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
-      *cell = ow;
+      *cell = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
     }
     sync_lds();
     {
