@@ -504,7 +504,7 @@ def practical_peak(dev, nbytes=1 << 30, reps=10):
     b = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(2)
     out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     moved = {"read": 1, "read_nt": 1, "write": 1, "write_nt": 1, "copy": 2, "copy_nt": 2,
-             "read2_write1": 3, "read2_write1_nt": 3}
+             "read2_write1": 3, "read2_write1_nt": 3, "read2_nt_write_eighth": 2.125}
 
     def run(fn):
         for _ in range(2):

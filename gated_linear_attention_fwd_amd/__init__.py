@@ -975,7 +975,7 @@ def gla_softmax_anchor(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: tor
 
 
 PROBE_KINDS = ("read", "read_nt", "write", "write_nt", "copy", "copy_nt", "read2_write1",
-               "read2_write1_nt")
+               "read2_write1_nt", "read2_nt_write_eighth")
 
 
 def stream_probe(kind: str, out: torch.Tensor, a: Optional[torch.Tensor] = None,

@@ -39,7 +39,8 @@ enum ProbeKind {
   kCopyNt = 5,
   kRead2Write1 = 6,
   kRead2Write1Nt = 7,
-  kNumProbeKinds = 8
+  kRead2WriteEighth = 8,
+  kNumProbeKinds = 9
 };
 
 template <bool kNt>
@@ -57,7 +58,8 @@ __global__ __launch_bounds__(kProbeThreads) void probe_kernel(const uint4 *__res
                                                              const uint4 *__restrict__ b,
                                                              uint4 *__restrict__ out, int64_t n,
                                                              uint32_t *__restrict__ sink) {
-  constexpr bool kNt = (kKind & 1) != 0;
+  constexpr bool kNt = (kKind & 1) != 0 || kKind == kRead2WriteEighth;
+  constexpr bool kTwo = kKind == kRead2Write1 || kKind == kRead2Write1Nt || kKind == kRead2WriteEighth;
   constexpr bool kRanges = kKind == kWrite || kKind == kWriteNt;
   // ranges: [r0, r1) of this workgroup; striding: the whole buffer
   const int64_t r0 = kRanges ? (int64_t)blockIdx.x * kRangePieces : 0;
@@ -65,19 +67,26 @@ __global__ __launch_bounds__(kProbeThreads) void probe_kernel(const uint4 *__res
   const int64_t first = kRanges ? r0 : (int64_t)blockIdx.x * kProbeThreads * kUnroll;
   const int64_t step = kProbeThreads * kUnroll * (kRanges ? 1 : (int64_t)gridDim.x);
   uint32_t fold = 0;
-  for (int64_t base = first + threadIdx.x; base < r1; base += step) {
+  int64_t it = blockIdx.x;  // kRead2WriteEighth: this iteration writes when it % 8 == 7
+  for (int64_t base = first + threadIdx.x; base < r1; base += step, ++it) {
     uint4 x[kUnroll], y[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = min(base + (int64_t)u * kProbeThreads, r1 - 1);
       if constexpr (kKind != kWrite && kKind != kWriteNt) x[u] = ld_stream16<kNt>(a + i);
-      if constexpr (kKind == kRead2Write1 || kKind == kRead2Write1Nt) y[u] = ld_stream16<kNt>(b + i);
+      if constexpr (kTwo) y[u] = ld_stream16<kNt>(b + i);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = base + (int64_t)u * kProbeThreads;
       if constexpr (kKind == kRead || kKind == kReadNt) {
         fold ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+      } else if constexpr (kKind == kRead2WriteEighth) {
+        // every workgroup writes on one iteration in eight, a different one for
+        // neighbouring workgroups (with the grid a multiple of 8, exactly an
+        // eighth of each iteration's pieces)
+        if ((it & 7) == 7 && i < r1)
+          out[i] = make_uint4(x[u].x ^ y[u].x, x[u].y ^ y[u].y, x[u].z ^ y[u].z, x[u].w ^ y[u].w);
       } else if (i < r1) {
         if constexpr (kKind == kWrite || kKind == kWriteNt) {
           const uint32_t w = (uint32_t)i;
@@ -130,6 +139,7 @@ hipError_t launch_probe(int kind, const void *a, const void *b, void *out, size_
     GLA_PROBE(kCopyNt)
     GLA_PROBE(kRead2Write1)
     GLA_PROBE(kRead2Write1Nt)
+    GLA_PROBE(kRead2WriteEighth)
     default:
       return hipErrorInvalidValue;
   }

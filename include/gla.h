@@ -495,7 +495,10 @@ gla_status gla_profile_end(gla_kernel_time *out, int max_out, int *n_out);
  * kernels are held against. kind: 0 read a, 1 read a nontemporal, 2 write
  * out, 3 write out nontemporal, 4 copy a to out, 5 the copy nontemporal,
  * 6 out = a ^ b (two reads and one write, the readout's pattern), 7 that
- * nontemporal. a, b, out: device buffers of `bytes` bytes each (as the kind
+ * nontemporal, 8 a and b read nontemporally with plain stores of a ^ b into
+ * one eighth of out (kv's pattern: two streamed reads with its frame states
+ * written between them; every workgroup writes on one grid iteration in
+ * eight). a, b, out: device buffers of `bytes` bytes each (as the kind
  * uses them; out is required for every kind: the read kinds may write a few
  * words into it), 16-byte aligned, out overlapping neither a nor b; `bytes` a
  * positive multiple of 256 KiB. Errors: GLA_ERR_VALUE (kind), GLA_ERR_SHAPE,

@@ -486,12 +486,13 @@ def test_stream_probe_validation(lib):
     f = lib.gla_stream_probe
     MiB = 1 << 20
     a, b, o = FAKE, FAKE + 0x10000000, FAKE + 0x20000000
-    assert f(8, p(a), p(b), p(o), MiB, None) == VALUE
+    assert f(9, p(a), p(b), p(o), MiB, None) == VALUE
     assert f(-1, p(a), p(b), p(o), MiB, None) == VALUE
     assert f(0, p(a), None, p(o), MiB + 16, None) == SHAPE  # not a multiple of 256 KiB
     assert f(0, p(a), None, p(o), 0, None) == SHAPE
     assert f(0, None, None, p(o), MiB, None) == NULL        # read needs a
     assert f(6, p(a), None, p(o), MiB, None) == NULL        # two reads need b
+    assert f(8, p(a), None, p(o), MiB, None) == NULL
     assert f(2, None, None, None, MiB, None) == NULL        # every kind needs out
     assert f(4, p(a + 4), None, p(o), MiB, None) == ALIGN
     assert f(4, p(a), None, p(a + MiB // 2), MiB, None) == ALIAS
