@@ -290,13 +290,14 @@ void noalloc_calls() {
 void probe_and_profile_calls() {
   const size_t n = 256 << 10;
   Buf a(n), b(n), out(n);
-  for (int kind = 0; kind < 8; ++kind) {
+  for (int kind = 0; kind < 9; ++kind) {
     reset();
     CHECK(gla_stream_probe(kind, a.p, b.p, out.p, n, nullptr) == GLA_OK, "probe kind %d", kind);
     CHECK(launches() == "probe", "probe launches %s", launches().c_str());
   }
   reset();
-  CHECK(gla_stream_probe(8, a.p, b.p, out.p, n, nullptr) != GLA_OK, "probe kind 8 accepted");
+  CHECK(gla_stream_probe(9, a.p, b.p, out.p, n, nullptr) != GLA_OK, "probe kind 9 accepted");
+  CHECK(gla_stream_probe(8, a.p, nullptr, out.p, n, nullptr) != GLA_OK, "kv-mix probe without b");
   CHECK(gla_stream_probe(0, a.p, b.p, out.p, n + 16, nullptr) != GLA_OK, "odd size accepted");
   CHECK(gla_stream_probe(4, a.p, b.p, a.p, n, nullptr) != GLA_OK, "aliased copy accepted");
   CHECK(stubs::g_log.empty(), "refused probes launched %s", launches().c_str());

@@ -280,7 +280,7 @@ void *noalloc_scratch(hipError_t *err) {
   return buf;
 }
 
-int probe_kinds() { return 8; }
+int probe_kinds() { return 9; }
 
 hipError_t launch_probe(int kind, const void *a, const void *b, void *out, size_t bytes,
                         hipStream_t) {

@@ -64,8 +64,45 @@ def test_json_line_carries_the_contract_keys():
     for k in ("read_GBps", "read_nt_GBps", "copy_GBps", "read2_write1_nt_GBps",
               "torch_copy_GBps"):
         assert 0 < peak[k] < 8000, k
+    # kv's mix rewrites the same eighth of its buffer on every launch, which
+    # the last-level cache may partly hold
+    assert 0 < peak["read2_nt_write_eighth_GBps"] < 10000
     for name in ("720p_5s_bidir", "720p_5s_framecausal", "720p_60s_stream_d128"):
         wl = d["workloads"][name]
         assert wl["ms"]["min"] <= wl["ms"]["median"] <= wl["ms"]["max"], name
         assert wl["tokens_per_s"] > 0 and 0 < wl["frac_of_hbm_peak"] < 1, name
         assert wl["parity"]["max_slab_rel_err"] <= wl["parity"]["bar"], name
+
+
+@pytest.mark.gpu
+def test_stream_probes_move_what_they_document():
+    """Each bandwidth probe kind writes what gla_stream_probe documents (2 MiB
+    buffers): the write kinds piece i as four copies of i, the copies a, the two
+    reads plus one write a ^ b, and kv's mix a ^ b into exactly one eighth of
+    the 16-byte pieces, the others untouched."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import gated_linear_attention_fwd_amd as gla
+
+    n = 2 << 20
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen)
+    b = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen)
+    xor = torch.bitwise_xor(a, b)
+    pieces = torch.arange(n // 16, dtype=torch.int32, device="cuda").repeat_interleave(4)
+    for kind in gla.PROBE_KINDS:
+        out = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+        gla.stream_probe(kind, out, a, b)
+        torch.cuda.synchronize()
+        if kind.startswith("write"):
+            assert torch.equal(out.view(torch.int32), pieces), kind
+        elif kind.startswith("copy"):
+            assert torch.equal(out, a), kind
+        elif kind.startswith("read2_write1"):
+            assert torch.equal(out, xor), kind
+        elif kind == "read2_nt_write_eighth":
+            written = (out.view(-1, 16) != 0x5A).any(dim=1)
+            assert int(written.sum()) == n // 16 // 8, int(written.sum())
+            assert torch.equal(out.view(-1, 16)[written], xor.view(-1, 16)[written])
+        else:
+            assert kind in ("read", "read_nt"), kind
