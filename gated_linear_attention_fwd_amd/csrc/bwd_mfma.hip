@@ -47,8 +47,15 @@ struct BkCfg {
   static constexpr int ROWS_PER_PASS = kBwThreads / ROW_CHUNKS;
 };
 
+// Waves per SIMD bwd_k is held to: 4 (128 registers) at d = 128 without
+// rotary positions, so that two of its 8-wave workgroups share a CU (136
+// registers left it one)
 template <int D, bool kRope>
-__global__ __launch_bounds__(kBwThreads) void bwd_k_mfma_kernel(
+constexpr int kBkWaves = (D == 128 && !kRope) ? 4 : 1;
+
+template <int D, bool kRope>
+__global__ __launch_bounds__(kBwThreads)
+__attribute__((amdgpu_waves_per_eu(kBkWaves<D, kRope>))) void bwd_k_mfma_kernel(
     View kview, View vview, View dkview, View dvview, int H, const float *__restrict__ gs, int F,
     int64_t T, int P, int R, int64_t part_len, int adj_frame, RopeK rope) {
   using C = BkCfg<D>;
